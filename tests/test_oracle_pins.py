@@ -1,0 +1,457 @@
+"""Pins that hold the CPU oracle to something other than itself.
+
+Each test names the fact it checks: a published test vector, a closed form,
+a textbook special case, brute force on tiny inputs, an invariant, or the
+method's own statistical claim (unbiasedness, 1/m variance).  A plausible
+mistake in the oracle (dropped term, wrong sign or index, transposed operand,
+wrong constant) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy import integrate
+
+import oracle as O
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- O1 PRNG
+def test_splitmix64_published_vector():
+    # SplitMix64 from state 0: the first outputs of the reference generator
+    # (Steele, Lea & Flood 2014; Vigna's splitmix64.c) are these three words.
+    w = O.splitmix64(0, 0, np.arange(3))
+    assert [int(x) for x in w] == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    # seed ^ tag keys the stream
+    assert int(O.splitmix64(5, 5, [0])[0]) == 0xE220A8397B1DCDAF
+
+
+def test_gaussian_matrix_is_standard_normal():
+    S = O.gaussian_matrix(1024, 1024, seed=7).astype(np.float64).ravel()
+    n = S.size
+    se = 1 / math.sqrt(n)
+    assert abs(S.mean()) < 4 * se
+    assert abs(S.var() - 1) < 4 * math.sqrt(2 / n)
+    kurt = np.mean(S ** 4) / S.var() ** 2
+    assert abs(kurt - 3) < 4 * math.sqrt(24 / n)
+    # P(|g| > 1.96) = 0.05 for a standard normal
+    frac = np.mean(np.abs(S) > 1.959963984540054)
+    assert abs(frac - 0.05) < 4 * math.sqrt(0.05 * 0.95 / n)
+    # cos and sin halves of a pair are uncorrelated
+    c, s = S[0::2], S[1::2]
+    assert abs(np.mean(c * s)) < 4 / math.sqrt(c.size)
+
+
+def test_rademacher_signs_balanced():
+    D = O.rademacher_signs(1 << 16, seed=3)
+    assert set(np.unique(D)) == {-1.0, 1.0}
+    assert abs(D.mean()) < 4 / math.sqrt(D.size)
+
+
+# ---------------------------------------------------------------- O2 rotation
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16])
+def test_sylvester_equals_walsh_closed_form(d):
+    # Brute force: the natural-order Sylvester matrix has H_ij = (-1)^popcount(i & j).
+    H = O.sylvester_hadamard(d)
+    ref = np.array([[(-1) ** bin(i & j).count("1") for j in range(d)] for i in range(d)])
+    assert np.array_equal(H, ref)
+
+
+def test_paley_12_is_hadamard():
+    H = O.paley_hadamard_12()
+    assert set(np.unique(H)) == {-1, 1}
+    assert np.array_equal(H @ H.T, 12 * np.eye(12, dtype=np.int64))
+
+
+@pytest.mark.parametrize("d", [16, 128, 1536])
+def test_rotation_orthogonal_norm_preserving(d):
+    R = O.rotation_matrix(d, seed=1234)
+    assert np.max(np.abs(R.T @ R - np.eye(d))) < 1e-13
+    x = np.random.default_rng(0).standard_normal((5, d))
+    assert np.allclose(np.linalg.norm(x @ R.T, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+
+
+def test_rotation_is_hadamard_times_signs():
+    d = 128
+    R = O.rotation_matrix(d, seed=99)
+    D = O.rademacher_signs(d, 99)
+    # column j of R = D_j * column j of H / sqrt(d), with H Walsh closed form
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(d)] for i in range(d)])
+    assert np.array_equal(R * math.sqrt(d), H * D[None, :])
+
+
+def test_kron_index_convention_1536():
+    H = O.hadamard(1536)
+    H12, H128 = O.paley_hadamard_12(), O.sylvester_hadamard(128)
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        a, b, i, j = rng.integers(0, 12), rng.integers(0, 12), rng.integers(0, 128), rng.integers(0, 128)
+        assert H[a * 128 + i, b * 128 + j] == H12[a, b] * H128[i, j]
+
+
+# ---------------------------------------------------------------- density / Lloyd-Max
+@pytest.mark.parametrize("d", [16, 128, 1536])
+def test_density_normalised_and_second_moment(d):
+    f = lambda x: float(O.sphere_coordinate_density(x, d))
+    s = 6 / math.sqrt(d)
+    tot = integrate.quad(f, -1, 1, points=[-s, 0, s], limit=200)[0]
+    m2 = integrate.quad(lambda x: x * x * f(x), -1, 1, points=[-s, 0, s], limit=200)[0]
+    assert abs(tot - 1) < 1e-10
+    assert abs(m2 * d - 1) < 1e-9      # E[X^2] = 1/d for a coordinate of a unit vector
+
+
+@pytest.mark.parametrize("d", [128, 1536])
+def test_cdf_and_moment_match_quadrature(d):
+    f = lambda x: float(O.sphere_coordinate_density(x, d))
+    for t in np.array([-2.0, -0.7, 0.0, 0.3, 1.1, 2.5]) / math.sqrt(d):
+        ref = integrate.quad(f, -1, t, limit=400, points=[0.0] if t > 0 else None)[0]
+        assert abs(float(O.sphere_coordinate_cdf(t, d)) - ref) < 1e-10
+    lo, hi = -0.4 / math.sqrt(d), 1.3 / math.sqrt(d)
+    ref = integrate.quad(lambda x: x * f(x), lo, hi)[0]
+    assert abs(float(O.sphere_coordinate_first_moment(lo, hi, d)) - ref) < 1e-12
+
+
+@pytest.mark.parametrize("d", [128, 1536])
+def test_lloyd_max_one_bit_closed_form(d):
+    # b = 1: c = E|X| = Γ(d/2) / (√π Γ((d+1)/2)),  D = 1 - d c²
+    c, t, _ = O.lloyd_max(d, 1)
+    ref = math.exp(math.lgamma(d / 2) - 0.5 * math.log(math.pi) - math.lgamma((d + 1) / 2))
+    assert abs(c[1] - ref) < 1e-11 * ref and abs(c[0] + ref) < 1e-11 * ref
+    assert t[0] == 0.0
+    if d == 128:
+        assert abs(ref - 0.070661572738) < 1e-11
+        assert abs((1 - d * ref * ref) - 0.360888594) < 1e-8
+
+
+# Max (1960), "Quantizing for minimum distortion", optimum quantizer for the
+# unit Gaussian: output levels and mean squared error for N = 2, 4, 8 levels.
+MAX_1960 = {1: ([0.7979], 0.3634), 2: ([0.4528, 1.510], 0.1175), 3: ([0.2451, 0.7560, 1.344, 2.152], 0.03454)}
+
+
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_lloyd_max_gaussian_limit_matches_max_1960(b):
+    d = 1 << 16   # the sphere law tends to N(0, 1/d); sqrt(d)*c tends to Max's levels
+    c, t, _ = O.lloyd_max(d, b)
+    levels, mse = MAX_1960[b]
+    got = c[len(c) // 2:] * math.sqrt(d)
+    assert np.allclose(got, levels, atol=1.5e-3)
+    D = _distortion_by_quadrature(c, t, d)
+    assert abs(D - mse) < 2e-4
+
+
+def _distortion_by_quadrature(c, t, d):
+    f = lambda x: float(O.sphere_coordinate_density(x, d))
+    edges = np.concatenate([[-1.0], t, [1.0]])
+    tot = 0.0
+    for k in range(len(c)):
+        lo, hi = edges[k], edges[k + 1]
+        # integrate on a window that holds all the mass (|x| < 12/sqrt(d)) to keep quad accurate
+        w = 12 / math.sqrt(d)
+        lo, hi = max(lo, -w), min(hi, w)
+        tot += integrate.quad(lambda x: (x - c[k]) ** 2 * f(x), lo, hi, limit=200)[0]
+    return tot * d
+
+
+@pytest.mark.parametrize("d,b", [(128, 2), (128, 3), (1536, 2), (1536, 3)])
+def test_lloyd_max_fixed_point_and_bound(d, b):
+    c, t, _ = O.lloyd_max(d, b)
+    f = lambda x: float(O.sphere_coordinate_density(x, d))
+    edges = np.concatenate([[-1.0], t, [1.0]])
+    w = 14 / math.sqrt(d)
+    for k in range(len(c)):   # centroid condition, checked by quadrature
+        lo, hi = max(edges[k], -w), min(edges[k + 1], w)
+        m0 = integrate.quad(f, lo, hi, limit=200, epsabs=1e-15)[0]
+        m1 = integrate.quad(lambda x: x * f(x), lo, hi, limit=200, epsabs=1e-16)[0]
+        assert abs(m1 / m0 - c[k]) * math.sqrt(d) < 1e-9
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=1e-17)   # nearest neighbour
+    assert np.array_equal(c, -c[::-1])                                    # symmetric
+    D = _distortion_by_quadrature(c, t, d)
+    # information-theoretic lower bound D_MSE >= 4^-b (深度拆解 第六部分)
+    assert D >= 4.0 ** -b
+    assert D < {2: 0.12, 3: 0.036}[b]
+
+
+def test_walsh_expansion_symmetric_codebook_has_only_odd_terms():
+    for b in (2, 3):
+        c, _, _ = O.lloyd_max(128, b)
+        coef = O.walsh_plane_coefficients(c)
+        for S, v in coef.items():
+            if len(S) % 2 == 0:
+                assert abs(v) < 1e-16
+        # reconstruct
+        for idx in range(1 << b):
+            acc = 0.0
+            for S, v in coef.items():
+                s = 1.0
+                for i in S:
+                    s *= 2 * ((idx >> i) & 1) - 1
+                acc += v * s
+            assert abs(acc - c[idx]) < 1e-15
+
+
+# ---------------------------------------------------------------- packing / storage
+def test_packing_bit_positions():
+    d, b = 128, 3
+    idx = np.zeros((1, d), dtype=np.int64)
+    idx[0, 37] = 0b101
+    codes = O.pack_planes(idx, b)
+    assert codes.shape == (1, 12)
+    expect = np.zeros(12, dtype=np.uint32)
+    expect[0 * 4 + 1] = 1 << 5     # plane 0, word 37//32 = 1, bit 5
+    expect[2 * 4 + 1] = 1 << 5     # plane 2
+    assert np.array_equal(codes[0], expect)
+    rnd = np.random.default_rng(0).integers(0, 8, size=(7, d))
+    assert np.array_equal(O.unpack_planes(O.pack_planes(rnd, b), b, d), rnd)
+    bits = np.random.default_rng(1).integers(0, 2, size=(3, 256))
+    assert np.array_equal(O.unpack_bits(O.pack_bits(bits), 256), bits)
+
+
+@pytest.mark.parametrize("bits,ratio", [(3, 16 / 3), (4, 4.0)])
+def test_storage_ratio_vs_fp16(bits, ratio):
+    cd = O.make_codec(128, bits)
+    payload = 4 * (cd.code_words + cd.sign_words)
+    assert payload == 128 * bits // 8            # d * B_t / 8 bytes
+    assert (2 * 128) / payload == pytest.approx(ratio, rel=0, abs=1e-15)
+    assert cd.record_bytes == payload + 8         # + fp32 ν and γ
+
+
+# ---------------------------------------------------------------- O4 encode
+@pytest.fixture(scope="module")
+def codec3():
+    return O.make_codec(128, 3, seed=1234)
+
+
+@pytest.fixture(scope="module")
+def codec4():
+    return O.make_codec(128, 4, seed=1234)
+
+
+@pytest.mark.parametrize("which", ["codec3", "codec4"])
+def test_encode_mc_distortion_equals_codebook_distortion(which, request):
+    # Gaussian x: x/||x|| is uniform on the sphere, so after any fixed rotation
+    # each coordinate follows the sphere law and E||u - Rᵀ ĉ||² = d·E(X - Q(X))².
+    cd = request.getfixturevalue(which)
+    x = np.random.default_rng(5).standard_normal((100_000, cd.d))
+    enc = O.encode(cd, x)
+    u = x / np.linalg.norm(x, axis=1, keepdims=True)
+    chat = cd.c32.astype(np.float64)[enc["idx"]]
+    err = np.sum((u - chat @ cd.R) ** 2, axis=1)
+    D = _distortion_by_quadrature(cd.c32.astype(np.float64), cd.t32.astype(np.float64), cd.d)
+    se = err.std() / math.sqrt(err.size)
+    assert abs(err.mean() - D) < 3.5 * se
+    assert np.allclose(enc["rnorm"] ** 2, err, rtol=2e-6)
+    assert np.allclose(enc["norm"], np.linalg.norm(x, axis=1).astype(np.float32), rtol=0)
+
+
+@pytest.mark.parametrize("which", ["codec3", "codec4"])
+def test_encode_basis_vector_worked_case(which, request):
+    # x = e_k: y_j = D_k H_jk / sqrt(d), so every |y_j| = 1/sqrt(d); every code
+    # sits in the cell holding ±1/sqrt(d) and γ = |1 - sqrt(d) c_level|.
+    cd = request.getfixturevalue(which)
+    d = cd.d
+    k = 17
+    x = np.zeros((1, d)); x[0, k] = 3.0
+    enc = O.encode(cd, x)
+    t = cd.t32.astype(np.float64) * math.sqrt(d)
+    level = int(np.sum(t < 1.0))                 # cell of +1/sqrt(d)
+    H = np.array([(-1) ** bin(j & k).count("1") for j in range(d)])
+    sign = cd.D[k] * H
+    expect_idx = np.where(sign > 0, level, (1 << cd.b) - 1 - level)
+    assert np.array_equal(enc["idx"][0], expect_idx)
+    c_lvl = float(cd.c32[level]) * math.sqrt(d)
+    assert abs(float(enc["rnorm"][0]) - abs(1 - c_lvl)) < 1e-6
+    assert float(enc["norm"][0]) == 3.0
+
+
+def test_encode_zero_vector(codec3):
+    enc = O.encode(codec3, np.zeros((2, 128)))
+    assert np.all(enc["norm"] == 0)
+    # y = 0: idx = #{t < 0} (ties low)
+    assert np.all(enc["idx"] == np.sum(codec3.t32 < 0))
+    q = np.random.default_rng(0).standard_normal((3, 128))
+    assert np.all(O.score(codec3, q, enc) == 0)
+    assert np.all(O.dequantize(codec3, enc) == 0)
+
+
+def test_encode_ties_go_low(codec3):
+    # a coordinate exactly on a boundary takes the lower code
+    cd = codec3
+    y = np.zeros(128); y[0] = float(cd.t32[2]); y[1] = -0.2
+    y /= np.linalg.norm(y)
+    # y[0] is no longer on the boundary after normalisation; check the rule directly
+    t = cd.t32.astype(np.float64)
+    v = np.array([t[2], np.nextafter(np.float32(t[2]), np.float32(1))], dtype=np.float64)
+    idx = np.sum(t[None, :] < v[:, None], axis=1)
+    assert list(idx) == [2, 3]
+
+
+# ---------------------------------------------------------------- QJL estimator
+def test_qjl_estimator_unbiased_and_variance_closed_form():
+    # Fix q', r; draw S fresh (independent rows of one seeded stream); the
+    # estimator sqrt(pi/2)/m ||r|| <S q', sign(S r)> is unbiased with variance
+    # ((pi/2) ||r||² ||q'||² - <q', r>²) / m   (深度拆解 第六部分: unbiased, 1/m).
+    d = m = 32
+    rng = np.random.default_rng(11)
+    qv = rng.standard_normal(d)
+    r = rng.standard_normal(d) * 0.3 + 0.2 * qv
+    gamma = np.linalg.norm(r)
+    n_trials = 100_000
+    kappa = O.qjl_constant(m)
+    ests = []
+    per = 20_000
+    for blk in range(n_trials // per):
+        S = O.gaussian_matrix(per * m, d, seed=777 + blk).astype(np.float64).reshape(per, m, d)
+        p = S @ qv
+        z = S @ r
+        tau = np.where(z >= 0, 1.0, -1.0)
+        ests.append(kappa * gamma * np.sum(p * tau, axis=1))
+    e = np.concatenate(ests)
+    truth = qv @ r
+    var_cf = ((math.pi / 2) * gamma ** 2 * (qv @ qv) - truth ** 2) / m
+    se = math.sqrt(var_cf / e.size)
+    assert abs(e.mean() - truth) < 3 * se
+    # sample variance within a 99.9% chi-square band (normal approx of its SE)
+    assert abs(e.var() / var_cf - 1) < 3.3 * math.sqrt(2 / (e.size - 1)) * 1.5
+
+
+def test_score_end_to_end_unbiased_over_qjl_matrix():
+    # For a fixed rotation, E_S[ℓ] = ν <q', ŷ + r> = <q, x>: the full score is
+    # unbiased over the QJL matrix; a wrong constant or sign in the QJL term
+    # breaks this.
+    d = 32
+    base = O.make_codec(d, 3, seed=5)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, d)) * 2.0
+    q = rng.standard_normal((1, d))
+    vals = []
+    for s in range(4000):
+        cd = O.Codec(d=d, bits=3, m=d, seed=s, D=base.D, R=base.R,
+                     S=O.gaussian_matrix(d, d, seed=10_000 + s),
+                     centroids=base.centroids, bounds=base.bounds, iters=base.iters)
+        vals.append(float(O.score(cd, q, O.encode(cd, x))[0, 0]))
+    vals = np.array(vals)
+    se = vals.std() / math.sqrt(vals.size)
+    assert abs(vals.mean() - float((q @ x.T)[0, 0])) < 3.5 * se
+
+
+def test_inner_product_distortion_lower_bound(codec3):
+    # D_prod >= (||q||²/d) 4^-b for unit keys (深度拆解 第六部分)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((20_000, 128))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    q = rng.standard_normal(128)
+    enc = O.encode(codec3, x)
+    err = (O.score(codec3, q, enc)[0] - x @ q) ** 2
+    assert err.mean() >= (q @ q / 128) * 4.0 ** -codec3.b
+
+
+# ---------------------------------------------------------------- O5 score invariants
+def test_score_invariants(codec3):
+    rng = np.random.default_rng(2)
+    keys = rng.standard_normal((300, 128))
+    enc = O.encode(codec3, keys)
+    q1, q2 = rng.standard_normal((2, 128))
+    s1, s2 = O.score(codec3, q1, enc)[0], O.score(codec3, q2, enc)[0]
+    s12 = O.score(codec3, 2.5 * q1 - 0.5 * q2, enc)[0]
+    assert np.allclose(s12, 2.5 * s1 - 0.5 * s2, rtol=1e-12, atol=1e-12)
+    assert np.all(O.score(codec3, np.zeros(128), enc) == 0)
+    perm = rng.permutation(300)
+    enc_p = {k: enc[k][perm] for k in ("codes", "signs", "norm", "rnorm")}
+    assert np.array_equal(O.score(codec3, q1, enc_p)[0], s1[perm])
+    # scaling the key scales ν only
+    enc2 = O.encode(codec3, 4.0 * keys)
+    assert np.array_equal(enc2["codes"], enc["codes"]) and np.array_equal(enc2["signs"], enc["signs"])
+
+
+def test_score_matches_explicit_sum(codec3):
+    # one key, one query, the estimator written out term by term
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((1, 128)); q = rng.standard_normal(128)
+    enc = O.encode(codec3, x)
+    qr = codec3.R @ q
+    p = codec3.S.astype(np.float64) @ qr
+    idx = enc["idx"][0]
+    tau = 2 * O.unpack_bits(enc["signs"], 128)[0] - 1
+    mse = sum(qr[j] * float(codec3.c32[idx[j]]) for j in range(128))
+    qjl = sum(p[i] * tau[i] for i in range(128))
+    ref = float(enc["norm"][0]) * (mse + math.sqrt(math.pi / 2) / 128 * float(enc["rnorm"][0]) * qjl)
+    assert abs(O.score(codec3, q, enc)[0, 0] - ref) < 1e-11 * abs(ref) + 1e-12
+
+
+def test_attn_logits_gqa_layout(codec3):
+    rng = np.random.default_rng(6)
+    B, Hq, Hk, T, Q = 2, 4, 2, 50, 3
+    keys = rng.standard_normal((B * Hk * T, 128))
+    enc = O.encode(codec3, keys)
+    q = rng.standard_normal((B, Q, Hq, 128))
+    out = O.attn_logits(codec3, q, enc, B, Hq, Hk, Q, T)
+    b, h, qi = 1, 3, 2
+    kh = h // (Hq // Hk)
+    rows = slice((b * Hk + kh) * T, (b * Hk + kh + 1) * T)
+    ref = O.score(codec3, q[b, qi, h], {k: enc[k][rows] for k in ("codes", "signs", "norm", "rnorm")})[0]
+    assert np.allclose(out[b, h, qi], ref, rtol=1e-13, atol=1e-12)
+
+
+# ---------------------------------------------------------------- O6 attention
+def test_decode_attention_two_formulations_agree(codec3):
+    rng = np.random.default_rng(9)
+    B, Hq, Hk, T = 1, 4, 2, 257
+    K = O.encode(codec3, rng.standard_normal((B * Hk * T, 128)))
+    V = O.encode(codec3, rng.standard_normal((B * Hk * T, 128)))
+    q = rng.standard_normal((B, Hq, 128))
+    a = O.decode_attn_materialized(codec3, codec3, q, K, V, B, Hq, Hk, T, 1 / math.sqrt(128))
+    b = O.decode_attn_accumulated(codec3, codec3, q, K, V, B, Hq, Hk, T, 1 / math.sqrt(128))
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+
+
+def test_decode_attention_one_hot_and_uniform(codec3, codec4):
+    rng = np.random.default_rng(10)
+    T = 64
+    keys = rng.standard_normal((T, 128))
+    q = rng.standard_normal((1, 1, 128))
+    K = O.encode(codec3, keys)
+    V = O.encode(codec4, rng.standard_normal((T, 128)))
+    vhat = O.dequantize(codec4, V)
+    # one key with a huge norm dominates the softmax: output = that value
+    lg = O.score(codec3, q[0], K)[0]
+    j = int(np.argmax(lg))
+    K1 = dict(K); K1["norm"] = K["norm"].copy(); K1["norm"][j] *= 1e4
+    out = O.decode_attn_accumulated(codec3, codec4, q, K1, V, 1, 1, 1, T, 1.0)
+    assert np.allclose(out[0, 0], vhat[j], rtol=1e-12, atol=1e-12)
+    # identical keys: uniform weights, output = mean of the values
+    Ku = O.encode(codec3, np.repeat(keys[:1], T, axis=0))
+    out = O.decode_attn_materialized(codec3, codec4, q, Ku, V, 1, 1, 1, T, 1.0)
+    assert np.allclose(out[0, 0], vhat.mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_dequantize_unbiased_over_qjl_matrix():
+    # E_S[v̂] = v for a fixed rotation
+    d = 32
+    base = O.make_codec(d, 3, seed=6)
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((1, d))
+    acc = []
+    for s in range(3000):
+        cd = O.Codec(d=d, bits=3, m=d, seed=s, D=base.D, R=base.R,
+                     S=O.gaussian_matrix(d, d, seed=50_000 + s),
+                     centroids=base.centroids, bounds=base.bounds, iters=base.iters)
+        acc.append(O.dequantize(cd, O.encode(cd, x))[0])
+    acc = np.array(acc)
+    se = acc.std(axis=0) / math.sqrt(acc.shape[0])
+    assert np.all(np.abs(acc.mean(axis=0) - x[0]) < 4 * se)
+
+
+# ---------------------------------------------------------------- O7 search
+def test_search_topk_matches_brute_force_sort(codec3):
+    rng = np.random.default_rng(13)
+    db = O.encode(codec3, rng.standard_normal((500, 128)))
+    # duplicate a record to create exact ties
+    for k in ("codes", "signs", "norm", "rnorm"):
+        db[k][7] = db[k][3]
+    qs = rng.standard_normal((4, 128))
+    idx, sc, full = O.search_topk(codec3, db, qs, 10, chunk=128)
+    for qi in range(4):
+        order = sorted(range(500), key=lambda i: (-full[qi, i], i))[:10]
+        assert list(idx[qi]) == order
+        assert np.array_equal(sc[qi], full[qi, order])
