@@ -1,0 +1,297 @@
+"""Benchmark: compressed keys scored per second on the Llama-3.1-8B-shaped
+decode-logits workload (batch 1, 32 query heads / 8 KV heads, head_dim 128,
+32768-token context, 3-bit keys), one MI355X.
+
+A step is one decode-step scoring pass: prepare the 32 queries (q' = R q,
+p = S q' and the scoring operands), then score them against the resident
+compressed K cache of that step.  Steps rotate over enough distinct
+(cache, query, logits) buffer sets that the 256 MB Infinity Cache cannot hold
+them, so every step streams its compressed keys from HBM.
+
+Prints ONE JSON line (rank 0).  The dominant kernel is the logits kernel; its
+roofline entry divides the algorithmic bytes of one launch (compressed
+records read + prepared queries read + logits written) by the average launch
+duration measured with HIP events on the stream the kernel runs on.
+
+Other stages of the path (encode, 4-bit logits, fused decode attention at
+128K context, search) are timed once each and reported under "stages".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed keys scored/sec + effective HBM GB/s (% of peak), 3-bit, 32K ctx"
+PEAK_HBM_GBS = 8000.0
+INFINITY_CACHE = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--bits", type=int, default=3)
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--stage-search", action="store_true", help="also time the 1M x 1536 search stage")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc"))):
+        if f.startswith("kernels_logits"):
+            h.update(open(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current logits kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "logits_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except Exception:
+        return None
+    if rec.get("kernel_sha") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU mode (the codec is data-oblivious, "
+              "a sharded deployment would run one independent instance per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from kv_cache_quantization_03_amd import binding as B
+    from kv_cache_quantization_03_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bits = args.bits
+    w = I.llama8b_decode(bits=bits)
+    d, hq, hkv, ctx, batch = w["d"], w["n_q_heads"], w["n_kv_heads"], w["ctx"], w["batch"]
+    n_keys = batch * hkv * ctx
+    codec = B.tq_codec_create(d, bits, 0, I.CODEC_SEED)
+
+    t0 = time.time()
+    k_host = w["keys"].rows()
+    q_host = w["queries"].rows().reshape(batch, 1, hq, d)
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    k_dev = torch.from_numpy(k_host).to(dev).to(torch.bfloat16)
+    q_dev = torch.from_numpy(q_host).to(dev).to(torch.bfloat16)
+
+    # ---- encode the cache (timed as a stage)
+    stream = torch.cuda.current_stream()
+    kp = B.alloc_packed(codec, n_keys, dev)
+    enc_ws = torch.empty(B.tq_encode_workspace(codec, n_keys), dtype=torch.uint8, device=dev)
+    B.tq_encode_kv(codec, k_dev, k_out=kp, ws=enc_ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_enc = 5
+    e0.record(stream)
+    for _ in range(n_enc):
+        B.tq_encode_kv(codec, k_dev, k_out=kp, ws=enc_ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1) / n_enc
+
+    # ---- buffer sets: distinct memory for every step of a rotation
+    rec_bytes = n_keys * codec.record_bytes
+    logit_bytes = batch * hq * ctx * 4
+    prep_bytes = B.tq_attn_logits_workspace(codec, batch, hq, hkv, 1)
+    set_bytes = rec_bytes + logit_bytes + prep_bytes
+    n_sets = max(4, math.ceil(2 * INFINITY_CACHE / set_bytes))
+    sets = []
+    for s in range(n_sets):
+        pk = B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone())
+        sets.append({
+            "k": pk,
+            "q": q_dev.clone(),
+            "prep": torch.empty(prep_bytes, dtype=torch.uint8, device=dev),
+            "logits": torch.empty((batch, hq, 1, ctx), dtype=torch.float32, device=dev),
+        })
+    torch.cuda.synchronize()
+
+    def step(s):
+        S = sets[s % n_sets]
+        B.tq_attn_query_prep(codec, S["q"], hkv, prep=S["prep"])
+        B.tq_attn_logits_prepped(codec, S["prep"], (batch, 1, hq), S["k"], ctx, hkv, logits=S["logits"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; logits launches bracketed by events on this stream
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        S = sets[i % n_sets]
+        B.tq_attn_query_prep(codec, S["q"], hkv, prep=S["prep"])
+        ev[i][0].record(stream)
+        B.tq_attn_logits_prepped(codec, S["prep"], (batch, 1, hq), S["k"], ctx, hkv, logits=S["logits"])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    logits_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = wall * 1e3 / K
+    scores_per_step = batch * hq * ctx
+    value = scores_per_step / (ms_per_step * 1e-3)
+
+    alg_bytes = rec_bytes + logit_bytes + prep_bytes
+    achieved = alg_bytes / (logits_ms * 1e-3) / 1e9
+    workload = w["name"]
+    traffic = measured_traffic(workload)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
+                   "ctx_len": ctx, "bits": bits, "key_dtype": "bf16", "buffer_sets": n_sets,
+                   "record_bytes_per_key": codec.record_bytes},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "logits", "kernel_ms": logits_ms, "algorithmic_bytes": alg_bytes,
+                     "keys_per_s_kernel": scores_per_step / (logits_ms * 1e-3),
+                     "k_only_GBs": rec_bytes / (logits_ms * 1e-3) / 1e9},
+        "stages": {"encode_k_ms": enc_ms, "encode_vectors_per_s": n_keys / (enc_ms * 1e-3)},
+    }
+    print(f"[bench] step {ms_per_step * 1e3:.2f} us, logits kernel {logits_ms * 1e3:.2f} us, "
+          f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
+
+    if not args.no_stages:
+        out["stages"].update(time_stages(B, I, codec, dev, args))
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, k_host, q_host, bits)
+    print(json.dumps(out))
+
+
+def _time(fn, n=5):
+    import torch
+    s = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(s)
+    for _ in range(n):
+        fn()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def time_stages(B, I, codec3, dev, args):
+    """One-off timings of the other rows of the path, on synthetic data
+    generated on the GPU (torch, seeded) with the workloads' shapes."""
+    import torch
+    res = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    # 4-bit logits on the same shape
+    c4 = B.tq_codec_create(128, 4, 0, I.CODEC_SEED)
+    k = torch.randn((8 * 32768, 128), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((1, 1, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    kp4, _ = B.tq_encode_kv(c4, k)
+    prep = B.tq_attn_query_prep(c4, q, 8)
+    lg = torch.empty((1, 32, 1, 32768), device=dev)
+    ms = _time(lambda: B.tq_attn_logits_prepped(c4, prep, (1, 1, 32), kp4, 32768, 8, logits=lg), 20)
+    res["logits_4bit_ms"] = ms
+    res["logits_4bit_keys_per_s"] = 32 * 32768 / (ms * 1e-3)
+    print(f"[bench] 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del k, kp4
+    # fused decode attention, 128K context, K and V 3-bit
+    ctx = 131072
+    k = torch.randn((8 * ctx, 128), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((8 * ctx, 128), generator=g, device=dev).to(torch.bfloat16)
+    qd = torch.randn((1, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    kp, vp = B.tq_encode_kv(codec3, k, v)
+    out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.tq_decode_attn_workspace(codec3, codec3, 1, 32, 8, ctx), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_decode_attn(codec3, codec3, qd, kp, vp, ctx, 8, 1 / math.sqrt(128), out=out, ws=ws), 5)
+    res["decode_attn_128k_ms"] = ms
+    res["decode_attn_128k_GBs"] = 2 * 8 * ctx * codec3.record_bytes / (ms * 1e-3) / 1e9
+    print(f"[bench] decode attention 128K {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    # prefill-shaped encode: K and V [16][8][8192][128] bf16
+    n = 16 * 8 * 8192
+    del k, v, kp, vp
+    k = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
+    kp, vp = B.alloc_packed(codec3, n, dev), B.alloc_packed(codec3, n, dev)
+    ws = torch.empty(B.tq_encode_workspace(codec3, n), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_encode_kv(codec3, k, v, k_out=kp, v_out=vp, ws=ws), 3)
+    res["encode_prefill_kv_ms"] = ms
+    res["encode_prefill_vectors_per_s"] = 2 * n / (ms * 1e-3)
+    print(f"[bench] prefill encode {ms:.2f} ms", file=sys.stderr, flush=True)
+    del k, v, kp, vp, ws
+    if args.stage_search:
+        c16 = B.tq_codec_create(1536, 4, 0, I.CODEC_SEED)
+        n_db = 1_000_000
+        db = torch.randn((n_db, 1536), generator=g, device=dev)
+        db /= db.norm(dim=1, keepdim=True)
+        dbp, _ = B.tq_encode_kv(c16, db)
+        qs = torch.randn((1024, 1536), generator=g, device=dev)
+        ms = _time(lambda: B.tq_search_topk(c16, dbp, qs, 10), 1)
+        res["search_1M_x1536_ms"] = ms
+        res["search_scores_per_s"] = 1024 * n_db / (ms * 1e-3)
+    return res
+
+
+def cpu_baseline(w, k_host, q_host, bits):
+    """The fp64 NumPy oracle timed on this host: encode + score of the full
+    decode-logits workload (one step), repeated until about 10 s have run."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
+    except Exception:
+        blas_threads = os.cpu_count()
+    oc = O.make_codec(w["d"], bits, seed=1234)
+    k64 = k_host.astype(np.float64)
+    t = time.perf_counter()
+    rec = O.encode(oc, k64)
+    enc_s = time.perf_counter() - t
+    reps, tot = 0, 0.0
+    while tot < 8.0 and reps < 5:
+        t = time.perf_counter()
+        O.attn_logits(oc, q_host.astype(np.float64), rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1, w["ctx"])
+        tot += time.perf_counter() - t
+        reps += 1
+    score_s = tot / reps
+    n_scores = w["batch"] * w["n_q_heads"] * w["ctx"]
+    return {"value": n_scores / score_s, "unit": "keys/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"full workload ({n_scores} scores) x{reps}; encode of {k_host.shape[0]} keys took "
+                      f"{enc_s:.2f}s ({k_host.shape[0] / enc_s:.0f} vectors/s)",
+            "os_cpu_count": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+/*
+ * tq.h — TurboQuant KV-cache and vector codec for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only.  Every compute call is asynchronous on
+ * the caller's HIP stream.  Every device pointer is owned by the caller: the
+ * library never allocates or frees it.  tq_codec_create is the one synchronous
+ * call: it builds the codec tables on the host and uploads them.
+ *
+ * Method (pages cited by title and section):
+ *   「谷歌 TurboQuant 深度拆解：LLM 内存压缩 6 倍、推理加速 8 倍、零精度损失，
+ *    它是怎么做到的？」 第二部分, the two-stage method:
+ *     (1) a random rotation, after which each coordinate follows a known law,
+ *         so an optimal scalar (Lloyd-Max) quantizer needs no per-block scale
+ *         or zero-point;
+ *     (2) QJL: the residual is projected with a Gaussian JL matrix and only
+ *         one sign bit is kept per projected coordinate; a full-precision
+ *         query scores the compressed key with an unbiased estimator.
+ *   Same page, 第六部分: the coordinate density
+ *     f(x) = Γ(d/2)/(√π Γ((d-1)/2)) (1-x²)^((d-3)/2), and the estimator is
+ *     unbiased with variance falling as 1/m.
+ *   「TurboQuant+ 深度解析：当前 Google 工程师决定单挑大厂」 第二部分: the
+ *     rotation is a random-sign Walsh–Hadamard transform.
+ *   「TurboQuant 学习路径：论文 → 技术 → 数学」 二.2: FJLT y = P·H·D·x and
+ *     Gaussian JL; 三.1: Hadamard recursion H_n = H_1 ⊗ H_{n-1}.
+ *
+ * Codec parameters: head_dim d, total bits B (2, 3 or 4) = b Lloyd-Max bits
+ * (b = B-1) + 1 QJL bit per projected coordinate, QJL dimension m = d, seed.
+ *   R = H diag(D)/√d.  H is Sylvester natural order for d = 2^k; for d = 1536
+ *     it is H12 ⊗ H128, with H12 the Paley type-I matrix.  D = ±1 from
+ *     SplitMix64(seed ^ 1).
+ *   S = m x d i.i.d. N(0,1): SplitMix64(seed ^ 2) fed to Box–Muller, then
+ *     rounded to fp32.
+ *   c, t = the Lloyd-Max centroids and boundaries of f (fp64 fit, fp32 on the
+ *     device).
+ *
+ * Encode, per vector x:
+ *   ν = ||x||, y = R x/ν, idx_j = #{k : t_k < y_j}, r = y - c[idx], γ = ||r||,
+ *   sign bit i = [(S r)_i >= 0].
+ * Score against a query q:
+ *   q' = R q, p = S q',
+ *   ℓ = ν (Σ_j q'_j c[idx_j] + √(π/2)/m · γ · Σ_i p_i (2 bit_i - 1)).
+ *
+ * Packed record layout (tq_packed_t).  Each array has one row per vector, in
+ * the caller's row order (for a KV cache: [batch][kv_head][token]):
+ *   codes[n][b*d/32] u32  bit-planes.  Word p*(d/32) + j/32, bit j%32 holds
+ *                         bit p of idx_j.
+ *   signs[n][m/32]   u32  word i/32, bit i%32 holds sign bit i.
+ *   norm[n]  f32          ν = ||x||.
+ *   rnorm[n] f32          γ = ||r|| of the unit-vector residual.
+ * Bytes per vector: d·B/8 + 8 (3-bit, d=128: 48 + 8 = 56 B, vs 256 B of fp16).
+ *
+ * Errors.  Every call returns a tq_status_t and never throws.  Arguments are
+ * validated on the host before any launch, so an invalid call has no side
+ * effect.  tq_last_error() returns a thread-local message for the last failing
+ * call on this thread.  Launch failures map to TQ_ERROR_HIP.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+typedef struct tq_codec_s* tq_codec_t; /* opaque; immutable after create, usable from any stream */
+
+typedef enum {
+  TQ_SUCCESS = 0,
+  TQ_ERROR_INVALID_VALUE = 1,        /* NULL handle/pointer, negative size, bad enum, bad shape */
+  TQ_ERROR_NOT_SUPPORTED = 2,        /* a valid request this build does not implement */
+  TQ_ERROR_MISALIGNED = 3,           /* a pointer breaks the alignment stated below */
+  TQ_ERROR_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes < the matching *_workspace() size */
+  TQ_ERROR_OUT_OF_MEMORY = 5,        /* host or device allocation inside tq_codec_create failed */
+  TQ_ERROR_HIP = 6                   /* a HIP runtime call or kernel launch failed */
+} tq_status_t;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype_t;
+
+/* Device pointers to one packed cache or database; all arrays have n rows. */
+typedef struct {
+  uint32_t* codes; /* [n][code_words], 4-byte aligned */
+  uint32_t* signs; /* [n][sign_words], 4-byte aligned */
+  float* norm;     /* [n] */
+  float* rnorm;    /* [n] */
+} tq_packed_t;
+
+typedef struct {
+  int32_t head_dim;     /* d */
+  int32_t bits;         /* B = b + 1 */
+  int32_t mse_bits;     /* b */
+  int32_t qjl_dim;      /* m */
+  int32_t code_words;   /* b*d/32 */
+  int32_t sign_words;   /* m/32 */
+  int32_t record_bytes; /* 4*(code_words+sign_words) + 8 */
+  int32_t lloyd_max_iterations;
+  uint64_t seed;
+  double centroids[16]; /* 2^b entries, ascending, fp64 */
+  double bounds[15];    /* 2^b - 1 entries, midpoints of the centroids */
+} tq_codec_info_t;
+
+/* ---------------------------------------------------------------- status */
+const char* tq_status_string(tq_status_t s);
+/* Thread-local message for the last failing call on this thread ("" if none). */
+const char* tq_last_error(void);
+int32_t tq_abi_version(void);
+
+/* ---------------------------------------------------------------- codec
+ * Supported: head_dim in {64, 128, 256, 512, 1024, 1536}; bits in {2, 3, 4};
+ * qjl_dim 0 (meaning d) or d.  Other values -> TQ_ERROR_NOT_SUPPORTED.
+ * The tables depend only on (head_dim, bits, qjl_dim, seed): the codec is
+ * data-oblivious (深度拆解 第二部分: no training, tuning or calibration).
+ */
+
+/* Host only, no GPU needed: writes the codec tables into caller-owned host
+ * buffers.  Any output pointer may be NULL.
+ * D_out[d] (±1), S_out[m*d] (row-major fp32), centroids[2^b], bounds[2^b-1],
+ * iterations = number of Lloyd-Max iterations. */
+tq_status_t tq_codec_build_host(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
+                                float* D_out, float* S_out, double* centroids, double* bounds,
+                                int32_t* iterations);
+
+/* Builds the tables on the host and uploads them to the current HIP device
+ * (synchronous).  *out receives the handle.  The handle stays bound to that
+ * device. */
+tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
+                            tq_codec_t* out);
+/* The caller guarantees that no work using c is still in flight. */
+tq_status_t tq_codec_destroy(tq_codec_t c);
+tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info);
+
+/* ---------------------------------------------------------------- encode
+ * Compresses n_vec rows of k (and of v if v != NULL) with codec c.
+ *   k, v : device [n_vec][d] in dtype dt (element-aligned).
+ *   k_out, v_out : device packed arrays with n_vec rows.  To append to an
+ *          existing cache, offset each pointer by the first row to write.
+ *   ws   : device workspace of at least tq_encode_workspace(c, n_vec) bytes,
+ *          16-byte aligned (may be NULL when that size is 0).
+ * n_vec = 0 is a valid no-op.  To give K and V different codecs (for example
+ * 4-bit K and 3-bit V), call once per codec with v = NULL.
+ */
+size_t tq_encode_workspace(tq_codec_t c, int64_t n_vec);
+tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, tq_dtype_t dt, int64_t n_vec,
+                         tq_packed_t k_out, tq_packed_t v_out, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ---------------------------------------------------------------- logits
+ * Unbiased attention logits of every query against every compressed key
+ * (深度拆解 第二部分: full-precision query against the compressed key;
+ * 第三部分 推理速度: attention logits are bound by memory bandwidth).
+ *   q      : device [batch][n_queries][n_q_heads][d], dtype q_dt.
+ *   k      : packed rows [batch][n_kv_heads][ctx_len].
+ *   logits : device fp32 [batch][n_q_heads][n_queries][ctx_len].  These are
+ *            raw <q,k> estimates: no 1/sqrt(d) scaling is applied.
+ * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
+ * must be a multiple of n_kv_heads.  ctx_len = 0 is a valid no-op.
+ * Workspace: tq_attn_logits_workspace(...) bytes, 16-byte aligned.
+ */
+size_t tq_attn_logits_workspace(tq_codec_t c, int32_t batch, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t n_queries);
+tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch,
+                           int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
+                           tq_packed_t k, int64_t ctx_len, float* logits, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* Split form of tq_attn_logits for callers that score one set of queries
+ * against several caches, or that time the two stages apart.
+ * tq_attn_query_prep writes the prepared queries (q' = R q, p = S q' and
+ * their scoring operands) into `prep`, a device buffer of at least
+ * tq_attn_logits_workspace(...) bytes, 16-byte aligned.
+ * tq_attn_logits_prepped reads `prep` and writes the logits exactly as
+ * tq_attn_logits does.  Both calls must use the same shape arguments. */
+tq_status_t tq_attn_query_prep(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch,
+                               int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries, void* prep,
+                               size_t prep_bytes, void* stream);
+tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, size_t prep_bytes, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
+                                   tq_packed_t k, int64_t ctx_len, float* logits, void* stream);
+
+/* ---------------------------------------------------------------- decode attention
+ * One decode step of attention over a compressed K/V cache:
+ *   out[b][h] = Σ_t softmax_t(softmax_scale · ℓ_t) · v̂_t
+ * where v̂ = ν Rᵀ (c[idx] + √(π/2)/m · γ · Sᵀ τ) is the value's unbiased
+ * reconstruction.  K and V use the same codec layout
+ * (TurboQuant+ 深度解析 第五部分: K and V are compressed the same way).  V is
+ * accumulated in the codec domain and mapped back once per head.
+ *   ck, cv : codecs of K and V (they may be the same handle; their bits may
+ *            differ; head_dim must match).
+ *   q      : device [batch][n_q_heads][d], dtype q_dt.
+ *   k, v   : packed rows [batch][n_kv_heads][ctx_len].
+ *   out    : device [batch][n_q_heads][d], dtype out_dt (TQ_F32 or TQ_BF16,
+ *            the latter rounded to nearest even).
+ *   ctx_len >= 1.  Workspace: tq_decode_attn_workspace(...) bytes.
+ */
+size_t tq_decode_attn_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch, int32_t n_q_heads,
+                                int32_t n_kv_heads, int64_t ctx_len);
+tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                           int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k,
+                           tq_packed_t v, int64_t ctx_len, float softmax_scale, void* out,
+                           tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- search
+ * Exhaustive inner-product search over a compressed database
+ * (深度拆解 第三部分 向量搜索: the compressed vectors are the index; nothing
+ * is trained).  Scores use the same estimator as tq_attn_logits.
+ *   db        : packed rows [n_db].
+ *   queries   : device fp32 [n_queries][d].
+ *   out_idx   : device int64 [n_queries][topk], best first.  Ties go to the
+ *               lower index.
+ *   out_score : device fp32 [n_queries][topk].
+ * 1 <= topk <= min(n_db, 1024).  Workspace: tq_search_workspace(...) bytes.
+ */
+size_t tq_search_workspace(tq_codec_t c, int64_t n_db, int32_t n_queries, int32_t topk);
+tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db, const float* queries,
+                           int32_t n_queries, int32_t topk, int64_t* out_idx, float* out_score,
+                           void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

@@ -1,0 +1,126 @@
+// Attention logits over a compressed K cache: the unbiased estimator
+//   ℓ = ν (Σ_j q'_j c[idx_j] + √(π/2)/m · γ · Σ_i p_i τ_i),
+// q' = R q and p = S q' prepared once per query (「谷歌 TurboQuant 深度拆解」
+// 第二部分: a full-precision query against the compressed key, unbiased).
+//
+// This file holds the general VALU kernel (one thread per key, any head_dim,
+// any number of query vectors per KV head).  It is the reference kernel on the
+// GPU and covers shapes the MFMA kernel does not.
+#include "kernels_common.h"
+
+namespace tq {
+
+constexpr int kLogitsQC = 8;  // query vectors per block (grid.z splits the rest)
+
+// Prepped query rows: qrot[row][d], proj[row][m] with row = (b*nq + qi)*Hq + h.
+__global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const float* __restrict__ qrot,
+                                                          const float* __restrict__ proj, int Hq, int nq,
+                                                          int G, int nkv, int64_t ctx, tq_packed_t k,
+                                                          float* __restrict__ logits) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int bk = blockIdx.y;
+  const int b = bk / nkv, kh = bk % nkv;
+  const int nqv = nq * G;
+  const int qv0 = blockIdx.z * kLogitsQC;
+  const bool valid = t < ctx;
+  const int64_t row = static_cast<int64_t>(bk) * ctx + (valid ? t : 0);
+  const int d = P.d, m = P.m, W = d / 32, CW = P.code_words, SW = P.sign_words;
+  const int L = 1 << P.b;
+
+  int64_t qrow[kLogitsQC];
+  int hq[kLogitsQC], qiq[kLogitsQC];
+  bool qok[kLogitsQC];
+#pragma unroll
+  for (int c = 0; c < kLogitsQC; ++c) {
+    const int qv = qv0 + c;
+    qok[c] = qv < nqv;
+    const int qi = qok[c] ? qv / G : 0, g = qok[c] ? qv % G : 0;
+    hq[c] = kh * G + g;
+    qiq[c] = qi;
+    qrow[c] = (static_cast<int64_t>(b) * nq + qi) * Hq + hq[c];
+  }
+  float cent[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cent[i] = P.cent[i];
+
+  float mse[kLogitsQC] = {}, qjl[kLogitsQC] = {};
+  const uint32_t* crow = k.codes + row * CW;
+  for (int w = 0; w < W; ++w) {
+    uint32_t pw[3] = {0, 0, 0};
+    for (int p = 0; p < P.b; ++p) pw[p] = crow[p * W + w];
+    for (int bit = 0; bit < 32; ++bit) {
+      int idx = 0;
+#pragma unroll
+      for (int p = 0; p < 3; ++p) idx |= ((pw[p] >> bit) & 1u) << p;
+      float cv = cent[0];
+#pragma unroll
+      for (int l = 1; l < 8; ++l) cv = (idx == l && l < L) ? cent[l] : cv;
+      const int j = w * 32 + bit;
+#pragma unroll
+      for (int c = 0; c < kLogitsQC; ++c) mse[c] = fmaf(qrot[(qok[c] ? qrow[c] : 0) * d + j], cv, mse[c]);
+    }
+  }
+  const uint32_t* srow = k.signs + row * SW;
+  for (int w = 0; w < m / 32; ++w) {
+    const uint32_t sw = srow[w];
+    for (int bit = 0; bit < 32; ++bit) {
+      const float tau = ((sw >> bit) & 1u) ? 1.f : -1.f;
+      const int i = w * 32 + bit;
+#pragma unroll
+      for (int c = 0; c < kLogitsQC; ++c) qjl[c] = fmaf(proj[(qok[c] ? qrow[c] : 0) * m + i], tau, qjl[c]);
+    }
+  }
+  if (!valid) return;
+  const float nu = k.norm[row], ga = k.rnorm[row];
+#pragma unroll
+  for (int c = 0; c < kLogitsQC; ++c) {
+    if (!qok[c]) continue;
+    const int64_t o = ((static_cast<int64_t>(b) * Hq + hq[c]) * nq + qiq[c]) * ctx + t;
+    logits[o] = nu * (mse[c] + P.qjl_kappa * ga * qjl[c]);
+  }
+}
+
+size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int /*n_kv_heads*/, int n_queries) {
+  const size_t nv = static_cast<size_t>(batch) * n_queries * n_q_heads;
+  return nv * (c->prm.d + c->prm.m) * sizeof(float);
+}
+
+hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                              int /*n_kv_heads*/, int n_queries, void* ws, hipStream_t s) {
+  const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
+  float* qrot = static_cast<float*>(ws);
+  float* proj = qrot + nv * c->prm.d;
+  return launch_qprep(c, q, dt, nv, qrot, proj, s);
+}
+
+hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                         int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits, void* ws,
+                         hipStream_t s) {
+  hipError_t e = launch_logits_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_logits_prepped(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
+}
+
+hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                                 int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+  const DevParams& P = c->prm;
+  const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
+  const float* qrot = static_cast<const float*>(ws);
+  const float* proj = qrot + nv * P.d;
+  const int G = n_q_heads / n_kv_heads;
+  dim3 grid(static_cast<unsigned>(ceil_div(ctx, 256)), batch * n_kv_heads,
+            static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_queries) * G, kLogitsQC)));
+  hipLaunchKernelGGL(logits_valu_kernel, grid, dim3(256), 0, s, P, qrot, proj, n_q_heads, n_queries, G,
+                     n_kv_heads, ctx, k, logits);
+  return hipGetLastError();
+}
+
+// Scores of nq prepped query vectors against n packed rows: scores[q][t].
+hipError_t launch_scores(const tq_codec_s* c, const float* qrot, const float* proj, int nq, tq_packed_t db,
+                         int64_t n, float* scores, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(ceil_div(n, 256)), 1, static_cast<unsigned>(ceil_div(nq, kLogitsQC)));
+  hipLaunchKernelGGL(logits_valu_kernel, grid, dim3(256), 0, s, c->prm, qrot, proj, nq, 1, nq, 1, n, db, scores);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,202 @@
+// Exhaustive search over a compressed database: estimator scores per DB chunk,
+// exact top-k per (query, chunk) by radix select on the score bits, then the
+// same selection over the per-chunk candidates.
+//
+// Pages: 「谷歌 TurboQuant 深度拆解」 第三部分 向量搜索 (the compressed vectors
+// are the index; nothing is trained) and 第二部分 (unbiased inner-product
+// estimate from a full-precision query).
+#include "kernels_common.h"
+
+namespace tq {
+
+hipError_t launch_scores(const tq_codec_s* c, const float* qrot, const float* proj, int nq, tq_packed_t db,
+                         int64_t n, float* scores, hipStream_t s);
+
+namespace {
+constexpr int64_t kSearchChunk = 65536;
+constexpr int kSelThreads = 256;
+
+// Sort key: ascending order of the key = descending order of the score.
+__device__ __forceinline__ uint32_t desc_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+__device__ __forceinline__ float key_to_score(uint32_t k) {
+  const uint32_t asc = ~k;
+  const uint32_t u = (asc & 0x80000000u) ? (asc & 0x7FFFFFFFu) : ~asc;
+  return __uint_as_float(u);
+}
+}  // namespace
+
+// One block per row.  Row r: scores src[r*src_stride + pos], pos < len_r;
+// global index = idx_in ? idx_in[r*src_stride + pos] : idx_base + pos.
+// Writes the k best (score desc, index asc) to out_score/out_idx[r*k ...].
+// When len_r < k the tail is filled with (-inf, INT64_MAX).
+__global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(const float* __restrict__ src,
+                                                                const int64_t* __restrict__ idx_in,
+                                                                int64_t src_stride, int64_t len, int64_t idx_base,
+                                                                int k, float* __restrict__ out_score,
+                                                                int64_t* __restrict__ out_idx, int64_t out_stride) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sel_key[1024];
+  __shared__ int64_t sel_idx[1024];
+  __shared__ uint32_t sh_prefix, sh_need, sh_cnt_lt;
+  __shared__ uint32_t scan[kSelThreads];
+  const int r = blockIdx.x;
+  const float* row = src + static_cast<int64_t>(r) * src_stride;
+  const int64_t* irow = idx_in ? idx_in + static_cast<int64_t>(r) * src_stride : nullptr;
+  const int tid = threadIdx.x;
+  const int kk = static_cast<int>(min<int64_t>(k, len));
+  auto gidx = [&](int64_t pos) -> int64_t { return irow ? irow[pos] : idx_base + pos; };
+
+  uint32_t prefix = 0, mask = 0, need = kk;
+  for (int pass = 0; pass < 4 && kk > 0; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    for (int64_t pos = tid; pos < len; pos += kSelThreads) {
+      const uint32_t key = desc_key(row[pos]);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t cum = 0, sel = 255;
+      for (int bsel = 0; bsel < 256; ++bsel) {
+        if (cum + hist[bsel] >= need) { sel = bsel; break; }
+        cum += hist[bsel];
+      }
+      sh_prefix = prefix | (sel << shift);
+      sh_need = need - cum;
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    need = sh_need;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;           // key of the kk-th best
+  const uint32_t n_lt = kk - need;     // strictly better than T
+  if (tid == 0) sh_cnt_lt = 0;
+  __syncthreads();
+  for (int64_t pos = tid; pos < len && kk > 0; pos += kSelThreads) {
+    const uint32_t key = desc_key(row[pos]);
+    if (key < T) {
+      const uint32_t slot = atomicAdd(&sh_cnt_lt, 1u);
+      sel_key[slot] = key;
+      sel_idx[slot] = gidx(pos);
+    }
+  }
+  // equal to T: the first `need` of them in position order (position order is
+  // index order for both call sites)
+  uint32_t taken = 0;
+  for (int64_t base = 0; base < len && taken < need; base += kSelThreads) {
+    const int64_t pos = base + tid;
+    const uint32_t f = (pos < len && desc_key(row[pos]) == T) ? 1u : 0u;
+    scan[tid] = f;
+    __syncthreads();
+    for (int off = 1; off < kSelThreads; off <<= 1) {
+      const uint32_t v = tid >= off ? scan[tid - off] : 0u;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const uint32_t incl = scan[tid];
+    const uint32_t total = scan[kSelThreads - 1];
+    if (f && taken + incl - 1 < need) {
+      const uint32_t slot = n_lt + taken + incl - 1;
+      sel_key[slot] = T;
+      sel_idx[slot] = gidx(pos);
+    }
+    taken += total;
+    __syncthreads();
+  }
+  // pad and bitonic-sort by (key, idx)
+  int P2 = 1;
+  while (P2 < k) P2 <<= 1;
+  for (int i = tid; i < P2; i += kSelThreads)
+    if (i >= kk) {
+      sel_key[i] = 0xFFFFFFFFu;
+      sel_idx[i] = INT64_MAX;
+    }
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P2; i += kSelThreads) {
+        const int jx = i ^ stride;
+        if (jx > i) {
+          const bool up = (i & size) == 0;
+          const uint32_t ka = sel_key[i], kb = sel_key[jx];
+          const int64_t ia = sel_idx[i], ib = sel_idx[jx];
+          const bool a_gt_b = (ka > kb) || (ka == kb && ia > ib);
+          if (a_gt_b == up) {
+            sel_key[i] = kb; sel_key[jx] = ka;
+            sel_idx[i] = ib; sel_idx[jx] = ia;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += kSelThreads) {
+    const int64_t o = static_cast<int64_t>(r) * out_stride + i;
+    const bool real = i < kk;
+    out_score[o] = real ? key_to_score(sel_key[i]) : -INFINITY;
+    out_idx[o] = real ? sel_idx[i] : INT64_MAX;
+  }
+}
+
+namespace {
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+struct SearchLayout {
+  size_t qrot, proj, scores, cand_idx, cand_score, total;
+};
+SearchLayout search_layout(const tq_codec_s* c, int64_t n_db, int nq, int topk) {
+  const int64_t chunk = std::min<int64_t>(kSearchChunk, n_db);
+  const int64_t n_chunks = ceil_div(n_db, chunk);
+  SearchLayout L{};
+  L.qrot = 0;
+  L.proj = align256(L.qrot + static_cast<size_t>(nq) * c->prm.d * sizeof(float));
+  L.scores = align256(L.proj + static_cast<size_t>(nq) * c->prm.m * sizeof(float));
+  L.cand_idx = align256(L.scores + static_cast<size_t>(nq) * chunk * sizeof(float));
+  L.cand_score = align256(L.cand_idx + static_cast<size_t>(nq) * n_chunks * topk * sizeof(int64_t));
+  L.total = align256(L.cand_score + static_cast<size_t>(nq) * n_chunks * topk * sizeof(float));
+  return L;
+}
+}  // namespace
+
+size_t search_ws_bytes(const tq_codec_s* c, int64_t n_db, int n_queries, int topk) {
+  return search_layout(c, n_db, n_queries, topk).total;
+}
+
+hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, const float* queries, int nq, int topk,
+                         int64_t* out_idx, float* out_score, void* ws, hipStream_t s) {
+  const DevParams& P = c->prm;
+  const int64_t chunk = std::min<int64_t>(kSearchChunk, n_db);
+  const int64_t n_chunks = ceil_div(n_db, chunk);
+  char* w = static_cast<char*>(ws);
+  const SearchLayout SL = search_layout(c, n_db, nq, topk);
+  float* qrot = reinterpret_cast<float*>(w + SL.qrot);
+  float* proj = reinterpret_cast<float*>(w + SL.proj);
+  float* scores = reinterpret_cast<float*>(w + SL.scores);
+  int64_t* cand_idx = reinterpret_cast<int64_t*>(w + SL.cand_idx);
+  float* cand_score = reinterpret_cast<float*>(w + SL.cand_score);
+  hipError_t e = launch_qprep(c, queries, TQ_F32, nq, qrot, proj, s);
+  if (e != hipSuccess) return e;
+  for (int64_t ci = 0; ci < n_chunks; ++ci) {
+    const int64_t lo = ci * chunk;
+    const int64_t len = std::min<int64_t>(chunk, n_db - lo);
+    tq_packed_t sub{db.codes + lo * P.code_words, db.signs + lo * P.sign_words, db.norm + lo, db.rnorm + lo};
+    if ((e = launch_scores(c, qrot, proj, nq, sub, len, scores, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(nq), dim3(kSelThreads), 0, s, scores, static_cast<const int64_t*>(nullptr),
+                       len, len, lo, topk, cand_score + ci * topk, cand_idx + ci * topk,
+                       static_cast<int64_t>(n_chunks * topk));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(nq), dim3(kSelThreads), 0, s, cand_score, cand_idx,
+                     static_cast<int64_t>(n_chunks * topk), static_cast<int64_t>(n_chunks * topk),
+                     static_cast<int64_t>(0), topk, out_score, out_idx, static_cast<int64_t>(topk));
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,249 @@
+// C-ABI layer: argument validation, workspace sizing, error strings, and the
+// dispatch to the kernel launchers.  Validation happens before any HIP call, so
+// an invalid request has no side effect.
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace tq
+
+using tq::set_error;
+
+extern "C" const char* tq_status_string(tq_status_t s) {
+  switch (s) {
+    case TQ_SUCCESS: return "TQ_SUCCESS";
+    case TQ_ERROR_INVALID_VALUE: return "TQ_ERROR_INVALID_VALUE";
+    case TQ_ERROR_NOT_SUPPORTED: return "TQ_ERROR_NOT_SUPPORTED";
+    case TQ_ERROR_MISALIGNED: return "TQ_ERROR_MISALIGNED";
+    case TQ_ERROR_WORKSPACE_TOO_SMALL: return "TQ_ERROR_WORKSPACE_TOO_SMALL";
+    case TQ_ERROR_OUT_OF_MEMORY: return "TQ_ERROR_OUT_OF_MEMORY";
+    case TQ_ERROR_HIP: return "TQ_ERROR_HIP";
+  }
+  return "TQ_ERROR_UNKNOWN";
+}
+
+extern "C" const char* tq_last_error(void) { return tq::g_last_error.c_str(); }
+extern "C" int32_t tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dtype_size(tq_dtype_t dt) { return dt == TQ_F32 ? 4 : 2; }
+
+bool valid_dtype(tq_dtype_t dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+
+tq_status_t check_packed(const tq_packed_t& p, const char* name) {
+  if (!p.codes || !p.signs || !p.norm || !p.rnorm) {
+    set_error(std::string(name) + ": a packed array pointer is NULL");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (!aligned(p.codes, 4) || !aligned(p.signs, 4) || !aligned(p.norm, 4) || !aligned(p.rnorm, 4)) {
+    set_error(std::string(name) + ": packed arrays must be 4-byte aligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  return TQ_SUCCESS;
+}
+
+tq_status_t check_ws(void* ws, size_t have, size_t need) {
+  if (have < need) {
+    set_error("workspace too small: need " + std::to_string(need) + " bytes, got " + std::to_string(have));
+    return TQ_ERROR_WORKSPACE_TOO_SMALL;
+  }
+  if (need > 0 && (!ws || !aligned(ws, 16))) {
+    set_error("workspace must be non-NULL and 16-byte aligned");
+    return ws ? TQ_ERROR_MISALIGNED : TQ_ERROR_INVALID_VALUE;
+  }
+  return TQ_SUCCESS;
+}
+
+tq_status_t finish(hipError_t e, const char* what) {
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error(std::string(what) + ": " + hipGetErrorString(e));
+    return TQ_ERROR_HIP;
+  }
+  return TQ_SUCCESS;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("TQ_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+tq_status_t check_heads(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads) {
+  if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) {
+    set_error("need batch >= 0, n_q_heads > 0, n_kv_heads > 0 and n_q_heads % n_kv_heads == 0");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  return TQ_SUCCESS;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- encode
+extern "C" size_t tq_encode_workspace(tq_codec_t c, int64_t n_vec) {
+  if (!c || n_vec < 0) return 0;
+  return tq::encode_ws_bytes(c, n_vec);
+}
+
+extern "C" tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, tq_dtype_t dt,
+                                    int64_t n_vec, tq_packed_t k_out, tq_packed_t v_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(dt)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
+  if (n_vec < 0) { set_error("n_vec < 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (n_vec == 0) return TQ_SUCCESS;
+  if (!k) { set_error("k is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(k, dtype_size(dt)) || (v && !aligned(v, dtype_size(dt)))) {
+    set_error("k/v must be aligned to their element size");
+    return TQ_ERROR_MISALIGNED;
+  }
+  tq_status_t st = check_packed(k_out, "k_out");
+  if (st != TQ_SUCCESS) return st;
+  if (v && (st = check_packed(v_out, "v_out")) != TQ_SUCCESS) return st;
+  if ((st = check_ws(ws, ws_bytes, tq::encode_ws_bytes(c, n_vec))) != TQ_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (log_enabled()) std::fprintf(stderr, "[tq] encode n=%lld d=%d bits=%d v=%d\n", (long long)n_vec, c->prm.d, c->host.bits, v != nullptr);
+  hipError_t e = tq::launch_encode(c, k, dt, n_vec, k_out, static_cast<float*>(ws), s);
+  if (e == hipSuccess && v) e = tq::launch_encode(c, v, dt, n_vec, v_out, static_cast<float*>(ws), s);
+  return finish(e, "tq_encode_kv launch");
+}
+
+// ---------------------------------------------------------------- logits
+extern "C" size_t tq_attn_logits_workspace(tq_codec_t c, int32_t batch, int32_t n_q_heads,
+                                           int32_t n_kv_heads, int32_t n_queries) {
+  if (!c || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_queries < 0) return 0;
+  return tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
+}
+
+extern "C" tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
+                                      tq_packed_t k, int64_t ctx_len, float* logits, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
+  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  if (st != TQ_SUCCESS) return st;
+  if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
+  if (!q || !logits) { set_error("q or logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(q, dtype_size(q_dt)) || !aligned(logits, 4)) { set_error("q/logits misaligned"); return TQ_ERROR_MISALIGNED; }
+  if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
+  if ((st = check_ws(ws, ws_bytes, tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) != TQ_SUCCESS) return st;
+  if (log_enabled()) std::fprintf(stderr, "[tq] logits b=%d hq=%d hkv=%d nq=%d ctx=%lld\n", batch, n_q_heads, n_kv_heads, n_queries, (long long)ctx_len);
+  hipError_t e = tq::launch_logits(c, q, q_dt, batch, n_q_heads, n_kv_heads, n_queries, k, ctx_len,
+                                   logits, ws, static_cast<hipStream_t>(stream));
+  return finish(e, "tq_attn_logits launch");
+}
+
+extern "C" tq_status_t tq_attn_query_prep(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch,
+                                          int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries, void* prep,
+                                          size_t prep_bytes, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
+  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  if (st != TQ_SUCCESS) return st;
+  if (n_queries < 0) { set_error("n_queries must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (batch == 0 || n_queries == 0) return TQ_SUCCESS;
+  if (!q) { set_error("q is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(q, dtype_size(q_dt))) { set_error("q misaligned"); return TQ_ERROR_MISALIGNED; }
+  if ((st = check_ws(prep, prep_bytes, tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) != TQ_SUCCESS) return st;
+  hipError_t e = tq::launch_logits_prep(c, q, q_dt, batch, n_q_heads, n_kv_heads, n_queries, prep,
+                                        static_cast<hipStream_t>(stream));
+  return finish(e, "tq_attn_query_prep launch");
+}
+
+extern "C" tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, size_t prep_bytes, int32_t batch,
+                                              int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
+                                              tq_packed_t k, int64_t ctx_len, float* logits, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  if (st != TQ_SUCCESS) return st;
+  if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
+  if (!logits) { set_error("logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(logits, 4)) { set_error("logits misaligned"); return TQ_ERROR_MISALIGNED; }
+  if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
+  if ((st = check_ws(const_cast<void*>(prep), prep_bytes, tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) != TQ_SUCCESS) return st;
+  hipError_t e = tq::launch_logits_prepped(c, prep, batch, n_q_heads, n_kv_heads, n_queries, k, ctx_len, logits,
+                                           static_cast<hipStream_t>(stream));
+  return finish(e, "tq_attn_logits_prepped launch");
+}
+
+// ---------------------------------------------------------------- decode attention
+extern "C" size_t tq_decode_attn_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch,
+                                           int32_t n_q_heads, int32_t n_kv_heads, int64_t ctx_len) {
+  if (!ck || !cv || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || ctx_len < 0) return 0;
+  return tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len);
+}
+
+extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      tq_packed_t k, tq_packed_t v, int64_t ctx_len,
+                                      float softmax_scale, void* out, tq_dtype_t out_dt, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
+  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  if (st != TQ_SUCCESS) return st;
+  if (ctx_len < 1) { set_error("ctx_len must be >= 1"); return TQ_ERROR_INVALID_VALUE; }
+  if (!(softmax_scale == softmax_scale)) { set_error("softmax_scale is NaN"); return TQ_ERROR_INVALID_VALUE; }
+  const char* why = nullptr;
+  if (!tq::decode_supported(cv, n_q_heads, n_kv_heads, ctx_len, &why)) { set_error(why); return TQ_ERROR_NOT_SUPPORTED; }
+  if (batch == 0) return TQ_SUCCESS;
+  if (!q || !out) { set_error("q or out is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(q, dtype_size(q_dt)) || !aligned(out, dtype_size(out_dt))) { set_error("q/out misaligned"); return TQ_ERROR_MISALIGNED; }
+  if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
+  if ((st = check_packed(v, "v")) != TQ_SUCCESS) return st;
+  if ((st = check_ws(ws, ws_bytes, tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len))) != TQ_SUCCESS) return st;
+  if (log_enabled()) std::fprintf(stderr, "[tq] decode b=%d hq=%d hkv=%d ctx=%lld\n", batch, n_q_heads, n_kv_heads, (long long)ctx_len);
+  hipError_t e = tq::launch_decode(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len,
+                                   softmax_scale, out, out_dt, ws, static_cast<hipStream_t>(stream));
+  return finish(e, "tq_decode_attn launch");
+}
+
+// ---------------------------------------------------------------- search
+extern "C" size_t tq_search_workspace(tq_codec_t c, int64_t n_db, int32_t n_queries, int32_t topk) {
+  if (!c || n_db < 0 || n_queries < 0 || topk < 1) return 0;
+  return tq::search_ws_bytes(c, n_db, n_queries, topk);
+}
+
+extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db, const float* queries,
+                                      int32_t n_queries, int32_t topk, int64_t* out_idx,
+                                      float* out_score, void* ws, size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (n_db < 1 || n_queries < 0) { set_error("need n_db >= 1 and n_queries >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (topk < 1 || topk > 1024 || topk > n_db) { set_error("need 1 <= topk <= min(n_db, 1024)"); return TQ_ERROR_INVALID_VALUE; }
+  if (n_queries == 0) return TQ_SUCCESS;
+  if (!queries || !out_idx || !out_score) { set_error("queries/out_idx/out_score is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(queries, 4) || !aligned(out_idx, 8) || !aligned(out_score, 4)) { set_error("search arrays misaligned"); return TQ_ERROR_MISALIGNED; }
+  tq_status_t st = check_packed(db, "db");
+  if (st != TQ_SUCCESS) return st;
+  if ((st = check_ws(ws, ws_bytes, tq::search_ws_bytes(c, n_db, n_queries, topk))) != TQ_SUCCESS) return st;
+  if (log_enabled()) std::fprintf(stderr, "[tq] search n_db=%lld nq=%d k=%d\n", (long long)n_db, n_queries, topk);
+  hipError_t e = tq::launch_search(c, db, n_db, queries, n_queries, topk, out_idx, out_score, ws,
+                                   static_cast<hipStream_t>(stream));
+  return finish(e, "tq_search_topk launch");
+}

@@ -1,0 +1,97 @@
+// Internal declarations shared by the host codec builder, the C-ABI layer and
+// the kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+// Thread-local error message (tq_last_error).
+void set_error(const std::string& msg);
+void clear_error();
+
+// Host tables of one codec (fp64 fit, fp32 canonical where stated).
+struct HostTables {
+  int d = 0, bits = 0, b = 0, m = 0;
+  uint64_t seed = 0;
+  std::vector<float> D;          // [d] ±1
+  std::vector<float> S;          // [m*d] row-major, canonical fp32
+  std::vector<double> centroids; // [2^b] ascending
+  std::vector<double> bounds;    // [2^b-1]
+  int iterations = 0;
+};
+
+// Builds every table on the host.  Returns TQ_SUCCESS or an error status (and
+// sets the thread-local message).
+tq_status_t build_host_tables(int d, int bits, int m, uint64_t seed, HostTables* out);
+bool supported_dim(int d);
+
+// Device constant block of one codec: everything a kernel needs besides S.
+// Laid out for a single struct-by-value kernel argument.
+struct DevParams {
+  float cent[8];       // fp32 centroids (2^b <= 8)
+  float bound[8];      // fp32 boundaries (2^b - 1 used)
+  float plane_coef[4]; // MSE plane weights of the bit-plane expansion of c[idx]
+  float plane_bias;    // constant term of that expansion
+  float qjl_kappa;     // sqrt(pi/2)/m
+  float inv_sqrt_d;    // 1/sqrt(d)
+  int d, b, m, code_words, sign_words, n_planes;
+};
+
+}  // namespace tq
+
+struct tq_codec_s {
+  tq::HostTables host;
+  tq::DevParams prm;
+  int device = 0;
+  // device tables (one allocation)
+  void* dev_block = nullptr;
+  float* dS = nullptr;   // [m][d] row-major
+  float* dSt = nullptr;  // [d][m] (transpose of S)
+  float* dD = nullptr;   // [d] ±1
+};
+
+namespace tq {
+
+// ---- kernel launchers (kernels_*.hip).  All arguments were validated. ----
+// Encode: rotate + quantize (codes, norm, rnorm) and write the residual r (fp32
+// [n][d]) into ws_r; then the QJL projection writes the sign words.
+hipError_t launch_encode(const tq_codec_s* c, const void* x, tq_dtype_t dt, int64_t n,
+                         tq_packed_t out, float* ws_r, hipStream_t s);
+size_t encode_ws_bytes(const tq_codec_s* c, int64_t n);
+
+// Query prep: q' = R q and p = S q' for n query vectors (fp32 outputs [n][d],[n][m]).
+hipError_t launch_qprep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int64_t n, float* qrot,
+                        float* proj, hipStream_t s);
+
+// Logits for the [batch][n_q_heads][n_queries][ctx] layout (prepped queries
+// in ws).
+size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
+hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                         int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
+                         void* ws, hipStream_t s);
+hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                              int n_kv_heads, int n_queries, void* ws, hipStream_t s);
+hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                                 int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+
+bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why);
+size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads,
+                       int n_kv_heads, int64_t ctx);
+hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
+                         int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v,
+                         int64_t ctx, float scale, void* out, tq_dtype_t out_dt, void* ws,
+                         hipStream_t s);
+
+size_t search_ws_bytes(const tq_codec_s* c, int64_t n_db, int n_queries, int topk);
+hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, const float* queries,
+                         int n_queries, int topk, int64_t* out_idx, float* out_score, void* ws,
+                         hipStream_t s);
+
+}  // namespace tq

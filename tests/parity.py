@@ -1,0 +1,71 @@
+"""Comparison helpers for the GPU-vs-oracle parity tests.
+
+Bars (stated once here, used by every GPU test):
+* codes: bit-exact except coordinates whose fp32 rotated value lies within
+  1e-5 of the boundary between the two codes; at most 1e-5 of all coordinates
+  may differ.  A vector with a differing code is re-derived by the oracle
+  given the GPU's codes (r, γ, signs all depend on them).
+* signs: bit-exact except where the oracle's |z| < 1e-5.
+* ν and γ: relative error <= 2e-6 (fp32 accumulation of d terms).
+* logits / attention outputs: per row max_i|a_i - b_i| / max_i|b_i| <= 1e-3
+  for bf16 inputs, 1e-4 for fp32 inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+BAND = 1e-5
+NORM_RTOL = 2e-6
+
+
+def tol_for(dtype: str) -> float:
+    return 1e-4 if dtype == "f32" else 1e-3
+
+
+def row_rel_err(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    a = np.asarray(a, np.float64).reshape(-1, np.shape(a)[-1])
+    b = np.asarray(b, np.float64).reshape(-1, np.shape(b)[-1])
+    den = np.maximum(np.max(np.abs(b), axis=1), 1e-30)
+    return np.max(np.abs(a - b), axis=1) / den
+
+
+def check_encode(cd: O.Codec, x64: np.ndarray, gpu: dict, label: str = "") -> dict:
+    """Compare one GPU encode (numpy dict) with the oracle on inputs x64."""
+    ref = O.encode(cd, x64)
+    n, d = x64.shape
+    gi = O.unpack_planes(gpu["codes"], cd.b, d)
+    ri = ref["idx"]
+    diff = gi != ri
+    n_diff = int(diff.sum())
+    assert n_diff <= max(1, int(1e-5 * diff.size)), f"{label}: {n_diff} codes differ of {diff.size}"
+    if n_diff:
+        y32 = ref["y"].astype(np.float32).astype(np.float64)
+        t32 = cd.t32.astype(np.float64)
+        vv, jj = np.nonzero(diff)
+        for v, j in zip(vv, jj):
+            a, b = int(gi[v, j]), int(ri[v, j])
+            assert abs(a - b) == 1, f"{label}: code jump {b}->{a} at ({v},{j})"
+            tb = t32[min(a, b)]
+            assert abs(y32[v, j] - tb) < BAND, f"{label}: mismatch at ({v},{j}) y={y32[v,j]} boundary {tb}"
+    # norms
+    assert np.allclose(gpu["norm"], ref["norm"], rtol=NORM_RTOL, atol=0), f"{label}: norm"
+    # re-derive rows whose codes differ
+    rows = np.unique(np.nonzero(diff)[0]) if n_diff else np.array([], np.int64)
+    exp_signs = ref["signs"].copy()
+    exp_rnorm = ref["rnorm"].copy()
+    z = ref["z"].copy()
+    if rows.size:
+        rd = O.encode_given_codes(cd, x64[rows], gi[rows])
+        exp_signs[rows] = rd["signs"]
+        exp_rnorm[rows] = rd["rnorm"]
+        z[rows] = rd["z"]
+    assert np.allclose(gpu["rnorm"], exp_rnorm, rtol=NORM_RTOL, atol=1e-7), f"{label}: rnorm"
+    gs = O.unpack_bits(gpu["signs"], cd.m)
+    es = O.unpack_bits(exp_signs, cd.m)
+    sd = gs != es
+    if sd.any():
+        assert np.all(np.abs(z[sd]) < BAND), f"{label}: {int(sd.sum())} sign bits differ outside the band " \
+                                             f"(max |z| {np.max(np.abs(z[sd]))})"
+    return {"code_mismatch": n_diff, "sign_mismatch": int(sd.sum()), "ref": ref}
