@@ -80,13 +80,23 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
   }
 }
 
-size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int /*n_kv_heads*/, int n_queries) {
+bool logits_mfma_eligible(const tq_codec_s* c);
+size_t logits_mfma_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
+hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                                   int n_kv_heads, int n_queries, void* ws, hipStream_t s);
+hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                              int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+
+size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
+  if (logits_mfma_eligible(c)) return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
   const size_t nv = static_cast<size_t>(batch) * n_queries * n_q_heads;
   return nv * (c->prm.d + c->prm.m) * sizeof(float);
 }
 
 hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
-                              int /*n_kv_heads*/, int n_queries, void* ws, hipStream_t s) {
+                              int n_kv_heads, int n_queries, void* ws, hipStream_t s) {
+  if (logits_mfma_eligible(c))
+    return launch_logits_mfma_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
   float* qrot = static_cast<float*>(ws);
   float* proj = qrot + nv * c->prm.d;
@@ -103,6 +113,8 @@ hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int 
 
 hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                                  int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+  if (logits_mfma_eligible(c))
+    return launch_logits_mfma(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   const DevParams& P = c->prm;
   const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
   const float* qrot = static_cast<const float*>(ws);

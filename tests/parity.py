@@ -69,3 +69,20 @@ def check_encode(cd: O.Codec, x64: np.ndarray, gpu: dict, label: str = "") -> di
         assert np.all(np.abs(z[sd]) < BAND), f"{label}: {int(sd.sum())} sign bits differ outside the band " \
                                              f"(max |z| {np.max(np.abs(z[sd]))})"
     return {"code_mismatch": n_diff, "sign_mismatch": int(sd.sum()), "ref": ref}
+
+
+def oracle_records_like(cd: O.Codec, x64: np.ndarray, gpu: dict) -> dict:
+    """The oracle's records for x64, with the GPU's codes on rows where they
+    legitimately differ (checked by check_encode first) and r, γ and the signs
+    re-derived from those codes."""
+    check_encode(cd, x64, gpu, "conditioned")
+    ref = O.encode(cd, x64)
+    gi = O.unpack_planes(gpu["codes"], cd.b, x64.shape[1])
+    rows = np.nonzero(np.any(gi != ref["idx"], axis=1))[0]
+    out = {k: ref[k].copy() for k in ("codes", "signs", "norm", "rnorm")}
+    if rows.size:
+        rd = O.encode_given_codes(cd, x64[rows], gi[rows])
+        out["codes"][rows] = gpu["codes"][rows]
+        out["signs"][rows] = rd["signs"]
+        out["rnorm"][rows] = rd["rnorm"]
+    return out
