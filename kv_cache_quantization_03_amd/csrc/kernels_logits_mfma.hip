@@ -212,8 +212,8 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
     float* cst = reinterpret_cast<float*>(base + NKB * kOpBytes);
     cst[hl * 4 + 0] = ldexpf(1.f, -limb_exponent(2.f * cmax * mx[hl][0]));
     cst[hl * 4 + 1] = ldexpf(1.f, -limb_exponent(4.f * mx[hl][1]));
-    cst[hl * 4 + 2] = P.plane_bias * sall - 0.5f * csum * s3;
-    cst[hl * 4 + 3] = -pall - p3;
+    cst[hl * 4 + 2] = P.plane_bias * sall + 0.5f * csum * s3;  // slots j%4 = 3 hold -x/2 against 1-2bit
+    cst[hl * 4 + 3] = -pall + p3;
   }
 }
 
@@ -310,6 +310,11 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint8_t* __restr
 #pragma unroll
       for (int i = 0; i < NMT; ++i) acc_q[i] = mfma_fp8_fp4(a[i][NP * WB + wb], bop, acc_q[i]);
     }
+    // An MFMA reads operands from all 64 lanes, so it must run with the full
+    // EXEC mask: pin every accumulator here, in wave-uniform control flow, so
+    // the compiler cannot sink the matrix ops into the lane-divergent stores.
+#pragma unroll
+    for (int i = 0; i < NMT; ++i) asm volatile("" : "+v"(acc_m[i]), "+v"(acc_q[i]));
     if (key >= ctx) continue;
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {

@@ -193,3 +193,27 @@ def vector_search(n_db=1_000_000, n_queries=1024, d=1536, n_centers=256, bits=4,
     db = GaussianMixtureUnit(seed=501, n_rows=n_db, d=d, n_centers=n_centers)
     q = GaussianMixtureUnit(seed=502, n_rows=n_queries, d=d, n_centers=n_centers, centers_seed=501)
     return dict(name=f"search_{n_db}x{d}_{bits}bit", bits=bits, d=d, db=db, queries=q, k=k)
+
+
+def vector_search_torch(device, n_db=1_000_000, n_queries=1024, d=1536, n_centers=256, chunk=65536):
+    """The vector-search workload drawn on the GPU (torch Philox, seeded), for
+    full-size runs where drawing 1.5e9 normals in NumPy would dominate:
+    centres μ_k ~ N(0, I_d) (k < 256), row = μ_k + N(0, I_d) with k uniform,
+    normalised to unit length; fp32.  Database seed 501, query seed 502,
+    centres from the database generator."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(501)
+    centers = torch.randn((n_centers, d), generator=g, device=device)
+    db = torch.empty((n_db, d), dtype=torch.float32, device=device)
+    for s in range(0, n_db, chunk):
+        e = min(n_db, s + chunk)
+        comp = torch.randint(0, n_centers, (e - s,), generator=g, device=device)
+        x = centers[comp] + torch.randn((e - s, d), generator=g, device=device)
+        db[s:e] = x / x.norm(dim=1, keepdim=True)
+    gq = torch.Generator(device=device)
+    gq.manual_seed(502)
+    comp = torch.randint(0, n_centers, (n_queries,), generator=gq, device=device)
+    q = centers[comp] + torch.randn((n_queries, d), generator=gq, device=device)
+    q = q / q.norm(dim=1, keepdim=True)
+    return db, q.contiguous()
