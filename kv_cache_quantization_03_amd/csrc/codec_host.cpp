@@ -211,6 +211,36 @@ void plane_expansion(const std::vector<double>& c, int b, float* coef, float* bi
   *n_planes = np;
 }
 
+// v <- Hᵀ v for the codec's Hadamard matrix: Sylvester (symmetric) for
+// d = 2^k, H12 ⊗ H_{d/12} for d = 12 * 2^k (Hᵀ = H12ᵀ ⊗ H_{d/12}).
+void fwht_inplace(double* v, int n) {
+  for (int h = 1; h < n; h <<= 1)
+    for (int i = 0; i < n; i += 2 * h)
+      for (int j = i; j < i + h; ++j) {
+        const double a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+void apply_hadamard_transposed(double* v, int d) {
+  if ((d & (d - 1)) == 0) {
+    fwht_inplace(v, d);
+    return;
+  }
+  const int n = d / 12;
+  for (int a = 0; a < 12; ++a) fwht_inplace(v + a * n, n);
+  std::vector<double> t(12);
+  for (int j = 0; j < n; ++j) {
+    for (int b = 0; b < 12; ++b) {
+      double acc = 0;
+      for (int a = 0; a < 12; ++a) acc += tq::paley12(a, b) * v[a * n + j];
+      t[b] = acc;
+    }
+    for (int b = 0; b < 12; ++b) v[b * n + j] = t[b];
+  }
+}
+
 }  // namespace
 
 extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim,
@@ -261,13 +291,21 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
     return e == hipErrorOutOfMemory ? TQ_ERROR_OUT_OF_MEMORY : TQ_ERROR_HIP;
   }
   c->dS = static_cast<float*>(c->dev_block);
-  c->dSt = c->dS + nS;
-  c->dD = c->dSt + nS;
-  std::vector<float> St(nS);
-  for (int i = 0; i < h.m; ++i)
-    for (int j = 0; j < h.d; ++j) St[static_cast<size_t>(j) * h.m + i] = h.S[static_cast<size_t>(i) * h.d + j];
+  c->dMt = c->dS + nS;
+  c->dD = c->dMt + nS;
+  // M = S R, row by row in fp64: M[i][j] = (Hᵀ S[i,:])[j] D[j] / sqrt(d); stored transposed.
+  std::vector<float> Mt(nS);
+  {
+    std::vector<double> v(h.d);
+    const double inv = 1.0 / std::sqrt(static_cast<double>(h.d));
+    for (int i = 0; i < h.m; ++i) {
+      for (int j = 0; j < h.d; ++j) v[j] = h.S[static_cast<size_t>(i) * h.d + j];
+      apply_hadamard_transposed(v.data(), h.d);
+      for (int j = 0; j < h.d; ++j) Mt[static_cast<size_t>(j) * h.m + i] = static_cast<float>(v[j] * h.D[j] * inv);
+    }
+  }
   e = hipMemcpy(c->dS, h.S.data(), nS * sizeof(float), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(c->dSt, St.data(), nS * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->dMt, Mt.data(), nS * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->dD, h.D.data(), h.d * sizeof(float), hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     set_error(std::string("uploading codec tables failed: ") + hipGetErrorString(e));

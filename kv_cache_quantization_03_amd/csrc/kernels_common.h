@@ -38,19 +38,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Paley type-I Hadamard matrix of order 12 (q = 11): H = I + S with
-// S = [[0, 1ᵀ], [-1, Q]], Q_ab = χ(b - a) the quadratic character mod 11.
-__host__ __device__ constexpr int legendre11(int a) {
-  a = ((a % 11) + 11) % 11;
-  if (a == 0) return 0;
-  int r = 1;
-  for (int k = 0; k < 5; ++k) r = (r * a) % 11;  // Euler's criterion: a^5 mod 11
-  return r == 1 ? 1 : -1;
-}
-__host__ __device__ constexpr int paley12(int a, int b) {
-  return a == b ? 1 : (a == 0 ? 1 : (b == 0 ? -1 : legendre11(b - a)));
-}
-
 // Unnormalised Walsh–Hadamard transform along the 64 lanes (bits 0..5 of j):
 // butterfly partner = lane ^ mask; lower lane keeps a+b, upper keeps a-b.
 template <int E>

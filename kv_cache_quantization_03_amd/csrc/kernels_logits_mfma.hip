@@ -43,7 +43,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kOpBytes = 64 * 32;  // one K-block of A for one M-tile: 64 lanes x 32 bytes
-constexpr int kConstFloats = 16;   // per M-tile: 4 query vectors x (scale_m, scale_q, bias_m, bias_q)
+// Per M-tile after the operands: float[4][4] (scale_m, scale_q, bias_m, bias_q)
+// per query vector, then int32[4] output rows ((b*Hq + h)*nq + qi, or -1 for
+// a padding slot), padded to 128 bytes.
+constexpr int kConstBytes = 128;
 constexpr int kKeysPerTile = 16;
 
 __device__ __forceinline__ v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c) {
@@ -69,18 +72,6 @@ __device__ __forceinline__ float from_fp8(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(byte), 0);
 }
 
-// Limb `limb` of R = R0 + R1/16 + R2/256 + R3/4096 (|R| <= 256).
-__device__ __forceinline__ uint32_t fp8_limb(float R, int limb) {
-  uint32_t out = 0;
-#pragma unroll
-  for (int l = 0; l < 4; ++l) {
-    const uint32_t b = to_fp8(R);
-    if (l == limb) out = b;
-    R = (R - from_fp8(b)) * 16.f;
-  }
-  return out;
-}
-
 // Power-of-two scale 2^E with sigma * 2^E < 256 (E = 8 - exponent of sigma).
 __device__ __forceinline__ int limb_exponent(float sigma) {
   if (!(sigma > 0.f)) return 0;
@@ -98,18 +89,29 @@ __device__ __forceinline__ int limb_exponent(float sigma) {
 template <int E, typename T>
 __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict__ q, DevParams P,
                                                              const float* __restrict__ Dsign,
-                                                             const float* __restrict__ St, int Hq, int nq, int G,
+                                                             const float* __restrict__ Mt, int Hq, int nq, int G,
                                                              int nkv, int n_mt, uint8_t* __restrict__ prep) {
   constexpr int d = E * kWave;
   constexpr int W = d / 32;
-  __shared__ float qs[4][d];
-  __shared__ float ps[4][d];
+  constexpr int TPO = 256 / d >= 1 ? 256 / d : 1;  // threads per output of p (2 for d=128, 1 for d=256)
+  constexpr int JPT = d / TPO;                      // inputs per thread
+  constexpr int CH = JPT < 64 ? JPT : 64;           // loads per batch
+  __shared__ float qs[4][d];  // q' = R q
+  __shared__ float qr[4][d];  // q
+  __shared__ float ps[4][d];  // p = S R q
   __shared__ float mx[4][2];
+  __shared__ __attribute__((aligned(16))) uint8_t opst[5 * (d / 128) * kOpBytes];  // A operands being built
   const int blk = blockIdx.x;
   const int mt = blk % n_mt, bk = blk / n_mt;
   const int b = bk / nkv, kh = bk % nkv;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int Gq = nq * G;
+  // The first batch of M = S R (transposed) loads goes out before anything else:
+  // p = M q needs no rotated query, so it overlaps the query load and rotation.
+  const int pi = threadIdx.x % d, part = threadIdx.x / d;
+  float mv[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) mv[u] = Mt[static_cast<int64_t>(part * JPT + u) * d + pi];
   {
     const int qv = mt * 4 + wv;
     float v[E];
@@ -117,12 +119,17 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
       const int qi = qv / G, g = qv % G;
       const int64_t row = (static_cast<int64_t>(b) * nq + qi) * Hq + kh * G + g;
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[e] = load_elem(q + row * d, e * kWave + lane) * Dsign[e * kWave + lane];
-      hadamard_wave<E>(v, lane);
+      for (int e = 0; e < E; ++e) v[e] = load_elem(q + row * d, e * kWave + lane);
     } else {
 #pragma unroll
       for (int e = 0; e < E; ++e) v[e] = 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      qr[wv][e * kWave + lane] = v[e];
+      v[e] *= Dsign[e * kWave + lane];
+    }
+    hadamard_wave<E>(v, lane);
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -134,19 +141,34 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
     if (lane == 0) mx[wv][0] = amax;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < d; i += 256) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      const float s = St[static_cast<int64_t>(j) * d + i];
-      a0 = fmaf(s, qs[0][j], a0);
-      a1 = fmaf(s, qs[1][j], a1);
-      a2 = fmaf(s, qs[2][j], a2);
-      a3 = fmaf(s, qs[3][j], a3);
+  {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = part * JPT; j0 < (part + 1) * JPT; j0 += CH) {
+      if (j0 != part * JPT) {
+#pragma unroll
+        for (int u = 0; u < CH; ++u) mv[u] = Mt[static_cast<int64_t>(j0 + u) * d + pi];
+      }
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) acc[vq] = fmaf(mv[u], qr[vq][j0 + u], acc[vq]);
+      }
     }
-    ps[0][i] = a0;
-    ps[1][i] = a1;
-    ps[2][i] = a2;
-    ps[3][i] = a3;
+    if (TPO == 1) {
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq) ps[vq][pi] = acc[vq];
+    } else {
+      // two partial sums per output: the upper half parks its sums in ps, the lower adds them
+      if (part == 1) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) ps[vq][pi] = acc[vq];
+      }
+      __syncthreads();
+      if (part == 0) {
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) ps[vq][pi] += acc[vq];
+      }
+    }
   }
   __syncthreads();
   {
@@ -164,108 +186,138 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
     cmax = fmaxf(cmax, fabsf(P.plane_coef[k]));
     csum += P.plane_coef[k];
   }
-  uint8_t* base = prep + (static_cast<int64_t>(bk) * n_mt + mt) * (NKB * kOpBytes + kConstFloats * 4);
-  // operands: K-block kbi -> (plane, word block); wave wv builds kbi = wv, wv+4, ...
-  for (int kbi = wv; kbi < NKB; kbi += 4) {
+  uint8_t* base = prep + (static_cast<int64_t>(bk) * n_mt + mt) * (NKB * kOpBytes + kConstBytes);
+  // Operands.  Every (query vector hl, K-block kbi, coordinate j) value is cut
+  // into its four fp8 limbs once, and each limb byte is placed at its slot of
+  // the A layout in LDS: limb l of vector hl is row 4hl+l; coordinate j of
+  // word wi (0..3 in the block) at bit 4i+v is contraction index
+  // kk = 32wi + 8v + i (the B nibble order), held by A lane group (kk%64)/16,
+  // byte kk%16 + 16(kk/64) (A byte order measured on gfx950).
+  for (int e = threadIdx.x; e < 4 * NKB * 128; e += 256) {
+    const int jl = e & 127, kbi = (e >> 7) % NKB, hl = (e >> 7) / NKB;
     const int plane = kbi / (W / 4), kb = kbi % (W / 4);
     const bool qjl = plane >= NP;
     const float kappa = qjl ? 2.f : P.plane_coef[plane];
-    const int row = lane & 15, hl = row >> 2, limb = row & 3, g = lane >> 4;
     const float sigma = qjl ? 4.f * mx[hl][1] : 2.f * cmax * mx[hl][0];
-    const float scale = ldexpf(1.f, limb_exponent(sigma));
+    const int wi = jl >> 5, rr = jl & 31, i = rr >> 2, v = rr & 3;
+    const float inv_val = v == 0 ? 2.f : (v == 1 ? 1.f : (v == 2 ? 0.5f : -0.5f));
     const float* src = qjl ? ps[hl] : qs[hl];
-    uint32_t words[8];
+    float R = ldexpf(kappa * src[128 * kb + jl] * inv_val, limb_exponent(sigma));
+    const int kk = 32 * wi + 8 * v + i;
+    const int grp = (kk & 63) >> 4, byte = (kk & 15) + 16 * (kk >> 6);
 #pragma unroll
-    for (int dw = 0; dw < 8; ++dw) {
-      uint32_t wbits = 0;
-#pragma unroll
-      for (int by = 0; by < 4; ++by) {
-        // A byte s of lane group g holds contraction index kk; B nibble kk%32
-        // of lane group kk/32 holds the same kk (lane layout measured on gfx950)
-        const int s = dw * 4 + by;
-        const int kk = s < 16 ? 16 * g + s : 64 + 16 * g + (s - 16);
-        const int wi = kk >> 5, sp = kk & 31;
-        const int v = sp >> 3, i = sp & 7;  // nibble i of B VGPR v = bit 4i+v of the word
-        const int j = 32 * (4 * kb + wi) + 4 * i + v;
-        const float inv_val = v == 0 ? 2.f : (v == 1 ? 1.f : (v == 2 ? 0.5f : -0.5f));
-        const float x = kappa * src[j] * inv_val * scale;
-        wbits |= fp8_limb(x, limb) << (8 * by);
-      }
-      words[dw] = wbits;
+    for (int l = 0; l < 4; ++l) {
+      const uint32_t bl = to_fp8(R);
+      opst[kbi * kOpBytes + (16 * grp + 4 * hl + l) * 32 + byte] = static_cast<uint8_t>(bl);
+      R = (R - from_fp8(bl)) * 16.f;
     }
-    uint4* dst = reinterpret_cast<uint4*>(base + static_cast<int64_t>(kbi) * kOpBytes + lane * 32);
-    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
   }
-  // constants per query vector of the tile
-  if (threadIdx.x < 4) {
-    const int hl = threadIdx.x;
+  __syncthreads();
+  for (int e = threadIdx.x; e < NKB * kOpBytes / 16; e += 256)
+    reinterpret_cast<uint4*>(base)[e] = reinterpret_cast<const uint4*>(opst)[e];
+  // constants per query vector of the tile: wave hl reduces vector hl
+  {
+    const int hl = wv;
     float sall = 0.f, s3 = 0.f, pall = 0.f, p3 = 0.f;
-    for (int j = 0; j < d; ++j) {
-      sall += qs[hl][j];
-      pall += ps[hl][j];
+    for (int j = lane; j < d; j += kWave) {
+      const float a = qs[hl][j], pj = ps[hl][j];
+      sall += a;
+      pall += pj;
       if ((j & 3) == 3) {
-        s3 += qs[hl][j];
-        p3 += ps[hl][j];
+        s3 += a;
+        p3 += pj;
       }
     }
-    float* cst = reinterpret_cast<float*>(base + NKB * kOpBytes);
-    cst[hl * 4 + 0] = ldexpf(1.f, -limb_exponent(2.f * cmax * mx[hl][0]));
-    cst[hl * 4 + 1] = ldexpf(1.f, -limb_exponent(4.f * mx[hl][1]));
-    cst[hl * 4 + 2] = P.plane_bias * sall + 0.5f * csum * s3;  // slots j%4 = 3 hold -x/2 against 1-2bit
-    cst[hl * 4 + 3] = -pall + p3;
+    sall = wave_sum(sall);
+    s3 = wave_sum(s3);
+    pall = wave_sum(pall);
+    p3 = wave_sum(p3);
+    if (lane == 0) {
+      const int qv = mt * 4 + hl;
+      int orow = -1;
+      if (qv < Gq) orow = (b * Hq + kh * G + qv % G) * nq + qv / G;
+      reinterpret_cast<int*>(base + NKB * kOpBytes + 64)[hl] = orow;
+      float* cst = reinterpret_cast<float*>(base + NKB * kOpBytes);
+      cst[hl * 4 + 0] = ldexpf(1.f, -limb_exponent(2.f * cmax * mx[hl][0]));
+      cst[hl * 4 + 1] = ldexpf(1.f, -limb_exponent(4.f * mx[hl][1]));
+      // slots with j%4 = 3 hold -x/2 against the +-1 nibble: add the x/2 back
+      cst[hl * 4 + 2] = P.plane_bias * sall + 0.5f * csum * s3;
+      cst[hl * 4 + 3] = -pall + p3;
+    }
   }
 }
 
 // ----------------------------------------------------------------------------
-// Logits: block = 4 waves, each wave scores T tiles of 16 keys of one
+// Logits: each wave scores 64 consecutive keys (4 tiles of 16) of one
 // (batch, kv head) against NMT M-tiles of its query group.
+//
+// Memory: the wave's records are contiguous in each array (64 rows), so they
+// are read with fully coalesced 16-byte loads (one instruction covers 1 KB),
+// staged in the wave's own LDS slice, and read back in the MFMA lane layout
+// (lane L: word L/16 of key L%16 of a tile).  Rows are padded by 4 words in
+// LDS to spread the reads over the banks.  The wave's 64 norms ν and γ are
+// loaded one per lane and moved to the owning lane with a cross-lane read.
+// Reading the words in the MFMA layout straight from global memory touches
+// every cache line from several instructions and costs ~1.7x the time.
 // ----------------------------------------------------------------------------
-template <int NP, int WB, int NMT, int T>
-__global__ __launch_bounds__(256) void logits_mfma_kernel(const uint8_t* __restrict__ prep, DevParams P, int Hq,
-                                                          int nq, int G, int nkv, int n_mt, int64_t ctx,
-                                                          tq_packed_t k, float* __restrict__ logits) {
-  constexpr int NKB = (NP + 1) * WB;  // K-blocks: MSE planes x word blocks, then QJL word blocks
-  constexpr int W = 4 * WB;           // words per plane
+constexpr int kKeysPerWave = 64;
+
+template <int NP, int WB, int NMT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* __restrict__ prep, int n_mt, int ctx,
+                                                                 const uint32_t* __restrict__ codes,
+                                                                 const uint32_t* __restrict__ signs,
+                                                                 const float* __restrict__ norm,
+                                                                 const float* __restrict__ rnorm, float kappa,
+                                                                 float* __restrict__ logits) {
+  constexpr int NKB = (NP + 1) * WB;   // K-blocks: MSE planes x word blocks, then QJL word blocks
+  constexpr int W = 4 * WB;            // words per plane (d/32)
+  constexpr int NB = NP > 3 ? 3 : NP;  // stored planes (the parity plane is computed)
+  constexpr int CW = NB * W;           // code words per key
+  constexpr int SW = W;                // sign words per key
+  constexpr int CS = CW + 4, SS = SW + 4;  // LDS row strides (words)
+  constexpr int MT_BYTES = NKB * kOpBytes + kConstBytes;
+  __shared__ uint32_t s_codes[WAVES][kKeysPerWave * CS];
+  __shared__ uint32_t s_signs[WAVES][kKeysPerWave * SS];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, kl = lane & 15;
   const int bk = blockIdx.y;
-  const int b = bk / nkv, kh = bk % nkv;
-  const int mt0 = blockIdx.z * NMT;
-  const int64_t key0 = (static_cast<int64_t>(blockIdx.x) * 4 + wv) * (T * kKeysPerTile);
-  if (key0 >= ctx) return;
-  const int CW = P.code_words, SW = P.sign_words;
+  const int key0 = (blockIdx.x * WAVES + wv) * kKeysPerWave;
+  if (key0 >= ctx) return;  // wave-uniform
+  const int nvalid = min(kKeysPerWave, ctx - key0);
+  const int64_t row0 = static_cast<int64_t>(bk) * ctx + key0;
+  codes += row0 * CW;
+  signs += row0 * SW;
+  norm += row0;
+  rnorm += row0;
 
-  // ---- loads for all T tiles first (memory-level parallelism)
-  constexpr int NB = NP > 3 ? 3 : NP;  // stored planes (the parity plane is computed)
-  uint32_t cw[T][NB * WB];
-  uint32_t sw[T][WB];
-  float nu[T], ga[T];
+  // ---- coalesced record loads, all issued before any use: 16 B per lane per
+  // instruction; rows past the end of the context re-read the last valid row
+  // (branch-free, always in bounds) and are never stored.
+  uint4 cv[CW / 4], sv[SW / 4];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    int64_t key = key0 + t * kKeysPerTile + kl;
-    key = key < ctx ? key : ctx - 1;
-    const int64_t row = static_cast<int64_t>(bk) * ctx + key;
-    const uint32_t* crow = k.codes + row * CW;
-#pragma unroll
-    for (int p = 0; p < NB; ++p)
-#pragma unroll
-      for (int wb = 0; wb < WB; ++wb) cw[t][p * WB + wb] = crow[p * W + 4 * wb + g];
-#pragma unroll
-    for (int wb = 0; wb < WB; ++wb) sw[t][wb] = k.signs[row * SW + 4 * wb + g];
-    nu[t] = k.norm[row];
-    ga[t] = k.rnorm[row];
+  for (int r = 0; r < CW / 4; ++r) {
+    const int w = 4 * (r * 64 + lane);
+    const int kk = min(w / CW, nvalid - 1);
+    cv[r] = reinterpret_cast<const uint4*>(codes)[(kk * CW + w % CW) / 4];
   }
-  // ---- query operands and constants (shared by every tile)
+#pragma unroll
+  for (int r = 0; r < SW / 4; ++r) {
+    const int w = 4 * (r * 64 + lane);
+    const int kk = min(w / SW, nvalid - 1);
+    sv[r] = reinterpret_cast<const uint4*>(signs)[(kk * SW + w % SW) / 4];
+  }
+  const int ln = min(lane, nvalid - 1);
+  const float nu_l = norm[ln], ga_l = rnorm[ln];
+
+  // ---- query operands, constants and output rows (from L2)
+  const int mt0 = blockIdx.z * NMT;
   v8i a[NMT][NKB];
   float sc_m[NMT], sc_q[NMT], bi_m[NMT], bi_q[NMT];
-  bool mt_ok[NMT];
+  float* out[NMT];
 #pragma unroll
   for (int i = 0; i < NMT; ++i) {
-    const int mt = mt0 + i;
-    mt_ok[i] = mt < n_mt;
-    const int mtc = mt_ok[i] ? mt : 0;
-    const uint8_t* base = prep + (static_cast<int64_t>(bk) * n_mt + mtc) * (NKB * kOpBytes + kConstFloats * 4);
+    const int mt = min(mt0 + i, n_mt - 1);
+    const uint8_t* base = prep + (static_cast<int64_t>(bk) * n_mt + mt) * MT_BYTES;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const uint4* src = reinterpret_cast<const uint4*>(base + kb * kOpBytes + lane * 32);
@@ -273,16 +325,36 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint8_t* __restr
       a[i][kb][0] = x.x; a[i][kb][1] = x.y; a[i][kb][2] = x.z; a[i][kb][3] = x.w;
       a[i][kb][4] = y.x; a[i][kb][5] = y.y; a[i][kb][6] = y.z; a[i][kb][7] = y.w;
     }
-    const float* cst = reinterpret_cast<const float*>(base + NKB * kOpBytes) + g * 4;
-    sc_m[i] = cst[0];
-    sc_q[i] = cst[1];
-    bi_m[i] = cst[2];
-    bi_q[i] = cst[3];
+    const float4 c4 = reinterpret_cast<const float4*>(base + NKB * kOpBytes)[g];
+    sc_m[i] = c4.x;
+    sc_q[i] = c4.y;
+    bi_m[i] = c4.z;
+    bi_q[i] = c4.w;
+    const int orow = reinterpret_cast<const int*>(base + NKB * kOpBytes + 64)[g];
+    out[i] = (mt0 + i < n_mt && orow >= 0) ? logits + static_cast<int64_t>(orow) * ctx + key0 : nullptr;
   }
-  const float kappa = P.qjl_kappa;
+
+  // ---- stage the records in the wave's LDS slice (rows padded by 4 words)
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int64_t key = key0 + t * kKeysPerTile + kl;
+  for (int r = 0; r < CW / 4; ++r) {
+    const int w = 4 * (r * 64 + lane);
+    *reinterpret_cast<uint4*>(&s_codes[wv][(w / CW) * CS + w % CW]) = cv[r];
+  }
+#pragma unroll
+  for (int r = 0; r < SW / 4; ++r) {
+    const int w = 4 * (r * 64 + lane);
+    *reinterpret_cast<uint4*>(&s_signs[wv][(w / SW) * SS + w % SW]) = sv[r];
+  }
+  // the wave reads back only what it wrote: LDS ops of one wave complete in
+  // order; the barrier keeps the compiler from moving the reads above the writes
+  __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+  for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) {
+    const int kk = t * kKeysPerTile + kl;
+    const uint32_t* crow = &s_codes[wv][kk * CS];
+    const uint32_t* srow = &s_signs[wv][kk * SS];
+    const float nu = __shfl(nu_l, kk, kWave), ga = __shfl(ga_l, kk, kWave);
     v4f acc_m[NMT], acc_q[NMT];
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
@@ -290,23 +362,18 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint8_t* __restr
       acc_q[i] = v4f{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
+    for (int wb = 0; wb < WB; ++wb) {
+      uint32_t pw[NB];
 #pragma unroll
-      for (int wb = 0; wb < WB; ++wb) {
-        uint32_t w;
-        if (p < 3 && p < NB) {
-          w = cw[t][p * WB + wb];
-        } else {  // parity plane of a 3-bit code
-          w = cw[t][0 * WB + wb] ^ cw[t][1 * WB + wb] ^ cw[t][2 * WB + wb];
-        }
+      for (int p = 0; p < NB; ++p) pw[p] = crow[p * W + 4 * wb + g];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const uint32_t w = (p < NB) ? pw[p < NB ? p : 0] : (pw[0] ^ pw[NB > 1 ? 1 : 0] ^ pw[NB > 2 ? 2 : 0]);
         const v8i bop = fp4_operand(w);
 #pragma unroll
         for (int i = 0; i < NMT; ++i) acc_m[i] = mfma_fp8_fp4(a[i][p * WB + wb], bop, acc_m[i]);
       }
-    }
-#pragma unroll
-    for (int wb = 0; wb < WB; ++wb) {
-      const v8i bop = fp4_operand(sw[t][wb]);
+      const v8i bop = fp4_operand(srow[4 * wb + g]);
 #pragma unroll
       for (int i = 0; i < NMT; ++i) acc_q[i] = mfma_fp8_fp4(a[i][NP * WB + wb], bop, acc_q[i]);
     }
@@ -315,23 +382,17 @@ __global__ __launch_bounds__(256) void logits_mfma_kernel(const uint8_t* __restr
     // the compiler cannot sink the matrix ops into the lane-divergent stores.
 #pragma unroll
     for (int i = 0; i < NMT; ++i) asm volatile("" : "+v"(acc_m[i]), "+v"(acc_q[i]));
-    if (key >= ctx) continue;
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
-      const int qv = (mt0 + i) * 4 + g;
-      if (!mt_ok[i] || qv >= nq * G) continue;
       const float mse = sc_m[i] * (acc_m[i][0] + acc_m[i][1] * 0.0625f + acc_m[i][2] * 0.00390625f +
                                    acc_m[i][3] * 0.000244140625f) + bi_m[i];
       const float qj = sc_q[i] * (acc_q[i][0] + acc_q[i][1] * 0.0625f + acc_q[i][2] * 0.00390625f +
                                   acc_q[i][3] * 0.000244140625f) + bi_q[i];
-      const int qi = qv / G, gg = qv % G;
-      const int h = kh * G + gg;
-      logits[((static_cast<int64_t>(b) * Hq + h) * nq + qi) * ctx + key] = nu[t] * (mse + kappa * ga[t] * qj);
+      if (out[i] != nullptr && kk < nvalid) out[i][kk] = nu * (mse + kappa * ga * qj);
     }
   }
 }
 
-// ----------------------------------------------------------------------------
 // TQ_LOGITS_KERNEL=valu selects the general VALU kernel (A/B comparisons).
 bool logits_mfma_eligible(const tq_codec_s* c) {
   const char* v = std::getenv("TQ_LOGITS_KERNEL");
@@ -343,7 +404,7 @@ size_t logits_mfma_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n
   const int G = n_q_heads / n_kv_heads;
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
   const int NKB = (c->prm.n_planes + 1) * (c->prm.d / 128);
-  return static_cast<size_t>(batch) * n_kv_heads * n_mt * (NKB * kOpBytes + kConstFloats * 4);
+  return static_cast<size_t>(batch) * n_kv_heads * n_mt * (NKB * kOpBytes + kConstBytes);
 }
 
 hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
@@ -352,7 +413,7 @@ hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
   const dim3 grid(static_cast<unsigned>(batch * n_kv_heads * n_mt));
   auto go = [&]<int E, typename T>(const T* qq) -> hipError_t {
-    hipLaunchKernelGGL((attn_prep_mfma_kernel<E, T>), grid, dim3(256), 0, s, qq, c->prm, c->dD, c->dSt, n_q_heads,
+    hipLaunchKernelGGL((attn_prep_mfma_kernel<E, T>), grid, dim3(256), 0, s, qq, c->prm, c->dD, c->dMt, n_q_heads,
                        n_queries, G, n_kv_heads, n_mt, static_cast<uint8_t*>(ws));
     return hipGetLastError();
   };
@@ -371,13 +432,13 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
-  constexpr int T = 4;
   auto go = [&]<int NP, int WB, int NMT>() -> hipError_t {
-    const dim3 grid(static_cast<unsigned>(ceil_div(ctx, 4 * T * kKeysPerTile)), batch * n_kv_heads,
+    constexpr int WAVES = WB == 1 ? 8 : 4;
+    const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * kKeysPerWave)), batch * n_kv_heads,
                     static_cast<unsigned>(ceil_div(n_mt, NMT)));
-    hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, T>), grid, dim3(256), 0, s,
-                       static_cast<const uint8_t*>(ws), c->prm, n_q_heads, n_queries, G, n_kv_heads, n_mt, ctx, k,
-                       logits);
+    hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES>), grid, dim3(WAVES * 64), 0, s,
+                       static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
+                       k.rnorm, c->prm.qjl_kappa, logits);
     return hipGetLastError();
   };
   const int NP = c->prm.n_planes;

@@ -46,6 +46,21 @@ struct DevParams {
 
 }  // namespace tq
 
+namespace tq {
+// Paley type-I Hadamard matrix of order 12 (q = 11): H = I + S with
+// S = [[0, 1ᵀ], [-1, Q]], Q_ab = χ(b - a), χ the quadratic character mod 11.
+__host__ __device__ constexpr int legendre11(int a) {
+  a = ((a % 11) + 11) % 11;
+  if (a == 0) return 0;
+  int r = 1;
+  for (int k = 0; k < 5; ++k) r = (r * a) % 11;  // Euler's criterion: a^5 mod 11
+  return r == 1 ? 1 : -1;
+}
+__host__ __device__ constexpr int paley12(int a, int b) {
+  return a == b ? 1 : (a == 0 ? 1 : (b == 0 ? -1 : legendre11(b - a)));
+}
+}  // namespace tq
+
 struct tq_codec_s {
   tq::HostTables host;
   tq::DevParams prm;
@@ -53,7 +68,7 @@ struct tq_codec_s {
   // device tables (one allocation)
   void* dev_block = nullptr;
   float* dS = nullptr;   // [m][d] row-major
-  float* dSt = nullptr;  // [d][m] (transpose of S)
+  float* dMt = nullptr;  // [d][m]: (S R)ᵀ, so that p = S R q needs no rotated query
   float* dD = nullptr;   // [d] ±1
 };
 
