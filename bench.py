@@ -131,12 +131,14 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
+        # one decode step of scoring: query prep and logits in one launch
+        S = sets[i % n_sets]
+        B.tq_attn_logits(codec, S["q"], S["k"], ctx, hkv, logits=S["logits"], ws=S["prep"])
+
+    def two_kernel_step(i):
+        # the split form: query prep, then logits from the prepared operands
         S = sets[i % n_sets]
         B.tq_attn_query_prep(codec, S["q"], hkv, prep=S["prep"])
-        B.tq_attn_logits_prepped(codec, S["prep"], (batch, 1, hq), S["k"], ctx, hkv, logits=S["logits"])
-
-    def logits_only(i):
-        S = sets[i % n_sets]
         B.tq_attn_logits_prepped(codec, S["prep"], (batch, 1, hq), S["k"], ctx, hkv, logits=S["logits"])
 
     for i in range(max(args.warmup, n_sets)):
@@ -145,10 +147,10 @@ def main():
     eager = [S["logits"].clone() for S in sets]
 
     if args.pmc_pass:
-        # short fixed workload for rocprofv3 --pmc: 20 logits launches, then plain
+        # short fixed workload for rocprofv3 --pmc: 20 step launches, then plain
         # 64 MiB device copies that calibrate the byte counters
         for i in range(20):
-            logits_only(i)
+            step(i)
         src = torch.empty(64 * 2 ** 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(5):
@@ -163,10 +165,6 @@ def main():
     with torch.cuda.graph(g_steps):
         for i in range(K):
             step(i)
-    g_logits = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_logits):
-        for i in range(K):
-            logits_only(i)
     # every replay must reproduce the eager results
     g_steps.replay()
     torch.cuda.synchronize()
@@ -174,29 +172,43 @@ def main():
         if not torch.equal(S["logits"], eager[s_i]):
             raise RuntimeError(f"graph replay differs from the eager step on buffer set {s_i}")
 
+    # timed region: K steps; HIP events on the launch stream bracket the same
+    # replay, so the kernel's average duration comes from the timed run itself
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    e0.record(stream)
     g_steps.replay()
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / K
+    logits_ms = e0.elapsed_time(e1) / K
     scores_per_step = batch * hq * ctx
     value = scores_per_step / (ms_per_step * 1e-3)
-
-    # dominant kernel: K back-to-back logits launches, HIP events on this stream
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g_logits.replay()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    g_logits.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    logits_ms = e0.elapsed_time(e1) / K
     for s_i, S in enumerate(sets[:min(n_sets, K)]):
         if not torch.equal(S["logits"], eager[s_i]):
-            raise RuntimeError(f"logits graph replay differs from the eager result on buffer set {s_i}")
+            raise RuntimeError(f"timed replay differs from the eager step on buffer set {s_i}")
+    del g_steps
 
-    alg_bytes = rec_bytes + logit_bytes + prep_bytes
+    # the split two-launch form on the same buffers, for comparison
+    g_two = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_two):
+        for i in range(K):
+            two_kernel_step(i)
+    g_two.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g_two.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    two_ms = e0.elapsed_time(e1) / K
+    two_diff = max(float(((S["logits"] - eager[s_i]).abs().amax(dim=-1) / eager[s_i].abs().amax(dim=-1)).max())
+                   for s_i, S in enumerate(sets[:min(n_sets, K)]))
+    del g_two
+
+    q_bytes = batch * hq * d * 2
+    alg_bytes = rec_bytes + logit_bytes + q_bytes
     achieved = alg_bytes / (logits_ms * 1e-3) / 1e9
     workload = w["name"]
     traffic = measured_traffic(workload)
@@ -219,14 +231,15 @@ def main():
                    "record_bytes_per_key": codec.record_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "logits", "kernel_ms": logits_ms, "algorithmic_bytes": alg_bytes,
+                     "kernel": "logits_fused_kernel", "kernel_ms": logits_ms, "algorithmic_bytes": alg_bytes,
                      "keys_per_s_kernel": scores_per_step / (logits_ms * 1e-3),
                      "k_only_GBs": rec_bytes / (logits_ms * 1e-3) / 1e9},
-        "stages": {"encode_k_ms": enc_ms, "encode_vectors_per_s": n_keys / (enc_ms * 1e-3)},
+        "stages": {"encode_k_ms": enc_ms, "encode_vectors_per_s": n_keys / (enc_ms * 1e-3),
+                   "two_kernel_step_ms": two_ms, "two_kernel_vs_fused_max_row_rel": two_diff},
     }
-    print(f"[bench] step {ms_per_step * 1e3:.2f} us, logits kernel {logits_ms * 1e3:.2f} us, "
-          f"{achieved:.0f} GB/s", file=sys.stderr, flush=True)
-    del g_steps, g_logits
+    print(f"[bench] step {ms_per_step * 1e3:.2f} us, fused kernel {logits_ms * 1e3:.2f} us, "
+          f"{achieved:.0f} GB/s; two-kernel step {two_ms * 1e3:.2f} us (max row rel diff {two_diff:.1e})",
+          file=sys.stderr, flush=True)
 
     if not args.no_stages:
         out["stages"].update(time_stages(B, I, codec, dev, args))
@@ -275,9 +288,9 @@ def time_stages(B, I, codec3, dev, args):
     k = torch.randn((8 * 32768, 128), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((1, 1, 32, 128), generator=g, device=dev).to(torch.bfloat16)
     kp4, _ = B.tq_encode_kv(c4, k)
-    prep = B.tq_attn_query_prep(c4, q, 8)
     lg = torch.empty((1, 32, 1, 32768), device=dev)
-    ms = _time(lambda: B.tq_attn_logits_prepped(c4, prep, (1, 1, 32), kp4, 32768, 8, logits=lg), 200, graph=True)
+    wsl = torch.empty(B.tq_attn_logits_workspace(c4, 1, 32, 8, 1), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_attn_logits(c4, q, kp4, 32768, 8, logits=lg, ws=wsl), 200, graph=True)
     res["logits_4bit_ms"] = ms
     res["logits_4bit_keys_per_s"] = 32 * 32768 / (ms * 1e-3)
     print(f"[bench] 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)

@@ -7,6 +7,7 @@
 // projection) and 第六部分 (the coordinate density);
 // 「TurboQuant 学习路径」 二.2 (Gaussian JL matrix, random signs D of the FJLT)
 // and 三.4 (Lloyd-Max).
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -303,6 +304,18 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
       apply_hadamard_transposed(v.data(), h.d);
       for (int j = 0; j < h.d; ++j) Mt[static_cast<size_t>(j) * h.m + i] = static_cast<float>(v[j] * h.D[j] * inv);
     }
+  }
+  {
+    double mx = 0.0;
+    for (int i = 0; i < h.m; ++i) {
+      double ss = 0.0;
+      for (int j = 0; j < h.d; ++j) {
+        const double x = Mt[static_cast<size_t>(j) * h.m + i];
+        ss += x * x;
+      }
+      mx = std::max(mx, std::sqrt(ss));
+    }
+    p.mrow_bound = std::nextafter(static_cast<float>(mx * (1.0 + 1e-6)), INFINITY);
   }
   e = hipMemcpy(c->dS, h.S.data(), nS * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->dMt, Mt.data(), nS * sizeof(float), hipMemcpyHostToDevice);

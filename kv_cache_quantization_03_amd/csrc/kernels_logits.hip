@@ -86,6 +86,10 @@ hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_
                                    int n_kv_heads, int n_queries, void* ws, hipStream_t s);
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+bool logits_fused_eligible(const tq_codec_s* c, int n_q_heads, int n_kv_heads, int n_queries);
+hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                               int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
+                               hipStream_t s);
 
 size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
   if (logits_mfma_eligible(c)) return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
@@ -106,6 +110,8 @@ hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt,
 hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                          int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits, void* ws,
                          hipStream_t s) {
+  if (logits_fused_eligible(c, n_q_heads, n_kv_heads, n_queries))
+    return launch_logits_fused(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   hipError_t e = launch_logits_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   if (e != hipSuccess) return e;
   return launch_logits_prepped(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);

@@ -41,6 +41,7 @@ struct DevParams {
   float plane_bias;    // constant term of that expansion
   float qjl_kappa;     // sqrt(pi/2)/m
   float inv_sqrt_d;    // 1/sqrt(d)
+  float mrow_bound;    // max_i ||row i of M = S R||_2 (fp32 M, rounded up): |(M q)_i| <= mrow_bound ||q||
   int d, b, m, code_words, sign_words, n_planes;
 };
 

@@ -199,6 +199,32 @@ def test_logits_mfma_and_valu_kernels_agree(B, bits, monkeypatch):
     assert ea <= 1e-4 and ev <= 1e-4
 
 
+@pytest.mark.parametrize("bits,qdt,batch,hq,hkv,nq,ctx", [(3, "bf16", 1, 32, 8, 1, 777), (2, "f32", 2, 4, 2, 2, 1500),
+                                                         (4, "f16", 1, 3, 1, 1, 64), (3, "f32", 3, 2, 2, 3, 513),
+                                                         (4, "bf16", 1, 8, 2, 1, 4097), (3, "bf16", 1, 1, 1, 1, 5)])
+def test_logits_fused_matches_two_kernel_path(B, bits, qdt, batch, hq, hkv, nq, ctx, monkeypatch):
+    # decode-shaped groups (at most 4 query vectors per KV head) take the single
+    # fused kernel; the two-kernel path (query prep, then logits) must agree,
+    # and both must match the oracle
+    say(f"fused logits bits={bits} q={qdt} batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx}")
+    gc, oc = pair(B, 128, bits)
+    rng = np.random.default_rng(ctx + bits)
+    k = as_exact(rng.standard_normal((batch * hkv * ctx, 128)), "f32")
+    q = as_exact(rng.standard_normal((batch, nq, hq, 128)), qdt)
+    rec = O.encode(oc, k.astype(np.float64))
+    kp = B.packed_from_numpy(rec)
+    fused = B.tq_attn_logits(gc, to_dev(q, qdt), kp, ctx, hkv).cpu().numpy()
+    monkeypatch.setenv("TQ_LOGITS_FUSED", "0")
+    two = B.tq_attn_logits(gc, to_dev(q, qdt), kp, ctx, hkv).cpu().numpy()
+    monkeypatch.delenv("TQ_LOGITS_FUSED")
+    ref = O.attn_logits(oc, q.astype(np.float64), rec, batch, hq, hkv, nq, ctx)
+    ef, et = row_rel_err(fused, ref).max(), row_rel_err(two, ref).max()
+    between = row_rel_err(fused, two.astype(np.float64)).max()
+    say(f"  fused err {ef:.2e}  two-kernel err {et:.2e}  between {between:.2e}")
+    assert ef <= tol_for(qdt) and et <= tol_for(qdt)
+    assert between <= 1e-4
+
+
 def test_logits_ctx_zero_is_noop(B):
     gc, _ = pair(B, 128, 3)
     kp = B.alloc_packed(gc, 1)
