@@ -222,22 +222,35 @@ size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, in
   return prep + part;
 }
 
+bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
+int decode_mfma_chunk();
+hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
+                              int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
+                              float* part, int n_chunks, hipStream_t s);
+
 hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
                          int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
                          void* out, tq_dtype_t out_dt, void* ws, hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int CH = attn_chunk(G);
-  const int n_chunks = static_cast<int>(ceil_div(ctx, CH));
+  int n_chunks = static_cast<int>(ceil_div(ctx, CH));
   const int64_t nq = static_cast<int64_t>(batch) * n_q_heads;
   float* qrot = static_cast<float*>(ws);
   float* proj = qrot + nq * ck->prm.d;
   float* part = proj + nq * ck->prm.m;
-  hipError_t e = launch_qprep(ck, q, q_dt, nq, qrot, proj, s);
-  if (e != hipSuccess) return e;
-  const size_t sh = (static_cast<size_t>(G) * CH + 8) * sizeof(float);
-  hipLaunchKernelGGL(decode_split_kernel, dim3(n_chunks, batch * n_kv_heads), dim3(kAttnThreads), sh, s, ck->prm,
-                     cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
+  if (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH) {
+    // matrix-core split kernel (query prep inside); same partial layout
+    e = launch_decode_mfma(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, part, n_chunks, s);
+    if (e != hipSuccess) return e;
+  } else {
+    e = launch_qprep(ck, q, q_dt, nq, qrot, proj, s);
+    if (e != hipSuccess) return e;
+    const size_t sh = (static_cast<size_t>(G) * CH + 8) * sizeof(float);
+    hipLaunchKernelGGL(decode_split_kernel, dim3(n_chunks, batch * n_kv_heads), dim3(kAttnThreads), sh, s, ck->prm,
+                       cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   auto run = [&]<int E>() -> hipError_t {
     hipLaunchKernelGGL((decode_combine_kernel<E>), dim3(batch * n_q_heads), dim3(kAttnThreads), 0, s, cv->prm,
                        part, n_q_heads, n_kv_heads, n_chunks, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);

@@ -1,0 +1,440 @@
+// Fused decode attention on the CDNA4 matrix cores (d = 128 for K and V, at
+// most 4 query heads per KV head).
+//
+// One block per (batch*kv_head, chunk of 1024 keys), 8 waves of 128 keys:
+//   1. the K query operands are rebuilt in LDS while the records load
+//      (query_prep_*, as in the fused logits kernel);
+//   2. each wave scores its 128 keys on the matrix cores (score_wave_values);
+//   3. softmax against the chunk's per-head maximum;
+//   4. V is accumulated in the codec domain on the matrix cores:
+//        M[g][j] = Σ_k w_gk ν_k c(idx_kj),   J[g][i] = Σ_k w_gk ν_k γ_k τ_ki,
+//      a contraction over keys, with the softmax weights as fp8 limb A
+//      operands and the V bit planes as fp4 B operands;
+//   5. the chunk partials (max, Σw, M, J) go to the combine kernel, which
+//      merges the chunks (log-sum-exp) and maps back to the input domain.
+// Pages: 「谷歌 TurboQuant 深度拆解」 第二部分 (the unbiased estimator);
+// 「TurboQuant+ 深度解析」 第五部分 (V compressed like K) and 第六部分 (V
+// dequantization dominates long-context decode).
+//
+// V as a matrix operand.  The contraction over keys needs, in each lane, the
+// bits of one coordinate across 32 keys, while a stored word holds 32
+// coordinates of one key.  Each lane therefore loads the V records of two
+// keys and a 32x32 bit transpose runs in registers: four lane stages (lane
+// bits 0-3, partners through DPP within rows of 16) and one stage between the
+// lane's two registers.  The key each lane loads is chosen so that the
+// transposed words land exactly in the B-operand layout with contraction
+// index = key index (see v_key_of_row).  The parity plane of a 3-bit codebook
+// is the XOR of the transposed stored planes.
+#include <cstdlib>
+#include <string>
+
+#include "mfma_common.h"
+
+namespace tq {
+
+namespace {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecKeysPerWave = 128;
+constexpr int kDecChunk = kDecWaves * kDecKeysPerWave;  // keys per block
+
+// Value of lane (lane ^ 2^K) within rows of 16 lanes, through DPP.
+template <int K>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int v = static_cast<int>(x);
+  if constexpr (K == 0) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  if constexpr (K == 1) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  if constexpr (K == 2) {  // quad reverse (i^3), then half-row mirror (i^7): i^4
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xF, 0xF, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false));
+  }
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8 = i^8
+}
+
+__device__ __forceinline__ float lane_xor_f(float x, int k) {
+  switch (k) {
+    case 0: return __uint_as_float(lane_xor<0>(__float_as_uint(x)));
+    case 1: return __uint_as_float(lane_xor<1>(__float_as_uint(x)));
+    case 2: return __uint_as_float(lane_xor<2>(__float_as_uint(x)));
+    default: return __uint_as_float(lane_xor<3>(__float_as_uint(x)));
+  }
+}
+
+// Max / sum over the 16 lanes of each row (one query head per row).
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v = fmaxf(v, lane_xor_f(v, k));
+  return v;
+}
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v += lane_xor_f(v, k);
+  return v;
+}
+
+// One stage of the bit transpose: swap row bit K (lane bit K) with column bit K.
+template <int K>
+__device__ __forceinline__ uint32_t transpose_stage(uint32_t w, int lane) {
+  constexpr uint32_t M = K == 0 ? 0x55555555u : (K == 1 ? 0x33333333u : (K == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu));
+  constexpr int s = 1 << K;
+  const uint32_t x = lane_xor<K>(w);
+  const bool hi = (lane >> K) & 1;
+  const uint32_t t = hi ? (x >> s) : (x << s);
+  const uint32_t keep = hi ? ~M : M;
+  return (w & keep) | (t & ~keep);
+}
+
+// 32x32 bit transpose within each row of 16 lanes: input row ρ = lane%16 + 16·reg
+// (r0: reg 0, r1: reg 1), column = bit; output lane%16 + 16·reg = column,
+// bit = row.
+__device__ __forceinline__ void transpose32(uint32_t& r0, uint32_t& r1, int lane) {
+  r0 = transpose_stage<0>(r0, lane);
+  r1 = transpose_stage<0>(r1, lane);
+  r0 = transpose_stage<1>(r0, lane);
+  r1 = transpose_stage<1>(r1, lane);
+  r0 = transpose_stage<2>(r0, lane);
+  r1 = transpose_stage<2>(r1, lane);
+  r0 = transpose_stage<3>(r0, lane);
+  r1 = transpose_stage<3>(r1, lane);
+  const uint32_t t = ((r0 >> 16) ^ r1) & 0x0000FFFFu;
+  r1 ^= t;
+  r0 ^= t << 16;
+}
+
+// Key (within the lane group's 32) whose words lane%16 + 16·reg loads: row
+// ρ = 4i + r carries key 8r + i, so that after the transpose bit 4i + r of the
+// word — FP4 nibble i of mask r, contraction index 8r + i — is that key.
+__device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (rho >> 2); }
+
+}  // namespace
+
+template <int NPK, int NPV, typename T>
+__global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
+    const T* q, DevParams PK, DevParams PV, const float* DsignK, const float* MtK, int Hq, int nkv, int ctx,
+    int n_chunks, float scale, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
+    const float* __restrict__ kn, const float* __restrict__ kr, const uint32_t* __restrict__ vc,
+    const uint32_t* __restrict__ vs, const float* __restrict__ vn, const float* __restrict__ vr,
+    float* __restrict__ part) {
+  using LK = RecLayout<NPK, 1>;
+  using LV = RecLayout<NPV, 1>;
+  constexpr int NT = kDecWaves * 64, NKB = LK::NKB, NBV = LV::NB;
+  constexpr int KSTAGE = kKeysPerWave * (LK::CS + LK::SS);
+  constexpr int SCR = KSTAGE > 1024 ? KSTAGE : 1024;  // words of per-wave scratch
+  __shared__ QueryPrepShared<NT, NKB> sh;
+  __shared__ __attribute__((aligned(16))) uint32_t wsc[kDecWaves][SCR];
+  __shared__ float hmax[kDecWaves][4];
+  __shared__ int ubexp[kDecWaves][2][4][4];  // V weight block exponents [type][head][key block]
+  __shared__ float hsum[kDecWaves][4][4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, kl = lane & 15;
+  const int bk = blockIdx.y, chunk = blockIdx.x;
+  const int G = Hq / nkv;
+  const QueryTile tile{bk / nkv, 1, Hq, G, bk % nkv, 0, G};
+  const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
+  const int64_t hrow = static_cast<int64_t>(bk) * ctx;         // first row of the head
+
+  // ---- loads: query operands first (see query_prep_load), then K and V records
+  QueryPrepRegs<NT> pr;
+  query_prep_load<NT>(pr, q, DsignK, MtK, tile);
+  __syncthreads();
+  v4u kcv[2][LK::CW / 4], ksv[2][LK::SW / 4];
+  float knu[2], kga[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k0 = kbase + 64 * h;
+    const int nv = min(64, ctx - k0);  // may be <= 0: then re-read the last key, never used
+    const int64_t r0 = hrow + (nv > 0 ? k0 : ctx - 1);
+    load_wave_records<NPK, 1>(kcv[h], ksv[h], knu[h], kga[h], kc + r0 * LK::CW, ks + r0 * LK::SW, kn + r0,
+                              kr + r0, nv > 0 ? nv : 1, lane);
+  }
+  // V: lane loads the whole records of keys kbase + 32·(lane/16) + v_key_of_row(lane%16 + 16·reg)
+  v4u vcv[2][NBV], vsv[2];
+#pragma unroll
+  for (int reg = 0; reg < 2; ++reg) {
+    const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
+    const int64_t row = hrow + key;
+#pragma unroll
+    for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
+    vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+  }
+  // ν and γ of V for the scoring layout: key 16t + lane%16 of the wave
+  float vnu[8], vga[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
+    vnu[t] = vn[row];
+    vga[t] = vr[row];
+  }
+
+  // ---- K query operands, then logits of the wave's 128 keys (8 per lane)
+  query_prep_build<NT, NPK, NKB>(sh, pr, PK, tile);
+  float s[8];
+  {
+    v8i a[1][NKB];
+    query_prep_operands<NT, NKB>(sh, a, lane);
+    const float4 cst = query_prep_constants<NT, NPK, NKB>(sh, PK, g);
+    uint32_t* stage = wsc[wv];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float val[4];
+      score_wave_values<NPK, 1>(kcv[h], ksv[h], knu[h], kga[h], stage, stage + kKeysPerWave * LK::CS, a, cst,
+                                PK.qjl_kappa, lane, val);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int key = kbase + 64 * h + 16 * t + kl;
+        s[4 * h + t] = (key < ctx && g < G) ? scale * val[t] : -INFINITY;
+      }
+    }
+  }
+
+  // ---- chunk maximum per head
+  {
+    float m = s[0];
+#pragma unroll
+    for (int t = 1; t < 8; ++t) m = fmaxf(m, s[t]);
+    m = row_max(m);
+    if (kl == 0) hmax[wv][g] = m;
+  }
+  __syncthreads();
+  float mg = hmax[0][g];
+#pragma unroll
+  for (int w = 1; w < kDecWaves; ++w) mg = fmaxf(mg, hmax[w][g]);
+
+  // ---- softmax weights and the V weight operands.
+  // The matrix op aligns the products of each group of 8 contraction
+  // elements to the largest and keeps 13 bits below it (measured on gfx950),
+  // so floating-point limbs of weights that span many octaves lose the small
+  // ones.  Instead u = w ν (MSE) and u = 2 w ν γ (QJL) become 16-bit fixed
+  // point relative to the maximum of their (head, 32-key block): four base-16
+  // digits, each an exact fp8 integer (times the nibble's 1/value), so every
+  // product sum is exact.  The block exponent and the digit weight 16^-l go
+  // into the op's per-block E8M0 scale (row r, keys 32b..32b+31: lane 16b + r).
+  // LW[type][g][key] = the key's four digit bytes; ub = block exponents.
+  uint32_t* LW = wsc[wv];
+  {
+    float u[2][8];
+    float l_sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float w = s[t] == -INFINITY ? 0.f : __expf(s[t] - mg);
+      l_sum += w;
+      u[0][t] = w * vnu[t];
+      u[1][t] = 2.f * u[0][t] * vga[t];
+    }
+    int eb[2][4];
+#pragma unroll
+    for (int ty = 0; ty < 2; ++ty) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {  // block kb = keys 32kb..32kb+31 = tiles 2kb, 2kb+1
+        const float m = row_max(fmaxf(u[ty][2 * kb], u[ty][2 * kb + 1]));
+        int e = 0;
+        if (m > 0.f) (void)frexpf(m, &e);  // m in [2^(e-1), 2^e)
+        eb[ty][kb] = max(e - 1, -100);
+        if (kl == 0) ubexp[wv][ty][g][kb] = eb[ty][kb];
+      }
+    }
+    float w_all = 0.f, w_3 = 0.f, q_n3 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int key = 16 * t + kl;    // within the wave
+      const int r = (key & 31) >> 3;  // FP4 mask index of this key in the B operand
+      const float inv_val = r == 0 ? 2.f : (r == 1 ? 1.f : (r == 2 ? 0.5f : -0.5f));
+#pragma unroll
+      for (int ty = 0; ty < 2; ++ty) {
+        const int e = eb[ty][t >> 1];
+        const float V = fminf(rintf(ldexpf(u[ty][t], 15 - e)), 65535.f);  // 16-bit fixed point
+        const float ut = ldexpf(V, e - 15);                                 // the value the digits carry
+        if (ty == 0) {
+          w_all += ut;
+          if (r == 3) w_3 += ut;
+        } else if (r != 3) {
+          q_n3 += 0.5f * ut;
+        }
+        const float d0 = floorf(V * 0.000244140625f);
+        const float r1 = fmaf(d0, -4096.f, V);
+        const float d1 = floorf(r1 * 0.00390625f);
+        const float r2 = fmaf(d1, -256.f, r1);
+        const float d2 = floorf(r2 * 0.0625f);
+        const float d3 = fmaf(d2, -16.f, r2);
+        uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(d0 * inv_val, d1 * inv_val, 0, false));
+        dw = static_cast<uint32_t>(
+            __builtin_amdgcn_cvt_pk_fp8_f32(d2 * inv_val, d3 * inv_val, static_cast<int>(dw), true));
+        LW[(ty * 4 + g) * kDecKeysPerWave + key] = dw;
+      }
+    }
+    l_sum = row_sum(l_sum);
+    w_all = row_sum(w_all);
+    w_3 = row_sum(w_3);
+    q_n3 = row_sum(q_n3);
+    if (kl == 0) {
+      hsum[wv][g][0] = l_sum;
+      hsum[wv][g][1] = w_all;
+      hsum[wv][g][2] = w_3;
+      hsum[wv][g][3] = q_n3;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // A operands: lane (row 4g'+l, group grp) holds digit l of keys 16grp..+15 and
+  // 64+16grp..+15 (A byte order measured on gfx950); its E8M0 scale serves
+  // row 4g'+l of key block grp: 2^(block exponent - 3 - 4l).
+  v8i av[2];
+  int sav[2];
+  {
+    const int row = lane & 15, grp = lane >> 4, gq = row >> 2, l = row & 3;
+    const uint32_t sel = static_cast<uint32_t>(l) | (static_cast<uint32_t>(4 + l) << 8) | 0x0C0C0000u;
+#pragma unroll
+    for (int ty = 0; ty < 2; ++ty) {
+      const uint32_t* src = LW + (ty * 4 + gq) * kDecKeysPerWave;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key0 = (j < 4 ? 16 * grp + 4 * j : 64 + 16 * grp + 4 * (j - 4));
+        const v4u d4 = *reinterpret_cast<const v4u*>(src + key0);
+        const uint32_t lo = __builtin_amdgcn_perm(d4[1], d4[0], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(d4[3], d4[2], sel);
+        av[ty][j] = static_cast<int>((lo & 0xFFFFu) | (hi << 16));
+      }
+      sav[ty] = 127 + ubexp[wv][ty][gq][grp] - 3 - 4 * l;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- V on the matrix cores: per plane and 16-coordinate block cb,
+  // Σ_k A[row][k] B[k][n] with B the transposed bits of coordinate 16cb + n
+  float macc[8], jacc[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) macc[cb] = jacc[cb] = 0.f;
+  uint32_t par[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) par[cb] = 0u;
+  const v4f zero = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p <= NBV; ++p) {  // stored planes, then the signs
+    uint32_t tw[8];
+#pragma unroll
+    for (int wb = 0; wb < 4; ++wb) {
+      uint32_t r0 = p < NBV ? vcv[0][p < NBV ? p : 0][wb] : vsv[0][wb];
+      uint32_t r1 = p < NBV ? vcv[1][p < NBV ? p : 0][wb] : vsv[1][wb];
+      transpose32(r0, r1, lane);
+      tw[2 * wb] = r0;
+      tw[2 * wb + 1] = r1;
+    }
+    v4f acc[8];
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      acc[cb] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[cb]), zero, p < NBV ? sav[0] : sav[1]);
+    v4f accp[8];
+    if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
+      if (p == NBV - 1) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) accp[cb] = mfma_fp8_fp4_scaled(av[0], fp4_operand(par[cb] ^ tw[cb]), zero, sav[0]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) asm volatile("" : "+v"(acc[cb]));
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      const float v = (acc[cb][0] + acc[cb][1]) + (acc[cb][2] + acc[cb][3]);  // digit weights are in the scales
+      if (p < NBV) {
+        macc[cb] = fmaf(PV.plane_coef[p < NBV ? p : 0], v, macc[cb]);
+        par[cb] ^= tw[cb];
+      } else {
+        jacc[cb] = v;
+      }
+    }
+    if constexpr (NPV > NBV) {
+      if (p == NBV - 1) {
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          asm volatile("" : "+v"(accp[cb]));
+          const float v = (accp[cb][0] + accp[cb][1]) + (accp[cb][2] + accp[cb][3]);
+          macc[cb] = fmaf(PV.plane_coef[NPV - 1], v, macc[cb]);
+        }
+      }
+    }
+  }
+
+  // ---- chunk partials: sum the 8 waves, add the per-head constant terms
+  __syncthreads();  // every wave is done with its scratch
+  {
+    float* red = reinterpret_cast<float*>(wsc[wv]);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) {
+      red[cb * 64 + lane] = macc[cb];
+      red[(8 + cb) * 64 + lane] = jacc[cb];
+    }
+  }
+  __syncthreads();
+  float csum = 0.f;
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) csum += PV.plane_coef[k];
+  for (int e = threadIdx.x; e < 16 * 64; e += NT) {
+    const int slot = e >> 6, L = e & 63, gh = L >> 4;
+    if (gh >= G) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) v += reinterpret_cast<const float*>(wsc[w])[e];
+    float l_sum = 0.f, w_all = 0.f, w_3 = 0.f, q_n3 = 0.f, m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      l_sum += hsum[w][gh][0];
+      w_all += hsum[w][gh][1];
+      w_3 += hsum[w][gh][2];
+      q_n3 += hsum[w][gh][3];
+      m = fmaxf(m, hmax[w][gh]);
+    }
+    const bool is_m = slot < 8;
+    const int j = 16 * (slot & 7) + (L & 15);
+    v += is_m ? PV.plane_bias * w_all + 0.5f * csum * w_3 : -q_n3;
+    float* out = part + ((static_cast<int64_t>(bk) * n_chunks + chunk) * G + gh) * (2 + 2 * kPrepD);
+    out[2 + (is_m ? 0 : kPrepD) + j] = v;
+    if (e == gh * 16) {  // one thread per head writes the max and the weight sum
+      out[0] = m;
+      out[1] = l_sum;
+    }
+  }
+}
+
+// d = 128 for K and V (QJL dimension 128), at most 4 query heads per KV head.
+bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
+  const char* v = std::getenv("TQ_DECODE_KERNEL");
+  if (v && std::string(v) == "valu") return false;
+  const int G = n_q_heads / n_kv_heads;
+  return ck->prm.d == 128 && cv->prm.d == 128 && ck->prm.m == 128 && cv->prm.m == 128 && G <= 4;
+}
+
+int decode_mfma_chunk() { return kDecChunk; }
+
+hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
+                              int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
+                              float* part, int n_chunks, hipStream_t s) {
+  auto go = [&]<int NPK, int NPV, typename T>(const T* qq) -> hipError_t {
+    hipLaunchKernelGGL((decode_mfma_kernel<NPK, NPV, T>), dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
+                       0, s, qq, ck->prm, cv->prm, ck->dD, ck->dMt, n_q_heads, n_kv_heads, static_cast<int>(ctx),
+                       n_chunks, scale, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm, part);
+    return hipGetLastError();
+  };
+  auto by_v = [&]<int NPK, typename T>(const T* qq) -> hipError_t {
+    switch (cv->prm.n_planes) {
+      case 1: return go.template operator()<NPK, 1>(qq);
+      case 2: return go.template operator()<NPK, 2>(qq);
+      case 4: return go.template operator()<NPK, 4>(qq);
+    }
+    return hipErrorInvalidValue;
+  };
+  auto by_k = [&]<typename T>(const T* qq) -> hipError_t {
+    switch (ck->prm.n_planes) {
+      case 1: return by_v.template operator()<1>(qq);
+      case 2: return by_v.template operator()<2>(qq);
+      case 4: return by_v.template operator()<4>(qq);
+    }
+    return hipErrorInvalidValue;
+  };
+  switch (q_dt) {
+    case TQ_F32: return by_k(static_cast<const float*>(q));
+    case TQ_BF16: return by_k(static_cast<const __hip_bfloat16*>(q));
+    case TQ_F16: return by_k(static_cast<const __half*>(q));
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tq

@@ -33,55 +33,9 @@
 #include <cstdlib>
 #include <string>
 
-#include "kernels_common.h"
+#include "mfma_common.h"
 
 namespace tq {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // 16-byte record piece (a plain vector, kept in VGPRs)
-
-namespace {
-
-constexpr int kOpBytes = 64 * 32;  // one K-block of A for one M-tile: 64 lanes x 32 bytes
-// Per M-tile after the operands: float[4][4] (scale_m, scale_q, bias_m, bias_q)
-// per query vector, then int32[4] output rows ((b*Hq + h)*nq + qi, or -1 for
-// a padding slot), padded to 128 bytes.
-constexpr int kConstBytes = 128;
-constexpr int kKeysPerTile = 16;
-
-__device__ __forceinline__ v4f mfma_fp8_fp4(const v8i& a, const v8i& b, const v4f& c) {
-  // cbsz = 0: A is fp8 e4m3; blgp = 4: B is fp4 e2m1; E8M0 scales 127 = 2^0.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, 127, 0, 127);
-}
-
-__device__ __forceinline__ v8i fp4_operand(uint32_t w) {
-  v8i b;
-  b[0] = static_cast<int>(w & 0x11111111u);                 // 0 or 0.5
-  b[1] = static_cast<int>(w & 0x22222222u);                 // 0 or 1
-  b[2] = static_cast<int>(w & 0x44444444u);                 // 0 or 2
-  b[3] = static_cast<int>((w & 0x88888888u) | 0x22222222u);  // +1 (bit 0) or -1 (bit 1)
-  b[4] = b[5] = b[6] = b[7] = 0;
-  return b;
-}
-
-// fp32 -> fp8 (e4m3, hardware round to nearest even) and back.
-__device__ __forceinline__ uint32_t to_fp8(float x) {
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false)) & 0xFFu;
-}
-__device__ __forceinline__ float from_fp8(uint32_t byte) {
-  return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(byte), 0);
-}
-
-// Power-of-two scale 2^E with sigma * 2^E < 256 (E = 8 - exponent of sigma).
-__device__ __forceinline__ int limb_exponent(float sigma) {
-  if (!(sigma > 0.f)) return 0;
-  int k;
-  (void)frexpf(sigma, &k);
-  return 8 - k;
-}
-
-}  // namespace
 
 // ----------------------------------------------------------------------------
 // Query prep: one block (4 waves) per (batch*kv_head, M-tile of 4 query vectors).
@@ -249,132 +203,6 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
 }
 
 // ----------------------------------------------------------------------------
-// Records and scoring, shared by the two logits kernels.
-//
-// Each wave scores 64 consecutive keys (4 tiles of 16) of one (batch, kv head).
-// Memory: the wave's records are contiguous in each array (64 rows), so they
-// are read with fully coalesced 16-byte loads (one instruction covers 1 KB),
-// staged in the wave's own LDS slice, and read back in the MFMA lane layout
-// (lane L: word L/16 of key L%16 of a tile).  Rows are padded by 4 words in
-// LDS to spread the reads over the banks.  The wave's 64 norms ν and γ are
-// loaded one per lane and moved to the owning lane with a cross-lane read.
-// Reading the words in the MFMA layout straight from global memory touches
-// every cache line from several instructions and costs ~1.7x the time.
-// ----------------------------------------------------------------------------
-constexpr int kKeysPerWave = 64;
-
-template <int NP, int WB>
-struct RecLayout {
-  static constexpr int W = 4 * WB;            // words per plane (d/32)
-  static constexpr int NB = NP > 3 ? 3 : NP;  // stored planes (the parity plane is computed)
-  static constexpr int CW = NB * W;           // code words per key
-  static constexpr int SW = W;                // sign words per key
-  static constexpr int CS = CW + 4, SS = SW + 4;  // LDS row strides (words)
-  static constexpr int NKB = (NP + 1) * WB;   // K-blocks: MSE planes x word blocks, then QJL word blocks
-};
-
-// Issue the wave's record loads (pointers at the wave's first row): 16 B per
-// lane per instruction; rows past the end of the context re-read the last
-// valid row (branch-free, always in bounds) and are never stored.
-// cv, sv: the wave's code and sign words as 16-byte pieces; nu, ga: ν and γ of
-// key `lane`.
-template <int NP, int WB, int NC, int NS>
-__device__ __forceinline__ void load_wave_records(v4u (&cv)[NC], v4u (&sv)[NS], float& nu, float& ga,
-                                                  const uint32_t* __restrict__ codes,
-                                                  const uint32_t* __restrict__ signs,
-                                                  const float* __restrict__ norm,
-                                                  const float* __restrict__ rnorm, int nvalid, int lane) {
-  using L = RecLayout<NP, WB>;
-  static_assert(NC == L::CW / 4 && NS == L::SW / 4, "record pieces");
-#pragma unroll
-  for (int i = 0; i < L::CW / 4; ++i) {
-    const int w = 4 * (i * 64 + lane);
-    const int kk = min(w / L::CW, nvalid - 1);
-    cv[i] = reinterpret_cast<const v4u*>(codes)[(kk * L::CW + w % L::CW) / 4];
-  }
-#pragma unroll
-  for (int i = 0; i < L::SW / 4; ++i) {
-    const int w = 4 * (i * 64 + lane);
-    const int kk = min(w / L::SW, nvalid - 1);
-    sv[i] = reinterpret_cast<const v4u*>(signs)[(kk * L::SW + w % L::SW) / 4];
-  }
-  const int ln = min(lane, nvalid - 1);
-  nu = norm[ln];
-  ga = rnorm[ln];
-}
-
-// Scatter the records into the wave's LDS slice, then score the 64 keys
-// against NMT M-tiles: a = A operands, cst = (scale_m, scale_q, bias_m,
-// bias_q) of query vector `lane/16` per tile, out = its logits row at the
-// wave's first key (nullptr: padding slot, not stored).
-template <int NP, int WB, int NMT, int NC, int NS, int NKB>
-__device__ __forceinline__ void score_wave(const v4u (&cv)[NC], const v4u (&sv)[NS], float nu_l, float ga_l,
-                                           uint32_t* __restrict__ s_codes,
-                                           uint32_t* __restrict__ s_signs, const v8i (&a)[NMT][NKB],
-                                           const float4 (&cst)[NMT], float* const (&out)[NMT], int nvalid,
-                                           float kappa, int lane) {
-  using L = RecLayout<NP, WB>;
-  const int g = lane >> 4, kl = lane & 15;
-#pragma unroll
-  for (int i = 0; i < L::CW / 4; ++i) {
-    const int w = 4 * (i * 64 + lane);
-    *reinterpret_cast<v4u*>(&s_codes[(w / L::CW) * L::CS + w % L::CW]) = cv[i];
-  }
-#pragma unroll
-  for (int i = 0; i < L::SW / 4; ++i) {
-    const int w = 4 * (i * 64 + lane);
-    *reinterpret_cast<v4u*>(&s_signs[(w / L::SW) * L::SS + w % L::SW]) = sv[i];
-  }
-  // the wave reads back only what it wrote: LDS ops of one wave complete in
-  // order; the barrier keeps the compiler from moving the reads above the writes
-  __builtin_amdgcn_wave_barrier();
-
-#pragma unroll
-  for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) {
-    const int kk = t * kKeysPerTile + kl;
-    const uint32_t* crow = &s_codes[kk * L::CS];
-    const uint32_t* srow = &s_signs[kk * L::SS];
-    const float nu = __shfl(nu_l, kk, kWave), ga = __shfl(ga_l, kk, kWave);
-    v4f acc_m[NMT], acc_q[NMT];
-#pragma unroll
-    for (int i = 0; i < NMT; ++i) {
-      acc_m[i] = v4f{0.f, 0.f, 0.f, 0.f};
-      acc_q[i] = v4f{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int wb = 0; wb < WB; ++wb) {
-      uint32_t pw[L::NB];
-#pragma unroll
-      for (int p = 0; p < L::NB; ++p) pw[p] = crow[p * L::W + 4 * wb + g];
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        constexpr int NB = L::NB;
-        const uint32_t w = (p < NB) ? pw[p < NB ? p : 0] : (pw[0] ^ pw[NB > 1 ? 1 : 0] ^ pw[NB > 2 ? 2 : 0]);
-        const v8i bop = fp4_operand(w);
-#pragma unroll
-        for (int i = 0; i < NMT; ++i) acc_m[i] = mfma_fp8_fp4(a[i][p * WB + wb], bop, acc_m[i]);
-      }
-      const v8i bop = fp4_operand(srow[4 * wb + g]);
-#pragma unroll
-      for (int i = 0; i < NMT; ++i) acc_q[i] = mfma_fp8_fp4(a[i][NP * WB + wb], bop, acc_q[i]);
-    }
-    // An MFMA reads operands from all 64 lanes, so it must run with the full
-    // EXEC mask: pin every accumulator here, in wave-uniform control flow, so
-    // the compiler cannot sink the matrix ops into the lane-divergent stores.
-#pragma unroll
-    for (int i = 0; i < NMT; ++i) asm volatile("" : "+v"(acc_m[i]), "+v"(acc_q[i]));
-#pragma unroll
-    for (int i = 0; i < NMT; ++i) {
-      const float mse = cst[i].x * (acc_m[i][0] + acc_m[i][1] * 0.0625f + acc_m[i][2] * 0.00390625f +
-                                    acc_m[i][3] * 0.000244140625f) + cst[i].z;
-      const float qj = cst[i].y * (acc_q[i][0] + acc_q[i][1] * 0.0625f + acc_q[i][2] * 0.00390625f +
-                                   acc_q[i][3] * 0.000244140625f) + cst[i].w;
-      if (out[i] != nullptr && kk < nvalid) out[i][kk] = nu * (mse + kappa * ga * qj);
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
 // Logits from prepared query operands: each wave scores its 64 keys against
 // NMT M-tiles of its query group, operands and constants read from `prep`.
 // ----------------------------------------------------------------------------
@@ -425,88 +253,34 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
   score_wave<NP, WB, NMT>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, out, nvalid, kappa, lane);
 }
 
-// Wave-wide sum / max of non-negative values through DPP (no LDS round
-// trips): butterflies inside quads, half-row and row mirrors, then the
-// row broadcasts; the total lands in lane 63 and is read back as a scalar.
-#define TQ_DPP_F(x, ctrl, rmask) \
-  __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), (ctrl), (rmask), 0xF, false))
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += TQ_DPP_F(v, 0xB1, 0xF);   // quad_perm [1,0,3,2]
-  v += TQ_DPP_F(v, 0x4E, 0xF);   // quad_perm [2,3,0,1]
-  v += TQ_DPP_F(v, 0x141, 0xF);  // row_half_mirror
-  v += TQ_DPP_F(v, 0x140, 0xF);  // row_mirror
-  v += TQ_DPP_F(v, 0x142, 0xA);  // row_bcast:15 into rows 1, 3
-  v += TQ_DPP_F(v, 0x143, 0xC);  // row_bcast:31 into rows 2, 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {  // v >= 0
-  v = fmaxf(v, TQ_DPP_F(v, 0xB1, 0xF));
-  v = fmaxf(v, TQ_DPP_F(v, 0x4E, 0xF));
-  v = fmaxf(v, TQ_DPP_F(v, 0x141, 0xF));
-  v = fmaxf(v, TQ_DPP_F(v, 0x140, 0xF));
-  v = fmaxf(v, TQ_DPP_F(v, 0x142, 0xA));
-  v = fmaxf(v, TQ_DPP_F(v, 0x143, 0xC));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-}
-#undef TQ_DPP_F
-
 // ----------------------------------------------------------------------------
 // Fused logits (d = 128, one M-tile of 4 query vectors per KV head): every
 // block rebuilds the query operands of its (batch, kv head) in LDS while its
-// records are in flight, so a decode step is one launch.
-//
-// Because the fp8 limbs are floating point, the power-of-two operand scales
-// need only upper bounds of the operands, not their maxima: with
-// β = √d max_k |q_k| >= ||q||, |q'_j| <= β (R is orthogonal) and
-// |p_i| <= max_i ||M_i|| β (Cauchy-Schwarz), so one max over the raw query
-// replaces the reductions over q' and p.  The two constant
-// sums of q' come from the Hadamard matrix's row sums: Σ_j q'_j = √d D_0 q_0
-// and Σ_{j≡3 mod 4} q'_j = (√d/4)(D_0q_0 - D_1q_1 - D_2q_2 + D_3q_3).  Each
-// thread then cuts the limbs of its own (vector, coordinate).
+// records are in flight (query_prep_*), so a decode step is one launch.
 // ----------------------------------------------------------------------------
 template <int NP, int WAVES, typename T>
 __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
-    const T* q, DevParams P, const float* Dsign, const float* Mt, int Hq,
-    int nq, int G, int nkv, int ctx, const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs,
-    const float* __restrict__ norm, const float* __restrict__ rnorm, float* __restrict__ logits) {
+    const T* q, DevParams P, const float* Dsign, const float* Mt, int Hq, int nq, int G, int nkv, int ctx,
+    const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs, const float* __restrict__ norm,
+    const float* __restrict__ rnorm, float* __restrict__ logits) {
   using L = RecLayout<NP, 1>;
-  constexpr int d = 128, NT = WAVES * 64, PARTS = NT / d, JP = d / PARTS, NKB = L::NKB;
-  static_assert(NT >= 4 * d, "one thread per (query vector, coordinate) of the tile");
+  constexpr int NT = WAVES * 64, NKB = L::NKB;
   __shared__ uint32_t s_codes[WAVES][kKeysPerWave * L::CS];
   __shared__ uint32_t s_signs[WAVES][kKeysPerWave * L::SS];
-  __shared__ float qr[4][d];         // q
-  __shared__ float qs[4][d];         // D ⊙ q, then q' = R q
-  __shared__ float pp[PARTS][4][d];  // partial sums of p = M q over slices of j
-  __shared__ float qmx[4][2];        // max |q_k| per vector, per half
-  __shared__ float dq4[4][4];        // (D ⊙ q)_0..3 per vector
-  __shared__ float psum[4][2][2];    // Σ p and Σ_{i%4=3} p per vector, per half
-  __shared__ __attribute__((aligned(16))) uint8_t opst[NKB * kOpBytes];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int bk = blockIdx.y, mt = blockIdx.z;
-  const int b = bk / nkv, kh = bk % nkv, Gq = nq * G;
+  __shared__ QueryPrepShared<NT, NKB> sh;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int bk = blockIdx.y;
+  const QueryTile tile{bk / nkv, nq, Hq, G, bk % nkv, static_cast<int>(blockIdx.z), nq * G};
   const int key0 = (blockIdx.x * WAVES + wv) * kKeysPerWave;
   const bool active = key0 < ctx;  // wave-uniform; idle waves still help with the operands
   const int nvalid = active ? min(kKeysPerWave, ctx - key0) : 0;
 
-  // Operand-side loads go out first, all unconditional.  Loads complete in
-  // issue order as far as the wait counter is concerned, so the operand math
-  // below waits for these while the record loads issued after them are still
-  // in flight.  p_i = Σ_j M_ij q_j: thread (part, i) sums its slice of j for
-  // all four vectors.
-  const int pi = tid & (d - 1), part = tid / d;
-  float mv[JP];
-#pragma unroll
-  for (int u = 0; u < JP; ++u) mv[u] = Mt[(part * JP + u) * d + pi];
-  // the thread's (vector, coordinate) of the tile; threads past 4d repeat vector 3
-  const int lv = min(tid / d, 3), qv = mt * 4 + lv, qc = min(qv, Gq - 1);
-  const float qraw =
-      load_elem(q + ((static_cast<int64_t>(b) * nq + qc / G) * Hq + kh * G + qc % G) * d, pi);
-  const float dx = Dsign[pi];
   // The vector memory path returns data in request order, so an operand load
   // queued behind record loads (HBM misses) would wait for them: every wave's
   // operand loads are queued before any wave issues its records.  The barrier
-  // waits for no data; q, D and M are not declared __restrict__ so that their
-  // loads are not sunk below it.
+  // waits for no data.
+  QueryPrepRegs<NT> pr;
+  query_prep_load<NT>(pr, q, Dsign, Mt, tile);
   __syncthreads();
   // Records: every wave loads (an idle wave re-reads the last key and never
   // uses it), so no branch sits around the loads.
@@ -518,105 +292,16 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
     load_wave_records<NP, 1>(cv, sv, nu_l, ga_l, codes + row0 * L::CW, signs + row0 * L::SW, norm + row0,
                              rnorm + row0, active ? nvalid : 1, lane);
   }
-  const float qx = qv < Gq ? qraw : 0.f;
-  if (NT == 4 * d || tid < 4 * d) {
-    qr[lv][pi] = qx;
-    qs[lv][pi] = qx * dx;
-    if (pi < 4) dq4[lv][pi] = qx * dx;
-    const float mx = wave_max_dpp(fabsf(qx));
-    if (lane == 0) qmx[lv][(tid >> 6) & 1] = mx;
-  }
-  __syncthreads();
-
-  // q' = H (D ⊙ q)/√d in place by waves 0..3 (one vector each); p partial sums by all
-  if (wv < 4) {
-    float v[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) v[e] = qs[wv][e * kWave + lane];
-    hadamard_wave<2>(v, lane);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) qs[wv][e * kWave + lane] = v[e] * P.inv_sqrt_d;
-  }
-  {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < JP; ++u) {
-#pragma unroll
-      for (int vq = 0; vq < 4; ++vq) acc[vq] = fmaf(mv[u], qr[vq][part * JP + u], acc[vq]);
-    }
-#pragma unroll
-    for (int vq = 0; vq < 4; ++vq) pp[part][vq][pi] = acc[vq];
-  }
-  float cmax = 0.f, csum = 0.f;
-#pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    cmax = fmaxf(cmax, fabsf(P.plane_coef[k]));
-    csum += P.plane_coef[k];
-  }
-  __syncthreads();
-
-  // Limbs of the thread's own (vector lv, coordinate pi): the MSE planes from
-  // q'_pi and the QJL block from p_pi.  Coordinate j of K-block kbi sits at
-  // bit 4i+v of word wi (j = 32wi + 4i + v), contraction index kk = 32wi + 8v + i
-  // (the B nibble order), held by A lane group (kk%64)/16 at byte
-  // kk%16 + 16(kk/64) (the A byte order measured on gfx950).
-  if (NT == 4 * d || tid < 4 * d) {
-    const float beta = fmaxf(qmx[lv][0], qmx[lv][1]) * (sqrtf(static_cast<float>(d)) * 1.001f);
-    const int em = limb_exponent(2.f * cmax * beta);
-    const int eq = limb_exponent(4.f * P.mrow_bound * beta);
-    float pv = 0.f;
-#pragma unroll
-    for (int u = 0; u < PARTS; ++u) pv += pp[u][lv][pi];
-    const int wi = pi >> 5, i8 = (pi & 31) >> 2, vb = pi & 3;
-    const int kk = 32 * wi + 8 * vb + i8;
-    const int slot = (16 * ((kk & 63) >> 4) + 4 * lv) * 32 + (kk & 15) + 16 * (kk >> 6);
-    const float inv_val = vb == 0 ? 2.f : (vb == 1 ? 1.f : (vb == 2 ? 0.5f : -0.5f));
-    const float qp = qs[lv][pi];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float kappa = kb < NP ? P.plane_coef[kb < NP ? kb : 0] : 2.f;
-      float R = ldexpf(kappa * (kb < NP ? qp : pv) * inv_val, kb < NP ? em : eq);
-#pragma unroll
-      for (int l = 0; l < 4; ++l) {
-        const uint32_t bl = to_fp8(R);
-        opst[kb * kOpBytes + slot + 32 * l] = static_cast<uint8_t>(bl);
-        R = (R - from_fp8(bl)) * 16.f;
-      }
-    }
-    const float s_all = wave_sum_dpp(pv);
-    const float s_3 = wave_sum_dpp(vb == 3 ? pv : 0.f);
-    if (lane == 0) {
-      psum[lv][(tid >> 6) & 1][0] = s_all;
-      psum[lv][(tid >> 6) & 1][1] = s_3;
-    }
-  }
-  __syncthreads();
+  query_prep_build<NT, NP, NKB>(sh, pr, P, tile);
   if (!active) return;  // wave-uniform
 
-  // A operands of the wave's lanes and the constants of query vector g = lane/16
   const int g = lane >> 4;
   v8i a[1][NKB];
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const uint4* src = reinterpret_cast<const uint4*>(opst + kb * kOpBytes + lane * 32);
-    const uint4 x = src[0], y = src[1];
-    a[0][kb][0] = x.x; a[0][kb][1] = x.y; a[0][kb][2] = x.z; a[0][kb][3] = x.w;
-    a[0][kb][4] = y.x; a[0][kb][5] = y.y; a[0][kb][6] = y.z; a[0][kb][7] = y.w;
-  }
-  float4 cst[1];
-  {
-    const float sq = sqrtf(static_cast<float>(d));
-    const float beta = fmaxf(qmx[g][0], qmx[g][1]) * (sq * 1.001f);
-    const float s_all = sq * dq4[g][0];                                     // Σ_j q'_j
-    const float s_3 = 0.25f * sq * (dq4[g][0] - dq4[g][1] - dq4[g][2] + dq4[g][3]);  // Σ_{j%4=3} q'_j
-    const float p_all = psum[g][0][0] + psum[g][1][0], p_3 = psum[g][0][1] + psum[g][1][1];
-    // slots with j%4 = 3 hold -x/2 against the +-1 nibble: add the x/2 back
-    cst[0] = float4{ldexpf(1.f, -limb_exponent(2.f * cmax * beta)), ldexpf(1.f, -limb_exponent(4.f * P.mrow_bound * beta)),
-                    P.plane_bias * s_all + 0.5f * csum * s_3, -p_all + p_3};
-  }
-  const int qvg = mt * 4 + g;
-  float* const out[1] = {qvg < Gq ? logits + (static_cast<int64_t>(b * Hq + kh * G + qvg % G) * nq + qvg / G) * ctx + key0
-                                  : nullptr};
+  query_prep_operands<NT, NKB>(sh, a, lane);
+  const float4 cst[1] = {query_prep_constants<NT, NP, NKB>(sh, P, g)};
+  const int qvg = tile.mt * 4 + g;
+  float* const out[1] = {qvg < tile.Gq ? logits + (static_cast<int64_t>(tile.b * Hq + tile.kh * G + qvg % G) * nq + qvg / G) * ctx + key0
+                                       : nullptr};
   score_wave<NP, 1, 1>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, out, nvalid, P.qjl_kappa, lane);
 }
 
