@@ -51,7 +51,7 @@ def parse():
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc"))):
-        if f.startswith("kernels_logits"):
+        if f.startswith("kernels_logits") or f == "mfma_common.h" or f == "kernels_common.h":
             h.update(open(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

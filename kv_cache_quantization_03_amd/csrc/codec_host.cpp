@@ -283,7 +283,8 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
     return TQ_ERROR_HIP;
   }
   const size_t nS = static_cast<size_t>(h.m) * h.d;
-  const size_t bytes = (2 * nS + h.d) * sizeof(float);
+  const bool with16 = h.d == 128 && h.m == 128;  // the fused encode's fp16 split of S
+  const size_t bytes = (2 * nS + h.d) * sizeof(float) + (with16 ? 2 * nS * sizeof(_Float16) : 0);
   hipError_t e = hipMalloc(&c->dev_block, bytes);
   if (e != hipSuccess) {
     set_error(std::string("hipMalloc of codec tables failed: ") + hipGetErrorString(e));
@@ -294,6 +295,7 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
   c->dS = static_cast<float*>(c->dev_block);
   c->dMt = c->dS + nS;
   c->dD = c->dMt + nS;
+  c->dS16 = with16 ? reinterpret_cast<_Float16*>(c->dD + h.d) : nullptr;
   // M = S R, row by row in fp64: M[i][j] = (Hᵀ S[i,:])[j] D[j] / sqrt(d); stored transposed.
   std::vector<float> Mt(nS);
   {
@@ -320,6 +322,17 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
   e = hipMemcpy(c->dS, h.S.data(), nS * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->dMt, Mt.data(), nS * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->dD, h.D.data(), h.d * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess && with16) {
+    // S = hi + lo: hi = fp16(S) (round to nearest even), lo = fp16(S - hi)
+    std::vector<_Float16> s16(2 * nS);
+    for (size_t i = 0; i < nS; ++i) {
+      const float sv = h.S[i];
+      const _Float16 hi = static_cast<_Float16>(sv);
+      s16[i] = hi;
+      s16[nS + i] = static_cast<_Float16>(sv - static_cast<float>(hi));
+    }
+    e = hipMemcpy(c->dS16, s16.data(), 2 * nS * sizeof(_Float16), hipMemcpyHostToDevice);
+  }
   if (e != hipSuccess) {
     set_error(std::string("uploading codec tables failed: ") + hipGetErrorString(e));
     (void)hipFree(c->dev_block);

@@ -38,6 +38,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Value of lane (lane ^ 2^K) within rows of 16 lanes, through DPP.
+template <int K>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  const int v = static_cast<int>(x);
+  if constexpr (K == 0) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  if constexpr (K == 1) return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  if constexpr (K == 2) {  // quad reverse (i^3), then half-row mirror (i^7): i^4
+    const int y = __builtin_amdgcn_update_dpp(0, v, 0x1B, 0xF, 0xF, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, y, 0x141, 0xF, 0xF, false));
+  }
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));  // row_ror:8 = i^8
+}
+
+__device__ __forceinline__ float lane_xor_f(float x, int k) {
+  switch (k) {
+    case 0: return __uint_as_float(lane_xor<0>(__float_as_uint(x)));
+    case 1: return __uint_as_float(lane_xor<1>(__float_as_uint(x)));
+    case 2: return __uint_as_float(lane_xor<2>(__float_as_uint(x)));
+    default: return __uint_as_float(lane_xor<3>(__float_as_uint(x)));
+  }
+}
+
+// Max / sum over the 16 lanes of each row (all 16 lanes get the result).
+__device__ __forceinline__ float row_max(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v = fmaxf(v, lane_xor_f(v, k));
+  return v;
+}
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v += lane_xor_f(v, k);
+  return v;
+}
+
 // Unnormalised Walsh–Hadamard transform along the 64 lanes (bits 0..5 of j):
 // butterfly partner = lane ^ mask; lower lane keeps a+b, upper keeps a-b.
 template <int E>

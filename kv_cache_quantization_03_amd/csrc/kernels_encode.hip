@@ -6,6 +6,9 @@
 // (random-sign Walsh–Hadamard rotation) and 第四部分 (the rotation must be
 // computed in high precision: here fp32 throughout); 「TurboQuant 学习路径」
 // 二.4 (bit-packing into 32-bit words).
+#include <cstdlib>
+#include <string>
+
 #include "kernels_common.h"
 
 namespace tq {
@@ -173,7 +176,185 @@ __global__ __launch_bounds__(256) void sproj_kernel(const float* __restrict__ A,
   }
 }
 
+// ----------------------------------------------------------------------------
+// Fused encode for d = m = 128: rotate, quantize, pack and the QJL signs in
+// one pass, with S·r on the matrix cores.
+//
+// * 16 lanes per vector, lane l holding coordinates 8l..8l+7 (one 16-byte
+//   load of a bf16/fp16 row): the Walsh-Hadamard butterflies of coordinate
+//   bits 0-2 run between registers, bits 3-6 between lanes through DPP.
+// * The residual r (scaled by 2^6) goes to LDS as an fp16 pair hi + lo; with
+//   S = S_hi + S_lo prepared in fp16 at codec creation, z = S r is
+//   S_hi r_hi + S_hi r_lo + S_lo r_hi on v_mfma_f32_16x16x32_f16, whose sums
+//   keep fp32 precision (measured), so z carries ~1e-7 absolute error
+//   against the 1e-5 band the sign decisions are held to.
+// * A block encodes 16 vectors per pass; wave w owns outputs 32w..32w+31 of
+//   z and keeps its fp16 rows of S in registers for all passes.
+// ----------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int kEncPasses = 8;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load8(const __hip_bfloat16* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8(const __half* p, float (&v)[8]) {
+  const h8 a = *reinterpret_cast<const h8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(a[i]);
+}
+
+template <typename T, int B>
+__global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__ x, int64_t n, DevParams P,
+                                                           const float* __restrict__ Dsign,
+                                                           const _Float16* __restrict__ S16,
+                                                           uint32_t* __restrict__ codes, uint32_t* __restrict__ signs,
+                                                           float* __restrict__ norm, float* __restrict__ rnorm) {
+  constexpr int d = 128, NL = 1 << B;
+  __shared__ __attribute__((aligned(16))) _Float16 rh[2][16][d + 8];  // r hi / lo of the pass's 16 vectors
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l = lane & 15;
+  const int vrow = 4 * wv + (lane >> 4);  // the lane's vector within the pass
+  // fp16 S rows of this wave's outputs: A fragments [row block][K step][hi, lo]
+  h8 sf[2][4][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        sf[rb][ks][hl] = *reinterpret_cast<const h8*>(S16 + hl * d * d + (32 * wv + 16 * rb + l) * d + 32 * ks +
+                                                      8 * (lane >> 4));
+  float dsg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dsg[e] = Dsign[8 * l + e];
+
+  for (int pass = 0; pass < kEncPasses; ++pass) {
+    const int64_t tile0 = (static_cast<int64_t>(blockIdx.x) * kEncPasses + pass) * 16;
+    if (tile0 >= n) break;  // block-uniform
+    const int64_t vec = tile0 + vrow;
+    const bool valid = vec < n;
+    float v[8];
+    load8(x + (valid ? vec : n - 1) * d + 8 * l, v);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
+    const float nu = sqrtf(row_sum(ss));
+    const float inv = nu > 0.f ? 1.0f / nu : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= inv * dsg[e];
+    // y = H (D ⊙ x/ν)/√d: coordinate bits 0-2 in registers, 3-6 across lanes
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e & h) continue;
+        const float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool upper = (l >> k) & 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float o = lane_xor_f(v[e], k);
+        v[e] = upper ? (o - v[e]) : (v[e] + o);
+      }
+    }
+    // quantize (idx = #{k : t_k < y}, ties low), residual, bit planes
+    uint32_t bits[B];
+#pragma unroll
+    for (int p = 0; p < B; ++p) bits[p] = 0u;
+    float rr[8], rs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = v[e] * P.inv_sqrt_d;
+      int c = 0;
+      float yh = P.cent[0];
+#pragma unroll
+      for (int k = 0; k < NL - 1; ++k) {
+        const bool gt = P.bound[k] < y;
+        c += gt;
+        yh = gt ? P.cent[k + 1] : yh;
+      }
+#pragma unroll
+      for (int p = 0; p < B; ++p) bits[p] |= static_cast<uint32_t>((c >> p) & 1) << e;
+      rr[e] = y - yh;
+      rs = fmaf(rr[e], rr[e], rs);
+    }
+    rs = row_sum(rs);
+    // code word w (coordinates 32w..32w+31) of plane p from lanes 4w..4w+3
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      uint32_t word = bits[p] << (8 * (l & 3));
+      word |= lane_xor<0>(word);
+      word |= lane_xor<1>(word);
+      if (valid && (l & 3) == 0) codes[vec * (B * 4) + 4 * p + (l >> 2)] = word;
+    }
+    if (valid && l == 0) {
+      norm[vec] = nu;
+      rnorm[vec] = sqrtf(rs);
+    }
+    h8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float rsc = rr[e] * 64.f;
+      hi[e] = static_cast<_Float16>(rsc);
+      lo[e] = static_cast<_Float16>(rsc - static_cast<float>(hi[e]));
+    }
+    *reinterpret_cast<h8*>(&rh[0][vrow][8 * l]) = hi;
+    *reinterpret_cast<h8*>(&rh[1][vrow][8 * l]) = lo;
+    __syncthreads();
+    // z = S r: rows = this wave's outputs, columns = the pass's 16 vectors
+    f4v acc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const h8 bh = *reinterpret_cast<const h8*>(&rh[0][l][32 * ks + 8 * (lane >> 4)]);
+      const h8 bl = *reinterpret_cast<const h8*>(&rh[1][l][32 * ks + 8 * (lane >> 4)]);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[rb][ks][0], bh, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[rb][ks][0], bl, acc[rb], 0, 0, 0);
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[rb][ks][1], bh, acc[rb], 0, 0, 0);
+      }
+    }
+    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));  // matrix ops stay in wave-uniform flow
+    // sign bits [z >= 0]: lane (g, v) holds outputs 32w + 16rb + 4g + r of vector v
+    uint32_t part = 0u;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part |= static_cast<uint32_t>(acc[rb][r] >= 0.f) << (16 * rb + 4 * (lane >> 4) + r);
+    part |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(part), 16, kWave));
+    part |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(part), 32, kWave));
+    if (lane < 16 && tile0 + lane < n) signs[(tile0 + lane) * 4 + wv] = part;
+    __syncthreads();  // the next pass rewrites rh
+  }
+}
+
+bool encode_fused_eligible(const tq_codec_s* c) {
+  const char* v = std::getenv("TQ_ENCODE_KERNEL");
+  if (v && std::string(v) == "split") return false;
+  return c->prm.d == 128 && c->prm.m == 128 && c->dS16 != nullptr;
+}
+
 size_t encode_ws_bytes(const tq_codec_s* c, int64_t n) {
+  if (encode_fused_eligible(c)) return 0;  // the fused kernel keeps r on chip
   return static_cast<size_t>(n) * c->prm.d * sizeof(float);
 }
 
@@ -182,6 +363,20 @@ template <typename T>
 hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t out, float* ws_r,
                         hipStream_t s) {
   const DevParams& P = c->prm;
+  if (encode_fused_eligible(c)) {
+    const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * kEncPasses)));
+    auto go = [&]<int B>() -> hipError_t {
+      hipLaunchKernelGGL((encode_fused_kernel<T, B>), grid, dim3(256), 0, s, x, n, P, c->dD, c->dS16, out.codes,
+                         out.signs, out.norm, out.rnorm);
+      return hipGetLastError();
+    };
+    switch (P.b) {
+      case 1: return go.template operator()<1>();
+      case 2: return go.template operator()<2>();
+      case 3: return go.template operator()<3>();
+    }
+    return hipErrorInvalidValue;
+  }
   auto run = [&]<int E>() -> hipError_t {
     hipLaunchKernelGGL((encode_rq_kernel<E, T>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0, s,
                        x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r);

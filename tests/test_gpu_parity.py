@@ -81,6 +81,25 @@ def test_encode_parity(B, d, bits, dtype):
     say("  mismatches", st["code_mismatch"], st["sign_mismatch"])
 
 
+@pytest.mark.parametrize("bits,dtype,n", [(2, "f32", 1), (3, "bf16", 15), (4, "f16", 17), (3, "f32", 127),
+                                         (2, "bf16", 129), (4, "bf16", 2049), (3, "bf16", 5000)])
+def test_encode_fused_and_split_kernels(B, bits, dtype, n, monkeypatch):
+    # d = 128 takes the fused kernel (S·r on the matrix cores); the split path
+    # (fp32 rotation kernel, then the fp32 S-projection GEMM) is the other
+    # implementation: both must pass the encode bar against the oracle
+    say(f"encode fused vs split bits={bits} {dtype} n={n}")
+    gc, oc = pair(B, 128, bits)
+    x = rand_keys(n, 128, seed=n + bits, dtype=dtype)
+    kf, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
+    monkeypatch.setenv("TQ_ENCODE_KERNEL", "split")
+    ks, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
+    monkeypatch.delenv("TQ_ENCODE_KERNEL")
+    torch.cuda.synchronize()
+    sf = check_encode(oc, x.astype(np.float64), kf.numpy(), "fused")
+    ss = check_encode(oc, x.astype(np.float64), ks.numpy(), "split")
+    say(f"  fused mismatches {sf['code_mismatch']}/{sf['sign_mismatch']}, split {ss['code_mismatch']}/{ss['sign_mismatch']}")
+
+
 def test_encode_k_and_v_together(B):
     gc, oc = pair(B, 128, 3)
     k = rand_keys(777, 128, 1, "bf16")
