@@ -141,16 +141,24 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
   }
 }
 
+// Combine: one block of 1024 threads per (batch, q head).  Every loop that
+// reads chunk partials is spread over the threads (the chunk loads are
+// independent), so the kernel is not a chain of dependent L2 round trips.
+constexpr int kCombThreads = 1024;
+
 template <int E>
-__global__ __launch_bounds__(kAttnThreads) void decode_combine_kernel(DevParams PV, const float* __restrict__ part,
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams PV, const float* __restrict__ part,
                                                                       int Hq, int nkv, int n_chunks,
                                                                       const float* __restrict__ S,
                                                                       const float* __restrict__ Dsign, void* out,
                                                                       int out_bf16) {
   constexpr int d = E * kWave;
+  constexpr int NW = kCombThreads / kWave;
   __shared__ float Jsh[d];
   __shared__ float osh[d];
-  __shared__ float wsh[1024];
+  __shared__ float wsh[1024];           // chunk weights exp(m_c - max)
+  __shared__ float red[NW];
+  __shared__ float acc_sh[4][256];     // partial sums (d = m = 128 paths below)
   const int G = Hq / nkv;
   const int bh = blockIdx.x;  // b*Hq + h
   const int b = bh / Hq, h = bh % Hq;
@@ -158,33 +166,86 @@ __global__ __launch_bounds__(kAttnThreads) void decode_combine_kernel(DevParams 
   const int bk = b * nkv + kh;
   const int m = PV.m;
   const int rec = 2 + d + m;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const float* base = part + (static_cast<int64_t>(bk) * n_chunks * G + g) * rec;
   const int64_t cstride = static_cast<int64_t>(G) * rec;
-  // global max, chunk weights
+  // global max over chunks
   float gm = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) gm = fmaxf(gm, base[c * cstride]);
+  for (int c = tid; c < n_chunks; c += kCombThreads) gm = fmaxf(gm, base[c * cstride]);
+  gm = wave_max(gm);
+  if (lane == 0) red[wv] = gm;
+  __syncthreads();
+  gm = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) gm = fmaxf(gm, red[w]);
+  __syncthreads();
+  // chunk weights and the total weight
+  float lt = 0.f;
+  for (int c = tid; c < n_chunks; c += kCombThreads) {
+    const float wc = __expf(base[c * cstride] - gm);
+    wsh[c] = wc;
+    lt = fmaf(wc, base[c * cstride + 1], lt);
+  }
+  lt = wave_sum(lt);
+  if (lane == 0) red[wv] = lt;
+  __syncthreads();
   float ltot = 0.f;
-  for (int c = threadIdx.x; c < n_chunks; c += kAttnThreads) wsh[c] = __expf(base[c * cstride] - gm);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; ++c) ltot += wsh[c] * base[c * cstride + 1];
-  for (int j = threadIdx.x; j < d + m; j += kAttnThreads) {
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ltot += red[w];
+  // M and J: value j = tid % (d + m) over a quarter of the chunks each
+  const int nv = d + m;
+  if (nv <= 2 * 128 && d == 128) {
+    const int j = tid & 255, qtr = tid >> 8;
     float a = 0.f;
-    for (int c = 0; c < n_chunks; ++c) a = fmaf(wsh[c], base[c * cstride + 2 + j], a);
-    if (j < d)
-      osh[j] = a;
-    else
-      Jsh[j - d] = a;
+#pragma unroll 8
+    for (int c = qtr; c < n_chunks; c += 4) a = fmaf(wsh[c], base[c * cstride + 2 + j], a);
+    acc_sh[qtr][j] = a;
+    __syncthreads();
+    if (tid < nv) {
+      const float v = acc_sh[0][tid] + acc_sh[1][tid] + acc_sh[2][tid] + acc_sh[3][tid];
+      if (tid < d)
+        osh[tid] = v;
+      else
+        Jsh[tid - d] = v;
+    }
+  } else {
+    for (int j = tid; j < nv; j += kCombThreads) {
+      float a = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < n_chunks; ++c) a = fmaf(wsh[c], base[c * cstride + 2 + j], a);
+      if (j < d)
+        osh[j] = a;
+      else
+        Jsh[j - d] = a;
+    }
   }
   __syncthreads();
+  // o' = (M + κ Sᵀ J)/l: coordinate j over four slices of i
   const float inv_l = 1.0f / ltot;
-  for (int j = threadIdx.x; j < d; j += kAttnThreads) {
+  if (d == 128) {
+    const int j = tid & 127, part4 = tid >> 7;  // 8 slices of i
+    const int i0 = part4 * (m / 8), i1 = i0 + m / 8;
     float a = 0.f;
-    for (int i = 0; i < m; ++i) a = fmaf(S[static_cast<int64_t>(i) * d + j], Jsh[i], a);
-    osh[j] = (osh[j] + PV.qjl_kappa * a) * inv_l;
+#pragma unroll 8
+    for (int i = i0; i < i1; ++i) a = fmaf(S[static_cast<int64_t>(i) * d + j], Jsh[i], a);
+    reinterpret_cast<float*>(acc_sh)[part4 * 128 + j] = a;
+    __syncthreads();
+    if (tid < d) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t += reinterpret_cast<float*>(acc_sh)[q * 128 + tid];
+      osh[tid] = (osh[tid] + PV.qjl_kappa * t) * inv_l;
+    }
+  } else {
+    for (int j = tid; j < d; j += kCombThreads) {
+      float a = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < m; ++i) a = fmaf(S[static_cast<int64_t>(i) * d + j], Jsh[i], a);
+      osh[j] = (osh[j] + PV.qjl_kappa * a) * inv_l;
+    }
   }
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
+  if (tid < kWave) {
     float v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = osh[e * kWave + lane];
@@ -252,7 +313,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto run = [&]<int E>() -> hipError_t {
-    hipLaunchKernelGGL((decode_combine_kernel<E>), dim3(batch * n_q_heads), dim3(kAttnThreads), 0, s, cv->prm,
+    hipLaunchKernelGGL((decode_combine_kernel<E>), dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm,
                        part, n_q_heads, n_kv_heads, n_chunks, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);
     return hipGetLastError();
   };

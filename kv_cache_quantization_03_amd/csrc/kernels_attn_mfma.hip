@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
   const int64_t hrow = static_cast<int64_t>(bk) * ctx;         // first row of the head
 
-  // ---- loads: query operands first (see query_prep_load), then K and V records
+  // ---- loads: query operands first (see query_prep_load), then the K records
   QueryPrepRegs<NT> pr;
   query_prep_load<NT>(pr, q, DsignK, MtK, tile);
   __syncthreads();
@@ -112,24 +112,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     const int64_t r0 = hrow + (nv > 0 ? k0 : ctx - 1);
     load_wave_records<NPK, 1>(kcv[h], ksv[h], knu[h], kga[h], kc + r0 * LK::CW, ks + r0 * LK::SW, kn + r0,
                               kr + r0, nv > 0 ? nv : 1, lane);
-  }
-  // V: lane loads the whole records of keys kbase + 32·(lane/16) + v_key_of_row(lane%16 + 16·reg)
-  v4u vcv[2][NBV], vsv[2];
-#pragma unroll
-  for (int reg = 0; reg < 2; ++reg) {
-    const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
-    const int64_t row = hrow + key;
-#pragma unroll
-    for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
-    vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
-  }
-  // ν and γ of V for the scoring layout: key 16t + lane%16 of the wave
-  float vnu[8], vga[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
-    vnu[t] = vn[row];
-    vga[t] = vr[row];
   }
 
   // ---- K query operands, then logits of the wave's 128 keys (8 per lane)
@@ -151,6 +133,27 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
         s[4 * h + t] = (key < ctx && g < G) ? scale * val[t] : -INFINITY;
       }
     }
+  }
+
+  // V: lane loads the whole records of keys kbase + 32·(lane/16) + v_key_of_row(lane%16 + 16·reg).
+  // Issued only now: held through the query prep they push the kernel past 128
+  // registers, and then a CU runs one 8-wave block instead of two.
+  v4u vcv[2][NBV], vsv[2];
+#pragma unroll
+  for (int reg = 0; reg < 2; ++reg) {
+    const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
+    const int64_t row = hrow + key;
+#pragma unroll
+    for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
+    vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+  }
+  // ν and γ of V for the scoring layout: key 16t + lane%16 of the wave
+  float vnu[8], vga[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
+    vnu[t] = vn[row];
+    vga[t] = vr[row];
   }
 
   // ---- chunk maximum per head
@@ -284,36 +287,42 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
       tw[2 * wb] = r0;
       tw[2 * wb + 1] = r1;
     }
-    v4f acc[8];
+    // two halves of four 16-coordinate blocks keep the live accumulators at 8 registers
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-      acc[cb] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[cb]), zero, p < NBV ? sav[0] : sav[1]);
-    v4f accp[8];
-    if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
-      if (p == NBV - 1) {
+    for (int hb = 0; hb < 2; ++hb) {
+      v4f acc[4], accp[4];
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) accp[cb] = mfma_fp8_fp4_scaled(av[0], fp4_operand(par[cb] ^ tw[cb]), zero, sav[0]);
+      for (int c = 0; c < 4; ++c)
+        acc[c] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[4 * hb + c]), zero,
+                                     p < NBV ? sav[0] : sav[1]);
+      if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
+        if (p == NBV - 1) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            accp[c] = mfma_fp8_fp4_scaled(av[0], fp4_operand(par[4 * hb + c] ^ tw[4 * hb + c]), zero, sav[0]);
+        }
       }
-    }
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) asm volatile("" : "+v"(acc[cb]));
+      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(acc[c]));
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      const float v = (acc[cb][0] + acc[cb][1]) + (acc[cb][2] + acc[cb][3]);  // digit weights are in the scales
-      if (p < NBV) {
-        macc[cb] = fmaf(PV.plane_coef[p < NBV ? p : 0], v, macc[cb]);
-        par[cb] ^= tw[cb];
-      } else {
-        jacc[cb] = v;
+      for (int c = 0; c < 4; ++c) {
+        const int cb = 4 * hb + c;
+        const float v = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);  // digit weights are in the scales
+        if (p < NBV) {
+          macc[cb] = fmaf(PV.plane_coef[p < NBV ? p : 0], v, macc[cb]);
+          par[cb] ^= tw[cb];
+        } else {
+          jacc[cb] = v;
+        }
       }
-    }
-    if constexpr (NPV > NBV) {
-      if (p == NBV - 1) {
+      if constexpr (NPV > NBV) {
+        if (p == NBV - 1) {
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          asm volatile("" : "+v"(accp[cb]));
-          const float v = (accp[cb][0] + accp[cb][1]) + (accp[cb][2] + accp[cb][3]);
-          macc[cb] = fmaf(PV.plane_coef[NPV - 1], v, macc[cb]);
+          for (int c = 0; c < 4; ++c) {
+            asm volatile("" : "+v"(accp[c]));
+            const float v = (accp[c][0] + accp[c][1]) + (accp[c][2] + accp[c][3]);
+            macc[4 * hb + c] = fmaf(PV.plane_coef[NPV - 1], v, macc[4 * hb + c]);
+          }
         }
       }
     }
