@@ -11,6 +11,12 @@ namespace tq {
 
 hipError_t launch_scores(const tq_codec_s* c, const float* qrot, const float* proj, int nq, tq_packed_t db,
                          int64_t n, float* scores, hipStream_t s);
+bool search_mfma_eligible(const tq_codec_s* c);
+size_t search_mfma_prep_bytes(const tq_codec_s* c, int nq);
+hipError_t launch_search_mfma_prep(const tq_codec_s* c, const float* qrot, const float* proj, int nq, void* prep,
+                                   hipStream_t s);
+hipError_t launch_search_mfma_scores(const tq_codec_s* c, const void* prep, int nq, tq_packed_t db, int64_t n,
+                                     float* scores, int64_t ld, hipStream_t s);
 
 namespace {
 constexpr int64_t kSearchChunk = 65536;
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(const float* __r
 namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct SearchLayout {
-  size_t qrot, proj, scores, cand_idx, cand_score, total;
+  size_t qrot, proj, prep, scores, cand_idx, cand_score, total;
 };
 SearchLayout search_layout(const tq_codec_s* c, int64_t n_db, int nq, int topk) {
   const int64_t chunk = std::min<int64_t>(kSearchChunk, n_db);
@@ -157,7 +163,8 @@ SearchLayout search_layout(const tq_codec_s* c, int64_t n_db, int nq, int topk) 
   SearchLayout L{};
   L.qrot = 0;
   L.proj = align256(L.qrot + static_cast<size_t>(nq) * c->prm.d * sizeof(float));
-  L.scores = align256(L.proj + static_cast<size_t>(nq) * c->prm.m * sizeof(float));
+  L.prep = align256(L.proj + static_cast<size_t>(nq) * c->prm.m * sizeof(float));
+  L.scores = L.prep + (search_mfma_eligible(c) ? search_mfma_prep_bytes(c, nq) : 0);
   L.cand_idx = align256(L.scores + static_cast<size_t>(nq) * chunk * sizeof(float));
   L.cand_score = align256(L.cand_idx + static_cast<size_t>(nq) * n_chunks * topk * sizeof(int64_t));
   L.total = align256(L.cand_score + static_cast<size_t>(nq) * n_chunks * topk * sizeof(float));
@@ -181,13 +188,17 @@ hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, cons
   float* scores = reinterpret_cast<float*>(w + SL.scores);
   int64_t* cand_idx = reinterpret_cast<int64_t*>(w + SL.cand_idx);
   float* cand_score = reinterpret_cast<float*>(w + SL.cand_score);
+  const bool mfma = search_mfma_eligible(c);
   hipError_t e = launch_qprep(c, queries, TQ_F32, nq, qrot, proj, s);
   if (e != hipSuccess) return e;
+  if (mfma && (e = launch_search_mfma_prep(c, qrot, proj, nq, w + SL.prep, s)) != hipSuccess) return e;
   for (int64_t ci = 0; ci < n_chunks; ++ci) {
     const int64_t lo = ci * chunk;
     const int64_t len = std::min<int64_t>(chunk, n_db - lo);
     tq_packed_t sub{db.codes + lo * P.code_words, db.signs + lo * P.sign_words, db.norm + lo, db.rnorm + lo};
-    if ((e = launch_scores(c, qrot, proj, nq, sub, len, scores, s)) != hipSuccess) return e;
+    e = mfma ? launch_search_mfma_scores(c, w + SL.prep, nq, sub, len, scores, len, s)
+             : launch_scores(c, qrot, proj, nq, sub, len, scores, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_rows_kernel, dim3(nq), dim3(kSelThreads), 0, s, scores, static_cast<const int64_t*>(nullptr),
                        len, len, lo, topk, cand_score + ci * topk, cand_idx + ci * topk,
                        static_cast<int64_t>(n_chunks * topk));
