@@ -153,6 +153,194 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(const float* __r
 }
 
 namespace {
+constexpr int kTopThreads = 1024;
+constexpr int kTopCap = 4096;  // candidates sorted in LDS
+constexpr int kTopVPT = static_cast<int>(kSearchChunk / kTopThreads);  // scores per thread
+
+// The want-th smallest (1-based) of the values val(i) with ok(i), over the
+// VPT slots of every thread of the block, by 8-bit radix passes
+// from the top.  Returns T and need = want - #(values < T) (>= 1).  Every
+// thread of the block calls it; hist[257] and sel[2] are LDS scratch.
+template <int PASSES, int VPT, typename V, typename OK>
+__device__ __forceinline__ void block_radix_select(V val, OK ok, uint32_t want, uint32_t* hist, uint32_t* sel,
+                                                   uint32_t& T, uint32_t& need) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t prefix = 0, mask = 0;
+  need = want;
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int shift = 8 * (PASSES - 1 - pass);
+    if (tid <= 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = 0; i < VPT; ++i) {  // values outside the prefix count in bin 256
+      const uint32_t v = val(i);
+      const bool in = ok(i) && (v & mask) == prefix;
+      atomicAdd(&hist[in ? (v >> shift) & 255u : 256u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {  // wave 0: lane l scans bins 4l..4l+3
+      uint32_t h[4], sum = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        h[b] = hist[4 * lane + b];
+        sum += h[b];
+      }
+      uint32_t inc = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += y;
+      }
+      uint32_t cum = inc - sum;
+      if (cum < need && need <= inc) {  // exactly one lane
+        int b = 0;
+        while (cum + h[b] < need) cum += h[b++];
+        sel[0] = 4 * lane + b;
+        sel[1] = cum;
+      }
+    }
+    __syncthreads();
+    prefix |= sel[0] << shift;
+    need -= sel[1];
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  T = prefix;
+}
+}  // namespace
+
+// Top-k of one row of up to kSearchChunk scores per block, the row held in
+// registers (one read of the scores).  Row r: src[r*len + pos]; global index
+// idx_base + pos.  Writes the k best (score desc, index asc) to
+// out_score/out_idx[r*out_stride ...]; when len < k the tail is (-inf, INT64_MAX).
+//
+// Candidates first: every thread's best key is a real score, so the k-th best
+// of those 1024 bests, T0, has at least k scores at or above it and every
+// member of the top k scores at least T0.  The scores at or above T0 (about
+// 64k of them for k << 1024) go to LDS and are sorted there by (score desc,
+// position asc).  When more than kTopCap pass (massive ties), the block falls
+// back to an exact radix selection that re-reads the row.
+__global__ __launch_bounds__(kTopThreads) void topk_regs_kernel(const float* __restrict__ src, int64_t len,
+                                                                int64_t idx_base, int k,
+                                                                float* __restrict__ out_score,
+                                                                int64_t* __restrict__ out_idx, int64_t out_stride) {
+  __shared__ uint32_t hist[257];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t ck[kTopCap];
+  __shared__ uint32_t cpos[kTopCap];
+  __shared__ uint32_t cnt;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  // buffer loads: one VGPR offset for all kTopVPT loads (the slot stride goes in
+  // the scalar offset), and reads past the row's end return 0
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(src + static_cast<int64_t>(r) * len), 0, static_cast<int>(len * sizeof(float)), 0x00020000);
+  const int nslot = static_cast<int>((len - tid + kTopThreads - 1) / kTopThreads);  // slots of this thread in the row
+  // 0xFFFFFFFF marks an empty slot; a real score never maps there (a NaN that
+  // would is moved one step up)
+  auto load_key = [&](int i) {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(rsrc, tid * 4, i * kTopThreads * 4, 0);
+    return min(desc_key(__uint_as_float(u)), 0xFFFFFFFEu) | (i < nslot ? 0u : 0xFFFFFFFFu);
+  };
+  uint32_t key[kTopVPT];
+#pragma unroll
+  for (int i = 0; i < kTopVPT; ++i) key[i] = load_key(i);
+  const uint32_t kk = static_cast<uint32_t>(min<int64_t>(k, len));
+  uint32_t total = 0;
+  if (kk > 0) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < kTopVPT; ++i) best = min(best, key[i]);
+    uint32_t T0, need0;  // at least kk threads hold a key (kk <= min(len, kTopThreads))
+    block_radix_select<4, 1>([&](int) { return best; }, [&](int) { return best != 0xFFFFFFFFu; }, kk, hist, sel,
+                             T0, need0);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < kTopVPT; ++i) c += key[i] <= T0 ? 1u : 0u;
+    if (tid == 0) cnt = 0;
+    __syncthreads();
+    c = static_cast<uint32_t>(wave_sum(static_cast<float>(c)));  // exact: counts < 2^24
+    if (lane == 0 && c) atomicAdd(&cnt, c);
+    __syncthreads();
+    total = cnt;
+    __syncthreads();
+    if (tid == 0) cnt = 0;
+    __syncthreads();
+    if (total <= kTopCap) {
+#pragma unroll
+      for (int i = 0; i < kTopVPT; ++i) {
+        if (key[i] <= T0) {
+          const uint32_t slot = atomicAdd(&cnt, 1u);
+          ck[slot] = key[i];
+          cpos[slot] = static_cast<uint32_t>(i * kTopThreads + tid);
+        }
+      }
+    } else {
+      // exact radix selection over the row, re-read from memory (no register copy
+      // of the row is kept live through this path)
+      asm volatile("" ::: "memory");
+      uint32_t T, need;
+      block_radix_select<4, kTopVPT>(load_key, [&](int i) { return i < nslot; }, kk, hist, sel, T, need);
+      if (tid <= 256) hist[tid] = 0;
+      __syncthreads();
+      uint32_t my_eq = 0;
+      for (int i = 0; i < nslot; ++i) my_eq += load_key(i) == T ? 1u : 0u;
+      if (my_eq) atomicAdd(&hist[0], my_eq);
+      __syncthreads();
+      const uint32_t total_eq = hist[0];
+      __syncthreads();  // hist is reused below
+      uint32_t pos_cut = 0xFFFFFFFFu;  // keys equal to T with position <= pos_cut are taken
+      if (total_eq > need) {
+        uint32_t Tp, needp;
+        block_radix_select<3, kTopVPT>([&](int i) { return static_cast<uint32_t>(i * kTopThreads + tid); },
+                                       [&](int i) { return i < nslot && load_key(i) == T; }, need, hist, sel, Tp,
+                                       needp);
+        pos_cut = Tp;
+      }
+      for (int i = 0; i < nslot; ++i) {
+        const uint32_t kx = load_key(i), pos = static_cast<uint32_t>(i * kTopThreads + tid);
+        if (kx < T || (kx == T && pos <= pos_cut)) {
+          const uint32_t slot = atomicAdd(&cnt, 1u);
+          ck[slot] = kx;
+          cpos[slot] = pos;
+        }
+      }
+      total = kk;
+    }
+  }
+  // sort the candidates by (key, position) and write the first kk
+  int P2 = 1;
+  while (P2 < static_cast<int>(max<uint32_t>(total, static_cast<uint32_t>(k)))) P2 <<= 1;
+  __syncthreads();
+  for (int i = static_cast<int>(total) + tid; i < P2; i += kTopThreads) {
+    ck[i] = 0xFFFFFFFFu;
+    cpos[i] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P2; i += kTopThreads) {
+        const int jx = i ^ stride;
+        if (jx > i) {
+          const bool up = (i & size) == 0;
+          const uint32_t ka = ck[i], kb = ck[jx], pa = cpos[i], pb = cpos[jx];
+          const bool a_gt_b = (ka > kb) || (ka == kb && pa > pb);
+          if (a_gt_b == up) {
+            ck[i] = kb; ck[jx] = ka;
+            cpos[i] = pb; cpos[jx] = pa;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += kTopThreads) {
+    const int64_t o = static_cast<int64_t>(r) * out_stride + i;
+    const bool real = i < static_cast<int>(kk);
+    out_score[o] = real ? key_to_score(ck[i]) : -INFINITY;
+    out_idx[o] = real ? idx_base + cpos[i] : INT64_MAX;
+  }
+}
+
+namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 struct SearchLayout {
   size_t qrot, proj, prep, scores, cand_idx, cand_score, total;
@@ -199,9 +387,8 @@ hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, cons
     e = mfma ? launch_search_mfma_scores(c, w + SL.prep, nq, sub, len, scores, len, s)
              : launch_scores(c, qrot, proj, nq, sub, len, scores, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(nq), dim3(kSelThreads), 0, s, scores, static_cast<const int64_t*>(nullptr),
-                       len, len, lo, topk, cand_score + ci * topk, cand_idx + ci * topk,
-                       static_cast<int64_t>(n_chunks * topk));
+    hipLaunchKernelGGL(topk_regs_kernel, dim3(nq), dim3(kTopThreads), 0, s, scores, len, lo, topk,
+                       cand_score + ci * topk, cand_idx + ci * topk, static_cast<int64_t>(n_chunks * topk));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(topk_rows_kernel, dim3(nq), dim3(kSelThreads), 0, s, cand_score, cand_idx,

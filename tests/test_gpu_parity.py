@@ -394,6 +394,39 @@ def test_search_parity(B, d, bits, n_db, nq, k):
         assert row.index(4) < row.index(10) < row.index(n_db - 1)
 
 
+@pytest.mark.parametrize("bits,k", [(4, 10), (3, 100)])
+def test_search_massive_ties(B, bits, k):
+    """A database of 70001 copies of one record, with two better records among
+    them: the first 65536-record chunk has far more equal scores than the
+    candidate buffer of the per-chunk selection holds, so its exact fallback
+    runs; ties go to the lower index."""
+    say(f"search massive ties bits={bits} k={k}")
+    d, n_db = 128, 70001
+    gc, oc = pair(B, d, bits)
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, d))
+    x0 = rng.standard_normal((1, d))
+    x0 -= (x0 @ q.T) / (q @ q.T) * q        # orthogonal to the query
+    pair_rec = O.encode(oc, np.vstack([x0, q]).astype(np.float32).astype(np.float64))
+    rec = {key: np.repeat(v[:1], n_db, axis=0) for key, v in pair_rec.items()}
+    for pos in (5000, 66000):
+        for key in rec:
+            rec[key][pos] = pair_rec[key][1]
+    qs = q.astype(np.float32)
+    idx, sc = B.tq_search_topk(gc, B.packed_from_numpy(rec), torch.from_numpy(qs).cuda(), k)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy()[0], sc.cpu().numpy()[0]
+    # (the oracle's BLAS products may round equal records apart by an ulp, so
+    # the expected order is stated, not taken from its sort)
+    _, _, full = O.search_topk(oc, rec, qs.astype(np.float64), k)
+    rest = np.delete(full[0], [5000, 66000])
+    assert np.max(np.abs(rest - full[0, 0])) <= 1e-12 * abs(full[0, 0])
+    assert full[0, 5000] > full[0, 0] and full[0, 66000] > full[0, 0]
+    assert idx[:2].tolist() == [5000, 66000] and idx[2:].tolist() == list(range(k - 2))
+    assert len(set(sc[2:].tolist())) == 1          # identical records score identically
+    assert np.allclose(sc, full[0, idx], rtol=0, atol=1e-4 * np.max(np.abs(full[0])))
+
+
 # ---------------------------------------------------------------- argument checks with a real codec
 def test_invalid_arguments_rejected(B):
     gc, _ = pair(B, 128, 3)
