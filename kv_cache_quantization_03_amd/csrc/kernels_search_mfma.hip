@@ -13,16 +13,17 @@
 //   kernel: the word's bits 4j+v become nibble j of operand dword v with value
 //   0 or 0.5, 1, 2 (v = 0, 1, 2), and ±1 (v = 3).
 // * A operands are the queries in fixed point.  Per (query, 32-coordinate
-//   block) with |a| < 2^E, a is rounded to a 16-bit integer times 2^(E-16)
-//   and split into four base-16 digits with the sign.  A digit times the
-//   nibble compensation (2, 1, 1/2, -1/2) is an exact e4m3 number, and the
-//   digit's weight 16^(3-l) 2^(E-16) is the op's E8M0 block scale (the scale of
-//   lane 16b + r covers row r, contraction elements 32b..32b+31).  Every product
-//   is then a multiple of 1/2 below 16, so the op's group sums are exact and
-//   the only error is the 2^-17 rounding of the digits, relative to the block
+//   block) with |a| < 2^E, a is rounded to a B-bit integer times 2^(E-B) and
+//   split into B/4 base-16 digits with the sign (B = 16 for q'; B = 12 for p,
+//   whose term carries the factor √(π/2)/m).  A digit times the nibble
+//   compensation (2, 1, 1/2, -1/2) is an exact e4m3 number, and the digit's
+//   weight 16^(B/4-1-l) 2^(E-B) is the op's E8M0 block scale (the scale of lane
+//   16b + r covers row r, contraction elements 32b..32b+31).  Every product is
+//   then a multiple of 1/2 below 16, so the op's group sums are exact and the
+//   only error is the 2^-(B+1) rounding of the digits, relative to the block
 //   maximum.  (Sums of eight products are aligned to their maximum and cut 13
 //   bits below it on gfx950, so floating-point limbs would lose more; twelve
-//   bits of digits leave errors of 1e-4 of the score for Gaussian queries.)
+//   bits of q' leave errors of 1e-4 of the score for Gaussian queries.)
 // * Every code plane multiplies the same query digits, so one accumulator per
 //   plane keeps one A operand set per contraction step; the plane weights of the
 //   codebook expansion c(idx) = bias + Σ_P coef_P plane_P(idx) are applied with
@@ -32,8 +33,8 @@
 //   τ = 2·bit - 1 into one constant per query and estimator part.
 //
 // Work split.  The digits of one 16-query tile for every contraction step
-// (d/128 steps x 4 digits x 2 KiB = 96 KiB at d = 1536) stay in LDS for a
-// block of 4096 records.  q' and p together would not fit the 160 KiB of LDS,
+// (d/128 steps x 4 digits x 2 KiB = 96 KiB for q' at d = 1536) stay in LDS for
+// a block of 4096 records.  q' and p together would not fit the 160 KiB of LDS,
 // so the MSE part and the QJL part are two launches of one kernel: the first
 // writes ν(Σ q'c) and the second adds ν κ γ Σ p τ.  Each of the 8 waves takes
 // a few record tiles of 16 at a time and streams their plane words with 8- or
@@ -44,30 +45,37 @@
 namespace tq {
 
 namespace {
-constexpr int kSDig = 4;            // base-16 digits per query value (16 bits)
+constexpr int kDigQ = 4;            // base-16 digits of q' (16 bits)
+constexpr int kDigP = 3;            // base-16 digits of p (12 bits: the QJL term carries a factor 1/m)
 constexpr int kSWaves = 8;
-constexpr int kSLoadWords = 2;      // plane words per lane and load
+#ifndef TQ_MSE_TILES
+#define TQ_MSE_TILES 4
+#define TQ_MSE_LW 2
+#define TQ_QJL_TILES 4
+#define TQ_QJL_LW 4
+#endif
+// record tiles per wave and plane words per lane and load, per estimator part
+constexpr int kMseTiles = TQ_MSE_TILES, kMseLW = TQ_MSE_LW, kQjlTiles = TQ_QJL_TILES, kQjlLW = TQ_QJL_LW;
 constexpr int kSPrepThreads = 256;
 constexpr int64_t kSPerBlock = 4096;  // records per block
 
-// Prepared operands of query tile qt for vector v (0: q', 1: p):
-// aop[v][qt][s][l][lane][32] fp8 digits, ascl[v][qt][s][l][lane] E8M0 scales,
-// qconst[qt*16 + row][v] the constant of the estimator part.
-template <int NS>
-__global__ __launch_bounds__(kSPrepThreads) void search_prep_kernel(DevParams P, const float* __restrict__ qrot,
-                                                                   const float* __restrict__ proj, int nq, int nqt,
-                                                                   uint8_t* __restrict__ aop,
+// Prepared operands of query tile qt for vector vec (0: q', 1: p) with DIG
+// digits: aop[qt][s][l][lane][32] fp8 digits, ascl[qt][s][l][lane] E8M0
+// scales, qconst[qt*16 + row][vec] the constant of the estimator part.
+template <int NS, int DIG>
+__global__ __launch_bounds__(kSPrepThreads) void search_prep_kernel(DevParams P, const float* __restrict__ src,
+                                                                   int vec, int nq, uint8_t* __restrict__ aop,
                                                                    uint8_t* __restrict__ ascl,
                                                                    float* __restrict__ qconst) {
   constexpr int W = 4 * NS, d = 128 * NS, HW = kSPrepThreads / 32;
-  __shared__ float part[HW][16][2];  // per half-wave and row: Σ_{v=3} â, Σ â
-  const int qt = blockIdx.x, vec = blockIdx.y;
+  __shared__ float part[HW][16][3];  // per half-wave and row: Σ_{v=3} â, Σ â, Σ_{v=3} â without its last digit
+  constexpr int BITS = 4 * DIG;
+  const int qt = blockIdx.x;
   const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
-  for (int i = threadIdx.x; i < HW * 16 * 2; i += kSPrepThreads) (&part[0][0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < HW * 16 * 3; i += kSPrepThreads) (&part[0][0][0])[i] = 0.f;
   __syncthreads();
-  const float* src = vec == 0 ? qrot : proj;
-  uint8_t* A = aop + (static_cast<size_t>(vec) * nqt + qt) * NS * kSDig * kOpBytes;
-  uint8_t* SC = ascl + (static_cast<size_t>(vec) * nqt + qt) * NS * kSDig * 64;
+  uint8_t* A = aop + static_cast<size_t>(qt) * NS * DIG * kOpBytes;
+  uint8_t* SC = ascl + static_cast<size_t>(qt) * NS * DIG * 64;
   const int v = l32 & 3, j = l32 >> 2;  // nibble class and nibble of coordinate bit l32 of the word
   const float comp = v == 0 ? 2.f : (v == 1 ? 1.f : (v == 2 ? 0.5f : -0.5f));
   for (int pi = hw; pi < 16 * W; pi += HW) {  // (row, word) pairs, one per half-wave
@@ -77,13 +85,13 @@ __global__ __launch_bounds__(kSPrepThreads) void search_prep_kernel(DevParams P,
     float mx = fabsf(a);
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    int E = -111;  // keeps every digit scale 2^(E-4-4l) inside E8M0
+    int E = -111;  // keeps every digit scale 2^(E-BITS+4(DIG-1-l)) inside E8M0
     if (mx > 0.f) {
       int e;
       (void)frexpf(mx, &e);  // mx in [2^(e-1), 2^e)
       E = max(e, -111);
     }
-    const float V = fminf(rintf(ldexpf(fabsf(a), 16 - E)), 65535.f);
+    const float V = fminf(rintf(ldexpf(fabsf(a), BITS - E)), static_cast<float>((1 << BITS) - 1));
     const int vi = static_cast<int>(V);
     const float sg = a < 0.f ? -1.f : 1.f;
     const int b = w / NS, s = w % NS;  // word w feeds contraction block b of step s
@@ -91,38 +99,44 @@ __global__ __launch_bounds__(kSPrepThreads) void search_prep_kernel(DevParams P,
     const int lane = 16 * ((k & 63) >> 4) + row;
     const int byte = (k & 15) + 16 * (k >> 6);
 #pragma unroll
-    for (int l = 0; l < kSDig; ++l) {
-      const int dig = (vi >> (4 * (kSDig - 1 - l))) & 15;
+    for (int l = 0; l < DIG; ++l) {
+      const int dig = (vi >> (4 * (DIG - 1 - l))) & 15;
       const float x = sg * static_cast<float>(dig) * comp;
       const int f8 = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
-      A[((static_cast<size_t>(s) * kSDig + l) * 64 + lane) * 32 + byte] = static_cast<uint8_t>(f8 & 0xFF);
-      if (l32 == 0) SC[(s * kSDig + l) * 64 + 16 * b + row] = static_cast<uint8_t>(127 + E - 4 - 4 * l);
+      A[((static_cast<size_t>(s) * DIG + l) * 64 + lane) * 32 + byte] = static_cast<uint8_t>(f8 & 0xFF);
+      if (l32 == 0) SC[(s * DIG + l) * 64 + 16 * b + row] = static_cast<uint8_t>(127 + E - BITS + 4 * (DIG - 1 - l));
     }
-    const float ahat = sg * ldexpf(V, E - 16);  // the value the digits carry
-    float c3 = v == 3 ? ahat : 0.f, sa = ahat;
+    const float ahat = sg * ldexpf(V, E - BITS);  // the value the digits carry
+    const float ahat_t = sg * ldexpf(static_cast<float>(vi & ~15), E - BITS);  // without the last digit
+    float c3 = v == 3 ? ahat : 0.f, sa = ahat, c3t = v == 3 ? ahat_t : 0.f;
 #pragma unroll
     for (int o = 16; o >= 1; o >>= 1) {
       c3 += __shfl_xor(c3, o, 32);
       sa += __shfl_xor(sa, o, 32);
+      c3t += __shfl_xor(c3t, o, 32);
     }
     if (l32 == 0) {
       part[hw][row][0] += c3;
       part[hw][row][1] += sa;
+      part[hw][row][2] += c3t;
     }
   }
   __syncthreads();
   if (threadIdx.x < 16) {
-    float c3 = 0.f, sa = 0.f;
+    float c3 = 0.f, sa = 0.f, c3t = 0.f;
     for (int h = 0; h < HW; ++h) {
       c3 += part[h][threadIdx.x][0];
       sa += part[h][threadIdx.x][1];
+      c3t += part[h][threadIdx.x][2];
     }
     c3 *= 0.5f;  // the ±1 nibbles' offset: true Σ â·bit = op sum + c3
+    c3t *= 0.5f;
     float cst;
     if (vec == 0) {
       float csum = 0.f;
       for (int i = 0; i < P.n_planes; ++i) csum += P.plane_coef[i];
       cst = P.plane_bias * sa + csum * c3;
+      if (P.n_planes == 4) cst += P.plane_coef[3] * (c3t - c3);  // the parity plane drops the last digit
     } else {
       cst = 2.f * c3 - sa;  // Σ p τ = 2 Σ p·bit - Σ p
     }
@@ -150,7 +164,7 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&o)[SG])
 // QJL = false: the NB code planes (+ parity), A = q' digits; writes
 //   scores = ν (const_q + Σ_P coef_P ⟨plane_P, q̂'⟩).
 // QJL = true: the sign plane, A = p digits; adds ν κ γ (2 ⟨bits, p̂⟩ + const_p).
-template <int NS, int NB, bool QJL, int TILES>
+template <int NS, int NB, bool QJL, int TILES, int DIG, int LW>
 __global__ __launch_bounds__(kSWaves * 64) void search_part_kernel(DevParams P, const uint8_t* __restrict__ aop,
                                                                   const uint8_t* __restrict__ ascl,
                                                                   const float* __restrict__ qconst, int nq,
@@ -159,8 +173,8 @@ __global__ __launch_bounds__(kSWaves * 64) void search_part_kernel(DevParams P, 
   constexpr int NW = QJL ? 1 : NB;                   // planes loaded per record
   constexpr int NPL = QJL ? 1 : (NB == 3 ? 4 : NB);  // planes multiplied (+ parity for b = 3)
   constexpr int W = 4 * NS, RW = NW * W;             // words per plane, per record
-  constexpr int SG = NS % kSLoadWords == 0 ? kSLoadWords : 1;  // contraction steps per record load
-  constexpr int ABYTES = NS * kSDig * kOpBytes, SBYTES = NS * kSDig * 64;
+  constexpr int SG = NS % LW == 0 ? LW : 1;  // contraction steps per record load
+  constexpr int ABYTES = NS * DIG * kOpBytes, SBYTES = NS * DIG * 64;
   __shared__ __attribute__((aligned(16))) uint8_t sa[ABYTES];
   __shared__ __attribute__((aligned(16))) uint8_t ss[SBYTES];
   const int qt = blockIdx.x;
@@ -203,12 +217,12 @@ __global__ __launch_bounds__(kSWaves * 64) void search_part_kernel(DevParams P, 
 #pragma unroll
       for (int s1 = 0; s1 < SG; ++s1) {
         const int s = s0 + s1;
-        v8i a[kSDig];
-        int sc[kSDig];
+        v8i a[DIG];
+        int sc[DIG];
 #pragma unroll
-        for (int l = 0; l < kSDig; ++l) {
-          a[l] = *reinterpret_cast<const v8i*>(sa + ((s * kSDig + l) * 64 + lane) * 32);
-          sc[l] = ss[(s * kSDig + l) * 64 + lane];
+        for (int l = 0; l < DIG; ++l) {
+          a[l] = *reinterpret_cast<const v8i*>(sa + ((s * DIG + l) * 64 + lane) * 32);
+          sc[l] = ss[(s * DIG + l) * 64 + lane];
         }
         // plane-major, so only one plane's B operands (one per tile) are live
 #pragma unroll
@@ -219,8 +233,11 @@ __global__ __launch_bounds__(kSWaves * 64) void search_part_kernel(DevParams P, 
             if (NB == 3 && !QJL && pl == 3) w = wd[t][0][s1] ^ wd[t][NW > 1 ? 1 : 0][s1] ^ wd[t][NW - 1][s1];
             else w = wd[t][pl < NW ? pl : 0][s1];
             const v8i bo = fp4_operand(w);
+            // the parity plane's weight is ~1/16 of the largest bit plane's (Lloyd-Max
+            // codebooks are close to uniform), so its last digit is below the others' error
+            const int ND = (!QJL && pl == 3) ? DIG - 1 : DIG;  // pl is unrolled: constant
 #pragma unroll
-            for (int l = 0; l < kSDig; ++l) acc[t][pl] = mfma_fp8_fp4_scaled(a[l], bo, acc[t][pl], sc[l]);
+            for (int l = 0; l < ND; ++l) acc[t][pl] = mfma_fp8_fp4_scaled(a[l], bo, acc[t][pl], sc[l]);
           }
         }
       }
@@ -264,18 +281,17 @@ hipError_t dispatch_ns(int ns, F&& f) {
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct PrepLayout {
-  size_t aop, ascl, qconst, total;
-  size_t op_stride, scl_stride;  // bytes per vector (q' or p)
+  size_t aq, ap, sq, sp, qconst, total;  // q' digits, p digits, their scales, constants
 };
 PrepLayout prep_layout(const tq_codec_s* c, int nq) {
   const size_t nqt = static_cast<size_t>(ceil_div(nq, 16));
   const size_t ns = c->prm.d / 128;
   PrepLayout L{};
-  L.op_stride = nqt * ns * kSDig * kOpBytes;
-  L.scl_stride = nqt * ns * kSDig * 64;
-  L.aop = 0;
-  L.ascl = align256(2 * L.op_stride);
-  L.qconst = L.ascl + align256(2 * L.scl_stride);
+  L.aq = 0;
+  L.ap = L.aq + align256(nqt * ns * kDigQ * kOpBytes);
+  L.sq = L.ap + align256(nqt * ns * kDigP * kOpBytes);
+  L.sp = L.sq + align256(nqt * ns * kDigQ * 64);
+  L.qconst = L.sp + align256(nqt * ns * kDigP * 64);
   L.total = L.qconst + align256(nqt * 16 * 2 * sizeof(float));
   return L;
 }
@@ -299,9 +315,12 @@ hipError_t launch_search_mfma_prep(const tq_codec_s* c, const float* qrot, const
   const int nqt = static_cast<int>(ceil_div(nq, 16));
   const PrepLayout L = prep_layout(c, nq);
   uint8_t* base = static_cast<uint8_t*>(prep);
+  float* qc = reinterpret_cast<float*>(base + L.qconst);
   auto run = [&]<int NS>() -> hipError_t {
-    hipLaunchKernelGGL((search_prep_kernel<NS>), dim3(nqt, 2), dim3(kSPrepThreads), 0, s, P, qrot, proj, nq, nqt,
-                       base + L.aop, base + L.ascl, reinterpret_cast<float*>(base + L.qconst));
+    hipLaunchKernelGGL((search_prep_kernel<NS, kDigQ>), dim3(nqt), dim3(kSPrepThreads), 0, s, P, qrot, 0, nq,
+                       base + L.aq, base + L.sq, qc);
+    hipLaunchKernelGGL((search_prep_kernel<NS, kDigP>), dim3(nqt), dim3(kSPrepThreads), 0, s, P, proj, 1, nq,
+                       base + L.ap, base + L.sp, qc);
     return hipGetLastError();
   };
   return dispatch_ns(P.d / 128, run);
@@ -314,24 +333,20 @@ hipError_t launch_search_mfma_scores(const tq_codec_s* c, const void* prep, int 
   const int nqt = static_cast<int>(ceil_div(nq, 16));
   const PrepLayout L = prep_layout(c, nq);
   const uint8_t* base = static_cast<const uint8_t*>(prep);
-  const uint8_t* aq = base + L.aop;
-  const uint8_t* ap = aq + L.op_stride;
-  const uint8_t* sq = base + L.ascl;
-  const uint8_t* sp = sq + L.scl_stride;
   const float* qc = reinterpret_cast<const float*>(base + L.qconst);
   const dim3 grid(nqt, static_cast<unsigned>(ceil_div(n, kSPerBlock)));
   const dim3 block(kSWaves * 64);
   auto run = [&]<int NS>() -> hipError_t {
     if (P.b == 3)
-      hipLaunchKernelGGL((search_part_kernel<NS, 3, false, 4>), grid, block, 0, s, P, aq, sq, qc, nq, db, n, scores,
-                         ld);
+      hipLaunchKernelGGL((search_part_kernel<NS, 3, false, kMseTiles, kDigQ, kMseLW>), grid, block, 0, s, P, base + L.aq,
+                         base + L.sq, qc, nq, db, n, scores, ld);
     else
-      hipLaunchKernelGGL((search_part_kernel<NS, 2, false, 4>), grid, block, 0, s, P, aq, sq, qc, nq, db, n, scores,
-                         ld);
+      hipLaunchKernelGGL((search_part_kernel<NS, 2, false, kMseTiles, kDigQ, kMseLW>), grid, block, 0, s, P, base + L.aq,
+                         base + L.sq, qc, nq, db, n, scores, ld);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((search_part_kernel<NS, 2, true, 8>), grid, block, 0, s, P, ap, sp, qc, nq, db, n, scores,
-                       ld);
+    hipLaunchKernelGGL((search_part_kernel<NS, 2, true, kQjlTiles, kDigP, kQjlLW>), grid, block, 0, s, P, base + L.ap, base + L.sp,
+                       qc, nq, db, n, scores, ld);
     return hipGetLastError();
   };
   return dispatch_ns(P.d / 128, run);
