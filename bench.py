@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--bits", type=int, default=3)
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--stage-search", action="store_true", help="also time the 1M x 1536 search stage")
+    ap.add_argument("--no-stage-search", action="store_true", help="skip the 1M x 1536 encode and search stages")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a short fixed workload for rocprofv3 --pmc (20 logits launches + calibration copies)")
     return ap.parse_args()
@@ -276,59 +276,96 @@ def _time(fn, n=5, graph=False):
     return a.elapsed_time(b) / n
 
 
+PEAK_FP32_VALU_TFLOPS = 78.6   # fp32 FMA on the vector units, packed fp32 disabled
+PEAK_FP8_TFLOPS = 5000.0       # dense fp8 matrix ops (the f8f6f4 op with an fp8 operand runs at this rate)
+
+
+def _hbm(ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+
 def time_stages(B, I, codec3, dev, args):
-    """One-off timings of the other rows of the path, on synthetic data
-    generated on the GPU (torch, seeded) with the workloads' shapes."""
+    """The other rows of the path, each timed on its own configuration with
+    synthetic data drawn on the GPU (torch, seeded), with the roofline that
+    bounds it: algorithmic bytes (or flops) per call over the measured time."""
     import torch
     res = {}
     g = torch.Generator(device=dev)
     g.manual_seed(7)
-    # 4-bit logits on the same shape
-    c4 = B.tq_codec_create(128, 4, 0, I.CODEC_SEED)
-    k = torch.randn((8 * 32768, 128), generator=g, device=dev).to(torch.bfloat16)
-    q = torch.randn((1, 1, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    d = 128
+    # C2 4-bit: 4-bit logits on the Llama-8B decode shape
+    c4 = B.tq_codec_create(d, 4, 0, I.CODEC_SEED)
+    ctx = 32768
+    k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((1, 1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp4, _ = B.tq_encode_kv(c4, k)
-    lg = torch.empty((1, 32, 1, 32768), device=dev)
+    lg = torch.empty((1, 32, 1, ctx), device=dev)
     wsl = torch.empty(B.tq_attn_logits_workspace(c4, 1, 32, 8, 1), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_attn_logits(c4, q, kp4, 32768, 8, logits=lg, ws=wsl), 200, graph=True)
-    res["logits_4bit_ms"] = ms
-    res["logits_4bit_keys_per_s"] = 32 * 32768 / (ms * 1e-3)
-    print(f"[bench] 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    del k, kp4
-    # fused decode attention, 128K context, K and V 3-bit
+    ms = _time(lambda: B.tq_attn_logits(c4, q, kp4, ctx, 8, logits=lg, ws=wsl), 200, graph=True)
+    res["logits_c2_4bit"] = {"ms": ms, "keys_per_s": 32 * ctx / (ms * 1e-3),
+                             **_hbm(ms, 8 * ctx * c4.record_bytes + 32 * ctx * 4 + 32 * d * 2)}
+    print(f"[bench] C2 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del k, kp4, lg
+    # C4: fused decode attention, 128K context, K and V 3-bit
     ctx = 131072
-    k = torch.randn((8 * ctx, 128), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((8 * ctx, 128), generator=g, device=dev).to(torch.bfloat16)
-    qd = torch.randn((1, 32, 128), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    qd = torch.randn((1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp, vp = B.tq_encode_kv(codec3, k, v)
-    out = torch.empty((1, 32, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(B.tq_decode_attn_workspace(codec3, codec3, 1, 32, 8, ctx), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_decode_attn(codec3, codec3, qd, kp, vp, ctx, 8, 1 / math.sqrt(128), out=out, ws=ws), 5)
-    res["decode_attn_128k_ms"] = ms
-    res["decode_attn_128k_GBs"] = 2 * 8 * ctx * codec3.record_bytes / (ms * 1e-3) / 1e9
-    print(f"[bench] decode attention 128K {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    # prefill-shaped encode: K and V [16][8][8192][128] bf16
-    n = 16 * 8 * 8192
-    del k, v, kp, vp
-    k = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((n, 128), generator=g, device=dev).to(torch.bfloat16)
-    kp, vp = B.alloc_packed(codec3, n, dev), B.alloc_packed(codec3, n, dev)
-    ws = torch.empty(B.tq_encode_workspace(codec3, n), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_encode_kv(codec3, k, v, k_out=kp, v_out=vp, ws=ws), 3)
-    res["encode_prefill_kv_ms"] = ms
-    res["encode_prefill_vectors_per_s"] = 2 * n / (ms * 1e-3)
-    print(f"[bench] prefill encode {ms:.2f} ms", file=sys.stderr, flush=True)
+    ms = _time(lambda: B.tq_decode_attn(codec3, codec3, qd, kp, vp, ctx, 8, 1 / math.sqrt(d), out=out, ws=ws), 20,
+               graph=True)
+    res["decode_attn_c4"] = {"ms": ms, **_hbm(ms, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
+    print(f"[bench] C4 decode attention {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     del k, v, kp, vp, ws
-    if args.stage_search:
+    # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
+    bsz, hkv, ctx, nq = 16, 8, 8192, 16
+    n = bsz * hkv * ctx
+    k = torch.randn((n, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((n, d), generator=g, device=dev).to(torch.bfloat16)
+    kp, vp = B.alloc_packed(codec3, n, dev), B.alloc_packed(codec3, n, dev)
+    ws = torch.empty(max(B.tq_encode_workspace(codec3, n), 1), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_encode_kv(codec3, k, v, k_out=kp, v_out=vp, ws=ws), 5, graph=True)
+    res["encode_c3"] = {"ms": ms, "vectors_per_s": 2 * n / (ms * 1e-3),
+                        **_hbm(ms, 2 * n * (d * 2 + codec3.record_bytes))}
+    print(f"[bench] C3 prefill encode {ms:.3f} ms", file=sys.stderr, flush=True)
+    qp = torch.randn((bsz, nq, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    lg = torch.empty((bsz, hkv, nq, ctx), device=dev)
+    wsl = torch.empty(B.tq_attn_logits_workspace(codec3, bsz, hkv, hkv, nq), dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_attn_logits(codec3, qp, kp, ctx, hkv, logits=lg, ws=wsl), 20, graph=True)
+    res["logits_c3"] = {"ms": ms, "scores_per_s": bsz * hkv * nq * ctx / (ms * 1e-3),
+                        **_hbm(ms, n * codec3.record_bytes + bsz * hkv * nq * ctx * 4 + bsz * nq * hkv * d * 2)}
+    print(f"[bench] C3 logits {ms:.3f} ms", file=sys.stderr, flush=True)
+    del k, v, kp, vp, ws, qp, lg
+    if not args.no_stage_search:
+        # C5: encode the 10^6 x 1536 database (4-bit), then 1024 queries top-10
         c16 = B.tq_codec_create(1536, 4, 0, I.CODEC_SEED)
-        n_db = 1_000_000
-        db = torch.randn((n_db, 1536), generator=g, device=dev)
-        db /= db.norm(dim=1, keepdim=True)
-        dbp, _ = B.tq_encode_kv(c16, db)
-        qs = torch.randn((1024, 1536), generator=g, device=dev)
-        ms = _time(lambda: B.tq_search_topk(c16, dbp, qs, 10), 1)
-        res["search_1M_x1536_ms"] = ms
-        res["search_scores_per_s"] = 1024 * n_db / (ms * 1e-3)
+        db, qs = I.vector_search_torch(dev)
+        n_db, nqs, ds = db.shape[0], qs.shape[0], db.shape[1]
+        dbp = B.alloc_packed(c16, n_db, dev)
+        ws = torch.empty(max(B.tq_encode_workspace(c16, n_db), 1), dtype=torch.uint8, device=dev)
+        ms = _time(lambda: B.tq_encode_kv(c16, db, k_out=dbp, ws=ws), 3)
+        flops = 2.0 * ds * ds * n_db  # the QJL projection z = S r
+        res["encode_c5"] = {"ms": ms, "vectors_per_s": n_db / (ms * 1e-3), "bound": "fp32 valu",
+                            "algorithmic_tflop": flops / 1e12, "achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+                            "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP32_VALU_TFLOPS}
+        print(f"[bench] C5 encode {ms:.2f} ms", file=sys.stderr, flush=True)
+        del db, ws
+        ws = torch.empty(B.tq_search_workspace(c16, n_db, nqs, 10), dtype=torch.uint8, device=dev)
+        idx = torch.empty((nqs, 10), dtype=torch.int64, device=dev)
+        sc = torch.empty((nqs, 10), dtype=torch.float32, device=dev)
+        ms = _time(lambda: B.tq_search_topk(c16, dbp, qs, 10, out_idx=idx, out_score=sc, ws=ws), 3)
+        alg = 2.0 * (ds + ds) * nqs * n_db  # the estimator's multiply-adds, fp32-grade
+        # matrix ops issued: per (16 queries, 16 records, 128 coordinates) 15 (MSE, 4 planes) + 3 (QJL)
+        ops = (nqs // 16) * (n_db // 16) * (ds // 128) * 18
+        executed = ops * 16 * 16 * 128 * 2
+        res["search_c5"] = {"ms": ms, "scores_per_s": nqs * n_db / (ms * 1e-3), "bound": "mfma",
+                            "algorithmic_tflop": alg / 1e12, "algorithmic_TFLOPs": alg / (ms * 1e-3) / 1e12,
+                            "matrix_TFLOPs": executed / (ms * 1e-3) / 1e12,
+                            "frac": executed / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+        print(f"[bench] C5 search {ms:.2f} ms", file=sys.stderr, flush=True)
     return res
 
 
