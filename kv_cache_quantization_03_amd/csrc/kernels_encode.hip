@@ -254,10 +254,11 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
     const float nu = sqrtf(row_sum(ss));
-    const float inv = nu > 0.f ? 1.0f / nu : 0.f;
+    // 1/(ν √d) by the hardware reciprocal (1 ulp; the codes tolerate far more)
+    const float kscale = nu > 0.f ? __builtin_amdgcn_rcpf(nu) * P.inv_sqrt_d : 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] *= inv * dsg[e];
-    // y = H (D ⊙ x/ν)/√d: coordinate bits 0-2 in registers, 3-6 across lanes
+    for (int e = 0; e < 8; ++e) v[e] *= dsg[e];
+    // y = H (D ⊙ x)/(ν √d): coordinate bits 0-2 in registers, 3-6 across lanes
 #pragma unroll
     for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
@@ -276,24 +277,34 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
         v[e] = upper ? (o - v[e]) : (v[e] + o);
       }
     }
-    // quantize (idx = #{k : t_k < y}, ties low), residual, bit planes
+    // quantize (idx = #{k : t_k < y}, ties low), residual, bit planes.  The
+    // codebook is symmetric (c[L-1-k] = -c[k], middle boundary 0), so with
+    // s = [y > 0] and m = #{positive boundaries t below |y|} (at or below it
+    // when y <= 0, hence |y| one ulp up there): idx = s ? L/2 + m : L/2-1 - m,
+    // c[idx] = ±c[L/2 + m], the top bit is s and the others are m's, inverted
+    // when y <= 0.
     uint32_t bits[B];
 #pragma unroll
     for (int p = 0; p < B; ++p) bits[p] = 0u;
     float rr[8], rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float y = v[e] * P.inv_sqrt_d;
-      int c = 0;
-      float yh = P.cent[0];
+      const float y = v[e] * kscale;
+      const bool pos = y > 0.f;
+      const float a = __uint_as_float((__float_as_uint(y) & 0x7FFFFFFFu) + (pos ? 0u : 1u));
+      int mm = 0;
+      float mag = P.cent[NL / 2];
 #pragma unroll
-      for (int k = 0; k < NL - 1; ++k) {
-        const bool gt = P.bound[k] < y;
-        c += gt;
-        yh = gt ? P.cent[k + 1] : yh;
+      for (int j = 0; j < NL / 2 - 1; ++j) {
+        const bool gt = P.bound[NL / 2 + j] < a;
+        mm += gt;
+        mag = gt ? P.cent[NL / 2 + j + 1] : mag;
       }
+      const float yh = pos ? mag : -mag;
+      const int lowbits = pos ? mm : ~mm;
 #pragma unroll
-      for (int p = 0; p < B; ++p) bits[p] |= static_cast<uint32_t>((c >> p) & 1) << e;
+      for (int p = 0; p + 1 < B; ++p) bits[p] |= static_cast<uint32_t>((lowbits >> p) & 1) << e;
+      bits[B - 1] |= static_cast<uint32_t>(pos) << e;
       rr[e] = y - yh;
       rs = fmaf(rr[e], rr[e], rs);
     }
