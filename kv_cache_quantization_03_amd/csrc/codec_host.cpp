@@ -283,7 +283,7 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
     return TQ_ERROR_HIP;
   }
   const size_t nS = static_cast<size_t>(h.m) * h.d;
-  const bool with16 = h.d == 128 && h.m == 128;  // the fused encode's fp16 split of S
+  const bool with16 = h.m == h.d && h.d % 128 == 0;  // fp16 split of S for the matrix-core projections
   const size_t bytes = (2 * nS + h.d) * sizeof(float) + (with16 ? 2 * nS * sizeof(_Float16) : 0);
   hipError_t e = hipMalloc(&c->dev_block, bytes);
   if (e != hipSuccess) {

@@ -6,6 +6,7 @@
 // (random-sign Walsh–Hadamard rotation) and 第四部分 (the rotation must be
 // computed in high precision: here fp32 throughout); 「TurboQuant 学习路径」
 // 二.4 (bit-packing into 32-bit words).
+#include <cmath>
 #include <cstdlib>
 #include <string>
 
@@ -358,6 +359,132 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
   }
 }
 
+// The QJL projection z = S r with its sign bits on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16), for d = m a multiple of 128: the split encode's
+// second step.  S = S_hi + S_lo (fp16 pair, made at codec creation) and
+// r·2^sc = r_hi + r_lo (made here; 2^sc keeps r_lo out of the fp16
+// subnormals and does not change a sign); z·2^sc = S_hi r_hi + S_hi r_lo +
+// S_lo r_hi in fp32, about 2^-22 of |S_i||r| from the fp32 product.
+//
+// Block: 128 outputs x 128 vectors, 4 waves of 64 x 64 (4 x 4 tiles of 16),
+// contraction in steps of 32 through double-buffered LDS (one barrier a step);
+// each thread converts its 16 r values per step to the fp16 pair on the way
+// in.  The result tile holds output 4(L/16)+reg of vector L%16 in lane L, so
+// sign words are ORed over the four lane groups.
+namespace {
+constexpr int kPjB = 128;   // outputs and vectors per block
+constexpr int kPjK = 32;    // contraction step
+constexpr int kPjRow = 40;  // LDS row stride in halfs: 16-byte reads of 8 lanes hit distinct banks
+
+__global__ __launch_bounds__(256) void sproj_mfma_kernel(const float* __restrict__ r, int64_t n, int d, int m,
+                                                         const _Float16* __restrict__ S16, float rscale,
+                                                         uint32_t* __restrict__ signs) {
+  __shared__ __attribute__((aligned(16))) _Float16 sa[2][2][kPjB][kPjRow];  // [buffer][hi, lo][output][k]
+  __shared__ __attribute__((aligned(16))) _Float16 sb[2][2][kPjB][kPjRow];  // [buffer][hi, lo][vector][k]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;  // the wave's 64 outputs and 64 vectors
+  const int o0 = blockIdx.x * kPjB;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.y) * kPjB;
+  // staging: thread t moves row t/2, contraction elements 16(t%2)..+15 of both operands
+  const int srow = tid >> 1, sk = 16 * (tid & 1);
+  const _Float16* sp_hi = S16 + static_cast<int64_t>(o0 + srow) * d + sk;
+  const _Float16* sp_lo = sp_hi + static_cast<int64_t>(m) * d;
+  const float* rp = r + min(v0 + srow, n - 1) * d + sk;
+  h8 ga[2][2];  // S hi/lo, two 8-half pieces
+  float gr[16];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      ga[0][i] = *reinterpret_cast<const h8*>(sp_hi + k0 + 8 * i);
+      ga[1][i] = *reinterpret_cast<const h8*>(sp_lo + k0 + 8 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = reinterpret_cast<const float4*>(rp + k0)[i];
+      gr[4 * i] = x.x; gr[4 * i + 1] = x.y; gr[4 * i + 2] = x.z; gr[4 * i + 3] = x.w;
+    }
+  };
+  auto sstore = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<h8*>(&sa[b][0][srow][sk + 8 * i]) = ga[0][i];
+      *reinterpret_cast<h8*>(&sa[b][1][srow][sk + 8 * i]) = ga[1][i];
+      h8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = gr[8 * i + e] * rscale;
+        hi[e] = static_cast<_Float16>(x);
+        lo[e] = static_cast<_Float16>(x - static_cast<float>(hi[e]));
+      }
+      *reinterpret_cast<h8*>(&sb[b][0][srow][sk + 8 * i]) = hi;
+      *reinterpret_cast<h8*>(&sb[b][1][srow][sk + 8 * i]) = lo;
+    }
+  };
+  f4v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4v{0.f, 0.f, 0.f, 0.f};
+  const int nk = d / kPjK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = 8 * (lane >> 4);  // fragment row and first contraction element
+#pragma unroll 1
+  for (int ks = 0; ks < nk; ++ks) {
+    const int b = ks & 1;
+    if (ks + 1 < nk) gload(kPjK * (ks + 1));
+    h8 ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ah[i] = *reinterpret_cast<const h8*>(&sa[b][0][64 * wm + 16 * i + fr][fk]);
+      al[i] = *reinterpret_cast<const h8*>(&sa[b][1][64 * wm + 16 * i + fr][fk]);
+      bh[i] = *reinterpret_cast<const h8*>(&sb[b][0][64 * wn + 16 * i + fr][fk]);
+      bl[i] = *reinterpret_cast<const h8*>(&sb[b][1][64 * wn + 16 * i + fr][fk]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[i], bh[j], acc[i][j], 0, 0, 0);
+      }
+    if (ks + 1 < nk) sstore(b ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(acc[i][j]));  // matrix ops stay in wave-uniform flow
+  // sign words: outputs o0 + 64wm + 16i + 4(lane/16) + reg of vector v0 + 64wn + 16j + lane%16
+  const int g = lane >> 4, sw = m / 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t bit = static_cast<uint32_t>(acc[i][j][q] >= 0.f) << (16 * (i & 1) + 4 * g + q);
+        if (i < 2) w0 |= bit; else w1 |= bit;
+      }
+    w0 |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w0), 16, kWave));
+    w0 |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w0), 32, kWave));
+    w1 |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w1), 16, kWave));
+    w1 |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(w1), 32, kWave));
+    const int64_t vec = v0 + 64 * wn + 16 * j + fr;
+    if (g < 2 && vec < n) signs[vec * sw + (o0 + 64 * wm) / 32 + g] = g == 0 ? w0 : w1;
+  }
+}
+}  // namespace
+
+bool sproj_mfma_eligible(const tq_codec_s* c) {
+  const char* v = std::getenv("TQ_SPROJ_KERNEL");
+  if (v && std::string(v) == "valu") return false;
+  return c->dS16 != nullptr && c->prm.m == c->prm.d && c->prm.d % kPjB == 0;
+}
+
 bool encode_fused_eligible(const tq_codec_s* c) {
   const char* v = std::getenv("TQ_ENCODE_KERNEL");
   if (v && std::string(v) == "split") return false;
@@ -395,6 +522,20 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
   };
   hipError_t e = dispatch_E(P.d, run);
   if (e != hipSuccess) return e;
+  if (sproj_mfma_eligible(c)) {
+    // 2^sc with sc = ceil(log2 sqrt(d)) + 4: r·2^sc is O(1) per coordinate and below 2^11
+    const int sc = static_cast<int>(std::ceil(std::log2(std::sqrt(static_cast<double>(P.d))))) + 4;
+    const int64_t per_launch = static_cast<int64_t>(65535) * kPjB;  // grid.y limit
+    for (int64_t v0 = 0; v0 < n; v0 += per_launch) {
+      const int64_t nv = std::min(per_launch, n - v0);
+      const dim3 grid(static_cast<unsigned>(P.m / kPjB), static_cast<unsigned>(ceil_div(nv, kPjB)));
+      hipLaunchKernelGGL(sproj_mfma_kernel, grid, dim3(256), 0, s, ws_r + v0 * P.d, nv, P.d, P.m, c->dS16,
+                         std::ldexp(1.0f, sc), out.signs + v0 * P.sign_words);
+      const hipError_t e2 = hipGetLastError();
+      if (e2 != hipSuccess) return e2;
+    }
+    return hipSuccess;
+  }
   dim3 grid(static_cast<unsigned>(ceil_div(n, kTileV)), P.m / kTileI);
   hipLaunchKernelGGL((sproj_kernel<true>), grid, dim3(256), 0, s, ws_r, n, P.d, P.m, c->dS,
                      static_cast<float*>(nullptr), out.signs);

@@ -71,7 +71,7 @@ struct tq_codec_s {
   float* dS = nullptr;   // [m][d] row-major
   float* dMt = nullptr;  // [d][m]: (S R)ᵀ, so that p = S R q needs no rotated query
   float* dD = nullptr;   // [d] ±1
-  _Float16* dS16 = nullptr;  // [2][m][d]: S = hi + lo in fp16 (d = m = 128 only; else nullptr)
+  _Float16* dS16 = nullptr;  // [2][m][d]: S = hi + lo in fp16 (m = d, d a multiple of 128; else nullptr)
 };
 
 namespace tq {
