@@ -19,11 +19,15 @@ namespace tq {
 //   ν = ||x||, y = H (D ⊙ x/ν)/√d, idx_j = #{k : t_k < y_j} (ties low),
 //   r = y - c[idx] -> rbuf (fp32), γ = ||r||, codes packed as bit-planes.
 // ----------------------------------------------------------------------------
-template <int E, typename T>
+// The residual goes to rbuf as fp32 [n][d] (HL = false) or, for the matrix-core
+// projection, as r·rscale split into an fp16 pair [n][hi, lo][d] (HL = true;
+// the same bytes).
+template <int E, typename T, bool HL>
 __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x, int64_t n, DevParams P,
                                                         const float* __restrict__ Dsign,
                                                         uint32_t* __restrict__ codes, float* __restrict__ norm,
-                                                        float* __restrict__ rnorm, float* __restrict__ rbuf) {
+                                                        float* __restrict__ rnorm, float* __restrict__ rbuf,
+                                                        float rscale) {
   constexpr int d = E * kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -47,6 +51,7 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
   int idx[E];
   float rs = 0.f;
   float* rr = rbuf + vec * d;
+  _Float16* rh = reinterpret_cast<_Float16*>(rbuf) + vec * 2 * d;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float y = v[e] * P.inv_sqrt_d;
@@ -59,7 +64,14 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
     }
     idx[e] = c;
     const float r = y - yh;
-    rr[e * kWave + lane] = r;
+    if constexpr (HL) {
+      const float rsc = r * rscale;
+      const _Float16 hi = static_cast<_Float16>(rsc);
+      rh[e * kWave + lane] = hi;
+      rh[d + e * kWave + lane] = static_cast<_Float16>(rsc - static_cast<float>(hi));
+    } else {
+      rr[e * kWave + lane] = r;
+    }
     rs = fmaf(r, r, rs);
   }
   rs = wave_sum(rs);
@@ -362,63 +374,60 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 // The QJL projection z = S r with its sign bits on the fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16), for d = m a multiple of 128: the split encode's
 // second step.  S = S_hi + S_lo (fp16 pair, made at codec creation) and
-// r·2^sc = r_hi + r_lo (made here; 2^sc keeps r_lo out of the fp16
-// subnormals and does not change a sign); z·2^sc = S_hi r_hi + S_hi r_lo +
-// S_lo r_hi in fp32, about 2^-22 of |S_i||r| from the fp32 product.
+// r·2^sc = r_hi + r_lo (written so by encode_rq_kernel; 2^sc keeps r_lo out
+// of the fp16 subnormals and does not change a sign); z·2^sc = S_hi r_hi +
+// S_hi r_lo + S_lo r_hi in fp32, about 2^-22 of |S_i||r| from the fp32 product.
 //
 // Block: 128 outputs x 128 vectors, 4 waves of 64 x 64 (4 x 4 tiles of 16),
-// contraction in steps of 32 through double-buffered LDS (one barrier a step);
-// each thread converts its 16 r values per step to the fp16 pair on the way
-// in.  The result tile holds output 4(L/16)+reg of vector L%16 in lane L, so
-// sign words are ORed over the four lane groups.
+// contraction in steps of 32 through double-buffered LDS (one barrier a step).
+// The result tile holds output 4(L/16)+reg of vector L%16 in lane L, so sign
+// words are ORed over the four lane groups.
 namespace {
 constexpr int kPjB = 128;   // outputs and vectors per block
 constexpr int kPjK = 32;    // contraction step
 constexpr int kPjRow = 40;  // LDS row stride in halfs: 16-byte reads of 8 lanes hit distinct banks
 
-__global__ __launch_bounds__(256) void sproj_mfma_kernel(const float* __restrict__ r, int64_t n, int d, int m,
-                                                         const _Float16* __restrict__ S16, float rscale,
+__global__ __launch_bounds__(256) void sproj_mfma_kernel(const _Float16* __restrict__ r16, int64_t n, int d, int m,
+                                                         const _Float16* __restrict__ S16,
                                                          uint32_t* __restrict__ signs) {
   __shared__ __attribute__((aligned(16))) _Float16 sa[2][2][kPjB][kPjRow];  // [buffer][hi, lo][output][k]
   __shared__ __attribute__((aligned(16))) _Float16 sb[2][2][kPjB][kPjRow];  // [buffer][hi, lo][vector][k]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv & 1, wn = wv >> 1;  // the wave's 64 outputs and 64 vectors
-  const int o0 = blockIdx.x * kPjB;
-  const int64_t v0 = static_cast<int64_t>(blockIdx.y) * kPjB;
+  // Blocks go to the 8 XCDs round-robin (block p to XCD p % 8).  All m/128 output
+  // tiles of one vector tile run on one XCD at about the same time, so that
+  // XCD's L2 serves the tile's r after the first read.
+  const int nob = m / kPjB;
+  const int64_t p = blockIdx.x, xcd = p % 8, kq = p / 8;
+  const int ot = static_cast<int>(kq % nob);
+  const int64_t vt = (kq / nob) * 8 + xcd;
+  const int o0 = ot * kPjB;
+  const int64_t v0 = vt * kPjB;
+  if (v0 >= n) return;  // block-uniform: the padding of the last group of 8
   // staging: thread t moves row t/2, contraction elements 16(t%2)..+15 of both operands
   const int srow = tid >> 1, sk = 16 * (tid & 1);
   const _Float16* sp_hi = S16 + static_cast<int64_t>(o0 + srow) * d + sk;
   const _Float16* sp_lo = sp_hi + static_cast<int64_t>(m) * d;
-  const float* rp = r + min(v0 + srow, n - 1) * d + sk;
-  h8 ga[2][2];  // S hi/lo, two 8-half pieces
-  float gr[16];
+  const _Float16* rp_hi = r16 + min(v0 + srow, n - 1) * 2 * d + sk;
+  const _Float16* rp_lo = rp_hi + d;
+  h8 ga[2][2], gb[2][2];  // S and r, hi/lo, two 8-half pieces each
   auto gload = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       ga[0][i] = *reinterpret_cast<const h8*>(sp_hi + k0 + 8 * i);
       ga[1][i] = *reinterpret_cast<const h8*>(sp_lo + k0 + 8 * i);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 x = reinterpret_cast<const float4*>(rp + k0)[i];
-      gr[4 * i] = x.x; gr[4 * i + 1] = x.y; gr[4 * i + 2] = x.z; gr[4 * i + 3] = x.w;
+      gb[0][i] = *reinterpret_cast<const h8*>(rp_hi + k0 + 8 * i);
+      gb[1][i] = *reinterpret_cast<const h8*>(rp_lo + k0 + 8 * i);
     }
   };
   auto sstore = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<h8*>(&sa[b][0][srow][sk + 8 * i]) = ga[0][i];
-      *reinterpret_cast<h8*>(&sa[b][1][srow][sk + 8 * i]) = ga[1][i];
-      h8 hi, lo;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = gr[8 * i + e] * rscale;
-        hi[e] = static_cast<_Float16>(x);
-        lo[e] = static_cast<_Float16>(x - static_cast<float>(hi[e]));
+      for (int hl = 0; hl < 2; ++hl) {
+        *reinterpret_cast<h8*>(&sa[b][hl][srow][sk + 8 * i]) = ga[hl][i];
+        *reinterpret_cast<h8*>(&sb[b][hl][srow][sk + 8 * i]) = gb[hl][i];
       }
-      *reinterpret_cast<h8*>(&sb[b][0][srow][sk + 8 * i]) = hi;
-      *reinterpret_cast<h8*>(&sb[b][1][srow][sk + 8 * i]) = lo;
-    }
   };
   f4v acc[4][4];
 #pragma unroll
@@ -515,22 +524,29 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
     }
     return hipErrorInvalidValue;
   }
+  const bool mfma = sproj_mfma_eligible(c);
+  // 2^sc with sc = ceil(log2 sqrt(d)) + 4: r·2^sc is O(1) per coordinate and below 2^11
+  const int sc = static_cast<int>(std::ceil(std::log2(std::sqrt(static_cast<double>(P.d))))) + 4;
   auto run = [&]<int E>() -> hipError_t {
-    hipLaunchKernelGGL((encode_rq_kernel<E, T>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0, s,
-                       x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r);
+    if (mfma)
+      hipLaunchKernelGGL((encode_rq_kernel<E, T, true>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
+                         s, x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r, std::ldexp(1.0f, sc));
+    else
+      hipLaunchKernelGGL((encode_rq_kernel<E, T, false>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
+                         s, x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r, 1.0f);
     return hipGetLastError();
   };
   hipError_t e = dispatch_E(P.d, run);
   if (e != hipSuccess) return e;
-  if (sproj_mfma_eligible(c)) {
-    // 2^sc with sc = ceil(log2 sqrt(d)) + 4: r·2^sc is O(1) per coordinate and below 2^11
-    const int sc = static_cast<int>(std::ceil(std::log2(std::sqrt(static_cast<double>(P.d))))) + 4;
-    const int64_t per_launch = static_cast<int64_t>(65535) * kPjB;  // grid.y limit
+  if (mfma) {
+    const _Float16* r16 = reinterpret_cast<const _Float16*>(ws_r);
+    const int64_t per_launch = static_cast<int64_t>(1) << 24;  // vectors per launch (grid size well inside 2^32)
     for (int64_t v0 = 0; v0 < n; v0 += per_launch) {
       const int64_t nv = std::min(per_launch, n - v0);
-      const dim3 grid(static_cast<unsigned>(P.m / kPjB), static_cast<unsigned>(ceil_div(nv, kPjB)));
-      hipLaunchKernelGGL(sproj_mfma_kernel, grid, dim3(256), 0, s, ws_r + v0 * P.d, nv, P.d, P.m, c->dS16,
-                         std::ldexp(1.0f, sc), out.signs + v0 * P.sign_words);
+      // one-dimensional grid: every vector tile (rounded up to 8) times every output tile
+      const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(nv, kPjB), 8) * 8 * (P.m / kPjB)));
+      hipLaunchKernelGGL(sproj_mfma_kernel, grid, dim3(256), 0, s, r16 + v0 * 2 * P.d, nv, P.d, P.m, c->dS16,
+                         out.signs + v0 * P.sign_words);
       const hipError_t e2 = hipGetLastError();
       if (e2 != hipSuccess) return e2;
     }
