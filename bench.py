@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--bits", type=int, default=3)
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timings")
+    ap.add_argument("--only-stages", action="store_true",
+                    help="run only the per-stage timings (one JSON line of stages; for kernel-trace profiles)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-stage-search", action="store_true", help="skip the 1M x 1536 encode and search stages")
     ap.add_argument("--pmc-pass", action="store_true",
@@ -90,6 +92,9 @@ def main():
     d, hq, hkv, ctx, batch = w["d"], w["n_q_heads"], w["n_kv_heads"], w["ctx"], w["batch"]
     n_keys = batch * hkv * ctx
     codec = B.tq_codec_create(d, bits, 0, I.CODEC_SEED)
+    if args.only_stages:
+        print(json.dumps({"stages": time_stages(B, I, codec, dev, args)}))
+        return
 
     t0 = time.time()
     k_host = w["keys"].rows()
