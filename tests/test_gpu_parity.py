@@ -85,7 +85,7 @@ def test_encode_parity(B, d, bits, dtype):
                                          (2, "bf16", 129), (4, "bf16", 2049), (3, "bf16", 5000)])
 def test_encode_fused_and_split_kernels(B, bits, dtype, n, monkeypatch):
     # d = 128 takes the fused kernel (S·r on the matrix cores); the split path
-    # (fp32 rotation kernel, then the fp32 S-projection GEMM) is the other
+    # (rotation kernel, then the S-projection kernel) is the other
     # implementation: both must pass the encode bar against the oracle
     say(f"encode fused vs split bits={bits} {dtype} n={n}")
     gc, oc = pair(B, 128, bits)
@@ -98,6 +98,28 @@ def test_encode_fused_and_split_kernels(B, bits, dtype, n, monkeypatch):
     sf = check_encode(oc, x.astype(np.float64), kf.numpy(), "fused")
     ss = check_encode(oc, x.astype(np.float64), ks.numpy(), "split")
     say(f"  fused mismatches {sf['code_mismatch']}/{sf['sign_mismatch']}, split {ss['code_mismatch']}/{ss['sign_mismatch']}")
+
+
+@pytest.mark.parametrize("d,bits,n", [(128, 3, 1000), (256, 4, 777), (1536, 4, 300), (512, 3, 129)])
+def test_encode_projection_matrix_and_vector_kernels(B, d, bits, n, monkeypatch):
+    """The split encode's QJL projection on the fp16 matrix cores (S and r as
+    hi/lo pairs) and on the fp32 vector units: both pass the encode bar against
+    the oracle, and they share every code word, norm and residual norm."""
+    say(f"encode projection matrix vs vector d={d} bits={bits} n={n}")
+    gc, oc = pair(B, d, bits)
+    x = rand_keys(n, d, seed=n + d, dtype="f32")
+    monkeypatch.setenv("TQ_ENCODE_KERNEL", "split")
+    km, _ = B.tq_encode_kv(gc, to_dev(x, "f32"))
+    monkeypatch.setenv("TQ_SPROJ_KERNEL", "valu")
+    kv, _ = B.tq_encode_kv(gc, to_dev(x, "f32"))
+    torch.cuda.synchronize()
+    a, b = km.numpy(), kv.numpy()
+    for key in ("codes", "norm", "rnorm"):
+        assert np.array_equal(a[key], b[key]), key
+    sm = check_encode(oc, x.astype(np.float64), a, "matrix")
+    sv = check_encode(oc, x.astype(np.float64), b, "vector")
+    say(f"  sign mismatches vs oracle: matrix {sm['sign_mismatch']}, vector {sv['sign_mismatch']}; "
+        f"differing sign words {int(np.sum(a['signs'] != b['signs']))}")
 
 
 def test_encode_k_and_v_together(B):
