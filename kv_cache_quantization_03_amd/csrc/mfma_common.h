@@ -127,17 +127,17 @@ __device__ __forceinline__ void load_wave_records(v4u (&cv)[NC], v4u (&sv)[NS], 
   for (int i = 0; i < L::CW / 4; ++i) {
     const int w = 4 * (i * 64 + lane);
     const int kk = min(w / L::CW, nvalid - 1);
-    cv[i] = reinterpret_cast<const v4u*>(codes)[(kk * L::CW + w % L::CW) / 4];
+    cv[i] = __builtin_nontemporal_load(&reinterpret_cast<const v4u*>(codes)[(kk * L::CW + w % L::CW) / 4]);
   }
 #pragma unroll
   for (int i = 0; i < L::SW / 4; ++i) {
     const int w = 4 * (i * 64 + lane);
     const int kk = min(w / L::SW, nvalid - 1);
-    sv[i] = reinterpret_cast<const v4u*>(signs)[(kk * L::SW + w % L::SW) / 4];
+    sv[i] = __builtin_nontemporal_load(&reinterpret_cast<const v4u*>(signs)[(kk * L::SW + w % L::SW) / 4]);
   }
   const int ln = min(lane, nvalid - 1);
-  nu = norm[ln];
-  ga = rnorm[ln];
+  nu = __builtin_nontemporal_load(&norm[ln]);
+  ga = __builtin_nontemporal_load(&rnorm[ln]);
 }
 
 // Scatter the records into the wave's LDS slice, then score the 64 keys
@@ -206,7 +206,7 @@ __device__ __forceinline__ void score_wave(const v4u (&cv)[NC], const v4u (&sv)[
                                     acc_m[i][3] * 0.000244140625f) + cst[i].z;
       const float qj = cst[i].y * (acc_q[i][0] + acc_q[i][1] * 0.0625f + acc_q[i][2] * 0.00390625f +
                                    acc_q[i][3] * 0.000244140625f) + cst[i].w;
-      if (out[i] != nullptr && kk < nvalid) out[i][kk] = nu * (mse + kappa * ga * qj);
+      if (out[i] != nullptr && kk < nvalid) __builtin_nontemporal_store(nu * (mse + kappa * ga * qj), &out[i][kk]);
     }
   }
 }
