@@ -385,7 +385,8 @@ def test_decode_attn_one_hot(B):
 
 # ---------------------------------------------------------------- search
 @pytest.mark.parametrize("d,bits,n_db,nq,k", [(128, 4, 70001, 8, 10), (128, 3, 3000, 5, 1), (128, 4, 2000, 3, 100),
-                                              (1536, 4, 2500, 4, 10)])
+                                              (1536, 4, 2500, 4, 10), (256, 4, 5000, 17, 10), (512, 3, 1500, 2, 5),
+                                              (1024, 4, 700, 3, 7), (64, 3, 3000, 4, 10)])
 def test_search_parity(B, d, bits, n_db, nq, k):
     say(f"search d={d} n_db={n_db} nq={nq} k={k}")
     gc, oc = pair(B, d, bits)
