@@ -299,32 +299,52 @@ def time_stages(B, I, codec3, dev, args):
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     d = 128
+    # Every HBM-bound stage rotates over enough buffer sets that the 256 MB
+    # Infinity Cache cannot hold them, so its data streams from HBM.
     # C2 4-bit: 4-bit logits on the Llama-8B decode shape
     c4 = B.tq_codec_create(d, 4, 0, I.CODEC_SEED)
     ctx = 32768
     k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((1, 1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp4, _ = B.tq_encode_kv(c4, k)
-    lg = torch.empty((1, 32, 1, ctx), device=dev)
-    wsl = torch.empty(B.tq_attn_logits_workspace(c4, 1, 32, 8, 1), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_attn_logits(c4, q, kp4, ctx, 8, logits=lg, ws=wsl), 200, graph=True)
-    res["logits_c2_4bit"] = {"ms": ms, "keys_per_s": 32 * ctx / (ms * 1e-3),
+    ns = 24
+    sets = [(B.Packed(kp4.codes.clone(), kp4.signs.clone(), kp4.norm.clone(), kp4.rnorm.clone()), q.clone(),
+             torch.empty((1, 32, 1, ctx), device=dev),
+             torch.empty(B.tq_attn_logits_workspace(c4, 1, 32, 8, 1), dtype=torch.uint8, device=dev))
+            for _ in range(ns)]
+    it = iter(range(10 ** 9))
+
+    def c2():
+        kk, qq, ll, ww = sets[next(it) % ns]
+        B.tq_attn_logits(c4, qq, kk, ctx, 8, logits=ll, ws=ww)
+    ms = _time(c2, 240, graph=True)
+    res["logits_c2_4bit"] = {"ms": ms, "keys_per_s": 32 * ctx / (ms * 1e-3), "buffer_sets": ns,
                              **_hbm(ms, 8 * ctx * c4.record_bytes + 32 * ctx * 4 + 32 * d * 2)}
     print(f"[bench] C2 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    del k, kp4, lg
+    del k, kp4, sets
     # C4: fused decode attention, 128K context, K and V 3-bit
     ctx = 131072
     k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
     v = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
     qd = torch.randn((1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp, vp = B.tq_encode_kv(codec3, k, v)
+    del k, v
+    ns = 3
+    dsets = [(kp, vp)] + [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
+                           B.Packed(vp.codes.clone(), vp.signs.clone(), vp.norm.clone(), vp.rnorm.clone()))
+                          for _ in range(ns - 1)]
     out = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(B.tq_decode_attn_workspace(codec3, codec3, 1, 32, 8, ctx), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_decode_attn(codec3, codec3, qd, kp, vp, ctx, 8, 1 / math.sqrt(d), out=out, ws=ws), 20,
-               graph=True)
-    res["decode_attn_c4"] = {"ms": ms, **_hbm(ms, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
+    it = iter(range(10 ** 9))
+
+    def c4():
+        kk, vv = dsets[next(it) % ns]
+        B.tq_decode_attn(codec3, codec3, qd, kk, vv, ctx, 8, 1 / math.sqrt(d), out=out, ws=ws)
+    ms = _time(c4, 30, graph=True)
+    res["decode_attn_c4"] = {"ms": ms, "buffer_sets": ns,
+                             **_hbm(ms, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
     print(f"[bench] C4 decode attention {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    del k, v, kp, vp, ws
+    del kp, vp, dsets, ws
     # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
     bsz, hkv, ctx, nq = 16, 8, 8192, 16
     n = bsz * hkv * ctx
@@ -336,14 +356,23 @@ def time_stages(B, I, codec3, dev, args):
     res["encode_c3"] = {"ms": ms, "vectors_per_s": 2 * n / (ms * 1e-3),
                         **_hbm(ms, 2 * n * (d * 2 + codec3.record_bytes))}
     print(f"[bench] C3 prefill encode {ms:.3f} ms", file=sys.stderr, flush=True)
+    del k, v, vp, ws
     qp = torch.randn((bsz, nq, hkv, d), generator=g, device=dev).to(torch.bfloat16)
-    lg = torch.empty((bsz, hkv, nq, ctx), device=dev)
-    wsl = torch.empty(B.tq_attn_logits_workspace(codec3, bsz, hkv, hkv, nq), dtype=torch.uint8, device=dev)
-    ms = _time(lambda: B.tq_attn_logits(codec3, qp, kp, ctx, hkv, logits=lg, ws=wsl), 20, graph=True)
-    res["logits_c3"] = {"ms": ms, "scores_per_s": bsz * hkv * nq * ctx / (ms * 1e-3),
+    ns = 3
+    lsets = [(kp if i == 0 else B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
+              qp.clone(), torch.empty((bsz, hkv, nq, ctx), device=dev),
+              torch.empty(B.tq_attn_logits_workspace(codec3, bsz, hkv, hkv, nq), dtype=torch.uint8, device=dev))
+             for i in range(ns)]
+    it = iter(range(10 ** 9))
+
+    def c3():
+        kk, qq, ll, ww = lsets[next(it) % ns]
+        B.tq_attn_logits(codec3, qq, kk, ctx, hkv, logits=ll, ws=ww)
+    ms = _time(c3, 30, graph=True)
+    res["logits_c3"] = {"ms": ms, "scores_per_s": bsz * hkv * nq * ctx / (ms * 1e-3), "buffer_sets": ns,
                         **_hbm(ms, n * codec3.record_bytes + bsz * hkv * nq * ctx * 4 + bsz * nq * hkv * d * 2)}
     print(f"[bench] C3 logits {ms:.3f} ms", file=sys.stderr, flush=True)
-    del k, v, kp, vp, ws, qp, lg
+    del kp, qp, lsets
     if not args.no_stage_search:
         # C5: encode the 10^6 x 1536 database (4-bit), then 1024 queries top-10
         c16 = B.tq_codec_create(1536, 4, 0, I.CODEC_SEED)
