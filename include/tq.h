@@ -71,7 +71,7 @@ typedef struct tq_codec_s* tq_codec_t; /* opaque; immutable after create, usable
 typedef enum {
   TQ_SUCCESS = 0,
   TQ_ERROR_INVALID_VALUE = 1,        /* NULL handle/pointer, negative size, bad enum, bad shape */
-  TQ_ERROR_NOT_SUPPORTED = 2,        /* a valid request this build does not implement */
+  TQ_ERROR_NOT_SUPPORTED = 2,        /* a valid request the library does not implement */
   TQ_ERROR_MISALIGNED = 3,           /* a pointer breaks the alignment stated below */
   TQ_ERROR_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes < the matching *_workspace() size */
   TQ_ERROR_OUT_OF_MEMORY = 5,        /* host or device allocation inside tq_codec_create failed */
