@@ -248,6 +248,10 @@ def main():
 
     if not args.no_stages:
         out["stages"].update(time_stages(B, I, codec, dev, args))
+        ceil = out["stages"].get("stream_read_ceiling_c2_bytes")
+        if ceil:  # the same byte count read by a plain streaming kernel, on this machine
+            out["roofline"]["stream_ceiling_GBs"] = ceil["achieved_GBs"]
+            out["roofline"]["frac_of_stream_ceiling"] = achieved / ceil["achieved_GBs"]
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, k_host, q_host, bits)
@@ -322,6 +326,38 @@ def time_stages(B, I, codec3, dev, args):
                              **_hbm(ms, 8 * ctx * c4.record_bytes + 32 * ctx * 4 + 32 * d * 2)}
     print(f"[bench] C2 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     del k, kp4, sets
+    # Streaming-read ceiling at the C2 step's algorithmic byte count: plain
+    # 16-byte loads (tq_diag_stream_read), rotating buffers, timed the same way
+    nbytes = (8 * 32768 * codec3.record_bytes + 32 * 32768 * 4 + 32 * d * 2) // 16 * 16
+    ns = 29
+    bufs = [torch.randint(0, 1 << 30, (nbytes // 4,), generator=g, device=dev, dtype=torch.int32) for _ in range(ns)]
+    sink = torch.empty(B.lib.tq_diag_stream_blocks(), dtype=torch.int32, device=dev)
+    it = iter(range(10 ** 9))
+    ms = _time(lambda: B.tq_diag_stream_read(bufs[next(it) % ns], sink), 240, graph=True)
+    res["stream_read_ceiling_c2_bytes"] = {"ms": ms, **_hbm(ms, nbytes), "buffer_sets": ns}
+    print(f"[bench] streaming read of {nbytes / 1e6:.1f} MB: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+    del bufs, sink
+    # C2 at batch 16: the same decode step, 16 sequences (the streaming asymptote)
+    bsz = 16
+    k = torch.randn((bsz * 8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    kb = B.tq_encode_kv(codec3, k)[0]
+    del k
+    qb = torch.randn((bsz, 1, 32, d), generator=g, device=dev).to(torch.bfloat16)
+    ns = 2
+    bsets = [(kb if i == 0 else B.Packed(kb.codes.clone(), kb.signs.clone(), kb.norm.clone(), kb.rnorm.clone()),
+              qb.clone(), torch.empty((bsz, 32, 1, ctx), device=dev),
+              torch.empty(B.tq_attn_logits_workspace(codec3, bsz, 32, 8, 1), dtype=torch.uint8, device=dev))
+             for i in range(ns)]
+    it = iter(range(10 ** 9))
+
+    def c2b():
+        kk, qq, ll, ww = bsets[next(it) % ns]
+        B.tq_attn_logits(codec3, qq, kk, ctx, 8, logits=ll, ws=ww)
+    ms = _time(c2b, 40, graph=True)
+    res["logits_c2_3bit_batch16"] = {"ms": ms, "keys_per_s": bsz * 32 * ctx / (ms * 1e-3), "buffer_sets": ns,
+                                     **_hbm(ms, bsz * (8 * ctx * codec3.record_bytes + 32 * ctx * 4 + 32 * d * 2))}
+    print(f"[bench] C2 3-bit logits at batch 16 {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del kb, qb, bsets
     # C4: fused decode attention, 128K context, K and V 3-bit
     ctx = 131072
     k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
@@ -428,10 +464,20 @@ def cpu_baseline(w, k_host, q_host, bits):
         reps += 1
     score_s = tot / reps
     n_scores = w["batch"] * w["n_q_heads"] * w["ctx"]
+    one_core = None
+    try:  # the same scoring with the BLAS pool limited to one thread
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t = time.perf_counter()
+            O.attn_logits(oc, q_host.astype(np.float64), rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1,
+                          w["ctx"])
+            one_core = n_scores / (time.perf_counter() - t)
+    except Exception:
+        pass
     return {"value": n_scores / score_s, "unit": "keys/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"full workload ({n_scores} scores) x{reps}; encode of {k_host.shape[0]} keys took "
                       f"{enc_s:.2f}s ({k_host.shape[0] / enc_s:.0f} vectors/s)",
-            "os_cpu_count": os.cpu_count()}
+            "os_cpu_count": os.cpu_count(), "value_one_thread": one_core}
 
 
 if __name__ == "__main__":

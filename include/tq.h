@@ -218,6 +218,17 @@ tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db, const flo
                            int32_t n_queries, int32_t topk, int64_t* out_idx, float* out_score,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- measurement
+ * Not part of the method: the streaming-read ceiling the kernels' HBM rates are
+ * compared with.  Reads `bytes` (a multiple of 16) at the 16-byte aligned
+ * device pointer `src` with plain 16-byte loads, as one launch of
+ * tq_diag_stream_blocks() blocks of 256 threads, and writes one XOR word per
+ * block to the device array sink[tq_diag_stream_blocks()] (so the loads are
+ * not removed).  TQ_ERROR_INVALID_VALUE for a null pointer or a byte count
+ * that is not a multiple of 16, TQ_ERROR_MISALIGNED for a misaligned src. */
+int32_t tq_diag_stream_blocks(void);
+tq_status_t tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,8 @@ def _load():
                                      vp, sz, vp]),
         "tq_search_workspace": (sz, [vp, i64, i32, i32]),
         "tq_search_topk": (C.c_int, [vp, P, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
+        "tq_diag_stream_blocks": (i32, []),
+        "tq_diag_stream_read": (C.c_int, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -75,7 +77,7 @@ EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_bui
             "tq_codec_destroy", "tq_codec_info", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn",
-            "tq_search_workspace", "tq_search_topk")
+            "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
 
 
 def _check(status: int, where: str):
@@ -301,3 +303,15 @@ def tq_search_topk(codec: Codec, db: Packed, queries, topk: int, out_idx=None, o
                             _ptr(ws), ws.numel(), _stream(queries))
     _check(st, "tq_search_topk")
     return out_idx, out_score
+
+
+def tq_diag_stream_read(buf, sink=None):
+    """Streaming-read ceiling: plain 16-byte loads over the device tensor buf
+    (measurement helper, not part of the method).  sink: uint32 device tensor of
+    tq_diag_stream_blocks() words (allocated when None); returns it."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(lib.tq_diag_stream_blocks(), dtype=torch.int32, device=buf.device)
+    st = lib.tq_diag_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf))
+    _check(st, "tq_diag_stream_read")
+    return sink

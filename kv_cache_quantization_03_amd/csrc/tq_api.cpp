@@ -247,3 +247,18 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
                                    static_cast<hipStream_t>(stream));
   return finish(e, "tq_search_topk launch");
 }
+
+namespace tq {
+int diag_stream_blocks();
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+}  // namespace tq
+
+extern "C" int32_t tq_diag_stream_blocks(void) { return tq::diag_stream_blocks(); }
+
+extern "C" tq_status_t tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  tq::clear_error();
+  if (!src || !sink || bytes % 16 != 0) { set_error("need src, sink and a byte count that is a multiple of 16"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(src, 16) || !aligned(sink, 4)) { set_error("src must be 16-byte aligned, sink 4-byte aligned"); return TQ_ERROR_MISALIGNED; }
+  if (bytes == 0) return TQ_SUCCESS;
+  return finish(tq::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)), "tq_diag_stream_read launch");
+}

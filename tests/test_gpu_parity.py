@@ -450,6 +450,18 @@ def test_search_massive_ties(B, bits, k):
     assert np.allclose(sc, full[0, idx], rtol=0, atol=1e-4 * np.max(np.abs(full[0])))
 
 
+def test_diag_stream_read_touches_every_word(B):
+    """The streaming-read ceiling kernel reads every word: the XOR of its
+    per-block words is the XOR of the buffer."""
+    x = np.random.default_rng(9).integers(0, 2 ** 31, size=(1 << 18) + 12, dtype=np.int64).astype(np.int32)
+    t = torch.from_numpy(x).cuda()
+    sink = B.tq_diag_stream_read(t)
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(x)
+    st = B.lib.tq_diag_stream_read(t.data_ptr(), 40, sink.data_ptr(), None)  # not a multiple of 16
+    assert st == 1
+
+
 # ---------------------------------------------------------------- argument checks with a real codec
 def test_invalid_arguments_rejected(B):
     gc, _ = pair(B, 128, 3)
