@@ -303,6 +303,19 @@ def time_stages(B, I, codec3, dev, args):
     g = torch.Generator(device=dev)
     g.manual_seed(7)
     d = 128
+    # C1: the tiny reference (1 fp32 query, 4096 fp32 keys, 3-bit): latency only
+    w1 = I.tiny_ref()
+    k1 = torch.from_numpy(w1["keys"].rows()).to(dev)
+    q1 = torch.from_numpy(w1["queries"].rows().reshape(1, 1, 1, d)).to(dev)
+    kp1 = B.alloc_packed(codec3, k1.shape[0], dev)
+    ws1 = torch.empty(max(B.tq_encode_workspace(codec3, k1.shape[0]), 1), dtype=torch.uint8, device=dev)
+    ms_e = _time(lambda: B.tq_encode_kv(codec3, k1, k_out=kp1, ws=ws1), 50, graph=True)
+    lg1 = torch.empty((1, 1, 1, k1.shape[0]), device=dev)
+    wl1 = torch.empty(B.tq_attn_logits_workspace(codec3, 1, 1, 1, 1), dtype=torch.uint8, device=dev)
+    ms_l = _time(lambda: B.tq_attn_logits(codec3, q1, kp1, k1.shape[0], 1, logits=lg1, ws=wl1), 50, graph=True)
+    res["c1_tiny"] = {"encode_ms": ms_e, "logits_ms": ms_l, "bound": "latency"}
+    print(f"[bench] C1 encode {ms_e * 1e3:.1f} us, logits {ms_l * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del k1, q1, kp1, ws1, lg1, wl1
     # Every HBM-bound stage rotates over enough buffer sets that the 256 MB
     # Infinity Cache cannot hold them, so its data streams from HBM.
     # C2 4-bit: 4-bit logits on the Llama-8B decode shape
