@@ -40,7 +40,7 @@ __all__ = [
     "pack_planes", "unpack_planes", "pack_bits", "unpack_bits",
     "encode", "encode_given_codes", "dequantize",
     "prepare_query", "score", "attn_logits",
-    "decode_attn_materialized", "decode_attn_accumulated",
+    "decode_attn_materialized", "decode_attn_accumulated", "decode_attn_sparse_v",
     "search_topk", "bf16_round",
 ]
 
@@ -510,6 +510,51 @@ def decode_attn_accumulated(codec_k: Codec, codec_v: Codec, q, k_packed, v_packe
             o_rot = (M + kv * (J @ S)) / l
             out[bi, hs] = o_rot @ codec_v.R
     return out
+
+
+# --------------------------------------------------------------------------
+# O6b. Sparse V (TurboQuant+ 深度解析 第六部分 Sparse V Dequant): the
+# attention weights act as a gate, and a position whose weight is below a
+# threshold (1e-6 on that page) does not have its value decompressed or added.
+#
+# Reading: the weight the gate tests is the one known where the value is
+# accumulated.  Decode attention is split over the context into chunks of
+# `chunk` consecutive positions; inside a chunk the weight of position t for
+# query head h is exp(s_ht - m_hc) / l_hc, with m_hc and l_hc the maximum and
+# the sum of exp(s - m_hc) of head h's scaled scores over that chunk.  Since
+# the whole-context normaliser satisfies l·e^m >= l_hc·e^(m_hc), this
+# chunk-local weight is never below the final softmax weight, so every
+# position the gate drops has a final weight below the threshold too.  The
+# gate is taken per (query head, position); the normaliser l still sums every
+# position, only the value term is dropped.  With one chunk spanning the
+# context the gate is exactly "final weight < threshold".
+# --------------------------------------------------------------------------
+def decode_attn_sparse_v(codec_k: Codec, codec_v: Codec, q, k_packed, v_packed,
+                         batch, n_q_heads, n_kv_heads, ctx_len, scale, gate, chunk):
+    """Returns (out [batch][n_q_heads][d], keep [batch][n_q_heads][ctx_len]
+    bool, local [batch][n_q_heads][ctx_len] chunk-local weights)."""
+    q = np.asarray(q, dtype=np.float64).reshape(batch, n_q_heads, codec_k.d)
+    G = n_q_heads // n_kv_heads
+    out = np.zeros((batch, n_q_heads, codec_v.d))
+    keep = np.zeros((batch, n_q_heads, ctx_len), dtype=bool)
+    local = np.zeros((batch, n_q_heads, ctx_len))
+    for bi in range(batch):
+        for kh in range(n_kv_heads):
+            row0 = (bi * n_kv_heads + kh) * ctx_len
+            keys = _slice_packed(k_packed, row0, row0 + ctx_len)
+            vals = dequantize(codec_v, _slice_packed(v_packed, row0, row0 + ctx_len))
+            hs = slice(kh * G, (kh + 1) * G)
+            s = scale * score(codec_k, q[bi, hs], keys)          # [G][T]
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            l = np.sum(e, axis=-1, keepdims=True)               # every position
+            for c0 in range(0, ctx_len, chunk):
+                sc = s[:, c0:c0 + chunk]
+                ec = np.exp(sc - np.max(sc, axis=-1, keepdims=True))
+                local[bi, hs, c0:c0 + chunk] = ec / np.sum(ec, axis=-1, keepdims=True)
+            k = local[bi, hs] >= gate
+            keep[bi, hs] = k
+            out[bi, hs] = (e * k / l) @ vals
+    return out, keep, local
 
 
 # --------------------------------------------------------------------------

@@ -425,6 +425,71 @@ def test_decode_attention_one_hot_and_uniform(codec3, codec4):
     assert np.allclose(out[0, 0], vhat.mean(axis=0), rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- O6b Sparse V
+def _sparse_case(codec3, codec4, T, Hq, qscale, seed):
+    rng = np.random.default_rng(seed)
+    K = O.encode(codec3, rng.standard_normal((T, 128)))
+    V = O.encode(codec4, rng.standard_normal((T, 128)))
+    q = qscale * rng.standard_normal((1, Hq, 128))
+    return K, V, q
+
+
+def test_sparse_v_gate_zero_is_plain_attention(codec3, codec4):
+    K, V, q = _sparse_case(codec3, codec4, 300, 2, 3.0, 21)
+    ref = O.decode_attn_materialized(codec3, codec4, q, K, V, 1, 2, 1, 300, 1 / math.sqrt(128))
+    out, keep, _ = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, 2, 1, 300, 1 / math.sqrt(128), 0.0, 64)
+    assert keep.all()
+    assert np.array_equal(out, ref)
+
+
+def test_sparse_v_one_chunk_is_softmax_threshold(codec3, codec4):
+    # one chunk over the whole context: the gate is "softmax weight < gate",
+    # with the weights from SciPy's softmax of the scaled scores
+    from scipy import special
+    T, Hq, gate = 300, 2, 1e-3
+    K, V, q = _sparse_case(codec3, codec4, T, Hq, 3.0, 22)
+    w = special.softmax(O.score(codec3, q[0], K) / math.sqrt(128), axis=-1)
+    vhat = O.dequantize(codec4, V)
+    out, keep, local = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, Hq, 1, T, 1 / math.sqrt(128), gate, T)
+    assert np.array_equal(keep[0], w >= gate)
+    assert 0.1 < keep.mean() < 0.9                       # the case really gates
+    assert not np.array_equal(keep[0, 0], keep[0, 1])    # per head
+    assert np.allclose(local[0], w, rtol=1e-12, atol=0)
+    ref = (w * keep[0]) @ vhat
+    assert np.allclose(out[0], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_v_chunked_gate_is_conservative_and_bounded(codec3, codec4):
+    from scipy import special
+    T, Hq, gate = 1000, 2, 2e-3
+    K, V, q = _sparse_case(codec3, codec4, T, Hq, 3.0, 23)
+    w = special.softmax(O.score(codec3, q[0], K) / math.sqrt(128), axis=-1)
+    vhat = O.dequantize(codec4, V)
+    out, keep, local = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, Hq, 1, T, 1 / math.sqrt(128), gate, 128)
+    assert (~keep).sum() > 100
+    assert np.all(local[0] >= w * (1 - 1e-12))           # chunk-local weight bounds the final one
+    assert np.all(w[~keep[0]] < gate)                    # every dropped position is below the gate
+    full = O.decode_attn_materialized(codec3, codec4, q, K, V, 1, Hq, 1, T, 1 / math.sqrt(128))
+    dropped = (w * ~keep[0]) @ np.abs(vhat)              # per-coordinate bound on the dropped mass
+    assert np.all(np.abs(full[0] - out[0]) <= dropped * (1 + 1e-9) + 1e-15)
+    assert np.all(np.abs(full[0] - out[0]).max(axis=-1) <= gate * (~keep[0]).sum(axis=-1) * np.abs(vhat).max())
+
+
+def test_sparse_v_gate_uses_the_chunk_maximum(codec3, codec4):
+    # chunk 0 holds one dominant key; chunk 1 has no strong key, so its own
+    # maximum keeps every one of its positions although their final weights
+    # are negligible
+    T, gate = 128, 1e-3
+    K, V, q = _sparse_case(codec3, codec4, T, 1, 0.01, 24)
+    j = int(np.argmax(O.score(codec3, q[0], K)[0, :64]))
+    K = dict(K); K["norm"] = K["norm"].copy(); K["norm"][j] *= 1e4
+    out, keep, _ = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, 1, 1, T, 1.0, gate, 64)
+    want = np.zeros(T, dtype=bool); want[j] = True; want[64:] = True
+    assert np.array_equal(keep[0, 0], want)
+    vhat = O.dequantize(codec4, V)
+    assert np.allclose(out[0, 0], vhat[j], rtol=1e-12, atol=1e-12)
+
+
 def test_dequantize_unbiased_over_qjl_matrix():
     # E_S[v̂] = v for a fixed rotation
     d = 32
