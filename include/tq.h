@@ -202,6 +202,33 @@ tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype
                            tq_packed_t v, int64_t ctx_len, float softmax_scale, void* out,
                            tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- Sparse V decode attention
+ * tq_decode_attn with the value dequantization gated by the attention weights
+ * (TurboQuant+ 深度解析, 第六部分 Sparse V Dequant: positions whose weight is
+ * negligible, below about 1e-6, are not decompressed).
+ * The context is processed in chunks of tq_decode_attn_chunk(n_q_heads,
+ * n_kv_heads) consecutive positions.  For query head h and position t in
+ * chunk c, with s = softmax_scale · ℓ, m_hc = max of s over the chunk and
+ * l_hc = Σ_chunk exp(s - m_hc):
+ *   the term of v̂_t is dropped for head h iff exp(s_ht - m_hc) < v_gate · l_hc.
+ * This chunk-local weight is never below the final softmax weight, so every
+ * dropped position has a final weight below v_gate and the output differs from
+ * tq_decode_attn by at most v_gate · (dropped positions) · max ||v̂||_∞ per
+ * element.  The softmax normaliser still sums every position.  A run of keys
+ * dropped for every head of a KV group is not read from V at all.
+ *   v_gate : in [0, 1); 0 drops nothing (the result then equals tq_decode_attn
+ *            up to fp32 rounding order).
+ * Other arguments, workspace and errors as tq_decode_attn; TQ_ERROR_INVALID_VALUE
+ * for v_gate outside [0, 1) or NaN. */
+tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k,
+                                    tq_packed_t v, int64_t ctx_len, float softmax_scale, float v_gate,
+                                    void* out, tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream);
+/* Positions per chunk of the decode split (the Sparse V gate's normalisation
+ * window): 1024 for at most 4 query heads per KV head, 512 for at most 8, 256
+ * above.  0 for invalid head counts. */
+int32_t tq_decode_attn_chunk(int32_t n_q_heads, int32_t n_kv_heads);
+
 /* ---------------------------------------------------------------- search
  * Exhaustive inner-product search over a compressed database
  * (深度拆解 第三部分 向量搜索: the compressed vectors are the index; nothing

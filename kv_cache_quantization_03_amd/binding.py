@@ -60,6 +60,9 @@ def _load():
         "tq_decode_attn_workspace": (sz, [vp, vp, i32, i32, i32, i64]),
         "tq_decode_attn": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, i64, C.c_float, vp, C.c_int,
                                      vp, sz, vp]),
+        "tq_decode_attn_sparse_v": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, i64, C.c_float, C.c_float,
+                                              vp, C.c_int, vp, sz, vp]),
+        "tq_decode_attn_chunk": (i32, [i32, i32]),
         "tq_search_workspace": (sz, [vp, i64, i32, i32]),
         "tq_search_topk": (C.c_int, [vp, P, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
         "tq_diag_stream_blocks": (i32, []),
@@ -76,7 +79,7 @@ lib = _load()
 EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_build_host", "tq_codec_create",
             "tq_codec_destroy", "tq_codec_info", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
-            "tq_decode_attn_workspace", "tq_decode_attn",
+            "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
             "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
 
 
@@ -282,6 +285,28 @@ def tq_decode_attn(ck: Codec, cv: Codec, q, k: Packed, v: Packed, ctx_len: int, 
                             float(softmax_scale), _ptr(out), _dt(out), _ptr(ws), ws.numel(), _stream(q))
     _check(st, "tq_decode_attn")
     return out
+
+
+def tq_decode_attn_sparse_v(ck: Codec, cv: Codec, q, k: Packed, v: Packed, ctx_len: int, n_kv_heads: int,
+                            softmax_scale: float, v_gate: float, out_dtype=None, out=None, ws=None):
+    """tq_decode_attn with the value term of (head, position) dropped when its
+    chunk-local weight is below v_gate."""
+    torch = _torch()
+    batch, hq, d = q.shape
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=out_dtype, device=q.device)
+    need = tq_decode_attn_workspace(ck, cv, batch, hq, n_kv_heads, ctx_len)
+    ws = ws if ws is not None else _workspace(need, q.device)
+    st = lib.tq_decode_attn_sparse_v(ck.handle, cv.handle, _ptr(q), _dt(q), batch, hq, n_kv_heads, k.c(), v.c(),
+                                     ctx_len, float(softmax_scale), float(v_gate), _ptr(out), _dt(out), _ptr(ws),
+                                     ws.numel(), _stream(q))
+    _check(st, "tq_decode_attn_sparse_v")
+    return out
+
+
+def tq_decode_attn_chunk(n_q_heads: int, n_kv_heads: int) -> int:
+    return lib.tq_decode_attn_chunk(n_q_heads, n_kv_heads)
 
 
 # ---------------------------------------------------------------- search

@@ -34,10 +34,12 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 }  // namespace
 
-// Partials per (bk, chunk, g): [mx, l, M[d], J[m]].
+// Partials per (bk, chunk, g): [mx, l, M[d], J[m]].  gate > 0 (Sparse V): the
+// value term of (head, key) is dropped when exp(s - mx) < gate · l, l keeps
+// every key, and a key dropped for every head is not read.
 __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
     DevParams PK, DevParams PV, const float* __restrict__ qrot, const float* __restrict__ proj, int Hq, int nkv,
-    int64_t ctx, int CH, tq_packed_t K, tq_packed_t V, float scale, float* __restrict__ part) {
+    int64_t ctx, int CH, tq_packed_t K, tq_packed_t V, float scale, float gate, float* __restrict__ part) {
   extern __shared__ float smem[];  // s[G][CH] then red[4]
   const int G = Hq / nkv;
   const int bk = blockIdx.y, chunk = blockIdx.x;
@@ -98,6 +100,11 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
       acc += e;
     }
     lsum[g] = block_reduce(acc, red, false);
+    if (gate > 0.f) {  // the same threads rewrite the weights they wrote
+      const float thr = gate * lsum[g];
+      for (int tl = threadIdx.x; tl < CH; tl += kAttnThreads)
+        if (s[g * CH + tl] < thr) s[g * CH + tl] = 0.f;
+    }
   }
   __syncthreads();
   // ---- V accumulation: threads [0,128) own coordinates of M, [128,256) QJL indices of J
@@ -110,6 +117,11 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
   for (int g = 0; g < G; ++g)
     for (int u = 0; u < per; ++u) acc[g][u] = 0.f;
   for (int tl = 0; tl < n_in; ++tl) {
+    if (gate > 0.f) {  // uniform over the block: every thread reads the same weights
+      bool any = false;
+      for (int g = 0; g < G; ++g) any = any || s[g * CH + tl] > 0.f;
+      if (!any) continue;
+    }
     const int64_t row = static_cast<int64_t>(bk) * ctx + t0 + tl;
     const float nu = V.norm[row];
     const float scl = is_m ? nu : nu * V.rnorm[row];
@@ -287,11 +299,13 @@ bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_he
 int decode_mfma_chunk();
 hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
                               int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
-                              float* part, int n_chunks, hipStream_t s);
+                              bool sparse_v, float v_gate, float* part, int n_chunks, hipStream_t s);
+
+int decode_chunk(int n_q_heads, int n_kv_heads) { return attn_chunk(n_q_heads / n_kv_heads); }
 
 hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
                          int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
-                         void* out, tq_dtype_t out_dt, void* ws, hipStream_t s) {
+                         bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws, hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int CH = attn_chunk(G);
   int n_chunks = static_cast<int>(ceil_div(ctx, CH));
@@ -302,14 +316,16 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   hipError_t e;
   if (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH) {
     // matrix-core split kernel (query prep inside); same partial layout
-    e = launch_decode_mfma(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, part, n_chunks, s);
+    e = launch_decode_mfma(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, sparse_v, v_gate, part,
+                           n_chunks, s);
     if (e != hipSuccess) return e;
   } else {
     e = launch_qprep(ck, q, q_dt, nq, qrot, proj, s);
     if (e != hipSuccess) return e;
     const size_t sh = (static_cast<size_t>(G) * CH + 8) * sizeof(float);
     hipLaunchKernelGGL(decode_split_kernel, dim3(n_chunks, batch * n_kv_heads), dim3(kAttnThreads), sh, s, ck->prm,
-                       cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, part);
+                       cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, sparse_v ? v_gate : 0.f,
+                       part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   auto run = [&]<int E>() -> hipError_t {

@@ -12,6 +12,10 @@
 //      operands and the V bit planes as fp4 B operands;
 //   5. the chunk partials (max, Σw, M, J) go to the combine kernel, which
 //      merges the chunks (log-sum-exp) and maps back to the input domain.
+// The Sparse V variant (GATE) drops the value term of a (query head, key)
+// whose weight normalised within the chunk, exp(s - m_c) / l_c, is below the
+// gate, and a wave whose 128 keys are all dropped for every head of its group
+// loads no V record and runs none of step 4.  The normaliser keeps every key.
 // Pages: 「谷歌 TurboQuant 深度拆解」 第二部分 (the unbiased estimator);
 // 「TurboQuant+ 深度解析」 第五部分 (V compressed like K) and 第六部分 (V
 // dequantization dominates long-context decode).
@@ -74,10 +78,10 @@ __device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (r
 
 }  // namespace
 
-template <int NPK, int NPV, typename T>
+template <int NPK, int NPV, typename T, bool GATE>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     const T* q, DevParams PK, DevParams PV, const float* DsignK, const float* MtK, int Hq, int nkv, int ctx,
-    int n_chunks, float scale, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
+    int n_chunks, float scale, float gate, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
     const float* __restrict__ kn, const float* __restrict__ kr, const uint32_t* __restrict__ vc,
     const uint32_t* __restrict__ vs, const float* __restrict__ vn, const float* __restrict__ vr,
     float* __restrict__ part) {
@@ -135,26 +139,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     }
   }
 
-  // V: lane loads the whole records of keys kbase + 32·(lane/16) + v_key_of_row(lane%16 + 16·reg).
-  // Issued only now: held through the query prep they push the kernel past 128
-  // registers, and then a CU runs one 8-wave block instead of two.
+  // V: lane loads the whole records of keys kbase + 32·(lane/16) + v_key_of_row(lane%16 + 16·reg),
+  // and ν, γ of V for the scoring layout (key 16t + lane%16 of the wave).
+  // Issued only after the scores: held through the query prep they push the
+  // kernel past 128 registers, and then a CU runs one 8-wave block instead of
+  // two.  The gated kernel issues them once the gate has kept the wave.
   v4u vcv[2][NBV], vsv[2];
-#pragma unroll
-  for (int reg = 0; reg < 2; ++reg) {
-    const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
-    const int64_t row = hrow + key;
-#pragma unroll
-    for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
-    vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
-  }
-  // ν and γ of V for the scoring layout: key 16t + lane%16 of the wave
   float vnu[8], vga[8];
+  auto load_v = [&]() {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
-    vnu[t] = vn[row];
-    vga[t] = vr[row];
-  }
+    for (int reg = 0; reg < 2; ++reg) {
+      const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
+      const int64_t row = hrow + key;
+#pragma unroll
+      for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
+      vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
+      vnu[t] = vn[row];
+      vga[t] = vr[row];
+    }
+  };
+  if constexpr (!GATE) load_v();
 
   // ---- chunk maximum per head
   {
@@ -169,164 +177,192 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
 #pragma unroll
   for (int w = 1; w < kDecWaves; ++w) mg = fmaxf(mg, hmax[w][g]);
 
-  // ---- softmax weights and the V weight operands.
-  // The matrix op aligns the products of each group of 8 contraction
-  // elements to the largest and keeps 13 bits below it (measured on gfx950),
-  // so floating-point limbs of weights that span many octaves lose the small
-  // ones.  Instead u = w ν (MSE) and u = 2 w ν γ (QJL) become 16-bit fixed
-  // point relative to the maximum of their (head, 32-key block): four base-16
-  // digits, each an exact fp8 integer (times the nibble's 1/value), so every
-  // product sum is exact.  The block exponent and the digit weight 16^-l go
-  // into the op's per-block E8M0 scale (row r, keys 32b..32b+31: lane 16b + r).
-  // LW[type][g][key] = the key's four digit bytes; ub = block exponents.
-  uint32_t* LW = wsc[wv];
-  {
-    float u[2][8];
-    float l_sum = 0.f;
+  // ---- softmax weights against the chunk maximum; the sum keeps every key
+  float wt[8];
+  float l_sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    wt[t] = s[t] == -INFINITY ? 0.f : __expf(s[t] - mg);
+    l_sum += wt[t];
+  }
+  l_sum = row_sum(l_sum);
+  if (kl == 0) hsum[wv][g][0] = l_sum;
+  bool wave_on = true;
+  if constexpr (GATE) {
+    // Sparse V gate: keep (head, key) iff exp(s - m_c) >= gate · l_c
+    __syncthreads();
+    float lc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) lc += hsum[w][g][0];
+    const float thr = gate * lc;
+    bool any = false;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const float w = s[t] == -INFINITY ? 0.f : __expf(s[t] - mg);
-      l_sum += w;
-      u[0][t] = w * vnu[t];
-      u[1][t] = 2.f * u[0][t] * vga[t];
+      wt[t] = wt[t] >= thr ? wt[t] : 0.f;
+      any = any || wt[t] > 0.f;
     }
-    int eb[2][4];
-#pragma unroll
-    for (int ty = 0; ty < 2; ++ty) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {  // block kb = keys 32kb..32kb+31 = tiles 2kb, 2kb+1
-        const float m = row_max(fmaxf(u[ty][2 * kb], u[ty][2 * kb + 1]));
-        int e = 0;
-        if (m > 0.f) (void)frexpf(m, &e);  // m in [2^(e-1), 2^e)
-        eb[ty][kb] = max(e - 1, -100);
-        if (kl == 0) ubexp[wv][ty][g][kb] = eb[ty][kb];
-      }
-    }
-    float w_all = 0.f, w_3 = 0.f, q_n3 = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int key = 16 * t + kl;    // within the wave
-      const int r = (key & 31) >> 3;  // FP4 mask index of this key in the B operand
-      const float inv_val = r == 0 ? 2.f : (r == 1 ? 1.f : (r == 2 ? 0.5f : -0.5f));
-#pragma unroll
-      for (int ty = 0; ty < 2; ++ty) {
-        const int e = eb[ty][t >> 1];
-        const float V = fminf(rintf(ldexpf(u[ty][t], 15 - e)), 65535.f);  // 16-bit fixed point
-        const float ut = ldexpf(V, e - 15);                                 // the value the digits carry
-        if (ty == 0) {
-          w_all += ut;
-          if (r == 3) w_3 += ut;
-        } else if (r != 3) {
-          q_n3 += 0.5f * ut;
-        }
-        const float d0 = floorf(V * 0.000244140625f);
-        const float r1 = fmaf(d0, -4096.f, V);
-        const float d1 = floorf(r1 * 0.00390625f);
-        const float r2 = fmaf(d1, -256.f, r1);
-        const float d2 = floorf(r2 * 0.0625f);
-        const float d3 = fmaf(d2, -16.f, r2);
-        uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(d0 * inv_val, d1 * inv_val, 0, false));
-        dw = static_cast<uint32_t>(
-            __builtin_amdgcn_cvt_pk_fp8_f32(d2 * inv_val, d3 * inv_val, static_cast<int>(dw), true));
-        LW[(ty * 4 + g) * kDecKeysPerWave + key] = dw;
-      }
-    }
-    l_sum = row_sum(l_sum);
-    w_all = row_sum(w_all);
-    w_3 = row_sum(w_3);
-    q_n3 = row_sum(q_n3);
-    if (kl == 0) {
-      hsum[wv][g][0] = l_sum;
-      hsum[wv][g][1] = w_all;
-      hsum[wv][g][2] = w_3;
-      hsum[wv][g][3] = q_n3;
-    }
+    wave_on = __builtin_amdgcn_ballot_w64(any) != 0;  // heads g >= G have no weight
   }
-  __builtin_amdgcn_wave_barrier();
-  // A operands: lane (row 4g'+l, group grp) holds digit l of keys 16grp..+15 and
-  // 64+16grp..+15 (A byte order measured on gfx950); its E8M0 scale serves
-  // row 4g'+l of key block grp: 2^(block exponent - 3 - 4l).
-  v8i av[2];
-  int sav[2];
-  {
-    const int row = lane & 15, grp = lane >> 4, gq = row >> 2, l = row & 3;
-    const uint32_t sel = static_cast<uint32_t>(l) | (static_cast<uint32_t>(4 + l) << 8) | 0x0C0C0000u;
-#pragma unroll
-    for (int ty = 0; ty < 2; ++ty) {
-      const uint32_t* src = LW + (ty * 4 + gq) * kDecKeysPerWave;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key0 = (j < 4 ? 16 * grp + 4 * j : 64 + 16 * grp + 4 * (j - 4));
-        const v4u d4 = *reinterpret_cast<const v4u*>(src + key0);
-        const uint32_t lo = __builtin_amdgcn_perm(d4[1], d4[0], sel);
-        const uint32_t hi = __builtin_amdgcn_perm(d4[3], d4[2], sel);
-        av[ty][j] = static_cast<int>((lo & 0xFFFFu) | (hi << 16));
-      }
-      sav[ty] = 127 + ubexp[wv][ty][gq][grp] - 3 - 4 * l;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  // ---- V on the matrix cores: per plane and 16-coordinate block cb,
-  // Σ_k A[row][k] B[k][n] with B the transposed bits of coordinate 16cb + n
   float macc[8], jacc[8];
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) macc[cb] = jacc[cb] = 0.f;
-  uint32_t par[8];
+  if (!wave_on) {
+    if (kl == 0) hsum[wv][g][1] = hsum[wv][g][2] = hsum[wv][g][3] = 0.f;
+  } else {
+    if constexpr (GATE) load_v();
+
+    // ---- the V weight operands.
+    // The matrix op aligns the products of each group of 8 contraction
+    // elements to the largest and keeps 13 bits below it (measured on gfx950),
+    // so floating-point limbs of weights that span many octaves lose the small
+    // ones.  Instead u = w ν (MSE) and u = 2 w ν γ (QJL) become 16-bit fixed
+    // point relative to the maximum of their (head, 32-key block): four base-16
+    // digits, each an exact fp8 integer (times the nibble's 1/value), so every
+    // product sum is exact.  The block exponent and the digit weight 16^-l go
+    // into the op's per-block E8M0 scale (row r, keys 32b..32b+31: lane 16b + r).
+    // LW[type][g][key] = the key's four digit bytes; ub = block exponents.
+    uint32_t* LW = wsc[wv];
+    {
+      float u[2][8];
 #pragma unroll
-  for (int cb = 0; cb < 8; ++cb) par[cb] = 0u;
-  const v4f zero = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 8; ++t) {
+        u[0][t] = wt[t] * vnu[t];
+        u[1][t] = 2.f * u[0][t] * vga[t];
+      }
+      int eb[2][4];
 #pragma unroll
-  for (int p = 0; p <= NBV; ++p) {  // stored planes, then the signs
-    uint32_t tw[8];
+      for (int ty = 0; ty < 2; ++ty) {
 #pragma unroll
-    for (int wb = 0; wb < 4; ++wb) {
-      uint32_t r0 = p < NBV ? vcv[0][p < NBV ? p : 0][wb] : vsv[0][wb];
-      uint32_t r1 = p < NBV ? vcv[1][p < NBV ? p : 0][wb] : vsv[1][wb];
-      transpose32(r0, r1, lane);
-      tw[2 * wb] = r0;
-      tw[2 * wb + 1] = r1;
+        for (int kb = 0; kb < 4; ++kb) {  // block kb = keys 32kb..32kb+31 = tiles 2kb, 2kb+1
+          const float m = row_max(fmaxf(u[ty][2 * kb], u[ty][2 * kb + 1]));
+          int e = 0;
+          if (m > 0.f) (void)frexpf(m, &e);  // m in [2^(e-1), 2^e)
+          eb[ty][kb] = max(e - 1, -100);
+          if (kl == 0) ubexp[wv][ty][g][kb] = eb[ty][kb];
+        }
+      }
+      float w_all = 0.f, w_3 = 0.f, q_n3 = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int key = 16 * t + kl;    // within the wave
+        const int r = (key & 31) >> 3;  // FP4 mask index of this key in the B operand
+        const float inv_val = r == 0 ? 2.f : (r == 1 ? 1.f : (r == 2 ? 0.5f : -0.5f));
+#pragma unroll
+        for (int ty = 0; ty < 2; ++ty) {
+          const int e = eb[ty][t >> 1];
+          const float V = fminf(rintf(ldexpf(u[ty][t], 15 - e)), 65535.f);  // 16-bit fixed point
+          const float ut = ldexpf(V, e - 15);                                 // the value the digits carry
+          if (ty == 0) {
+            w_all += ut;
+            if (r == 3) w_3 += ut;
+          } else if (r != 3) {
+            q_n3 += 0.5f * ut;
+          }
+          const float d0 = floorf(V * 0.000244140625f);
+          const float r1 = fmaf(d0, -4096.f, V);
+          const float d1 = floorf(r1 * 0.00390625f);
+          const float r2 = fmaf(d1, -256.f, r1);
+          const float d2 = floorf(r2 * 0.0625f);
+          const float d3 = fmaf(d2, -16.f, r2);
+          uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(d0 * inv_val, d1 * inv_val, 0, false));
+          dw = static_cast<uint32_t>(
+              __builtin_amdgcn_cvt_pk_fp8_f32(d2 * inv_val, d3 * inv_val, static_cast<int>(dw), true));
+          LW[(ty * 4 + g) * kDecKeysPerWave + key] = dw;
+        }
+      }
+      w_all = row_sum(w_all);
+      w_3 = row_sum(w_3);
+      q_n3 = row_sum(q_n3);
+      if (kl == 0) {
+        hsum[wv][g][1] = w_all;
+        hsum[wv][g][2] = w_3;
+        hsum[wv][g][3] = q_n3;
+      }
     }
-    // two halves of four 16-coordinate blocks keep the live accumulators at 8 registers
+    __builtin_amdgcn_wave_barrier();
+    // A operands: lane (row 4g'+l, group grp) holds digit l of keys 16grp..+15 and
+    // 64+16grp..+15 (A byte order measured on gfx950); its E8M0 scale serves
+    // row 4g'+l of key block grp: 2^(block exponent - 3 - 4l).
+    v8i av[2];
+    int sav[2];
+    {
+      const int row = lane & 15, grp = lane >> 4, gq = row >> 2, l = row & 3;
+      const uint32_t sel = static_cast<uint32_t>(l) | (static_cast<uint32_t>(4 + l) << 8) | 0x0C0C0000u;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      v4f acc[4], accp[4];
+      for (int ty = 0; ty < 2; ++ty) {
+        const uint32_t* src = LW + (ty * 4 + gq) * kDecKeysPerWave;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[c] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[4 * hb + c]), zero,
-                                     p < NBV ? sav[0] : sav[1]);
-      if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
-        if (p == NBV - 1) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            accp[c] = mfma_fp8_fp4_scaled(av[0], fp4_operand(par[4 * hb + c] ^ tw[4 * hb + c]), zero, sav[0]);
+        for (int j = 0; j < 8; ++j) {
+          const int key0 = (j < 4 ? 16 * grp + 4 * j : 64 + 16 * grp + 4 * (j - 4));
+          const v4u d4 = *reinterpret_cast<const v4u*>(src + key0);
+          const uint32_t lo = __builtin_amdgcn_perm(d4[1], d4[0], sel);
+          const uint32_t hi = __builtin_amdgcn_perm(d4[3], d4[2], sel);
+          av[ty][j] = static_cast<int>((lo & 0xFFFFu) | (hi << 16));
         }
+        sav[ty] = 127 + ubexp[wv][ty][gq][grp] - 3 - 4 * l;
       }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- V on the matrix cores: per plane and 16-coordinate block cb,
+    // Σ_k A[row][k] B[k][n] with B the transposed bits of coordinate 16cb + n
+    uint32_t par[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(acc[c]));
+    for (int cb = 0; cb < 8; ++cb) par[cb] = 0u;
+    const v4f zero = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cb = 4 * hb + c;
-        const float v = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);  // digit weights are in the scales
-        if (p < NBV) {
-          macc[cb] = fmaf(PV.plane_coef[p < NBV ? p : 0], v, macc[cb]);
-          par[cb] ^= tw[cb];
-        } else {
-          jacc[cb] = v;
+    for (int p = 0; p <= NBV; ++p) {  // stored planes, then the signs
+      uint32_t tw[8];
+#pragma unroll
+      for (int wb = 0; wb < 4; ++wb) {
+        uint32_t r0 = p < NBV ? vcv[0][p < NBV ? p : 0][wb] : vsv[0][wb];
+        uint32_t r1 = p < NBV ? vcv[1][p < NBV ? p : 0][wb] : vsv[1][wb];
+        transpose32(r0, r1, lane);
+        tw[2 * wb] = r0;
+        tw[2 * wb + 1] = r1;
+      }
+      // two halves of four 16-coordinate blocks keep the live accumulators at 8 registers
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        v4f acc[4], accp[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[4 * hb + c]), zero,
+                                       p < NBV ? sav[0] : sav[1]);
+        if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
+          if (p == NBV - 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              accp[c] = mfma_fp8_fp4_scaled(av[0], fp4_operand(par[4 * hb + c] ^ tw[4 * hb + c]), zero, sav[0]);
+          }
         }
-      }
-      if constexpr (NPV > NBV) {
-        if (p == NBV - 1) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            asm volatile("" : "+v"(accp[c]));
-            const float v = (accp[c][0] + accp[c][1]) + (accp[c][2] + accp[c][3]);
-            macc[4 * hb + c] = fmaf(PV.plane_coef[NPV - 1], v, macc[4 * hb + c]);
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(acc[c]));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int cb = 4 * hb + c;
+          const float v = (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);  // digit weights are in the scales
+          if (p < NBV) {
+            macc[cb] = fmaf(PV.plane_coef[p < NBV ? p : 0], v, macc[cb]);
+            par[cb] ^= tw[cb];
+          } else {
+            jacc[cb] = v;
+          }
+        }
+        if constexpr (NPV > NBV) {
+          if (p == NBV - 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              asm volatile("" : "+v"(accp[c]));
+              const float v = (accp[c][0] + accp[c][1]) + (accp[c][2] + accp[c][3]);
+              macc[4 * hb + c] = fmaf(PV.plane_coef[NPV - 1], v, macc[4 * hb + c]);
+            }
           }
         }
       }
     }
-  }
+
+  }  // wave_on
 
   // ---- chunk partials: sum the 8 waves, add the per-head constant terms
   __syncthreads();  // every wave is done with its scratch
@@ -381,11 +417,13 @@ int decode_mfma_chunk() { return kDecChunk; }
 
 hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
                               int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
-                              float* part, int n_chunks, hipStream_t s) {
+                              bool sparse_v, float v_gate, float* part, int n_chunks, hipStream_t s) {
   auto go = [&]<int NPK, int NPV, typename T>(const T* qq) -> hipError_t {
-    hipLaunchKernelGGL((decode_mfma_kernel<NPK, NPV, T>), dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
+    auto kern = sparse_v ? decode_mfma_kernel<NPK, NPV, T, true> : decode_mfma_kernel<NPK, NPV, T, false>;
+    hipLaunchKernelGGL(kern, dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
                        0, s, qq, ck->prm, cv->prm, ck->dD, ck->dMt, n_q_heads, n_kv_heads, static_cast<int>(ctx),
-                       n_chunks, scale, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm, part);
+                       n_chunks, scale, v_gate, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm,
+                       part);
     return hipGetLastError();
   };
   auto by_v = [&]<int NPK, typename T>(const T* qq) -> hipError_t {

@@ -196,12 +196,11 @@ extern "C" size_t tq_decode_attn_workspace(tq_codec_t ck, tq_codec_t cv, int32_t
   return tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len);
 }
 
-extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
-                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
-                                      tq_packed_t k, tq_packed_t v, int64_t ctx_len,
-                                      float softmax_scale, void* out, tq_dtype_t out_dt, void* ws,
-                                      size_t ws_bytes, void* stream) {
-  tq::clear_error();
+namespace {
+tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt, int32_t batch,
+                          int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx_len,
+                          float softmax_scale, bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws,
+                          size_t ws_bytes, void* stream, const char* name) {
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
@@ -217,10 +216,39 @@ extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* 
   if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
   if ((st = check_packed(v, "v")) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len))) != TQ_SUCCESS) return st;
-  if (log_enabled()) std::fprintf(stderr, "[tq] decode b=%d hq=%d hkv=%d ctx=%lld\n", batch, n_q_heads, n_kv_heads, (long long)ctx_len);
-  hipError_t e = tq::launch_decode(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len,
-                                   softmax_scale, out, out_dt, ws, static_cast<hipStream_t>(stream));
-  return finish(e, "tq_decode_attn launch");
+  if (log_enabled())
+    std::fprintf(stderr, "[tq] %s b=%d hq=%d hkv=%d ctx=%lld gate=%g\n", name, batch, n_q_heads, n_kv_heads,
+                 (long long)ctx_len, sparse_v ? v_gate : 0.0);
+  hipError_t e = tq::launch_decode(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale,
+                                   sparse_v, v_gate, out, out_dt, ws, static_cast<hipStream_t>(stream));
+  return finish(e, name);
+}
+}  // namespace
+
+extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                      int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      tq_packed_t k, tq_packed_t v, int64_t ctx_len,
+                                      float softmax_scale, void* out, tq_dtype_t out_dt, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, false, 0.f, out,
+                       out_dt, ws, ws_bytes, stream, "tq_decode_attn");
+}
+
+extern "C" tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                               tq_packed_t k, tq_packed_t v, int64_t ctx_len,
+                                               float softmax_scale, float v_gate, void* out, tq_dtype_t out_dt,
+                                               void* ws, size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!(v_gate >= 0.f && v_gate < 1.f)) { set_error("v_gate must be in [0, 1)"); return TQ_ERROR_INVALID_VALUE; }
+  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, true, v_gate,
+                       out, out_dt, ws, ws_bytes, stream, "tq_decode_attn_sparse_v");
+}
+
+extern "C" int32_t tq_decode_attn_chunk(int32_t n_q_heads, int32_t n_kv_heads) {
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return 0;
+  return tq::decode_chunk(n_q_heads, n_kv_heads);
 }
 
 // ---------------------------------------------------------------- search

@@ -101,10 +101,11 @@ hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch,
 bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why);
 size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads,
                        int n_kv_heads, int64_t ctx);
+int decode_chunk(int n_q_heads, int n_kv_heads);
 hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
                          int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v,
-                         int64_t ctx, float scale, void* out, tq_dtype_t out_dt, void* ws,
-                         hipStream_t s);
+                         int64_t ctx, float scale, bool sparse_v, float v_gate, void* out,
+                         tq_dtype_t out_dt, void* ws, hipStream_t s);
 
 size_t search_ws_bytes(const tq_codec_s* c, int64_t n_db, int n_queries, int topk);
 hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, const float* queries,

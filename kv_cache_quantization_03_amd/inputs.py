@@ -136,6 +136,47 @@ class GaussianMixtureUnit:
         return _cast(self.rows64(lo, hi), self.dtype)
 
 
+@dataclass
+class NeedleKeys:
+    """Rows of a Gaussian workload plus beta · u_g on a seeded Bernoulli(p)
+    subset of rows ("needles"), u_g a given unit vector per group of
+    `group_rows` consecutive rows."""
+    base: Gaussian
+    directions: np.ndarray  # [n_groups][d], unit vectors
+    group_rows: int
+    p: float
+    beta: float
+    seed: int
+    dtype: str = "bf16"
+
+    def __post_init__(self):
+        self.n_rows, self.d = self.base.n_rows, self.base.d
+        self._block_seeds = np.random.SeedSequence(self.seed).spawn(max(1, math.ceil(self.n_rows / BLOCK)))
+
+    def needles(self, lo: int = 0, hi: int | None = None) -> np.ndarray:
+        hi = self.n_rows if hi is None else hi
+        out = np.empty(hi - lo, dtype=bool)
+        for blk in range(lo // BLOCK, (hi - 1) // BLOCK + 1):
+            rng = np.random.Generator(np.random.PCG64(self._block_seeds[blk]))
+            base = blk * BLOCK
+            n = min(BLOCK, self.n_rows - base)
+            m = rng.random(n) < self.p
+            s, e = max(lo, base), min(hi, base + n)
+            out[s - lo:e - lo] = m[s - base:e - base]
+        return out
+
+    def rows64(self, lo: int, hi: int) -> np.ndarray:
+        out = self.base.rows64(lo, hi)
+        m = self.needles(lo, hi)
+        rows = np.arange(lo, hi)[m]
+        out[m] += self.beta * self.directions[rows // self.group_rows]
+        return out
+
+    def rows(self, lo: int = 0, hi: int | None = None) -> np.ndarray:
+        hi = self.n_rows if hi is None else hi
+        return _cast(self.rows64(lo, hi), self.dtype)
+
+
 # ---------------------------------------------------------------------------
 # The five workloads (sizes can be shrunk for fast tests; defaults are full).
 # Codec seed 1234 everywhere; data seed = workload number.
@@ -186,6 +227,24 @@ def long_decode(ctx=131072, batch=1, n_q_heads=32, n_kv_heads=8, d=128, bits=3):
     return dict(name=f"long_decode_ctx{ctx}_{bits}bit", bits=bits, d=d, keys=keys, values=vals,
                 queries=q, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                 n_queries=1, ctx=ctx, scale=1.0 / math.sqrt(d))
+
+
+def long_decode_needles(ctx=131072, batch=1, n_q_heads=32, n_kv_heads=8, d=128, bits=3, p=1.0 / 512,
+                        beta=64.0):
+    """The long-context decode workload with peaked attention: the same bf16
+    queries, haystack keys and values, plus, with probability p per (KV head,
+    position), a needle key z + beta·u, u the unit vector of the sum of that
+    KV head's query heads.  A needle then scores about beta/2 above a
+    haystack key for every query head of the group, so almost all of the
+    softmax weight sits on the needles."""
+    w = long_decode(ctx=ctx, batch=batch, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads, d=d, bits=bits)
+    G = n_q_heads // n_kv_heads
+    q = w["queries"].rows().astype(np.float64).reshape(batch, n_kv_heads, G, d).sum(axis=2)
+    u = (q / np.linalg.norm(q, axis=-1, keepdims=True)).reshape(batch * n_kv_heads, d)
+    w["keys"] = NeedleKeys(base=w["keys"], directions=u, group_rows=ctx, p=p, beta=beta, seed=404)
+    w["name"] = f"long_decode_needles_ctx{ctx}_{bits}bit"
+    w["needle_p"], w["needle_beta"] = p, beta
+    return w
 
 
 def vector_search(n_db=1_000_000, n_queries=1024, d=1536, n_centers=256, bits=4, k=10):

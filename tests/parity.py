@@ -91,3 +91,22 @@ def oracle_records_like(cd: O.Codec, x64: np.ndarray, gpu: dict) -> dict:
         out["rnorm"][rows] = rd["rnorm"]
     out["signs"] = np.asarray(gpu["signs"]).copy()
     return out
+
+
+def assert_sparse_v_close(out, ref, local, gate, vhat, hkv, ctx, tol):  # batch 1
+    """out vs the gated oracle to `tol` of each row's maximum, plus, for the
+    positions within 1% of the gate (a floating-point decision either side
+    may take), the most their value terms can move the output: the
+    chunk-local weight bounds the final one."""
+    G = out.shape[1] // hkv
+    amb = np.abs(np.log(np.maximum(local[0], 1e-300) / gate)) < 1e-2      # [hq][ctx]
+    slack = np.zeros_like(ref[0])
+    for h in np.nonzero(amb.any(axis=1))[0]:
+        kh = h // G
+        t = np.nonzero(amb[h])[0]
+        slack[h] = local[0, h, t] @ np.abs(vhat[kh * ctx + t])
+    diff = np.abs(out[0] - ref[0])
+    bound = tol * np.max(np.abs(ref[0]), axis=-1, keepdims=True) + 1.01 * slack
+    print(f"  positions near the gate {int(amb.sum())}, max row err {row_rel_err(out, ref).max():.2e}, "
+          f"worst diff/bound {np.max(diff / bound):.3f}", flush=True)
+    assert np.all(diff <= bound)

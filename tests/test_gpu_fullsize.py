@@ -7,7 +7,8 @@ benchmark times, on sampled outputs the oracle computes one by one.
 * prefill encode + logits (16 x 8 x 8192 K and V, log-normal token scales):
   encode parity on sampled K and V rows, the 16 queries' logits on sampled keys.
 * long-context fused decode attention (128K tokens): two KV heads' outputs
-  (eight query heads) against the oracle over all 131072 keys of those heads.
+  (eight query heads) against the oracle over all 131072 keys of those heads;
+  the same with the Sparse V gate on the needle variant of that workload.
 * vector search (1e6 x 1536, 4-bit, top-10): sampled encode parity; for two
   queries, the returned top-10 against the oracle's scores of every database
   record (the GPU-encoded records, whose codes were checked on a sample).
@@ -20,7 +21,7 @@ import pytest
 
 import oracle as O
 from kv_cache_quantization_03_amd import inputs as I
-from tests.parity import check_encode, oracle_records_like, row_rel_err
+from tests.parity import assert_sparse_v_close, check_encode, oracle_records_like, row_rel_err
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -160,6 +161,42 @@ def test_full_long_decode_attention(B):
         err = row_rel_err(g32[:, hs], ref).max()
         say(f"  kv head {kh}: max row err {err:.2e}")
         assert err <= 1e-3
+
+
+def test_full_long_decode_sparse_v(B):
+    # the long-context decode step on the needle workload (peaked attention),
+    # Sparse V gate 1e-6: two KV heads against the gated oracle
+    w = I.long_decode_needles()
+    gate = 1e-6
+    say("Sparse V decode attention, 128K context with needles, gate 1e-6")
+    d, hq, hkv, ctx = 128, 32, 8, 131072
+    G = hq // hkv
+    gc = B.tq_codec_create(d, 3, 0, I.CODEC_SEED)
+    oc = O.make_codec(d, 3, seed=I.CODEC_SEED)
+    k = w["keys"].rows()
+    v = w["values"].rows()
+    kp, vp = B.tq_encode_kv(gc, dev_tensor(k, "bf16"), dev_tensor(v, "bf16"))
+    q = w["queries"].rows().reshape(1, hq, d)
+    chunk = B.tq_decode_attn_chunk(hq, hkv)
+    out32 = B.tq_decode_attn_sparse_v(gc, gc, dev_tensor(q, "bf16"), kp, vp, ctx, hkv, w["scale"], gate,
+                                      out_dtype=torch.float32)
+    out16 = B.tq_decode_attn_sparse_v(gc, gc, dev_tensor(q, "bf16"), kp, vp, ctx, hkv, w["scale"], gate,
+                                      out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = out32.cpu().numpy()
+    assert np.array_equal(out16.float().cpu().numpy(), O.bf16_round(g32))
+    gk, gvv = kp.numpy(), vp.numpy()
+    for kh in (0, hkv - 1):
+        rows = slice(kh * ctx, (kh + 1) * ctx)
+        kr = oracle_records_like(oc, k[rows].astype(np.float64), {kk: x[rows] for kk, x in gk.items()})
+        vr = oracle_records_like(oc, v[rows].astype(np.float64), {kk: x[rows] for kk, x in gvv.items()})
+        hs = slice(kh * G, (kh + 1) * G)
+        ref, keep, local = O.decode_attn_sparse_v(oc, oc, q[:, hs].astype(np.float64), kr, vr, 1, G, 1, ctx,
+                                                  w["scale"], gate, chunk)
+        blocks = np.mean(~keep[0].reshape(G, ctx // 128, 128).any(axis=(0, 2)))
+        say(f"  kv head {kh}: dropped (head, key) {np.mean(~keep):.4f}, 128-key blocks {blocks:.3f}")
+        assert blocks > 0.5
+        assert_sparse_v_close(g32[:, hs], ref, local, gate, O.dequantize(oc, vr), 1, ctx, 1e-3)
 
 
 def test_full_vector_search(B):

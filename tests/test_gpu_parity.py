@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.parity import check_encode, oracle_records_like, row_rel_err, tol_for
+from tests.parity import assert_sparse_v_close, check_encode, oracle_records_like, row_rel_err, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -381,6 +381,85 @@ def test_decode_attn_one_hot(B):
                            out_dtype=torch.float32).cpu().numpy()
     vhat = O.dequantize(oc, vr)[j]
     assert np.max(np.abs(out[0, 0] - vhat)) <= 1e-4 * np.max(np.abs(vhat))
+
+
+# ---------------------------------------------------------------- Sparse V decode attention
+def _sparse_case(hq, hkv, ctx, needles, qscale, seed):
+    """fp32 K, V N(0,1) and queries; with `needles`, position 1024c + 200 of
+    every KV head (one per 1024-key chunk) is z + 60·u, u the unit sum of the
+    group's queries, so one 128-key block per chunk holds all the weight."""
+    rng = np.random.default_rng(seed)
+    G = hq // hkv
+    q = qscale * rng.standard_normal((1, hq, 128))
+    k = rng.standard_normal((hkv * ctx, 128))
+    v = rng.standard_normal((hkv * ctx, 128))
+    if needles:
+        for kh in range(hkv):
+            u = q[0, kh * G:(kh + 1) * G].sum(axis=0)
+            u /= np.linalg.norm(u)
+            for t in range(200, ctx, 1024):
+                k[kh * ctx + t] += 60.0 * u
+    return as_exact(q, "f32"), as_exact(k, "f32"), as_exact(v, "f32")
+
+
+def _dropped_blocks(keep, ctx, hkv):
+    """Fraction of 128-key blocks dropped for every query head of their KV group."""
+    G = keep.shape[1] // hkv
+    nb = ctx // 128
+    k = keep[0, :, :nb * 128].reshape(hkv, G, nb, 128)
+    return float(np.mean(~k.any(axis=(1, 3))))
+
+
+@pytest.mark.parametrize("kbits,vbits,hq,hkv,ctx,gate,needles,qscale",
+                         [(3, 3, 8, 2, 3000, 1e-6, True, 1.0),     # matrix-core kernel, needles
+                          (4, 2, 4, 1, 2049, 1e-3, False, 3.0),    # per-key drops inside kept blocks
+                          (3, 4, 2, 2, 1100, 1e-2, True, 1.0),
+                          (3, 3, 16, 2, 1500, 1e-6, True, 1.0),    # general kernel, 512-key chunks
+                          (2, 3, 16, 1, 700, 1e-3, False, 3.0)])   # general kernel, 256-key chunks
+def test_decode_sparse_v_parity(B, kbits, vbits, hq, hkv, ctx, gate, needles, qscale):
+    say(f"sparse V K{kbits} V{vbits} hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles}")
+    gk, ok = pair(B, 128, kbits)
+    gv, ov = pair(B, 128, vbits)
+    q, k, v = _sparse_case(hq, hkv, ctx, needles, qscale, ctx + hq + kbits)
+    kr, vr = O.encode(ok, k.astype(np.float64)), O.encode(ov, v.astype(np.float64))
+    scale = 1 / math.sqrt(128)
+    chunk = B.tq_decode_attn_chunk(hq, hkv)
+    assert chunk == (1024 if hq // hkv <= 4 else (512 if hq // hkv <= 8 else 256))
+    ref, keep, local = O.decode_attn_sparse_v(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale, gate,
+                                              chunk)
+    blocks = _dropped_blocks(keep, ctx, hkv)
+    say(f"  dropped (head, key) {np.mean(~keep):.3f}, 128-key blocks {blocks:.3f}")
+    assert np.mean(~keep) > 0.3
+    if needles and chunk == 1024:
+        assert blocks > 0.5
+    kp, vp = B.packed_from_numpy(kr), B.packed_from_numpy(vr)
+    out = B.tq_decode_attn_sparse_v(gk, gv, to_dev(q, "f32"), kp, vp, ctx, hkv, scale, gate,
+                                    out_dtype=torch.float32).cpu().numpy()
+    full = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale)
+    say(f"  gated vs ungated oracle {row_rel_err(ref, full).max():.2e}")
+    assert_sparse_v_close(out, ref, local, gate, O.dequantize(ov, vr), hkv, ctx, 1e-4)
+
+
+@pytest.mark.parametrize("hq,hkv,ctx", [(8, 2, 3000), (16, 2, 1500)])
+def test_decode_sparse_v_gate_zero_is_plain_decode(B, hq, hkv, ctx):
+    gc, oc = pair(B, 128, 3)
+    q, k, v = _sparse_case(hq, hkv, ctx, True, 1.0, 99)
+    kp, vp = B.tq_encode_kv(gc, to_dev(k, "f32"), to_dev(v, "f32"))
+    qd = to_dev(q, "bf16")
+    a = B.tq_decode_attn(gc, gc, qd, kp, vp, ctx, hkv, 0.1, out_dtype=torch.float32).cpu().numpy()
+    b = B.tq_decode_attn_sparse_v(gc, gc, qd, kp, vp, ctx, hkv, 0.1, 0.0, out_dtype=torch.float32).cpu().numpy()
+    say(f"sparse V gate 0 vs plain, hq={hq}: bitwise {np.array_equal(a, b)}, err {row_rel_err(b, a).max():.1e}")
+    assert row_rel_err(b, a).max() <= 1e-6
+
+
+def test_decode_sparse_v_rejects_bad_gate(B):
+    gc, _ = pair(B, 128, 3)
+    q, k, v = _sparse_case(4, 1, 100, False, 1.0, 3)
+    kp, vp = B.tq_encode_kv(gc, to_dev(k, "f32"), to_dev(v, "f32"))
+    for bad in (-1e-3, 1.0, float("nan")):
+        with pytest.raises(B.TQError):
+            B.tq_decode_attn_sparse_v(gc, gc, to_dev(q, "f32"), kp, vp, 100, 1, 0.1, bad)
+    assert B.tq_decode_attn_chunk(32, 8) == 1024 and B.tq_decode_attn_chunk(3, 2) == 0
 
 
 # ---------------------------------------------------------------- search
