@@ -2,8 +2,8 @@
 // most 4 query heads per KV head).
 //
 // One block per (batch*kv_head, chunk of 1024 keys), 8 waves of 128 keys:
-//   1. the K query operands are rebuilt in LDS while the records load
-//      (query_prep_*, as in the fused logits kernel);
+//   1. the K records load; the K query operands of the head (prepared once per
+//      KV head by attn_prep_mfma_kernel, the logits path's prep) come from L2;
 //   2. each wave scores its 128 keys on the matrix cores (score_wave_values);
 //   3. softmax against the chunk's per-head maximum;
 //   4. V is accumulated in the codec domain on the matrix cores:
@@ -78,9 +78,9 @@ __device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (r
 
 }  // namespace
 
-template <int NPK, int NPV, typename T, bool GATE>
+template <int NPK, int NPV, bool GATE>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
-    const T* q, DevParams PK, DevParams PV, const float* DsignK, const float* MtK, int Hq, int nkv, int ctx,
+    const uint8_t* __restrict__ prep, DevParams PK, DevParams PV, int Hq, int nkv, int ctx,
     int n_chunks, float scale, float gate, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
     const float* __restrict__ kn, const float* __restrict__ kr, const uint32_t* __restrict__ vc,
     const uint32_t* __restrict__ vs, const float* __restrict__ vn, const float* __restrict__ vr,
@@ -90,7 +90,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   constexpr int NT = kDecWaves * 64, NKB = LK::NKB, NBV = LV::NB;
   constexpr int KSTAGE = kKeysPerWave * (LK::CS + LK::SS);
   constexpr int SCR = KSTAGE > 1024 ? KSTAGE : 1024;  // words of per-wave scratch
-  __shared__ QueryPrepShared<NT, NKB> sh;
   __shared__ __attribute__((aligned(16))) uint32_t wsc[kDecWaves][SCR];
   __shared__ float hmax[kDecWaves][4];
   __shared__ int ubexp[kDecWaves][2][4][4];  // V weight block exponents [type][head][key block]
@@ -99,14 +98,11 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   const int g = lane >> 4, kl = lane & 15;
   const int bk = blockIdx.y, chunk = blockIdx.x;
   const int G = Hq / nkv;
-  const QueryTile tile{bk / nkv, 1, Hq, G, bk % nkv, 0, G};
   const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
   const int64_t hrow = static_cast<int64_t>(bk) * ctx;         // first row of the head
 
-  // ---- loads: query operands first (see query_prep_load), then the K records
-  QueryPrepRegs<NT> pr;
-  query_prep_load<NT>(pr, q, DsignK, MtK, tile);
-  __syncthreads();
+  // ---- loads: the K records, then the head's query operands (prepared once
+  // per KV head by attn_prep_mfma_kernel; L2-resident)
   v4u kcv[2][LK::CW / 4], ksv[2][LK::SW / 4];
   float knu[2], kga[2];
 #pragma unroll
@@ -119,12 +115,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   }
 
   // ---- K query operands, then logits of the wave's 128 keys (8 per lane)
-  query_prep_build<NT, NPK, NKB>(sh, pr, PK, tile);
   float s[8];
   {
     v8i a[1][NKB];
-    query_prep_operands<NT, NKB>(sh, a, lane);
-    const float4 cst = query_prep_constants<NT, NPK, NKB>(sh, PK, g);
+    const uint8_t* base = prep + static_cast<int64_t>(bk) * (NKB * kOpBytes + kConstBytes);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const uint4* src = reinterpret_cast<const uint4*>(base + kb * kOpBytes + lane * 32);
+      const uint4 x = src[0], y = src[1];
+      a[0][kb][0] = x.x; a[0][kb][1] = x.y; a[0][kb][2] = x.z; a[0][kb][3] = x.w;
+      a[0][kb][4] = y.x; a[0][kb][5] = y.y; a[0][kb][6] = y.z; a[0][kb][7] = y.w;
+    }
+    const float4 cst = reinterpret_cast<const float4*>(base + NKB * kOpBytes)[g];
     uint32_t* stage = wsc[wv];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -415,37 +417,30 @@ bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_he
 
 int decode_mfma_chunk() { return kDecChunk; }
 
-hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
-                              int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
-                              bool sparse_v, float v_gate, float* part, int n_chunks, hipStream_t s) {
-  auto go = [&]<int NPK, int NPV, typename T>(const T* qq) -> hipError_t {
-    auto kern = sparse_v ? decode_mfma_kernel<NPK, NPV, T, true> : decode_mfma_kernel<NPK, NPV, T, false>;
+// `prep`: the query operands of every (batch, KV head), as attn_prep_mfma_kernel writes them.
+hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
+                              tq_packed_t k, tq_packed_t v, int64_t ctx, float scale, bool sparse_v, float v_gate,
+                              const uint8_t* prep, float* part, int n_chunks, hipStream_t s) {
+  auto go = [&]<int NPK, int NPV>() -> hipError_t {
+    auto kern = sparse_v ? decode_mfma_kernel<NPK, NPV, true> : decode_mfma_kernel<NPK, NPV, false>;
     hipLaunchKernelGGL(kern, dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
-                       0, s, qq, ck->prm, cv->prm, ck->dD, ck->dMt, n_q_heads, n_kv_heads, static_cast<int>(ctx),
+                       0, s, prep, ck->prm, cv->prm, n_q_heads, n_kv_heads, static_cast<int>(ctx),
                        n_chunks, scale, v_gate, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm,
                        part);
     return hipGetLastError();
   };
-  auto by_v = [&]<int NPK, typename T>(const T* qq) -> hipError_t {
+  auto by_v = [&]<int NPK>() -> hipError_t {
     switch (cv->prm.n_planes) {
-      case 1: return go.template operator()<NPK, 1>(qq);
-      case 2: return go.template operator()<NPK, 2>(qq);
-      case 4: return go.template operator()<NPK, 4>(qq);
+      case 1: return go.template operator()<NPK, 1>();
+      case 2: return go.template operator()<NPK, 2>();
+      case 4: return go.template operator()<NPK, 4>();
     }
     return hipErrorInvalidValue;
   };
-  auto by_k = [&]<typename T>(const T* qq) -> hipError_t {
-    switch (ck->prm.n_planes) {
-      case 1: return by_v.template operator()<1>(qq);
-      case 2: return by_v.template operator()<2>(qq);
-      case 4: return by_v.template operator()<4>(qq);
-    }
-    return hipErrorInvalidValue;
-  };
-  switch (q_dt) {
-    case TQ_F32: return by_k(static_cast<const float*>(q));
-    case TQ_BF16: return by_k(static_cast<const __hip_bfloat16*>(q));
-    case TQ_F16: return by_k(static_cast<const __half*>(q));
+  switch (ck->prm.n_planes) {
+    case 1: return by_v.template operator()<1>();
+    case 2: return by_v.template operator()<2>();
+    case 4: return by_v.template operator()<4>();
   }
   return hipErrorInvalidValue;
 }

@@ -86,7 +86,8 @@ hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_
                                    int n_kv_heads, int n_queries, void* ws, hipStream_t s);
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
-bool logits_fused_eligible(const tq_codec_s* c, int n_q_heads, int n_kv_heads, int n_queries);
+bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries,
+                           int64_t ctx);
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
                                hipStream_t s);
@@ -110,7 +111,7 @@ hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt,
 hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                          int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits, void* ws,
                          hipStream_t s) {
-  if (logits_fused_eligible(c, n_q_heads, n_kv_heads, n_queries))
+  if (logits_fused_eligible(c, batch, n_q_heads, n_kv_heads, n_queries, ctx))
     return launch_logits_fused(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   hipError_t e = launch_logits_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   if (e != hipSuccess) return e;

@@ -203,10 +203,12 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
 }
 
 // ----------------------------------------------------------------------------
-// Logits from prepared query operands: each wave scores its 64 keys against
-// NMT M-tiles of its query group, operands and constants read from `prep`.
+// Logits from prepared query operands: each wave scores NG consecutive groups
+// of 64 keys against NMT M-tiles of its query group, operands and constants
+// read once from `prep`; the next group's records load while the current one
+// is scored.
 // ----------------------------------------------------------------------------
-template <int NP, int WB, int NMT, int WAVES>
+template <int NP, int WB, int NMT, int WAVES, int NG>
 __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* __restrict__ prep, int n_mt, int ctx,
                                                                  const uint32_t* __restrict__ codes,
                                                                  const uint32_t* __restrict__ signs,
@@ -221,14 +223,17 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4;
   const int bk = blockIdx.y;
-  const int key0 = (blockIdx.x * WAVES + wv) * kKeysPerWave;
+  const int key0 = (blockIdx.x * WAVES + wv) * (NG * kKeysPerWave);
   if (key0 >= ctx) return;  // wave-uniform
-  const int nvalid = min(kKeysPerWave, ctx - key0);
-  const int64_t row0 = static_cast<int64_t>(bk) * ctx + key0;
-  v4u cv[L::CW / 4], sv[L::SW / 4];
-  float nu_l, ga_l;
-  load_wave_records<NP, WB>(cv, sv, nu_l, ga_l, codes + row0 * L::CW, signs + row0 * L::SW, norm + row0,
-                            rnorm + row0, nvalid, lane);
+  v4u cv[2][L::CW / 4], sv[2][L::SW / 4];
+  float nu_l[2], ga_l[2];
+  auto load_group = [&](int i, int buf) {
+    const int k0 = key0 + i * kKeysPerWave;
+    const int64_t r0 = static_cast<int64_t>(bk) * ctx + k0;
+    load_wave_records<NP, WB>(cv[buf], sv[buf], nu_l[buf], ga_l[buf], codes + r0 * L::CW, signs + r0 * L::SW,
+                              norm + r0, rnorm + r0, min(kKeysPerWave, ctx - k0), lane);
+  };
+  load_group(0, 0);
 
   // ---- query operands, constants and output rows (from L2)
   const int mt0 = blockIdx.z * NMT;
@@ -250,7 +255,18 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
     const int orow = reinterpret_cast<const int*>(base + NKB * kOpBytes + 64)[g];
     out[i] = (mt0 + i < n_mt && orow >= 0) ? logits + static_cast<int64_t>(orow) * ctx + key0 : nullptr;
   }
-  score_wave<NP, WB, NMT>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, out, nvalid, kappa, lane);
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const int k0 = key0 + i * kKeysPerWave;
+    if (k0 >= ctx) break;  // wave-uniform
+    if (i + 1 < NG && k0 + kKeysPerWave < ctx) load_group(i + 1, (i + 1) & 1);
+    float* oi[NMT];
+#pragma unroll
+    for (int j = 0; j < NMT; ++j) oi[j] = out[j] ? out[j] + i * kKeysPerWave : nullptr;
+    score_wave<NP, WB, NMT>(cv[i & 1], sv[i & 1], nu_l[i & 1], ga_l[i & 1], s_codes[wv], s_signs[wv], a, cst, oi,
+                            min(kKeysPerWave, ctx - k0), kappa, lane);
+    __builtin_amdgcn_wave_barrier();  // the next group's LDS staging follows this group's reads
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -340,18 +356,36 @@ hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_
   return c->prm.d == 128 ? by_type.template operator()<2>() : by_type.template operator()<4>();
 }
 
+constexpr int kFusedWaves = 16;  // 1024 keys per fused block
+
+static int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
   auto go = [&]<int NP, int WB, int NMT>() -> hipError_t {
     constexpr int WAVES = WB == 1 ? 8 : 4;
-    const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * kKeysPerWave)), batch * n_kv_heads,
-                    static_cast<unsigned>(ceil_div(n_mt, NMT)));
-    hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES>), grid, dim3(WAVES * 64), 0, s,
-                       static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                       k.rnorm, c->prm.qjl_kappa, logits);
-    return hipGetLastError();
+    auto launch = [&]<int NG>() -> hipError_t {
+      const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * NG * kKeysPerWave)), batch * n_kv_heads,
+                      static_cast<unsigned>(ceil_div(n_mt, NMT)));
+      hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG>), grid, dim3(WAVES * 64), 0, s,
+                         static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
+                         k.rnorm, c->prm.qjl_kappa, logits);
+      return hipGetLastError();
+    };
+    // Four groups per wave read the operands once per 256 keys (measured 49.8
+    // against 56.9 us for the 16 x 8 x 8192-key, 16-query prefill scores) when
+    // the grid still holds at least two blocks per compute unit.
+    const int64_t blocks4 = ceil_div(ctx, WAVES * 4 * kKeysPerWave) * batch * n_kv_heads * ceil_div(n_mt, NMT);
+    if (blocks4 >= 2 * device_cu_count()) return launch.template operator()<4>();
+    return launch.template operator()<1>();
   };
   const int NP = c->prm.n_planes;
   const int WB = c->prm.d / 128;
@@ -374,12 +408,19 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
 }
 
 // One launch for prep and logits when the query group is one M-tile (at most
-// 4 query vectors per KV head) and d = 128; TQ_LOGITS_FUSED=0 turns it off.
-bool logits_fused_eligible(const tq_codec_s* c, int n_q_heads, int n_kv_heads, int n_queries) {
+// 4 query vectors per KV head), d = 128, and the grid is at most one block per
+// compute unit: then the in-block operand rebuild overlaps the record loads.
+// Larger grids rebuild the operands once per block, which costs more than one
+// prep launch (measured at 32 heads x 32K keys: batch 1 fused 8.0 us against
+// 13.2 split; batch 4 29.8 against 24.9; batch 16 108.6 against 68.1).
+// TQ_LOGITS_FUSED=0 turns it off.
+bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries,
+                           int64_t ctx) {
   const char* v = std::getenv("TQ_LOGITS_FUSED");
   if (v && std::string(v) == "0") return false;
   const int64_t nv = static_cast<int64_t>(n_queries) * (n_q_heads / n_kv_heads);
-  return logits_mfma_eligible(c) && c->prm.d == 128 && nv <= 4;
+  const int64_t blocks = ceil_div(ctx, kFusedWaves * kKeysPerWave) * batch * n_kv_heads;
+  return logits_mfma_eligible(c) && c->prm.d == 128 && nv <= 4 && blocks <= device_cu_count();
 }
 
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
@@ -388,7 +429,7 @@ hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt
   // 16 waves (1024 keys) per block: one block per CU at the decode shapes, so
   // the operand rebuild is paid once per CU rather than twice (measured 8.7 us
   // against 9.2 us for 8-wave blocks at 32 query heads x 32K keys).
-  constexpr int WAVES = 16;
+  constexpr int WAVES = kFusedWaves;
   const int G = n_q_heads / n_kv_heads;
   auto go = [&]<int NP, typename T>(const T* qq) -> hipError_t {
     const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * kKeysPerWave)), batch * n_kv_heads, 1);

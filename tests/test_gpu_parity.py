@@ -266,6 +266,37 @@ def test_logits_fused_matches_two_kernel_path(B, bits, qdt, batch, hq, hkv, nq, 
     assert between <= 1e-4
 
 
+@pytest.mark.parametrize("batch,hq,hkv,nq,ctx", [(8, 32, 8, 1, 16411), (16, 8, 8, 16, 6200)])
+def test_logits_large_grid_ragged_sampled(B, batch, hq, hkv, nq, ctx):
+    # grids large enough for the two-kernel path with four 64-key groups per
+    # wave; ctx is not a multiple of the 2048 keys a block covers, so the last
+    # block of every head has a partial group and groups past the end.  The
+    # oracle scores the last 130 keys of every head and 3000 random keys.
+    say(f"logits large grid batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx}")
+    gc, oc = pair(B, 128, 3)
+    rng = np.random.default_rng(ctx)
+    k = as_exact(rng.standard_normal((batch * hkv * ctx, 128), dtype=np.float32), "bf16")
+    q = as_exact(rng.standard_normal((batch, nq, hq, 128)), "bf16")
+    kp, _ = B.tq_encode_kv(gc, to_dev(k, "bf16"))
+    lg = B.tq_attn_logits(gc, to_dev(q, "bf16"), kp, ctx, hkv).cpu().numpy()   # [b][h][q][t]
+    tail = (np.arange(batch * hkv)[:, None] * ctx + np.arange(ctx - 130, ctx)[None, :]).ravel()
+    rows = np.unique(np.concatenate([tail, rng.choice(batch * hkv * ctx, 3000, replace=False)]))
+    gk = {kk: x[rows] for kk, x in kp.numpy().items()}
+    rec = oracle_records_like(oc, k[rows].astype(np.float64), gk)
+    G = hq // hkv
+    worst = 0.0
+    for bk in np.unique(rows // ctx):
+        b, kh = bk // hkv, bk % hkv
+        sel = (rows // ctx) == bk
+        t = rows[sel] % ctx
+        qv = q[b, :, kh * G:(kh + 1) * G].transpose(1, 0, 2).reshape(G * nq, 128)   # (head, query) order
+        ref = O.score(oc, qv.astype(np.float64), {kk: x[sel] for kk, x in rec.items()})
+        got = lg[b, kh * G:(kh + 1) * G][:, :, t].reshape(G * nq, -1)
+        worst = max(worst, row_rel_err(got, ref).max())
+    say(f"  max row err {worst:.2e}")
+    assert worst <= 1e-3
+
+
 def test_logits_ctx_zero_is_noop(B):
     gc, _ = pair(B, 128, 3)
     kp = B.alloc_packed(gc, 1)
