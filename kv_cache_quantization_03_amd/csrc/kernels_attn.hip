@@ -278,6 +278,114 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
   }
 }
 
+// Combine for d = m = 128 with one round of global loads: every thread issues
+// its chunk's (max, Σw), its value j = t % 256 (M below 128, J above) of every
+// fourth chunk, and its slice of S for Sᵀ J before using any of them; the
+// chunk weights then go through LDS.  (Contexts over 128 chunks load the
+// values of the further chunks in more rounds.)
+__global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevParams PV, const float* __restrict__ part,
+                                                                         int Hq, int nkv, int n_chunks,
+                                                                         const float* __restrict__ S,
+                                                                         const float* __restrict__ Dsign, void* out,
+                                                                         int out_bf16) {
+  constexpr int d = 128, U = 32, NW = kCombThreads / kWave;
+  __shared__ float wsh[kCombThreads];  // chunk weights exp(m_c - max)
+  __shared__ float red[NW], red2[NW];
+  __shared__ float qa[4][256];
+  __shared__ float osh[d], Jsh[d];
+  __shared__ float sj[8][d];
+  const int G = Hq / nkv;
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
+  const int bk = b * nkv + h / G, g = h % G;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid & 255, qtr = tid >> 8;
+  const int rec = 2 + 2 * d;
+  const float* base = part + (static_cast<int64_t>(bk) * n_chunks * G + g) * rec;
+  // unsigned 32-bit offsets from the block's base: the loads take the scalar base plus one offset register
+  const unsigned cstride = static_cast<unsigned>(G * rec);
+  // ---- loads
+  const bool has_c = tid < n_chunks;
+  const float* own = base + (has_c ? static_cast<unsigned>(tid) : 0u) * cstride;
+  const float m_own = has_c ? own[0] : -INFINITY;
+  const float l_own = has_c ? own[1] : 0.f;
+  const int jj = tid & 127, pp = tid >> 7;  // o'_jj += Σ_{i in [16pp, 16pp+16)} S[i][jj] J_i
+  float sv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) sv[u] = S[static_cast<unsigned>((pp * 16 + u) * d + jj)];
+  float vc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) vc[u] = base[static_cast<unsigned>(min(qtr + 4 * u, n_chunks - 1)) * cstride + 2u + j];
+  // ---- global max and chunk weights
+  float m = wave_max(m_own);
+  if (lane == 0) red[wv] = m;
+  __syncthreads();
+  float gm = red[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) gm = fmaxf(gm, red[w]);
+  const float w_own = has_c ? __expf(m_own - gm) : 0.f;
+  wsh[tid] = w_own;
+  const float lw = wave_sum(w_own * l_own);
+  if (lane == 0) red2[wv] = lw;
+  __syncthreads();
+  float ltot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ltot += red2[w];
+  // ---- weighted sum of the thread's chunks
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = qtr + 4 * u;
+    if (c < n_chunks) acc = fmaf(wsh[c], vc[u], acc);
+  }
+  for (int c0 = qtr + 4 * U; c0 < n_chunks; c0 += 4 * U) {  // contexts over 128 chunks
+#pragma unroll
+    for (int u = 0; u < U; ++u) vc[u] = base[static_cast<unsigned>(min(c0 + 4 * u, n_chunks - 1)) * cstride + 2u + j];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 4 * u;
+      if (c < n_chunks) acc = fmaf(wsh[c], vc[u], acc);
+    }
+  }
+  qa[qtr][j] = acc;
+  __syncthreads();
+  if (tid < 256) {
+    const float a = (qa[0][tid] + qa[1][tid]) + (qa[2][tid] + qa[3][tid]);
+    if (tid < d) osh[tid] = a;
+    else Jsh[tid - d] = a;
+  }
+  __syncthreads();
+  {
+    float a = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) a = fmaf(sv[u], Jsh[pp * 16 + u], a);
+    sj[pp][jj] = a;
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    const float inv_l = 1.0f / ltot;
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jo = e * kWave + tid;
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) t += sj[q][jo];
+      v[e] = (osh[jo] + PV.qjl_kappa * t) * inv_l;
+    }
+    hadamard_wave<2, true>(v, tid);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int jo = e * kWave + tid;
+      const float o = v[e] * PV.inv_sqrt_d * Dsign[jo];
+      const int64_t oi = static_cast<int64_t>(bh) * d + jo;
+      if (out_bf16) {
+        reinterpret_cast<__hip_bfloat16*>(out)[oi] = __float2bfloat16(o);
+      } else {
+        reinterpret_cast<float*>(out)[oi] = o;
+      }
+    }
+  }
+}
+
 bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why) {
   const int G = n_q_heads / n_kv_heads;
   if (G > 16) { *why = "at most 16 query heads per KV head"; return false; }
@@ -344,6 +452,11 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
                        cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, sparse_v ? v_gate : 0.f,
                        part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (cv->prm.d == 128 && cv->prm.m == 128) {
+    hipLaunchKernelGGL(decode_combine128_kernel, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part,
+                       n_q_heads, n_kv_heads, n_chunks, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);
+    return hipGetLastError();
   }
   auto run = [&]<int E>() -> hipError_t {
     hipLaunchKernelGGL((decode_combine_kernel<E>), dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm,
