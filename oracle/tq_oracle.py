@@ -41,6 +41,7 @@ __all__ = [
     "encode", "encode_given_codes", "dequantize",
     "prepare_query", "score", "attn_logits",
     "decode_attn_materialized", "decode_attn_accumulated", "decode_attn_sparse_v",
+    "paged_row", "append_paged", "gather_paged", "decode_attn_paged",
     "search_topk", "bf16_round",
 ]
 
@@ -555,6 +556,68 @@ def decode_attn_sparse_v(codec_k: Codec, codec_v: Codec, q, k_packed, v_packed,
             keep[bi, hs] = k
             out[bi, hs] = (e * k / l) @ vals
     return out, keep, local
+
+
+# --------------------------------------------------------------------------
+# O6c. Paged cache (the KV cache of 深度拆解 第一部分 "KV 缓存是什么" grows by one
+# token per decode step).  Reading: the cache is split into pages of
+# `page_size` positions; page p holds, for every KV head kh, the records of
+# its positions at rows (p * n_kv_heads + kh) * page_size + slot, and
+# page_table[b][i] names the page holding positions [i*page_size,
+# (i+1)*page_size) of sequence b.  New tokens are encoded like any other
+# vector and written at positions ctx_lens[b], ctx_lens[b] + 1, ...  Decode
+# attention of sequence b runs over its first ctx_lens[b] positions; an empty
+# context gives a zero output (the pages never consider one).
+# --------------------------------------------------------------------------
+def paged_row(page_table, b: int, kh: int, pos: int, n_kv_heads: int, page_size: int) -> int:
+    page = int(np.asarray(page_table)[b][pos // page_size])
+    return (page * n_kv_heads + kh) * page_size + pos % page_size
+
+
+def append_paged(codec: Codec, cache: dict, x, ctx_lens, page_table, page_size: int):
+    """x: (batch, n_kv_heads, n_new, d).  Writes the records into `cache`
+    (numpy arrays, modified in place) and returns it."""
+    x = np.asarray(x, dtype=np.float64)
+    batch, hkv, n_new, d = x.shape
+    enc = encode(codec, x.reshape(-1, d))
+    i = 0
+    for b in range(batch):
+        for kh in range(hkv):
+            for t in range(n_new):
+                row = paged_row(page_table, b, kh, int(ctx_lens[b]) + t, hkv, page_size)
+                for key in ("codes", "signs", "norm", "rnorm"):
+                    cache[key][row] = enc[key][i]
+                i += 1
+    return cache
+
+
+def gather_paged(cache: dict, page_table, b: int, n_kv_heads: int, ctx_len: int, page_size: int) -> dict:
+    """Sequence b's records as contiguous rows [kv_head][position]."""
+    rows = [paged_row(page_table, b, kh, t, n_kv_heads, page_size)
+            for kh in range(n_kv_heads) for t in range(ctx_len)]
+    return {k: np.asarray(cache[k])[rows] for k in ("codes", "signs", "norm", "rnorm")}
+
+
+def decode_attn_paged(codec_k: Codec, codec_v: Codec, q, k_cache, v_cache, page_table, ctx_lens,
+                      n_q_heads, n_kv_heads, page_size, scale, gate=None, chunk=None):
+    """q: (batch, n_q_heads, d).  gate=None: plain attention; else Sparse V
+    (O6b) with the given gate and chunk."""
+    q = np.asarray(q, dtype=np.float64)
+    batch = q.shape[0]
+    out = np.zeros((batch, n_q_heads, codec_v.d))
+    for b in range(batch):
+        n = int(ctx_lens[b])
+        if n == 0:
+            continue
+        kr = gather_paged(k_cache, page_table, b, n_kv_heads, n, page_size)
+        vr = gather_paged(v_cache, page_table, b, n_kv_heads, n, page_size)
+        if gate is None:
+            out[b] = decode_attn_accumulated(codec_k, codec_v, q[b:b + 1], kr, vr, 1, n_q_heads, n_kv_heads, n,
+                                             scale)[0]
+        else:
+            out[b] = decode_attn_sparse_v(codec_k, codec_v, q[b:b + 1], kr, vr, 1, n_q_heads, n_kv_heads, n,
+                                          scale, gate, chunk)[0][0]
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -490,6 +490,66 @@ def test_sparse_v_gate_uses_the_chunk_maximum(codec3, codec4):
     assert np.allclose(out[0, 0], vhat[j], rtol=1e-12, atol=1e-12)
 
 
+# ---------------------------------------------------------------- O6c paged cache
+def test_paged_rows_closed_form_and_disjoint():
+    # one KV head with the identity page table is the contiguous layout
+    assert [O.paged_row([[0, 1, 2]], 0, 0, t, 1, 4) for t in range(12)] == list(range(12))
+    # two sequences with disjoint pages: every (sequence, head, position) has its own row
+    pt = [[3, 0], [1, 2]]
+    rows = {O.paged_row(pt, b, kh, t, 2, 8) for b in range(2) for kh in range(2) for t in range(16)}
+    assert rows == set(range(4 * 2 * 8))
+
+
+def test_paged_decode_reduces_to_contiguous_and_ignores_page_order(codec3, codec4):
+    rng = np.random.default_rng(41)
+    P, T = 16, 40
+    K = O.encode(codec3, rng.standard_normal((T, 128)))
+    V = O.encode(codec4, rng.standard_normal((T, 128)))
+    q = rng.standard_normal((1, 2, 128))
+    ref = O.decode_attn_accumulated(codec3, codec4, q, K, V, 1, 2, 1, T, 0.1)
+    ident = [[0, 1, 2]]
+    assert np.array_equal(O.decode_attn_paged(codec3, codec4, q, K, V, ident, [T], 2, 1, P, 0.1), ref)
+    # the same logical cache in shuffled physical pages (with junk in a spare page)
+    perm = [4, 1, 3]
+    def scatter(R):
+        out = {k: np.zeros((5 * P,) + np.asarray(R[k]).shape[1:], dtype=np.asarray(R[k]).dtype) for k in R}
+        for k in out:
+            out[k][:] = np.asarray(R[k])[rng.integers(0, T, 5 * P)]
+            for i, p in enumerate(perm):
+                n = min(P, T - i * P)
+                out[k][p * P:p * P + n] = np.asarray(R[k])[i * P:i * P + n]
+        return out
+    Kp, Vp = scatter(K), scatter(V)
+    got = O.decode_attn_paged(codec3, codec4, q, Kp, Vp, [perm], [T], 2, 1, P, 0.1)
+    assert np.array_equal(got, ref)
+    # a shorter context reads only its first positions
+    first = lambda R: {k: np.asarray(R[k])[:21] for k in ("codes", "signs", "norm", "rnorm")}
+    short = O.decode_attn_accumulated(codec3, codec4, q, first(K), first(V), 1, 2, 1, 21, 0.1)
+    assert np.array_equal(O.decode_attn_paged(codec3, codec4, q, Kp, Vp, [perm], [21], 2, 1, P, 0.1), short)
+    # an empty context gives zeros
+    assert np.all(O.decode_attn_paged(codec3, codec4, q, Kp, Vp, [perm], [0], 2, 1, P, 0.1) == 0)
+
+
+def test_append_paged_round_trip(codec3):
+    # appending token by token into pages, then gathering, equals encoding the rows at once
+    rng = np.random.default_rng(42)
+    hkv, P, steps = 2, 4, 11
+    x = rng.standard_normal((2, hkv, steps, 128))
+    pt = np.array([[5, 0, 7, 3], [2, 6, 1, 4]])
+    cache = {"codes": np.zeros((8 * hkv * P, codec3.b * 4), np.uint32), "signs": np.zeros((8 * hkv * P, 4), np.uint32),
+             "norm": np.zeros(8 * hkv * P, np.float32), "rnorm": np.zeros(8 * hkv * P, np.float32)}
+    ctx = np.array([0, 3])
+    for t in range(steps):
+        O.append_paged(codec3, cache, x[:, :, t:t + 1], ctx, pt, P)
+        ctx = ctx + 1
+    for b, start in ((0, 0), (1, 3)):
+        g = O.gather_paged(cache, pt, b, hkv, start + steps, P)
+        want = O.encode(codec3, x[b].reshape(-1, 128))
+        for key in ("codes", "signs", "norm", "rnorm"):
+            got = np.asarray(g[key]).reshape((hkv, start + steps) + np.asarray(g[key]).shape[1:])[:, start:]
+            assert np.array_equal(got.reshape(np.asarray(want[key]).shape), np.asarray(want[key], dtype=got.dtype))
+
+
 def test_dequantize_unbiased_over_qjl_matrix():
     # E_S[v̂] = v for a fixed rotation
     d = 32
