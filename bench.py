@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--only-stages", action="store_true",
                     help="run only the per-stage timings (one JSON line of stages; for kernel-trace profiles)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-stage-sparse-v", action="store_true", help="skip the Sparse V decode stage")
     ap.add_argument("--no-stage-search", action="store_true", help="skip the 1M x 1536 encode and search stages")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run a short fixed workload for rocprofv3 --pmc (20 logits launches + calibration copies)")
@@ -294,6 +295,56 @@ def _hbm(ms, nbytes):
     return {"bound": "hbm", "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
 
 
+def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d):
+    """Sparse V on the long-context decode shape.  Needle cache: the same
+    haystack keys plus, with probability 1/512 per (KV head, position), a key
+    z + 64·u, u the unit sum of that KV head's four queries (peaked attention,
+    as in long-context decoding); values unchanged.  Times plain decode and
+    the gate 1e-6 on the needle cache, and the gate on the Gaussian cache
+    (where it drops nothing: its cost).  The dropped fraction of 128-key
+    blocks comes from the cache's own logits (tq_attn_logits)."""
+    import torch
+    gate, scale, hkv, hq = 1e-6, 1 / math.sqrt(d), 8, 32
+    u = qd.float().view(hkv, hq // hkv, d).sum(1)
+    u = u / u.norm(dim=1, keepdim=True)
+    mask = torch.rand(hkv * ctx, generator=g, device=dev) < 1.0 / 512
+    kn = k.float()
+    kn[mask] += 64.0 * u.repeat_interleave(ctx, dim=0)[mask]
+    kpn = B.tq_encode_kv(codec3, kn.to(torch.bfloat16))[0]
+    del kn
+    lg = B.tq_attn_logits(codec3, qd.view(1, 1, hq, d), kpn, ctx, hkv).view(hkv, hq // hkv, ctx // 1024, 1024)
+    sc = lg * scale
+    e = torch.exp(sc - sc.amax(dim=-1, keepdim=True))
+    keep = e >= gate * e.sum(dim=-1, keepdim=True)
+    dropped = float((~keep.view(hkv, hq // hkv, ctx // 128, 128).any(dim=3).any(dim=1)).float().mean())
+    del lg, sc, e, keep
+    ns = 4
+    nsets = [(kpn if i == 0 else B.Packed(kpn.codes.clone(), kpn.signs.clone(), kpn.norm.clone(), kpn.rnorm.clone()),
+              dsets[i % len(dsets)][1]) for i in range(ns)]
+    res = {}
+    for name, sets, gated in (("decode_attn_c4_needles_plain", nsets, False),
+                              ("decode_attn_c4_needles_sparse_v", nsets, True),
+                              ("decode_attn_c4_gaussian_sparse_v", dsets, True)):
+        it = iter(range(10 ** 9))
+
+        def step():
+            kk, vv = sets[next(it) % len(sets)]
+            if gated:
+                B.tq_decode_attn_sparse_v(codec3, codec3, qd, kk, vv, ctx, hkv, scale, gate, out=out, ws=ws)
+            else:
+                B.tq_decode_attn(codec3, codec3, qd, kk, vv, ctx, hkv, scale, out=out, ws=ws)
+        ms = _time(step, 30, graph=True)
+        res[name] = {"ms": ms, "buffer_sets": len(sets), "gate": gate if gated else None}
+        print(f"[bench] {name} {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    needle_v = 8 * ctx * codec3.record_bytes * (1 - dropped)
+    r = res["decode_attn_c4_needles_sparse_v"]
+    r["dropped_block_fraction"] = dropped
+    r["speedup_vs_plain"] = res["decode_attn_c4_needles_plain"]["ms"] / r["ms"]
+    r.update(_hbm(r["ms"], 8 * ctx * codec3.record_bytes + needle_v + 2 * hq * d * 2))
+    del kpn, nsets
+    return res
+
+
 def time_stages(B, I, codec3, dev, args):
     """The other rows of the path, each timed on its own configuration with
     synthetic data drawn on the GPU (torch, seeded), with the roofline that
@@ -377,6 +428,7 @@ def time_stages(B, I, codec3, dev, args):
     v = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
     qd = torch.randn((1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp, vp = B.tq_encode_kv(codec3, k, v)
+    k_c4 = k
     del k, v
     ns = 3
     dsets = [(kp, vp)] + [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
@@ -393,7 +445,9 @@ def time_stages(B, I, codec3, dev, args):
     res["decode_attn_c4"] = {"ms": ms, "buffer_sets": ns,
                              **_hbm(ms, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
     print(f"[bench] C4 decode attention {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    del kp, vp, dsets, ws
+    if not args.no_stage_sparse_v:
+        res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d))
+    del kp, vp, dsets, ws, k_c4
     # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
     bsz, hkv, ctx, nq = 16, 8, 8192, 16
     n = bsz * hkv * ctx
