@@ -229,6 +229,52 @@ tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, const void* q,
  * above.  0 for invalid head counts. */
 int32_t tq_decode_attn_chunk(int32_t n_q_heads, int32_t n_kv_heads);
 
+/* ---------------------------------------------------------------- paged cache
+ * A KV cache that grows by one token per decode step (深度拆解 第一部分: the
+ * cache keeps the K and V of every past token), stored in pages so that
+ * sequences of different lengths share one pool.
+ * Layout.  A cache is one set of packed arrays of n_pages * n_kv_heads *
+ * page_size rows.  Page p holds, for KV head kh, the records of page_size
+ * consecutive positions at rows (p * n_kv_heads + kh) * page_size + slot.
+ * page_table (device int32 [batch][max_pages]): page_table[b][i] is the page
+ * holding positions [i*page_size, (i+1)*page_size) of sequence b.
+ * ctx_lens (device int32 [batch]): positions in use per sequence.
+ *
+ * tq_encode_append_paged encodes x (device [batch][n_kv_heads][n_new][d],
+ * dtype dt) and writes token t of sequence b, KV head kh at position
+ * ctx_lens[b] + t.  The records are exactly those tq_encode_kv writes for the
+ * same rows.  A position whose page index is >= max_pages, or whose page id is
+ * outside [0, n_pages), is not written.  ctx_lens is read, not updated: the
+ * caller advances it (for example by n_new) before the next step.  Call once
+ * per cache (K and V may use different codecs).  page_size >= 1 here; decode
+ * needs a multiple of 128.  Workspace: tq_encode_append_paged_workspace(...)
+ * bytes, 16-byte aligned.  batch = 0 or n_new = 0 is a no-op. */
+size_t tq_encode_append_paged_workspace(tq_codec_t c, int32_t batch, int32_t n_kv_heads, int32_t n_new);
+tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dtype_t dt, int32_t batch,
+                                   int32_t n_kv_heads, int32_t n_new, const int32_t* ctx_lens,
+                                   const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                                   int32_t n_pages, tq_packed_t cache, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* tq_decode_attn over paged K and V caches (same layout and page table):
+ * sequence b attends over its first ctx_lens[b] positions (clamped to
+ * [0, max_ctx]); an empty context gives a zero output.  max_ctx (host) bounds
+ * every ctx_lens[b] and sizes the grid and the workspace:
+ * tq_decode_attn_paged_workspace(..., max_ctx) bytes.  v_gate > 0 applies the
+ * Sparse V gate of tq_decode_attn_sparse_v (0: plain attention).
+ * Needs head_dim = qjl_dim = 128 for K and V and at most 4 query heads per KV
+ * head (else TQ_ERROR_NOT_SUPPORTED), page_size a multiple of 128 and
+ * 1 <= max_ctx <= max_pages * page_size (else TQ_ERROR_INVALID_VALUE).  Page
+ * ids in the used part of the page table must be valid pages of the caches. */
+size_t tq_decode_attn_paged_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch, int32_t n_q_heads,
+                                      int32_t n_kv_heads, int64_t max_ctx);
+tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                 int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k_cache,
+                                 tq_packed_t v_cache, const int32_t* ctx_lens, const int32_t* page_table,
+                                 int32_t max_pages, int32_t page_size, int64_t max_ctx, float softmax_scale,
+                                 float v_gate, void* out, tq_dtype_t out_dt, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* ---------------------------------------------------------------- search
  * Exhaustive inner-product search over a compressed database
  * (深度拆解 第三部分 向量搜索: the compressed vectors are the index; nothing

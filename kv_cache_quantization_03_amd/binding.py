@@ -63,6 +63,11 @@ def _load():
         "tq_decode_attn_sparse_v": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, i64, C.c_float, C.c_float,
                                               vp, C.c_int, vp, sz, vp]),
         "tq_decode_attn_chunk": (i32, [i32, i32]),
+        "tq_encode_append_paged_workspace": (sz, [vp, i32, i32, i32]),
+        "tq_encode_append_paged": (C.c_int, [vp, vp, C.c_int, i32, i32, i32, vp, vp, i32, i32, i32, P, vp, sz, vp]),
+        "tq_decode_attn_paged_workspace": (sz, [vp, vp, i32, i32, i32, i64]),
+        "tq_decode_attn_paged": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, vp, vp, i32, i32, i64,
+                                           C.c_float, C.c_float, vp, C.c_int, vp, sz, vp]),
         "tq_search_workspace": (sz, [vp, i64, i32, i32]),
         "tq_search_topk": (C.c_int, [vp, P, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
         "tq_diag_stream_blocks": (i32, []),
@@ -80,6 +85,8 @@ EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_bui
             "tq_codec_destroy", "tq_codec_info", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
+            "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
+            "tq_decode_attn_paged",
             "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
 
 
@@ -307,6 +314,41 @@ def tq_decode_attn_sparse_v(ck: Codec, cv: Codec, q, k: Packed, v: Packed, ctx_l
 
 def tq_decode_attn_chunk(n_q_heads: int, n_kv_heads: int) -> int:
     return lib.tq_decode_attn_chunk(n_q_heads, n_kv_heads)
+
+
+# ---------------------------------------------------------------- paged cache
+def tq_encode_append_paged(codec: Codec, x, ctx_lens, page_table, page_size: int, n_pages: int, cache: Packed,
+                           ws=None):
+    """x: [batch][n_kv_heads][n_new][d]; ctx_lens int32 [batch], page_table
+    int32 [batch][max_pages] (device).  Writes into `cache` in place."""
+    batch, hkv, n_new, d = x.shape
+    assert d == codec.d and x.is_contiguous() and page_table.is_contiguous()
+    need = lib.tq_encode_append_paged_workspace(codec.handle, batch, hkv, n_new)
+    ws = ws if ws is not None else _workspace(need, x.device)
+    st = lib.tq_encode_append_paged(codec.handle, _ptr(x), _dt(x), batch, hkv, n_new, _ptr(ctx_lens),
+                                    _ptr(page_table), page_table.shape[1], page_size, n_pages, cache.c(), _ptr(ws),
+                                    ws.numel(), _stream(x))
+    _check(st, "tq_encode_append_paged")
+    return cache
+
+
+def tq_decode_attn_paged(ck: Codec, cv: Codec, q, k_cache: Packed, v_cache: Packed, ctx_lens, page_table,
+                         page_size: int, max_ctx: int, n_kv_heads: int, softmax_scale: float, v_gate: float = 0.0,
+                         out_dtype=None, out=None, ws=None):
+    """q: [batch][n_q_heads][d]; returns out [batch][n_q_heads][d]."""
+    torch = _torch()
+    batch, hq, d = q.shape
+    out_dtype = out_dtype or torch.bfloat16
+    if out is None:
+        out = torch.empty((batch, hq, d), dtype=out_dtype, device=q.device)
+    need = lib.tq_decode_attn_paged_workspace(ck.handle, cv.handle, batch, hq, n_kv_heads, max_ctx)
+    ws = ws if ws is not None else _workspace(need, q.device)
+    st = lib.tq_decode_attn_paged(ck.handle, cv.handle, _ptr(q), _dt(q), batch, hq, n_kv_heads, k_cache.c(),
+                                  v_cache.c(), _ptr(ctx_lens), _ptr(page_table), page_table.shape[1], page_size,
+                                  max_ctx, float(softmax_scale), float(v_gate), _ptr(out), _dt(out), _ptr(ws),
+                                  ws.numel(), _stream(q))
+    _check(st, "tq_decode_attn_paged")
+    return out
 
 
 # ---------------------------------------------------------------- search

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   float gm = red[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) gm = fmaxf(gm, red[w]);
-  const float w_own = has_c ? __expf(m_own - gm) : 0.f;
+  // chunks with no position (m = -inf; an empty context has only those) weigh 0
+  const float w_own = has_c && m_own != -INFINITY ? __expf(m_own - gm) : 0.f;
   wsh[tid] = w_own;
   const float lw = wave_sum(w_own * l_own);
   if (lane == 0) red2[wv] = lw;
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   }
   __syncthreads();
   if (tid < kWave) {
-    const float inv_l = 1.0f / ltot;
+    const float inv_l = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty context gives 0
     float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -420,13 +421,20 @@ bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_he
 int decode_mfma_chunk();
 hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                               tq_packed_t k, tq_packed_t v, int64_t ctx, float scale, bool sparse_v, float v_gate,
-                              const uint8_t* prep, float* part, int n_chunks, hipStream_t s);
+                              const PageMap* pm, const uint8_t* prep, float* part, int n_chunks, hipStream_t s);
+
+// Paged caches are read by the matrix-core kernel only (d = 128, at most 4
+// query heads per KV head), with the d = m = 128 combine.
+bool decode_paged_supported(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
+  return decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == attn_chunk(n_q_heads / n_kv_heads);
+}
 
 int decode_chunk(int n_q_heads, int n_kv_heads) { return attn_chunk(n_q_heads / n_kv_heads); }
 
 hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt, int batch,
                          int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx, float scale,
-                         bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws, hipStream_t s) {
+                         bool sparse_v, float v_gate, const PageMap* pm, void* out, tq_dtype_t out_dt, void* ws,
+                         hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int CH = attn_chunk(G);
   int n_chunks = static_cast<int>(ceil_div(ctx, CH));
@@ -436,12 +444,12 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                          decode_prep_region(ck, batch, n_q_heads, n_kv_heads));
   hipError_t e;
-  if (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH) {
+  if (pm || (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH)) {
     // matrix-core split kernel, same partial layout.  The query operands are
     // prepared once per KV head by their own launch (rebuilding them in every
     // block measured 58.7 against 55.5 us at 32 heads x 128K keys).
     if ((e = launch_logits_mfma_prep(ck, q, q_dt, batch, n_q_heads, n_kv_heads, 1, ws, s)) != hipSuccess) return e;
-    e = launch_decode_mfma(ck, cv, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, sparse_v, v_gate,
+    e = launch_decode_mfma(ck, cv, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, sparse_v, v_gate, pm,
                            static_cast<const uint8_t*>(ws), part, n_chunks, s);
     if (e != hipSuccess) return e;
   } else {

@@ -78,9 +78,9 @@ __device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (r
 
 }  // namespace
 
-template <int NPK, int NPV, bool GATE>
+template <int NPK, int NPV, bool GATE, bool PAGED>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
-    const uint8_t* __restrict__ prep, DevParams PK, DevParams PV, int Hq, int nkv, int ctx,
+    const uint8_t* __restrict__ prep, DevParams PK, DevParams PV, PageMap pm, int Hq, int nkv, int ctx_max,
     int n_chunks, float scale, float gate, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
     const float* __restrict__ kn, const float* __restrict__ kr, const uint32_t* __restrict__ vc,
     const uint32_t* __restrict__ vs, const float* __restrict__ vn, const float* __restrict__ vr,
@@ -99,17 +99,37 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   const int bk = blockIdx.y, chunk = blockIdx.x;
   const int G = Hq / nkv;
   const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
-  const int64_t hrow = static_cast<int64_t>(bk) * ctx;         // first row of the head
+  const int64_t hrow = static_cast<int64_t>(bk) * ctx_max;     // first row of the head (contiguous cache)
+  // the sequence's context: ctx_max for a contiguous cache; for a paged one its
+  // own length, clamped to the grid and to the page table
+  int ctx = ctx_max;
+  if constexpr (PAGED) ctx = max(0, min(min(pm.ctx_lens[bk / nkv], ctx_max), pm.max_pages * pm.page_size));
+  // record row of a key (position) of this head; page_size is a multiple of 128,
+  // so the 64 or 128 keys of a wave share one page
+  auto row_of = [&](int key) -> int64_t {
+    if constexpr (PAGED) {
+      const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + key / pm.page_size];
+      return (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + key % pm.page_size;
+    } else {
+      return hrow + key;
+    }
+  };
+  if (PAGED && chunk * kDecChunk >= ctx) {  // block-uniform: an empty chunk of a shorter sequence
+    constexpr int REC = 2 + 2 * kPrepD;       // max = -inf, weight sum and M, J = 0
+    float* out = part + (static_cast<int64_t>(bk) * n_chunks + chunk) * G * REC;
+    for (int e = threadIdx.x; e < G * REC; e += NT) out[e] = e % REC == 0 ? -INFINITY : 0.f;
+    return;
+  }
 
   // ---- loads: the K records, then the head's query operands (prepared once
-  // per KV head by attn_prep_mfma_kernel; L2-resident)
+  // per KV head by attn_prep_inblock_kernel; L2-resident)
   v4u kcv[2][LK::CW / 4], ksv[2][LK::SW / 4];
   float knu[2], kga[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int k0 = kbase + 64 * h;
     const int nv = min(64, ctx - k0);  // may be <= 0: then re-read the last key, never used
-    const int64_t r0 = hrow + (nv > 0 ? k0 : ctx - 1);
+    const int64_t r0 = row_of(nv > 0 ? k0 : ctx - 1);
     load_wave_records<NPK, 1>(kcv[h], ksv[h], knu[h], kga[h], kc + r0 * LK::CW, ks + r0 * LK::SW, kn + r0,
                               kr + r0, nv > 0 ? nv : 1, lane);
   }
@@ -152,14 +172,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
 #pragma unroll
     for (int reg = 0; reg < 2; ++reg) {
       const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
-      const int64_t row = hrow + key;
+      const int64_t row = row_of(key);
 #pragma unroll
       for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
       vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int64_t row = hrow + min(kbase + 16 * t + kl, ctx - 1);
+      const int64_t row = row_of(min(kbase + 16 * t + kl, ctx - 1));
       vnu[t] = vn[row];
       vga[t] = vr[row];
     }
@@ -420,11 +440,14 @@ int decode_mfma_chunk() { return kDecChunk; }
 // `prep`: the query operands of every (batch, KV head), as attn_prep_mfma_kernel writes them.
 hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                               tq_packed_t k, tq_packed_t v, int64_t ctx, float scale, bool sparse_v, float v_gate,
-                              const uint8_t* prep, float* part, int n_chunks, hipStream_t s) {
+                              const PageMap* pm, const uint8_t* prep, float* part, int n_chunks, hipStream_t s) {
+  const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   auto go = [&]<int NPK, int NPV>() -> hipError_t {
-    auto kern = sparse_v ? decode_mfma_kernel<NPK, NPV, true> : decode_mfma_kernel<NPK, NPV, false>;
+    auto kern = pm ? (sparse_v ? decode_mfma_kernel<NPK, NPV, true, true> : decode_mfma_kernel<NPK, NPV, false, true>)
+                   : (sparse_v ? decode_mfma_kernel<NPK, NPV, true, false>
+                               : decode_mfma_kernel<NPK, NPV, false, false>);
     hipLaunchKernelGGL(kern, dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
-                       0, s, prep, ck->prm, cv->prm, n_q_heads, n_kv_heads, static_cast<int>(ctx),
+                       0, s, prep, ck->prm, cv->prm, pmv, n_q_heads, n_kv_heads, static_cast<int>(ctx),
                        n_chunks, scale, v_gate, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm,
                        part);
     return hipGetLastError();

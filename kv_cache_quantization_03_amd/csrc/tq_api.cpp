@@ -199,8 +199,8 @@ extern "C" size_t tq_decode_attn_workspace(tq_codec_t ck, tq_codec_t cv, int32_t
 namespace {
 tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt, int32_t batch,
                           int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx_len,
-                          float softmax_scale, bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws,
-                          size_t ws_bytes, void* stream, const char* name) {
+                          float softmax_scale, bool sparse_v, float v_gate, const tq::PageMap* pm, void* out,
+                          tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream, const char* name) {
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
@@ -220,7 +220,7 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
     std::fprintf(stderr, "[tq] %s b=%d hq=%d hkv=%d ctx=%lld gate=%g\n", name, batch, n_q_heads, n_kv_heads,
                  (long long)ctx_len, sparse_v ? v_gate : 0.0);
   hipError_t e = tq::launch_decode(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale,
-                                   sparse_v, v_gate, out, out_dt, ws, static_cast<hipStream_t>(stream));
+                                   sparse_v, v_gate, pm, out, out_dt, ws, static_cast<hipStream_t>(stream));
   return finish(e, name);
 }
 }  // namespace
@@ -231,8 +231,8 @@ extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* 
                                       float softmax_scale, void* out, tq_dtype_t out_dt, void* ws,
                                       size_t ws_bytes, void* stream) {
   tq::clear_error();
-  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, false, 0.f, out,
-                       out_dt, ws, ws_bytes, stream, "tq_decode_attn");
+  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, false, 0.f,
+                       nullptr, out, out_dt, ws, ws_bytes, stream, "tq_decode_attn");
 }
 
 extern "C" tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
@@ -243,12 +243,85 @@ extern "C" tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, con
   tq::clear_error();
   if (!(v_gate >= 0.f && v_gate < 1.f)) { set_error("v_gate must be in [0, 1)"); return TQ_ERROR_INVALID_VALUE; }
   return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, true, v_gate,
-                       out, out_dt, ws, ws_bytes, stream, "tq_decode_attn_sparse_v");
+                       nullptr, out, out_dt, ws, ws_bytes, stream, "tq_decode_attn_sparse_v");
 }
 
 extern "C" int32_t tq_decode_attn_chunk(int32_t n_q_heads, int32_t n_kv_heads) {
   if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return 0;
   return tq::decode_chunk(n_q_heads, n_kv_heads);
+}
+
+// ---------------------------------------------------------------- paged cache
+extern "C" size_t tq_encode_append_paged_workspace(tq_codec_t c, int32_t batch, int32_t n_kv_heads, int32_t n_new) {
+  if (!c || batch < 0 || n_kv_heads <= 0 || n_new < 0) return 0;
+  return tq::append_paged_ws_bytes(c, static_cast<int64_t>(batch) * n_kv_heads * n_new);
+}
+
+extern "C" tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dtype_t dt, int32_t batch,
+                                              int32_t n_kv_heads, int32_t n_new, const int32_t* ctx_lens,
+                                              const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                                              int32_t n_pages, tq_packed_t cache, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(dt)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
+  if (batch < 0 || n_kv_heads <= 0 || n_new < 0) {
+    set_error("need batch >= 0, n_kv_heads > 0, n_new >= 0");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (max_pages <= 0 || page_size <= 0 || n_pages <= 0) {
+    set_error("max_pages, page_size and n_pages must be > 0");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (batch == 0 || n_new == 0) return TQ_SUCCESS;
+  if (!x || !ctx_lens || !page_table) { set_error("x, ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!aligned(x, dtype_size(dt)) || !aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
+    set_error("x, ctx_lens or page_table misaligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  tq_status_t st = check_packed(cache, "cache");
+  if (st != TQ_SUCCESS) return st;
+  const int64_t n = static_cast<int64_t>(batch) * n_kv_heads * n_new;
+  if ((st = check_ws(ws, ws_bytes, tq::append_paged_ws_bytes(c, n))) != TQ_SUCCESS) return st;
+  hipError_t e = tq::launch_append_paged(c, x, dt, batch, n_kv_heads, n_new, ctx_lens, page_table, max_pages,
+                                         page_size, n_pages, cache, ws, static_cast<hipStream_t>(stream));
+  return finish(e, "tq_encode_append_paged launch");
+}
+
+extern "C" size_t tq_decode_attn_paged_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int64_t max_ctx) {
+  return tq_decode_attn_workspace(ck, cv, batch, n_q_heads, n_kv_heads, max_ctx);
+}
+
+extern "C" tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                            int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                            tq_packed_t k_cache, tq_packed_t v_cache, const int32_t* ctx_lens,
+                                            const int32_t* page_table, int32_t max_pages, int32_t page_size,
+                                            int64_t max_ctx, float softmax_scale, float v_gate, void* out,
+                                            tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!(v_gate >= 0.f && v_gate < 1.f)) { set_error("v_gate must be in [0, 1)"); return TQ_ERROR_INVALID_VALUE; }
+  if (max_pages <= 0 || page_size <= 0 || page_size % 128 != 0) {
+    set_error("need max_pages > 0 and page_size a positive multiple of 128");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (max_ctx < 1 || max_ctx > static_cast<int64_t>(max_pages) * page_size) {
+    set_error("need 1 <= max_ctx <= max_pages * page_size");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (n_kv_heads > 0 && n_q_heads % n_kv_heads == 0 && !tq::decode_paged_supported(ck, cv, n_q_heads, n_kv_heads)) {
+    set_error("paged decode needs head_dim = qjl_dim = 128 for K and V and at most 4 query heads per KV head");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  if (batch > 0 && (!ctx_lens || !page_table)) { set_error("ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (batch > 0 && (!aligned(ctx_lens, 4) || !aligned(page_table, 4))) {
+    set_error("ctx_lens or page_table misaligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  const tq::PageMap pm{page_table, ctx_lens, max_pages, page_size};
+  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k_cache, v_cache, max_ctx, softmax_scale,
+                       v_gate > 0.f, v_gate, &pm, out, out_dt, ws, ws_bytes, stream, "tq_decode_attn_paged");
 }
 
 // ---------------------------------------------------------------- search

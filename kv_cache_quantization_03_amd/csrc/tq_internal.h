@@ -45,6 +45,15 @@ struct DevParams {
   int d, b, m, code_words, sign_words, n_planes;
 };
 
+// A paged cache (see tq_decode_attn_paged): page_table[b][i] holds positions
+// [i*page_size, (i+1)*page_size) of sequence b; page p, KV head kh, slot s is
+// row (p * n_kv_heads + kh) * page_size + s.  ctx_lens[b]: positions in use.
+struct PageMap {
+  const int32_t* table;
+  const int32_t* ctx_lens;
+  int max_pages, page_size;
+};
+
 }  // namespace tq
 
 namespace tq {
@@ -102,10 +111,18 @@ bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64
 size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads,
                        int n_kv_heads, int64_t ctx);
 int decode_chunk(int n_q_heads, int n_kv_heads);
+// pm: nullptr for a contiguous cache [batch][kv_head][ctx]; else a paged
+// cache read through pm, ctx being the largest context (grid size).
 hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
                          int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v,
-                         int64_t ctx, float scale, bool sparse_v, float v_gate, void* out,
+                         int64_t ctx, float scale, bool sparse_v, float v_gate, const PageMap* pm, void* out,
                          tq_dtype_t out_dt, void* ws, hipStream_t s);
+bool decode_paged_supported(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
+
+size_t append_paged_ws_bytes(const tq_codec_s* c, int64_t n_rec);
+hipError_t launch_append_paged(const tq_codec_s* c, const void* x, tq_dtype_t dt, int batch, int n_kv_heads,
+                               int n_new, const int32_t* ctx_lens, const int32_t* page_table, int max_pages,
+                               int page_size, int n_pages, tq_packed_t cache, void* ws, hipStream_t s);
 
 size_t search_ws_bytes(const tq_codec_s* c, int64_t n_db, int n_queries, int topk);
 hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, const float* queries,

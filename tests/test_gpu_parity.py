@@ -493,6 +493,140 @@ def test_decode_sparse_v_rejects_bad_gate(B):
     assert B.tq_decode_attn_chunk(32, 8) == 1024 and B.tq_decode_attn_chunk(3, 2) == 0
 
 
+# ---------------------------------------------------------------- paged cache
+def _fill_pages(rec_by_seq, page_table, hkv, P, n_pages, junk):
+    """A numpy cache with sequence b's records (rows [kv_head][position]) at
+    their page slots; every other row holds a junk record."""
+    cache = {k: np.asarray(junk[k])[np.arange(n_pages * hkv * P) % len(junk["norm"])].copy()
+             for k in ("codes", "signs", "norm", "rnorm")}
+    for b, rec in enumerate(rec_by_seq):
+        n = len(rec["norm"]) // hkv
+        for kh in range(hkv):
+            for t in range(n):
+                row = O.paged_row(page_table, b, kh, t, hkv, P)
+                for k in cache:
+                    cache[k][row] = np.asarray(rec[k])[kh * n + t]
+    return cache
+
+
+def test_append_paged_matches_contiguous_encode(B):
+    # tokens appended step by step (and one 70-token prefill) land at their page
+    # slots with exactly the records of a contiguous encode; rows that no append
+    # reaches, and positions past the page table, keep their old contents
+    gc, oc = pair(B, 128, 3)
+    batch, hkv, P, max_pages, n_pages = 3, 2, 128, 4, 13
+    rng = np.random.default_rng(51)
+    pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    ctx0 = np.array([0, 5, 4 * P - 2], dtype=np.int32)
+    steps = [1, 1, 70, 1]
+    xs = [as_exact(rng.standard_normal((batch, hkv, n, 128)), "bf16") for n in steps]
+    n_rows = n_pages * hkv * P
+    cache = B.alloc_packed(gc, n_rows)
+    for t in (cache.codes, cache.signs):
+        t.fill_(0x5A5A5A5A)
+    cache.norm.fill_(-7.0)
+    cache.rnorm.fill_(-7.0)
+    ctx = torch.from_numpy(ctx0.copy()).cuda()
+    ptd = torch.from_numpy(pt).cuda()
+    for x in xs:
+        B.tq_encode_append_paged(gc, to_dev(x, "bf16"), ctx, ptd, P, n_pages, cache)
+        ctx += x.shape[2]
+    torch.cuda.synchronize()
+    got = cache.numpy()
+    allx = np.concatenate(xs, axis=2)              # [batch][hkv][73][d]
+    ref, _ = B.tq_encode_kv(gc, to_dev(allx.reshape(-1, 128), "bf16"))
+    ref = ref.numpy()
+    written = np.zeros(n_rows, dtype=bool)
+    for b in range(batch):
+        for kh in range(hkv):
+            for t in range(allx.shape[2]):
+                pos = int(ctx0[b]) + t
+                if pos >= max_pages * P:
+                    continue                        # past the page table: not written
+                row = O.paged_row(pt, b, kh, pos, hkv, P)
+                i = (b * hkv + kh) * allx.shape[2] + t
+                for k in got:
+                    assert np.array_equal(got[k][row], ref[k][i]), (b, kh, t, k)
+                written[row] = True
+    assert np.all(got["norm"][~written] == -7.0) and np.all(got["codes"][~written] == 0x5A5A5A5A)
+    say(f"append paged: {written.sum()} rows written, {(~written).sum()} untouched")
+
+
+@pytest.mark.parametrize("kbits,vbits,gate", [(3, 3, 0.0), (4, 2, 0.0), (3, 3, 1e-3)])
+def test_decode_paged_parity(B, kbits, vbits, gate):
+    # four sequences of different lengths (one empty, one of a single token,
+    # one filling its page table) in shuffled pages with junk in the rest
+    say(f"paged decode K{kbits} V{vbits} gate={gate}")
+    gk, ok = pair(B, 128, kbits)
+    gv, ov = pair(B, 128, vbits)
+    hq, hkv, P, max_pages = 8, 2, 256, 8
+    ctxs = [1500, 1, 0, max_pages * P]
+    batch = len(ctxs)
+    n_pages = batch * max_pages + 3
+    rng = np.random.default_rng(52 + kbits)
+    pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    q = as_exact((3.0 if gate else 1.0) * rng.standard_normal((batch, hq, 128)), "f32")
+    krec = [O.encode(ok, rng.standard_normal((hkv * n, 128))) if n else None for n in ctxs]
+    vrec = [O.encode(ov, rng.standard_normal((hkv * n, 128))) if n else None for n in ctxs]
+    junk_k = O.encode(ok, rng.standard_normal((50, 128)))
+    junk_v = O.encode(ov, rng.standard_normal((50, 128)))
+    empty = lambda R: {k: np.asarray(R[k])[:0] for k in R}
+    kc = _fill_pages([r if r is not None else empty(junk_k) for r in krec], pt, hkv, P, n_pages, junk_k)
+    vc = _fill_pages([r if r is not None else empty(junk_v) for r in vrec], pt, hkv, P, n_pages, junk_v)
+    scale = 1 / math.sqrt(128)
+    out = B.tq_decode_attn_paged(gk, gv, to_dev(q, "f32"), B.packed_from_numpy(kc), B.packed_from_numpy(vc),
+                                 torch.tensor(ctxs, dtype=torch.int32, device="cuda"), torch.from_numpy(pt).cuda(), P,
+                                 max(ctxs), hkv, scale, gate, out_dtype=torch.float32).cpu().numpy()
+    assert np.all(out[2] == 0)                      # the empty context
+    G = hq // hkv
+    for b, n in enumerate(ctxs):
+        if n == 0:
+            continue
+        kr = O.gather_paged(kc, pt, b, hkv, n, P)
+        vr = O.gather_paged(vc, pt, b, hkv, n, P)
+        if gate == 0:
+            ref = O.decode_attn_accumulated(ok, ov, q[b:b + 1].astype(np.float64), kr, vr, 1, hq, hkv, n, scale)
+            err = row_rel_err(out[b:b + 1], ref).max()
+            say(f"  sequence {b} (ctx {n}): max row err {err:.2e}")
+            assert err <= 1e-4
+        else:
+            ref, keep, local = O.decode_attn_sparse_v(ok, ov, q[b:b + 1].astype(np.float64), kr, vr, 1, hq, hkv,
+                                                      n, scale, gate, B.tq_decode_attn_chunk(hq, hkv))
+            say(f"  sequence {b} (ctx {n}): dropped {np.mean(~keep):.3f}")
+            assert_sparse_v_close(out[b:b + 1], ref, local, gate, O.dequantize(ov, vr), hkv, n, 1e-4)
+
+
+def test_decode_paged_identity_equals_contiguous(B):
+    # one KV head and the identity page table: the paged layout is the
+    # contiguous one, and the output is bitwise that of tq_decode_attn
+    gc, oc = pair(B, 128, 3)
+    ctx, P = 3000, 1024
+    rng = np.random.default_rng(53)
+    k = as_exact(rng.standard_normal((ctx, 128)), "bf16")
+    v = as_exact(rng.standard_normal((ctx, 128)), "bf16")
+    q = as_exact(rng.standard_normal((1, 4, 128)), "bf16")
+    kp, vp = B.tq_encode_kv(gc, to_dev(k, "bf16"), to_dev(v, "bf16"))
+    a = B.tq_decode_attn(gc, gc, to_dev(q, "bf16"), kp, vp, ctx, 1, 0.1, out_dtype=torch.float32)
+    pt = torch.arange(3, dtype=torch.int32, device="cuda").view(1, 3)
+    b = B.tq_decode_attn_paged(gc, gc, to_dev(q, "bf16"), kp, vp, torch.tensor([ctx], dtype=torch.int32,
+                               device="cuda"), pt, P, ctx, 1, 0.1, out_dtype=torch.float32)
+    assert torch.equal(a, b)
+
+
+def test_decode_paged_rejects_bad_arguments(B):
+    gc, _ = pair(B, 128, 3)
+    kp = B.alloc_packed(gc, 1024)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    ctx = torch.ones(1, dtype=torch.int32, device="cuda")
+    pt = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    with pytest.raises(B.TQError):      # page size not a multiple of 128
+        B.tq_decode_attn_paged(gc, gc, q, kp, kp, ctx, pt, 100, 100, 1, 0.1)
+    with pytest.raises(B.TQError):      # max_ctx beyond the page table
+        B.tq_decode_attn_paged(gc, gc, q, kp, kp, ctx, pt, 128, 257, 1, 0.1)
+    with pytest.raises(B.TQError):      # more than 4 query heads per KV head
+        B.tq_decode_attn_paged(gc, gc, torch.zeros((1, 8, 128), device="cuda"), kp, kp, ctx, pt, 128, 128, 1, 0.1)
+
+
 # ---------------------------------------------------------------- search
 @pytest.mark.parametrize("d,bits,n_db,nq,k", [(128, 4, 70001, 8, 10), (128, 3, 3000, 5, 1), (128, 4, 2000, 3, 100),
                                               (1536, 4, 2500, 4, 10), (256, 4, 5000, 17, 10), (512, 3, 1500, 2, 5),
