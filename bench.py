@@ -345,6 +345,86 @@ def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d):
     return res
 
 
+def paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d):
+    """Paged cache on the long-context decode shape.  (1) The same caches
+    copied into 256-position pages in shuffled order, read through the page
+    table, against the contiguous call.  (2) Eight sequences of 128K, 64K, ...,
+    1K positions in one paged pool (one decode step for all).  (3) Appending
+    one token per KV head to K and V of those eight sequences."""
+    import torch
+    hkv, hq, P = 8, 32, 256
+    scale = 1 / math.sqrt(d)
+    res = {}
+    npg = ctx // P
+
+    def to_pages(src, perm):  # rows [kv_head][position] -> [page][kv_head][slot]
+        idx = torch.empty(hkv * ctx, dtype=torch.int64, device=dev)
+        pos = torch.arange(ctx, device=dev)
+        for kh in range(hkv):
+            idx[(perm[pos // P] * hkv + kh) * P + pos % P] = kh * ctx + pos
+        return B.Packed(src.codes[idx].contiguous(), src.signs[idx].contiguous(), src.norm[idx].contiguous(),
+                        src.rnorm[idx].contiguous())
+    perm = torch.randperm(npg, generator=g, device=dev)
+    psets = [(to_pages(kk, perm), to_pages(vv, perm)) for kk, vv in dsets]
+    pt = perm.to(torch.int32).view(1, npg).contiguous()  # position block i sits in page perm[i]
+    cl = torch.tensor([ctx], dtype=torch.int32, device=dev)
+    it = iter(range(10 ** 9))
+
+    def paged():
+        kk, vv = psets[next(it) % len(psets)]
+        B.tq_decode_attn_paged(codec3, codec3, qd, kk, vv, cl, pt, P, ctx, hkv, scale, out=out, ws=ws)
+    ms = _time(paged, 30, graph=True)
+    res["decode_attn_c4_paged256"] = {"ms": ms, "page_size": P, "buffer_sets": len(psets),
+                                      **_hbm(ms, 2 * hkv * ctx * codec3.record_bytes + 2 * hq * d * 2)}
+    print(f"[bench] C4 decode attention, 256-position pages {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del psets
+    # eight sequences of different lengths in one pool
+    lens = [ctx >> i for i in range(8)]
+    bsz, mp = len(lens), ctx // P
+    n_pages = sum(n // P for n in lens)
+    pool_k = B.alloc_packed(codec3, n_pages * hkv * P, dev)
+    pool_v = B.alloc_packed(codec3, n_pages * hkv * P, dev)
+    for t in (pool_k.codes, pool_k.signs, pool_v.codes, pool_v.signs):
+        t.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, t.shape, generator=g, device=dev, dtype=torch.int32))
+    for t in (pool_k.norm, pool_v.norm):
+        t.copy_(torch.rand(t.shape, generator=g, device=dev) + 0.5)
+    for t in (pool_k.rnorm, pool_v.rnorm):
+        t.copy_(torch.rand(t.shape, generator=g, device=dev) * 0.3)
+    order = torch.randperm(n_pages, generator=g, device=dev).to(torch.int32)
+    ptab = torch.zeros((bsz, mp), dtype=torch.int32, device=dev)
+    o = 0
+    for b, n in enumerate(lens):
+        ptab[b, :n // P] = order[o:o + n // P]
+        o += n // P
+    cls = torch.tensor(lens, dtype=torch.int32, device=dev)
+    qb = torch.randn((bsz, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    outb = torch.empty((bsz, hq, d), dtype=torch.bfloat16, device=dev)
+    wsb = torch.empty(B.lib.tq_decode_attn_paged_workspace(codec3.handle, codec3.handle, bsz, hq, hkv, ctx),
+                      dtype=torch.uint8, device=dev)
+    ms = _time(lambda: B.tq_decode_attn_paged(codec3, codec3, qb, pool_k, pool_v, cls, ptab, P, ctx, hkv, scale,
+                                              out=outb, ws=wsb), 30, graph=True)
+    tot = sum(lens)
+    res["decode_attn_paged_8seq"] = {"ms": ms, "ctx_lens": lens, "page_size": P,
+                                     "keys_per_s": hq // hkv * hkv * tot / (ms * 1e-3),
+                                     **_hbm(ms, 2 * hkv * tot * codec3.record_bytes + 2 * bsz * hq * d * 2)}
+    print(f"[bench] paged decode, 8 sequences 1K..128K {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    # append one token per (sequence, KV head) to K and V: the step before decode
+    xk = torch.randn((bsz, hkv, 1, d), generator=g, device=dev).to(torch.bfloat16)
+    xv = torch.randn((bsz, hkv, 1, d), generator=g, device=dev).to(torch.bfloat16)
+    cla = (cls - 1).contiguous()      # rewrite each sequence's last position
+    wsa = torch.empty(max(B.lib.tq_encode_append_paged_workspace(codec3.handle, bsz, hkv, 1), 16), dtype=torch.uint8,
+                      device=dev)
+
+    def append():
+        B.tq_encode_append_paged(codec3, xk, cla, ptab, P, n_pages, pool_k, ws=wsa)
+        B.tq_encode_append_paged(codec3, xv, cla, ptab, P, n_pages, pool_v, ws=wsa)
+    ms = _time(append, 50, graph=True)
+    res["append_paged_8seq"] = {"ms": ms, "tokens": 2 * bsz * hkv, "bound": "latency"}
+    print(f"[bench] paged append of K and V, 8 x 8 tokens {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    del pool_k, pool_v
+    return res
+
+
 def time_stages(B, I, codec3, dev, args):
     """The other rows of the path, each timed on its own configuration with
     synthetic data drawn on the GPU (torch, seeded), with the roofline that
@@ -447,6 +527,7 @@ def time_stages(B, I, codec3, dev, args):
     print(f"[bench] C4 decode attention {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     if not args.no_stage_sparse_v:
         res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d))
+    res.update(paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d))
     del kp, vp, dsets, ws, k_c4
     # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
     bsz, hkv, ctx, nq = 16, 8, 8192, 16

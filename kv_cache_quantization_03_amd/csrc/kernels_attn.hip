@@ -283,8 +283,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
 // fourth chunk, and its slice of S for Sᵀ J before using any of them; the
 // chunk weights then go through LDS.  (Contexts over 128 chunks load the
 // values of the further chunks in more rounds.)
+// ctx_lens (paged caches, else nullptr): sequence b uses its first
+// ceil(ctx_lens[b] / 1024) chunks; the decode kernel did not write the rest.
 __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevParams PV, const float* __restrict__ part,
-                                                                         int Hq, int nkv, int n_chunks,
+                                                                         int Hq, int nkv, int n_chunks_grid,
+                                                                         const int32_t* __restrict__ ctx_lens,
                                                                          const float* __restrict__ S,
                                                                          const float* __restrict__ Dsign, void* out,
                                                                          int out_bf16) {
@@ -298,8 +301,9 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int bk = b * nkv + h / G, g = h % G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid & 255, qtr = tid >> 8;
+  const int n_chunks = ctx_lens ? min(n_chunks_grid, (max(ctx_lens[b], 0) + 1023) / 1024) : n_chunks_grid;
   const int rec = 2 + 2 * d;
-  const float* base = part + (static_cast<int64_t>(bk) * n_chunks * G + g) * rec;
+  const float* base = part + (static_cast<int64_t>(bk) * n_chunks_grid * G + g) * rec;
   // unsigned 32-bit offsets from the block's base: the loads take the scalar base plus one offset register
   const unsigned cstride = static_cast<unsigned>(G * rec);
   // ---- loads
@@ -313,7 +317,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   for (int u = 0; u < 16; ++u) sv[u] = S[static_cast<unsigned>((pp * 16 + u) * d + jj)];
   float vc[U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) vc[u] = base[static_cast<unsigned>(min(qtr + 4 * u, n_chunks - 1)) * cstride + 2u + j];
+  for (int u = 0; u < U; ++u)
+    vc[u] = base[static_cast<unsigned>(max(0, min(qtr + 4 * u, n_chunks - 1))) * cstride + 2u + j];
   // ---- global max and chunk weights
   float m = wave_max(m_own);
   if (lane == 0) red[wv] = m;
@@ -339,7 +344,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   }
   for (int c0 = qtr + 4 * U; c0 < n_chunks; c0 += 4 * U) {  // contexts over 128 chunks
 #pragma unroll
-    for (int u = 0; u < U; ++u) vc[u] = base[static_cast<unsigned>(min(c0 + 4 * u, n_chunks - 1)) * cstride + 2u + j];
+    for (int u = 0; u < U; ++u)
+      vc[u] = base[static_cast<unsigned>(max(0, min(c0 + 4 * u, n_chunks - 1))) * cstride + 2u + j];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + 4 * u;
@@ -463,7 +469,8 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   }
   if (cv->prm.d == 128 && cv->prm.m == 128) {
     hipLaunchKernelGGL(decode_combine128_kernel, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part,
-                       n_q_heads, n_kv_heads, n_chunks, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);
+                       n_q_heads, n_kv_heads, n_chunks, pm ? pm->ctx_lens : nullptr, cv->dS, cv->dD, out,
+                       out_dt == TQ_BF16 ? 1 : 0);
     return hipGetLastError();
   }
   auto run = [&]<int E>() -> hipError_t {

@@ -104,22 +104,19 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   // own length, clamped to the grid and to the page table
   int ctx = ctx_max;
   if constexpr (PAGED) ctx = max(0, min(min(pm.ctx_lens[bk / nkv], ctx_max), pm.max_pages * pm.page_size));
-  // record row of a key (position) of this head; page_size is a multiple of 128,
-  // so the 64 or 128 keys of a wave share one page
-  auto row_of = [&](int key) -> int64_t {
-    if constexpr (PAGED) {
-      const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + key / pm.page_size];
-      return (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + key % pm.page_size;
-    } else {
-      return hrow + key;
-    }
-  };
-  if (PAGED && chunk * kDecChunk >= ctx) {  // block-uniform: an empty chunk of a shorter sequence
-    constexpr int REC = 2 + 2 * kPrepD;       // max = -inf, weight sum and M, J = 0
-    float* out = part + (static_cast<int64_t>(bk) * n_chunks + chunk) * G * REC;
-    for (int e = threadIdx.x; e < G * REC; e += NT) out[e] = e % REC == 0 ? -INFINITY : 0.f;
-    return;
+  // a chunk past a shorter sequence's end: the combine reads only the chunks in use
+  if (PAGED && chunk * kDecChunk >= ctx) return;  // block-uniform
+  // Record rows.  Every key the wave touches, clamped to ctx - 1, lies in the
+  // wave's 128-key block, or for a wave past the end in the block of key
+  // ctx - 1; page_size is a multiple of 128, so that block sits in one page,
+  // found with one page-table read per wave: row(key) = wrow + key - wkey.
+  const int wkey = kbase < ctx ? kbase : ((ctx - 1) & ~(kDecKeysPerWave - 1));
+  int64_t wrow = hrow + wkey;
+  if constexpr (PAGED) {
+    const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + wkey / pm.page_size];
+    wrow = (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + wkey % pm.page_size;
   }
+  auto row_of = [&](int key) -> int64_t { return wrow + (key - wkey); };
 
   // ---- loads: the K records, then the head's query operands (prepared once
   // per KV head by attn_prep_inblock_kernel; L2-resident)
