@@ -29,7 +29,7 @@ import math
 from dataclasses import dataclass
 
 import numpy as np
-from scipy import special
+from scipy import integrate, special
 
 __all__ = [
     "splitmix64", "rademacher_signs", "gaussian_matrix",
@@ -42,6 +42,9 @@ __all__ = [
     "prepare_query", "score", "attn_logits",
     "decode_attn_materialized", "decode_attn_accumulated", "decode_attn_sparse_v",
     "paged_row", "append_paged", "gather_paged", "decode_attn_paged",
+    "polar_angle_cdf", "polar_angle_density", "polar_lloyd_max", "polar_transform", "polar_reconstruct",
+    "polar_slots", "PolarCodec", "make_polar_codec", "polar_encode", "polar_encode_given_codes",
+    "polar_dequantize", "polar_score",
     "search_topk", "bf16_round",
 ]
 
@@ -618,6 +621,239 @@ def decode_attn_paged(codec_k: Codec, codec_v: Codec, q, k_cache, v_cache, page_
             out[b] = decode_attn_sparse_v(codec_k, codec_v, q[b:b + 1], kr, vr, 1, n_q_heads, n_kv_heads, n,
                                           scale, gate, chunk)[0][0]
     return out
+
+
+# --------------------------------------------------------------------------
+# O8. PolarQuant first stage (深度拆解 第二部分 PolarQuant; vocus 第一階段):
+# rotate, write the rotated vector in polar form by pairing coordinates into
+# (radius, angle), pair the radii again and recurse until one radius is left,
+# and quantize every angle with a Lloyd-Max quantizer fitted to that angle's
+# known law; then the same residual QJL stage as before.
+#
+# Readings.
+# * y = R x/ν as in O4 (unit vector), d a power of two: log2(d) levels.  Level
+#   1 pairs (y_2i, y_2i+1); level l > 1 pairs the radii (r_2i, r_2i+1) of level
+#   l-1; angle θ = atan2(second, first), radius = hypot.  The last radius is
+#   ‖y‖ = 1 and is not stored (ν is).
+# * Angle laws for y uniform on the sphere: level 1 is uniform on the circle
+#   (taken in [0, 2π)); for l > 1 with n = 2^(l-1) coordinates per half,
+#   sin²θ ~ Beta(n/2, n/2), i.e. f(θ) = 2/B(n/2, n/2) (sin θ cos θ)^(n-1) on
+#   [0, π/2] (the ratio of the norms of two independent Gaussian halves).
+# * b bits for every angle: d-1 angles in about the b·d bits the scalar stage
+#   spends, so "bits" keeps its meaning (b angle bits + 1 QJL bit).  Level 1's
+#   optimal quantizer is the uniform one (centroids (k+1/2)·2π/2^b); levels > 1
+#   run Lloyd-Max on f (MSE in the angle).
+# * Code slots: level l's d/2^l angles take slots [d - d/2^(l-1), d - d/2^l) in
+#   order, slot d-1 is unused (code 0); the codes are packed in bit planes as in
+#   O4.  The stored reconstruction tables are cos and sin of every centroid
+#   rounded to fp32; ŷ is rebuilt top-down from radius 1 with them.
+# * Decisions are taken in fp64 here; the kernels take them in fp32, so an
+#   angle within 1e-5 rad of a boundary may legitimately get the other code.
+# --------------------------------------------------------------------------
+def polar_angle_density(theta, level: int):
+    theta = np.asarray(theta, dtype=np.float64)
+    if level == 1:
+        return np.where((theta >= 0) & (theta < 2 * math.pi), 1.0 / (2 * math.pi), 0.0)
+    n = 1 << (level - 1)
+    with np.errstate(divide="ignore"):
+        logf = (math.log(2.0) - special.betaln(n / 2, n / 2)
+                + (n - 1) * np.log(np.clip(np.sin(theta) * np.cos(theta), 0, None)))
+    return np.where((theta >= 0) & (theta <= math.pi / 2), np.exp(logf), 0.0)
+
+
+def polar_angle_cdf(theta, level: int):
+    theta = np.asarray(theta, dtype=np.float64)
+    if level == 1:
+        return np.clip(theta / (2 * math.pi), 0.0, 1.0)
+    n = 1 << (level - 1)
+    t = np.clip(theta, 0.0, math.pi / 2)
+    return special.betainc(n / 2, n / 2, np.sin(t) ** 2)
+
+
+def _polar_first_moment(lo: float, hi: float, level: int) -> float:
+    mid = math.pi / 4
+    pts = [mid] if lo < mid < hi else None
+    val, _ = integrate.quad(lambda t: t * float(polar_angle_density(t, level)), lo, hi, points=pts,
+                            epsabs=0.0, epsrel=1e-13, limit=200)
+    return val
+
+
+def polar_lloyd_max(level: int, b: int, tol: float = 1e-13, max_iter: int = 5000):
+    """(centroids, boundaries, iterations) of the 2^b-level quantizer of the
+    level's angle, ascending, fp64."""
+    L = 1 << b
+    if level == 1:
+        step = 2 * math.pi / L
+        return (np.arange(L) + 0.5) * step, np.arange(1, L) * step, 0
+    n = 1 << (level - 1)
+    c = np.arcsin(np.sqrt(special.betaincinv(n / 2, n / 2, (np.arange(L) + 0.5) / L)))
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = np.concatenate([[0.0], t, [math.pi / 2]])
+        mass = polar_angle_cdf(edges[1:], level) - polar_angle_cdf(edges[:-1], level)
+        mom = np.array([_polar_first_moment(edges[k], edges[k + 1], level) for k in range(L)])
+        new = mom / mass
+        new = 0.5 * (new + (math.pi / 2 - new[::-1]))      # symmetric about π/4
+        delta = float(np.max(np.abs(new - c)))
+        c = new
+        if delta < tol:
+            break
+    return c, 0.5 * (c[:-1] + c[1:]), it
+
+
+def polar_transform(y):
+    """y: (n, d), d a power of two.  Returns (angles, radius): angles[l-1] is
+    the (n, d/2^l) array of level-l angles, radius the (n,) final radius."""
+    r = np.asarray(y, dtype=np.float64)
+    angles = []
+    level = 1
+    while r.shape[1] > 1:
+        a, b = r[:, 0::2], r[:, 1::2]
+        th = np.arctan2(b, a)
+        if level == 1:
+            th = np.where(th < 0, th + 2 * math.pi, th)
+        angles.append(th)
+        r = np.hypot(a, b)
+        level += 1
+    return angles, r[:, 0]
+
+
+def polar_reconstruct(cos_tabs, sin_tabs, idx_levels, radius=None):
+    """Top-down rebuild: cos_tabs[l-1][k], sin_tabs[l-1][k] = cos, sin of the
+    level's centroid k; idx_levels[l-1] = (n, d/2^l) codes.  Returns (n, d)."""
+    n = idx_levels[0].shape[0]
+    r = np.ones((n, 1)) if radius is None else np.asarray(radius, dtype=np.float64).reshape(n, 1)
+    for lv in range(len(idx_levels), 0, -1):
+        k = idx_levels[lv - 1]
+        ca = np.asarray(cos_tabs[lv - 1], dtype=np.float64)[k]
+        sa = np.asarray(sin_tabs[lv - 1], dtype=np.float64)[k]
+        nxt = np.empty((n, 2 * r.shape[1]))
+        nxt[:, 0::2] = r * ca
+        nxt[:, 1::2] = r * sa
+        r = nxt
+    return r
+
+
+def polar_slots(d: int):
+    """Slot ranges [lo, hi) of each level's angles in the code vector."""
+    out, lo, cnt = [], 0, d // 2
+    while cnt >= 1:
+        out.append((lo, lo + cnt))
+        lo += cnt
+        cnt //= 2
+    return out
+
+
+@dataclass
+class PolarCodec:
+    d: int
+    bits: int
+    m: int
+    seed: int
+    D: np.ndarray
+    R: np.ndarray
+    S: np.ndarray
+    centroids: list       # per level, fp64 ascending
+    bounds: list          # per level, fp64
+    iters: list
+
+    @property
+    def b(self) -> int:
+        return self.bits - 1
+
+    @property
+    def levels(self) -> int:
+        return len(self.centroids)
+
+    @property
+    def cos32(self) -> list:
+        return [np.cos(c).astype(np.float32) for c in self.centroids]
+
+    @property
+    def sin32(self) -> list:
+        return [np.sin(c).astype(np.float32) for c in self.centroids]
+
+    @property
+    def code_words(self) -> int:
+        return self.b * self.d // 32
+
+    @property
+    def sign_words(self) -> int:
+        return self.m // 32
+
+    @property
+    def record_bytes(self) -> int:
+        return 4 * (self.code_words + self.sign_words) + 8
+
+
+def make_polar_codec(d: int, bits: int, m: int | None = None, seed: int = 1234) -> PolarCodec:
+    if d < 2 or d & (d - 1):
+        raise ValueError("the recursive polar stage needs d a power of two")
+    if bits < 2:
+        raise ValueError("bits must be >= 2")
+    m = d if m is None else m
+    books = [polar_lloyd_max(lv, bits - 1) for lv in range(1, int(math.log2(d)) + 1)]
+    return PolarCodec(d=d, bits=bits, m=m, seed=seed, D=rademacher_signs(d, seed), R=rotation_matrix(d, seed),
+                      S=gaussian_matrix(m, d, seed), centroids=[c for c, _, _ in books],
+                      bounds=[t for _, t, _ in books], iters=[i for _, _, i in books])
+
+
+def _polar_yhat_from_slots(codec: PolarCodec, idx):
+    levels = [idx[:, lo:hi] for lo, hi in polar_slots(codec.d)]
+    return polar_reconstruct(codec.cos32, codec.sin32, levels)
+
+
+def polar_encode(codec: PolarCodec, x: np.ndarray) -> dict:
+    x = np.asarray(x, dtype=np.float64)
+    nu = np.sqrt(np.sum(x * x, axis=1))
+    safe = np.where(nu > 0, nu, 1.0)
+    u = np.where(nu[:, None] > 0, x / safe[:, None], 0.0)
+    y = u @ codec.R.T
+    angles, _ = polar_transform(y)
+    idx = np.zeros((x.shape[0], codec.d), dtype=np.int64)
+    for lv, ((lo, hi), th) in enumerate(zip(polar_slots(codec.d), angles), start=1):
+        idx[:, lo:hi] = np.sum(codec.bounds[lv - 1][None, None, :] < th[:, :, None], axis=2)
+    out = polar_encode_given_codes(codec, x, idx)
+    out.update(codes=pack_planes(idx, codec.b), norm=nu.astype(np.float32), idx=idx, angles=angles)
+    return out
+
+
+def polar_encode_given_codes(codec: PolarCodec, x: np.ndarray, idx: np.ndarray) -> dict:
+    x = np.asarray(x, dtype=np.float64)
+    nu = np.sqrt(np.sum(x * x, axis=1))
+    safe = np.where(nu > 0, nu, 1.0)
+    u = np.where(nu[:, None] > 0, x / safe[:, None], 0.0)
+    y = u @ codec.R.T
+    yhat = _polar_yhat_from_slots(codec, np.asarray(idx, np.int64))
+    r = y - yhat
+    gamma = np.sqrt(np.sum(r * r, axis=1))
+    z = r @ codec.S.astype(np.float64).T
+    return {"signs": pack_bits((z >= 0).astype(np.int64)), "rnorm": gamma.astype(np.float32), "z": z,
+            "y": y, "yhat": yhat, "r": r}
+
+
+def _polar_unpack(codec: PolarCodec, packed: dict):
+    idx = unpack_planes(np.asarray(packed["codes"]), codec.b, codec.d)
+    tau = (2 * unpack_bits(np.asarray(packed["signs"]), codec.m) - 1).astype(np.float64)
+    nu = np.asarray(packed["norm"], dtype=np.float32).astype(np.float64)
+    gamma = np.asarray(packed["rnorm"], dtype=np.float32).astype(np.float64)
+    return _polar_yhat_from_slots(codec, idx), tau, nu, gamma
+
+
+def polar_dequantize(codec: PolarCodec, packed: dict) -> np.ndarray:
+    yhat, tau, nu, gamma = _polar_unpack(codec, packed)
+    corr = qjl_constant(codec.m) * gamma[:, None] * (tau @ codec.S.astype(np.float64))
+    return nu[:, None] * ((yhat + corr) @ codec.R)
+
+
+def polar_score(codec: PolarCodec, q: np.ndarray, packed: dict) -> np.ndarray:
+    """ℓ = ν (⟨q', ŷ⟩ + sqrt(pi/2)/m · γ · ⟨p, τ⟩), q' = R q, p = S q'."""
+    q = np.atleast_2d(np.asarray(q, dtype=np.float64))
+    qr = q @ codec.R.T
+    p = qr @ codec.S.astype(np.float64).T
+    yhat, tau, nu, gamma = _polar_unpack(codec, packed)
+    return nu[None, :] * (qr @ yhat.T + qjl_constant(codec.m) * gamma[None, :] * (p @ tau.T))
 
 
 # --------------------------------------------------------------------------

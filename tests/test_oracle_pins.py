@@ -580,3 +580,108 @@ def test_search_topk_matches_brute_force_sort(codec3):
         order = sorted(range(500), key=lambda i: (-full[qi, i], i))[:10]
         assert list(idx[qi]) == order
         assert np.array_equal(sc[qi], full[qi, order])
+
+
+# ---------------------------------------------------------------- O8 PolarQuant first stage
+def test_polar_transform_worked_cases():
+    # d = 4 by hand: level-1 angles of (y0, y1), (y2, y3) in [0, 2π), then the
+    # level-2 angle atan2(‖(y2, y3)‖, ‖(y0, y1)‖)
+    ang, r = O.polar_transform(np.array([[1.0, 0, 0, 0], [0, 0, 0, 1.0], [-1.0, 0, 0, 0], [0, -1.0, 0, 0],
+                                         [3.0, 4.0, 0, 12.0]]))
+    two_pi = 2 * math.pi
+    assert np.allclose(ang[0], [[0, 0], [0, math.pi / 2], [math.pi, 0], [1.5 * math.pi, 0],
+                                [math.atan2(4, 3), math.pi / 2]])
+    assert np.allclose(ang[1][:, 0], [0, math.pi / 2, 0, 0, math.atan2(12, 5)])
+    assert np.allclose(r, [1, 1, 1, 1, 13])
+    assert np.all((ang[0] >= 0) & (ang[0] < two_pi))
+
+
+def test_polar_angle_laws_match_beta():
+    # Monte Carlo: for Gaussian (hence uniform-direction) vectors the level-1
+    # angles are uniform and, for level l > 1, sin²θ ~ Beta(n/2, n/2) with
+    # n = 2^(l-1) (SciPy's beta distribution as the reference)
+    from scipy import stats
+    y = np.random.default_rng(61).standard_normal((20000, 64))
+    ang, r = O.polar_transform(y)
+    assert stats.kstest(ang[0].ravel() / (2 * math.pi), "uniform").pvalue > 1e-3
+    for lv in range(2, 7):
+        n = 1 << (lv - 1)
+        s2 = np.sin(ang[lv - 1][:, 0]) ** 2
+        assert stats.kstest(s2, stats.beta(n / 2, n / 2).cdf).pvalue > 1e-3, lv
+    assert np.allclose(r, np.linalg.norm(y, axis=1))
+
+
+def test_polar_density_and_cdf_consistent():
+    from scipy import integrate
+    for lv in range(2, 8):
+        tot, _ = integrate.quad(lambda t: float(O.polar_angle_density(t, lv)), 0, math.pi / 2, points=[math.pi / 4])
+        assert abs(tot - 1) < 1e-10
+        for t in (0.3, 0.7, 0.8, 1.2):
+            part, _ = integrate.quad(lambda u: float(O.polar_angle_density(u, lv)), 0, t, epsabs=1e-14)
+            assert abs(part - float(O.polar_angle_cdf(t, lv))) < 1e-9
+
+
+@pytest.mark.parametrize("b", [1, 2, 3])
+def test_polar_lloyd_max_conditions(b):
+    from scipy import integrate
+    # level 1: the uniform quantizer of the circle
+    c, t, _ = O.polar_lloyd_max(1, b)
+    L = 1 << b
+    assert np.allclose(c, (np.arange(L) + 0.5) * 2 * math.pi / L) and np.allclose(t, np.arange(1, L) * 2 * math.pi / L)
+    for lv in (2, 4, 7):
+        c, t, _ = O.polar_lloyd_max(lv, b)
+        assert np.allclose(c + c[::-1], math.pi / 2, atol=1e-12)           # symmetric about π/4
+        assert np.allclose(t, 0.5 * (c[:-1] + c[1:]))                       # nearest neighbour
+        edges = np.concatenate([[0], t, [math.pi / 2]])
+        f = lambda u: float(O.polar_angle_density(u, lv))
+        for k in range(L):                                                  # centroid condition
+            m0, _ = integrate.quad(f, edges[k], edges[k + 1], epsabs=0, epsrel=1e-12, limit=200)
+            m1, _ = integrate.quad(lambda u: u * f(u), edges[k], edges[k + 1], epsabs=0, epsrel=1e-12, limit=200)
+            assert abs(m1 / m0 - c[k]) < 1e-9
+
+
+def test_polar_reconstruction_closed_form_and_unit_norm():
+    pc = O.make_polar_codec(4, 3, seed=7)
+    # slots: level-1 angles at 0, 1; the level-2 angle at 2; slot 3 unused
+    idx = np.array([[1, 3, 2, 0]])
+    y = O.polar_reconstruct(pc.cos32, pc.sin32, [idx[:, 0:2], idx[:, 2:3]])
+    a, b0, b1 = pc.centroids[1][2], pc.centroids[0][1], pc.centroids[0][3]
+    want = [math.cos(a) * math.cos(b0), math.cos(a) * math.sin(b0), math.sin(a) * math.cos(b1), math.sin(a) * math.sin(b1)]
+    assert np.allclose(y[0], want, atol=1e-7)
+    assert O.polar_slots(128) == [(0, 64), (64, 96), (96, 112), (112, 120), (120, 124), (124, 126), (126, 127)]
+    pc = O.make_polar_codec(128, 3, seed=7)
+    rnd = np.random.default_rng(62).integers(0, 4, (50, 128))
+    rec = {"codes": O.pack_planes(rnd, 2), "signs": np.zeros((50, 4), np.uint32),
+           "norm": np.ones(50, np.float32), "rnorm": np.zeros(50, np.float32)}
+    # ν = 1, γ = 0: the reconstruction is Rᵀ ŷ, whose norm is ‖ŷ‖
+    assert np.allclose(np.linalg.norm(O.polar_dequantize(pc, rec), axis=1), 1, atol=1e-6)
+
+
+def test_polar_encode_picks_nearest_angle():
+    pc = O.make_polar_codec(128, 4, seed=7)
+    e = O.polar_encode(pc, np.random.default_rng(63).standard_normal((200, 128)))
+    for lv, (lo, hi) in enumerate(O.polar_slots(128), start=1):
+        th = e["angles"][lv - 1]
+        c = pc.centroids[lv - 1]
+        dist = np.abs(th[:, :, None] - c[None, None, :])
+        if lv == 1:
+            dist = np.minimum(dist, 2 * math.pi - dist)
+        assert np.array_equal(e["idx"][:, lo:hi], np.argmin(dist, axis=2)), lv
+    assert np.all(e["idx"][:, 127] == 0)
+
+
+def test_polar_score_unbiased_and_matches_dequantize():
+    d = 32
+    base = O.make_polar_codec(d, 3, seed=5)
+    rng = np.random.default_rng(64)
+    x = rng.standard_normal((1, d)) * 2.0
+    q = rng.standard_normal((1, d))
+    e = O.polar_encode(base, x)
+    assert np.allclose(O.polar_score(base, q, e), q @ O.polar_dequantize(base, e).T, rtol=1e-12, atol=1e-12)
+    vals = []
+    for s in range(4000):
+        pc = O.PolarCodec(d=d, bits=3, m=d, seed=s, D=base.D, R=base.R, S=O.gaussian_matrix(d, d, seed=20_000 + s),
+                          centroids=base.centroids, bounds=base.bounds, iters=base.iters)
+        vals.append(float(O.polar_score(pc, q, O.polar_encode(pc, x))[0, 0]))
+    vals = np.array(vals)
+    assert abs(vals.mean() - float((q @ x.T)[0, 0])) < 3.5 * vals.std() / math.sqrt(vals.size)
