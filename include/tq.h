@@ -100,6 +100,7 @@ typedef struct {
   uint64_t seed;
   double centroids[16]; /* 2^b entries, ascending, fp64 */
   double bounds[15];    /* 2^b - 1 entries, midpoints of the centroids */
+  int32_t stage1;       /* 0: per-coordinate Lloyd-Max codes; 1: recursive polar angles */
 } tq_codec_info_t;
 
 /* ---------------------------------------------------------------- status */
@@ -128,6 +129,29 @@ tq_status_t tq_codec_build_host(int32_t head_dim, int32_t bits, int32_t qjl_dim,
  * device. */
 tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                             tq_codec_t* out);
+/* A codec whose first stage is PolarQuant's recursive polar form
+ * (深度拆解 第二部分 PolarQuant; vocus 第一階段: 3- or 4-bit angles): after
+ * the same rotation y = R x/ν, level 1 pairs the coordinates (y_2i, y_2i+1)
+ * into (radius, angle), each further level pairs the radii of the level
+ * below, down to one radius (‖y‖ = 1, not stored).  Every angle gets b =
+ * bits-1 bits: level 1's angles (in [0, 2π)) the uniform quantizer of the
+ * circle, level l > 1's (in [0, π/2], sin²θ ~ Beta(n/2, n/2), n = 2^(l-1))
+ * the Lloyd-Max quantizer of that law.  Codes: level l's d/2^l angles in
+ * slots [d - d/2^(l-1), d - d/2^l) of the usual bit-plane record, slot d-1
+ * unused (0); ŷ is rebuilt from radius 1 with cos and sin of the centroids
+ * (fp32), and the residual y - ŷ takes the same QJL stage, so the record size
+ * and the score ν(⟨q', ŷ⟩ + √(π/2)/m γ ⟨p, τ⟩) keep their form.
+ * head_dim 128 only; bits 2, 3 or 4.  Such codecs are accepted by
+ * tq_encode_kv, tq_attn_logits and its split form; the other calls return
+ * TQ_ERROR_NOT_SUPPORTED for them. */
+tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
+                                  tq_codec_t* out);
+/* Host only (no GPU needed): level l's (1..7) angle codebook of the polar
+ * stage for head_dim 128 and the given bits: centroids[2^b] and
+ * bounds[2^b - 1], fp64, ascending, and the Lloyd-Max iterations (0 for the
+ * uniform level 1).  Any output pointer may be NULL. */
+tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
+                               double* bounds, int32_t* iterations);
 /* The caller guarantees that no work using c is still in flight. */
 tq_status_t tq_codec_destroy(tq_codec_t c);
 tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info);

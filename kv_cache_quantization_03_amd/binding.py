@@ -33,7 +33,8 @@ class tq_codec_info_t(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("bits", C.c_int32), ("mse_bits", C.c_int32),
                 ("qjl_dim", C.c_int32), ("code_words", C.c_int32), ("sign_words", C.c_int32),
                 ("record_bytes", C.c_int32), ("lloyd_max_iterations", C.c_int32),
-                ("seed", C.c_uint64), ("centroids", C.c_double * 16), ("bounds", C.c_double * 15)]
+                ("seed", C.c_uint64), ("centroids", C.c_double * 16), ("bounds", C.c_double * 15),
+                ("stage1", C.c_int32)]
 
 
 def _load():
@@ -51,6 +52,9 @@ def _load():
         "tq_codec_create": (C.c_int, [i32, i32, i32, u64, C.POINTER(vp)]),
         "tq_codec_destroy": (C.c_int, [vp]),
         "tq_codec_info": (C.c_int, [vp, C.POINTER(tq_codec_info_t)]),
+        "tq_codec_create_polar": (C.c_int, [i32, i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
+        "tq_polar_book_host": (C.c_int, [i32, i32, i32, C.POINTER(C.c_double), C.POINTER(C.c_double),
+                                         C.POINTER(i32)]),
         "tq_encode_workspace": (sz, [vp, i64]),
         "tq_encode_kv": (C.c_int, [vp, vp, vp, C.c_int, i64, P, P, vp, sz, vp]),
         "tq_attn_logits_workspace": (sz, [vp, i32, i32, i32, i32]),
@@ -82,7 +86,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_build_host", "tq_codec_create",
-            "tq_codec_destroy", "tq_codec_info", "tq_encode_workspace", "tq_encode_kv",
+            "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
             "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
@@ -146,6 +150,7 @@ class Codec:
         self.iterations = info.lloyd_max_iterations
         self.centroids = np.array(info.centroids[:1 << self.b])
         self.bounds = np.array(info.bounds[:(1 << self.b) - 1])
+        self.polar = info.stage1 == 1
 
     def __del__(self):
         if getattr(self, "handle", None) and lib is not None:
@@ -159,6 +164,24 @@ def tq_codec_create(head_dim: int, bits: int, qjl_dim: int = 0, seed: int = 1234
     info = tq_codec_info_t()
     _check(lib.tq_codec_info(h, C.byref(info)), "tq_codec_info")
     return Codec(h, info)
+
+
+def tq_codec_create_polar(head_dim: int, bits: int, qjl_dim: int = 0, seed: int = 1234) -> Codec:
+    h = C.c_void_p()
+    _check(lib.tq_codec_create_polar(head_dim, bits, qjl_dim, seed, C.byref(h)), "tq_codec_create_polar")
+    info = tq_codec_info_t()
+    _check(lib.tq_codec_info(h, C.byref(info)), "tq_codec_info")
+    return Codec(h, info)
+
+
+def tq_polar_book_host(head_dim: int, bits: int, level: int):
+    """(centroids, bounds, iterations) of one level's angle codebook, fp64 (host only)."""
+    n = 1 << (bits - 1)
+    c = (C.c_double * n)()
+    t = (C.c_double * max(n - 1, 1))()
+    it = C.c_int32()
+    _check(lib.tq_polar_book_host(head_dim, bits, level, c, t, C.byref(it)), "tq_polar_book_host")
+    return np.array(c[:]), np.array(t[:n - 1]), it.value
 
 
 # ---------------------------------------------------------------- packed arrays

@@ -101,7 +101,128 @@ int lloyd_max(int d, int b, std::vector<double>* cent, std::vector<double>* bnd)
   return it;
 }
 
+// ---- recursive polar angle laws ---------------------------------------------
+// Level 1 angles are uniform on [0, 2π).  For level l > 1 with n = 2^(l-1),
+// sin²θ ~ Beta(n/2, n/2): f(θ) = 2/B(n/2, n/2) (sin θ cos θ)^(n-1) on [0, π/2].
+// With x = -cos 2θ, (sin θ cos θ)^(n-1) dθ ∝ (1 - x²)^((n-2)/2) dx: x follows
+// the coordinate law of a unit vector in n + 1 dimensions, so the CDF is
+// SphereLaw(n + 1).cdf(-cos 2θ).  The first moment ∫ θ f(θ) dθ is integrated
+// with composite Gauss-Legendre (16 nodes, nodes by Newton on P_16).
+struct GaussLegendre16 {
+  double x[16], w[16];
+  GaussLegendre16() {
+    const int n = 16;
+    for (int i = 0; i < n; ++i) {
+      double z = std::cos(M_PI * (i + 0.75) / (n + 0.5)), pp = 0;
+      for (int it = 0; it < 100; ++it) {
+        double p1 = 1, p2 = 0;
+        for (int j = 1; j <= n; ++j) {
+          const double p3 = p2;
+          p2 = p1;
+          p1 = ((2.0 * j - 1.0) * z * p2 - (j - 1.0) * p3) / j;
+        }
+        pp = n * (z * p1 - p2) / (z * z - 1.0);
+        const double z1 = z;
+        z = z1 - p1 / pp;
+        if (std::fabs(z - z1) < 1e-16) break;
+      }
+      x[i] = z;
+      w[i] = 2.0 / ((1.0 - z * z) * pp * pp);
+    }
+  }
+};
+
+struct PolarLaw {
+  int n;
+  double logC;
+  SphereLaw x_law;
+  explicit PolarLaw(int level) : n(1 << (level - 1)), x_law(n + 1) {
+    logC = std::log(2.0) - (2.0 * std::lgamma(n / 2.0) - std::lgamma(static_cast<double>(n)));
+  }
+  double density(double t) const {
+    const double sc = std::sin(t) * std::cos(t);
+    return sc <= 0 ? 0.0 : std::exp(logC + (n - 1) * std::log(sc));
+  }
+  double cdf(double t) const {
+    if (t <= 0) return 0.0;
+    if (t >= M_PI / 2) return 1.0;
+    return x_law.cdf(-std::cos(2.0 * t));
+  }
+  double first_moment(double lo, double hi) const {
+    static const GaussLegendre16 gl;
+    constexpr int kPanels = 64;
+    const double h = (hi - lo) / kPanels;
+    double acc = 0;
+    for (int p = 0; p < kPanels; ++p) {
+      const double a = lo + p * h, mid = a + 0.5 * h;
+      for (int i = 0; i < 16; ++i) {
+        const double t = mid + 0.5 * h * gl.x[i];
+        acc += 0.5 * h * gl.w[i] * t * density(t);
+      }
+    }
+    return acc;
+  }
+};
+
+// Codebook of one level's angle: level 1 the uniform quantizer of the circle;
+// level > 1 Lloyd-Max on f, kept symmetric about π/4 (f is log-concave there,
+// so the fixed point is unique).
+int polar_lloyd_max(int level, int b, std::vector<double>* cent, std::vector<double>* bnd) {
+  const int L = 1 << b;
+  cent->assign(L, 0.0);
+  bnd->assign(L - 1, 0.0);
+  if (level == 1) {
+    const double step = 2.0 * M_PI / L;
+    for (int k = 0; k < L; ++k) (*cent)[k] = (k + 0.5) * step;
+    for (int k = 1; k < L; ++k) (*bnd)[k - 1] = k * step;
+    return 0;
+  }
+  PolarLaw law(level);
+  const double w = std::fmin(M_PI / 4, 2.0 / std::sqrt(static_cast<double>(law.n)));
+  std::vector<double> c(L), nc(L), edges(L + 1);
+  for (int k = 0; k < L; ++k) c[k] = M_PI / 4 + ((2.0 * k + 1.0) / L - 1.0) * w;
+  int it = 0;
+  for (it = 1; it <= 5000; ++it) {
+    edges[0] = 0.0;
+    edges[L] = M_PI / 2;
+    for (int k = 1; k < L; ++k) edges[k] = 0.5 * (c[k - 1] + c[k]);
+    for (int k = 0; k < L; ++k)
+      nc[k] = law.first_moment(edges[k], edges[k + 1]) / (law.cdf(edges[k + 1]) - law.cdf(edges[k]));
+    double delta = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const double v = 0.5 * (nc[k] + (M_PI / 2 - nc[L - 1 - k]));
+      delta = std::fmax(delta, std::fabs(v - c[k]));
+      c[k] = v;
+    }
+    if (delta < 1e-13) break;
+  }
+  *cent = c;
+  for (int k = 0; k + 1 < L; ++k) (*bnd)[k] = 0.5 * (c[k] + c[k + 1]);
+  return it;
+}
+
 }  // namespace
+
+tq_status_t build_polar_tables(int d, int bits, int m, uint64_t seed, HostTables* out) {
+  if (d != 128) {
+    set_error("the recursive polar stage is built for head_dim 128");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  tq_status_t st = build_host_tables(d, bits, m, seed, out);
+  if (st != TQ_SUCCESS) return st;
+  try {
+    out->polar = true;
+    const int levels = 7;
+    out->pcent.resize(levels);
+    out->pbound.resize(levels);
+    out->piters.resize(levels);
+    for (int l = 1; l <= levels; ++l) out->piters[l - 1] = polar_lloyd_max(l, out->b, &out->pcent[l - 1], &out->pbound[l - 1]);
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed while building codec tables");
+    return TQ_ERROR_OUT_OF_MEMORY;
+  }
+  return TQ_SUCCESS;
+}
 
 bool supported_dim(int d) {
   return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024 || d == 1536;
@@ -244,8 +365,9 @@ void apply_hadamard_transposed(double* v, int d) {
 
 }  // namespace
 
-extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim,
-                                       uint64_t seed, tq_codec_t* out) {
+namespace {
+tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed, bool polar,
+                         tq_codec_t* out) {
   tq::clear_error();
   if (!out) {
     set_error("out is NULL");
@@ -257,10 +379,24 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
     set_error("host allocation failed");
     return TQ_ERROR_OUT_OF_MEMORY;
   }
-  tq_status_t st = tq::build_host_tables(head_dim, bits, qjl_dim, seed, &c->host);
+  tq_status_t st = polar ? tq::build_polar_tables(head_dim, bits, qjl_dim, seed, &c->host)
+                         : tq::build_host_tables(head_dim, bits, qjl_dim, seed, &c->host);
   if (st != TQ_SUCCESS) {
     delete c;
     return st;
+  }
+  if (polar) {
+    c->polar = true;
+    tq::PolarParams& pp = c->pol;
+    pp.levels = static_cast<int>(c->host.pcent.size());
+    pp.nl = 1 << c->host.b;
+    for (int l = 0; l < tq::kPolarMaxLevels; ++l)
+      for (int k = 0; k < 16; ++k) {
+        const bool in = l < pp.levels && k < pp.nl;
+        pp.cosc[l][k] = in ? static_cast<float>(std::cos(c->host.pcent[l][k])) : 0.f;
+        pp.sinc[l][k] = in ? static_cast<float>(std::sin(c->host.pcent[l][k])) : 0.f;
+        pp.bound[l][k] = in && k + 1 < pp.nl ? static_cast<float>(c->host.pbound[l][k]) : INFINITY;
+      }
   }
   const auto& h = c->host;
   tq::DevParams& p = c->prm;
@@ -343,6 +479,37 @@ extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t q
   return TQ_SUCCESS;
 }
 
+}  // namespace
+
+extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
+                                       tq_codec_t* out) {
+  return codec_create(head_dim, bits, qjl_dim, seed, false, out);
+}
+
+extern "C" tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
+                                             tq_codec_t* out) {
+  return codec_create(head_dim, bits, qjl_dim, seed, true, out);
+}
+
+extern "C" tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
+                                          double* bounds, int32_t* iterations) {
+  tq::clear_error();
+  if (head_dim != 128 || bits < 2 || bits > 4) {
+    set_error("the recursive polar stage is built for head_dim 128 and bits 2, 3 or 4");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  if (level < 1 || level > 7) {
+    set_error("level must be in 1..7 for head_dim 128");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  std::vector<double> c, t;
+  const int it = tq::polar_lloyd_max(level, bits - 1, &c, &t);
+  if (centroids) std::memcpy(centroids, c.data(), c.size() * sizeof(double));
+  if (bounds) std::memcpy(bounds, t.data(), t.size() * sizeof(double));
+  if (iterations) *iterations = it;
+  return TQ_SUCCESS;
+}
+
 extern "C" tq_status_t tq_codec_destroy(tq_codec_t c) {
   tq::clear_error();
   if (!c) {
@@ -378,6 +545,7 @@ extern "C" tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info) {
   info->sign_words = c->prm.sign_words;
   info->record_bytes = 4 * (c->prm.code_words + c->prm.sign_words) + 8;
   info->lloyd_max_iterations = h.iterations;
+  info->stage1 = c->polar ? 1 : 0;
   info->seed = h.seed;
   for (size_t k = 0; k < h.centroids.size(); ++k) info->centroids[k] = h.centroids[k];
   for (size_t k = 0; k < h.bounds.size(); ++k) info->bounds[k] = h.bounds[k];

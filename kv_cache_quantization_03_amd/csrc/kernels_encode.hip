@@ -232,16 +232,41 @@ __device__ __forceinline__ void load8(const __half* p, float (&v)[8]) {
   for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(a[i]);
 }
 
-template <typename T, int B>
+// Code of an angle: #{boundaries of its level below th} (ties low).
+template <int NL>
+__device__ __forceinline__ int polar_code(const float (&bound)[16], float th) {
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k + 1 < NL; ++k) c += bound[k] < th;
+  return c;
+}
+
+// POLAR: the recursive polar first stage (「谷歌 TurboQuant 深度拆解」 第二部分
+// PolarQuant) replaces the per-coordinate quantizer.  Lane l holds y_8l..y_8l+7:
+// levels 1-3 pair registers (4, 2, 1 angles per lane), levels 4-7 pair the
+// lanes l and l ^ 2^(level-4) (both lanes of a pair compute the same angle
+// from the same two radii).  Codes go to their slots in LDS (level 1: 4l + i,
+// level 2: 64 + 2l + i, level 3: 96 + l, level k >= 4: 128 - 2^(8-k) + node),
+// and ŷ is rebuilt top-down from radius 1 with the fp32 cos and sin tables.
+template <typename T, int B, bool POLAR>
 __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__ x, int64_t n, DevParams P,
-                                                           const float* __restrict__ Dsign,
+                                                           PolarParams PP, const float* __restrict__ Dsign,
                                                            const _Float16* __restrict__ S16,
                                                            uint32_t* __restrict__ codes, uint32_t* __restrict__ signs,
                                                            float* __restrict__ norm, float* __restrict__ rnorm) {
   constexpr int d = 128, NL = 1 << B;
   __shared__ __attribute__((aligned(16))) _Float16 rh[2][16][d + 8];  // r hi / lo of the pass's 16 vectors
+  __shared__ float ptab[POLAR ? 2 : 1][POLAR ? 7 : 1][POLAR ? NL : 1];  // cos, sin of every level's centroids
+  __shared__ uint8_t pcode[POLAR ? 16 : 1][POLAR ? d : 1];            // angle codes by slot
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l = lane & 15;
   const int vrow = 4 * wv + (lane >> 4);  // the lane's vector within the pass
+  if constexpr (POLAR) {
+    for (int e = threadIdx.x; e < 7 * NL; e += blockDim.x) {
+      ptab[0][e / NL][e % NL] = PP.cosc[e / NL][e % NL];
+      ptab[1][e / NL][e % NL] = PP.sinc[e / NL][e % NL];
+    }
+    __syncthreads();
+  }
   // fp16 S rows of this wave's outputs: A fragments [row block][K step][hi, lo]
   h8 sf[2][4][2];
 #pragma unroll
@@ -300,6 +325,70 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 #pragma unroll
     for (int p = 0; p < B; ++p) bits[p] = 0u;
     float rr[8], rs = 0.f;
+    if constexpr (POLAR) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = v[e] * kscale;
+      int c1[4], c2[2];
+      float r1[4], r2[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // level 1: angles in [0, 2π)
+        float th = atan2f(y[2 * i + 1], y[2 * i]);
+        th = th < 0.f ? th + 6.28318530717958647f : th;
+        c1[i] = polar_code<NL>(PP.bound[0], th);
+        r1[i] = sqrtf(y[2 * i] * y[2 * i] + y[2 * i + 1] * y[2 * i + 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        c2[i] = polar_code<NL>(PP.bound[1], atan2f(r1[2 * i + 1], r1[2 * i]));
+        r2[i] = sqrtf(r1[2 * i] * r1[2 * i] + r1[2 * i + 1] * r1[2 * i + 1]);
+      }
+      const int c3 = polar_code<NL>(PP.bound[2], atan2f(r2[1], r2[0]));
+      float rad = sqrtf(r2[0] * r2[0] + r2[1] * r2[1]);
+      int ck[4];  // levels 4..7: lanes l and l ^ 2^k
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float o = lane_xor_f(rad, k);
+        const bool hi = (l >> k) & 1;
+        const float a = hi ? o : rad, b = hi ? rad : o;
+        ck[k] = polar_code<NL>(PP.bound[3 + k], atan2f(b, a));
+        rad = sqrtf(a * a + b * b);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pcode[vrow][4 * l + i] = static_cast<uint8_t>(c1[i]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) pcode[vrow][64 + 2 * l + i] = static_cast<uint8_t>(c2[i]);
+      pcode[vrow][96 + l] = static_cast<uint8_t>(c3);
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if ((l & ((2 << k) - 1)) == 0) pcode[vrow][128 - (16 >> k) + (l >> (k + 1))] = static_cast<uint8_t>(ck[k]);
+      if (l == 0) pcode[vrow][127] = 0;
+      // ŷ top-down from radius 1
+      float R = 1.f;
+#pragma unroll
+      for (int k = 3; k >= 0; --k) R *= ((l >> k) & 1) ? ptab[1][3 + k][ck[k]] : ptab[0][3 + k][ck[k]];
+      float q2[2] = {R * ptab[0][2][c3], R * ptab[1][2][c3]};
+      float q1[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        q1[2 * i] = q2[i] * ptab[0][1][c2[i]];
+        q1[2 * i + 1] = q2[i] * ptab[1][1][c2[i]];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rr[2 * i] = y[2 * i] - q1[i] * ptab[0][0][c1[i]];
+        rr[2 * i + 1] = y[2 * i + 1] - q1[i] * ptab[1][0][c1[i]];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rs = fmaf(rr[e], rr[e], rs);
+      __builtin_amdgcn_wave_barrier();  // a vector's 16 lanes are one wave's: its LDS writes land first
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int cd = pcode[vrow][8 * l + e];
+#pragma unroll
+        for (int p = 0; p < B; ++p) bits[p] |= static_cast<uint32_t>((cd >> p) & 1) << e;
+      }
+    } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float y = v[e] * kscale;
@@ -321,6 +410,7 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
       rr[e] = y - yh;
       rs = fmaf(rr[e], rr[e], rs);
     }
+    }  // POLAR
     rs = row_sum(rs);
     // code word w (coordinates 32w..32w+31) of plane p from lanes 4w..4w+3
 #pragma unroll
@@ -495,6 +585,7 @@ bool sproj_mfma_eligible(const tq_codec_s* c) {
 }
 
 bool encode_fused_eligible(const tq_codec_s* c) {
+  if (c->polar) return true;  // the only polar encode (d = 128, made so at codec creation)
   const char* v = std::getenv("TQ_ENCODE_KERNEL");
   if (v && std::string(v) == "split") return false;
   return c->prm.d == 128 && c->prm.m == 128 && c->dS16 != nullptr;
@@ -513,8 +604,12 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
   if (encode_fused_eligible(c)) {
     const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * kEncPasses)));
     auto go = [&]<int B>() -> hipError_t {
-      hipLaunchKernelGGL((encode_fused_kernel<T, B>), grid, dim3(256), 0, s, x, n, P, c->dD, c->dS16, out.codes,
-                         out.signs, out.norm, out.rnorm);
+      if (c->polar)
+        hipLaunchKernelGGL((encode_fused_kernel<T, B, true>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD, c->dS16,
+                           out.codes, out.signs, out.norm, out.rnorm);
+      else
+        hipLaunchKernelGGL((encode_fused_kernel<T, B, false>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD,
+                           c->dS16, out.codes, out.signs, out.norm, out.rnorm);
       return hipGetLastError();
     };
     switch (P.b) {

@@ -80,6 +80,120 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
   }
 }
 
+// ----------------------------------------------------------------------------
+// Logits for a codec with the recursive polar first stage (d = 128): the MSE
+// term is ⟨q', ŷ⟩ with ŷ rebuilt from the angle codes, the QJL term is the
+// usual one.  16 lanes per key, lane l rebuilding ŷ_8l..ŷ_8l+7 from the codes
+// of its path (levels 7..4: nodes l >> (k+1), level 3: slot 96 + l, level 2:
+// slots 64 + 2l + i, level 1: slots 4l + i) with the cos and sin tables in
+// LDS; a block of 256 threads scores kPolarKeys keys against up to 4 query
+// vectors.  VALU-bound: ~200 lane-instructions per key and lane.
+// ----------------------------------------------------------------------------
+constexpr int kPolarKeys = 256;
+
+template <int B>
+__global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
+                                                           const float* __restrict__ proj, int Hq, int nq, int G,
+                                                           int nkv, int64_t ctx, tq_packed_t k,
+                                                           float* __restrict__ logits) {
+  constexpr int d = 128, NL = 1 << B;
+  __shared__ float tab[2][7][NL];
+  for (int e = threadIdx.x; e < 7 * NL; e += 256) {
+    tab[0][e / NL][e % NL] = PP.cosc[e / NL][e % NL];
+    tab[1][e / NL][e % NL] = PP.sinc[e / NL][e % NL];
+  }
+  __syncthreads();
+  const int l = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
+  const int nqv = nq * G, qv0 = blockIdx.z * 4;
+  float qv[4][8], pv[4][8];
+  int64_t orow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int v = qv0 + t;
+    const bool ok = v < nqv;
+    const int qi = ok ? v / G : 0, h = kh * G + (ok ? v % G : 0);
+    const int64_t qr = (static_cast<int64_t>(b) * nq + qi) * Hq + h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qv[t][e] = ok ? qrot[qr * d + 8 * l + e] : 0.f;
+      pv[t][e] = ok ? proj[qr * d + 8 * l + e] : 0.f;
+    }
+    orow[t] = ok ? ((static_cast<int64_t>(b) * Hq + h) * nq + qi) * ctx : -1;
+  }
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kPolarKeys;
+  const int64_t k1 = min(ctx, k0 + kPolarKeys);
+  for (int64_t key = k0 + grp; key < k1; key += 16) {  // uniform within the 16-lane group
+    const int64_t row = static_cast<int64_t>(bk) * ctx + key;
+    uint32_t w[B][4];
+#pragma unroll
+    for (int p = 0; p < B; ++p) {
+      const uint4 u = reinterpret_cast<const uint4*>(k.codes + row * (4 * B))[p];
+      w[p][0] = u.x; w[p][1] = u.y; w[p][2] = u.z; w[p][3] = u.w;
+    }
+    auto code = [&](int slot) {
+      int c = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) c |= static_cast<int>((w[p][slot >> 5] >> (slot & 31)) & 1u) << p;
+      return c;
+    };
+    float R = 1.f;
+#pragma unroll
+    for (int kk = 3; kk >= 0; --kk) {  // levels 7..4
+      const int c = code(128 - (16 >> kk) + (l >> (kk + 1)));
+      R *= ((l >> kk) & 1) ? tab[1][3 + kk][c] : tab[0][3 + kk][c];
+    }
+    const int c3 = code(96 + l);
+    const float q2[2] = {R * tab[0][2][c3], R * tab[1][2][c3]};
+    float yh[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c2 = code(64 + 2 * l + i);
+      const float qa = q2[i] * tab[0][1][c2], qb = q2[i] * tab[1][1][c2];
+      const int ca = code(4 * l + 2 * i), cb = code(4 * l + 2 * i + 1);
+      yh[4 * i] = qa * tab[0][0][ca];
+      yh[4 * i + 1] = qa * tab[1][0][ca];
+      yh[4 * i + 2] = qb * tab[0][0][cb];
+      yh[4 * i + 3] = qb * tab[1][0][cb];
+    }
+    const uint32_t sw = k.signs[row * 4 + (l >> 2)] >> (8 * (l & 3));
+    const float nu = k.norm[row], ga = k.rnorm[row];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float mse = 0.f, qj = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mse = fmaf(qv[t][e], yh[e], mse);
+        qj += ((sw >> e) & 1u) ? pv[t][e] : -pv[t][e];
+      }
+      mse = row_sum(mse);
+      qj = row_sum(qj);
+      if (l == 0 && orow[t] >= 0) logits[orow[t] + key] = nu * (mse + P.qjl_kappa * ga * qj);
+    }
+  }
+}
+
+hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+  const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
+  const float* qrot = static_cast<const float*>(ws);
+  const float* proj = qrot + nv * c->prm.d;
+  const int G = n_q_heads / n_kv_heads;
+  const dim3 grid(static_cast<unsigned>(ceil_div(ctx, kPolarKeys)), batch * n_kv_heads,
+                  static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_queries) * G, 4)));
+  auto go = [&]<int B>() -> hipError_t {
+    hipLaunchKernelGGL((logits_polar_kernel<B>), grid, dim3(256), 0, s, c->prm, c->pol, qrot, proj, n_q_heads,
+                       n_queries, G, n_kv_heads, ctx, k, logits);
+    return hipGetLastError();
+  };
+  switch (c->prm.b) {
+    case 1: return go.template operator()<1>();
+    case 2: return go.template operator()<2>();
+    case 3: return go.template operator()<3>();
+  }
+  return hipErrorInvalidValue;
+}
+
 bool logits_mfma_eligible(const tq_codec_s* c);
 size_t logits_mfma_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
 hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
@@ -93,14 +207,14 @@ hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt
                                hipStream_t s);
 
 size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
-  if (logits_mfma_eligible(c)) return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
+  if (!c->polar && logits_mfma_eligible(c)) return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
   const size_t nv = static_cast<size_t>(batch) * n_queries * n_q_heads;
   return nv * (c->prm.d + c->prm.m) * sizeof(float);
 }
 
 hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                               int n_kv_heads, int n_queries, void* ws, hipStream_t s) {
-  if (logits_mfma_eligible(c))
+  if (!c->polar && logits_mfma_eligible(c))
     return launch_logits_mfma_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
   float* qrot = static_cast<float*>(ws);
@@ -111,7 +225,7 @@ hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt,
 hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                          int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits, void* ws,
                          hipStream_t s) {
-  if (logits_fused_eligible(c, batch, n_q_heads, n_kv_heads, n_queries, ctx))
+  if (!c->polar && logits_fused_eligible(c, batch, n_q_heads, n_kv_heads, n_queries, ctx))
     return launch_logits_fused(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   hipError_t e = launch_logits_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   if (e != hipSuccess) return e;
@@ -120,6 +234,7 @@ hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int 
 
 hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                                  int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+  if (c->polar) return launch_logits_polar(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   if (logits_mfma_eligible(c))
     return launch_logits_mfma(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, ctx, logits, s);
   const DevParams& P = c->prm;

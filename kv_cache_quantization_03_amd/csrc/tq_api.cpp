@@ -203,6 +203,10 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
                           tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream, const char* name) {
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
+  if (ck->polar || cv->polar) {
+    set_error("decode attention takes codecs with the per-coordinate first stage");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
   if (st != TQ_SUCCESS) return st;
@@ -335,6 +339,7 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
                                       float* out_score, void* ws, size_t ws_bytes, void* stream) {
   tq::clear_error();
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (c->polar) { set_error("search takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
   if (n_db < 1 || n_queries < 0) { set_error("need n_db >= 1 and n_queries >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (topk < 1 || topk > 1024 || topk > n_db) { set_error("need 1 <= topk <= min(n_db, 1024)"); return TQ_ERROR_INVALID_VALUE; }
   if (n_queries == 0) return TQ_SUCCESS;

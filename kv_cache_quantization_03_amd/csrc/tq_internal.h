@@ -25,11 +25,18 @@ struct HostTables {
   std::vector<double> centroids; // [2^b] ascending
   std::vector<double> bounds;    // [2^b-1]
   int iterations = 0;
+  // recursive polar first stage (when polar): per level (1..log2 d) the angle
+  // codebook, ascending, and its boundaries
+  bool polar = false;
+  std::vector<std::vector<double>> pcent, pbound;
+  std::vector<int> piters;
 };
 
 // Builds every table on the host.  Returns TQ_SUCCESS or an error status (and
 // sets the thread-local message).
 tq_status_t build_host_tables(int d, int bits, int m, uint64_t seed, HostTables* out);
+// The same plus the per-level angle codebooks of the recursive polar stage.
+tq_status_t build_polar_tables(int d, int bits, int m, uint64_t seed, HostTables* out);
 bool supported_dim(int d);
 
 // Device constant block of one codec: everything a kernel needs besides S.
@@ -43,6 +50,16 @@ struct DevParams {
   float inv_sqrt_d;    // 1/sqrt(d)
   float mrow_bound;    // max_i ||row i of M = S R||_2 (fp32 M, rounded up): |(M q)_i| <= mrow_bound ||q||
   int d, b, m, code_words, sign_words, n_planes;
+};
+
+// Tables of the recursive polar stage for the kernels: per level l (index
+// l-1), cos and sin of every centroid (fp32) and the boundaries (unused +inf).
+constexpr int kPolarMaxLevels = 8;
+struct PolarParams {
+  float cosc[kPolarMaxLevels][16];
+  float sinc[kPolarMaxLevels][16];
+  float bound[kPolarMaxLevels][16];
+  int levels, nl;  // log2 d, 2^b
 };
 
 // A paged cache (see tq_decode_attn_paged): page_table[b][i] holds positions
@@ -81,6 +98,8 @@ struct tq_codec_s {
   float* dMt = nullptr;  // [d][m]: (S R)ᵀ, so that p = S R q needs no rotated query
   float* dD = nullptr;   // [d] ±1
   _Float16* dS16 = nullptr;  // [2][m][d]: S = hi + lo in fp16 (m = d, d a multiple of 128; else nullptr)
+  bool polar = false;        // first stage: recursive polar angles instead of per-coordinate codes
+  tq::PolarParams pol{};
 };
 
 namespace tq {

@@ -110,3 +110,58 @@ def assert_sparse_v_close(out, ref, local, gate, vhat, hkv, ctx, tol):  # batch 
     print(f"  positions near the gate {int(amb.sum())}, max row err {row_rel_err(out, ref).max():.2e}, "
           f"worst diff/bound {np.max(diff / bound):.3f}", flush=True)
     assert np.all(diff <= bound)
+
+
+ANGLE_BAND = 1e-5  # rad
+
+
+def check_polar_encode(pc: O.PolarCodec, x64: np.ndarray, gpu: dict, label: str = "") -> dict:
+    """Compare a GPU encode with a polar codec against the oracle.  Angle
+    codes: bit-exact except angles within ANGLE_BAND of the boundary between
+    the two codes (for level 1 also of the wrap 0 = 2π), each checked; no rate
+    cap, because a vector whose rotated coordinates share one magnitude (a
+    basis vector) puts many angles exactly on a boundary (multiples of π/4).
+    Vectors with a differing code are re-derived by the oracle given the
+    GPU's codes.  ν and γ: relative 2e-6 and 1e-5 (γ carries
+    the fp32 products of the reconstruction); signs: bit-exact except |z| < BAND."""
+    ref = O.polar_encode(pc, x64)
+    n, d = x64.shape
+    gi = O.unpack_planes(gpu["codes"], pc.b, d)
+    ri = ref["idx"]
+    diff = gi != ri
+    n_diff = int(diff.sum())
+    if n_diff:
+        L = 1 << pc.b
+        for v, s in zip(*np.nonzero(diff)):
+            lv = next(i for i, (lo, hi) in enumerate(O.polar_slots(d), start=1) if lo <= s < hi)
+            lo = O.polar_slots(d)[lv - 1][0]
+            th = ref["angles"][lv - 1][v, s - lo]
+            a, b = sorted((int(gi[v, s]), int(ri[v, s])))
+            if lv == 1 and (a, b) == (0, L - 1):
+                dist = min(th, 2 * np.pi - th)
+            else:
+                assert b == a + 1, f"{label}: code jump at ({v},{s})"
+                dist = abs(th - pc.bounds[lv - 1][a])
+            assert dist < ANGLE_BAND, f"{label}: angle code differs at ({v},{s}), {dist:.2e} rad from the boundary"
+    assert np.allclose(gpu["norm"], ref["norm"], rtol=NORM_RTOL, atol=0), f"{label}: norm"
+    rows = np.unique(np.nonzero(diff)[0]) if n_diff else np.array([], np.int64)
+    exp_signs, exp_rnorm, z = ref["signs"].copy(), ref["rnorm"].copy(), ref["z"].copy()
+    if rows.size:
+        rd = O.polar_encode_given_codes(pc, x64[rows], gi[rows])
+        exp_signs[rows], exp_rnorm[rows], z[rows] = rd["signs"], rd["rnorm"], rd["z"]
+    assert np.allclose(gpu["rnorm"], exp_rnorm, rtol=1e-5, atol=1e-7), f"{label}: rnorm"
+    sd = O.unpack_bits(gpu["signs"], pc.m) != O.unpack_bits(exp_signs, pc.m)
+    if sd.any():
+        assert np.all(np.abs(z[sd]) < BAND), f"{label}: {int(sd.sum())} sign bits differ outside the band"
+    return {"code_mismatch": n_diff, "sign_mismatch": int(sd.sum()), "ref": ref}
+
+
+def polar_records_like(pc: O.PolarCodec, x64: np.ndarray, gpu: dict) -> dict:
+    """The oracle's polar records for x64 conditioned on the GPU's legitimate
+    choices (its angle codes and its sign bits), after check_polar_encode."""
+    check_polar_encode(pc, x64, gpu, "conditioned")
+    gi = O.unpack_planes(gpu["codes"], pc.b, x64.shape[1])
+    rd = O.polar_encode_given_codes(pc, x64, gi)
+    nu = np.sqrt(np.sum(np.asarray(x64, np.float64) ** 2, axis=1)).astype(np.float32)
+    return {"codes": np.asarray(gpu["codes"]).copy(), "signs": np.asarray(gpu["signs"]).copy(), "norm": nu,
+            "rnorm": rd["rnorm"]}

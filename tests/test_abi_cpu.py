@@ -98,3 +98,21 @@ def test_codec_create_without_gpu_reports_hip_error(B):
     st = B.lib.tq_codec_create(128, 3, 0, 1, C.byref(h))
     assert st == 6 and not h.value
     assert B.lib.tq_last_error().decode()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_host_polar_books_match_oracle(B, bits):
+    # the C++ per-level angle codebooks (composite Gauss-Legendre first
+    # moments) against the oracle's (SciPy quadrature)
+    for level in range(1, 8):
+        c, t, it = B.tq_polar_book_host(128, bits, level)
+        oc, ot, _ = O.polar_lloyd_max(level, bits - 1)
+        assert np.allclose(c, oc, rtol=0, atol=1e-10) and np.allclose(t, ot, rtol=0, atol=1e-10), (bits, level)
+        assert (it == 0) == (level == 1)
+
+
+def test_host_polar_books_reject(B):
+    with pytest.raises(B.TQError):
+        B.tq_polar_book_host(256, 3, 1)
+    with pytest.raises(B.TQError):
+        B.tq_polar_book_host(128, 3, 8)

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.parity import assert_sparse_v_close, check_encode, oracle_records_like, row_rel_err, tol_for
+from tests.parity import (assert_sparse_v_close, check_encode, check_polar_encode, oracle_records_like,
+                          polar_records_like, row_rel_err, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -625,6 +626,87 @@ def test_decode_paged_rejects_bad_arguments(B):
         B.tq_decode_attn_paged(gc, gc, q, kp, kp, ctx, pt, 128, 257, 1, 0.1)
     with pytest.raises(B.TQError):      # more than 4 query heads per KV head
         B.tq_decode_attn_paged(gc, gc, torch.zeros((1, 8, 128), device="cuda"), kp, kp, ctx, pt, 128, 128, 1, 0.1)
+
+
+# ---------------------------------------------------------------- PolarQuant first stage
+_polar = {}
+
+
+def polar_pair(B, bits, seed=1234):
+    if (bits, seed) not in _polar:
+        _polar[(bits, seed)] = (B.tq_codec_create_polar(128, bits, 0, seed), O.make_polar_codec(128, bits, seed=seed))
+    return _polar[(bits, seed)]
+
+
+@pytest.mark.parametrize("bits,dtype", [(2, "f32"), (3, "bf16"), (3, "f32"), (4, "f16"), (4, "f32")])
+def test_polar_encode_parity(B, bits, dtype):
+    say(f"polar encode bits={bits} {dtype}")
+    gc, pc = polar_pair(B, bits)
+    assert gc.polar and gc.record_bytes == pc.record_bytes
+    x = rand_keys(1500, 128, seed=300 + bits, dtype=dtype)   # includes a zero vector and a near-basis one
+    kp, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
+    torch.cuda.synchronize()
+    st = check_polar_encode(pc, x.astype(np.float64), kp.numpy(), f"polar b{bits}")
+    say(f"  angle codes differing (in band): {st['code_mismatch']}, signs in band: {st['sign_mismatch']}")
+
+
+@pytest.mark.parametrize("bits,batch,hq,hkv,nq,ctx", [(3, 1, 8, 2, 1, 1000), (2, 2, 4, 4, 3, 333), (4, 1, 32, 8, 1, 257),
+                                                     (3, 1, 1, 1, 5, 1)])
+def test_polar_logits_oracle_records(B, bits, batch, hq, hkv, nq, ctx):
+    # the scorer alone: oracle-encoded records, fp32 queries, bar 1e-4
+    say(f"polar logits bits={bits} batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx}")
+    gc, pc = polar_pair(B, bits)
+    rng = np.random.default_rng(ctx + 17 * bits)
+    rec = O.polar_encode(pc, rng.standard_normal((batch * hkv * ctx, 128)) * rng.lognormal(0, 0.5, (batch * hkv * ctx, 1)))
+    q = as_exact(rng.standard_normal((batch, nq, hq, 128)), "f32")
+    lg = B.tq_attn_logits(gc, to_dev(q, "f32"), B.packed_from_numpy(rec), ctx, hkv).cpu().numpy()
+    G = hq // hkv
+    worst = 0.0
+    for b in range(batch):
+        for kh in range(hkv):
+            rows = slice((b * hkv + kh) * ctx, (b * hkv + kh + 1) * ctx)
+            qv = q[b, :, kh * G:(kh + 1) * G].transpose(1, 0, 2).reshape(G * nq, 128)
+            ref = O.polar_score(pc, qv.astype(np.float64), {k: rec[k][rows] for k in ("codes", "signs", "norm", "rnorm")})
+            got = lg[b, kh * G:(kh + 1) * G].reshape(G * nq, ctx)
+            worst = max(worst, row_rel_err(got, ref).max())
+    say(f"  max row err {worst:.2e}")
+    assert worst <= 1e-4
+
+
+def test_polar_end_to_end_and_split_form(B):
+    gc, pc = polar_pair(B, 3)
+    hq, hkv, ctx = 8, 2, 2000
+    rng = np.random.default_rng(71)
+    k = as_exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    q = as_exact(rng.standard_normal((1, 1, hq, 128)), "bf16")
+    kp, _ = B.tq_encode_kv(gc, to_dev(k, "bf16"))
+    lg = B.tq_attn_logits(gc, to_dev(q, "bf16"), kp, ctx, hkv)
+    prep = B.tq_attn_query_prep(gc, to_dev(q, "bf16"), hkv)
+    lg2 = B.tq_attn_logits_prepped(gc, prep, (1, 1, hq), kp, ctx, hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(lg, lg2)
+    rec = polar_records_like(pc, k.astype(np.float64), kp.numpy())
+    G = hq // hkv
+    worst = 0.0
+    for kh in range(hkv):
+        rows = slice(kh * ctx, (kh + 1) * ctx)
+        ref = O.polar_score(pc, q[0, 0, kh * G:(kh + 1) * G].astype(np.float64),
+                            {kk: x[rows] for kk, x in rec.items()})
+        worst = max(worst, row_rel_err(lg[0, kh * G:(kh + 1) * G, 0].cpu().numpy(), ref).max())
+    say(f"polar end to end: max row err {worst:.2e}")
+    assert worst <= 1e-3
+
+
+def test_polar_codec_limits(B):
+    gc, _ = polar_pair(B, 3)
+    with pytest.raises(B.TQError):
+        B.tq_codec_create_polar(256, 3)
+    kp = B.alloc_packed(gc, 64)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn(gc, gc, q, kp, kp, 64, 1, 0.1)
+    with pytest.raises(B.TQError):
+        B.tq_search_topk(gc, kp, torch.zeros((1, 128), device="cuda"), 5)
 
 
 # ---------------------------------------------------------------- search
