@@ -345,6 +345,32 @@ def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d):
     return res
 
 
+def polar_stage(B, I, dev, k, q, ctx, d):
+    """The PolarQuant first stage (3-bit: 2-bit angles + 1 QJL bit) on the
+    Llama-8B decode shape: encode of the 262144 keys, then one decode step of
+    logits (prep launch + the polar scorer), 24 rotating buffer sets."""
+    import torch
+    pc = B.tq_codec_create_polar(d, 3, 0, I.CODEC_SEED)
+    kp = B.alloc_packed(pc, k.shape[0], dev)
+    ms_e = _time(lambda: B.tq_encode_kv(pc, k, k_out=kp), 20, graph=True)
+    ns = 24
+    sets = [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()), q.clone(),
+             torch.empty((1, 32, 1, ctx), device=dev),
+             torch.empty(B.tq_attn_logits_workspace(pc, 1, 32, 8, 1), dtype=torch.uint8, device=dev))
+            for _ in range(ns)]
+    it = iter(range(10 ** 9))
+
+    def step():
+        kk, qq, ll, ww = sets[next(it) % ns]
+        B.tq_attn_logits(pc, qq, kk, ctx, 8, logits=ll, ws=ww)
+    ms = _time(step, 240, graph=True)
+    print(f"[bench] polar 3-bit: encode {ms_e * 1e3:.1f} us, logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    return {"polar_encode_c2": {"ms": ms_e, "vectors_per_s": k.shape[0] / (ms_e * 1e-3), "bound": "alu"},
+            "polar_logits_c2_3bit": {"ms": ms, "keys_per_s": 32 * ctx / (ms * 1e-3), "buffer_sets": ns,
+                                     **_hbm(ms, 8 * ctx * pc.record_bytes + 32 * ctx * 4 + 32 * d * 2),
+                                     "note": "VALU-bound: y-hat rebuilt per key from the angle codes"}}
+
+
 def paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d):
     """Paged cache on the long-context decode shape.  (1) The same caches
     copied into 256-position pages in shuffled order, read through the page
@@ -469,7 +495,9 @@ def time_stages(B, I, codec3, dev, args):
     res["logits_c2_4bit"] = {"ms": ms, "keys_per_s": 32 * ctx / (ms * 1e-3), "buffer_sets": ns,
                              **_hbm(ms, 8 * ctx * c4.record_bytes + 32 * ctx * 4 + 32 * d * 2)}
     print(f"[bench] C2 4-bit logits {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
-    del k, kp4, sets
+    del kp4, sets
+    res.update(polar_stage(B, I, dev, k, q, ctx, d))
+    del k
     # Streaming-read ceiling at the C2 step's algorithmic byte count: plain
     # 16-byte loads (tq_diag_stream_read), rotating buffers, timed the same way
     nbytes = (8 * 32768 * codec3.record_bytes + 32 * 32768 * 4 + 32 * d * 2) // 16 * 16
