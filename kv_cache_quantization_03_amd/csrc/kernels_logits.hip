@@ -83,11 +83,13 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // ----------------------------------------------------------------------------
 // Logits for a codec with the recursive polar first stage (d = 128): the MSE
 // term is ⟨q', ŷ⟩ with ŷ rebuilt from the angle codes, the QJL term is the
-// usual one.  16 lanes per key, lane l rebuilding ŷ_8l..ŷ_8l+7 from the codes
-// of its path (levels 7..4: nodes l >> (k+1), level 3: slot 96 + l, level 2:
-// slots 64 + 2l + i, level 1: slots 4l + i) with the cos and sin tables in
-// LDS; a block of 256 threads scores kPolarKeys keys against up to 4 query
-// vectors.  VALU-bound: ~200 lane-instructions per key and lane.
+// usual one.  One thread per key: it walks the 64 level-1 pairs in order,
+// keeping the products of the upper levels' factors along its path (the
+// factors of levels <= ctz(i) + 2 change at pair i, two per pair on average),
+// so ŷ costs about four multiplications per pair.  The query values are the
+// same for every thread of the block, so they are read as scalar operands;
+// the loops are unrolled, so every code's slot and bit are constants.  Up to
+// 4 query vectors per block (grid.z splits the rest).
 // ----------------------------------------------------------------------------
 constexpr int kPolarKeys = 256;
 
@@ -97,16 +99,13 @@ __global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarPar
                                                            int nkv, int64_t ctx, tq_packed_t k,
                                                            float* __restrict__ logits) {
   constexpr int d = 128, NL = 1 << B;
-  __shared__ float tab[2][7][NL];
-  for (int e = threadIdx.x; e < 7 * NL; e += 256) {
-    tab[0][e / NL][e % NL] = PP.cosc[e / NL][e % NL];
-    tab[1][e / NL][e % NL] = PP.sinc[e / NL][e % NL];
-  }
-  __syncthreads();
-  const int l = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  __shared__ float2 tab[7][NL];  // (cos, sin) of every level's centroids
+  __shared__ float psum[4];      // Σ_i p_i of each tile vector
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
-  float qv[4][8], pv[4][8];
+  const float* qp[4];
+  const float* pp[4];
   int64_t orow[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -114,63 +113,73 @@ __global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarPar
     const bool ok = v < nqv;
     const int qi = ok ? v / G : 0, h = kh * G + (ok ? v % G : 0);
     const int64_t qr = (static_cast<int64_t>(b) * nq + qi) * Hq + h;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qv[t][e] = ok ? qrot[qr * d + 8 * l + e] : 0.f;
-      pv[t][e] = ok ? proj[qr * d + 8 * l + e] : 0.f;
-    }
+    qp[t] = qrot + qr * d;
+    pp[t] = proj + qr * d;
     orow[t] = ok ? ((static_cast<int64_t>(b) * Hq + h) * nq + qi) * ctx : -1;
   }
-  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kPolarKeys;
-  const int64_t k1 = min(ctx, k0 + kPolarKeys);
-  for (int64_t key = k0 + grp; key < k1; key += 16) {  // uniform within the 16-lane group
-    const int64_t row = static_cast<int64_t>(bk) * ctx + key;
-    uint32_t w[B][4];
+  if (tid < 7 * NL) tab[tid / NL][tid % NL] = float2{PP.cosc[tid / NL][tid % NL], PP.sinc[tid / NL][tid % NL]};
+  {
+    const float s = wave_sum(pp[wv][lane] + pp[wv][lane + 64]);  // wave w: tile vector w
+    if (lane == 0) psum[wv] = s;
+  }
+  __syncthreads();
+  const int64_t key = static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid;
+  if (key >= ctx) return;
+  const int64_t row = static_cast<int64_t>(bk) * ctx + key;
+  uint32_t w[B][4];
 #pragma unroll
-    for (int p = 0; p < B; ++p) {
-      const uint4 u = reinterpret_cast<const uint4*>(k.codes + row * (4 * B))[p];
-      w[p][0] = u.x; w[p][1] = u.y; w[p][2] = u.z; w[p][3] = u.w;
+  for (int p = 0; p < B; ++p) {
+    const uint4 u = reinterpret_cast<const uint4*>(k.codes + row * (4 * B))[p];
+    w[p][0] = u.x; w[p][1] = u.y; w[p][2] = u.z; w[p][3] = u.w;
+  }
+  const uint4 sg = reinterpret_cast<const uint4*>(k.signs)[row];
+  const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+  auto code = [&](int slot) {  // slot is a constant after unrolling
+    int c = 0;
+#pragma unroll
+    for (int p = 0; p < B; ++p) c |= static_cast<int>((w[p][slot >> 5] >> (slot & 31)) & 1u) << p;
+    return c;
+  };
+  float mse[4] = {0.f, 0.f, 0.f, 0.f}, qj[4] = {0.f, 0.f, 0.f, 0.f};
+  float prod[9];  // prod[lv]: product of the factors of levels 7..lv along the current path
+  prod[8] = 1.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    // levels whose factor changes at pair i: lv <= ctz(i) + 2 (all at i = 0)
+    const int hi = i == 0 ? 7 : (__builtin_ctz(i) + 2 < 7 ? __builtin_ctz(i) + 2 : 7);
+#pragma unroll
+    for (int lv = 7; lv >= 2; --lv) {
+      if (lv > hi) continue;
+      const int node = i >> (lv - 1), side = (i >> (lv - 2)) & 1;
+      const int slot = 128 - (256 >> lv) + node;  // level lv's angles start at 128 - 2^(8-lv)
+      const float2 cs = tab[lv - 1][code(slot)];
+      prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
     }
-    auto code = [&](int slot) {
-      int c = 0;
+    const float2 c1 = tab[0][code(i)];
+    const float y0 = prod[2] * c1.x, y1 = prod[2] * c1.y;
 #pragma unroll
-      for (int p = 0; p < B; ++p) c |= static_cast<int>((w[p][slot >> 5] >> (slot & 31)) & 1u) << p;
-      return c;
-    };
-    float R = 1.f;
+    for (int t = 0; t < 4; ++t) mse[t] = fmaf(qp[t][2 * i + 1], y1, fmaf(qp[t][2 * i], y0, mse[t]));
+    // one pair's work stays together: without these the compiler keeps all
+    // 128 ŷ values live and forms the dot products afterwards (256 registers)
 #pragma unroll
-    for (int kk = 3; kk >= 0; --kk) {  // levels 7..4
-      const int c = code(128 - (16 >> kk) + (l >> (kk + 1)));
-      R *= ((l >> kk) & 1) ? tab[1][3 + kk][c] : tab[0][3 + kk][c];
-    }
-    const int c3 = code(96 + l);
-    const float q2[2] = {R * tab[0][2][c3], R * tab[1][2][c3]};
-    float yh[8];
+    for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(mse[t]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c2 = code(64 + 2 * l + i);
-      const float qa = q2[i] * tab[0][1][c2], qb = q2[i] * tab[1][1][c2];
-      const int ca = code(4 * l + 2 * i), cb = code(4 * l + 2 * i + 1);
-      yh[4 * i] = qa * tab[0][0][ca];
-      yh[4 * i + 1] = qa * tab[1][0][ca];
-      yh[4 * i + 2] = qb * tab[0][0][cb];
-      yh[4 * i + 3] = qb * tab[1][0][cb];
-    }
-    const uint32_t sw = k.signs[row * 4 + (l >> 2)] >> (8 * (l & 3));
-    const float nu = k.norm[row], ga = k.rnorm[row];
+  for (int j = 0; j < d; ++j) {
+    const float bit = static_cast<float>((sw[j >> 5] >> (j & 31)) & 1u);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float mse = 0.f, qj = 0.f;
+    for (int t = 0; t < 4; ++t) qj[t] = fmaf(pp[t][j], bit, qj[t]);
+    if ((j & 7) == 7) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        mse = fmaf(qv[t][e], yh[e], mse);
-        qj += ((sw >> e) & 1u) ? pv[t][e] : -pv[t][e];
-      }
-      mse = row_sum(mse);
-      qj = row_sum(qj);
-      if (l == 0 && orow[t] >= 0) logits[orow[t] + key] = nu * (mse + P.qjl_kappa * ga * qj);
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(qj[t]));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  const float nu = k.norm[row], ga = k.rnorm[row];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)  // Σ p τ = 2 Σ_{τ=+1} p - Σ p
+    if (orow[t] >= 0) logits[orow[t] + key] = nu * (mse[t] + P.qjl_kappa * ga * (2.f * qj[t] - psum[t]));
 }
 
 hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
@@ -212,8 +221,16 @@ size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_h
   return nv * (c->prm.d + c->prm.m) * sizeof(float);
 }
 
+hipError_t launch_qprep128(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads, int n_kv_heads,
+                           int n_queries, float* qrot, float* proj, hipStream_t s);
+
 hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                               int n_kv_heads, int n_queries, void* ws, hipStream_t s) {
+  if (c->polar) {  // fp32 q' and p for the polar scorer (d = 128)
+    float* qrot = static_cast<float*>(ws);
+    float* proj = qrot + static_cast<int64_t>(batch) * n_queries * n_q_heads * c->prm.d;
+    return launch_qprep128(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, qrot, proj, s);
+  }
   if (!c->polar && logits_mfma_eligible(c))
     return launch_logits_mfma_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
