@@ -284,10 +284,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
 // chunk weights then go through LDS.  (Contexts over 128 chunks load the
 // values of the further chunks in more rounds.)
 // ctx_lens (paged caches, else nullptr): sequence b uses its first
-// ceil(ctx_lens[b] / 1024) chunks; the decode kernel did not write the rest.
+// ceil(ctx_lens[b] / chunk) chunks; the decode kernel did not write the rest.
 __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevParams PV, const float* __restrict__ part,
                                                                          int Hq, int nkv, int n_chunks_grid,
                                                                          const int32_t* __restrict__ ctx_lens,
+                                                                         int chunk,
                                                                          const float* __restrict__ S,
                                                                          const float* __restrict__ Dsign, void* out,
                                                                          int out_bf16) {
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int bk = b * nkv + h / G, g = h % G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid & 255, qtr = tid >> 8;
-  const int n_chunks = ctx_lens ? min(n_chunks_grid, (max(ctx_lens[b], 0) + 1023) / 1024) : n_chunks_grid;
+  const int n_chunks = ctx_lens ? min(n_chunks_grid, (max(ctx_lens[b], 0) + chunk - 1) / chunk) : n_chunks_grid;
   const int rec = 2 + 2 * d;
   const float* base = part + (static_cast<int64_t>(bk) * n_chunks_grid * G + g) * rec;
   // unsigned 32-bit offsets from the block's base: the loads take the scalar base plus one offset register
@@ -469,7 +470,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   }
   if (cv->prm.d == 128 && cv->prm.m == 128) {
     hipLaunchKernelGGL(decode_combine128_kernel, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part,
-                       n_q_heads, n_kv_heads, n_chunks, pm ? pm->ctx_lens : nullptr, cv->dS, cv->dD, out,
+                       n_q_heads, n_kv_heads, n_chunks, pm ? pm->ctx_lens : nullptr, CH, cv->dS, cv->dD, out,
                        out_dt == TQ_BF16 ? 1 : 0);
     return hipGetLastError();
   }
