@@ -57,6 +57,17 @@
 #ifndef TQ_H_
 #define TQ_H_
 
+/* Environment switches (read at each call; for comparisons and tests, not
+ * needed in normal use).  Each forces the general VALU kernel of one step, or
+ * the two-kernel form, instead of the matrix-core or fused one:
+ *   TQ_LOGITS_KERNEL=valu   logits (any head_dim)
+ *   TQ_LOGITS_FUSED=0       logits: query-prep launch + logits launch
+ *   TQ_DECODE_KERNEL=valu   decode attention (contiguous caches only)
+ *   TQ_ENCODE_KERNEL=split  encode: rotate/quantize, then the projection
+ *   TQ_SPROJ_KERNEL=valu    encode's QJL projection on the fp32 VALU
+ *   TQ_SEARCH_KERNEL=valu   search scores
+ *   TQ_LOG=1                one line per call on stderr. */
+
 #include <stddef.h>
 #include <stdint.h>
 
