@@ -36,7 +36,7 @@ __all__ = [
     "sylvester_hadamard", "paley_hadamard_12", "hadamard", "rotation_matrix",
     "sphere_coordinate_density", "sphere_coordinate_cdf",
     "sphere_coordinate_first_moment", "lloyd_max", "walsh_plane_coefficients",
-    "Codec", "make_codec", "qjl_constant",
+    "Codec", "make_codec", "make_mse_codec", "qjl_constant",
     "pack_planes", "unpack_planes", "pack_bits", "unpack_bits",
     "encode", "encode_given_codes", "dequantize",
     "prepare_query", "score", "attn_logits",
@@ -273,10 +273,11 @@ class Codec:
     centroids: np.ndarray   # (2^b,) fp64 ascending
     bounds: np.ndarray      # (2^b - 1,) fp64
     iters: int
+    qjl: bool = True        # False: first stage only (see make_mse_codec)
 
     @property
     def b(self) -> int:
-        return self.bits - 1
+        return self.bits - 1 if self.qjl else self.bits
 
     @property
     def c32(self) -> np.ndarray:
@@ -296,7 +297,7 @@ class Codec:
 
     @property
     def record_bytes(self) -> int:
-        return 4 * (self.code_words + self.sign_words) + 8
+        return 4 * (self.code_words + self.sign_words) + (8 if self.qjl else 4)
 
 
 def make_codec(d: int, bits: int, m: int | None = None, seed: int = 1234) -> Codec:
@@ -307,6 +308,26 @@ def make_codec(d: int, bits: int, m: int | None = None, seed: int = 1234) -> Cod
     return Codec(d=d, bits=bits, m=m, seed=seed, D=rademacher_signs(d, seed),
                  R=rotation_matrix(d, seed), S=gaussian_matrix(m, d, seed),
                  centroids=c, bounds=t, iters=it)
+
+
+# --------------------------------------------------------------------------
+# MSE-only codec for values.  TurboQuant+ 深度解析 第五部分 reports that the
+# value cache tolerates much coarser compression than the key cache (keys route
+# attention, values only carry what is read).  Reading: a value codec may drop
+# the QJL stage and give all `bits` to the first stage's Lloyd-Max code (the
+# two-stage split of 深度拆解 第二部分 exists to make inner products with a
+# query unbiased, which the value path does not need).  The record is the
+# codes and ν only, and v̂ = ν Rᵀ c[idx], the reconstruction of least mean
+# squared error for the codebook.  Such a codec has no unbiased score, so it
+# never serves as a key codec.
+# --------------------------------------------------------------------------
+def make_mse_codec(d: int, bits: int, seed: int = 1234) -> Codec:
+    if bits < 1:
+        raise ValueError("bits must be >= 1")
+    c, t, it = lloyd_max(d, bits)
+    return Codec(d=d, bits=bits, m=0, seed=seed, D=rademacher_signs(d, seed),
+                 R=rotation_matrix(d, seed), S=np.zeros((0, d), np.float32),
+                 centroids=c, bounds=t, iters=it, qjl=False)
 
 
 # --------------------------------------------------------------------------
@@ -403,17 +424,22 @@ def encode_given_codes(codec: Codec, x: np.ndarray, idx: np.ndarray) -> dict:
 
 def _unpack_record(codec: Codec, packed: dict):
     idx = unpack_planes(np.asarray(packed["codes"]), codec.b, codec.d)
-    tau = 2 * unpack_bits(np.asarray(packed["signs"]), codec.m) - 1
     nu = np.asarray(packed["norm"], dtype=np.float32).astype(np.float64)
+    if not codec.qjl:  # MSE-only records hold no signs and no γ
+        n = idx.shape[0]
+        return idx, np.zeros((n, 0)), nu, np.zeros(n)
+    tau = 2 * unpack_bits(np.asarray(packed["signs"]), codec.m) - 1
     gamma = np.asarray(packed["rnorm"], dtype=np.float32).astype(np.float64)
     return idx, tau.astype(np.float64), nu, gamma
 
 
 def dequantize(codec: Codec, packed: dict) -> np.ndarray:
     """v̂ = ν Rᵀ (c[idx] + sqrt(pi/2)/m · γ · Sᵀ τ): the unbiased reconstruction
-    (E_S[Sᵀ sign(S r)] = sqrt(2/pi) m r/||r||)."""
+    (E_S[Sᵀ sign(S r)] = sqrt(2/pi) m r/||r||); ν Rᵀ c[idx] for an MSE-only codec."""
     idx, tau, nu, gamma = _unpack_record(codec, packed)
     chat = codec.c32.astype(np.float64)[idx]
+    if not codec.qjl:
+        return nu[:, None] * (chat @ codec.R)
     corr = qjl_constant(codec.m) * gamma[:, None] * (tau @ codec.S.astype(np.float64))
     return nu[:, None] * ((chat + corr) @ codec.R)
 
@@ -433,6 +459,8 @@ def prepare_query(codec: Codec, q: np.ndarray):
 
 def score(codec: Codec, q: np.ndarray, packed: dict) -> np.ndarray:
     """Logits of every query row against every packed key: (n_q, n_keys) fp64."""
+    if not codec.qjl:
+        raise ValueError("an MSE-only codec has no unbiased score; keys take the two-stage codec")
     qr, p = prepare_query(codec, np.atleast_2d(q))
     idx, tau, nu, gamma = _unpack_record(codec, packed)
     chat = codec.c32.astype(np.float64)[idx]
@@ -498,7 +526,7 @@ def decode_attn_accumulated(codec_k: Codec, codec_v: Codec, q, k_packed, v_packe
     q = np.asarray(q, dtype=np.float64).reshape(batch, n_q_heads, codec_k.d)
     G = n_q_heads // n_kv_heads
     out = np.zeros((batch, n_q_heads, codec_v.d))
-    kv = qjl_constant(codec_v.m)
+    kv = qjl_constant(codec_v.m) if codec_v.qjl else 0.0
     S = codec_v.S.astype(np.float64)
     for bi in range(batch):
         for kh in range(n_kv_heads):
@@ -510,8 +538,10 @@ def decode_attn_accumulated(codec_k: Codec, codec_v: Codec, q, k_packed, v_packe
             lg = score(codec_k, q[bi, hs], keys)
             e, l = _softmax_weights(lg, scale)
             M = (e * nu[None, :]) @ chat
-            J = (e * (nu * gamma)[None, :]) @ tau
-            o_rot = (M + kv * (J @ S)) / l
+            o_rot = M / l
+            if codec_v.qjl:
+                J = (e * (nu * gamma)[None, :]) @ tau
+                o_rot = o_rot + kv * (J @ S) / l
             out[bi, hs] = o_rot @ codec_v.R
     return out
 

@@ -425,6 +425,71 @@ def test_decode_attention_one_hot_and_uniform(codec3, codec4):
     assert np.allclose(out[0, 0], vhat.mean(axis=0), rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------- MSE-only value codec
+@pytest.mark.parametrize("bits", [2, 3])
+def test_mse_codec_record_and_codebook(bits):
+    # all bits go to the Lloyd-Max code: d*bits/8 code bytes + 4 bytes of ν,
+    # and the codebook is the b = bits Lloyd-Max quantizer (Appendix A values
+    # at d = 128, scaled by sqrt(d))
+    cd = O.make_mse_codec(128, bits)
+    assert cd.b == bits and cd.m == 0 and cd.sign_words == 0
+    assert cd.record_bytes == 128 * bits // 8 + 4
+    expect = {2: [0.452453, 1.505193], 3: [0.244425, 0.753330, 1.336599, 2.131471]}[bits]
+    assert np.allclose(cd.centroids[1 << (bits - 1):] * math.sqrt(128), expect, atol=2e-6)
+    with pytest.raises(ValueError):
+        O.score(cd, np.ones((1, 128)), O.encode(cd, np.ones((1, 128))))
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_mse_codec_distortion_equals_codebook_distortion(bits):
+    # v̂ = ν Rᵀ c[idx]: for Gaussian x the mean of ||x/ν - v̂/ν||² is the
+    # codebook's distortion d·E(X - Q(X))² (sphere law), with no QJL term
+    cd = O.make_mse_codec(128, bits)
+    x = np.random.default_rng(31).standard_normal((50_000, 128))
+    enc = O.encode(cd, x)
+    assert enc["signs"].shape == (x.shape[0], 0)
+    vhat = O.dequantize(cd, enc)
+    nu = np.linalg.norm(x, axis=1, keepdims=True)
+    err = np.sum((x / nu - vhat / nu) ** 2, axis=1)
+    D = _distortion_by_quadrature(cd.c32.astype(np.float64), cd.t32.astype(np.float64), 128)
+    assert abs(err.mean() - D) < 3.5 * err.std() / math.sqrt(err.size)
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_mse_dequantize_basis_vector_closed_form(bits):
+    # x = ν e_k: every |y_j| = 1/sqrt(d), so c[idx] = sqrt(d) c_level · y and
+    # v̂ = ν Rᵀ c[idx] = ν sqrt(d) c_level e_k exactly (a transposed R fails this)
+    cd = O.make_mse_codec(128, bits)
+    x = np.zeros((1, 128)); x[0, 41] = 2.5
+    vhat = O.dequantize(cd, O.encode(cd, x))[0]
+    t = cd.t32.astype(np.float64) * math.sqrt(128)
+    level = int(np.sum(t < 1.0))
+    expect = np.zeros(128); expect[41] = 2.5 * math.sqrt(128) * float(cd.c32[level])
+    assert np.allclose(vhat, expect, rtol=0, atol=1e-12)
+    assert float(cd.c32[level]) * math.sqrt(128) == pytest.approx({2: 1.505193, 3: 0.753330}[bits], abs=2e-6)
+
+
+def test_decode_attention_mse_values(codec3):
+    rng = np.random.default_rng(12)
+    B, Hq, Hk, T = 1, 4, 2, 200
+    cv = O.make_mse_codec(128, 3)
+    K = O.encode(codec3, rng.standard_normal((B * Hk * T, 128)))
+    V = O.encode(cv, rng.standard_normal((B * Hk * T, 128)))
+    q = rng.standard_normal((B, Hq, 128))
+    a = O.decode_attn_materialized(codec3, cv, q, K, V, B, Hq, Hk, T, 1 / math.sqrt(128))
+    b = O.decode_attn_accumulated(codec3, cv, q, K, V, B, Hq, Hk, T, 1 / math.sqrt(128))
+    assert np.max(np.abs(a - b)) <= 1e-12 * np.max(np.abs(a))
+    # one dominant key returns its v̂ = ν Rᵀ c[idx]
+    vhat = O.dequantize(cv, V)
+    lg = O.score(codec3, q[0, :1], {k: K[k][:T] for k in ("codes", "signs", "norm", "rnorm")})[0]
+    j = int(np.argmax(lg))
+    K1 = {k: np.array(K[k][:T]) for k in ("codes", "signs", "norm", "rnorm")}
+    K1["norm"][j] *= 1e4
+    V1 = {k: np.array(V[k][:T]) for k in ("codes", "signs", "norm", "rnorm")}
+    out = O.decode_attn_accumulated(codec3, cv, q[:, :1], K1, V1, 1, 1, 1, T, 1.0)
+    assert np.allclose(out[0, 0], vhat[j], rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- O6b Sparse V
 def _sparse_case(codec3, codec4, T, Hq, qscale, seed):
     rng = np.random.default_rng(seed)
