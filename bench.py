@@ -371,6 +371,37 @@ def polar_stage(B, I, dev, k, q, ctx, d):
                                      "note": "VALU-bound: y-hat rebuilt per key from the angle codes"}}
 
 
+def mse_v_stage(B, codec3, dev, g, dsets, qd, out, ctx, d):
+    """Decode attention on the long-context shape with 3-bit K and an MSE-only
+    V codec (3 and 2 code bits, no QJL stage; records of 52 and 36 bytes), and
+    the encode of that V cache."""
+    import torch
+    hkv, hq, scale = 8, 32, 1 / math.sqrt(d)
+    v = torch.randn((hkv * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    res = {}
+    for bits in (3, 2):
+        cv = B.tq_codec_create_mse(d, bits)
+        vp = B.alloc_packed(cv, hkv * ctx, dev)
+        ms_e = _time(lambda: B.tq_encode_kv(cv, v, k_out=vp), 10, graph=True)
+        sets = [(kk, vp if i == 0 else B.Packed(vp.codes.clone(), None, vp.norm.clone(), None))
+                for i, (kk, _) in enumerate(dsets)]
+        ws = torch.empty(B.tq_decode_attn_workspace(codec3, cv, 1, hq, hkv, ctx), dtype=torch.uint8, device=dev)
+        it = iter(range(10 ** 9))
+
+        def step():
+            kk, vv = sets[next(it) % len(sets)]
+            B.tq_decode_attn(codec3, cv, qd, kk, vv, ctx, hkv, scale, out=out, ws=ws)
+        ms = _time(step, 30, graph=True)
+        name = f"decode_attn_c4_mse_v{bits}"
+        res[name] = {"ms": ms, "buffer_sets": len(sets), "v_record_bytes": cv.record_bytes,
+                     **_hbm(ms, hkv * ctx * (codec3.record_bytes + cv.record_bytes) + 2 * hq * d * 2)}
+        res[f"encode_mse_v{bits}_c4"] = {"ms": ms_e, "vectors_per_s": hkv * ctx / (ms_e * 1e-3)}
+        print(f"[bench] {name} {ms * 1e3:.1f} us (V encode {ms_e * 1e3:.1f} us)", file=sys.stderr, flush=True)
+        del sets, vp, ws, cv
+    del v
+    return res
+
+
 def paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d):
     """Paged cache on the long-context decode shape.  (1) The same caches
     copied into 256-position pages in shuffled order, read through the page
@@ -556,6 +587,7 @@ def time_stages(B, I, codec3, dev, args):
     if not args.no_stage_sparse_v:
         res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d))
     res.update(paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d))
+    res.update(mse_v_stage(B, codec3, dev, g, dsets, qd, out, ctx, d))
     del kp, vp, dsets, ws, k_c4
     # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
     bsz, hkv, ctx, nq = 16, 8, 8192, 16

@@ -91,7 +91,9 @@ typedef enum {
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype_t;
 
-/* Device pointers to one packed cache or database; all arrays have n rows. */
+/* Device pointers to one packed cache or database; all arrays have n rows.
+ * Records of an MSE-only codec (tq_codec_create_mse) have no signs and no γ:
+ * signs and rnorm are ignored and may be NULL. */
 typedef struct {
   uint32_t* codes; /* [n][code_words], 4-byte aligned */
   uint32_t* signs; /* [n][sign_words], 4-byte aligned */
@@ -101,9 +103,9 @@ typedef struct {
 
 typedef struct {
   int32_t head_dim;     /* d */
-  int32_t bits;         /* B = b + 1 */
+  int32_t bits;         /* B = b + 1 (an MSE-only codec: B = b) */
   int32_t mse_bits;     /* b */
-  int32_t qjl_dim;      /* m */
+  int32_t qjl_dim;      /* m (0: MSE-only codec, no QJL stage) */
   int32_t code_words;   /* b*d/32 */
   int32_t sign_words;   /* m/32 */
   int32_t record_bytes; /* 4*(code_words+sign_words) + 8 */
@@ -157,6 +159,17 @@ tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uin
  * TQ_ERROR_NOT_SUPPORTED for them. */
 tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                   tq_codec_t* out);
+/* An MSE-only value codec: the same rotation and per-coordinate Lloyd-Max
+ * stage with all `bits` (2 or 3) given to the code, and no QJL stage
+ * (TurboQuant+ 深度解析 第五部分: the value cache tolerates coarser
+ * compression than the key cache, which routes attention).  A record is the
+ * codes (d*bits/8 bytes) and ν; the value reconstruction is v̂ = ν Rᵀ c[idx]
+ * (least mean squared error; biased for inner products).  Accepted by
+ * tq_encode_kv, tq_encode_append_paged and as the V codec (cv) of the decode
+ * attention calls; tq_attn_logits, its split form, tq_search_topk and the K
+ * codec role return TQ_ERROR_NOT_SUPPORTED.  head_dim as tq_codec_create;
+ * tq_codec_info reports qjl_dim = 0 and sign_words = 0. */
+tq_status_t tq_codec_create_mse(int32_t head_dim, int32_t bits, uint64_t seed, tq_codec_t* out);
 /* Host only (no GPU needed): level l's (1..7) angle codebook of the polar
  * stage for head_dim 128 and the given bits: centroids[2^b] and
  * bounds[2^b - 1], fp64, ascending, and the Lloyd-Max iterations (0 for the
@@ -223,7 +236,9 @@ tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, size_t prep_b
  * (TurboQuant+ 深度解析 第五部分: K and V are compressed the same way).  V is
  * accumulated in the codec domain and mapped back once per head.
  *   ck, cv : codecs of K and V (they may be the same handle; their bits may
- *            differ; head_dim must match).
+ *            differ; head_dim must match).  cv may be an MSE-only codec
+ *            (tq_codec_create_mse): then v̂ = ν Rᵀ c[idx] and v.signs,
+ *            v.rnorm are not read.
  *   q      : device [batch][n_q_heads][d], dtype q_dt.
  *   k, v   : packed rows [batch][n_kv_heads][ctx_len].
  *   out    : device [batch][n_q_heads][d], dtype out_dt (TQ_F32 or TQ_BF16,

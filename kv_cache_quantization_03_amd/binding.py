@@ -53,6 +53,7 @@ def _load():
         "tq_codec_destroy": (C.c_int, [vp]),
         "tq_codec_info": (C.c_int, [vp, C.POINTER(tq_codec_info_t)]),
         "tq_codec_create_polar": (C.c_int, [i32, i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
+        "tq_codec_create_mse": (C.c_int, [i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
         "tq_polar_book_host": (C.c_int, [i32, i32, i32, C.POINTER(C.c_double), C.POINTER(C.c_double),
                                          C.POINTER(i32)]),
         "tq_encode_workspace": (sz, [vp, i64]),
@@ -86,7 +87,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_build_host", "tq_codec_create",
-            "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
+            "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_codec_create_mse", "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
             "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
@@ -151,6 +152,7 @@ class Codec:
         self.centroids = np.array(info.centroids[:1 << self.b])
         self.bounds = np.array(info.bounds[:(1 << self.b) - 1])
         self.polar = info.stage1 == 1
+        self.qjl = info.qjl_dim > 0  # False: MSE-only value codec (records: codes and ν)
 
     def __del__(self):
         if getattr(self, "handle", None) and lib is not None:
@@ -174,6 +176,14 @@ def tq_codec_create_polar(head_dim: int, bits: int, qjl_dim: int = 0, seed: int 
     return Codec(h, info)
 
 
+def tq_codec_create_mse(head_dim: int, bits: int, seed: int = 1234) -> Codec:
+    h = C.c_void_p()
+    _check(lib.tq_codec_create_mse(head_dim, bits, seed, C.byref(h)), "tq_codec_create_mse")
+    info = tq_codec_info_t()
+    _check(lib.tq_codec_info(h, C.byref(info)), "tq_codec_info")
+    return Codec(h, info)
+
+
 def tq_polar_book_host(head_dim: int, bits: int, level: int):
     """(centroids, bounds, iterations) of one level's angle codebook, fp64 (host only)."""
     n = 1 << (bits - 1)
@@ -188,32 +198,38 @@ def tq_polar_book_host(head_dim: int, bits: int, level: int):
 @dataclass
 class Packed:
     codes: object   # torch uint32-compatible int32 [n][code_words]
-    signs: object   # [n][sign_words]
+    signs: object   # [n][sign_words]; None for an MSE-only codec
     norm: object    # float32 [n]
-    rnorm: object   # float32 [n]
+    rnorm: object   # float32 [n]; None for an MSE-only codec
 
     @property
     def n(self) -> int:
         return self.norm.shape[0]
 
     def c(self) -> tq_packed_t:
-        return tq_packed_t(self.codes.data_ptr(), self.signs.data_ptr(), self.norm.data_ptr(),
-                           self.rnorm.data_ptr())
+        return tq_packed_t(self.codes.data_ptr(), None if self.signs is None else self.signs.data_ptr(),
+                           self.norm.data_ptr(), None if self.rnorm is None else self.rnorm.data_ptr())
 
     def rows(self, lo: int, hi: int) -> "Packed":
-        return Packed(self.codes[lo:hi], self.signs[lo:hi], self.norm[lo:hi], self.rnorm[lo:hi])
+        return Packed(self.codes[lo:hi], None if self.signs is None else self.signs[lo:hi], self.norm[lo:hi],
+                      None if self.rnorm is None else self.rnorm[lo:hi])
 
     def numpy(self) -> dict:
-        return {"codes": self.codes.cpu().numpy().view(np.uint32), "signs": self.signs.cpu().numpy().view(np.uint32),
-                "norm": self.norm.cpu().numpy(), "rnorm": self.rnorm.cpu().numpy()}
+        n = self.n
+        return {"codes": self.codes.cpu().numpy().view(np.uint32),
+                "signs": (np.zeros((n, 0), np.uint32) if self.signs is None
+                          else self.signs.cpu().numpy().view(np.uint32)),
+                "norm": self.norm.cpu().numpy(),
+                "rnorm": np.zeros(n, np.float32) if self.rnorm is None else self.rnorm.cpu().numpy()}
 
 
 def alloc_packed(codec: Codec, n: int, device="cuda") -> Packed:
     torch = _torch()
+    q = getattr(codec, "qjl", True)
     return Packed(torch.empty((n, codec.code_words), dtype=torch.int32, device=device),
-                  torch.empty((n, codec.sign_words), dtype=torch.int32, device=device),
+                  torch.empty((n, codec.sign_words), dtype=torch.int32, device=device) if q else None,
                   torch.empty(n, dtype=torch.float32, device=device),
-                  torch.empty(n, dtype=torch.float32, device=device))
+                  torch.empty(n, dtype=torch.float32, device=device) if q else None)
 
 
 def packed_from_numpy(rec: dict, device="cuda") -> Packed:

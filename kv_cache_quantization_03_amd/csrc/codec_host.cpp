@@ -224,6 +224,21 @@ tq_status_t build_polar_tables(int d, int bits, int m, uint64_t seed, HostTables
   return TQ_SUCCESS;
 }
 
+tq_status_t build_mse_tables(int d, int bits, uint64_t seed, HostTables* out) {
+  if (bits < 2 || bits > 3) {
+    set_error("an MSE-only codec takes bits 2 or 3 (all bits to the Lloyd-Max code)");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  // the two-stage tables of bits + 1 carry the b = bits codebook and D; S is dropped
+  tq_status_t st = build_host_tables(d, bits + 1, 0, seed, out);
+  if (st != TQ_SUCCESS) return st;
+  out->bits = bits;
+  out->m = 0;
+  out->S.clear();
+  out->S.shrink_to_fit();
+  return TQ_SUCCESS;
+}
+
 bool supported_dim(int d) {
   return d == 64 || d == 128 || d == 256 || d == 512 || d == 1024 || d == 1536;
 }
@@ -366,8 +381,11 @@ void apply_hadamard_transposed(double* v, int d) {
 }  // namespace
 
 namespace {
-tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed, bool polar,
+enum Stage { kTwoStage, kPolar, kMseOnly };
+
+tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed, Stage stage,
                          tq_codec_t* out) {
+  const bool polar = stage == kPolar;
   tq::clear_error();
   if (!out) {
     set_error("out is NULL");
@@ -379,8 +397,9 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
     set_error("host allocation failed");
     return TQ_ERROR_OUT_OF_MEMORY;
   }
-  tq_status_t st = polar ? tq::build_polar_tables(head_dim, bits, qjl_dim, seed, &c->host)
-                         : tq::build_host_tables(head_dim, bits, qjl_dim, seed, &c->host);
+  tq_status_t st = polar               ? tq::build_polar_tables(head_dim, bits, qjl_dim, seed, &c->host)
+                   : stage == kMseOnly ? tq::build_mse_tables(head_dim, bits, seed, &c->host)
+                                       : tq::build_host_tables(head_dim, bits, qjl_dim, seed, &c->host);
   if (st != TQ_SUCCESS) {
     delete c;
     return st;
@@ -405,7 +424,8 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
   for (size_t k = 0; k < h.bounds.size(); ++k) p.bound[k] = static_cast<float>(h.bounds[k]);
   for (size_t k = h.bounds.size(); k < 8; ++k) p.bound[k] = INFINITY;
   plane_expansion(h.centroids, h.b, p.plane_coef, &p.plane_bias, &p.n_planes);
-  p.qjl_kappa = static_cast<float>(std::sqrt(M_PI / 2.0) / h.m);
+  c->qjl = h.m > 0;
+  p.qjl_kappa = c->qjl ? static_cast<float>(std::sqrt(M_PI / 2.0) / h.m) : 0.f;
   p.inv_sqrt_d = static_cast<float>(1.0 / std::sqrt(static_cast<double>(h.d)));
   p.d = h.d;
   p.b = h.b;
@@ -431,6 +451,7 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
   c->dS = static_cast<float*>(c->dev_block);
   c->dMt = c->dS + nS;
   c->dD = c->dMt + nS;
+  if (nS == 0) c->dS = c->dMt = nullptr;  // MSE-only: no projection
   c->dS16 = with16 ? reinterpret_cast<_Float16*>(c->dD + h.d) : nullptr;
   // M = S R, row by row in fp64: M[i][j] = (Hᵀ S[i,:])[j] D[j] / sqrt(d); stored transposed.
   std::vector<float> Mt(nS);
@@ -455,8 +476,9 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
     }
     p.mrow_bound = std::nextafter(static_cast<float>(mx * (1.0 + 1e-6)), INFINITY);
   }
-  e = hipMemcpy(c->dS, h.S.data(), nS * sizeof(float), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(c->dMt, Mt.data(), nS * sizeof(float), hipMemcpyHostToDevice);
+  e = hipSuccess;
+  if (nS > 0) e = hipMemcpy(c->dS, h.S.data(), nS * sizeof(float), hipMemcpyHostToDevice);
+  if (e == hipSuccess && nS > 0) e = hipMemcpy(c->dMt, Mt.data(), nS * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->dD, h.D.data(), h.d * sizeof(float), hipMemcpyHostToDevice);
   if (e == hipSuccess && with16) {
     // S = hi + lo: hi = fp16(S) (round to nearest even), lo = fp16(S - hi)
@@ -483,12 +505,16 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
 
 extern "C" tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                        tq_codec_t* out) {
-  return codec_create(head_dim, bits, qjl_dim, seed, false, out);
+  return codec_create(head_dim, bits, qjl_dim, seed, kTwoStage, out);
+}
+
+extern "C" tq_status_t tq_codec_create_mse(int32_t head_dim, int32_t bits, uint64_t seed, tq_codec_t* out) {
+  return codec_create(head_dim, bits, 0, seed, kMseOnly, out);
 }
 
 extern "C" tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                              tq_codec_t* out) {
-  return codec_create(head_dim, bits, qjl_dim, seed, true, out);
+  return codec_create(head_dim, bits, qjl_dim, seed, kPolar, out);
 }
 
 extern "C" tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
@@ -543,7 +569,7 @@ extern "C" tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info) {
   info->qjl_dim = h.m;
   info->code_words = c->prm.code_words;
   info->sign_words = c->prm.sign_words;
-  info->record_bytes = 4 * (c->prm.code_words + c->prm.sign_words) + 8;
+  info->record_bytes = 4 * (c->prm.code_words + c->prm.sign_words) + (c->qjl ? 8 : 4);
   info->lloyd_max_iterations = h.iterations;
   info->stage1 = c->polar ? 1 : 0;
   info->seed = h.seed;

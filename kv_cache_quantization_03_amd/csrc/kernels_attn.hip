@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
     }
     const int64_t row = static_cast<int64_t>(bk) * ctx + t0 + tl;
     const float nu = V.norm[row];
-    const float scl = is_m ? nu : nu * V.rnorm[row];
+    const float scl = is_m ? nu : (per > 0 ? nu * V.rnorm[row] : 0.f);  // an MSE-only V codec has no γ (mv = 0)
     for (int u = 0; u < per; ++u) {
       const int j = lt + u * 128;
       float val;
@@ -211,8 +211,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
   if (nv <= 2 * 128 && d == 128) {
     const int j = tid & 255, qtr = tid >> 8;
     float a = 0.f;
+    if (j < nv) {  // records hold nv = d + m values (m = 0 for an MSE-only V codec)
 #pragma unroll 8
-    for (int c = qtr; c < n_chunks; c += 4) a = fmaf(wsh[c], base[c * cstride + 2 + j], a);
+      for (int c = qtr; c < n_chunks; c += 4) a = fmaf(wsh[c], base[c * cstride + 2 + j], a);
+    }
     acc_sh[qtr][j] = a;
     __syncthreads();
     if (tid < nv) {
@@ -282,9 +284,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
 // its chunk's (max, Σw), its value j = t % 256 (M below 128, J above) of every
 // fourth chunk, and its slice of S for Sᵀ J before using any of them; the
 // chunk weights then go through LDS.  (Contexts over 128 chunks load the
-// values of the further chunks in more rounds.)
+// values of the further chunks in more rounds.)  With an MSE-only V codec
+// (VQ = false) the records hold M only: value j = t % 128 of every eighth
+// chunk, and no Sᵀ J.
 // ctx_lens (paged caches, else nullptr): sequence b uses its first
 // ceil(ctx_lens[b] / chunk) chunks; the decode kernel did not write the rest.
+template <bool VQ>
 __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevParams PV, const float* __restrict__ part,
                                                                          int Hq, int nkv, int n_chunks_grid,
                                                                          const int32_t* __restrict__ ctx_lens,
@@ -292,18 +297,21 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
                                                                          const float* __restrict__ S,
                                                                          const float* __restrict__ Dsign, void* out,
                                                                          int out_bf16) {
-  constexpr int d = 128, U = 32, NW = kCombThreads / kWave;
+  constexpr int d = 128, NW = kCombThreads / kWave;
+  constexpr int NV = VQ ? 2 * d : d;    // values per record
+  constexpr int NS = kCombThreads / NV;  // chunk slices (4 or 8)
+  constexpr int U = 128 / NS;            // chunks per thread in the first round
   __shared__ float wsh[kCombThreads];  // chunk weights exp(m_c - max)
   __shared__ float red[NW], red2[NW];
-  __shared__ float qa[4][256];
+  __shared__ float qa[NS][NV];
   __shared__ float osh[d], Jsh[d];
   __shared__ float sj[8][d];
   const int G = Hq / nkv;
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int bk = b * nkv + h / G, g = h % G;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid & 255, qtr = tid >> 8;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid % NV, qtr = tid / NV;
   const int n_chunks = ctx_lens ? min(n_chunks_grid, (max(ctx_lens[b], 0) + chunk - 1) / chunk) : n_chunks_grid;
-  const int rec = 2 + 2 * d;
+  const int rec = 2 + NV;
   const float* base = part + (static_cast<int64_t>(bk) * n_chunks_grid * G + g) * rec;
   // unsigned 32-bit offsets from the block's base: the loads take the scalar base plus one offset register
   const unsigned cstride = static_cast<unsigned>(G * rec);
@@ -314,12 +322,14 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   const float l_own = has_c ? own[1] : 0.f;
   const int jj = tid & 127, pp = tid >> 7;  // o'_jj += Σ_{i in [16pp, 16pp+16)} S[i][jj] J_i
   float sv[16];
+  if constexpr (VQ) {
 #pragma unroll
-  for (int u = 0; u < 16; ++u) sv[u] = S[static_cast<unsigned>((pp * 16 + u) * d + jj)];
+    for (int u = 0; u < 16; ++u) sv[u] = S[static_cast<unsigned>((pp * 16 + u) * d + jj)];
+  }
   float vc[U];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    vc[u] = base[static_cast<unsigned>(max(0, min(qtr + 4 * u, n_chunks - 1))) * cstride + 2u + j];
+    vc[u] = base[static_cast<unsigned>(max(0, min(qtr + NS * u, n_chunks - 1))) * cstride + 2u + j];
   // ---- global max and chunk weights
   float m = wave_max(m_own);
   if (lane == 0) red[wv] = m;
@@ -340,34 +350,36 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int c = qtr + 4 * u;
+    const int c = qtr + NS * u;
     if (c < n_chunks) acc = fmaf(wsh[c], vc[u], acc);
   }
-  for (int c0 = qtr + 4 * U; c0 < n_chunks; c0 += 4 * U) {  // contexts over 128 chunks
+  for (int c0 = qtr + NS * U; c0 < n_chunks; c0 += NS * U) {  // contexts over 128 chunks
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      vc[u] = base[static_cast<unsigned>(max(0, min(c0 + 4 * u, n_chunks - 1))) * cstride + 2u + j];
+      vc[u] = base[static_cast<unsigned>(max(0, min(c0 + NS * u, n_chunks - 1))) * cstride + 2u + j];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + 4 * u;
+      const int c = c0 + NS * u;
       if (c < n_chunks) acc = fmaf(wsh[c], vc[u], acc);
     }
   }
   qa[qtr][j] = acc;
   __syncthreads();
-  if (tid < 256) {
-    const float a = (qa[0][tid] + qa[1][tid]) + (qa[2][tid] + qa[3][tid]);
+  if (tid < NV) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) a += qa[q][tid];
     if (tid < d) osh[tid] = a;
     else Jsh[tid - d] = a;
   }
   __syncthreads();
-  {
+  if constexpr (VQ) {
     float a = 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) a = fmaf(sv[u], Jsh[pp * 16 + u], a);
     sj[pp][jj] = a;
+    __syncthreads();
   }
-  __syncthreads();
   if (tid < kWave) {
     const float inv_l = ltot > 0.f ? 1.0f / ltot : 0.f;  // an empty context gives 0
     float v[2];
@@ -375,8 +387,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
     for (int e = 0; e < 2; ++e) {
       const int jo = e * kWave + tid;
       float t = 0.f;
+      if constexpr (VQ) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) t += sj[q][jo];
+        for (int q = 0; q < 8; ++q) t += sj[q][jo];
+      }
       v[e] = (osh[jo] + PV.qjl_kappa * t) * inv_l;
     }
     hadamard_wave<2, true>(v, tid);
@@ -468,10 +482,10 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
                        part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (cv->prm.d == 128 && cv->prm.m == 128) {
-    hipLaunchKernelGGL(decode_combine128_kernel, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part,
-                       n_q_heads, n_kv_heads, n_chunks, pm ? pm->ctx_lens : nullptr, CH, cv->dS, cv->dD, out,
-                       out_dt == TQ_BF16 ? 1 : 0);
+  if (cv->prm.d == 128 && (cv->prm.m == 128 || !cv->qjl)) {
+    auto kern = cv->qjl ? decode_combine128_kernel<true> : decode_combine128_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part, n_q_heads, n_kv_heads,
+                       n_chunks, pm ? pm->ctx_lens : nullptr, CH, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);
     return hipGetLastError();
   }
   auto run = [&]<int E>() -> hipError_t {

@@ -16,6 +16,8 @@
 // whose weight normalised within the chunk, exp(s - m_c) / l_c, is below the
 // gate, and a wave whose 128 keys are all dropped for every head of its group
 // loads no V record and runs none of step 4.  The normaliser keeps every key.
+// With an MSE-only V codec (VQ = false) the V records hold codes and ν only:
+// step 4 has no J, and the partials are (max, Σw, M).
 // Pages: 「谷歌 TurboQuant 深度拆解」 第二部分 (the unbiased estimator);
 // 「TurboQuant+ 深度解析」 第五部分 (V compressed like K) and 第六部分 (V
 // dequantization dominates long-context decode).
@@ -78,7 +80,7 @@ __device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (r
 
 }  // namespace
 
-template <int NPK, int NPV, bool GATE, bool PAGED>
+template <int NPK, int NPV, bool GATE, bool PAGED, bool VQ>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     const uint8_t* __restrict__ prep, DevParams PK, DevParams PV, PageMap pm, int Hq, int nkv, int ctx_max,
     int n_chunks, float scale, float gate, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
@@ -90,6 +92,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   constexpr int NT = kDecWaves * 64, NKB = LK::NKB, NBV = LV::NB;
   constexpr int KSTAGE = kKeysPerWave * (LK::CS + LK::SS);
   constexpr int SCR = KSTAGE > 1024 ? KSTAGE : 1024;  // words of per-wave scratch
+  constexpr int NTY = VQ ? 2 : 1;                      // V weight types: MSE (and QJL)
+  constexpr int REC = 2 + (VQ ? 2 : 1) * kPrepD;       // floats per partial record
   __shared__ __attribute__((aligned(16))) uint32_t wsc[kDecWaves][SCR];
   __shared__ float hmax[kDecWaves][4];
   __shared__ int ubexp[kDecWaves][2][4][4];  // V weight block exponents [type][head][key block]
@@ -172,13 +176,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
       const int64_t row = row_of(key);
 #pragma unroll
       for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
-      vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+      if constexpr (VQ) vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int64_t row = row_of(min(kbase + 16 * t + kl, ctx - 1));
       vnu[t] = vn[row];
-      vga[t] = vr[row];
+      if constexpr (VQ) vga[t] = vr[row];
     }
   };
   if constexpr (!GATE) load_v();
@@ -242,15 +246,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     // LW[type][g][key] = the key's four digit bytes; ub = block exponents.
     uint32_t* LW = wsc[wv];
     {
-      float u[2][8];
+      float u[NTY][8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         u[0][t] = wt[t] * vnu[t];
-        u[1][t] = 2.f * u[0][t] * vga[t];
+        if constexpr (VQ) u[NTY - 1][t] = 2.f * u[0][t] * vga[t];
       }
-      int eb[2][4];
+      int eb[NTY][4];
 #pragma unroll
-      for (int ty = 0; ty < 2; ++ty) {
+      for (int ty = 0; ty < NTY; ++ty) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {  // block kb = keys 32kb..32kb+31 = tiles 2kb, 2kb+1
           const float m = row_max(fmaxf(u[ty][2 * kb], u[ty][2 * kb + 1]));
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
         const int r = (key & 31) >> 3;  // FP4 mask index of this key in the B operand
         const float inv_val = r == 0 ? 2.f : (r == 1 ? 1.f : (r == 2 ? 0.5f : -0.5f));
 #pragma unroll
-        for (int ty = 0; ty < 2; ++ty) {
+        for (int ty = 0; ty < NTY; ++ty) {
           const int e = eb[ty][t >> 1];
           const float V = fminf(rintf(ldexpf(u[ty][t], 15 - e)), 65535.f);  // 16-bit fixed point
           const float ut = ldexpf(V, e - 15);                                 // the value the digits carry
@@ -302,13 +306,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     // A operands: lane (row 4g'+l, group grp) holds digit l of keys 16grp..+15 and
     // 64+16grp..+15 (A byte order measured on gfx950); its E8M0 scale serves
     // row 4g'+l of key block grp: 2^(block exponent - 3 - 4l).
-    v8i av[2];
-    int sav[2];
+    v8i av[NTY];
+    int sav[NTY];
     {
       const int row = lane & 15, grp = lane >> 4, gq = row >> 2, l = row & 3;
       const uint32_t sel = static_cast<uint32_t>(l) | (static_cast<uint32_t>(4 + l) << 8) | 0x0C0C0000u;
 #pragma unroll
-      for (int ty = 0; ty < 2; ++ty) {
+      for (int ty = 0; ty < NTY; ++ty) {
         const uint32_t* src = LW + (ty * 4 + gq) * kDecKeysPerWave;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     for (int cb = 0; cb < 8; ++cb) par[cb] = 0u;
     const v4f zero = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p <= NBV; ++p) {  // stored planes, then the signs
+    for (int p = 0; p < NBV + (VQ ? 1 : 0); ++p) {  // stored planes, then the signs
       uint32_t tw[8];
 #pragma unroll
       for (int wb = 0; wb < 4; ++wb) {
@@ -346,8 +350,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
         v4f acc[4], accp[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          acc[c] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[1], fp4_operand(tw[4 * hb + c]), zero,
-                                       p < NBV ? sav[0] : sav[1]);
+          acc[c] = mfma_fp8_fp4_scaled(p < NBV ? av[0] : av[NTY - 1], fp4_operand(tw[4 * hb + c]), zero,
+                                       p < NBV ? sav[0] : sav[NTY - 1]);
         if constexpr (NPV > NBV) {  // parity plane once the last stored plane is in
           if (p == NBV - 1) {
 #pragma unroll
@@ -390,14 +394,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       red[cb * 64 + lane] = macc[cb];
-      red[(8 + cb) * 64 + lane] = jacc[cb];
+      if constexpr (VQ) red[(8 + cb) * 64 + lane] = jacc[cb];
     }
   }
   __syncthreads();
   float csum = 0.f;
 #pragma unroll
   for (int k = 0; k < NPV; ++k) csum += PV.plane_coef[k];
-  for (int e = threadIdx.x; e < 16 * 64; e += NT) {
+  for (int e = threadIdx.x; e < (VQ ? 16 : 8) * 64; e += NT) {
     const int slot = e >> 6, L = e & 63, gh = L >> 4;
     if (gh >= G) continue;
     float v = 0.f;
@@ -415,7 +419,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     const bool is_m = slot < 8;
     const int j = 16 * (slot & 7) + (L & 15);
     v += is_m ? PV.plane_bias * w_all + 0.5f * csum * w_3 : -q_n3;
-    float* out = part + ((static_cast<int64_t>(bk) * n_chunks + chunk) * G + gh) * (2 + 2 * kPrepD);
+    float* out = part + ((static_cast<int64_t>(bk) * n_chunks + chunk) * G + gh) * REC;
     out[2 + (is_m ? 0 : kPrepD) + j] = v;
     if (e == gh * 16) {  // one thread per head writes the max and the weight sum
       out[0] = m;
@@ -424,12 +428,13 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   }
 }
 
-// d = 128 for K and V (QJL dimension 128), at most 4 query heads per KV head.
+// d = 128 for K and V (QJL dimension 128, or an MSE-only V codec), at most 4
+// query heads per KV head.
 bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
   const char* v = std::getenv("TQ_DECODE_KERNEL");
   if (v && std::string(v) == "valu") return false;
   const int G = n_q_heads / n_kv_heads;
-  return ck->prm.d == 128 && cv->prm.d == 128 && ck->prm.m == 128 && cv->prm.m == 128 && G <= 4;
+  return ck->prm.d == 128 && cv->prm.d == 128 && ck->prm.m == 128 && (cv->prm.m == 128 || !cv->qjl) && G <= 4;
 }
 
 int decode_mfma_chunk() { return kDecChunk; }
@@ -439,10 +444,11 @@ hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int ba
                               tq_packed_t k, tq_packed_t v, int64_t ctx, float scale, bool sparse_v, float v_gate,
                               const PageMap* pm, const uint8_t* prep, float* part, int n_chunks, hipStream_t s) {
   const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
-  auto go = [&]<int NPK, int NPV>() -> hipError_t {
-    auto kern = pm ? (sparse_v ? decode_mfma_kernel<NPK, NPV, true, true> : decode_mfma_kernel<NPK, NPV, false, true>)
-                   : (sparse_v ? decode_mfma_kernel<NPK, NPV, true, false>
-                               : decode_mfma_kernel<NPK, NPV, false, false>);
+  auto go = [&]<int NPK, int NPV, bool VQ>() -> hipError_t {
+    auto kern = pm ? (sparse_v ? decode_mfma_kernel<NPK, NPV, true, true, VQ>
+                               : decode_mfma_kernel<NPK, NPV, false, true, VQ>)
+                   : (sparse_v ? decode_mfma_kernel<NPK, NPV, true, false, VQ>
+                               : decode_mfma_kernel<NPK, NPV, false, false, VQ>);
     hipLaunchKernelGGL(kern, dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
                        0, s, prep, ck->prm, cv->prm, pmv, n_q_heads, n_kv_heads, static_cast<int>(ctx),
                        n_chunks, scale, v_gate, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm,
@@ -450,10 +456,17 @@ hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int ba
     return hipGetLastError();
   };
   auto by_v = [&]<int NPK>() -> hipError_t {
+    if (!cv->qjl) {  // MSE-only V codecs: 2 or 3 code bits
+      switch (cv->prm.n_planes) {
+        case 2: return go.template operator()<NPK, 2, false>();
+        case 4: return go.template operator()<NPK, 4, false>();
+      }
+      return hipErrorInvalidValue;
+    }
     switch (cv->prm.n_planes) {
-      case 1: return go.template operator()<NPK, 1>();
-      case 2: return go.template operator()<NPK, 2>();
-      case 4: return go.template operator()<NPK, 4>();
+      case 1: return go.template operator()<NPK, 1, true>();
+      case 2: return go.template operator()<NPK, 2, true>();
+      case 4: return go.template operator()<NPK, 4, true>();
     }
     return hipErrorInvalidValue;
   };

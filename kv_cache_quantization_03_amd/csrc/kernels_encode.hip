@@ -19,10 +19,13 @@ namespace tq {
 //   ν = ||x||, y = H (D ⊙ x/ν)/√d, idx_j = #{k : t_k < y_j} (ties low),
 //   r = y - c[idx] -> rbuf (fp32), γ = ||r||, codes packed as bit-planes.
 // ----------------------------------------------------------------------------
-// The residual goes to rbuf as fp32 [n][d] (HL = false) or, for the matrix-core
-// projection, as r·rscale split into an fp16 pair [n][hi, lo][d] (HL = true;
-// the same bytes).
-template <int E, typename T, bool HL>
+// The residual goes to rbuf as fp32 [n][d] (RM = kResF32) or, for the
+// matrix-core projection, as r·rscale split into an fp16 pair [n][hi, lo][d]
+// (RM = kResF16; the same bytes).  An MSE-only codec (RM = kResNone) keeps
+// neither the residual nor γ: its record is the codes and ν.
+enum ResidualMode { kResF32, kResF16, kResNone };
+
+template <int E, typename T, int RM>
 __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x, int64_t n, DevParams P,
                                                         const float* __restrict__ Dsign,
                                                         uint32_t* __restrict__ codes, float* __restrict__ norm,
@@ -64,17 +67,17 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
     }
     idx[e] = c;
     const float r = y - yh;
-    if constexpr (HL) {
+    if constexpr (RM == kResF16) {
       const float rsc = r * rscale;
       const _Float16 hi = static_cast<_Float16>(rsc);
       rh[e * kWave + lane] = hi;
       rh[d + e * kWave + lane] = static_cast<_Float16>(rsc - static_cast<float>(hi));
-    } else {
+    } else if constexpr (RM == kResF32) {
       rr[e * kWave + lane] = r;
     }
     rs = fmaf(r, r, rs);
   }
-  rs = wave_sum(rs);
+  if constexpr (RM != kResNone) rs = wave_sum(rs);
 
   // bit-plane packing: plane p, register e -> words p*(d/32) + 2e (+1)
   const int W = P.code_words;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
   }
   if (lane == 0) {
     norm[vec] = nu;
-    rnorm[vec] = sqrtf(rs);
+    if constexpr (RM != kResNone) rnorm[vec] = sqrtf(rs);
   }
 }
 
@@ -248,7 +251,8 @@ __device__ __forceinline__ int polar_code(const float (&bound)[16], float th) {
 // from the same two radii).  Codes go to their slots in LDS (level 1: 4l + i,
 // level 2: 64 + 2l + i, level 3: 96 + l, level k >= 4: 128 - 2^(8-k) + node),
 // and ŷ is rebuilt top-down from radius 1 with the fp32 cos and sin tables.
-template <typename T, int B, bool POLAR>
+// QJL = false (an MSE-only codec): codes and ν only, no residual, no S·r.
+template <typename T, int B, bool POLAR, bool QJL>
 __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__ x, int64_t n, DevParams P,
                                                            PolarParams PP, const float* __restrict__ Dsign,
                                                            const _Float16* __restrict__ S16,
@@ -269,14 +273,16 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
   }
   // fp16 S rows of this wave's outputs: A fragments [row block][K step][hi, lo]
   h8 sf[2][4][2];
+  if constexpr (QJL) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int hl = 0; hl < 2; ++hl)
-        sf[rb][ks][hl] = *reinterpret_cast<const h8*>(S16 + hl * d * d + (32 * wv + 16 * rb + l) * d + 32 * ks +
-                                                      8 * (lane >> 4));
+        for (int hl = 0; hl < 2; ++hl)
+          sf[rb][ks][hl] = *reinterpret_cast<const h8*>(S16 + hl * d * d + (32 * wv + 16 * rb + l) * d + 32 * ks +
+                                                        8 * (lane >> 4));
+  }
   float dsg[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) dsg[e] = Dsign[8 * l + e];
@@ -407,11 +413,13 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 #pragma unroll
       for (int p = 0; p + 1 < B; ++p) bits[p] |= static_cast<uint32_t>((lowbits >> p) & 1) << e;
       bits[B - 1] |= static_cast<uint32_t>(pos) << e;
-      rr[e] = y - yh;
-      rs = fmaf(rr[e], rr[e], rs);
+      if constexpr (QJL) {
+        rr[e] = y - yh;
+        rs = fmaf(rr[e], rr[e], rs);
+      }
     }
     }  // POLAR
-    rs = row_sum(rs);
+    if constexpr (QJL) rs = row_sum(rs);
     // code word w (coordinates 32w..32w+31) of plane p from lanes 4w..4w+3
 #pragma unroll
     for (int p = 0; p < B; ++p) {
@@ -422,8 +430,9 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
     }
     if (valid && l == 0) {
       norm[vec] = nu;
-      rnorm[vec] = sqrtf(rs);
+      if constexpr (QJL) rnorm[vec] = sqrtf(rs);
     }
+    if constexpr (!QJL) continue;  // an MSE-only record is complete
     h8 hi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -588,11 +597,13 @@ bool encode_fused_eligible(const tq_codec_s* c) {
   if (c->polar) return true;  // the only polar encode (d = 128, made so at codec creation)
   const char* v = std::getenv("TQ_ENCODE_KERNEL");
   if (v && std::string(v) == "split") return false;
+  if (!c->qjl) return c->prm.d == 128;  // MSE-only: no projection
   return c->prm.d == 128 && c->prm.m == 128 && c->dS16 != nullptr;
 }
 
 size_t encode_ws_bytes(const tq_codec_s* c, int64_t n) {
   if (encode_fused_eligible(c)) return 0;  // the fused kernel keeps r on chip
+  if (!c->qjl) return 0;                   // MSE-only: no residual to project
   return static_cast<size_t>(n) * c->prm.d * sizeof(float);
 }
 
@@ -605,11 +616,15 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
     const dim3 grid(static_cast<unsigned>(ceil_div(n, 16 * kEncPasses)));
     auto go = [&]<int B>() -> hipError_t {
       if (c->polar)
-        hipLaunchKernelGGL((encode_fused_kernel<T, B, true>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD, c->dS16,
-                           out.codes, out.signs, out.norm, out.rnorm);
-      else
-        hipLaunchKernelGGL((encode_fused_kernel<T, B, false>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD,
+        hipLaunchKernelGGL((encode_fused_kernel<T, B, true, true>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD,
                            c->dS16, out.codes, out.signs, out.norm, out.rnorm);
+      else if (c->qjl)
+        hipLaunchKernelGGL((encode_fused_kernel<T, B, false, true>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD,
+                           c->dS16, out.codes, out.signs, out.norm, out.rnorm);
+      else
+        hipLaunchKernelGGL((encode_fused_kernel<T, B, false, false>), grid, dim3(256), 0, s, x, n, P, c->pol, c->dD,
+                           static_cast<const _Float16*>(nullptr), out.codes, static_cast<uint32_t*>(nullptr),
+                           out.norm, static_cast<float*>(nullptr));
       return hipGetLastError();
     };
     switch (P.b) {
@@ -622,17 +637,21 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
   const bool mfma = sproj_mfma_eligible(c);
   // 2^sc with sc = ceil(log2 sqrt(d)) + 4: r·2^sc is O(1) per coordinate and below 2^11
   const int sc = static_cast<int>(std::ceil(std::log2(std::sqrt(static_cast<double>(P.d))))) + 4;
+  const dim3 grid_rq(static_cast<unsigned>(ceil_div(n, 4)));
   auto run = [&]<int E>() -> hipError_t {
-    if (mfma)
-      hipLaunchKernelGGL((encode_rq_kernel<E, T, true>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
-                         s, x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r, std::ldexp(1.0f, sc));
+    if (!c->qjl)
+      hipLaunchKernelGGL((encode_rq_kernel<E, T, kResNone>), grid_rq, dim3(256), 0, s, x, n, P, c->dD, out.codes,
+                         out.norm, static_cast<float*>(nullptr), static_cast<float*>(nullptr), 1.0f);
+    else if (mfma)
+      hipLaunchKernelGGL((encode_rq_kernel<E, T, kResF16>), grid_rq, dim3(256), 0, s, x, n, P, c->dD, out.codes,
+                         out.norm, out.rnorm, ws_r, std::ldexp(1.0f, sc));
     else
-      hipLaunchKernelGGL((encode_rq_kernel<E, T, false>), dim3(static_cast<unsigned>(ceil_div(n, 4))), dim3(256), 0,
-                         s, x, n, P, c->dD, out.codes, out.norm, out.rnorm, ws_r, 1.0f);
+      hipLaunchKernelGGL((encode_rq_kernel<E, T, kResF32>), grid_rq, dim3(256), 0, s, x, n, P, c->dD, out.codes,
+                         out.norm, out.rnorm, ws_r, 1.0f);
     return hipGetLastError();
   };
   hipError_t e = dispatch_E(P.d, run);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !c->qjl) return e;
   if (mfma) {
     const _Float16* r16 = reinterpret_cast<const _Float16*>(ws_r);
     const int64_t per_launch = static_cast<int64_t>(1) << 24;  // vectors per launch (grid size well inside 2^32)

@@ -18,14 +18,15 @@ namespace tq {
 namespace {
 
 // One thread per (record, 32-bit word); words of a record: code words, sign
-// words, ν, γ.  Records whose position falls outside the page table, or whose
-// page id is outside [0, n_pages), are not written.
-__global__ __launch_bounds__(256) void scatter_paged_kernel(tq_packed_t src, int cw, int sw, int n_kv_heads,
+// words, ν, γ (an MSE-only codec: code words and ν; sw = 0, qjl = 0).  Records
+// whose position falls outside the page table, or whose page id is outside
+// [0, n_pages), are not written.
+__global__ __launch_bounds__(256) void scatter_paged_kernel(tq_packed_t src, int cw, int sw, int qjl, int n_kv_heads,
                                                             int n_new, int64_t n_rec,
                                                             const int32_t* __restrict__ ctx_lens,
                                                             const int32_t* __restrict__ page_table, int max_pages,
                                                             int page_size, int n_pages, tq_packed_t dst) {
-  const int words = cw + sw + 2;
+  const int words = cw + sw + 1 + qjl;
   const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (e >= n_rec * words) return;
   const int64_t i = e / words;
@@ -76,9 +77,10 @@ hipError_t launch_append_paged(const tq_codec_s* c, const void* x, tq_dtype_t dt
   p += align256(n * 4);
   hipError_t e = launch_encode(c, x, dt, n, st, reinterpret_cast<float*>(p), s);
   if (e != hipSuccess) return e;
-  const int64_t total = n * (cw + sw + 2);
+  const int qjl = c->qjl ? 1 : 0;
+  const int64_t total = n * (cw + sw + 1 + qjl);
   hipLaunchKernelGGL(scatter_paged_kernel, dim3(static_cast<unsigned>(ceil_div(total, 256))), dim3(256), 0, s, st,
-                     cw, sw, n_kv_heads, n_new, n, ctx_lens, page_table, max_pages, page_size, n_pages, cache);
+                     cw, sw, qjl, n_kv_heads, n_new, n, ctx_lens, page_table, max_pages, page_size, n_pages, cache);
   return hipGetLastError();
 }
 

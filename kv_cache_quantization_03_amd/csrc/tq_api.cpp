@@ -44,12 +44,14 @@ size_t dtype_size(tq_dtype_t dt) { return dt == TQ_F32 ? 4 : 2; }
 
 bool valid_dtype(tq_dtype_t dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
 
-tq_status_t check_packed(const tq_packed_t& p, const char* name) {
-  if (!p.codes || !p.signs || !p.norm || !p.rnorm) {
+// Records of an MSE-only codec (qjl false) have no signs and no γ: those two
+// pointers are ignored and may be NULL.
+tq_status_t check_packed(const tq_packed_t& p, const char* name, bool qjl = true) {
+  if (!p.codes || !p.norm || (qjl && (!p.signs || !p.rnorm))) {
     set_error(std::string(name) + ": a packed array pointer is NULL");
     return TQ_ERROR_INVALID_VALUE;
   }
-  if (!aligned(p.codes, 4) || !aligned(p.signs, 4) || !aligned(p.norm, 4) || !aligned(p.rnorm, 4)) {
+  if (!aligned(p.codes, 4) || !aligned(p.norm, 4) || (qjl && (!aligned(p.signs, 4) || !aligned(p.rnorm, 4)))) {
     set_error(std::string(name) + ": packed arrays must be 4-byte aligned");
     return TQ_ERROR_MISALIGNED;
   }
@@ -93,6 +95,14 @@ tq_status_t check_heads(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads) {
   return TQ_SUCCESS;
 }
 
+// The logits and search estimators need the QJL stage (an MSE-only codec's
+// inner products are biased); such codecs serve as value codecs only.
+tq_status_t need_qjl(const tq_codec_s* c, const char* what) {
+  if (c->qjl) return TQ_SUCCESS;
+  set_error(std::string(what) + " needs a two-stage codec (an MSE-only codec is a value codec)");
+  return TQ_ERROR_NOT_SUPPORTED;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- encode
@@ -114,9 +124,9 @@ extern "C" tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, 
     set_error("k/v must be aligned to their element size");
     return TQ_ERROR_MISALIGNED;
   }
-  tq_status_t st = check_packed(k_out, "k_out");
+  tq_status_t st = check_packed(k_out, "k_out", c->qjl);
   if (st != TQ_SUCCESS) return st;
-  if (v && (st = check_packed(v_out, "v_out")) != TQ_SUCCESS) return st;
+  if (v && (st = check_packed(v_out, "v_out", c->qjl)) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::encode_ws_bytes(c, n_vec))) != TQ_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled()) std::fprintf(stderr, "[tq] encode n=%lld d=%d bits=%d v=%d\n", (long long)n_vec, c->prm.d, c->host.bits, v != nullptr);
@@ -139,8 +149,9 @@ extern "C" tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_
   tq::clear_error();
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  tq_status_t st = need_qjl(c, "tq_attn_logits");
   if (st != TQ_SUCCESS) return st;
+  if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
   if (!q || !logits) { set_error("q or logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
@@ -159,8 +170,9 @@ extern "C" tq_status_t tq_attn_query_prep(tq_codec_t c, const void* q, tq_dtype_
   tq::clear_error();
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  tq_status_t st = need_qjl(c, "tq_attn_query_prep");
   if (st != TQ_SUCCESS) return st;
+  if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0) { set_error("n_queries must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (batch == 0 || n_queries == 0) return TQ_SUCCESS;
   if (!q) { set_error("q is NULL"); return TQ_ERROR_INVALID_VALUE; }
@@ -176,8 +188,9 @@ extern "C" tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, si
                                               tq_packed_t k, int64_t ctx_len, float* logits, void* stream) {
   tq::clear_error();
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
+  tq_status_t st = need_qjl(c, "tq_attn_logits_prepped");
   if (st != TQ_SUCCESS) return st;
+  if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
   if (!logits) { set_error("logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
@@ -207,6 +220,7 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
     set_error("decode attention takes codecs with the per-coordinate first stage");
     return TQ_ERROR_NOT_SUPPORTED;
   }
+  if (!ck->qjl) { set_error("the K codec must be a two-stage codec (an MSE-only codec is a value codec)"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
   if (st != TQ_SUCCESS) return st;
@@ -218,7 +232,7 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (!q || !out) { set_error("q or out is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!aligned(q, dtype_size(q_dt)) || !aligned(out, dtype_size(out_dt))) { set_error("q/out misaligned"); return TQ_ERROR_MISALIGNED; }
   if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
-  if ((st = check_packed(v, "v")) != TQ_SUCCESS) return st;
+  if ((st = check_packed(v, "v", cv->qjl)) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len))) != TQ_SUCCESS) return st;
   if (log_enabled())
     std::fprintf(stderr, "[tq] %s b=%d hq=%d hkv=%d ctx=%lld gate=%g\n", name, batch, n_q_heads, n_kv_heads,
@@ -283,7 +297,7 @@ extern "C" tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dt
     set_error("x, ctx_lens or page_table misaligned");
     return TQ_ERROR_MISALIGNED;
   }
-  tq_status_t st = check_packed(cache, "cache");
+  tq_status_t st = check_packed(cache, "cache", c->qjl);
   if (st != TQ_SUCCESS) return st;
   const int64_t n = static_cast<int64_t>(batch) * n_kv_heads * n_new;
   if ((st = check_ws(ws, ws_bytes, tq::append_paged_ws_bytes(c, n))) != TQ_SUCCESS) return st;
@@ -315,7 +329,7 @@ extern "C" tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const 
     return TQ_ERROR_INVALID_VALUE;
   }
   if (n_kv_heads > 0 && n_q_heads % n_kv_heads == 0 && !tq::decode_paged_supported(ck, cv, n_q_heads, n_kv_heads)) {
-    set_error("paged decode needs head_dim = qjl_dim = 128 for K and V and at most 4 query heads per KV head");
+    set_error("paged decode needs head_dim = 128 for K and V, qjl_dim = 128 (or an MSE-only V codec) and at most 4 query heads per KV head");
     return TQ_ERROR_NOT_SUPPORTED;
   }
   if (batch > 0 && (!ctx_lens || !page_table)) { set_error("ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
@@ -340,6 +354,7 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
   tq::clear_error();
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (c->polar) { set_error("search takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
+  if (!c->qjl) return need_qjl(c, "tq_search_topk");
   if (n_db < 1 || n_queries < 0) { set_error("need n_db >= 1 and n_queries >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (topk < 1 || topk > 1024 || topk > n_db) { set_error("need 1 <= topk <= min(n_db, 1024)"); return TQ_ERROR_INVALID_VALUE; }
   if (n_queries == 0) return TQ_SUCCESS;

@@ -37,6 +37,8 @@ struct HostTables {
 tq_status_t build_host_tables(int d, int bits, int m, uint64_t seed, HostTables* out);
 // The same plus the per-level angle codebooks of the recursive polar stage.
 tq_status_t build_polar_tables(int d, int bits, int m, uint64_t seed, HostTables* out);
+// First stage only (MSE-only value codec): b = bits Lloyd-Max bits, m = 0, no S.
+tq_status_t build_mse_tables(int d, int bits, uint64_t seed, HostTables* out);
 bool supported_dim(int d);
 
 // Device constant block of one codec: everything a kernel needs besides S.
@@ -99,6 +101,7 @@ struct tq_codec_s {
   float* dD = nullptr;   // [d] ±1
   _Float16* dS16 = nullptr;  // [2][m][d]: S = hi + lo in fp16 (m = d, d a multiple of 128; else nullptr)
   bool polar = false;        // first stage: recursive polar angles instead of per-coordinate codes
+  bool qjl = true;           // false: MSE-only codec (m = 0: records hold codes and ν, no signs, no γ)
   tq::PolarParams pol{};
 };
 

@@ -51,6 +51,8 @@ def check_encode(cd: O.Codec, x64: np.ndarray, gpu: dict, label: str = "") -> di
             assert abs(y32[v, j] - tb) < BAND, f"{label}: mismatch at ({v},{j}) y={y32[v,j]} boundary {tb}"
     # norms
     assert np.allclose(gpu["norm"], ref["norm"], rtol=NORM_RTOL, atol=0), f"{label}: norm"
+    if not cd.qjl:  # an MSE-only record ends here: codes and ν
+        return {"code_mismatch": n_diff, "sign_mismatch": 0, "ref": ref}
     # re-derive rows whose codes differ
     rows = np.unique(np.nonzero(diff)[0]) if n_diff else np.array([], np.int64)
     exp_signs = ref["signs"].copy()

@@ -35,6 +35,21 @@ def pair(B, d, bits, seed=1234):
     return _codecs[key]
 
 
+_mse_codecs = {}
+
+
+def mse_pair(B, d, bits, seed=1234):
+    """An MSE-only value codec (codes and ν, no QJL stage) and its oracle."""
+    key = (d, bits, seed)
+    if key not in _mse_codecs:
+        _mse_codecs[key] = (B.tq_codec_create_mse(d, bits, seed), O.make_mse_codec(d, bits, seed=seed))
+    return _mse_codecs[key]
+
+
+def vpair(B, d, bits, mse):
+    return mse_pair(B, d, bits) if mse else pair(B, d, bits)
+
+
 def to_dev(x32: np.ndarray, dtype: str):
     t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).cuda()
     return {"f32": t, "bf16": t.to(torch.bfloat16), "f16": t.to(torch.float16)}[dtype]
@@ -445,16 +460,18 @@ def _dropped_blocks(keep, ctx, hkv):
     return float(np.mean(~k.any(axis=(1, 3))))
 
 
-@pytest.mark.parametrize("kbits,vbits,hq,hkv,ctx,gate,needles,qscale",
-                         [(3, 3, 8, 2, 3000, 1e-6, True, 1.0),     # matrix-core kernel, needles
-                          (4, 2, 4, 1, 2049, 1e-3, False, 3.0),    # per-key drops inside kept blocks
-                          (3, 4, 2, 2, 1100, 1e-2, True, 1.0),
-                          (3, 3, 16, 2, 1500, 1e-6, True, 1.0),    # general kernel, 512-key chunks
-                          (2, 3, 16, 1, 700, 1e-3, False, 3.0)])   # general kernel, 256-key chunks
-def test_decode_sparse_v_parity(B, kbits, vbits, hq, hkv, ctx, gate, needles, qscale):
-    say(f"sparse V K{kbits} V{vbits} hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles}")
+@pytest.mark.parametrize("kbits,vbits,hq,hkv,ctx,gate,needles,qscale,vmse",
+                         [(3, 3, 8, 2, 3000, 1e-6, True, 1.0, False),     # matrix-core kernel, needles
+                          (4, 2, 4, 1, 2049, 1e-3, False, 3.0, False),    # per-key drops inside kept blocks
+                          (3, 4, 2, 2, 1100, 1e-2, True, 1.0, False),
+                          (3, 3, 16, 2, 1500, 1e-6, True, 1.0, False),    # general kernel, 512-key chunks
+                          (2, 3, 16, 1, 700, 1e-3, False, 3.0, False),    # general kernel, 256-key chunks
+                          (3, 3, 8, 2, 3000, 1e-6, True, 1.0, True),      # MSE-only V, matrix-core kernel
+                          (3, 2, 16, 2, 1500, 1e-3, False, 3.0, True)])   # MSE-only V, general kernel
+def test_decode_sparse_v_parity(B, kbits, vbits, hq, hkv, ctx, gate, needles, qscale, vmse):
+    say(f"sparse V K{kbits} V{vbits}{' mse' if vmse else ''} hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles}")
     gk, ok = pair(B, 128, kbits)
-    gv, ov = pair(B, 128, vbits)
+    gv, ov = vpair(B, 128, vbits, vmse)
     q, k, v = _sparse_case(hq, hkv, ctx, needles, qscale, ctx + hq + kbits)
     kr, vr = O.encode(ok, k.astype(np.float64)), O.encode(ov, v.astype(np.float64))
     scale = 1 / math.sqrt(128)
@@ -513,11 +530,12 @@ def _fill_pages(rec_by_seq, page_table, hkv, P, n_pages, junk):
     return cache
 
 
-def test_append_paged_matches_contiguous_encode(B):
+@pytest.mark.parametrize("vmse", [False, True])
+def test_append_paged_matches_contiguous_encode(B, vmse):
     # tokens appended step by step (and one 70-token prefill) land at their page
     # slots with exactly the records of a contiguous encode; rows that no append
     # reaches, and positions past the page table, keep their old contents
-    gc, oc = pair(B, 128, 3)
+    gc, oc = vpair(B, 128, 3, vmse)
     batch, hkv, P, max_pages, n_pages = 3, 2, 128, 4, 13
     rng = np.random.default_rng(51)
     pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
@@ -527,9 +545,11 @@ def test_append_paged_matches_contiguous_encode(B):
     n_rows = n_pages * hkv * P
     cache = B.alloc_packed(gc, n_rows)
     for t in (cache.codes, cache.signs):
-        t.fill_(0x5A5A5A5A)
+        if t is not None:
+            t.fill_(0x5A5A5A5A)
     cache.norm.fill_(-7.0)
-    cache.rnorm.fill_(-7.0)
+    if cache.rnorm is not None:
+        cache.rnorm.fill_(-7.0)
     ctx = torch.from_numpy(ctx0.copy()).cuda()
     ptd = torch.from_numpy(pt).cuda()
     for x in xs:
@@ -556,13 +576,14 @@ def test_append_paged_matches_contiguous_encode(B):
     say(f"append paged: {written.sum()} rows written, {(~written).sum()} untouched")
 
 
-@pytest.mark.parametrize("kbits,vbits,gate", [(3, 3, 0.0), (4, 2, 0.0), (3, 3, 1e-3)])
-def test_decode_paged_parity(B, kbits, vbits, gate):
+@pytest.mark.parametrize("kbits,vbits,gate,vmse", [(3, 3, 0.0, False), (4, 2, 0.0, False), (3, 3, 1e-3, False),
+                                                  (3, 3, 0.0, True), (4, 2, 1e-3, True)])
+def test_decode_paged_parity(B, kbits, vbits, gate, vmse):
     # four sequences of different lengths (one empty, one of a single token,
     # one filling its page table) in shuffled pages with junk in the rest
-    say(f"paged decode K{kbits} V{vbits} gate={gate}")
+    say(f"paged decode K{kbits} V{vbits}{' mse' if vmse else ''} gate={gate}")
     gk, ok = pair(B, 128, kbits)
-    gv, ov = pair(B, 128, vbits)
+    gv, ov = vpair(B, 128, vbits, vmse)
     hq, hkv, P, max_pages = 8, 2, 256, 8
     ctxs = [1500, 1, 0, max_pages * P]
     batch = len(ctxs)
@@ -598,6 +619,91 @@ def test_decode_paged_parity(B, kbits, vbits, gate):
                                                       n, scale, gate, B.tq_decode_attn_chunk(hq, hkv))
             say(f"  sequence {b} (ctx {n}): dropped {np.mean(~keep):.3f}")
             assert_sparse_v_close(out[b:b + 1], ref, local, gate, O.dequantize(ov, vr), hkv, n, 1e-4)
+
+
+# ---------------------------------------------------------------- MSE-only value codec
+@pytest.mark.parametrize("d,bits,dtype,split", [(128, 2, "bf16", False), (128, 3, "f32", False), (128, 3, "f16", True),
+                                                (128, 2, "bf16", True), (256, 3, "bf16", False), (1536, 2, "f32", False)])
+def test_mse_encode_parity(B, d, bits, dtype, split, monkeypatch):
+    # d = 128 takes the fused kernel (split: the general one-wave-per-vector kernel)
+    say(f"mse encode d={d} bits={bits} {dtype} split={split}")
+    gc, oc = mse_pair(B, d, bits)
+    if split:
+        monkeypatch.setenv("TQ_ENCODE_KERNEL", "split")
+    assert (gc.m, gc.sign_words, gc.b, gc.record_bytes) == (0, 0, bits, d * bits // 8 + 4)
+    assert np.allclose(gc.centroids, oc.centroids, rtol=0, atol=1e-12)
+    n = 1000 if d < 1024 else 301
+    x = rand_keys(n, d, seed=d * 11 + bits, dtype=dtype)
+    kp, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
+    torch.cuda.synchronize()
+    assert kp.signs is None and kp.rnorm is None
+    st = check_encode(oc, x.astype(np.float64), kp.numpy(), f"mse d{d}b{bits}{dtype}")
+    say("  code mismatches", st["code_mismatch"])
+
+
+@pytest.mark.parametrize("d,kbits,vbits,hq,hkv,ctx,valu",
+                         [(128, 3, 3, 8, 2, 3000, False), (128, 4, 2, 4, 1, 1025, False), (128, 3, 3, 32, 8, 700, False),
+                          (128, 3, 2, 16, 1, 513, False),     # G = 16: the general kernel
+                          (128, 3, 3, 4, 2, 2049, True), (256, 3, 3, 8, 2, 900, False), (128, 3, 3, 2, 2, 1, False)])
+def test_decode_attn_mse_values_parity(B, d, kbits, vbits, hq, hkv, ctx, valu, monkeypatch):
+    # K two-stage, V MSE-only: v̂ = ν Rᵀ c[idx], no QJL term in the value path
+    say(f"decode mse V d={d} K{kbits} V{vbits} hq={hq} hkv={hkv} ctx={ctx} valu={valu}")
+    gk, ok = pair(B, d, kbits)
+    gv, ov = mse_pair(B, d, vbits)
+    rng = np.random.default_rng(ctx + hq + d)
+    k = as_exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    v = as_exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    q = as_exact(rng.standard_normal((1, hq, d)), "bf16")
+    kr, vr = O.encode(ok, k.astype(np.float64)), O.encode(ov, v.astype(np.float64))
+    scale = 1 / math.sqrt(d)
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale)
+    kp, vp = B.packed_from_numpy(kr), B.packed_from_numpy(vr)
+    vp.signs = vp.rnorm = None                      # not read for an MSE-only codec
+    if valu:
+        monkeypatch.setenv("TQ_DECODE_KERNEL", "valu")
+    out = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = row_rel_err(out.cpu().numpy(), ref)
+    say(f"  attn max row err {err.max():.3e}")
+    assert np.all(err <= 1e-4)
+
+
+def test_decode_attn_mse_values_end_to_end(B):
+    # GPU-encoded K (two-stage) and V (MSE-only) against the oracle on the same records
+    gk, ok = pair(B, 128, 3)
+    gv, ov = mse_pair(B, 128, 3)
+    hq, hkv, ctx = 8, 2, 2500
+    rng = np.random.default_rng(78)
+    k = as_exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    v = as_exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    q = as_exact(rng.standard_normal((1, hq, 128)), "bf16")
+    kp, _ = B.tq_encode_kv(gk, to_dev(k, "bf16"))
+    vp, _ = B.tq_encode_kv(gv, to_dev(v, "bf16"))
+    out = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, 1 / math.sqrt(128), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kr = oracle_records_like(ok, k.astype(np.float64), kp.numpy())
+    vr = oracle_records_like(ov, v.astype(np.float64), vp.numpy())
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, 1 / math.sqrt(128))
+    assert np.all(row_rel_err(out.cpu().numpy(), ref) <= 1e-4)
+
+
+def test_mse_codec_is_a_value_codec_only(B):
+    gv, _ = mse_pair(B, 128, 3)
+    gk, _ = pair(B, 128, 3)
+    for bad in ((128, 1), (128, 4), (100, 3)):
+        with pytest.raises(B.TQError):
+            B.tq_codec_create_mse(*bad)
+    kp, vp = B.alloc_packed(gk, 64), B.alloc_packed(gv, 64)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    with pytest.raises(B.TQError):                  # as the K codec
+        B.tq_decode_attn(gv, gv, q, vp, vp, 64, 1, 0.1)
+    with pytest.raises(B.TQError):
+        B.tq_attn_logits(gv, q.view(1, 1, 4, 128), vp, 64, 1)
+    with pytest.raises(B.TQError):
+        B.tq_search_topk(gv, vp, torch.zeros((1, 128), device="cuda"), 5)
+    out = B.tq_decode_attn(gk, gv, q, kp, vp, 64, 1, 0.1, out_dtype=torch.float32)   # as the V codec: accepted
+    torch.cuda.synchronize()
+    assert out.shape == (1, 4, 128)
 
 
 def test_decode_paged_identity_equals_contiguous(B):
