@@ -162,7 +162,23 @@ def main():
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_pass": True, "logits_launches": 20, "copy_bytes": 64 * 2 ** 20, "copies": 5}))
+        del src, dst
+        # then 5 decode-attention calls on the 128K-context shape (3-bit K and
+        # V) and 3 encodes of its keys, for the per-kernel instruction counters
+        cdc = B.tq_codec_create(d, 3, 0, I.CODEC_SEED)
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        kd = torch.randn((8 * 131072, d), generator=g, device=dev).to(torch.bfloat16)
+        qd = torch.randn((1, 32, d), generator=g, device=dev).to(torch.bfloat16)
+        kpd = B.alloc_packed(cdc, kd.shape[0], dev)
+        for _ in range(3):
+            B.tq_encode_kv(cdc, kd, k_out=kpd)
+        outd = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            B.tq_decode_attn(cdc, cdc, qd, kpd, kpd, 131072, 8, 1 / math.sqrt(d), out=outd)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "logits_launches": 20, "copy_bytes": 64 * 2 ** 20, "copies": 5,
+                          "decode_launches": 5, "encode_launches": 3}))
         return
 
     # ---- the timed steps run as one HIP graph (no host launch cost per step)
