@@ -51,6 +51,16 @@ def parse():
     return ap.parse_args()
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc"))):
@@ -701,7 +711,7 @@ def cpu_baseline(w, k_host, q_host, bits):
     return {"value": n_scores / score_s, "unit": "keys/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"full workload ({n_scores} scores) x{reps}; encode of {k_host.shape[0]} keys took "
                       f"{enc_s:.2f}s ({k_host.shape[0] / enc_s:.0f} vectors/s)",
-            "os_cpu_count": os.cpu_count(), "value_one_thread": one_core}
+            "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(), "value_one_thread": one_core}
 
 
 if __name__ == "__main__":
