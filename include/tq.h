@@ -204,7 +204,8 @@ tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, tq_dtype_t 
  *   logits : device fp32 [batch][n_q_heads][n_queries][ctx_len].  These are
  *            raw <q,k> estimates: no 1/sqrt(d) scaling is applied.
  * GQA: query head h reads KV head h / (n_q_heads / n_kv_heads); n_q_heads
- * must be a multiple of n_kv_heads.  ctx_len = 0 is a valid no-op.
+ * must be a multiple of n_kv_heads.  ctx_len = 0 is a valid no-op; ctx_len
+ * above 2^31 - 2^16 returns TQ_ERROR_NOT_SUPPORTED.
  * Workspace: tq_attn_logits_workspace(...) bytes, 16-byte aligned.
  */
 size_t tq_attn_logits_workspace(tq_codec_t c, int32_t batch, int32_t n_q_heads,

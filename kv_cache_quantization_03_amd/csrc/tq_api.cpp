@@ -95,6 +95,10 @@ tq_status_t check_heads(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads) {
   return TQ_SUCCESS;
 }
 
+// The logits kernels index keys within a head in 32 bits (a grid row spans at
+// most 2^31 keys, with room for the last block's rounding).
+constexpr int64_t kMaxLogitsCtx = (int64_t{1} << 31) - (int64_t{1} << 16);
+
 // The logits and search estimators need the QJL stage (an MSE-only codec's
 // inner products are biased); such codecs serve as value codecs only.
 tq_status_t need_qjl(const tq_codec_s* c, const char* what) {
@@ -153,6 +157,7 @@ extern "C" tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_
   if (st != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
   if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
   if (!q || !logits) { set_error("q or logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!aligned(q, dtype_size(q_dt)) || !aligned(logits, 4)) { set_error("q/logits misaligned"); return TQ_ERROR_MISALIGNED; }
@@ -192,6 +197,7 @@ extern "C" tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, si
   if (st != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
   if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
   if (!logits) { set_error("logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!aligned(logits, 4)) { set_error("logits misaligned"); return TQ_ERROR_MISALIGNED; }

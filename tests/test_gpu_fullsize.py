@@ -227,3 +227,28 @@ def test_full_vector_search(B):
         assert np.all(full[idx[qi]] >= kth - 1e-4 * scale)
         assert np.allclose(sc[qi], full[idx[qi]], rtol=0, atol=1e-4 * scale)
         say(f"  query {qi}: top-{topk} agree on {len(set(idx[qi]) & set(order))}/{topk} indices")
+
+
+def test_max_context_decode_attention(B):
+    # the longest context one decode call takes: 1024 chunks (2^20 positions at
+    # four query heads per KV head), on oracle-encoded K and V so that the
+    # comparison isolates the attention kernels; one position more is refused
+    # (tested with the other argument errors)
+    hq, hkv, d = 4, 1, 128
+    ctx = 1024 * B.tq_decode_attn_chunk(hq, hkv)
+    say(f"decode attention at the maximum context {ctx}")
+    gc = B.tq_codec_create(d, 3, 0, I.CODEC_SEED)
+    oc = O.make_codec(d, 3, seed=I.CODEC_SEED)
+    rng = np.random.default_rng(2024)
+    kr = O.encode(oc, rng.standard_normal((ctx, d)))   # the same records serve as K and V
+    for key in ("y", "idx", "z", "r"):
+        kr.pop(key)
+    vr = kr
+    q = O.bf16_round(rng.standard_normal((1, hq, d)).astype(np.float32))
+    out = B.tq_decode_attn(gc, gc, dev_tensor(q, "bf16"), B.packed_from_numpy(kr), B.packed_from_numpy(vr), ctx,
+                           hkv, 1 / math.sqrt(d), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.decode_attn_accumulated(oc, oc, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, 1 / math.sqrt(d))
+    err = row_rel_err(out.cpu().numpy(), ref).max()
+    say(f"  max row err {err:.2e}")
+    assert err <= 1e-4

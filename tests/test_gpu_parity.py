@@ -929,4 +929,14 @@ def test_invalid_arguments_rejected(B):
     st = lib.tq_decode_attn(gc.handle, gc.handle, q.data_ptr(), 0, 1, 6, 3, kp.c(), kp.c(), 0, 1.0, lg.data_ptr(), 0,
                             ws.data_ptr(), ws.numel(), None)
     assert st == 1
+    # contexts past the supported maxima are refused before any launch (nothing is read):
+    # logits index keys in 32 bits; one decode call takes at most 1024 chunks
+    st = lib.tq_attn_logits(gc.handle, q.data_ptr(), 0, 1, 6, 3, 1, kp.c(), 1 << 31, lg.data_ptr(), ws.data_ptr(),
+                            ws.numel(), None)
+    assert st == 2
+    q4 = torch.zeros((1, 4, 128), device="cuda")
+    chunk = B.tq_decode_attn_chunk(4, 1)
+    st = lib.tq_decode_attn(gc.handle, gc.handle, q4.data_ptr(), 0, 1, 4, 1, kp.c(), kp.c(), 1024 * chunk + 1, 1.0,
+                            lg.data_ptr(), 0, ws.data_ptr(), ws.numel(), None)
+    assert st == 2
     torch.cuda.synchronize()
