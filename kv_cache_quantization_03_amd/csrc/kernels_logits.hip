@@ -89,18 +89,24 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // so ŷ costs about four multiplications per pair.  The query values are the
 // same for every thread of the block, so they are read as scalar operands;
 // the loops are unrolled, so every code's slot and bit are constants.  Up to
-// 4 query vectors per block (grid.z splits the rest).
+// 4 query vectors per block (grid.z splits the rest).  The QJL sums
+// Σ_{τ_i = +1} p_i come from tables in LDS: for each byte g of the 128 sign
+// bits and each of its 256 values, the four vectors' sums of p over the set
+// bits (built once per block of 1024 keys), so a key takes 16 table reads
+// instead of 128 multiply-adds per vector.
 // ----------------------------------------------------------------------------
-constexpr int kPolarKeys = 256;
+constexpr int kPolarKeys = 1024;
 
 template <int B>
-__global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
+__global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
                                                            const float* __restrict__ proj, int Hq, int nq, int G,
                                                            int nkv, int64_t ctx, tq_packed_t k,
                                                            float* __restrict__ logits) {
   constexpr int d = 128, NL = 1 << B;
-  __shared__ float2 tab[7][NL];  // (cos, sin) of every level's centroids
-  __shared__ float psum[4];      // Σ_i p_i of each tile vector
+  __shared__ float2 tab[7][NL];     // (cos, sin) of every level's centroids
+  __shared__ float psum[4];         // Σ_i p_i of each tile vector
+  __shared__ float4 pj[d];          // p_j of the four tile vectors
+  __shared__ float4 ptab[16][256];  // [byte g][value]: Σ over the set bits k of p_{8g+k}
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
@@ -118,9 +124,23 @@ __global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarPar
     orow[t] = ok ? ((static_cast<int64_t>(b) * Hq + h) * nq + qi) * ctx : -1;
   }
   if (tid < 7 * NL) tab[tid / NL][tid % NL] = float2{PP.cosc[tid / NL][tid % NL], PP.sinc[tid / NL][tid % NL]};
-  {
+  if (wv < 4) {
     const float s = wave_sum(pp[wv][lane] + pp[wv][lane + 64]);  // wave w: tile vector w
     if (lane == 0) psum[wv] = s;
+  }
+  if (tid < d) pj[tid] = float4{pp[0][tid], pp[1][tid], pp[2][tid], pp[3][tid]};
+  __syncthreads();
+  for (int e = tid; e < 16 * 256; e += kPolarKeys) {
+    const int g = e >> 8, v = e & 255;
+    float4 a = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      if ((v >> kb) & 1) {
+        const float4 x = pj[8 * g + kb];
+        a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      }
+    }
+    ptab[g][v] = a;
   }
   __syncthreads();
   const int64_t key = static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid;
@@ -166,15 +186,9 @@ __global__ __launch_bounds__(256) void logits_polar_kernel(DevParams P, PolarPar
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 0; j < d; ++j) {
-    const float bit = static_cast<float>((sw[j >> 5] >> (j & 31)) & 1u);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) qj[t] = fmaf(pp[t][j], bit, qj[t]);
-    if ((j & 7) == 7) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(qj[t]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int g = 0; g < 16; ++g) {
+    const float4 x = ptab[g][(sw[g >> 2] >> (8 * (g & 3))) & 255u];
+    qj[0] += x.x; qj[1] += x.y; qj[2] += x.z; qj[3] += x.w;
   }
   const float nu = k.norm[row], ga = k.rnorm[row];
 #pragma unroll
@@ -191,7 +205,7 @@ hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, i
   const dim3 grid(static_cast<unsigned>(ceil_div(ctx, kPolarKeys)), batch * n_kv_heads,
                   static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_queries) * G, 4)));
   auto go = [&]<int B>() -> hipError_t {
-    hipLaunchKernelGGL((logits_polar_kernel<B>), grid, dim3(256), 0, s, c->prm, c->pol, qrot, proj, n_q_heads,
+    hipLaunchKernelGGL((logits_polar_kernel<B>), grid, dim3(kPolarKeys), 0, s, c->prm, c->pol, qrot, proj, n_q_heads,
                        n_queries, G, n_kv_heads, ctx, k, logits);
     return hipGetLastError();
   };
