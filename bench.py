@@ -64,7 +64,7 @@ def _cpu_model() -> str:
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc"))):
-        if f.startswith("kernels_logits") or f == "mfma_common.h" or f == "kernels_common.h":
+        if f in ("kernels_logits_mfma.hip", "mfma_common.h", "kernels_common.h"):  # the fused logits kernel's sources
             h.update(open(os.path.join(ROOT, "kv_cache_quantization_03_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
