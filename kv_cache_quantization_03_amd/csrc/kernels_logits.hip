@@ -93,7 +93,10 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // Σ_{τ_i = +1} p_i come from tables in LDS: for each byte g of the 128 sign
 // bits and each of its 256 values, the four vectors' sums of p over the set
 // bits (built once per block of 1024 keys), so a key takes 16 table reads
-// instead of 128 multiply-adds per vector.
+// instead of 128 multiply-adds per vector.  Likewise the level-1 pair i with
+// code c contributes r_i (q'_2i cos θ_c + q'_2i+1 sin θ_c) to each vector's
+// MSE sum, r_i the product of the upper levels' factors: the bracket is read
+// from a table of the four vectors' values for every (pair, code).
 // ----------------------------------------------------------------------------
 constexpr int kPolarKeys = 1024;
 
@@ -107,6 +110,7 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
   __shared__ float psum[4];         // Σ_i p_i of each tile vector
   __shared__ float4 pj[d];          // p_j of the four tile vectors
   __shared__ float4 ptab[16][256];  // [byte g][value]: Σ over the set bits k of p_{8g+k}
+  __shared__ float4 qtab[64][NL];   // [pair i][code c]: q'_2i cos θ_c + q'_2i+1 sin θ_c
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
@@ -129,6 +133,12 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     if (lane == 0) psum[wv] = s;
   }
   if (tid < d) pj[tid] = float4{pp[0][tid], pp[1][tid], pp[2][tid], pp[3][tid]};
+  if (tid < 64 * NL) {
+    const int i = tid / NL, c = tid % NL;
+    const float cs = PP.cosc[0][c], sn = PP.sinc[0][c];
+    qtab[i][c] = float4{fmaf(qp[0][2 * i + 1], sn, qp[0][2 * i] * cs), fmaf(qp[1][2 * i + 1], sn, qp[1][2 * i] * cs),
+                        fmaf(qp[2][2 * i + 1], sn, qp[2][2 * i] * cs), fmaf(qp[3][2 * i + 1], sn, qp[3][2 * i] * cs)};
+  }
   __syncthreads();
   for (int e = tid; e < 16 * 256; e += kPolarKeys) {
     const int g = e >> 8, v = e & 255;
@@ -175,10 +185,11 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
       const float2 cs = tab[lv - 1][code(slot)];
       prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
     }
-    const float2 c1 = tab[0][code(i)];
-    const float y0 = prod[2] * c1.x, y1 = prod[2] * c1.y;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) mse[t] = fmaf(qp[t][2 * i + 1], y1, fmaf(qp[t][2 * i], y0, mse[t]));
+    const float4 b = qtab[i][code(i)];
+    mse[0] = fmaf(prod[2], b.x, mse[0]);
+    mse[1] = fmaf(prod[2], b.y, mse[1]);
+    mse[2] = fmaf(prod[2], b.z, mse[2]);
+    mse[3] = fmaf(prod[2], b.w, mse[3]);
     // one pair's work stays together: without these the compiler keeps all
     // 128 ŷ values live and forms the dot products afterwards (256 registers)
 #pragma unroll
