@@ -96,7 +96,9 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // instead of 128 multiply-adds per vector.  Likewise the level-1 pair i with
 // code c contributes r_i (q'_2i cos θ_c + q'_2i+1 sin θ_c) to each vector's
 // MSE sum, r_i the product of the upper levels' factors: the bracket is read
-// from a table of the four vectors' values for every (pair, code).
+// from a table of the four vectors' values for every (pair, code); with at
+// most 4 codes per angle the same is done one level up, per (level-2 node,
+// its code, its two pairs' codes).
 // ----------------------------------------------------------------------------
 constexpr int kPolarKeys = 1024;
 
@@ -111,6 +113,9 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
   __shared__ float4 pj[d];          // p_j of the four tile vectors
   __shared__ float4 ptab[16][256];  // [byte g][value]: Σ over the set bits k of p_{8g+k}
   __shared__ float4 qtab[64][NL];   // [pair i][code c]: q'_2i cos θ_c + q'_2i+1 sin θ_c
+  constexpr bool L2T = NL <= 4;     // level-2 table: 32 nodes x NL^3 entries
+  constexpr int N3 = L2T ? NL * NL * NL : 1;
+  __shared__ float4 q2tab[L2T ? 32 : 1][N3];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
@@ -152,6 +157,16 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     }
     ptab[g][v] = a;
   }
+  if constexpr (L2T) {
+    // node n, codes (c2, ca, cb): cos θ2_c2 · qtab[2n][ca] + sin θ2_c2 · qtab[2n+1][cb]
+    for (int e = tid; e < 32 * N3; e += kPolarKeys) {
+      const int n = e / N3, r = e % N3, c2 = r / (NL * NL), ca = (r / NL) % NL, cb = r % NL;
+      const float cs = PP.cosc[1][c2], sn = PP.sinc[1][c2];
+      const float4 a = qtab[2 * n][ca], b = qtab[2 * n + 1][cb];
+      q2tab[n][r] = float4{fmaf(sn, b.x, cs * a.x), fmaf(sn, b.y, cs * a.y), fmaf(sn, b.z, cs * a.z),
+                           fmaf(sn, b.w, cs * a.w)};
+    }
+  }
   __syncthreads();
   const int64_t key = static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid;
   if (key >= ctx) return;
@@ -173,8 +188,30 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
   float mse[4] = {0.f, 0.f, 0.f, 0.f}, qj[4] = {0.f, 0.f, 0.f, 0.f};
   float prod[9];  // prod[lv]: product of the factors of levels 7..lv along the current path
   prod[8] = 1.f;
+  if constexpr (L2T) {
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
+    for (int n = 0; n < 32; ++n) {
+      // levels whose factor changes at level-2 node n: lv <= ctz(n) + 3 (all at n = 0)
+      const int hi = n == 0 ? 7 : (__builtin_ctz(n) + 3 < 7 ? __builtin_ctz(n) + 3 : 7);
+#pragma unroll
+      for (int lv = 7; lv >= 3; --lv) {
+        if (lv > hi) continue;
+        const int node = n >> (lv - 2), side = (n >> (lv - 3)) & 1;
+        const float2 cs = tab[lv - 1][code(128 - (256 >> lv) + node)];
+        prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
+      }
+      const float4 b = q2tab[n][(code(64 + n) * NL + code(2 * n)) * NL + code(2 * n + 1)];
+      mse[0] = fmaf(prod[3], b.x, mse[0]);
+      mse[1] = fmaf(prod[3], b.y, mse[1]);
+      mse[2] = fmaf(prod[3], b.z, mse[2]);
+      mse[3] = fmaf(prod[3], b.w, mse[3]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(mse[t]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < (L2T ? 0 : 64); ++i) {
     // levels whose factor changes at pair i: lv <= ctz(i) + 2 (all at i = 0)
     const int hi = i == 0 ? 7 : (__builtin_ctz(i) + 2 < 7 ? __builtin_ctz(i) + 2 : 7);
 #pragma unroll
