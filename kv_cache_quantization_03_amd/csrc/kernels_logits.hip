@@ -158,9 +158,17 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     ptab[g][v] = a;
   }
   if constexpr (L2T) {
-    // node n, codes (c2, ca, cb): cos θ2_c2 · qtab[2n][ca] + sin θ2_c2 · qtab[2n+1][cb]
+    // node n, codes (c2, ca, cb): cos θ2_c2 · qtab[2n][ca] + sin θ2_c2 · qtab[2n+1][cb].
+    // Entry r = c2·4^B + Σ_p q_p·4^p with q_p the two bits of plane p at the
+    // slots 2n, 2n+1 (bit 0: pair 2n), so a key forms r with one extract per plane.
     for (int e = tid; e < 32 * N3; e += kPolarKeys) {
-      const int n = e / N3, r = e % N3, c2 = r / (NL * NL), ca = (r / NL) % NL, cb = r % NL;
+      const int n = e / N3, r = e % N3, c2 = r >> (2 * B);
+      int ca = 0, cb = 0;
+#pragma unroll
+      for (int p = 0; p < B; ++p) {
+        ca |= ((r >> (2 * p)) & 1) << p;
+        cb |= ((r >> (2 * p + 1)) & 1) << p;
+      }
       const float cs = PP.cosc[1][c2], sn = PP.sinc[1][c2];
       const float4 a = qtab[2 * n][ca], b = qtab[2 * n + 1][cb];
       q2tab[n][r] = float4{fmaf(sn, b.x, cs * a.x), fmaf(sn, b.y, cs * a.y), fmaf(sn, b.z, cs * a.z),
@@ -200,7 +208,10 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
         const float2 cs = tab[lv - 1][code(128 - (256 >> lv) + node)];
         prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
       }
-      const float4 b = q2tab[n][(code(64 + n) * NL + code(2 * n)) * NL + code(2 * n + 1)];
+      int r = code(64 + n) << (2 * B);
+#pragma unroll
+      for (int p = 0; p < B; ++p) r |= static_cast<int>((w[p][n >> 4] >> (2 * (n & 15))) & 3u) << (2 * p);
+      const float4 b = q2tab[n][r];
       mse[0] = fmaf(prod[3], b.x, mse[0]);
       mse[1] = fmaf(prod[3], b.y, mse[1]);
       mse[2] = fmaf(prod[3], b.z, mse[2]);
