@@ -691,7 +691,7 @@ def cpu_baseline(w, k_host, q_host, bits):
     rec = O.encode(oc, k64)
     enc_s = time.perf_counter() - t
     reps, tot = 0, 0.0
-    while tot < 8.0 and reps < 5:
+    while tot < 10.0 and reps < 20:
         t = time.perf_counter()
         O.attn_logits(oc, q_host.astype(np.float64), rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1, w["ctx"])
         tot += time.perf_counter() - t
