@@ -326,6 +326,26 @@ tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const void* q, tq
                                  float v_gate, void* out, tq_dtype_t out_dt, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Logits over a paged cache (the layout of tq_decode_attn_paged: page p holds,
+ * for KV head kh, rows (p * n_kv_heads + kh) * page_size + slot;
+ * page_table[b][i] names the page of positions [i*page_size, (i+1)*page_size)
+ * of sequence b).  q and the logits as tq_attn_logits with max_ctx as the
+ * context: logits [batch][n_q_heads][n_queries][max_ctx] fp32; sequence b
+ * scores its first min(ctx_lens[b], max_ctx) positions, and the logits of the
+ * positions past them are not written.  Needs a per-coordinate two-stage
+ * codec with head_dim 128 or 256, page_size a positive multiple of 128 and
+ * 1 <= max_ctx <= max_pages * page_size (else an error, no launch).
+ * ctx_lens [batch] and page_table [batch][max_pages] are device int32 arrays
+ * that must hold valid page ids for every position below ctx_lens[b].
+ * Workspace: tq_attn_logits_paged_workspace(...) bytes, 16-byte aligned. */
+size_t tq_attn_logits_paged_workspace(tq_codec_t c, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t n_queries);
+tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t n_queries, tq_packed_t k_cache,
+                                 const int32_t* ctx_lens, const int32_t* page_table, int32_t max_pages,
+                                 int32_t page_size, int64_t max_ctx, float* logits, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* ---------------------------------------------------------------- search
  * Exhaustive inner-product search over a compressed database
  * (深度拆解 第三部分 向量搜索: the compressed vectors are the index; nothing

@@ -71,6 +71,9 @@ def _load():
         "tq_encode_append_paged_workspace": (sz, [vp, i32, i32, i32]),
         "tq_encode_append_paged": (C.c_int, [vp, vp, C.c_int, i32, i32, i32, vp, vp, i32, i32, i32, P, vp, sz, vp]),
         "tq_decode_attn_paged_workspace": (sz, [vp, vp, i32, i32, i32, i64]),
+        "tq_attn_logits_paged_workspace": (sz, [vp, i32, i32, i32, i32]),
+        "tq_attn_logits_paged": (C.c_int, [vp, vp, C.c_int, i32, i32, i32, i32, P, vp, vp, i32, i32, i64, vp, vp, sz,
+                                           vp]),
         "tq_decode_attn_paged": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, vp, vp, i32, i32, i64,
                                            C.c_float, C.c_float, vp, C.c_int, vp, sz, vp]),
         "tq_search_workspace": (sz, [vp, i64, i32, i32]),
@@ -91,7 +94,7 @@ EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_bui
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
             "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
-            "tq_decode_attn_paged",
+            "tq_decode_attn_paged", "tq_attn_logits_paged_workspace", "tq_attn_logits_paged",
             "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
 
 
@@ -388,6 +391,23 @@ def tq_decode_attn_paged(ck: Codec, cv: Codec, q, k_cache: Packed, v_cache: Pack
                                   ws.numel(), _stream(q))
     _check(st, "tq_decode_attn_paged")
     return out
+
+
+def tq_attn_logits_paged(codec: Codec, q, k_cache: Packed, ctx_lens, page_table, page_size: int, max_ctx: int,
+                         n_kv_heads: int, logits=None, ws=None):
+    """q: [batch][n_queries][n_q_heads][d]; returns logits [batch][n_q_heads][n_queries][max_ctx] (fp32);
+    positions at or past ctx_lens[b] are not written."""
+    torch = _torch()
+    batch, nq, hq, d = q.shape
+    if logits is None:
+        logits = torch.zeros((batch, hq, nq, max_ctx), dtype=torch.float32, device=q.device)
+    need = lib.tq_attn_logits_paged_workspace(codec.handle, batch, hq, n_kv_heads, nq)
+    ws = ws if ws is not None else _workspace(need, q.device)
+    st = lib.tq_attn_logits_paged(codec.handle, _ptr(q), _dt(q), batch, hq, n_kv_heads, nq, k_cache.c(),
+                                  _ptr(ctx_lens), _ptr(page_table), page_table.shape[1], page_size, max_ctx,
+                                  _ptr(logits), _ptr(ws), ws.numel(), _stream(q))
+    _check(st, "tq_attn_logits_paged")
+    return logits
 
 
 # ---------------------------------------------------------------- search

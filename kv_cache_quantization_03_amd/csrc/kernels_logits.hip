@@ -281,7 +281,8 @@ size_t logits_mfma_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n
 hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                    int n_kv_heads, int n_queries, void* ws, hipStream_t s);
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
-                              int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+                              int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s,
+                              const PageMap* pm = nullptr);
 bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries,
                            int64_t ctx);
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
@@ -337,6 +338,24 @@ hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch,
   hipLaunchKernelGGL(logits_valu_kernel, grid, dim3(256), 0, s, P, qrot, proj, n_q_heads, n_queries, G,
                      n_kv_heads, ctx, k, logits);
   return hipGetLastError();
+}
+
+// Paged cache: the query operands, then the matrix-core scorer reading each
+// 64-key group from its page (per-sequence context lengths).
+bool logits_paged_supported(const tq_codec_s* c) {
+  return !c->polar && c->qjl && (c->prm.d == 128 || c->prm.d == 256) && c->prm.m == c->prm.d;
+}
+
+size_t logits_paged_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
+  return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
+}
+
+hipError_t launch_logits_paged(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                               int n_kv_heads, int n_queries, tq_packed_t k, int64_t max_ctx, const PageMap& pm,
+                               float* logits, void* ws, hipStream_t s) {
+  hipError_t e = launch_logits_mfma_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_logits_mfma(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, max_ctx, logits, s, &pm);
 }
 
 // Scores of nq prepped query vectors against n packed rows: scores[q][t].

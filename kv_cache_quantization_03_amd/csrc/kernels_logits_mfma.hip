@@ -284,13 +284,17 @@ hipError_t launch_qprep128(const tq_codec_s* c, const void* q, tq_dtype_t dt, in
 // read once from `prep`; the next group's records load while the current one
 // is scored.
 // ----------------------------------------------------------------------------
-template <int NP, int WB, int NMT, int WAVES, int NG>
+// PAGED: the keys of (batch b, KV head kh) live in the pages of a paged cache
+// (see PageMap; page_size a multiple of 64, so a 64-key group lies in one
+// page); sequence b scores its first ctx_lens[b] keys, and ctx is the row
+// stride of the logits.
+template <int NP, int WB, int NMT, int WAVES, int NG, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* __restrict__ prep, int n_mt, int ctx,
                                                                  const uint32_t* __restrict__ codes,
                                                                  const uint32_t* __restrict__ signs,
                                                                  const float* __restrict__ norm,
                                                                  const float* __restrict__ rnorm, float kappa,
-                                                                 float* __restrict__ logits) {
+                                                                 float* __restrict__ logits, PageMap pm, int nkv) {
   using L = RecLayout<NP, WB>;
   constexpr int NKB = L::NKB;
   constexpr int MT_BYTES = NKB * kOpBytes + kConstBytes;
@@ -300,14 +304,20 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
   const int g = lane >> 4;
   const int bk = blockIdx.y;
   const int key0 = (blockIdx.x * WAVES + wv) * (NG * kKeysPerWave);
-  if (key0 >= ctx) return;  // wave-uniform
+  int ctx_v = ctx;  // keys to score in this row
+  if constexpr (PAGED) ctx_v = max(0, min(min(pm.ctx_lens[bk / nkv], ctx), pm.max_pages * pm.page_size));
+  if (key0 >= ctx_v) return;  // wave-uniform
   v4u cv[2][L::CW / 4], sv[2][L::SW / 4];
   float nu_l[2], ga_l[2];
   auto load_group = [&](int i, int buf) {
     const int k0 = key0 + i * kKeysPerWave;
-    const int64_t r0 = static_cast<int64_t>(bk) * ctx + k0;
+    int64_t r0 = static_cast<int64_t>(bk) * ctx + k0;
+    if constexpr (PAGED) {
+      const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + k0 / pm.page_size];
+      r0 = (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + k0 % pm.page_size;
+    }
     load_wave_records<NP, WB>(cv[buf], sv[buf], nu_l[buf], ga_l[buf], codes + r0 * L::CW, signs + r0 * L::SW,
-                              norm + r0, rnorm + r0, min(kKeysPerWave, ctx - k0), lane);
+                              norm + r0, rnorm + r0, min(kKeysPerWave, ctx_v - k0), lane);
   };
   load_group(0, 0);
 
@@ -334,13 +344,13 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
 #pragma unroll
   for (int i = 0; i < NG; ++i) {
     const int k0 = key0 + i * kKeysPerWave;
-    if (k0 >= ctx) break;  // wave-uniform
-    if (i + 1 < NG && k0 + kKeysPerWave < ctx) load_group(i + 1, (i + 1) & 1);
+    if (k0 >= ctx_v) break;  // wave-uniform
+    if (i + 1 < NG && k0 + kKeysPerWave < ctx_v) load_group(i + 1, (i + 1) & 1);
     float* oi[NMT];
 #pragma unroll
     for (int j = 0; j < NMT; ++j) oi[j] = out[j] ? out[j] + i * kKeysPerWave : nullptr;
     score_wave<NP, WB, NMT>(cv[i & 1], sv[i & 1], nu_l[i & 1], ga_l[i & 1], s_codes[wv], s_signs[wv], a, cst, oi,
-                            min(kKeysPerWave, ctx - k0), kappa, lane);
+                            min(kKeysPerWave, ctx_v - k0), kappa, lane);
     __builtin_amdgcn_wave_barrier();  // the next group's LDS staging follows this group's reads
   }
 }
@@ -462,7 +472,9 @@ static int device_cu_count() {
 }
 
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
-                              int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+                              int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s,
+                              const PageMap* pm) {
+  const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   const int G = n_q_heads / n_kv_heads;
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
   auto go = [&]<int NP, int WB, int NMT>() -> hipError_t {
@@ -470,9 +482,14 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
     auto launch = [&]<int NG>() -> hipError_t {
       const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * NG * kKeysPerWave)), batch * n_kv_heads,
                       static_cast<unsigned>(ceil_div(n_mt, NMT)));
-      hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG>), grid, dim3(WAVES * 64), 0, s,
-                         static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                         k.rnorm, c->prm.qjl_kappa, logits);
+      if (pm)
+        hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG, true>), grid, dim3(WAVES * 64), 0, s,
+                           static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
+                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads);
+      else
+        hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG, false>), grid, dim3(WAVES * 64), 0, s,
+                           static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
+                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads);
       return hipGetLastError();
     };
     // Four groups per wave read the operands once per 256 keys (measured 49.8

@@ -348,6 +348,56 @@ extern "C" tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const 
                        v_gate > 0.f, v_gate, &pm, out, out_dt, ws, ws_bytes, stream, "tq_decode_attn_paged");
 }
 
+extern "C" size_t tq_attn_logits_paged_workspace(tq_codec_t c, int32_t batch, int32_t n_q_heads,
+                                                 int32_t n_kv_heads, int32_t n_queries) {
+  if (!c || batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_queries < 0 || !tq::logits_paged_supported(c)) return 0;
+  return tq::logits_paged_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
+}
+
+extern "C" tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtype_t q_dt, int32_t batch,
+                                            int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
+                                            tq_packed_t k_cache, const int32_t* ctx_lens, const int32_t* page_table,
+                                            int32_t max_pages, int32_t page_size, int64_t max_ctx, float* logits,
+                                            void* ws, size_t ws_bytes, void* stream) {
+  tq::clear_error();
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
+  tq_status_t st = need_qjl(c, "tq_attn_logits_paged");
+  if (st != TQ_SUCCESS) return st;
+  if (!tq::logits_paged_supported(c)) {
+    set_error("paged logits need a per-coordinate codec with head_dim 128 or 256 and qjl_dim = head_dim");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
+  if (n_queries < 0) { set_error("n_queries must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (max_pages <= 0 || page_size <= 0 || page_size % 128 != 0) {
+    set_error("need max_pages > 0 and page_size a positive multiple of 128");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (max_ctx < 1 || max_ctx > static_cast<int64_t>(max_pages) * page_size) {
+    set_error("need 1 <= max_ctx <= max_pages * page_size");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (max_ctx > kMaxLogitsCtx) { set_error("max_ctx must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
+  if (batch == 0 || n_queries == 0) return TQ_SUCCESS;
+  if (!q || !logits || !ctx_lens || !page_table) {
+    set_error("q, logits, ctx_lens or page_table is NULL");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (!aligned(q, dtype_size(q_dt)) || !aligned(logits, 4) || !aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
+    set_error("q, logits, ctx_lens or page_table misaligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  if ((st = check_packed(k_cache, "k_cache")) != TQ_SUCCESS) return st;
+  if ((st = check_ws(ws, ws_bytes, tq::logits_paged_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) !=
+      TQ_SUCCESS)
+    return st;
+  const tq::PageMap pm{page_table, ctx_lens, max_pages, page_size};
+  hipError_t e = tq::launch_logits_paged(c, q, q_dt, batch, n_q_heads, n_kv_heads, n_queries, k_cache, max_ctx, pm,
+                                         logits, ws, static_cast<hipStream_t>(stream));
+  return finish(e, "tq_attn_logits_paged launch");
+}
+
 // ---------------------------------------------------------------- search
 extern "C" size_t tq_search_workspace(tq_codec_t c, int64_t n_db, int32_t n_queries, int32_t topk) {
   if (!c || n_db < 0 || n_queries < 0 || topk < 1) return 0;

@@ -121,6 +121,11 @@ hipError_t launch_qprep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int64
 // Logits for the [batch][n_q_heads][n_queries][ctx] layout (prepped queries
 // in ws).
 size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
+bool logits_paged_supported(const tq_codec_s* c);
+size_t logits_paged_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
+hipError_t launch_logits_paged(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
+                               int n_kv_heads, int n_queries, tq_packed_t k, int64_t max_ctx, const PageMap& pm,
+                               float* logits, void* ws, hipStream_t s);
 hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                          int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
                          void* ws, hipStream_t s);

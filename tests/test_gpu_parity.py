@@ -706,6 +706,62 @@ def test_mse_codec_is_a_value_codec_only(B):
     assert out.shape == (1, 4, 128)
 
 
+@pytest.mark.parametrize("d,bits,hq,hkv,nq,P", [(128, 3, 8, 2, 2, 256), (128, 4, 4, 4, 1, 128), (256, 3, 2, 1, 5, 384)])
+def test_logits_paged_parity(B, d, bits, hq, hkv, nq, P):
+    # sequences of different lengths (one empty, one of a single key, one filling
+    # its page table) in shuffled pages with junk elsewhere; logits past a
+    # sequence's length stay untouched
+    say(f"paged logits d={d} bits={bits} hq={hq} hkv={hkv} nq={nq} P={P}")
+    gc, oc = pair(B, d, bits)
+    max_pages = 4
+    max_ctx = max_pages * P
+    ctxs = [2 * max_ctx // 3 + 3, 1, 0, max_ctx]      # a ragged one, one key, none, the whole table
+    batch = len(ctxs)
+    n_pages = batch * max_pages + 2
+    rng = np.random.default_rng(61 + d + bits)
+    pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    krec = [O.encode(oc, rng.standard_normal((hkv * n, d))) if n else None for n in ctxs]
+    junk = O.encode(oc, rng.standard_normal((40, d)))
+    empty = {k: np.asarray(junk[k])[:0] for k in junk}
+    kc = _fill_pages([r if r is not None else empty for r in krec], pt, hkv, P, n_pages, junk)
+    q = as_exact(rng.standard_normal((batch, nq, hq, d)), "f32")
+    out = torch.full((batch, hq, nq, max_ctx), 7.0, device="cuda")
+    B.tq_attn_logits_paged(gc, to_dev(q, "f32"), B.packed_from_numpy(kc),
+                           torch.tensor(ctxs, dtype=torch.int32, device="cuda"), torch.from_numpy(pt).cuda(), P,
+                           max_ctx, hkv, logits=out)
+    g = out.cpu().numpy()
+    for b, n in enumerate(ctxs):
+        assert np.all(g[b, :, :, n:] == 7.0)
+        if n == 0:
+            continue
+        kr = O.gather_paged(kc, pt, b, hkv, n, P)
+        ref = O.attn_logits(oc, q[b:b + 1].astype(np.float64), kr, 1, hq, hkv, nq, n)
+        err = row_rel_err(g[b:b + 1, :, :, :n], ref).max()
+        say(f"  sequence {b} (ctx {n}): max row err {err:.2e}")
+        assert err <= 1e-4
+
+
+def test_logits_paged_identity_equals_contiguous(B):
+    # one KV head and the identity page table: the paged layout is the
+    # contiguous one, and the logits equal tq_attn_logits' bit for bit
+    gc, _ = pair(B, 128, 3)
+    ctx, P = 3000, 1024
+    rng = np.random.default_rng(62)
+    kp, _ = B.tq_encode_kv(gc, to_dev(as_exact(rng.standard_normal((ctx, 128)), "bf16"), "bf16"))
+    q = to_dev(as_exact(rng.standard_normal((1, 3, 4, 128)), "bf16"), "bf16")
+    a = B.tq_attn_logits(gc, q, kp, ctx, 1)
+    pt = torch.arange(3, dtype=torch.int32, device="cuda").view(1, 3)
+    b = B.tq_attn_logits_paged(gc, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
+    assert torch.equal(a, b)
+    # refused: page sizes that are not multiples of 128, max_ctx past the table, polar and MSE-only codecs
+    for bad in ((100, ctx), (P, 3 * P + 1)):
+        with pytest.raises(B.TQError):
+            B.tq_attn_logits_paged(gc, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, *bad, 1)
+    gv, _ = mse_pair(B, 128, 3)
+    with pytest.raises(B.TQError):
+        B.tq_attn_logits_paged(gv, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
+
+
 def test_decode_paged_identity_equals_contiguous(B):
     # one KV head and the identity page table: the paged layout is the
     # contiguous one, and the output is bitwise that of tq_decode_attn
