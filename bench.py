@@ -459,6 +459,26 @@ def paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d):
     ms = _time(paged, 30, graph=True)
     res["decode_attn_c4_paged256"] = {"ms": ms, "page_size": P, "buffer_sets": len(psets),
                                       **_hbm(ms, 2 * hkv * ctx * codec3.record_bytes + 2 * hq * d * 2)}
+    # logits of one decode step over the same paged K caches, and over the contiguous ones
+    ql = qd.view(1, 1, hq, d)
+    lg = torch.empty((1, hq, 1, ctx), dtype=torch.float32, device=dev)
+    wsl = torch.empty(max(B.lib.tq_attn_logits_paged_workspace(codec3.handle, 1, hq, hkv, 1),
+                          B.tq_attn_logits_workspace(codec3, 1, hq, hkv, 1), 1), dtype=torch.uint8, device=dev)
+    it2 = iter(range(10 ** 9))
+
+    def logits_paged():
+        kk = psets[next(it2) % len(psets)][0]
+        B.tq_attn_logits_paged(codec3, ql, kk, cl, pt, P, ctx, hkv, logits=lg, ws=wsl)
+
+    def logits_contig():
+        kk = dsets[next(it2) % len(dsets)][0]
+        B.tq_attn_logits(codec3, ql, kk, ctx, hkv, logits=lg, ws=wsl)
+    for name, fn in (("logits_c4_paged256", logits_paged), ("logits_c4_contiguous", logits_contig)):
+        ms = _time(fn, 30, graph=True)
+        res[name] = {"ms": ms, "page_size": P if "paged" in name else None, "buffer_sets": len(psets),
+                     "scores_per_s": hq * ctx / (ms * 1e-3),
+                     **_hbm(ms, hkv * ctx * codec3.record_bytes + hq * ctx * 4 + hq * d * 2)}
+        print(f"[bench] {name} (one decode step, 128K keys) {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     print(f"[bench] C4 decode attention, 256-position pages {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     del psets
     # eight sequences of different lengths in one pool
