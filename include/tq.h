@@ -49,6 +49,16 @@
  *   rnorm[n] f32          γ = ||r|| of the unit-vector residual.
  * Bytes per vector: d·B/8 + 8 (3-bit, d=128: 48 + 8 = 56 B, vs 256 B of fp16).
  *
+ * Alignment.  The kernels move record words and input vectors with 16-byte
+ * loads and stores, so codes, signs and every input vector array (q, k, v, x,
+ * search queries) must be 16-byte aligned; ν, γ, logits and fp32 outputs
+ * 4-byte aligned; workspaces 16-byte aligned.  Any other pointer gives
+ * TQ_ERROR_MISALIGNED.  A row offset into a cache keeps 16-byte alignment
+ * whenever a row's code and sign words are multiples of 16 bytes (every
+ * head_dim >= 128); for head_dim 64 only even row offsets keep it.  The
+ * alignment of the array arguments is checked first, before the codec
+ * handle.
+ *
  * Errors.  Every call returns a tq_status_t and never throws.  Arguments are
  * validated on the host before any launch, so an invalid call has no side
  * effect.  tq_last_error() returns a thread-local message for the last failing
@@ -95,10 +105,10 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype_t;
  * Records of an MSE-only codec (tq_codec_create_mse) have no signs and no γ:
  * signs and rnorm are ignored and may be NULL. */
 typedef struct {
-  uint32_t* codes; /* [n][code_words], 4-byte aligned */
-  uint32_t* signs; /* [n][sign_words], 4-byte aligned */
-  float* norm;     /* [n] */
-  float* rnorm;    /* [n] */
+  uint32_t* codes; /* [n][code_words], 16-byte aligned */
+  uint32_t* signs; /* [n][sign_words], 16-byte aligned */
+  float* norm;     /* [n], 4-byte aligned */
+  float* rnorm;    /* [n], 4-byte aligned */
 } tq_packed_t;
 
 typedef struct {
@@ -181,8 +191,12 @@ tq_status_t tq_codec_destroy(tq_codec_t c);
 tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info);
 
 /* ---------------------------------------------------------------- encode
- * Compresses n_vec rows of k (and of v if v != NULL) with codec c.
- *   k, v : device [n_vec][d] in dtype dt (element-aligned).
+ * Compresses n_vec rows of k (and of v if v != NULL) with codec c: the
+ * two-stage encode of 深度拆解 第二部分 (random rotation, then the optimal
+ * scalar code of each rotated coordinate with no per-block constants, then
+ * the QJL sign bits of the projected residual), applied to the KV cache that
+ * 第一部分 (KV 缓存是什么) describes: every past token's K and V.
+ *   k, v : device [n_vec][d] in dtype dt, 16-byte aligned.
  *   k_out, v_out : device packed arrays with n_vec rows.  To append to an
  *          existing cache, offset each pointer by the first row to write.
  *   ws   : device workspace of at least tq_encode_workspace(c, n_vec) bytes,

@@ -310,7 +310,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
   const int bk = b * nkv + h / G, g = h % G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, j = tid % NV, qtr = tid / NV;
-  const int n_chunks = ctx_lens ? min(n_chunks_grid, (max(ctx_lens[b], 0) + chunk - 1) / chunk) : n_chunks_grid;
+  // (64-bit: a length near 2^31 must not wrap when rounded up)
+  const int n_chunks =
+      ctx_lens ? static_cast<int>(min(static_cast<int64_t>(n_chunks_grid),
+                                      (static_cast<int64_t>(max(ctx_lens[b], 0)) + chunk - 1) / chunk))
+               : n_chunks_grid;
   const int rec = 2 + NV;
   const float* base = part + (static_cast<int64_t>(bk) * n_chunks_grid * G + g) * rec;
   // unsigned 32-bit offsets from the block's base: the loads take the scalar base plus one offset register

@@ -105,9 +105,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
   const int64_t hrow = static_cast<int64_t>(bk) * ctx_max;     // first row of the head (contiguous cache)
   // the sequence's context: ctx_max for a contiguous cache; for a paged one its
-  // own length, clamped to the grid and to the page table
+  // own length, clamped to the grid (the host checks ctx_max <= max_pages *
+  // page_size, so the clamp keeps every position inside the page table)
   int ctx = ctx_max;
-  if constexpr (PAGED) ctx = max(0, min(min(pm.ctx_lens[bk / nkv], ctx_max), pm.max_pages * pm.page_size));
+  if constexpr (PAGED) ctx = max(0, min(pm.ctx_lens[bk / nkv], ctx_max));
   // a chunk past a shorter sequence's end: the combine reads only the chunks in use
   if (PAGED && chunk * kDecChunk >= ctx) return;  // block-uniform
   // Record rows.  Every key the wave touches, clamped to ctx - 1, lies in the

@@ -305,7 +305,9 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
   const int bk = blockIdx.y;
   const int key0 = (blockIdx.x * WAVES + wv) * (NG * kKeysPerWave);
   int ctx_v = ctx;  // keys to score in this row
-  if constexpr (PAGED) ctx_v = max(0, min(min(pm.ctx_lens[bk / nkv], ctx), pm.max_pages * pm.page_size));
+  // paged: the sequence's own length, clamped to max_ctx (ctx here), which the
+  // host bounds by max_pages * page_size
+  if constexpr (PAGED) ctx_v = max(0, min(pm.ctx_lens[bk / nkv], ctx));
   if (key0 >= ctx_v) return;  // wave-uniform
   v4u cv[2][L::CW / 4], sv[2][L::SW / 4];
   float nu_l[2], ga_l[2];

@@ -44,6 +44,20 @@ size_t dtype_size(tq_dtype_t dt) { return dt == TQ_F32 ? 4 : 2; }
 
 bool valid_dtype(tq_dtype_t dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
 
+// The kernels read and write record words and input vectors with 16-byte
+// vector loads and stores, so codes, signs and the q/k/v/x arrays must be
+// 16-byte aligned; ν and γ are read as floats (4 bytes).  This check runs
+// first in every call that takes packed arrays, before the codec is looked
+// at, on every non-NULL pointer (a NULL one is reported later, once the codec
+// says whether the array is needed).
+tq_status_t check_packed_alignment(const tq_packed_t& p, const char* name) {
+  if (!aligned(p.codes, 16) || !aligned(p.signs, 16) || !aligned(p.norm, 4) || !aligned(p.rnorm, 4)) {
+    set_error(std::string(name) + ": codes and signs must be 16-byte aligned, norm and rnorm 4-byte aligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  return TQ_SUCCESS;
+}
+
 // Records of an MSE-only codec (qjl false) have no signs and no γ: those two
 // pointers are ignored and may be NULL.
 tq_status_t check_packed(const tq_packed_t& p, const char* name, bool qjl = true) {
@@ -51,12 +65,11 @@ tq_status_t check_packed(const tq_packed_t& p, const char* name, bool qjl = true
     set_error(std::string(name) + ": a packed array pointer is NULL");
     return TQ_ERROR_INVALID_VALUE;
   }
-  if (!aligned(p.codes, 4) || !aligned(p.norm, 4) || (qjl && (!aligned(p.signs, 4) || !aligned(p.rnorm, 4)))) {
-    set_error(std::string(name) + ": packed arrays must be 4-byte aligned");
-    return TQ_ERROR_MISALIGNED;
-  }
-  return TQ_SUCCESS;
+  return check_packed_alignment(p, name);
 }
+
+// Input vectors (q, k, v, x, search queries): 16-byte aligned, see above.
+bool vec_aligned(const void* p) { return aligned(p, 16); }
 
 tq_status_t check_ws(void* ws, size_t have, size_t need) {
   if (have < need) {
@@ -119,16 +132,16 @@ extern "C" tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, 
                                     int64_t n_vec, tq_packed_t k_out, tq_packed_t v_out, void* ws,
                                     size_t ws_bytes, void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(k_out, "k_out");
+  if (st != TQ_SUCCESS) return st;
+  if (v && (st = check_packed_alignment(v_out, "v_out")) != TQ_SUCCESS) return st;
+  if (!vec_aligned(k) || !vec_aligned(v)) { set_error("k/v must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(dt)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   if (n_vec < 0) { set_error("n_vec < 0"); return TQ_ERROR_INVALID_VALUE; }
   if (n_vec == 0) return TQ_SUCCESS;
   if (!k) { set_error("k is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(k, dtype_size(dt)) || (v && !aligned(v, dtype_size(dt)))) {
-    set_error("k/v must be aligned to their element size");
-    return TQ_ERROR_MISALIGNED;
-  }
-  tq_status_t st = check_packed(k_out, "k_out", c->qjl);
+  st = check_packed(k_out, "k_out", c->qjl);
   if (st != TQ_SUCCESS) return st;
   if (v && (st = check_packed(v_out, "v_out", c->qjl)) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::encode_ws_bytes(c, n_vec))) != TQ_SUCCESS) return st;
@@ -151,16 +164,18 @@ extern "C" tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_
                                       tq_packed_t k, int64_t ctx_len, float* logits, void* ws,
                                       size_t ws_bytes, void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(k, "k");
+  if (st != TQ_SUCCESS) return st;
+  if (!vec_aligned(q)) { set_error("q must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = need_qjl(c, "tq_attn_logits");
-  if (st != TQ_SUCCESS) return st;
+  if ((st = need_qjl(c, "tq_attn_logits")) != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
   if (batch == 0 || n_queries == 0 || ctx_len == 0) return TQ_SUCCESS;
   if (!q || !logits) { set_error("q or logits is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(q, dtype_size(q_dt)) || !aligned(logits, 4)) { set_error("q/logits misaligned"); return TQ_ERROR_MISALIGNED; }
+  if (!aligned(logits, 4)) { set_error("logits misaligned"); return TQ_ERROR_MISALIGNED; }
   if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) != TQ_SUCCESS) return st;
   if (log_enabled()) std::fprintf(stderr, "[tq] logits b=%d hq=%d hkv=%d nq=%d ctx=%lld\n", batch, n_q_heads, n_kv_heads, n_queries, (long long)ctx_len);
@@ -173,6 +188,7 @@ extern "C" tq_status_t tq_attn_query_prep(tq_codec_t c, const void* q, tq_dtype_
                                           int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries, void* prep,
                                           size_t prep_bytes, void* stream) {
   tq::clear_error();
+  if (!vec_aligned(q)) { set_error("q must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
   tq_status_t st = need_qjl(c, "tq_attn_query_prep");
@@ -181,7 +197,6 @@ extern "C" tq_status_t tq_attn_query_prep(tq_codec_t c, const void* q, tq_dtype_
   if (n_queries < 0) { set_error("n_queries must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (batch == 0 || n_queries == 0) return TQ_SUCCESS;
   if (!q) { set_error("q is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(q, dtype_size(q_dt))) { set_error("q misaligned"); return TQ_ERROR_MISALIGNED; }
   if ((st = check_ws(prep, prep_bytes, tq::logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries))) != TQ_SUCCESS) return st;
   hipError_t e = tq::launch_logits_prep(c, q, q_dt, batch, n_q_heads, n_kv_heads, n_queries, prep,
                                         static_cast<hipStream_t>(stream));
@@ -192,9 +207,10 @@ extern "C" tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, si
                                               int32_t n_q_heads, int32_t n_kv_heads, int32_t n_queries,
                                               tq_packed_t k, int64_t ctx_len, float* logits, void* stream) {
   tq::clear_error();
-  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = need_qjl(c, "tq_attn_logits_prepped");
+  tq_status_t st = check_packed_alignment(k, "k");
   if (st != TQ_SUCCESS) return st;
+  if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
+  if ((st = need_qjl(c, "tq_attn_logits_prepped")) != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
@@ -220,6 +236,10 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
                           int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx_len,
                           float softmax_scale, bool sparse_v, float v_gate, const tq::PageMap* pm, void* out,
                           tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream, const char* name) {
+  tq_status_t st = check_packed_alignment(k, "k");
+  if (st != TQ_SUCCESS) return st;
+  if ((st = check_packed_alignment(v, "v")) != TQ_SUCCESS) return st;
+  if (!vec_aligned(q)) { set_error("q must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->polar || cv->polar) {
@@ -228,15 +248,14 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   }
   if (!ck->qjl) { set_error("the K codec must be a two-stage codec (an MSE-only codec is a value codec)"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = check_heads(batch, n_q_heads, n_kv_heads);
-  if (st != TQ_SUCCESS) return st;
+  if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (ctx_len < 1) { set_error("ctx_len must be >= 1"); return TQ_ERROR_INVALID_VALUE; }
   if (!(softmax_scale == softmax_scale)) { set_error("softmax_scale is NaN"); return TQ_ERROR_INVALID_VALUE; }
   const char* why = nullptr;
   if (!tq::decode_supported(cv, n_q_heads, n_kv_heads, ctx_len, &why)) { set_error(why); return TQ_ERROR_NOT_SUPPORTED; }
   if (batch == 0) return TQ_SUCCESS;
   if (!q || !out) { set_error("q or out is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(q, dtype_size(q_dt)) || !aligned(out, dtype_size(out_dt))) { set_error("q/out misaligned"); return TQ_ERROR_MISALIGNED; }
+  if (!aligned(out, dtype_size(out_dt))) { set_error("out misaligned"); return TQ_ERROR_MISALIGNED; }
   if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
   if ((st = check_packed(v, "v", cv->qjl)) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len))) != TQ_SUCCESS) return st;
@@ -287,6 +306,9 @@ extern "C" tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dt
                                               int32_t n_pages, tq_packed_t cache, void* ws, size_t ws_bytes,
                                               void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(cache, "cache");
+  if (st != TQ_SUCCESS) return st;
+  if (!vec_aligned(x)) { set_error("x must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(dt)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   if (batch < 0 || n_kv_heads <= 0 || n_new < 0) {
@@ -299,12 +321,11 @@ extern "C" tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dt
   }
   if (batch == 0 || n_new == 0) return TQ_SUCCESS;
   if (!x || !ctx_lens || !page_table) { set_error("x, ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(x, dtype_size(dt)) || !aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
-    set_error("x, ctx_lens or page_table misaligned");
+  if (!aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
+    set_error("ctx_lens or page_table misaligned");
     return TQ_ERROR_MISALIGNED;
   }
-  tq_status_t st = check_packed(cache, "cache", c->qjl);
-  if (st != TQ_SUCCESS) return st;
+  if ((st = check_packed(cache, "cache", c->qjl)) != TQ_SUCCESS) return st;
   const int64_t n = static_cast<int64_t>(batch) * n_kv_heads * n_new;
   if ((st = check_ws(ws, ws_bytes, tq::append_paged_ws_bytes(c, n))) != TQ_SUCCESS) return st;
   hipError_t e = tq::launch_append_paged(c, x, dt, batch, n_kv_heads, n_new, ctx_lens, page_table, max_pages,
@@ -324,6 +345,10 @@ extern "C" tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const 
                                             int64_t max_ctx, float softmax_scale, float v_gate, void* out,
                                             tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(k_cache, "k_cache");
+  if (st != TQ_SUCCESS) return st;
+  if ((st = check_packed_alignment(v_cache, "v_cache")) != TQ_SUCCESS) return st;
+  if (!vec_aligned(q)) { set_error("q must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!(v_gate >= 0.f && v_gate < 1.f)) { set_error("v_gate must be in [0, 1)"); return TQ_ERROR_INVALID_VALUE; }
   if (max_pages <= 0 || page_size <= 0 || page_size % 128 != 0) {
@@ -360,10 +385,12 @@ extern "C" tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtyp
                                             int32_t max_pages, int32_t page_size, int64_t max_ctx, float* logits,
                                             void* ws, size_t ws_bytes, void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(k_cache, "k_cache");
+  if (st != TQ_SUCCESS) return st;
+  if (!vec_aligned(q)) { set_error("q must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
-  tq_status_t st = need_qjl(c, "tq_attn_logits_paged");
-  if (st != TQ_SUCCESS) return st;
+  if ((st = need_qjl(c, "tq_attn_logits_paged")) != TQ_SUCCESS) return st;
   if (!tq::logits_paged_supported(c)) {
     set_error("paged logits need a per-coordinate codec with head_dim 128 or 256 and qjl_dim = head_dim");
     return TQ_ERROR_NOT_SUPPORTED;
@@ -384,8 +411,8 @@ extern "C" tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtyp
     set_error("q, logits, ctx_lens or page_table is NULL");
     return TQ_ERROR_INVALID_VALUE;
   }
-  if (!aligned(q, dtype_size(q_dt)) || !aligned(logits, 4) || !aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
-    set_error("q, logits, ctx_lens or page_table misaligned");
+  if (!aligned(logits, 4) || !aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
+    set_error("logits, ctx_lens or page_table misaligned");
     return TQ_ERROR_MISALIGNED;
   }
   if ((st = check_packed(k_cache, "k_cache")) != TQ_SUCCESS) return st;
@@ -408,6 +435,9 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
                                       int32_t n_queries, int32_t topk, int64_t* out_idx,
                                       float* out_score, void* ws, size_t ws_bytes, void* stream) {
   tq::clear_error();
+  tq_status_t st = check_packed_alignment(db, "db");
+  if (st != TQ_SUCCESS) return st;
+  if (!vec_aligned(queries)) { set_error("queries must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (c->polar) { set_error("search takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!c->qjl) return need_qjl(c, "tq_search_topk");
@@ -415,9 +445,8 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
   if (topk < 1 || topk > 1024 || topk > n_db) { set_error("need 1 <= topk <= min(n_db, 1024)"); return TQ_ERROR_INVALID_VALUE; }
   if (n_queries == 0) return TQ_SUCCESS;
   if (!queries || !out_idx || !out_score) { set_error("queries/out_idx/out_score is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(queries, 4) || !aligned(out_idx, 8) || !aligned(out_score, 4)) { set_error("search arrays misaligned"); return TQ_ERROR_MISALIGNED; }
-  tq_status_t st = check_packed(db, "db");
-  if (st != TQ_SUCCESS) return st;
+  if (!aligned(out_idx, 8) || !aligned(out_score, 4)) { set_error("search outputs misaligned"); return TQ_ERROR_MISALIGNED; }
+  if ((st = check_packed(db, "db")) != TQ_SUCCESS) return st;
   if ((st = check_ws(ws, ws_bytes, tq::search_ws_bytes(c, n_db, n_queries, topk))) != TQ_SUCCESS) return st;
   if (log_enabled()) std::fprintf(stderr, "[tq] search n_db=%lld nq=%d k=%d\n", (long long)n_db, n_queries, topk);
   hipError_t e = tq::launch_search(c, db, n_db, queries, n_queries, topk, out_idx, out_score, ws,

@@ -41,6 +41,7 @@ __all__ = [
     "encode", "encode_given_codes", "dequantize",
     "prepare_query", "score", "attn_logits",
     "decode_attn_materialized", "decode_attn_accumulated", "decode_attn_sparse_v",
+    "decode_attn_sparse_v_plain",
     "paged_row", "append_paged", "gather_paged", "decode_attn_paged",
     "polar_angle_cdf", "polar_angle_density", "polar_lloyd_max", "polar_transform", "polar_reconstruct",
     "polar_slots", "PolarCodec", "make_polar_codec", "polar_encode", "polar_encode_given_codes",
@@ -591,6 +592,36 @@ def decode_attn_sparse_v(codec_k: Codec, codec_v: Codec, q, k_packed, v_packed,
     return out, keep, local
 
 
+def decode_attn_sparse_v_plain(codec_k: Codec, codec_v: Codec, q, k_packed, v_packed,
+                               batch, n_q_heads, n_kv_heads, ctx_len, scale, gate):
+    """Sparse V exactly as TurboQuant+ 深度解析 第六部分 states it: the value of
+    a position is neither decompressed nor added when its attention weight --
+    the final softmax weight over the whole context -- is below the gate; the
+    normaliser still sums every position.  No chunking: this is the page's
+    rule, which the split kernels bound from above (the chunk-local weight of
+    decode_attn_sparse_v is never below this one, so they keep a superset of
+    these positions).  Returns (out [batch][n_q_heads][d], keep
+    [batch][n_q_heads][ctx_len] bool, w [batch][n_q_heads][ctx_len] final
+    weights)."""
+    q = np.asarray(q, dtype=np.float64).reshape(batch, n_q_heads, codec_k.d)
+    G = n_q_heads // n_kv_heads
+    out = np.zeros((batch, n_q_heads, codec_v.d))
+    keep = np.zeros((batch, n_q_heads, ctx_len), dtype=bool)
+    w = np.zeros((batch, n_q_heads, ctx_len))
+    for bi in range(batch):
+        for kh in range(n_kv_heads):
+            row0 = (bi * n_kv_heads + kh) * ctx_len
+            keys = _slice_packed(k_packed, row0, row0 + ctx_len)
+            vals = dequantize(codec_v, _slice_packed(v_packed, row0, row0 + ctx_len))
+            hs = slice(kh * G, (kh + 1) * G)
+            e, l = _softmax_weights(score(codec_k, q[bi, hs], keys), scale)
+            wt = e / l
+            w[bi, hs] = wt
+            keep[bi, hs] = wt >= gate
+            out[bi, hs] = (wt * keep[bi, hs]) @ vals
+    return out, keep, w
+
+
 # --------------------------------------------------------------------------
 # O6c. Paged cache (the KV cache of 深度拆解 第一部分 "KV 缓存是什么" grows by one
 # token per decode step).  Reading: the cache is split into pages of
@@ -904,6 +935,10 @@ def search_topk(codec: Codec, db_packed: dict, queries: np.ndarray, k: int,
 
 # --------------------------------------------------------------------------
 # Numerics helper: round-to-nearest-even to bfloat16 (returned as fp32 values).
+# An fp64 input is first rounded to fp32 (RNE), as torch does for a double ->
+# bfloat16 cast; an fp32 input is rounded once.  Ties go to the even
+# significand; values at or above the overflow threshold become ±Inf; ±0,
+# subnormals and ±Inf keep their class; NaN stays NaN.
 # --------------------------------------------------------------------------
 def bf16_round(x: np.ndarray) -> np.ndarray:
     f = np.asarray(x, dtype=np.float32)

@@ -114,6 +114,33 @@ def assert_sparse_v_close(out, ref, local, gate, vhat, hkv, ctx, tol):  # batch 
     assert np.all(diff <= bound)
 
 
+def assert_sparse_v_within_plain_rule(out, plain, w, gate, vhat, hkv, ctx, tol):  # batch 1
+    """out (a kernel's gated attention) vs the page's own rule, which drops the
+    value term of every position whose final softmax weight w is below the
+    gate (oracle decode_attn_sparse_v_plain).  A split kernel may keep some of
+    those positions (its chunk-local weight bounds w from above) and, within
+    1% of the gate, take a floating-point decision either way, so the two
+    differ by at most the value mass of the positions with w < 1.01·gate,
+    per (head, coordinate), plus `tol` of each row's maximum.  Also checks the
+    coarser bound gate × (positions dropped by the plain rule) × max|v̂|."""
+    G = out.shape[1] // hkv
+    slack = np.zeros_like(plain[0])
+    coarse = np.zeros(plain.shape[1])
+    vmax = np.abs(vhat).max()
+    for h in range(out.shape[1]):
+        kh = h // G
+        t = np.nonzero(w[0, h] < 1.01 * gate)[0]
+        slack[h] = w[0, h, t] @ np.abs(vhat[kh * ctx + t])
+        coarse[h] = gate * np.count_nonzero(w[0, h] < gate) * vmax
+    diff = np.abs(out[0] - plain[0])
+    scale = tol * np.max(np.abs(plain[0]), axis=-1, keepdims=True)
+    bound = scale + 1.01 * slack
+    print(f"  plain rule: dropped (head, key) {np.mean(w < gate):.4f}, max |out - plain| {diff.max():.2e}, "
+          f"worst diff/bound {np.max(diff / bound):.3f}, coarse bound {coarse.max():.2e}", flush=True)
+    assert np.all(diff <= bound)
+    assert np.all(diff.max(axis=-1) <= scale[:, 0] + coarse * 1.01)
+
+
 ANGLE_BAND = 1e-5  # rad
 
 

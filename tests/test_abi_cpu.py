@@ -90,6 +90,57 @@ def test_null_handles_rejected_without_launch(B):
     assert "NULL" in lib.tq_last_error().decode()
 
 
+def test_misaligned_arrays_refused_before_launch(B):
+    """Codes, signs and input vectors must be 16-byte aligned (the kernels use
+    16-byte loads and stores); ν and γ 4-byte aligned.  The alignment is
+    checked before anything else, so fake host addresses never reach a kernel:
+    a misaligned array gives TQ_ERROR_MISALIGNED (3), the same call with
+    aligned arrays and no codec gives TQ_ERROR_INVALID_VALUE (1)."""
+    lib = B.lib
+    A = 0x10000  # fake, never dereferenced: every call below stops at its argument checks
+    good = B.tq_packed_t(A, A + 0x1000, A + 0x2000, A + 0x3000)
+    bads = [B.tq_packed_t(A + 4, A + 0x1000, A + 0x2000, A + 0x3000),   # codes 4-byte aligned
+            B.tq_packed_t(A + 8, A + 0x1000, A + 0x2000, A + 0x3000),   # codes 8-byte aligned
+            B.tq_packed_t(A, A + 0x1004, A + 0x2000, A + 0x3000),       # signs
+            B.tq_packed_t(A, A + 0x1000, A + 0x2002, A + 0x3000),       # norm
+            B.tq_packed_t(A, A + 0x1000, A + 0x2000, A + 0x3001)]       # rnorm
+    vec_ok, vec_bad = A + 0x4000, A + 0x4008
+
+    def calls(P, vec):
+        yield "encode", lambda: lib.tq_encode_kv(None, vec, None, 1, 10, P, P, None, 0, None)
+        yield "encode v_out", lambda: lib.tq_encode_kv(None, vec_ok, vec, 1, 10, good, P, None, 0, None)
+        yield "logits", lambda: lib.tq_attn_logits(None, vec, 1, 1, 4, 1, 1, P, 10, A, A, 1 << 20, None)
+        yield "prepped", lambda: lib.tq_attn_logits_prepped(None, A, 1 << 20, 1, 4, 1, 1, P, 10, A, None)
+        yield "decode", lambda: lib.tq_decode_attn(None, None, vec, 1, 1, 4, 1, P, good, 10, 1.0, A, 0, A, 1 << 20,
+                                                   None)
+        yield "decode v", lambda: lib.tq_decode_attn(None, None, vec, 1, 1, 4, 1, good, P, 10, 1.0, A, 0, A,
+                                                     1 << 20, None)
+        yield "sparse_v", lambda: lib.tq_decode_attn_sparse_v(None, None, vec, 1, 1, 4, 1, P, P, 10, 1.0, 1e-6, A, 0,
+                                                              A, 1 << 20, None)
+        yield "paged decode", lambda: lib.tq_decode_attn_paged(None, None, vec, 1, 1, 4, 1, P, P, A, A, 4, 128, 10,
+                                                               1.0, 0.0, A, 0, A, 1 << 20, None)
+        yield "paged logits", lambda: lib.tq_attn_logits_paged(None, vec, 1, 1, 4, 1, 1, P, A, A, 4, 128, 10, A, A,
+                                                               1 << 20, None)
+        yield "append", lambda: lib.tq_encode_append_paged(None, vec, 1, 1, 1, 1, A, A, 4, 128, 4, P, A, 1 << 20,
+                                                           None)
+        yield "search", lambda: lib.tq_search_topk(None, P, 10, vec, 1, 1, A, A, A, 1 << 20, None)
+
+    for name, f in calls(good, vec_ok):
+        assert f() == 1, name                      # aligned: the missing codec is what is reported
+    for P in bads:
+        for name, f in calls(P, vec_ok):
+            if name in ("encode v_out",):
+                continue
+            assert f() == 3, (name, P.codes, P.signs, P.norm, P.rnorm)
+            assert "aligned" in lib.tq_last_error().decode()
+    for name, f in calls(good, vec_bad):           # a misaligned input vector array
+        if name in ("prepped",):
+            continue                               # takes no input vectors
+        assert f() == 3, name
+    assert lib.tq_attn_query_prep(None, vec_bad, 1, 1, 4, 1, 1, A, 1 << 20, None) == 3
+    assert lib.tq_attn_query_prep(None, vec_ok, 1, 1, 4, 1, 1, A, 1 << 20, None) == 1
+
+
 def test_codec_create_without_gpu_reports_hip_error(B):
     import torch
     if torch.cuda.is_available():

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.parity import (assert_sparse_v_close, check_encode, check_polar_encode, oracle_records_like,
+from tests.parity import (assert_sparse_v_close, assert_sparse_v_within_plain_rule, check_encode, check_polar_encode, oracle_records_like,
                           polar_records_like, row_rel_err, tol_for)
 
 pytestmark = pytest.mark.gpu
@@ -489,7 +489,14 @@ def test_decode_sparse_v_parity(B, kbits, vbits, hq, hkv, ctx, gate, needles, qs
                                     out_dtype=torch.float32).cpu().numpy()
     full = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale)
     say(f"  gated vs ungated oracle {row_rel_err(ref, full).max():.2e}")
-    assert_sparse_v_close(out, ref, local, gate, O.dequantize(ov, vr), hkv, ctx, 1e-4)
+    vhat = O.dequantize(ov, vr)
+    # the product rule (chunk-local weight), exactly
+    assert_sparse_v_close(out, ref, local, gate, vhat, hkv, ctx, 1e-4)
+    # and the page's plain rule (final weight), within the mass it drops
+    plain, keep_p, w = O.decode_attn_sparse_v_plain(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale,
+                                                    gate)
+    assert np.all(keep | ~keep_p)
+    assert_sparse_v_within_plain_rule(out, plain, w, gate, vhat, hkv, ctx, 1e-4)
 
 
 @pytest.mark.parametrize("hq,hkv,ctx", [(8, 2, 3000), (16, 2, 1500)])
@@ -760,6 +767,114 @@ def test_logits_paged_identity_equals_contiguous(B):
     gv, _ = mse_pair(B, 128, 3)
     with pytest.raises(B.TQError):
         B.tq_attn_logits_paged(gv, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
+    gp, _ = polar_pair(B, 3)
+    with pytest.raises(B.TQError):
+        B.tq_attn_logits_paged(gp, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
+
+
+def _paged_pool(B, gc, seed, batch, hkv, P, max_pages, spare=2):
+    """A pool of batch*max_pages + spare pages, every row an encoded N(0,1)
+    bf16 key, and a shuffled page table (batch, max_pages)."""
+    n_pages = batch * max_pages + spare
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn((n_pages * hkv * P, 128), generator=g, device="cuda").to(torch.bfloat16)
+    pool, _ = B.tq_encode_kv(gc, x)
+    perm = np.random.default_rng(seed).permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages)
+    return pool, perm.astype(np.int32)
+
+
+def _paged_rows(pt, b, hkv, n, P):
+    """Pool rows of sequence b's first n positions, [kv_head][position]
+    (the layout O.paged_row defines, vectorised)."""
+    t = np.arange(n)
+    page = np.asarray(pt)[b][t // P].astype(np.int64)
+    return np.concatenate([(page * hkv + kh) * P + t % P for kh in range(hkv)])
+
+
+def _gather_rows(B, pool, rows):
+    idx = torch.from_numpy(np.asarray(rows, dtype=np.int64)).cuda()
+    return B.Packed(pool.codes.index_select(0, idx).contiguous(), pool.signs.index_select(0, idx).contiguous(),
+                    pool.norm.index_select(0, idx).contiguous(), pool.rnorm.index_select(0, idx).contiguous())
+
+
+def test_logits_paged_four_groups_per_wave(B):
+    # a grid of at least two blocks per compute unit takes the instance whose
+    # waves score four 64-key groups each (a page lookup per group, records of
+    # the next group prefetched across a page boundary at page_size 128); the
+    # contexts end inside a wave's 256-key span.  Logits equal the contiguous
+    # call's bit for bit on each sequence's positions and match the oracle on
+    # sampled heads; positions past a sequence's end stay untouched.
+    gc, oc = pair(B, 128, 3)
+    batch, hq, hkv, P, max_pages = 4, 32, 8, 128, 256
+    max_ctx = P * max_pages                                  # 32768
+    ctxs = [max_ctx, 20000 + 77, 12345, 129]
+    say(f"paged logits, four groups per wave: batch {batch} hq {hq} hkv {hkv} ctx {ctxs} P {P}")
+    pool, pt = _paged_pool(B, gc, 71, batch, hkv, P, max_pages)
+    q = to_dev(as_exact(np.random.default_rng(72).standard_normal((batch, 1, hq, 128)), "bf16"), "bf16")
+    out = torch.full((batch, hq, 1, max_ctx), 7.0, device="cuda")
+    B.tq_attn_logits_paged(gc, q, pool, torch.tensor(ctxs, dtype=torch.int32, device="cuda"),
+                           torch.from_numpy(pt).cuda(), P, max_ctx, hkv, logits=out)
+    # the same records in contiguous rows [batch][kv_head][max_ctx] (positions
+    # past a sequence's end repeat its page-table rows: never compared)
+    rows = np.concatenate([_paged_rows(pt, b, hkv, max_ctx, P) for b in range(batch)])
+    assert all(rows[i] == O.paged_row(pt, i // (hkv * max_ctx), (i // max_ctx) % hkv, i % max_ctx, hkv, P)
+               for i in np.random.default_rng(74).choice(len(rows), 200, replace=False))
+    contig = _gather_rows(B, pool, rows)
+    ref_gpu = B.tq_attn_logits(gc, q, contig, max_ctx, hkv)
+    torch.cuda.synchronize()
+    g, rg = out.cpu().numpy(), ref_gpu.cpu().numpy()
+    host = contig.numpy()
+    rng = np.random.default_rng(73)
+    for b, n in enumerate(ctxs):
+        assert np.array_equal(g[b, :, :, :n], rg[b, :, :, :n]), b
+        assert np.all(g[b, :, :, n:] == 7.0)
+        for kh in rng.choice(hkv, 2, replace=False):
+            r0 = (b * hkv + kh) * max_ctx
+            kr = {k_: x[r0:r0 + n] for k_, x in host.items()}
+            hs = slice(kh * 4, kh * 4 + 4)
+            ref = O.attn_logits(oc, q[b:b + 1, :, hs].float().cpu().numpy().astype(np.float64), kr, 1, 4, 1, 1, n)
+            err = row_rel_err(g[b:b + 1, hs, :, :n], ref).max()
+            say(f"  sequence {b} (ctx {n}) kv head {kh}: max row err {err:.2e}")
+            assert err <= 1e-3
+
+
+def test_paged_large_page_size_and_table(B):
+    # page_size 65536 and a 32768-entry page table: max_pages * page_size is
+    # 2^31, past a 32-bit int; a short context must still be scored (logits)
+    # and attended (decode) in full
+    gc, oc = pair(B, 128, 3)
+    P, max_pages, hkv, n, max_ctx = 65536, 32768, 1, 1000, 5000
+    say(f"paged, page_size {P}, max_pages {max_pages}, ctx {n}")
+    pool, _ = _paged_pool(B, gc, 81, 1, hkv, P, 1, spare=1)   # 2 pages
+    pt = np.zeros((1, max_pages), dtype=np.int32)
+    pt[0, 0] = 1
+    ptd = torch.from_numpy(pt).cuda()
+    cl = torch.tensor([n], dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(82)
+    q = to_dev(as_exact(rng.standard_normal((1, 1, 4, 128)), "bf16"), "bf16")
+    out = torch.full((1, 4, 1, max_ctx), 7.0, device="cuda")
+    B.tq_attn_logits_paged(gc, q, pool, cl, ptd, P, max_ctx, hkv, logits=out)
+    rows = [O.paged_row(pt, 0, 0, t, hkv, P) for t in range(n)]
+    contig = _gather_rows(B, pool, rows)
+    a = B.tq_attn_logits(gc, q, contig, n, hkv)
+    o = B.tq_decode_attn_paged(gc, gc, q.view(1, 4, 128), pool, pool, cl, ptd, P, max_ctx, hkv, 0.1,
+                               out_dtype=torch.float32)
+    ref_o = B.tq_decode_attn(gc, gc, q.view(1, 4, 128), contig, contig, n, hkv, 0.1, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    assert np.all(g[..., n:] == 7.0)
+    assert np.array_equal(g[..., :n], a.cpu().numpy())
+    host = contig.numpy()
+    ref = O.attn_logits(oc, q.float().cpu().numpy().astype(np.float64), host, 1, 4, 1, 1, n)
+    err = row_rel_err(g[..., :n], ref).max()
+    say(f"  logits max row err {err:.2e}; decode paged vs contiguous bitwise "
+        f"{torch.equal(o, ref_o)}")
+    assert err <= 1e-3
+    assert torch.equal(o, ref_o)
+    rd = O.decode_attn_accumulated(oc, oc, q.float().cpu().numpy().reshape(1, 4, 128).astype(np.float64), host, host,
+                                   1, 4, 1, n, 0.1)
+    assert row_rel_err(o.cpu().numpy(), rd).max() <= 1e-3
 
 
 def test_decode_paged_identity_equals_contiguous(B):

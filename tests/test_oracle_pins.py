@@ -555,6 +555,48 @@ def test_sparse_v_gate_uses_the_chunk_maximum(codec3, codec4):
     assert np.allclose(out[0, 0], vhat[j], rtol=1e-12, atol=1e-12)
 
 
+def test_sparse_v_plain_rule_is_the_final_weight_threshold(codec3, codec4):
+    # the page's rule on its own terms: final softmax weight (SciPy's softmax
+    # of the scaled scores) below the gate -> value term dropped, normaliser
+    # unchanged; gate 0 is plain attention
+    from scipy import special
+    T, Hq, gate = 700, 4, 2e-3
+    K, V, q = _sparse_case(codec3, codec4, T, Hq, 3.0, 31)
+    scale = 1 / math.sqrt(128)
+    w = special.softmax(O.score(codec3, q[0], K) * scale, axis=-1)
+    vhat = O.dequantize(codec4, V)
+    out, keep, wo = O.decode_attn_sparse_v_plain(codec3, codec4, q, K, V, 1, Hq, 2, T // 2, scale, 0.0)
+    ref = O.decode_attn_materialized(codec3, codec4, q, K, V, 1, Hq, 2, T // 2, scale)
+    assert keep.all() and np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+    out, keep, wo = O.decode_attn_sparse_v_plain(codec3, codec4, q, K, V, 1, Hq, 1, T, scale, gate)
+    assert np.allclose(wo[0], w, rtol=1e-12, atol=0)
+    assert np.array_equal(keep[0], w >= gate)
+    assert 0.02 < keep.mean() < 0.9                      # the case really gates
+    assert np.allclose(out[0], (w * (w >= gate)) @ vhat, rtol=1e-12, atol=1e-15)
+
+
+def test_sparse_v_chunked_rule_bounds_the_plain_rule(codec3, codec4):
+    # the chunk-local rule of the split kernels keeps a superset of the
+    # plain rule's positions, equals it with one chunk over the context, and
+    # moves the output by at most the dropped mass of the plain rule
+    T, Hq, gate = 2000, 2, 1e-3
+    K, V, q = _sparse_case(codec3, codec4, T, Hq, 3.0, 32)
+    scale = 1 / math.sqrt(128)
+    vhat = O.dequantize(codec4, V)
+    plain, keep_p, w = O.decode_attn_sparse_v_plain(codec3, codec4, q, K, V, 1, Hq, 1, T, scale, gate)
+    one, keep_1, _ = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, Hq, 1, T, scale, gate, T)
+    assert np.array_equal(keep_1, keep_p) and np.allclose(one, plain, rtol=1e-12, atol=1e-15)
+    for chunk in (128, 256, 1024):
+        out, keep_c, _ = O.decode_attn_sparse_v(codec3, codec4, q, K, V, 1, Hq, 1, T, scale, gate, chunk)
+        assert np.all(keep_c | ~keep_p)                       # superset
+        assert (keep_c & ~keep_p).any()                       # and a strict one here
+        extra = (w[0] * (keep_c[0] & ~keep_p[0])) @ np.abs(vhat)
+        assert np.allclose(out[0] - plain[0], (w[0] * (keep_c[0] & ~keep_p[0])) @ vhat, rtol=1e-9, atol=1e-15)
+        assert np.all(np.abs(out[0] - plain[0]) <= extra * (1 + 1e-9) + 1e-15)
+        bound = gate * (~keep_p[0]).sum(axis=-1) * np.abs(vhat).max()
+        assert np.all(np.abs(out[0] - plain[0]).max(axis=-1) <= bound)
+
+
 # ---------------------------------------------------------------- O6c paged cache
 def test_paged_rows_closed_form_and_disjoint():
     # one KV head with the identity page table is the contiguous layout
@@ -750,3 +792,70 @@ def test_polar_score_unbiased_and_matches_dequantize():
         vals.append(float(O.polar_score(pc, q, O.polar_encode(pc, x))[0, 0]))
     vals = np.array(vals)
     assert abs(vals.mean() - float((q @ x.T)[0, 0])) < 3.5 * vals.std() / math.sqrt(vals.size)
+
+
+# ---------------------------------------------------------------- bf16 rounding helper
+def _bf16_nearest(x32: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even to bfloat16 from its definition: of the two
+    bfloat16 neighbours of each fp32 value (truncation and the next value
+    away from zero; 2^128 stands for the overflow step), take the nearer in
+    exact fp64 arithmetic, ties to the even significand, then map 2^128 to
+    Inf.  Independent of the bit trick the oracle uses."""
+    out = np.empty_like(x32)
+    for i, v in enumerate(x32):
+        if np.isnan(v) or np.isinf(v):
+            out[i] = v
+            continue
+        u = int(np.float32(v).view(np.uint32))
+        sign, mag = u & 0x80000000, u & 0x7FFFFFFF
+        lo = mag & 0xFFFF0000
+        hi = lo + 0x10000
+        a = float(np.uint32(lo).view(np.float32))
+        b = 2.0 ** 128 if hi == 0x7F800000 else float(np.uint32(hi).view(np.float32))
+        m = abs(float(v))
+        if m - a < b - m or (m - a == b - m and (lo >> 16) % 2 == 0):
+            r = lo
+        else:
+            r = hi
+        out[i] = np.uint32(sign | r).view(np.float32)
+    return out
+
+
+def test_bf16_round_pinned_to_definition_and_torch():
+    torch = pytest.importorskip("torch")
+    f = np.float32
+    one = 1.0
+    cases = [0.0, -0.0, one, -one,
+             one + 2.0 ** -8,                 # tie between 1 and 1 + 2^-7: even is 1
+             one + 3 * 2.0 ** -8,             # tie: even is 1 + 2^-6
+             one + 2.0 ** -8 + 2.0 ** -23,    # just above the tie
+             one + 2.0 ** -8 - 2.0 ** -23,    # just below
+             -(one + 2.0 ** -8),
+             2.0 ** -126, 2.0 ** -130,        # fp32 normal minimum, subnormal
+             2.0 ** -133 * 3,                 # bf16 subnormal tie region
+             2.0 ** -149, -2.0 ** -149,       # fp32 smallest subnormal
+             2.0 ** -140 * 1.5,
+             float(np.finfo(np.float32).max),  # rounds up to Inf
+             3.3895313892515355e38,           # bfloat16 max, exact
+             3.3961775292304958e38,           # just below the overflow tie: stays finite
+             float("inf"), float("-inf"), float("nan")]
+    rng = np.random.default_rng(5)
+    rnd = np.concatenate([rng.standard_normal(4000), rng.standard_normal(2000) * 1e-39, rng.standard_normal(2000) * 1e37,
+                          rng.integers(-(2 ** 20), 2 ** 20, 2000) * 2.0 ** -16])  # many exact ties
+    x32 = np.array(cases + list(rnd), dtype=np.float64).astype(f)
+    got = O.bf16_round(x32)
+    want = _bf16_nearest(x32)
+    tch = torch.from_numpy(x32.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    nan = np.isnan(x32)
+    assert np.array_equal(np.isnan(got), nan) and np.array_equal(np.isnan(tch), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+    assert np.array_equal(got[~nan].view(np.uint32), tch[~nan].view(np.uint32))
+    assert np.isposinf(got[x32 == np.finfo(np.float32).max]).all()
+    assert got[4] == 1.0 and got[5] == 1.0 + 2.0 ** -6           # ties to even
+    assert np.signbit(got[1]) and got[1] == 0.0                  # -0 stays -0
+    # fp64 inputs round to fp32 first (RNE), as torch does for double -> bfloat16
+    x64 = np.concatenate([rnd, [1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -8 - 2.0 ** -30]])
+    g64 = O.bf16_round(x64)
+    t64 = torch.from_numpy(x64.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(g64.view(np.uint32), t64.view(np.uint32))
+    assert np.array_equal(g64.view(np.uint32), _bf16_nearest(x64.astype(f)).view(np.uint32))
