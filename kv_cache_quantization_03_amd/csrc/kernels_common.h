@@ -26,6 +26,51 @@ __device__ __forceinline__ float load_elem(const __hip_bfloat16* p, int64_t i) {
 }
 __device__ __forceinline__ float load_elem(const __half* p, int64_t i) { return __half2float(p[i]); }
 
+// Eight consecutive elements as fp32 (p 16-byte aligned), in two steps so a
+// caller can issue the load early and convert after a barrier: load_raw8
+// keeps the loaded bits, unpack8 converts them.
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<float> { float4 a, b; };
+template <>
+struct Raw8<__hip_bfloat16> { uint4 a; };
+template <>
+struct Raw8<__half> { h8 a; };
+
+__device__ __forceinline__ void load_raw8(const float* p, Raw8<float>& r) {
+  r.a = reinterpret_cast<const float4*>(p)[0];
+  r.b = reinterpret_cast<const float4*>(p)[1];
+}
+__device__ __forceinline__ void load_raw8(const __hip_bfloat16* p, Raw8<__hip_bfloat16>& r) {
+  r.a = *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void load_raw8(const __half* p, Raw8<__half>& r) { r.a = *reinterpret_cast<const h8*>(p); }
+
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float (&v)[8]) {
+  v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w; v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+}
+__device__ __forceinline__ void unpack8(const Raw8<__hip_bfloat16>& r, float (&v)[8]) {
+  const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<__half>& r, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(r.a[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+  Raw8<T> r;
+  load_raw8(p, r);
+  unpack8(r, v);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

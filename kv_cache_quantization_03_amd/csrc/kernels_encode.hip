@@ -207,33 +207,8 @@ __global__ __launch_bounds__(256) void sproj_kernel(const float* __restrict__ A,
 // * A block encodes 16 vectors per pass; wave w owns outputs 32w..32w+31 of
 //   z and keeps its fp16 rows of S in registers for all passes.
 // ----------------------------------------------------------------------------
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kEncPasses = 8;
-
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-template <>
-__device__ __forceinline__ void load8(const __hip_bfloat16* p, float (&v)[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load8(const __half* p, float (&v)[8]) {
-  const h8 a = *reinterpret_cast<const h8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = static_cast<float>(a[i]);
-}
 
 // Code of an angle: #{boundaries of its level below th} (ties low).
 template <int NL>

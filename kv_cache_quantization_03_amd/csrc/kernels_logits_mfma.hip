@@ -361,12 +361,17 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
 // Fused logits (d = 128, one M-tile of 4 query vectors per KV head): every
 // block rebuilds the query operands of its (batch, kv head) in LDS while its
 // records are in flight (query_prep_*), so a decode step is one launch.
+// The logits leave in whole lines: each wave's four 16-key tiles go through
+// its LDS slice and come back as four consecutive keys per lane, so a row of
+// 64 keys is written by 16 lanes with 16-byte stores (two full 128-byte
+// lines) instead of four 64-byte pieces.  vec_out = 0 (ctx not a multiple of
+// 4, or logits not 16-byte aligned) keeps the scalar stores.
 // ----------------------------------------------------------------------------
 template <int NP, int WAVES, typename T>
 __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
     const T* q, DevParams P, const float* Dsign, const float* Mt, int Hq, int nq, int G, int nkv, int ctx,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs, const float* __restrict__ norm,
-    const float* __restrict__ rnorm, float* __restrict__ logits) {
+    const float* __restrict__ rnorm, float* __restrict__ logits, int vec_out) {
   using L = RecLayout<NP, 1>;
   constexpr int NT = WAVES * 64, NKB = L::NKB;
   __shared__ uint32_t s_codes[WAVES][kKeysPerWave * L::CS];
@@ -399,14 +404,34 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   query_prep_build<NT, NP, NKB>(sh, pr, P, tile);
   if (!active) return;  // wave-uniform
 
-  const int g = lane >> 4;
+  const int g = lane >> 4, kl = lane & 15;
   v8i a[1][NKB];
   query_prep_operands<NT, NKB>(sh, a, lane);
-  const float4 cst[1] = {query_prep_constants<NT, NP, NKB>(sh, P, g)};
+  const float4 cst = query_prep_constants<NT, NP, NKB>(sh, P, g);
+  float val[kKeysPerWave / kKeysPerTile];
+  score_wave_values<NP, 1>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, P.qjl_kappa, lane, val);
   const int qvg = tile.mt * 4 + g;
-  float* const out[1] = {qvg < tile.Gq ? logits + (static_cast<int64_t>(tile.b * Hq + tile.kh * G + qvg % G) * nq + qvg / G) * ctx + key0
-                                       : nullptr};
-  score_wave<NP, 1, 1>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, out, nvalid, P.qjl_kappa, lane);
+  if (qvg >= tile.Gq) return;  // a padding slot of the tile (lane-divergent: no wave ops below)
+  float* orow = logits + (static_cast<int64_t>(tile.b * Hq + tile.kh * G + qvg % G) * nq + qvg / G) * ctx + key0;
+  if (vec_out) {
+    // val[t] is key 16t + kl; through the wave's LDS slice to keys 4kl..4kl+3
+    float* st = reinterpret_cast<float*>(s_codes[wv]) + g * kKeysPerWave;
+#pragma unroll
+    for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) st[kKeysPerTile * t + kl] = val[t];
+    __builtin_amdgcn_wave_barrier();
+    const v4f o = *reinterpret_cast<const v4f*>(st + 4 * kl);
+    if (4 * kl + 3 < nvalid) {
+      __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(orow + 4 * kl));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * kl + i < nvalid) __builtin_nontemporal_store(o[i], orow + 4 * kl + i);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t)
+      if (kKeysPerTile * t + kl < nvalid) __builtin_nontemporal_store(val[t], orow + kKeysPerTile * t + kl);
+  }
 }
 
 // TQ_LOGITS_KERNEL=valu selects the general VALU kernel (A/B comparisons).
@@ -545,11 +570,12 @@ hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt
   // against 9.2 us for 8-wave blocks at 32 query heads x 32K keys).
   constexpr int WAVES = kFusedWaves;
   const int G = n_q_heads / n_kv_heads;
+  const int vec_out = ctx % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
   auto go = [&]<int NP, typename T>(const T* qq) -> hipError_t {
     const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * kKeysPerWave)), batch * n_kv_heads, 1);
     hipLaunchKernelGGL((logits_fused_kernel<NP, WAVES, T>), grid, dim3(WAVES * 64), 0, s, qq, c->prm, c->dD, c->dMt,
                        n_q_heads, n_queries, G, n_kv_heads, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                       k.rnorm, logits);
+                       k.rnorm, logits, vec_out);
     return hipGetLastError();
   };
   auto by_np = [&]<typename T>(const T* qq) -> hipError_t {
