@@ -267,6 +267,26 @@ tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype
                            tq_packed_t v, int64_t ctx_len, float softmax_scale, void* out,
                            tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- decode attention, no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ * tq_decode_attn with the same arguments and results, minus the workspace:
+ * its partial results live in a static device array of the library,
+ * TQ_NO_ALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the library's load
+ * until the process ends.  The call allocates and frees nothing.
+ * A call that would need more than that (tq_decode_attn_workspace(...) >
+ * TQ_NO_ALLOC_SCRATCH_BYTES; e.g. 32 query heads, 8 KV heads and more than
+ * 4 million positions) returns TQ_ERROR_NOT_SUPPORTED before any launch.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (different streams, or threads)
+ * race and must be serialised by the caller.  Nothing in the array needs to
+ * start at zero (every value is written before it is read). */
+#define TQ_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+tq_status_t tq_decode_attn_no_alloc(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt, int32_t batch,
+                                    int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k, tq_packed_t v,
+                                    int64_t ctx_len, float softmax_scale, void* out, tq_dtype_t out_dt,
+                                    void* stream);
+
 /* ---------------------------------------------------------------- Sparse V decode attention
  * tq_decode_attn with the value dequantization gated by the attention weights
  * (TurboQuant+ 深度解析, 第六部分 Sparse V Dequant: positions whose weight is

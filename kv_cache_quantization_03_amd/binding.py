@@ -68,6 +68,8 @@ def _load():
         "tq_decode_attn_sparse_v": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, i64, C.c_float, C.c_float,
                                               vp, C.c_int, vp, sz, vp]),
         "tq_decode_attn_chunk": (i32, [i32, i32]),
+        "tq_decode_attn_no_alloc": (C.c_int, [vp, vp, vp, C.c_int, i32, i32, i32, P, P, i64, C.c_float, vp,
+                                              C.c_int, vp]),
         "tq_encode_append_paged_workspace": (sz, [vp, i32, i32, i32]),
         "tq_encode_append_paged": (C.c_int, [vp, vp, C.c_int, i32, i32, i32, vp, vp, i32, i32, i32, P, vp, sz, vp]),
         "tq_decode_attn_paged_workspace": (sz, [vp, vp, i32, i32, i32, i64]),
@@ -93,6 +95,7 @@ EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_bui
             "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_codec_create_mse", "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
+            "tq_decode_attn_no_alloc",
             "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
             "tq_decode_attn_paged", "tq_attn_logits_paged_workspace", "tq_attn_logits_paged",
             "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
@@ -333,6 +336,17 @@ def tq_decode_attn(ck: Codec, cv: Codec, q, k: Packed, v: Packed, ctx_len: int, 
     st = lib.tq_decode_attn(ck.handle, cv.handle, _ptr(q), _dt(q), batch, hq, n_kv_heads, k.c(), v.c(), ctx_len,
                             float(softmax_scale), _ptr(out), _dt(out), _ptr(ws), ws.numel(), _stream(q))
     _check(st, "tq_decode_attn")
+    return out
+
+
+def tq_decode_attn_no_alloc(ck: Codec, cv: Codec, q, k: Packed, v: Packed, ctx_len: int, n_kv_heads: int,
+                            softmax_scale: float, out):
+    """tq_decode_attn without a workspace (the library's static scratch);
+    `out` [batch][n_q_heads][d] is the caller's, so nothing is allocated."""
+    batch, hq, d = q.shape
+    st = lib.tq_decode_attn_no_alloc(ck.handle, cv.handle, _ptr(q), _dt(q), batch, hq, n_kv_heads, k.c(), v.c(),
+                                     ctx_len, float(softmax_scale), _ptr(out), _dt(out), _stream(q))
+    _check(st, "tq_decode_attn_no_alloc")
     return out
 
 

@@ -235,7 +235,8 @@ namespace {
 tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt, int32_t batch,
                           int32_t n_q_heads, int32_t n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx_len,
                           float softmax_scale, bool sparse_v, float v_gate, const tq::PageMap* pm, void* out,
-                          tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream, const char* name) {
+                          tq_dtype_t out_dt, void* ws, size_t ws_bytes, void* stream, const char* name,
+                          bool no_alloc = false) {
   tq_status_t st = check_packed_alignment(k, "k");
   if (st != TQ_SUCCESS) return st;
   if ((st = check_packed_alignment(v, "v")) != TQ_SUCCESS) return st;
@@ -258,6 +259,22 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (!aligned(out, dtype_size(out_dt))) { set_error("out misaligned"); return TQ_ERROR_MISALIGNED; }
   if ((st = check_packed(k, "k")) != TQ_SUCCESS) return st;
   if ((st = check_packed(v, "v", cv->qjl)) != TQ_SUCCESS) return st;
+  if (no_alloc) {
+    // the static scratch replaces the workspace: refuse what does not fit it
+    const size_t need = tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len);
+    if (need > tq::kNoAllocScratchBytes) {
+      set_error(std::string(name) + ": this call needs " + std::to_string(need) +
+                " bytes of scratch, above the static maximum of " + std::to_string(tq::kNoAllocScratchBytes) +
+                " bytes (call tq_decode_attn with a workspace instead)");
+      return TQ_ERROR_NOT_SUPPORTED;
+    }
+    const hipError_t e = tq::no_alloc_scratch(&ws);
+    if (e != hipSuccess) {
+      set_error(std::string(name) + ": looking up the static scratch failed: " + hipGetErrorString(e));
+      return TQ_ERROR_HIP;
+    }
+    ws_bytes = tq::kNoAllocScratchBytes;
+  }
   if ((st = check_ws(ws, ws_bytes, tq::decode_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx_len))) != TQ_SUCCESS) return st;
   if (log_enabled())
     std::fprintf(stderr, "[tq] %s b=%d hq=%d hkv=%d ctx=%lld gate=%g\n", name, batch, n_q_heads, n_kv_heads,
@@ -276,6 +293,15 @@ extern "C" tq_status_t tq_decode_attn(tq_codec_t ck, tq_codec_t cv, const void* 
   tq::clear_error();
   return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, false, 0.f,
                        nullptr, out, out_dt, ws, ws_bytes, stream, "tq_decode_attn");
+}
+
+extern "C" tq_status_t tq_decode_attn_no_alloc(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,
+                                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                               tq_packed_t k, tq_packed_t v, int64_t ctx_len, float softmax_scale,
+                                               void* out, tq_dtype_t out_dt, void* stream) {
+  tq::clear_error();
+  return decode_common(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx_len, softmax_scale, false, 0.f,
+                       nullptr, out, out_dt, nullptr, 0, stream, "tq_decode_attn_no_alloc", true);
 }
 
 extern "C" tq_status_t tq_decode_attn_sparse_v(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_t q_dt,

@@ -107,6 +107,12 @@ struct tq_codec_s {
 
 namespace tq {
 
+// Static device scratch of tq_decode_attn_no_alloc (scratch.hip): its size,
+// and its device address on the current device (looked up on the first call
+// per device; no allocation).
+constexpr size_t kNoAllocScratchBytes = TQ_NO_ALLOC_SCRATCH_BYTES;
+hipError_t no_alloc_scratch(void** out);
+
 // ---- kernel launchers (kernels_*.hip).  All arguments were validated. ----
 // Encode: rotate + quantize (codes, norm, rnorm) and write the residual r (fp32
 // [n][d]) into ws_r; then the QJL projection writes the sign words.
