@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compressed keys scored/sec + effective HBM GB/s (% of peak), 3-bit, 32K ctx"
 PEAK_HBM_GBS = 8000.0
+ROOFLINE_LAUNCHES = 200
 INFINITY_CACHE = 256 * 2 ** 20
 
 
@@ -216,12 +217,31 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / K
     logits_ms = e0.elapsed_time(e1) / K
+    roof_launches = K
     scores_per_step = batch * hq * ctx
     value = scores_per_step / (ms_per_step * 1e-3)
     for s_i, S in enumerate(sets[:min(n_sets, K)]):
         if not torch.equal(S["logits"], eager[s_i]):
             raise RuntimeError(f"timed replay differs from the eager step on buffer set {s_i}")
     del g_steps
+    if K < ROOFLINE_LAUNCHES:
+        # a short timed region is dominated by the graph's launch and drain; the
+        # kernel's per-launch duration for the roofline comes from a replay of
+        # ROOFLINE_LAUNCHES back-to-back steps right after it (value stays the
+        # K-step wall-clock rate)
+        g_r = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_r):
+            for i in range(ROOFLINE_LAUNCHES):
+                step(i)
+        g_r.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g_r.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        logits_ms = e0.elapsed_time(e1) / ROOFLINE_LAUNCHES
+        roof_launches = ROOFLINE_LAUNCHES
+        del g_r
 
     # the split two-launch form on the same buffers, for comparison
     g_two = torch.cuda.CUDAGraph()
@@ -256,14 +276,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp8xfp4",
         "data": "synthetic",
         "config": {"workload": workload, "batch": batch, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
                    "ctx_len": ctx, "bits": bits, "key_dtype": "bf16", "buffer_sets": n_sets,
                    "record_bytes_per_key": codec.record_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "logits_fused_kernel", "kernel_ms": logits_ms, "algorithmic_bytes": alg_bytes,
+                     "kernel": "logits_fused_kernel", "kernel_ms": logits_ms, "kernel_ms_launches": roof_launches,
+                     "kernel_ms_method": "HIP events around a graph replay of back-to-back launches on the "
+                                         "kernel's stream (per-launch time, the gap between launches included)",
+                     "algorithmic_bytes": alg_bytes,
                      "keys_per_s_kernel": scores_per_step / (logits_ms * 1e-3),
                      "k_only_GBs": rec_bytes / (logits_ms * 1e-3) / 1e9},
         "stages": {"encode_k_ms": enc_ms, "encode_vectors_per_s": n_keys / (enc_ms * 1e-3),
@@ -275,7 +298,7 @@ def main():
 
     if not args.no_stages:
         out["stages"].update(time_stages(B, I, codec, dev, args))
-        ceil = out["stages"].get("stream_read_ceiling_c2_bytes")
+        ceil = out["stages"].get("stream_ceiling_c2_traffic")
         if ceil:  # the same byte count read by a plain streaming kernel, on this machine
             out["roofline"]["stream_ceiling_GBs"] = ceil["achieved_GBs"]
             out["roofline"]["frac_of_stream_ceiling"] = achieved / ceil["achieved_GBs"]
@@ -584,17 +607,43 @@ def time_stages(B, I, codec3, dev, args):
     del kp4, sets
     res.update(polar_stage(B, I, dev, k, q, ctx, d))
     del k
-    # Streaming-read ceiling at the C2 step's algorithmic byte count: plain
-    # 16-byte loads (tq_diag_stream_read), rotating buffers, timed the same way
-    nbytes = (8 * 32768 * codec3.record_bytes + 32 * 32768 * 4 + 32 * d * 2) // 16 * 16
+    # Streaming ceiling at the C2 step's algorithmic traffic: one launch that
+    # reads the records' bytes and writes the logits' bytes (tq_diag_stream:
+    # four independent 16-byte loads per thread), rotating buffers, timed the
+    # same way; and a plain read of the whole byte count
+    rbytes = (8 * 32768 * codec3.record_bytes + 32 * d * 2) // 16 * 16
+    wbytes = 32 * 32768 * 4
     ns = 29
-    bufs = [torch.randint(0, 1 << 30, (nbytes // 4,), generator=g, device=dev, dtype=torch.int32) for _ in range(ns)]
-    sink = torch.empty(B.lib.tq_diag_stream_blocks(), dtype=torch.int32, device=dev)
+    bufs = [torch.randint(0, 1 << 30, (rbytes // 4,), generator=g, device=dev, dtype=torch.int32) for _ in range(ns)]
+    outs = [torch.empty(wbytes // 4, dtype=torch.int32, device=dev) for _ in range(ns)]
+    sink = torch.empty(B.lib.tq_diag_stream_sink_words(rbytes + wbytes), dtype=torch.int32, device=dev)
     it = iter(range(10 ** 9))
-    ms = _time(lambda: B.tq_diag_stream_read(bufs[next(it) % ns], sink), 240, graph=True)
-    res["stream_read_ceiling_c2_bytes"] = {"ms": ms, **_hbm(ms, nbytes), "buffer_sets": ns}
-    print(f"[bench] streaming read of {nbytes / 1e6:.1f} MB: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
-    del bufs, sink
+
+    def rw():
+        i = next(it) % ns
+        B.tq_diag_stream(bufs[i], outs[i], sink)
+    ms = _time(rw, 240, graph=True)
+    res["stream_ceiling_c2_traffic"] = {"ms": ms, **_hbm(ms, rbytes + wbytes), "read_bytes": rbytes,
+                                        "write_bytes": wbytes, "buffer_sets": ns}
+    print(f"[bench] streaming read {rbytes / 1e6:.1f} MB + write {wbytes / 1e6:.1f} MB: {ms * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+    del bufs, outs, sink
+    # the same at the batch-16 step's traffic (16x; two buffer sets of 302 MB)
+    bufs = [torch.randint(0, 1 << 30, (16 * rbytes // 4,), generator=g, device=dev, dtype=torch.int32)
+            for _ in range(2)]
+    outs = [torch.empty(16 * wbytes // 4, dtype=torch.int32, device=dev) for _ in range(2)]
+    sink = torch.empty(B.lib.tq_diag_stream_sink_words(16 * rbytes), dtype=torch.int32, device=dev)
+    it = iter(range(10 ** 9))
+
+    def rw16():
+        i = next(it) % 2
+        B.tq_diag_stream(bufs[i], outs[i], sink)
+    ms = _time(rw16, 40, graph=True)
+    res["stream_ceiling_c2_traffic_batch16"] = {"ms": ms, **_hbm(ms, 16 * (rbytes + wbytes)),
+                                                "read_bytes": 16 * rbytes, "write_bytes": 16 * wbytes,
+                                                "buffer_sets": 2}
+    print(f"[bench] streaming ceiling at batch 16: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
+    del bufs, outs, sink
     # C2 at batch 16: the same decode step, 16 sequences (the streaming asymptote)
     bsz = 16
     k = torch.randn((bsz * 8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
@@ -685,7 +734,8 @@ def time_stages(B, I, codec3, dev, args):
         res["encode_c5"] = {"ms": ms, "vectors_per_s": n_db / (ms * 1e-3), "bound": "mfma (fp16)",
                             "algorithmic_tflop": flops / 1e12, "algorithmic_TFLOPs": flops / (ms * 1e-3) / 1e12,
                             "matrix_TFLOPs": executed / (ms * 1e-3) / 1e12,
-                            "frac": executed / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS}
+                            "frac": flops / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+                            "frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS}
         print(f"[bench] C5 encode {ms:.2f} ms", file=sys.stderr, flush=True)
         del db, ws
         ws = torch.empty(B.tq_search_workspace(c16, n_db, nqs, 10), dtype=torch.uint8, device=dev)
@@ -696,51 +746,122 @@ def time_stages(B, I, codec3, dev, args):
         # matrix ops issued: per (16 queries, 16 records, 128 coordinates) 15 (MSE, 4 planes) + 3 (QJL)
         ops = (nqs // 16) * (n_db // 16) * (ds // 128) * 18
         executed = ops * 16 * 16 * 128 * 2
-        res["search_c5"] = {"ms": ms, "scores_per_s": nqs * n_db / (ms * 1e-3), "bound": "mfma",
+        res["search_c5"] = {"ms": ms, "scores_per_s": nqs * n_db / (ms * 1e-3), "bound": "mfma (fp8 x fp4)",
                             "algorithmic_tflop": alg / 1e12, "algorithmic_TFLOPs": alg / (ms * 1e-3) / 1e12,
                             "matrix_TFLOPs": executed / (ms * 1e-3) / 1e12,
-                            "frac": executed / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
+                            "frac": alg / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                            "frac_executed": executed / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS}
         print(f"[bench] C5 search {ms:.2f} ms", file=sys.stderr, flush=True)
     return res
 
 
+def _timed(fn, budget_s, max_reps=20):
+    """Median seconds of fn over repetitions that fit about budget_s (at least one)."""
+    ts = []
+    while not ts or (sum(ts) < budget_s and len(ts) < max_reps):
+        t = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t)
+    ts.sort()
+    return ts[len(ts) // 2], len(ts)
+
+
 def cpu_baseline(w, k_host, q_host, bits):
-    """The fp64 NumPy oracle timed on this host: encode + score of the full
-    decode-logits workload (one step), repeated until about 10 s have run."""
+    """The fp64 NumPy oracle (oracle/, unmodified) timed on this host, beside
+    the GPU: the headline decode-logits workload in full, and a bounded sample
+    of every other configuration (sizes stated in each entry, scaled to the
+    whole workload linearly in the number of vectors or scores).  Input
+    generation is outside the timed regions."""
     import numpy as np
     import oracle as O
+    from kv_cache_quantization_03_amd import inputs as I
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max((x.get("num_threads", 1) for x in threadpool_info()), default=1)
     except Exception:
+        threadpool_limits = None
         blas_threads = os.cpu_count()
+    one_thread = (lambda: threadpool_limits(limits=1)) if threadpool_limits else None
+    cfg = {}
+
+    # C2, the headline: one decode step's scores over the full 32K context
     oc = O.make_codec(w["d"], bits, seed=1234)
     k64 = k_host.astype(np.float64)
-    t = time.perf_counter()
+    n_enc = 32768
+    enc_s, _ = _timed(lambda: O.encode(oc, k64[:n_enc]), 3.0, 3)
     rec = O.encode(oc, k64)
-    enc_s = time.perf_counter() - t
-    reps, tot = 0, 0.0
-    while tot < 10.0 and reps < 20:
-        t = time.perf_counter()
-        O.attn_logits(oc, q_host.astype(np.float64), rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1, w["ctx"])
-        tot += time.perf_counter() - t
-        reps += 1
-    score_s = tot / reps
+    qh = q_host.astype(np.float64)
+    score = lambda: O.attn_logits(oc, qh, rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1, w["ctx"])
+    score_s, reps = _timed(score, 8.0)
     n_scores = w["batch"] * w["n_q_heads"] * w["ctx"]
     one_core = None
-    try:  # the same scoring with the BLAS pool limited to one thread
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            t = time.perf_counter()
-            O.attn_logits(oc, q_host.astype(np.float64), rec, w["batch"], w["n_q_heads"], w["n_kv_heads"], 1,
-                          w["ctx"])
-            one_core = n_scores / (time.perf_counter() - t)
-    except Exception:
-        pass
-    return {"value": n_scores / score_s, "unit": "keys/s", "cores": blas_threads, "kind": "oracle",
-            "sample": f"full workload ({n_scores} scores) x{reps}; encode of {k_host.shape[0]} keys took "
-                      f"{enc_s:.2f}s ({k_host.shape[0] / enc_s:.0f} vectors/s)",
-            "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(), "value_one_thread": one_core}
+    if one_thread:
+        with one_thread():
+            s1, _ = _timed(score, 2.0, 1)
+        one_core = n_scores / s1
+    headline = {"value": n_scores / score_s, "unit": "keys/s", "cores": blas_threads, "kind": "oracle",
+                "sample": f"the full workload ({n_scores} scores per step), median of {reps} runs; the step's "
+                          f"encode timed on {n_enc} of its {k_host.shape[0]} keys",
+                "encode_vectors_per_s": n_enc / enc_s, "value_one_thread": one_core,
+                "os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model()}
+
+    # C1: the whole tiny reference (4096 fp32 keys, one query)
+    t1 = I.tiny_ref()
+    kt = t1["keys"].rows().astype(np.float64)
+    qt = t1["queries"].rows().reshape(1, 1, 1, 128).astype(np.float64)
+    e1, _ = _timed(lambda: O.encode(oc, kt), 2.0, 5)
+    rt = O.encode(oc, kt)
+    s1, _ = _timed(lambda: O.attn_logits(oc, qt, rt, 1, 1, 1, 1, 4096), 1.0, 5)
+    c1 = {"encode_vectors_per_s": 4096 / e1, "scores_per_s": 4096 / s1, "sample": "whole workload"}
+    if one_thread:
+        with one_thread():
+            e1s, _ = _timed(lambda: O.encode(oc, kt), 1.0, 1)
+            s1s, _ = _timed(lambda: O.attn_logits(oc, qt, rt, 1, 1, 1, 1, 4096), 0.5, 1)
+        c1.update({"encode_vectors_per_s_one_thread": 4096 / e1s, "scores_per_s_one_thread": 4096 / s1s})
+    cfg["tiny_ref_4096x128_f32"] = c1
+    if one_thread:
+        with one_thread():
+            e2s, _ = _timed(lambda: O.encode(oc, k64[:8192]), 1.0, 1)
+        headline["encode_vectors_per_s_one_thread"] = 8192 / e2s
+
+    # C3: encode 16384 of the 2^21 K and V rows; score one (sequence, KV head):
+    # 16 queries x 8192 keys (of 16 x 8 such pairs)
+    p3 = I.prefill_encode()
+    k3 = p3["keys"].rows(0, 16384).astype(np.float64)
+    e3, _ = _timed(lambda: O.encode(oc, k3), 2.0, 2)
+    r3 = O.encode(oc, p3["keys"].rows(0, 8192).astype(np.float64))
+    q3 = p3["queries"].rows().reshape(16, 16, 8, 128)[0:1, :, 0:1].astype(np.float64)
+    s3, _ = _timed(lambda: O.attn_logits(oc, q3, r3, 1, 1, 1, 16, 8192), 2.0, 3)
+    cfg[p3["name"]] = {"encode_vectors_per_s": 16384 / e3, "scores_per_s": 16 * 8192 / s3,
+                       "encode_s_full": 2 * 16 * 8 * 8192 / (16384 / e3), "score_s_full": 128 * s3,
+                       "sample": "encode of 16384 K rows; scores of one (sequence, KV head): 16 queries x 8192 keys"}
+
+    # C4: decode attention of one KV head (4 query heads) over 32768 of the
+    # 131072 positions, scaled x4 (context) x8 (KV heads)
+    w4 = I.long_decode()
+    k4 = O.encode(oc, w4["keys"].rows(0, 32768).astype(np.float64))
+    v4 = O.encode(oc, w4["values"].rows(0, 32768).astype(np.float64))
+    q4 = w4["queries"].rows()[:4].reshape(1, 4, 128).astype(np.float64)
+    s4, _ = _timed(lambda: O.decode_attn_accumulated(oc, oc, q4, k4, v4, 1, 4, 1, 32768, w4["scale"]), 2.0, 3)
+    full4 = s4 * 4 * 8
+    cfg[w4["name"]] = {"step_s_full": full4, "keys_per_s": 4 * 32768 / s4,
+                       "sample": "one KV head (4 query heads) x 32768 positions, scaled x32 to the step"}
+
+    # C5: encode 2048 database rows; score 64 queries against them (scaled to
+    # 1024 queries x 10^6 rows)
+    w5 = I.vector_search()
+    c16 = O.make_codec(1536, 4, seed=1234)
+    x5 = w5["db"].rows(0, 2048).astype(np.float64)
+    e5, _ = _timed(lambda: O.encode(c16, x5), 2.0, 2)
+    r5 = O.encode(c16, x5)
+    q5 = w5["queries"].rows(0, 64).astype(np.float64)
+    s5, _ = _timed(lambda: O.score(c16, q5, r5), 2.0, 3)
+    sps = 64 * 2048 / s5
+    cfg[w5["name"]] = {"encode_vectors_per_s": 2048 / e5, "scores_per_s": sps,
+                       "encode_s_full": 1e6 / (2048 / e5), "search_s_full": 1024 * 1e6 / sps,
+                       "sample": "encode of 2048 rows; 64 queries x 2048 rows scored (linear in both)"}
+    headline["configs"] = cfg
+    return headline
 
 
 if __name__ == "__main__":

@@ -397,15 +397,18 @@ tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db, const flo
                            void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- measurement
- * Not part of the method: the streaming-read ceiling the kernels' HBM rates are
- * compared with.  Reads `bytes` (a multiple of 16) at the 16-byte aligned
- * device pointer `src` with plain 16-byte loads, as one launch of
- * tq_diag_stream_blocks() blocks of 256 threads, and writes one XOR word per
- * block to the device array sink[tq_diag_stream_blocks()] (so the loads are
- * not removed).  TQ_ERROR_INVALID_VALUE for a null pointer or a byte count
- * that is not a multiple of 16, TQ_ERROR_MISALIGNED for a misaligned src. */
-int32_t tq_diag_stream_blocks(void);
-tq_status_t tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+ * Not part of the method: the streaming ceiling the kernels' HBM rates are
+ * compared with.  One launch reads read_bytes at src and writes write_bytes
+ * (a fixed pattern) at dst, with the access pattern that keeps the most bytes
+ * in flight: blocks of 256 threads, each thread issuing four independent
+ * 16-byte non-temporal loads (or stores) before using any.  One XOR word per
+ * 16 KiB read block goes to the device array sink[tq_diag_stream_sink_words(
+ * read_bytes)], so the loads are not removed.  Both byte counts must be
+ * multiples of 16 (else TQ_ERROR_INVALID_VALUE), src and dst 16-byte aligned
+ * (else TQ_ERROR_MISALIGNED); either count may be 0. */
+int64_t tq_diag_stream_sink_words(size_t read_bytes);
+tq_status_t tq_diag_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                           void* stream);
 
 #ifdef __cplusplus
 }

@@ -80,8 +80,8 @@ def _load():
                                            C.c_float, C.c_float, vp, C.c_int, vp, sz, vp]),
         "tq_search_workspace": (sz, [vp, i64, i32, i32]),
         "tq_search_topk": (C.c_int, [vp, P, i64, vp, i32, i32, vp, vp, vp, sz, vp]),
-        "tq_diag_stream_blocks": (i32, []),
-        "tq_diag_stream_read": (C.c_int, [vp, sz, vp, vp]),
+        "tq_diag_stream_sink_words": (i64, [sz]),
+        "tq_diag_stream": (C.c_int, [vp, sz, vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -98,7 +98,7 @@ EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_bui
             "tq_decode_attn_no_alloc",
             "tq_encode_append_paged_workspace", "tq_encode_append_paged", "tq_decode_attn_paged_workspace",
             "tq_decode_attn_paged", "tq_attn_logits_paged_workspace", "tq_attn_logits_paged",
-            "tq_search_workspace", "tq_search_topk", "tq_diag_stream_blocks", "tq_diag_stream_read")
+            "tq_search_workspace", "tq_search_topk", "tq_diag_stream_sink_words", "tq_diag_stream")
 
 
 def _check(status: int, where: str):
@@ -445,13 +445,16 @@ def tq_search_topk(codec: Codec, db: Packed, queries, topk: int, out_idx=None, o
     return out_idx, out_score
 
 
-def tq_diag_stream_read(buf, sink=None):
-    """Streaming-read ceiling: plain 16-byte loads over the device tensor buf
-    (measurement helper, not part of the method).  sink: uint32 device tensor of
-    tq_diag_stream_blocks() words (allocated when None); returns it."""
+def tq_diag_stream(src, dst=None, sink=None):
+    """Streaming ceiling (measurement helper, not part of the method): reads
+    the device tensor src and writes dst (if given) in one launch.  sink:
+    int32 device tensor of tq_diag_stream_sink_words() words (allocated when
+    None); returns it."""
     torch = _torch()
+    rb = src.numel() * src.element_size()
+    wb = 0 if dst is None else dst.numel() * dst.element_size()
     if sink is None:
-        sink = torch.empty(lib.tq_diag_stream_blocks(), dtype=torch.int32, device=buf.device)
-    st = lib.tq_diag_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf))
-    _check(st, "tq_diag_stream_read")
+        sink = torch.empty(max(1, lib.tq_diag_stream_sink_words(rb)), dtype=torch.int32, device=src.device)
+    st = lib.tq_diag_stream(_ptr(src), rb, None if dst is None else _ptr(dst), wb, _ptr(sink), _stream(src))
+    _check(st, "tq_diag_stream")
     return sink

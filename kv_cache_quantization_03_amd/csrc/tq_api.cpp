@@ -481,16 +481,33 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
 }
 
 namespace tq {
-int diag_stream_blocks();
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
+int64_t diag_stream_sink_words(size_t read_bytes);
+hipError_t launch_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes, uint32_t* sink,
+                         hipStream_t s);
 }  // namespace tq
 
-extern "C" int32_t tq_diag_stream_blocks(void) { return tq::diag_stream_blocks(); }
+extern "C" int64_t tq_diag_stream_sink_words(size_t read_bytes) { return tq::diag_stream_sink_words(read_bytes); }
 
-extern "C" tq_status_t tq_diag_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+extern "C" tq_status_t tq_diag_stream(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                                      uint32_t* sink, void* stream) {
   tq::clear_error();
-  if (!src || !sink || bytes % 16 != 0) { set_error("need src, sink and a byte count that is a multiple of 16"); return TQ_ERROR_INVALID_VALUE; }
-  if (!aligned(src, 16) || !aligned(sink, 4)) { set_error("src must be 16-byte aligned, sink 4-byte aligned"); return TQ_ERROR_MISALIGNED; }
-  if (bytes == 0) return TQ_SUCCESS;
-  return finish(tq::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)), "tq_diag_stream_read launch");
+  if (read_bytes % 16 != 0 || write_bytes % 16 != 0) {
+    set_error("read_bytes and write_bytes must be multiples of 16");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if ((read_bytes && (!src || !sink)) || (write_bytes && !dst)) {
+    set_error("src and sink (with read_bytes > 0) and dst (with write_bytes > 0) must be non-NULL");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(sink, 4)) {
+    set_error("src and dst must be 16-byte aligned, sink 4-byte aligned");
+    return TQ_ERROR_MISALIGNED;
+  }
+  if (static_cast<uint64_t>(tq::diag_stream_sink_words(read_bytes)) +
+          (write_bytes + 16383) / 16384 > 0x7FFFFFFFull) {
+    set_error("read_bytes + write_bytes too large for one launch");
+    return TQ_ERROR_INVALID_VALUE;
+  }
+  return finish(tq::launch_stream(src, read_bytes, dst, write_bytes, sink, static_cast<hipStream_t>(stream)),
+                "tq_diag_stream launch");
 }

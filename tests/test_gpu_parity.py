@@ -1056,16 +1056,23 @@ def test_search_massive_ties(B, bits, k):
     assert np.allclose(sc, full[0, idx], rtol=0, atol=1e-4 * np.max(np.abs(full[0])))
 
 
-def test_diag_stream_read_touches_every_word(B):
-    """The streaming-read ceiling kernel reads every word: the XOR of its
-    per-block words is the XOR of the buffer."""
+def test_diag_stream_touches_every_word(B):
+    """The streaming ceiling kernel reads every word (the XOR of its per-block
+    words is the XOR of the buffer, ragged last block included) and writes
+    every word of dst."""
     x = np.random.default_rng(9).integers(0, 2 ** 31, size=(1 << 18) + 12, dtype=np.int64).astype(np.int32)
     t = torch.from_numpy(x).cuda()
-    sink = B.tq_diag_stream_read(t)
+    dst = torch.zeros((1 << 16) + 4, dtype=torch.int32, device="cuda")
+    sink = B.tq_diag_stream(t, dst)
     torch.cuda.synchronize()
+    assert sink.numel() == B.lib.tq_diag_stream_sink_words(t.numel() * 4) == -(-t.numel() * 4 // 16384)
     assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(x)
-    st = B.lib.tq_diag_stream_read(t.data_ptr(), 40, sink.data_ptr(), None)  # not a multiple of 16
+    d = dst.cpu().numpy().reshape(-1, 4)
+    assert np.all(d[:, 2] == np.int32(np.uint32(0x9E3779B9).astype(np.int32)))
+    st = B.lib.tq_diag_stream(t.data_ptr(), 40, None, 0, sink.data_ptr(), None)  # not a multiple of 16
     assert st == 1
+    st = B.lib.tq_diag_stream(t.data_ptr() + 4, 64, None, 0, sink.data_ptr(), None)
+    assert st == 3
 
 
 # ---------------------------------------------------------------- argument checks with a real codec
