@@ -144,12 +144,14 @@ def assert_sparse_v_within_plain_rule(out, plain, w, gate, vhat, hkv, ctx, tol):
 ANGLE_BAND = 1e-5  # rad
 
 
-def check_polar_encode(pc: O.PolarCodec, x64: np.ndarray, gpu: dict, label: str = "") -> dict:
+def check_polar_encode(pc: O.PolarCodec, x64: np.ndarray, gpu: dict, label: str = "", max_rate=None) -> dict:
     """Compare a GPU encode with a polar codec against the oracle.  Angle
     codes: bit-exact except angles within ANGLE_BAND of the boundary between
-    the two codes (for level 1 also of the wrap 0 = 2π), each checked; no rate
-    cap, because a vector whose rotated coordinates share one magnitude (a
-    basis vector) puts many angles exactly on a boundary (multiples of π/4).
+    the two codes (for level 1 also of the wrap 0 = 2π), each checked.  With
+    max_rate (Gaussian rows) the differing codes are also capped at that
+    fraction of all codes (at least one); without it (rows built to sit on
+    boundaries: a basis vector's rotated coordinates share one magnitude, so
+    its angles fall on multiples of π/4) only the per-code check applies.
     Vectors with a differing code are re-derived by the oracle given the
     GPU's codes.  ν and γ: relative 2e-6 and 1e-5 (γ carries
     the fp32 products of the reconstruction); signs: bit-exact except |z| < BAND."""
@@ -159,6 +161,8 @@ def check_polar_encode(pc: O.PolarCodec, x64: np.ndarray, gpu: dict, label: str 
     ri = ref["idx"]
     diff = gi != ri
     n_diff = int(diff.sum())
+    if max_rate is not None:
+        assert n_diff <= max(1, int(max_rate * diff.size)), f"{label}: {n_diff} angle codes differ of {diff.size}"
     if n_diff:
         L = 1 << pc.b
         for v, s in zip(*np.nonzero(diff)):

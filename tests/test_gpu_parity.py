@@ -926,8 +926,32 @@ def test_polar_encode_parity(B, bits, dtype):
     x = rand_keys(1500, 128, seed=300 + bits, dtype=dtype)   # includes a zero vector and a near-basis one
     kp, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
     torch.cuda.synchronize()
-    st = check_polar_encode(pc, x.astype(np.float64), kp.numpy(), f"polar b{bits}")
-    say(f"  angle codes differing (in band): {st['code_mismatch']}, signs in band: {st['sign_mismatch']}")
+    g = kp.numpy()
+    gauss = np.ones(len(x), dtype=bool)
+    gauss[[3, 5]] = False                                      # the zero and the basis-like rows
+    st = check_polar_encode(pc, x[gauss].astype(np.float64), {k: v[gauss] for k, v in g.items()},
+                            f"polar b{bits}", max_rate=1e-5)
+    say(f"  Gaussian rows: angle codes differing (in band): {st['code_mismatch']} of {gauss.sum() * 127}, "
+        f"signs in band: {st['sign_mismatch']}")
+    st = check_polar_encode(pc, x[~gauss].astype(np.float64), {k: v[~gauss] for k, v in g.items()},
+                            f"polar b{bits} special rows")
+    say(f"  zero and basis-like rows: angle codes differing (in band): {st['code_mismatch']}")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_polar_encode_basis_vectors(B, bits):
+    # x = s·e_k: the rotated coordinates all have magnitude s/√d, so every
+    # level-1 angle is an odd multiple of π/4 (a boundary of the uniform 2- and
+    # 3-bit level-1 quantizers) and every higher-level angle is π/4; codes may
+    # go either way there, each checked against its boundary, with no rate cap
+    gc, pc = polar_pair(B, bits)
+    x = np.zeros((128, 128))
+    x[np.arange(128), np.arange(128)] = np.linspace(0.5, 4.0, 128)
+    x = as_exact(x, "f32")
+    kp, _ = B.tq_encode_kv(gc, to_dev(x, "f32"))
+    torch.cuda.synchronize()
+    st = check_polar_encode(pc, x.astype(np.float64), kp.numpy(), f"polar basis b{bits}")
+    say(f"polar basis vectors b{bits}: angle codes differing (in band): {st['code_mismatch']} of {128 * 127}")
 
 
 @pytest.mark.parametrize("bits,batch,hq,hkv,nq,ctx", [(3, 1, 8, 2, 1, 1000), (2, 2, 4, 4, 3, 333), (4, 1, 32, 8, 1, 257),
