@@ -344,14 +344,16 @@ def _hbm(ms, nbytes):
     return {"bound": "hbm", "algorithmic_bytes": nbytes, "achieved_GBs": gbs, "frac": gbs / PEAK_HBM_GBS}
 
 
-def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d):
-    """Sparse V on the long-context decode shape.  Needle cache: the same
-    haystack keys plus, with probability 1/512 per (KV head, position), a key
-    z + 64·u, u the unit sum of that KV head's four queries (peaked attention,
-    as in long-context decoding); values unchanged.  Times plain decode and
-    the gate 1e-6 on the needle cache, and the gate on the Gaussian cache
-    (where it drops nothing: its cost).  The dropped fraction of 128-key
-    blocks comes from the cache's own logits (tq_attn_logits)."""
+def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d, tag="c4", vblock=None):
+    """Sparse V on a decode shape (32 query heads, 8 KV heads, ctx keys).
+    Needle cache: the same haystack keys plus, with probability 1/512 per (KV
+    head, position), a key z + 64·u, u the unit sum of that KV head's four
+    queries (peaked attention, as in long-context decoding); values unchanged.
+    Times plain decode and the gate 1e-6 on the needle cache, and the gate on
+    the Gaussian cache (where it drops nothing: its cost); with `vblock` =
+    (V codec in 32-row blocks, its V sets), plain and gated decode on the
+    needle cache again with that V.  The dropped fraction of 128-key blocks
+    comes from the cache's own logits (tq_attn_logits)."""
     import torch
     gate, scale, hkv, hq = 1e-6, 1 / math.sqrt(d), 8, 32
     u = qd.float().view(hkv, hq // hkv, d).sum(1)
@@ -367,29 +369,36 @@ def sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d):
     keep = e >= gate * e.sum(dim=-1, keepdim=True)
     dropped = float((~keep.view(hkv, hq // hkv, ctx // 128, 128).any(dim=3).any(dim=1)).float().mean())
     del lg, sc, e, keep
-    ns = 4
+    ns = max(4, len(dsets))
     nsets = [(kpn if i == 0 else B.Packed(kpn.codes.clone(), kpn.signs.clone(), kpn.norm.clone(), kpn.rnorm.clone()),
               dsets[i % len(dsets)][1]) for i in range(ns)]
+    runs = [(f"decode_attn_{tag}_needles_plain", nsets, False, codec3),
+            (f"decode_attn_{tag}_needles_sparse_v", nsets, True, codec3),
+            (f"decode_attn_{tag}_gaussian_sparse_v", dsets, True, codec3)]
+    if vblock is not None:
+        cvb, vbsets = vblock
+        bsets = [(kk, vbsets[i % len(vbsets)]) for i, (kk, _) in enumerate(nsets)]
+        runs += [(f"decode_attn_{tag}_needles_plain_vblock", bsets, False, cvb),
+                 (f"decode_attn_{tag}_needles_sparse_v_vblock", bsets, True, cvb)]
     res = {}
-    for name, sets, gated in (("decode_attn_c4_needles_plain", nsets, False),
-                              ("decode_attn_c4_needles_sparse_v", nsets, True),
-                              ("decode_attn_c4_gaussian_sparse_v", dsets, True)):
+    for name, sets, gated, cv in runs:
         it = iter(range(10 ** 9))
 
         def step():
             kk, vv = sets[next(it) % len(sets)]
             if gated:
-                B.tq_decode_attn_sparse_v(codec3, codec3, qd, kk, vv, ctx, hkv, scale, gate, out=out, ws=ws)
+                B.tq_decode_attn_sparse_v(codec3, cv, qd, kk, vv, ctx, hkv, scale, gate, out=out, ws=ws)
             else:
-                B.tq_decode_attn(codec3, codec3, qd, kk, vv, ctx, hkv, scale, out=out, ws=ws)
+                B.tq_decode_attn(codec3, cv, qd, kk, vv, ctx, hkv, scale, out=out, ws=ws)
         ms = _time(step, 30, graph=True)
         res[name] = {"ms": ms, "buffer_sets": len(sets), "gate": gate if gated else None}
         print(f"[bench] {name} {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
     needle_v = 8 * ctx * codec3.record_bytes * (1 - dropped)
-    r = res["decode_attn_c4_needles_sparse_v"]
-    r["dropped_block_fraction"] = dropped
-    r["speedup_vs_plain"] = res["decode_attn_c4_needles_plain"]["ms"] / r["ms"]
-    r.update(_hbm(r["ms"], 8 * ctx * codec3.record_bytes + needle_v + 2 * hq * d * 2))
+    for suffix in ("", "_vblock") if vblock is not None else ("",):
+        r = res[f"decode_attn_{tag}_needles_sparse_v{suffix}"]
+        r["dropped_block_fraction"] = dropped
+        r["speedup_vs_plain"] = res[f"decode_attn_{tag}_needles_plain{suffix}"]["ms"] / r["ms"]
+        r.update(_hbm(r["ms"], 8 * ctx * codec3.record_bytes + needle_v + 2 * hq * d * 2))
     del kpn, nsets
     return res
 
@@ -671,12 +680,20 @@ def time_stages(B, I, codec3, dev, args):
     v = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
     qd = torch.randn((1, 32, d), generator=g, device=dev).to(torch.bfloat16)
     kp, vp = B.tq_encode_kv(codec3, k, v)
+    # the same V in 32-row blocks (a codec with codec3's tables)
+    cvb = B.tq_codec_create_vblock(d, 3, False, I.CODEC_SEED)
+    vbp = B.alloc_packed(cvb, 8 * ctx, dev)
+    wse = torch.empty(max(B.tq_encode_workspace(cvb, 8 * ctx), 1), dtype=torch.uint8, device=dev)
+    ms_vbe = _time(lambda: B.tq_encode_kv(cvb, v, k_out=vbp, ws=wse), 10, graph=True)
+    ms_vre = _time(lambda: B.tq_encode_kv(codec3, v, k_out=vp, ws=wse), 10, graph=True)
     k_c4 = k
-    del k, v
+    del k, v, wse
     ns = 3
     dsets = [(kp, vp)] + [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
                            B.Packed(vp.codes.clone(), vp.signs.clone(), vp.norm.clone(), vp.rnorm.clone()))
                           for _ in range(ns - 1)]
+    vbsets = [vbp] + [B.Packed(vbp.codes.clone(), vbp.signs.clone(), vbp.norm.clone(), vbp.rnorm.clone())
+                      for _ in range(ns - 1)]
     out = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(B.tq_decode_attn_workspace(codec3, codec3, 1, 32, 8, ctx), dtype=torch.uint8, device=dev)
     it = iter(range(10 ** 9))
@@ -688,11 +705,46 @@ def time_stages(B, I, codec3, dev, args):
     res["decode_attn_c4"] = {"ms": ms, "buffer_sets": ns,
                              **_hbm(ms, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
     print(f"[bench] C4 decode attention {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+    it = iter(range(10 ** 9))
+
+    def c4b():
+        i = next(it) % ns
+        B.tq_decode_attn(codec3, cvb, qd, dsets[i][0], vbsets[i], ctx, 8, 1 / math.sqrt(d), out=out, ws=ws)
+    ms_b = _time(c4b, 30, graph=True)
+    o_row = B.tq_decode_attn(codec3, codec3, qd, kp, vp, ctx, 8, 1 / math.sqrt(d), out_dtype=torch.float32)
+    o_blk = B.tq_decode_attn(codec3, cvb, qd, kp, vbp, ctx, 8, 1 / math.sqrt(d), out_dtype=torch.float32)
+    res["decode_attn_c4_vblock"] = {"ms": ms_b, "buffer_sets": ns, "speedup_vs_row_v": ms / ms_b,
+                                    "equal_to_row_v": bool(torch.equal(o_row, o_blk)),
+                                    "v_encode_ms": ms_vbe, "v_encode_row_ms": ms_vre,
+                                    **_hbm(ms_b, 2 * 8 * ctx * codec3.record_bytes + 2 * 32 * d * 2)}
+    del o_row, o_blk
+    print(f"[bench] C4 decode attention, V in 32-row blocks {ms_b * 1e3:.1f} us "
+          f"(V encode {ms_vbe * 1e3:.1f} us, rows {ms_vre * 1e3:.1f} us)", file=sys.stderr, flush=True)
     if not args.no_stage_sparse_v:
-        res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d))
+        res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d, vblock=(cvb, vbsets)))
     res.update(paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d))
     res.update(mse_v_stage(B, codec3, dev, g, dsets, qd, out, ctx, d))
-    del kp, vp, dsets, ws, k_c4
+    del kp, vp, dsets, ws, k_c4, vbp, vbsets
+    if not args.no_stage_sparse_v:
+        # Sparse V on the 32K decode shape: 12 K/V sets (about 2.6x the Infinity Cache)
+        ctx = 32768
+        k = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((8 * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+        kp, vp = B.tq_encode_kv(codec3, k, v)
+        vbp = B.alloc_packed(cvb, 8 * ctx, dev)
+        B.tq_encode_kv(cvb, v, k_out=vbp)
+        del v
+        ns = 12
+        dsets = [(kp, vp)] + [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
+                               B.Packed(vp.codes.clone(), vp.signs.clone(), vp.norm.clone(), vp.rnorm.clone()))
+                              for _ in range(ns - 1)]
+        vbsets = [vbp] + [B.Packed(vbp.codes.clone(), vbp.signs.clone(), vbp.norm.clone(), vbp.rnorm.clone())
+                          for _ in range(ns - 1)]
+        ws = torch.empty(B.tq_decode_attn_workspace(codec3, codec3, 1, 32, 8, ctx), dtype=torch.uint8, device=dev)
+        res.update(sparse_v_stage(B, codec3, dev, g, k, vp, dsets, qd, out, ws, ctx, d, tag="c2",
+                                  vblock=(cvb, vbsets)))
+        del k, kp, vp, vbp, dsets, vbsets, ws
+    del cvb
     # C3: prefill encode of K and V [16][8][8192][128] bf16, then 16 queries per sequence
     bsz, hkv, ctx, nq = 16, 8, 8192, 16
     n = bsz * hkv * ctx

@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 
 typedef struct tq_codec_s* tq_codec_t; /* opaque; immutable after create, usable from any stream */
 
@@ -124,6 +124,7 @@ typedef struct {
   double centroids[16]; /* 2^b entries, ascending, fp64 */
   double bounds[15];    /* 2^b - 1 entries, midpoints of the centroids */
   int32_t stage1;       /* 0: per-coordinate Lloyd-Max codes; 1: recursive polar angles */
+  int32_t layout;       /* 0: row records; 1: 32-row blocks (tq_codec_create_vblock) */
 } tq_codec_info_t;
 
 /* ---------------------------------------------------------------- status */
@@ -180,6 +181,33 @@ tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_di
  * codec role return TQ_ERROR_NOT_SUPPORTED.  head_dim as tq_codec_create;
  * tq_codec_info reports qjl_dim = 0 and sign_words = 0. */
 tq_status_t tq_codec_create_mse(int32_t head_dim, int32_t bits, uint64_t seed, tq_codec_t* out);
+/* A value codec whose records are stored in blocks of 32 rows (head_dim 128;
+ * bits 2, 3 or 4 as tq_codec_create, or with mse_only != 0 the MSE-only codec
+ * of tq_codec_create_mse).  Decode attention accumulates the attention-weighted
+ * values as a contraction over keys (TurboQuant+ 深度解析 第五部分 compresses V
+ * like K; 第六部分: V dequantization is a large share of long-context decode),
+ * which needs each coordinate's bits across 32 consecutive rows; this layout
+ * stores them so:
+ *   block B = rows 32B..32B+31, b = mse_bits planes of codes (bit plane p of
+ *   every code index), then the sign plane.  For coordinate j = 16c + n
+ *   (n < 16, c < 8):
+ *     codes[(B*b + p)*128 + 8n + c]   (words, counting from the array start)
+ *     signs[B*128 + 8n + c]
+ *   bit 4i + r of such a word is the bit of row 32B + 8r + i.
+ *   norm[row] and rnorm[row] stay one float per row.
+ * The arrays have the sizes of row records (codes [n][code_words], ...), and
+ * rows 32B.. of the row layout and block B cover the same words, so offsets
+ * by a multiple of 32 rows work as for row records.  tq_encode_kv writes whole
+ * blocks (n_vec a multiple of 32, else TQ_ERROR_INVALID_VALUE), so an append
+ * through it starts at a multiple of 32 rows; tq_encode_append_paged merges
+ * single rows into their blocks (page_size a multiple of 32; two calls that
+ * write rows of one block may not run concurrently).  Accepted by tq_encode_kv, tq_encode_append_paged and as
+ * the V codec (cv) of the decode attention calls (the contiguous ones need
+ * ctx_len % 32 == 0); every other call returns TQ_ERROR_NOT_SUPPORTED.
+ * Decode results equal those with the row-record codec of the same head_dim,
+ * bits and seed (the codec tables are the same), bit for bit. */
+tq_status_t tq_codec_create_vblock(int32_t head_dim, int32_t bits, int32_t mse_only, uint64_t seed,
+                                   tq_codec_t* out);
 /* Host only (no GPU needed): level l's (1..7) angle codebook of the polar
  * stage for head_dim 128 and the given bits: centroids[2^b] and
  * bounds[2^b - 1], fp64, ascending, and the Lloyd-Max iterations (0 for the

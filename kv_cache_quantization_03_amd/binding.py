@@ -34,7 +34,7 @@ class tq_codec_info_t(C.Structure):
                 ("qjl_dim", C.c_int32), ("code_words", C.c_int32), ("sign_words", C.c_int32),
                 ("record_bytes", C.c_int32), ("lloyd_max_iterations", C.c_int32),
                 ("seed", C.c_uint64), ("centroids", C.c_double * 16), ("bounds", C.c_double * 15),
-                ("stage1", C.c_int32)]
+                ("stage1", C.c_int32), ("layout", C.c_int32)]
 
 
 def _load():
@@ -54,6 +54,7 @@ def _load():
         "tq_codec_info": (C.c_int, [vp, C.POINTER(tq_codec_info_t)]),
         "tq_codec_create_polar": (C.c_int, [i32, i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
         "tq_codec_create_mse": (C.c_int, [i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
+        "tq_codec_create_vblock": (C.c_int, [i32, i32, i32, C.c_uint64, C.POINTER(C.c_void_p)]),
         "tq_polar_book_host": (C.c_int, [i32, i32, i32, C.POINTER(C.c_double), C.POINTER(C.c_double),
                                          C.POINTER(i32)]),
         "tq_encode_workspace": (sz, [vp, i64]),
@@ -92,7 +93,8 @@ def _load():
 
 lib = _load()
 EXPORTED = ("tq_status_string", "tq_last_error", "tq_abi_version", "tq_codec_build_host", "tq_codec_create",
-            "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_codec_create_mse", "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
+            "tq_codec_destroy", "tq_codec_info", "tq_codec_create_polar", "tq_codec_create_mse", "tq_codec_create_vblock",
+            "tq_polar_book_host", "tq_encode_workspace", "tq_encode_kv",
             "tq_attn_logits_workspace", "tq_attn_logits", "tq_attn_query_prep", "tq_attn_logits_prepped",
             "tq_decode_attn_workspace", "tq_decode_attn", "tq_decode_attn_sparse_v", "tq_decode_attn_chunk",
             "tq_decode_attn_no_alloc",
@@ -159,6 +161,7 @@ class Codec:
         self.bounds = np.array(info.bounds[:(1 << self.b) - 1])
         self.polar = info.stage1 == 1
         self.qjl = info.qjl_dim > 0  # False: MSE-only value codec (records: codes and ν)
+        self.vblock = info.layout == 1  # codes and signs in 32-row blocks of transposed words
 
     def __del__(self):
         if getattr(self, "handle", None) and lib is not None:
@@ -185,6 +188,14 @@ def tq_codec_create_polar(head_dim: int, bits: int, qjl_dim: int = 0, seed: int 
 def tq_codec_create_mse(head_dim: int, bits: int, seed: int = 1234) -> Codec:
     h = C.c_void_p()
     _check(lib.tq_codec_create_mse(head_dim, bits, seed, C.byref(h)), "tq_codec_create_mse")
+    info = tq_codec_info_t()
+    _check(lib.tq_codec_info(h, C.byref(info)), "tq_codec_info")
+    return Codec(h, info)
+
+
+def tq_codec_create_vblock(head_dim: int, bits: int, mse_only: bool = False, seed: int = 1234) -> Codec:
+    h = C.c_void_p()
+    _check(lib.tq_codec_create_vblock(head_dim, bits, int(mse_only), seed, C.byref(h)), "tq_codec_create_vblock")
     info = tq_codec_info_t()
     _check(lib.tq_codec_info(h, C.byref(info)), "tq_codec_info")
     return Codec(h, info)

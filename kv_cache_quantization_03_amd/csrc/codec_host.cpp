@@ -517,6 +517,19 @@ extern "C" tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int
   return codec_create(head_dim, bits, qjl_dim, seed, kPolar, out);
 }
 
+extern "C" tq_status_t tq_codec_create_vblock(int32_t head_dim, int32_t bits, int32_t mse_only, uint64_t seed,
+                                              tq_codec_t* out) {
+  tq::clear_error();
+  if (out) *out = nullptr;
+  if (head_dim != 128) {
+    set_error("the 32-row block layout is built for head_dim 128");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  const tq_status_t st = codec_create(head_dim, bits, 0, seed, mse_only ? kMseOnly : kTwoStage, out);
+  if (st == TQ_SUCCESS) (*out)->vblock = true;
+  return st;
+}
+
 extern "C" tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
                                           double* bounds, int32_t* iterations) {
   tq::clear_error();
@@ -572,6 +585,7 @@ extern "C" tq_status_t tq_codec_info(tq_codec_t c, tq_codec_info_t* info) {
   info->record_bytes = 4 * (c->prm.code_words + c->prm.sign_words) + (c->qjl ? 8 : 4);
   info->lloyd_max_iterations = h.iterations;
   info->stage1 = c->polar ? 1 : 0;
+  info->layout = c->vblock ? 1 : 0;
   info->seed = h.seed;
   for (size_t k = 0; k < h.centroids.size(); ++k) info->centroids[k] = h.centroids[k];
   for (size_t k = 0; k < h.bounds.size(); ++k) info->bounds[k] = h.bounds[k];

@@ -443,15 +443,17 @@ size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, in
 }
 
 bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
+bool decode_mfma_shape_ok(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
 int decode_mfma_chunk();
 hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                               tq_packed_t k, tq_packed_t v, int64_t ctx, float scale, bool sparse_v, float v_gate,
                               const PageMap* pm, const uint8_t* prep, float* part, int n_chunks, hipStream_t s);
 
-// Paged caches are read by the matrix-core kernel only (d = 128, at most 4
-// query heads per KV head), with the d = m = 128 combine.
+// Paged caches and V caches in 32-row blocks are read by the matrix-core
+// kernel only (d = 128, at most 4 query heads per KV head), with the
+// d = m = 128 combine.
 bool decode_paged_supported(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
-  return decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == attn_chunk(n_q_heads / n_kv_heads);
+  return decode_mfma_shape_ok(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == attn_chunk(n_q_heads / n_kv_heads);
 }
 
 int decode_chunk(int n_q_heads, int n_kv_heads) { return attn_chunk(n_q_heads / n_kv_heads); }
@@ -469,7 +471,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                          decode_prep_region(ck, batch, n_q_heads, n_kv_heads));
   hipError_t e;
-  if (pm || (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH)) {
+  if (pm || cv->vblock || (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH)) {
     // matrix-core split kernel, same partial layout.  The query operands are
     // prepared once per KV head by their own launch (rebuilding them in every
     // block measured 58.7 against 55.5 us at 32 heads x 128K keys).

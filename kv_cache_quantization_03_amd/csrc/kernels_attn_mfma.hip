@@ -23,14 +23,17 @@
 // dequantization dominates long-context decode).
 //
 // V as a matrix operand.  The contraction over keys needs, in each lane, the
-// bits of one coordinate across 32 keys, while a stored word holds 32
-// coordinates of one key.  Each lane therefore loads the V records of two
-// keys and a 32x32 bit transpose runs in registers: four lane stages (lane
-// bits 0-3, partners through DPP within rows of 16) and one stage between the
-// lane's two registers.  The key each lane loads is chosen so that the
-// transposed words land exactly in the B-operand layout with contraction
-// index = key index (see v_key_of_row).  The parity plane of a 3-bit codebook
-// is the XOR of the transposed stored planes.
+// bits of one coordinate across 32 keys, while a row record holds 32
+// coordinates of one key.  With row records (VB = false) each lane loads the V
+// records of two keys and a 32x32 bit transpose runs in registers: four lane
+// stages (lane bits 0-3, partners through DPP within rows of 16) and one
+// stage between the lane's two registers.  The key each lane loads is chosen
+// so that the transposed words land exactly in the B-operand layout with
+// contraction index = key index (see v_key_of_row).  A V cache in 32-key
+// blocks (VB, tq_codec_create_vblock) holds those transposed words already,
+// written once at encode by the same transpose, and the lanes load them as
+// they are.  The parity plane of a 3-bit codebook is the XOR of the stored
+// planes' words.
 #include <cstdlib>
 #include <string>
 
@@ -44,43 +47,9 @@ constexpr int kDecWaves = 8;
 constexpr int kDecKeysPerWave = 128;
 constexpr int kDecChunk = kDecWaves * kDecKeysPerWave;  // keys per block
 
-// One stage of the bit transpose: swap row bit K (lane bit K) with column bit K.
-template <int K>
-__device__ __forceinline__ uint32_t transpose_stage(uint32_t w, int lane) {
-  constexpr uint32_t M = K == 0 ? 0x55555555u : (K == 1 ? 0x33333333u : (K == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu));
-  constexpr int s = 1 << K;
-  const uint32_t x = lane_xor<K>(w);
-  const bool hi = (lane >> K) & 1;
-  const uint32_t t = hi ? (x >> s) : (x << s);
-  const uint32_t keep = hi ? ~M : M;
-  return (w & keep) | (t & ~keep);
-}
-
-// 32x32 bit transpose within each row of 16 lanes: input row ρ = lane%16 + 16·reg
-// (r0: reg 0, r1: reg 1), column = bit; output lane%16 + 16·reg = column,
-// bit = row.
-__device__ __forceinline__ void transpose32(uint32_t& r0, uint32_t& r1, int lane) {
-  r0 = transpose_stage<0>(r0, lane);
-  r1 = transpose_stage<0>(r1, lane);
-  r0 = transpose_stage<1>(r0, lane);
-  r1 = transpose_stage<1>(r1, lane);
-  r0 = transpose_stage<2>(r0, lane);
-  r1 = transpose_stage<2>(r1, lane);
-  r0 = transpose_stage<3>(r0, lane);
-  r1 = transpose_stage<3>(r1, lane);
-  const uint32_t t = ((r0 >> 16) ^ r1) & 0x0000FFFFu;
-  r1 ^= t;
-  r0 ^= t << 16;
-}
-
-// Key (within the lane group's 32) whose words lane%16 + 16·reg loads: row
-// ρ = 4i + r carries key 8r + i, so that after the transpose bit 4i + r of the
-// word — FP4 nibble i of mask r, contraction index 8r + i — is that key.
-__device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (rho >> 2); }
-
 }  // namespace
 
-template <int NPK, int NPV, bool GATE, bool PAGED, bool VQ>
+template <int NPK, int NPV, bool GATE, bool PAGED, bool VQ, bool VB>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     const uint8_t* __restrict__ prep, DevParams PK, DevParams PV, PageMap pm, int Hq, int nkv, int ctx_max,
     int n_chunks, float scale, float gate, const uint32_t* __restrict__ kc, const uint32_t* __restrict__ ks,
@@ -168,16 +137,36 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   // Issued only after the scores: held through the query prep they push the
   // kernel past 128 registers, and then a CU runs one 8-wave block instead of
   // two.  The gated kernel issues them once the gate has kept the wave.
+  // VB (V in 32-key blocks, written so at encode): the lane's words are
+  // already the B operands: words 8·(lane%16)..+7 of each plane of its block
+  // (keys kbase + 32·(lane/16)..+31), coordinate 16·cb + lane%16 in word cb;
+  // vcv[0] holds cb 0..3, vcv[1] cb 4..7.
   v4u vcv[2][NBV], vsv[2];
   float vnu[8], vga[8];
   auto load_v = [&]() {
+    if constexpr (VB) {
+      const int key = min(kbase + 32 * g, (ctx - 1) & ~31);  // a block past the end re-reads the last one
+      const int64_t blk = row_of(key) >> 5;
 #pragma unroll
-    for (int reg = 0; reg < 2; ++reg) {
-      const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
-      const int64_t row = row_of(key);
+      for (int p = 0; p < NBV; ++p) {
+        const v4u* src = reinterpret_cast<const v4u*>(vc + ((blk * NBV + p) * 128 + kl * 8));
+        vcv[0][p] = src[0];
+        vcv[1][p] = src[1];
+      }
+      if constexpr (VQ) {
+        const v4u* src = reinterpret_cast<const v4u*>(vs + (blk * 128 + kl * 8));
+        vsv[0] = src[0];
+        vsv[1] = src[1];
+      }
+    } else {
 #pragma unroll
-      for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
-      if constexpr (VQ) vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+      for (int reg = 0; reg < 2; ++reg) {
+        const int key = min(kbase + 32 * g + v_key_of_row(kl + 16 * reg), ctx - 1);
+        const int64_t row = row_of(key);
+#pragma unroll
+        for (int p = 0; p < NBV; ++p) vcv[reg][p] = reinterpret_cast<const v4u*>(vc)[row * NBV + p];
+        if constexpr (VQ) vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
+      }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -337,13 +326,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
 #pragma unroll
     for (int p = 0; p < NBV + (VQ ? 1 : 0); ++p) {  // stored planes, then the signs
       uint32_t tw[8];
+      if constexpr (VB) {
 #pragma unroll
-      for (int wb = 0; wb < 4; ++wb) {
-        uint32_t r0 = p < NBV ? vcv[0][p < NBV ? p : 0][wb] : vsv[0][wb];
-        uint32_t r1 = p < NBV ? vcv[1][p < NBV ? p : 0][wb] : vsv[1][wb];
-        transpose32(r0, r1, lane);
-        tw[2 * wb] = r0;
-        tw[2 * wb + 1] = r1;
+        for (int cb = 0; cb < 8; ++cb) tw[cb] = p < NBV ? vcv[cb >> 2][p < NBV ? p : 0][cb & 3] : vsv[cb >> 2][cb & 3];
+      } else {
+#pragma unroll
+        for (int wb = 0; wb < 4; ++wb) {
+          uint32_t r0 = p < NBV ? vcv[0][p < NBV ? p : 0][wb] : vsv[0][wb];
+          uint32_t r1 = p < NBV ? vcv[1][p < NBV ? p : 0][wb] : vsv[1][wb];
+          transpose32(r0, r1, lane);
+          tw[2 * wb] = r0;
+          tw[2 * wb + 1] = r1;
+        }
       }
       // two halves of four 16-coordinate blocks keep the live accumulators at 8 registers
 #pragma unroll
@@ -431,11 +425,17 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
 
 // d = 128 for K and V (QJL dimension 128, or an MSE-only V codec), at most 4
 // query heads per KV head.
+bool decode_mfma_shape_ok(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
+  const int G = n_q_heads / n_kv_heads;
+  return ck->prm.d == 128 && cv->prm.d == 128 && ck->prm.m == 128 && (cv->prm.m == 128 || !cv->qjl) && G <= 4;
+}
+
+// The same, unless TQ_DECODE_KERNEL=valu asks for the general kernel (which
+// reads row records only, so paged and blocked V caches ignore it).
 bool decode_mfma_eligible(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads) {
   const char* v = std::getenv("TQ_DECODE_KERNEL");
   if (v && std::string(v) == "valu") return false;
-  const int G = n_q_heads / n_kv_heads;
-  return ck->prm.d == 128 && cv->prm.d == 128 && ck->prm.m == 128 && (cv->prm.m == 128 || !cv->qjl) && G <= 4;
+  return decode_mfma_shape_ok(ck, cv, n_q_heads, n_kv_heads);
 }
 
 int decode_mfma_chunk() { return kDecChunk; }
@@ -446,10 +446,13 @@ hipError_t launch_decode_mfma(const tq_codec_s* ck, const tq_codec_s* cv, int ba
                               const PageMap* pm, const uint8_t* prep, float* part, int n_chunks, hipStream_t s) {
   const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   auto go = [&]<int NPK, int NPV, bool VQ>() -> hipError_t {
-    auto kern = pm ? (sparse_v ? decode_mfma_kernel<NPK, NPV, true, true, VQ>
-                               : decode_mfma_kernel<NPK, NPV, false, true, VQ>)
-                   : (sparse_v ? decode_mfma_kernel<NPK, NPV, true, false, VQ>
-                               : decode_mfma_kernel<NPK, NPV, false, false, VQ>);
+    auto pick = [&]<bool VB>() {
+      return pm ? (sparse_v ? decode_mfma_kernel<NPK, NPV, true, true, VQ, VB>
+                            : decode_mfma_kernel<NPK, NPV, false, true, VQ, VB>)
+                : (sparse_v ? decode_mfma_kernel<NPK, NPV, true, false, VQ, VB>
+                            : decode_mfma_kernel<NPK, NPV, false, false, VQ, VB>);
+    };
+    auto kern = cv->vblock ? pick.template operator()<true>() : pick.template operator()<false>();
     hipLaunchKernelGGL(kern, dim3(n_chunks, batch * n_kv_heads), dim3(kDecWaves * 64),
                        0, s, prep, ck->prm, cv->prm, pmv, n_q_heads, n_kv_heads, static_cast<int>(ctx),
                        n_chunks, scale, v_gate, k.codes, k.signs, k.norm, k.rnorm, v.codes, v.signs, v.norm, v.rnorm,

@@ -576,7 +576,7 @@ bool encode_fused_eligible(const tq_codec_s* c) {
   return c->prm.d == 128 && c->prm.m == 128 && c->dS16 != nullptr;
 }
 
-size_t encode_ws_bytes(const tq_codec_s* c, int64_t n) {
+size_t encode_rows_ws_bytes(const tq_codec_s* c, int64_t n) {
   if (encode_fused_eligible(c)) return 0;  // the fused kernel keeps r on chip
   if (!c->qjl) return 0;                   // MSE-only: no residual to project
   return static_cast<size_t>(n) * c->prm.d * sizeof(float);
@@ -648,8 +648,8 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
 }
 }  // namespace
 
-hipError_t launch_encode(const tq_codec_s* c, const void* x, tq_dtype_t dt, int64_t n, tq_packed_t out,
-                         float* ws_r, hipStream_t s) {
+hipError_t launch_encode_rows(const tq_codec_s* c, const void* x, tq_dtype_t dt, int64_t n, tq_packed_t out,
+                              float* ws_r, hipStream_t s) {
   switch (dt) {
     case TQ_F32: return encode_typed(c, static_cast<const float*>(x), n, out, ws_r, s);
     case TQ_BF16: return encode_typed(c, static_cast<const __hip_bfloat16*>(x), n, out, ws_r, s);

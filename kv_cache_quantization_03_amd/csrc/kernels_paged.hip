@@ -57,7 +57,7 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Staging records (codes, signs, ν, γ, each 256-byte aligned), then the encode's own workspace.
 size_t append_paged_ws_bytes(const tq_codec_s* c, int64_t n_rec) {
   const size_t cw = c->prm.code_words, sw = c->prm.sign_words;
-  return align256(n_rec * cw * 4) + align256(n_rec * sw * 4) + 2 * align256(n_rec * 4) + encode_ws_bytes(c, n_rec);
+  return align256(n_rec * cw * 4) + align256(n_rec * sw * 4) + 2 * align256(n_rec * 4) + encode_rows_ws_bytes(c, n_rec);
 }
 
 hipError_t launch_append_paged(const tq_codec_s* c, const void* x, tq_dtype_t dt, int batch, int n_kv_heads,
@@ -75,8 +75,11 @@ hipError_t launch_append_paged(const tq_codec_s* c, const void* x, tq_dtype_t dt
   p += align256(n * 4);
   st.rnorm = reinterpret_cast<float*>(p);
   p += align256(n * 4);
-  hipError_t e = launch_encode(c, x, dt, n, st, reinterpret_cast<float*>(p), s);
+  hipError_t e = launch_encode_rows(c, x, dt, n, st, reinterpret_cast<float*>(p), s);
   if (e != hipSuccess) return e;
+  if (c->vblock)  // merge each record's bits into its 32-row block
+    return launch_vblock_append(c, st, n_kv_heads, n_new, n, ctx_lens, page_table, max_pages, page_size, n_pages,
+                                cache, s);
   const int qjl = c->qjl ? 1 : 0;
   const int64_t total = n * (cw + sw + 1 + qjl);
   hipLaunchKernelGGL(scatter_paged_kernel, dim3(static_cast<unsigned>(ceil_div(total, 256))), dim3(256), 0, s, st,

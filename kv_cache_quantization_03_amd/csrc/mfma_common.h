@@ -260,6 +260,48 @@ __device__ __forceinline__ void score_wave_values(const v4u (&cv)[NC], const v4u
   __builtin_amdgcn_wave_barrier();
 }
 
+// ----------------------------------------------------------------------------
+// V bits as matrix operands (decode attention, and the 32-token blocked V
+// layout written at encode).  The contraction over keys needs, in each lane,
+// the bits of one coordinate across 32 keys, while a row record holds 32
+// coordinates of one key: a 32x32 bit transpose in registers (four lane
+// stages with DPP partners within rows of 16 lanes, one stage between the
+// lane's two registers).
+// ----------------------------------------------------------------------------
+// One stage of the bit transpose: swap row bit K (lane bit K) with column bit K.
+template <int K>
+__device__ __forceinline__ uint32_t transpose_stage(uint32_t w, int lane) {
+  constexpr uint32_t M = K == 0 ? 0x55555555u : (K == 1 ? 0x33333333u : (K == 2 ? 0x0F0F0F0Fu : 0x00FF00FFu));
+  constexpr int s = 1 << K;
+  const uint32_t x = lane_xor<K>(w);
+  const bool hi = (lane >> K) & 1;
+  const uint32_t t = hi ? (x >> s) : (x << s);
+  const uint32_t keep = hi ? ~M : M;
+  return (w & keep) | (t & ~keep);
+}
+
+// 32x32 bit transpose within each row of 16 lanes: input row ρ = lane%16 + 16·reg
+// (r0: reg 0, r1: reg 1), column = bit; output lane%16 + 16·reg = column,
+// bit = row.
+__device__ __forceinline__ void transpose32(uint32_t& r0, uint32_t& r1, int lane) {
+  r0 = transpose_stage<0>(r0, lane);
+  r1 = transpose_stage<0>(r1, lane);
+  r0 = transpose_stage<1>(r0, lane);
+  r1 = transpose_stage<1>(r1, lane);
+  r0 = transpose_stage<2>(r0, lane);
+  r1 = transpose_stage<2>(r1, lane);
+  r0 = transpose_stage<3>(r0, lane);
+  r1 = transpose_stage<3>(r1, lane);
+  const uint32_t t = ((r0 >> 16) ^ r1) & 0x0000FFFFu;
+  r1 ^= t;
+  r0 ^= t << 16;
+}
+
+// Key (within the lane group's 32) whose words lane%16 + 16·reg loads: row
+// ρ = 4i + r carries key 8r + i, so that after the transpose bit 4i + r of the
+// word — FP4 nibble i of mask r, contraction index 8r + i — is that key.
+__device__ __forceinline__ int v_key_of_row(int rho) { return 8 * (rho & 3) + (rho >> 2); }
+
 // Wave-wide sum / max of non-negative values through DPP (no LDS round
 // trips): butterflies inside quads, half-row and row mirrors, then the
 // row broadcasts; the total lands in lane 63 and is read back as a scalar.

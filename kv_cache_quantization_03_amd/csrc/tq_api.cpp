@@ -120,6 +120,14 @@ tq_status_t need_qjl(const tq_codec_s* c, const char* what) {
   return TQ_ERROR_NOT_SUPPORTED;
 }
 
+// Scoring reads row records: a codec whose records are stored in 32-row
+// blocks is a value codec (decode attention's cv) only.
+tq_status_t need_rows(const tq_codec_s* c, const char* what) {
+  if (!c->vblock) return TQ_SUCCESS;
+  set_error(std::string(what) + " reads row records; a codec in 32-row blocks serves as the value codec of decode attention only");
+  return TQ_ERROR_NOT_SUPPORTED;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- encode
@@ -139,6 +147,10 @@ extern "C" tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, 
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(dt)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   if (n_vec < 0) { set_error("n_vec < 0"); return TQ_ERROR_INVALID_VALUE; }
+  if (c->vblock && n_vec % 32 != 0) {
+    set_error("a codec in 32-row blocks encodes whole blocks: n_vec must be a multiple of 32");
+    return TQ_ERROR_INVALID_VALUE;
+  }
   if (n_vec == 0) return TQ_SUCCESS;
   if (!k) { set_error("k is NULL"); return TQ_ERROR_INVALID_VALUE; }
   st = check_packed(k_out, "k_out", c->qjl);
@@ -147,8 +159,8 @@ extern "C" tq_status_t tq_encode_kv(tq_codec_t c, const void* k, const void* v, 
   if ((st = check_ws(ws, ws_bytes, tq::encode_ws_bytes(c, n_vec))) != TQ_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (log_enabled()) std::fprintf(stderr, "[tq] encode n=%lld d=%d bits=%d v=%d\n", (long long)n_vec, c->prm.d, c->host.bits, v != nullptr);
-  hipError_t e = tq::launch_encode(c, k, dt, n_vec, k_out, static_cast<float*>(ws), s);
-  if (e == hipSuccess && v) e = tq::launch_encode(c, v, dt, n_vec, v_out, static_cast<float*>(ws), s);
+  hipError_t e = tq::launch_encode(c, k, dt, n_vec, k_out, ws, s);
+  if (e == hipSuccess && v) e = tq::launch_encode(c, v, dt, n_vec, v_out, ws, s);
   return finish(e, "tq_encode_kv launch");
 }
 
@@ -170,6 +182,7 @@ extern "C" tq_status_t tq_attn_logits(tq_codec_t c, const void* q, tq_dtype_t q_
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
   if ((st = need_qjl(c, "tq_attn_logits")) != TQ_SUCCESS) return st;
+  if ((st = need_rows(c, "tq_attn_logits")) != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
@@ -211,6 +224,7 @@ extern "C" tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, si
   if (st != TQ_SUCCESS) return st;
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if ((st = need_qjl(c, "tq_attn_logits_prepped")) != TQ_SUCCESS) return st;
+  if ((st = need_rows(c, "tq_attn_logits_prepped")) != TQ_SUCCESS) return st;
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (n_queries < 0 || ctx_len < 0) { set_error("n_queries and ctx_len must be >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (ctx_len > kMaxLogitsCtx) { set_error("ctx_len must be below 2^31 - 2^16"); return TQ_ERROR_NOT_SUPPORTED; }
@@ -251,6 +265,18 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;
   if (ctx_len < 1) { set_error("ctx_len must be >= 1"); return TQ_ERROR_INVALID_VALUE; }
+  if (ck->vblock) {
+    set_error("the K codec must store row records (a codec in 32-row blocks is a value codec)");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  if (cv->vblock && !tq::decode_paged_supported(ck, cv, n_q_heads, n_kv_heads)) {
+    set_error("a V cache in 32-row blocks needs head_dim 128 for K and V, qjl_dim 128 and at most 4 query heads per KV head");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
+  if (cv->vblock && !pm && ctx_len % 32 != 0) {
+    set_error("a contiguous V cache in 32-row blocks needs ctx_len % 32 == 0 (each head's rows start a block)");
+    return TQ_ERROR_NOT_SUPPORTED;
+  }
   if (!(softmax_scale == softmax_scale)) { set_error("softmax_scale is NaN"); return TQ_ERROR_INVALID_VALUE; }
   const char* why = nullptr;
   if (!tq::decode_supported(cv, n_q_heads, n_kv_heads, ctx_len, &why)) { set_error(why); return TQ_ERROR_NOT_SUPPORTED; }
@@ -345,6 +371,10 @@ extern "C" tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dt
     set_error("max_pages, page_size and n_pages must be > 0");
     return TQ_ERROR_INVALID_VALUE;
   }
+  if (c->vblock && page_size % 32 != 0) {
+    set_error("a cache in 32-row blocks needs page_size % 32 == 0 (a block must not span pages)");
+    return TQ_ERROR_INVALID_VALUE;
+  }
   if (batch == 0 || n_new == 0) return TQ_SUCCESS;
   if (!x || !ctx_lens || !page_table) { set_error("x, ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!aligned(ctx_lens, 4) || !aligned(page_table, 4)) {
@@ -417,6 +447,7 @@ extern "C" tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtyp
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (!valid_dtype(q_dt)) { set_error("bad q dtype"); return TQ_ERROR_INVALID_VALUE; }
   if ((st = need_qjl(c, "tq_attn_logits_paged")) != TQ_SUCCESS) return st;
+  if ((st = need_rows(c, "tq_attn_logits_paged")) != TQ_SUCCESS) return st;
   if (!tq::logits_paged_supported(c)) {
     set_error("paged logits need a per-coordinate codec with head_dim 128 or 256 and qjl_dim = head_dim");
     return TQ_ERROR_NOT_SUPPORTED;
@@ -467,6 +498,7 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (c->polar) { set_error("search takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!c->qjl) return need_qjl(c, "tq_search_topk");
+  if ((st = need_rows(c, "tq_search_topk")) != TQ_SUCCESS) return st;
   if (n_db < 1 || n_queries < 0) { set_error("need n_db >= 1 and n_queries >= 0"); return TQ_ERROR_INVALID_VALUE; }
   if (topk < 1 || topk > 1024 || topk > n_db) { set_error("need 1 <= topk <= min(n_db, 1024)"); return TQ_ERROR_INVALID_VALUE; }
   if (n_queries == 0) return TQ_SUCCESS;

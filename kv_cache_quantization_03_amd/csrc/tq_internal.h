@@ -102,6 +102,7 @@ struct tq_codec_s {
   _Float16* dS16 = nullptr;  // [2][m][d]: S = hi + lo in fp16 (m = d, d a multiple of 128; else nullptr)
   bool polar = false;        // first stage: recursive polar angles instead of per-coordinate codes
   bool qjl = true;           // false: MSE-only codec (m = 0: records hold codes and ν, no signs, no γ)
+  bool vblock = false;       // codes and signs stored in 32-row blocks of transposed words (a value-cache layout)
   tq::PolarParams pol{};
 };
 
@@ -117,8 +118,20 @@ hipError_t no_alloc_scratch(void** out);
 // Encode: rotate + quantize (codes, norm, rnorm) and write the residual r (fp32
 // [n][d]) into ws_r; then the QJL projection writes the sign words.
 hipError_t launch_encode(const tq_codec_s* c, const void* x, tq_dtype_t dt, int64_t n,
-                         tq_packed_t out, float* ws_r, hipStream_t s);
+                         tq_packed_t out, void* ws, hipStream_t s);
 size_t encode_ws_bytes(const tq_codec_s* c, int64_t n);
+// The same in row records whatever the codec's layout (the blocked layout's
+// first step; the paged append's staging).
+hipError_t launch_encode_rows(const tq_codec_s* c, const void* x, tq_dtype_t dt, int64_t n, tq_packed_t out,
+                              float* ws_r, hipStream_t s);
+size_t encode_rows_ws_bytes(const tq_codec_s* c, int64_t n);
+// Blocked value layout (kernels_vblock.hip): row records -> 32-row blocks; the
+// paged append's bit merge.
+hipError_t launch_vblock_from_rows(const tq_codec_s* c, tq_packed_t rows, int64_t n, tq_packed_t out,
+                                   hipStream_t s);
+hipError_t launch_vblock_append(const tq_codec_s* c, tq_packed_t rows, int n_kv_heads, int n_new, int64_t n_rec,
+                                const int32_t* ctx_lens, const int32_t* page_table, int max_pages, int page_size,
+                                int n_pages, tq_packed_t cache, hipStream_t s);
 
 // Query prep: q' = R q and p = S q' for n query vectors (fp32 outputs [n][d],[n][m]).
 hipError_t launch_qprep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int64_t n, float* qrot,

@@ -43,6 +43,7 @@ __all__ = [
     "decode_attn_materialized", "decode_attn_accumulated", "decode_attn_sparse_v",
     "decode_attn_sparse_v_plain",
     "paged_row", "append_paged", "gather_paged", "decode_attn_paged",
+    "vblock_pack", "vblock_unpack",
     "polar_angle_cdf", "polar_angle_density", "polar_lloyd_max", "polar_transform", "polar_reconstruct",
     "polar_slots", "PolarCodec", "make_polar_codec", "polar_encode", "polar_encode_given_codes",
     "polar_dequantize", "polar_score",
@@ -682,6 +683,84 @@ def decode_attn_paged(codec_k: Codec, codec_v: Codec, q, k_cache, v_cache, page_
             out[b] = decode_attn_sparse_v(codec_k, codec_v, q[b:b + 1], kr, vr, 1, n_q_heads, n_kv_heads, n,
                                           scale, gate, chunk)[0][0]
     return out
+
+
+# --------------------------------------------------------------------------
+# O7b. Value records in blocks of 32 rows.  A storage order of the same bits
+# as O4's row records (the pages fix no memory layout; this one puts each
+# coordinate's bits of 32 consecutive rows in one word, the operand a
+# contraction over keys needs).  d = 128.  Block B holds rows 32B..32B+31.
+# Planes: the b code planes of O4, then the QJL sign plane (if any).  For
+# coordinate j = 16c + n (n < 16, c < 8):
+#   codes word (B*b + p)*128 + 8n + c,  signs word B*128 + 8n + c,
+# and row 32B + 8r + i (i < 8, r < 4) is bit 4i + r of that word.  The arrays
+# keep the row layout's sizes: n rows (a multiple of 32) of code_words and
+# sign_words words.  ν and γ stay per row.
+# Parity: a layout defined here, not by the pages; pinned by bits placed by
+# hand and by the round trip with vblock_unpack.
+# --------------------------------------------------------------------------
+def _vblock_word_of_coordinate(j):
+    j = np.asarray(j)
+    return 8 * (j % 16) + j // 16
+
+
+def _vblock_bit_of_row(tau: int) -> int:
+    return 4 * (tau % 8) + tau // 8
+
+
+def _record_planes(rec: dict, b: int, d: int) -> np.ndarray:
+    """(n, planes, d) 0/1 array: the code planes of O4, then the signs."""
+    wpp = d // 32
+    codes = np.asarray(rec["codes"], dtype=np.uint32)
+    planes = [unpack_bits(codes[:, p * wpp:(p + 1) * wpp], d) for p in range(b)]
+    signs = np.asarray(rec["signs"], dtype=np.uint32)
+    if signs.shape[1]:
+        planes.append(unpack_bits(signs, d))
+    return np.stack(planes, axis=1)
+
+
+def vblock_pack(rec: dict, b: int, d: int = 128) -> dict:
+    """Row records (O4) -> the same records in 32-row blocks."""
+    assert d == 128
+    bits = _record_planes(rec, b, d)
+    n, n_planes, _ = bits.shape
+    assert n % 32 == 0
+    nblk = n // 32
+    out = np.zeros((nblk, n_planes, 128), dtype=np.uint64)
+    w = _vblock_word_of_coordinate(np.arange(d))
+    for tau in range(32):
+        sh = np.uint64(_vblock_bit_of_row(tau))
+        for p in range(n_planes):
+            out[:, p, w] |= bits[tau::32, p, :].astype(np.uint64) << sh
+    out = out.astype(np.uint32)
+    codes = out[:, :b, :].reshape(n, b * d // 32)
+    signs = out[:, b, :].reshape(n, d // 32) if n_planes > b else np.zeros((n, 0), np.uint32)
+    return {"codes": codes, "signs": signs, "norm": np.asarray(rec["norm"]).copy(),
+            "rnorm": np.asarray(rec["rnorm"]).copy()}
+
+
+def vblock_unpack(blocked: dict, b: int, d: int = 128) -> dict:
+    """The inverse of vblock_pack."""
+    assert d == 128
+    codes = np.asarray(blocked["codes"], dtype=np.uint32)
+    n = codes.shape[0]
+    nblk = n // 32
+    signs = np.asarray(blocked["signs"], dtype=np.uint32)
+    words = [codes.reshape(nblk, b, 128)[:, p, :] for p in range(b)]
+    if signs.shape[1]:
+        words.append(signs.reshape(nblk, 128))
+    w = _vblock_word_of_coordinate(np.arange(d))
+    bits = np.zeros((n, len(words), d), dtype=np.int64)
+    for tau in range(32):
+        sh = np.uint64(_vblock_bit_of_row(tau))
+        for p, wp in enumerate(words):
+            bits[tau::32, p, :] = (wp[:, w].astype(np.uint64) >> sh) & np.uint64(1)
+    idx = np.zeros((n, d), dtype=np.int64)
+    for p in range(b):
+        idx |= bits[:, p, :] << p
+    return {"codes": pack_planes(idx, b),
+            "signs": pack_bits(bits[:, b, :]) if len(words) > b else np.zeros((n, 0), np.uint32),
+            "norm": np.asarray(blocked["norm"]).copy(), "rnorm": np.asarray(blocked["rnorm"]).copy()}
 
 
 # --------------------------------------------------------------------------

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(B):
     for s in syms:
         assert hasattr(lib, s), f"{s} declared in tq.h but not exported"
     assert set(B.EXPORTED) == set(syms)
-    assert B.lib.tq_abi_version() == 1
+    assert B.lib.tq_abi_version() == 2
 
 
 def test_status_strings(B):

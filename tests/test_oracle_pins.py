@@ -859,3 +859,60 @@ def test_bf16_round_pinned_to_definition_and_torch():
     t64 = torch.from_numpy(x64.copy()).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(g64.view(np.uint32), t64.view(np.uint32))
     assert np.array_equal(g64.view(np.uint32), _bf16_nearest(x64.astype(f)).view(np.uint32))
+
+
+# ---------------------------------------------------------------- O7b value records in 32-row blocks
+def _one_bit_record(n, b, row, plane, j):
+    """Row records (O4 layout) with a single bit set: plane `plane` (b = the
+    sign plane) of coordinate j in row `row`."""
+    rec = {"codes": np.zeros((n, 4 * b), np.uint32), "signs": np.zeros((n, 4), np.uint32),
+           "norm": np.arange(n, dtype=np.float32), "rnorm": -np.arange(n, dtype=np.float32)}
+    if plane < b:
+        rec["codes"][row, 4 * plane + j // 32] = np.uint32(1) << np.uint32(j % 32)
+    else:
+        rec["signs"][row, j // 32] = np.uint32(1) << np.uint32(j % 32)
+    return rec
+
+
+@pytest.mark.parametrize("b,row,plane,j,array,word,bit", [
+    # row 9 = 8*1 + 1 (r 1, i 1 -> bit 4*1 + 1); coordinate 17 = 16*1 + 1 (c 1, n 1 -> word 8 + 1);
+    # plane 1 of block 0 with b = 2 -> codes word (0*2 + 1)*128 + 9
+    (2, 9, 1, 17, "codes", 137, 5),
+    # row 63: block 1, tau 31 = 8*3 + 7 -> bit 31; coordinate 127 = 16*7 + 15 -> word 127; sign plane
+    (2, 63, 2, 127, "signs", 255, 31),
+    # row 32: block 1, tau 0 -> bit 0; coordinate 0 -> word 0; plane 0 of b = 3 -> (1*3 + 0)*128
+    (3, 32, 0, 0, "codes", 384, 0),
+    # row 2 (i 2, r 0 -> bit 8); coordinate 16 (c 1, n 0 -> word 1); plane 2 of b = 3 -> 2*128 + 1
+    (3, 2, 2, 16, "codes", 257, 8),
+    # row 24 (r 3, i 0 -> bit 3); coordinate 31 (c 1, n 15 -> word 121); plane 0
+    (1, 24, 0, 31, "codes", 121, 3),
+])
+def test_vblock_single_bits_land_where_the_layout_puts_them(b, row, plane, j, array, word, bit):
+    # hand-computed positions of single bits under the block layout
+    n = 64
+    blk = O.vblock_pack(_one_bit_record(n, b, row, plane, j), b)
+    flat = blk[array].reshape(-1)
+    assert int(flat[word]) == 1 << bit
+    assert np.count_nonzero(blk["codes"]) + np.count_nonzero(blk["signs"]) == 1
+    assert np.array_equal(blk["norm"], np.arange(n, dtype=np.float32))
+
+
+@pytest.mark.parametrize("b,qjl", [(1, True), (2, True), (3, True), (2, False), (3, False)])
+def test_vblock_round_trip_and_bit_count(b, qjl):
+    # a permutation of the bits: unpack inverts pack, and popcounts agree per block and plane
+    rng = np.random.default_rng(b + 10 * qjl)
+    n = 96
+    rec = {"codes": rng.integers(0, 2 ** 32, (n, 4 * b), dtype=np.uint64).astype(np.uint32),
+           "signs": (rng.integers(0, 2 ** 32, (n, 4), dtype=np.uint64).astype(np.uint32) if qjl
+                     else np.zeros((n, 0), np.uint32)),
+           "norm": rng.random(n).astype(np.float32), "rnorm": rng.random(n).astype(np.float32)}
+    blk = O.vblock_pack(rec, b)
+    assert blk["codes"].shape == rec["codes"].shape and blk["signs"].shape == rec["signs"].shape
+    back = O.vblock_unpack(blk, b)
+    for k in rec:
+        assert np.array_equal(back[k], rec[k]), k
+    pc = lambda a: np.unpackbits(np.ascontiguousarray(a).view(np.uint8)).sum()
+    for B_ in range(n // 32):
+        for p in range(b):
+            assert pc(rec["codes"][32 * B_:32 * B_ + 32, 4 * p:4 * p + 4]) == pc(blk["codes"].reshape(-1)[
+                (B_ * b + p) * 128:(B_ * b + p + 1) * 128])
