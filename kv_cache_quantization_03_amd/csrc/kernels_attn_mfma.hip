@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   __shared__ float hmax[kDecWaves][4];
   __shared__ int ubexp[kDecWaves][2][4][4];  // V weight block exponents [type][head][key block]
   __shared__ float hsum[kDecWaves][4][4];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // wave index through readfirstlane: every per-wave quantity is then known uniform (scalar registers)
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int g = lane >> 4, kl = lane & 15;
   const int bk = blockIdx.y, chunk = blockIdx.x;
   const int G = Hq / nkv;
@@ -168,11 +169,18 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
         if constexpr (VQ) vsv[reg] = reinterpret_cast<const v4u*>(vs)[row];
       }
     }
+    // ν, γ through buffers over the wave's rows from wkey (scalar base), one
+    // offset register: keys at or past ctx read 0 (their weight is 0)
+    {
+      const int nb = __builtin_amdgcn_readfirstlane(min(max(ctx - wkey, 0), 2 * kDecKeysPerWave) * 4);
+      const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vn + wrow), 0, nb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vr + wrow), 0, nb, 0x00020000);
+      const int off = (kbase - wkey + kl) * 4;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int64_t row = row_of(min(kbase + 16 * t + kl, ctx - 1));
-      vnu[t] = vn[row];
-      if constexpr (VQ) vga[t] = vr[row];
+      for (int t = 0; t < 8; ++t) {
+        vnu[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rn, off + 64 * t, 0, 0));
+        if constexpr (VQ) vga[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rr, off + 64 * t, 0, 0));
+      }
     }
   };
   if constexpr (!GATE) load_v();
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     float m = s[0];
 #pragma unroll
     for (int t = 1; t < 8; ++t) m = fmaxf(m, s[t]);
-    m = row_max(m);
+    m = row_max_rot(m);
     if (kl == 0) hmax[wv][g] = m;
   }
   __syncthreads();
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     wt[t] = s[t] == -INFINITY ? 0.f : __expf(s[t] - mg);
     l_sum += wt[t];
   }
-  l_sum = row_sum(l_sum);
+  l_sum = row_sum_rot(l_sum);  // lane kl = 0's is stored
   if (kl == 0) hsum[wv][g][0] = l_sum;
   bool wave_on = true;
   if constexpr (GATE) {
@@ -229,63 +237,70 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
     // elements to the largest and keeps 13 bits below it (measured on gfx950),
     // so floating-point limbs of weights that span many octaves lose the small
     // ones.  Instead u = w ν (MSE) and u = 2 w ν γ (QJL) become 16-bit fixed
-    // point relative to the maximum of their (head, 32-key block): four base-16
-    // digits, each an exact fp8 integer (times the nibble's 1/value), so every
-    // product sum is exact.  The block exponent and the digit weight 16^-l go
-    // into the op's per-block E8M0 scale (row r, keys 32b..32b+31: lane 16b + r).
-    // LW[type][g][key] = the key's four digit bytes; ub = block exponents.
+    // point V relative to the maximum of their (head, 32-key block): four
+    // base-16 digits, each an exact fp8 integer (times the nibble's 1/value),
+    // so every product sum is exact.  The block exponent and the digit weight
+    // go into the op's per-block E8M0 scale (row r, keys 32b..32b+31: lane
+    // 16b + r).  LW[type][g][key] = the key's four digit bytes, byte j = digit
+    // of weight 16^j; ub = block exponents.
+    // Digit bytes in integer arithmetic: the nibbles of V spread to bytes, then
+    // a byte-wise table lookup: v_perm over the lane's 8-entry table of
+    // fp8(d / value) for d < 8, and fp8(d / value) = d + C for d >= 8 (the
+    // exponent is then fixed: fp8 e4m3 of 8..15 times 2^k is 0x48 + 8k + d).
+    // The key's FP4 mask index r = 2·(t odd) + (lane%16 >= 8) fixes the value
+    // 1/2, 1, 2 or -2 (r = 0..3) the op multiplies the digit by.
     uint32_t* LW = wsc[wv];
     {
+      const bool hi8 = kl >= 8;
+      // tables for t even (r = 0 or 1) and t odd (r = 2 or 3): fp8 of d·{2, 1, 0.5, -0.5}
+      const uint32_t tlo_e = hi8 ? 0x44403800u : 0x4C484000u, thi_e = hi8 ? 0x4E4C4A48u : 0x56545250u;
+      const uint32_t tlo_o = hi8 ? 0xBCB8B080u : 0x3C383000u, thi_o = hi8 ? 0xC6C4C2C0u : 0x46444240u;
+      const uint32_t c8_e = hi8 ? 0x48484848u : 0x50505050u, c8_o = hi8 ? 0xC0C0C0C0u : 0x40404040u;
       float u[NTY][8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         u[0][t] = wt[t] * vnu[t];
         if constexpr (VQ) u[NTY - 1][t] = 2.f * u[0][t] * vga[t];
       }
-      int eb[NTY][4];
+      float w_all = 0.f, w_3 = 0.f, q_n3 = 0.f;
 #pragma unroll
       for (int ty = 0; ty < NTY; ++ty) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {  // block kb = keys 32kb..32kb+31 = tiles 2kb, 2kb+1
-          const float m = row_max(fmaxf(u[ty][2 * kb], u[ty][2 * kb + 1]));
+          const float m = row_max_nonneg(__uint_as_float(max(__float_as_uint(u[ty][2 * kb]), __float_as_uint(u[ty][2 * kb + 1]))));
           int e = 0;
-          if (m > 0.f) (void)frexpf(m, &e);  // m in [2^(e-1), 2^e)
-          eb[ty][kb] = max(e - 1, -100);
-          if (kl == 0) ubexp[wv][ty][g][kb] = eb[ty][kb];
-        }
-      }
-      float w_all = 0.f, w_3 = 0.f, q_n3 = 0.f;
+          (void)frexpf(m, &e);               // m in [2^(e-1), 2^e); 0 for m = 0
+          const int eb = max(e - 1, -100);   // every u of the block is below 2^(eb+1)
+          if (kl == 0) ubexp[wv][ty][g][kb] = eb;
+          const float scl = __uint_as_float(static_cast<uint32_t>(127 + 15 - eb) << 23);  // 2^(15 - eb)
+          const float isc = __uint_as_float(static_cast<uint32_t>(127 - 15 + eb) << 23);  // 2^(eb - 15)
+          uint32_t V[2];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int key = 16 * t + kl;    // within the wave
-        const int r = (key & 31) >> 3;  // FP4 mask index of this key in the B operand
-        const float inv_val = r == 0 ? 2.f : (r == 1 ? 1.f : (r == 2 ? 0.5f : -0.5f));
-#pragma unroll
-        for (int ty = 0; ty < NTY; ++ty) {
-          const int e = eb[ty][t >> 1];
-          const float V = fminf(rintf(ldexpf(u[ty][t], 15 - e)), 65535.f);  // 16-bit fixed point
-          const float ut = ldexpf(V, e - 15);                                 // the value the digits carry
-          if (ty == 0) {
-            w_all += ut;
-            if (r == 3) w_3 += ut;
-          } else if (r != 3) {
-            q_n3 += 0.5f * ut;
+          for (int h = 0; h < 2; ++h) {
+            const int t = 2 * kb + h;
+            // round to nearest (u >= 0), 16 bits
+            V[h] = min(static_cast<uint32_t>(fmaf(u[ty][t], scl, 0.5f)), 65535u);
+            const uint32_t y = (V[h] | (V[h] << 8)) & 0x00FF00FFu;
+            const uint32_t z = (y | (y << 4)) & 0x0F0F0F0Fu;  // byte j = nibble j
+            const uint32_t lo = __builtin_amdgcn_perm(h ? thi_o : thi_e, h ? tlo_o : tlo_e, z);  // d < 8
+            const uint32_t hi = z + (h ? c8_o : c8_e);                                           // d >= 8
+            // byte j from lo (selector j) or, where d >= 8, from hi (selector 4 + j)
+            const uint32_t sel = ((z >> 1) & 0x04040404u) | 0x03020100u;
+            LW[(ty * 4 + g) * kDecKeysPerWave + 16 * t + kl] = __builtin_amdgcn_perm(hi, lo, sel);
           }
-          const float d0 = floorf(V * 0.000244140625f);
-          const float r1 = fmaf(d0, -4096.f, V);
-          const float d1 = floorf(r1 * 0.00390625f);
-          const float r2 = fmaf(d1, -256.f, r1);
-          const float d2 = floorf(r2 * 0.0625f);
-          const float d3 = fmaf(d2, -16.f, r2);
-          uint32_t dw = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(d0 * inv_val, d1 * inv_val, 0, false));
-          dw = static_cast<uint32_t>(
-              __builtin_amdgcn_cvt_pk_fp8_f32(d2 * inv_val, d3 * inv_val, static_cast<int>(dw), true));
-          LW[(ty * 4 + g) * kDecKeysPerWave + key] = dw;
+          // the values the digits carry, for the constant terms: every key
+          // (MSE), the r = 3 keys (MSE), the r != 3 keys (QJL, halved)
+          if (ty == 0) {
+            w_all = fmaf(static_cast<float>(V[0] + V[1]), isc, w_all);
+            w_3 = fmaf(static_cast<float>(hi8 ? V[1] : 0u), isc, w_3);
+          } else {
+            q_n3 = fmaf(static_cast<float>(V[0] + (hi8 ? 0u : V[1])), 0.5f * isc, q_n3);
+          }
         }
       }
-      w_all = row_sum(w_all);
-      w_3 = row_sum(w_3);
-      q_n3 = row_sum(q_n3);
+      w_all = row_sum_rot(w_all);  // lane kl = 0's are stored
+      w_3 = row_sum_rot(w_3);
+      q_n3 = row_sum_rot(q_n3);
       if (kl == 0) {
         hsum[wv][g][1] = w_all;
         hsum[wv][g][2] = w_3;
@@ -293,14 +308,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
       }
     }
     __builtin_amdgcn_wave_barrier();
-    // A operands: lane (row 4g'+l, group grp) holds digit l of keys 16grp..+15 and
-    // 64+16grp..+15 (A byte order measured on gfx950); its E8M0 scale serves
-    // row 4g'+l of key block grp: 2^(block exponent - 3 - 4l).
+    // A operands: lane (row 4g'+l, group grp) holds digit l (weight 16^(3-l),
+    // byte 3 - l of the LW words) of keys 16grp..+15 and 64+16grp..+15 (A byte
+    // order measured on gfx950); its E8M0 scale serves row 4g'+l of key block
+    // grp: 2^(block exponent - 3 - 4l).
     v8i av[NTY];
     int sav[NTY];
     {
       const int row = lane & 15, grp = lane >> 4, gq = row >> 2, l = row & 3;
-      const uint32_t sel = static_cast<uint32_t>(l) | (static_cast<uint32_t>(4 + l) << 8) | 0x0C0C0000u;
+      const uint32_t sel = static_cast<uint32_t>(3 - l) | (static_cast<uint32_t>(7 - l) << 8) | 0x0C0C0000u;
 #pragma unroll
       for (int ty = 0; ty < NTY; ++ty) {
         const uint32_t* src = LW + (ty * 4 + gq) * kDecKeysPerWave;

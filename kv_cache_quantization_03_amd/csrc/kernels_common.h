@@ -117,6 +117,43 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// Row (16-lane) reductions through the rotations row_ror 1, 2, 4, 8: the
+// compiler folds each DPP move into the reducing op (one VALU op per step;
+// the lane_xor forms above take up to four).  row_max_rot is exact and equal
+// in every lane (-0 ranks below +0); row_max_nonneg is the same for v >= 0
+// (the float order is the integer order of the bits).  In row_sum_rot each
+// lane adds the 16 values in its own order: lanes may differ in the last
+// bits, so use it where one lane's sum is taken.
+template <int CTRL>
+__device__ __forceinline__ int row_ror_dpp(int x, int old) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row_max_nonneg(float v) {
+  uint32_t x = __float_as_uint(v);
+  x = max(x, static_cast<uint32_t>(row_ror_dpp<0x121>(static_cast<int>(x), 0)));
+  x = max(x, static_cast<uint32_t>(row_ror_dpp<0x122>(static_cast<int>(x), 0)));
+  x = max(x, static_cast<uint32_t>(row_ror_dpp<0x124>(static_cast<int>(x), 0)));
+  x = max(x, static_cast<uint32_t>(row_ror_dpp<0x128>(static_cast<int>(x), 0)));
+  return __uint_as_float(x);
+}
+__device__ __forceinline__ float row_max_rot(float v) {
+  const int b = __float_as_int(v);
+  int x = b ^ ((b >> 31) & 0x7FFFFFFF);  // monotone map of the float order to the signed order
+  constexpr int lo = static_cast<int>(0x80000000u);
+  x = max(x, row_ror_dpp<0x121>(x, lo));
+  x = max(x, row_ror_dpp<0x122>(x, lo));
+  x = max(x, row_ror_dpp<0x124>(x, lo));
+  x = max(x, row_ror_dpp<0x128>(x, lo));
+  return __int_as_float(x ^ ((x >> 31) & 0x7FFFFFFF));
+}
+__device__ __forceinline__ float row_sum_rot(float v) {
+  v += __int_as_float(row_ror_dpp<0x121>(__float_as_int(v), 0));
+  v += __int_as_float(row_ror_dpp<0x122>(__float_as_int(v), 0));
+  v += __int_as_float(row_ror_dpp<0x124>(__float_as_int(v), 0));
+  v += __int_as_float(row_ror_dpp<0x128>(__float_as_int(v), 0));
+  return v;
+}
+
 // Unnormalised Walsh–Hadamard transform along the 64 lanes (bits 0..5 of j):
 // butterfly partner = lane ^ mask; lower lane keeps a+b, upper keeps a-b.
 template <int E>

@@ -58,6 +58,16 @@ __device__ __forceinline__ v4f mfma_fp8_fp4_scaled(const v8i& a, const v8i& b, c
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, scale_a, 0, 127);
 }
 
+// A pointer the caller knows to be wave-uniform, moved to scalar registers
+// (for buffer resources, whose base must be scalar).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u & 0xFFFFFFFFu)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(u >> 32)));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ v8i fp4_operand(uint32_t w) {
   v8i b;
   b[0] = static_cast<int>(w & 0x11111111u);                 // 0 or 0.5
