@@ -282,7 +282,8 @@ hipError_t launch_qprep128(const tq_codec_s* c, const void* q, tq_dtype_t dt, in
 // Logits from prepared query operands: each wave scores NG consecutive groups
 // of 64 keys against NMT M-tiles of its query group, operands and constants
 // read once from `prep`; the next group's records load while the current one
-// is scored.
+// is scored.  With one M-tile and d = 128 the logits leave in whole lines as
+// in logits_fused_kernel below (vec_out).
 // ----------------------------------------------------------------------------
 // PAGED: the keys of (batch b, KV head kh) live in the pages of a paged cache
 // (see PageMap; page_size a multiple of 64, so a 64-key group lies in one
@@ -294,7 +295,8 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
                                                                  const uint32_t* __restrict__ signs,
                                                                  const float* __restrict__ norm,
                                                                  const float* __restrict__ rnorm, float kappa,
-                                                                 float* __restrict__ logits, PageMap pm, int nkv) {
+                                                                 float* __restrict__ logits, PageMap pm, int nkv,
+                                                                 int vec_out) {
   using L = RecLayout<NP, WB>;
   constexpr int NKB = L::NKB;
   constexpr int MT_BYTES = NKB * kOpBytes + kConstBytes;
@@ -348,11 +350,40 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
     const int k0 = key0 + i * kKeysPerWave;
     if (k0 >= ctx_v) break;  // wave-uniform
     if (i + 1 < NG && k0 + kKeysPerWave < ctx_v) load_group(i + 1, (i + 1) & 1);
+    const int nvalid = min(kKeysPerWave, ctx_v - k0);
+    if constexpr (NMT == 1 && WB == 1) {
+      if (vec_out) {
+        // the group's scores in registers, then out in whole lines: val[t] is
+        // key 16t + lane%16; through the wave's LDS slice to keys 4(lane%16)..+3,
+        // so 16 lanes write a 64-key row piece with 16-byte stores
+        float val[kKeysPerWave / kKeysPerTile];
+        score_wave_values<NP, 1>(cv[i & 1], sv[i & 1], nu_l[i & 1], ga_l[i & 1], s_codes[wv], s_signs[wv], a,
+                                 cst[0], kappa, lane, val);
+        const int kl = lane & 15;
+        float* st = reinterpret_cast<float*>(s_codes[wv]) + g * kKeysPerWave;
+#pragma unroll
+        for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) st[kKeysPerTile * t + kl] = val[t];
+        __builtin_amdgcn_wave_barrier();
+        const v4f o = *reinterpret_cast<const v4f*>(st + 4 * kl);
+        __builtin_amdgcn_wave_barrier();  // read before the next group's staging
+        if (out[0] != nullptr) {
+          float* orow = out[0] + i * kKeysPerWave;
+          if (4 * kl + 3 < nvalid) {
+            __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(orow + 4 * kl));
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * kl + e < nvalid) __builtin_nontemporal_store(o[e], orow + 4 * kl + e);
+          }
+        }
+        continue;
+      }
+    }
     float* oi[NMT];
 #pragma unroll
     for (int j = 0; j < NMT; ++j) oi[j] = out[j] ? out[j] + i * kKeysPerWave : nullptr;
     score_wave<NP, WB, NMT>(cv[i & 1], sv[i & 1], nu_l[i & 1], ga_l[i & 1], s_codes[wv], s_signs[wv], a, cst, oi,
-                            min(kKeysPerWave, ctx_v - k0), kappa, lane);
+                            nvalid, kappa, lane);
     __builtin_amdgcn_wave_barrier();  // the next group's LDS staging follows this group's reads
   }
 }
@@ -504,6 +535,8 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
   const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   const int G = n_q_heads / n_kv_heads;
   const int n_mt = static_cast<int>(ceil_div(static_cast<int64_t>(n_queries) * G, 4));
+  // whole-line stores need 16-byte aligned rows: ctx % 4 == 0 and aligned logits
+  const int vec_out = ctx % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
   auto go = [&]<int NP, int WB, int NMT>() -> hipError_t {
     constexpr int WAVES = WB == 1 ? 8 : 4;
     auto launch = [&]<int NG>() -> hipError_t {
@@ -512,11 +545,11 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
       if (pm)
         hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG, true>), grid, dim3(WAVES * 64), 0, s,
                            static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads);
+                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads, vec_out);
       else
         hipLaunchKernelGGL((logits_mfma_kernel<NP, WB, NMT, WAVES, NG, false>), grid, dim3(WAVES * 64), 0, s,
                            static_cast<const uint8_t*>(ws), n_mt, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads);
+                           k.rnorm, c->prm.qjl_kappa, logits, pmv, n_kv_heads, vec_out);
       return hipGetLastError();
     };
     // Four groups per wave read the operands once per 256 keys (measured 49.8
