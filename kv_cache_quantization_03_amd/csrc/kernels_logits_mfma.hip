@@ -398,11 +398,11 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
 // lines) instead of four 64-byte pieces.  vec_out = 0 (ctx not a multiple of
 // 4, or logits not 16-byte aligned) keeps the scalar stores.
 // ----------------------------------------------------------------------------
-template <int NP, int WAVES, typename T>
+template <int NP, int WAVES, typename T, bool LOOP>
 __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
     const T* q, DevParams P, const float* Dsign, const float* Mt, int Hq, int nq, int G, int nkv, int ctx,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs, const float* __restrict__ norm,
-    const float* __restrict__ rnorm, float* __restrict__ logits, int vec_out) {
+    const float* __restrict__ rnorm, float* __restrict__ logits, int vec_out, int ngw) {
   using L = RecLayout<NP, 1>;
   constexpr int NT = WAVES * 64, NKB = L::NKB;
   __shared__ uint32_t s_codes[WAVES][kKeysPerWave * L::CS];
@@ -411,9 +411,12 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bk = blockIdx.y;
   const QueryTile tile{bk / nkv, nq, Hq, G, bk % nkv, static_cast<int>(blockIdx.z), nq * G};
-  const int key0 = (blockIdx.x * WAVES + wv) * kKeysPerWave;
+  // The block's keys: ngw rounds of WAVES consecutive 64-key groups, wave wv
+  // taking group wv of each round (every round reads one contiguous range).
+  const int blk0 = blockIdx.x * ngw * (WAVES * kKeysPerWave);
+  auto group_key = [&](int i) { return blk0 + (i * WAVES + wv) * kKeysPerWave; };
+  const int key0 = group_key(0);
   const bool active = key0 < ctx;  // wave-uniform; idle waves still help with the operands
-  const int nvalid = active ? min(kKeysPerWave, ctx - key0) : 0;
 
   // The vector memory path returns data in request order, so an operand load
   // queued behind record loads (HBM misses) would wait for them: every wave's
@@ -422,16 +425,18 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   QueryPrepRegs<NT> pr;
   query_prep_load<NT>(pr, q, Dsign, Mt, tile);
   __syncthreads();
-  // Records: every wave loads (an idle wave re-reads the last key and never
+  // Records, double-buffered: group i + 1 loads while group i is scored.  Every
+  // wave loads its first group (an idle wave re-reads the last key and never
   // uses it), so no branch sits around the loads.
-  v4u cv[L::CW / 4], sv[L::SW / 4];
-  float nu_l, ga_l;
-  {
-    const int k0 = active ? key0 : ctx - 1;
-    const int64_t row0 = static_cast<int64_t>(bk) * ctx + k0;
-    load_wave_records<NP, 1>(cv, sv, nu_l, ga_l, codes + row0 * L::CW, signs + row0 * L::SW, norm + row0,
-                             rnorm + row0, active ? nvalid : 1, lane);
-  }
+  v4u cvA[L::CW / 4], svA[L::SW / 4], cvB[L::CW / 4], svB[L::SW / 4];
+  float nuA, gaA, nuB, gaB;
+  auto load = [&](int k0, v4u (&cv)[L::CW / 4], v4u (&sv)[L::SW / 4], float& nu, float& ga) {
+    const bool ok = k0 < ctx;
+    const int64_t row0 = static_cast<int64_t>(bk) * ctx + (ok ? k0 : ctx - 1);
+    load_wave_records<NP, 1>(cv, sv, nu, ga, codes + row0 * L::CW, signs + row0 * L::SW, norm + row0, rnorm + row0,
+                             ok ? min(kKeysPerWave, ctx - k0) : 1, lane);
+  };
+  load(key0, cvA, svA, nuA, gaA);
   query_prep_build<NT, NP, NKB>(sh, pr, P, tile);
   if (!active) return;  // wave-uniform
 
@@ -439,29 +444,56 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   v8i a[1][NKB];
   query_prep_operands<NT, NKB>(sh, a, lane);
   const float4 cst = query_prep_constants<NT, NP, NKB>(sh, P, g);
-  float val[kKeysPerWave / kKeysPerTile];
-  score_wave_values<NP, 1>(cv, sv, nu_l, ga_l, s_codes[wv], s_signs[wv], a, cst, P.qjl_kappa, lane, val);
   const int qvg = tile.mt * 4 + g;
-  if (qvg >= tile.Gq) return;  // a padding slot of the tile (lane-divergent: no wave ops below)
-  float* orow = logits + (static_cast<int64_t>(tile.b * Hq + tile.kh * G + qvg % G) * nq + qvg / G) * ctx + key0;
-  if (vec_out) {
-    // val[t] is key 16t + kl; through the wave's LDS slice to keys 4kl..4kl+3
-    float* st = reinterpret_cast<float*>(s_codes[wv]) + g * kKeysPerWave;
+  // a padding slot of the tile scores like the others (the matrix ops need
+  // every lane) but stores nothing
+  const bool store = qvg < tile.Gq;
+  float* const orow0 =
+      logits + (static_cast<int64_t>(tile.b * Hq + tile.kh * G + (store ? qvg % G : 0)) * nq + qvg / G) * ctx;
+  // score group i from (cv, sv, nu, ga); group i + 1 loads into (cvn, ...)
+  // before the scoring (prefetch) or after it (the same registers)
+  auto step = [&](int i, v4u (&cv)[L::CW / 4], v4u (&sv)[L::SW / 4], float& nu, float& ga, v4u (&cvn)[L::CW / 4],
+                  v4u (&svn)[L::SW / 4], float& nun, float& gan, bool prefetch) {
+    const int k0 = group_key(i);
+    const bool more = i + 1 < ngw && group_key(i + 1) < ctx;
+    if (prefetch && more) load(group_key(i + 1), cvn, svn, nun, gan);
+    const int nvalid = min(kKeysPerWave, ctx - k0);
+    float val[kKeysPerWave / kKeysPerTile];
+    score_wave_values<NP, 1>(cv, sv, nu, ga, s_codes[wv], s_signs[wv], a, cst, P.qjl_kappa, lane, val);
+    if (!prefetch && more) load(group_key(i + 1), cvn, svn, nun, gan);
+    float* orow = orow0 + k0;
+    if (vec_out) {
+      // val[t] is key 16t + kl; through the wave's LDS slice to keys 4kl..4kl+3
+      float* st = reinterpret_cast<float*>(s_codes[wv]) + g * kKeysPerWave;
 #pragma unroll
-    for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) st[kKeysPerTile * t + kl] = val[t];
-    __builtin_amdgcn_wave_barrier();
-    const v4f o = *reinterpret_cast<const v4f*>(st + 4 * kl);
-    if (4 * kl + 3 < nvalid) {
-      __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(orow + 4 * kl));
-    } else {
+      for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t) st[kKeysPerTile * t + kl] = val[t];
+      __builtin_amdgcn_wave_barrier();
+      const v4f o = *reinterpret_cast<const v4f*>(st + 4 * kl);
+      __builtin_amdgcn_wave_barrier();  // read before the next group's staging
+      if (store) {
+        if (4 * kl + 3 < nvalid) {
+          __builtin_nontemporal_store(o, reinterpret_cast<v4f*>(orow + 4 * kl));
+        } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * kl + i < nvalid) __builtin_nontemporal_store(o[i], orow + 4 * kl + i);
+          for (int e = 0; e < 4; ++e)
+            if (4 * kl + e < nvalid) __builtin_nontemporal_store(o[e], orow + 4 * kl + e);
+        }
+      }
+    } else if (store) {
+#pragma unroll
+      for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t)
+        if (kKeysPerTile * t + kl < nvalid) __builtin_nontemporal_store(val[t], orow + kKeysPerTile * t + kl);
     }
-  } else {
-#pragma unroll
-    for (int t = 0; t < kKeysPerWave / kKeysPerTile; ++t)
-      if (kKeysPerTile * t + kl < nvalid) __builtin_nontemporal_store(val[t], orow + kKeysPerTile * t + kl);
+  };
+  if constexpr (LOOP) {
+    for (int i = 0; i < ngw; i += 2) {
+      if (group_key(i) >= ctx) break;  // wave-uniform
+      step(i, cvA, svA, nuA, gaA, cvB, svB, nuB, gaB, true);
+      if (i + 1 >= ngw || group_key(i + 1) >= ctx) break;
+      step(i + 1, cvB, svB, nuB, gaB, cvA, svA, nuA, gaA, true);
+    }
+  } else {  // one round (ngw = 1)
+    step(0, cvA, svA, nuA, gaA, cvB, svB, nuB, gaB, false);
   }
 }
 
@@ -529,6 +561,16 @@ static int device_cu_count() {
   return n;
 }
 
+// Rounds of 64-key groups per wave of the fused kernel: enough that the grid
+// is about one block per compute unit (each block then rebuilds its operands
+// once and streams ngw rounds of records), never more rounds than the context
+// holds.
+static int fused_groups_per_wave(int batch, int n_kv_heads, int64_t ctx) {
+  const int64_t rounds = ceil_div(ctx, static_cast<int64_t>(kFusedWaves) * kKeysPerWave);
+  const int64_t blocks1 = rounds * batch * n_kv_heads;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(rounds, ceil_div(blocks1, device_cu_count()))));
+}
+
 hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s,
                               const PageMap* pm) {
@@ -580,19 +622,20 @@ hipError_t launch_logits_mfma(const tq_codec_s* c, const void* ws, int batch, in
 }
 
 // One launch for prep and logits when the query group is one M-tile (at most
-// 4 query vectors per KV head), d = 128, and the grid is at most one block per
-// compute unit: then the in-block operand rebuild overlaps the record loads.
-// Larger grids rebuild the operands once per block, which costs more than one
-// prep launch (measured at 32 heads x 32K keys: batch 1 fused 8.0 us against
-// 13.2 split; batch 4 29.8 against 24.9; batch 16 108.6 against 68.1).
+// 4 query vectors per KV head) and d = 128: about one block per compute unit,
+// each rebuilding its operands in LDS while its first records are in flight,
+// then streaming up to 4 rounds of records.  Measured at 32 heads x 32K keys
+// (kernel times, same box): batch 2 11.6 us against 4.5 + 9.7 split, batch 4
+// 17.4 against 4.2 + 17.1; at batch 16 (16 rounds) 66.5 against 5.4 + 54.4,
+// so longer streams take the split form, whose 2048 blocks balance better.
 // TQ_LOGITS_FUSED=0 turns it off.
 bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries,
                            int64_t ctx) {
   const char* v = std::getenv("TQ_LOGITS_FUSED");
   if (v && std::string(v) == "0") return false;
   const int64_t nv = static_cast<int64_t>(n_queries) * (n_q_heads / n_kv_heads);
-  const int64_t blocks = ceil_div(ctx, kFusedWaves * kKeysPerWave) * batch * n_kv_heads;
-  return logits_mfma_eligible(c) && c->prm.d == 128 && nv <= 4 && blocks <= device_cu_count();
+  const int ngw = fused_groups_per_wave(batch, n_kv_heads, ctx);
+  return logits_mfma_eligible(c) && c->prm.d == 128 && nv <= 4 && ngw <= 4 && (ngw == 1 || c->prm.n_planes < 4);
 }
 
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
@@ -604,11 +647,18 @@ hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt
   constexpr int WAVES = kFusedWaves;
   const int G = n_q_heads / n_kv_heads;
   const int vec_out = ctx % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+  const int ngw = fused_groups_per_wave(batch, n_kv_heads, ctx);
   auto go = [&]<int NP, typename T>(const T* qq) -> hipError_t {
-    const dim3 grid(static_cast<unsigned>(ceil_div(ctx, WAVES * kKeysPerWave)), batch * n_kv_heads, 1);
-    hipLaunchKernelGGL((logits_fused_kernel<NP, WAVES, T>), grid, dim3(WAVES * 64), 0, s, qq, c->prm, c->dD, c->dMt,
-                       n_q_heads, n_queries, G, n_kv_heads, static_cast<int>(ctx), k.codes, k.signs, k.norm,
-                       k.rnorm, logits, vec_out);
+    const dim3 grid(static_cast<unsigned>(ceil_div(ctx, static_cast<int64_t>(WAVES) * kKeysPerWave * ngw)),
+                    batch * n_kv_heads, 1);
+    // several rounds: the double-buffered loop (not for 72-byte records: their
+    // second buffer does not fit 128 registers, and the split form takes them)
+    auto kern = logits_fused_kernel<NP, WAVES, T, false>;
+    if constexpr (NP < 4) {
+      if (ngw > 1) kern = logits_fused_kernel<NP, WAVES, T, true>;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, s, qq, c->prm, c->dD, c->dMt, n_q_heads, n_queries, G,
+                       n_kv_heads, static_cast<int>(ctx), k.codes, k.signs, k.norm, k.rnorm, logits, vec_out, ngw);
     return hipGetLastError();
   };
   auto by_np = [&]<typename T>(const T* qq) -> hipError_t {

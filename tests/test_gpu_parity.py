@@ -316,6 +316,42 @@ def test_logits_large_grid_ragged_sampled(B, batch, hq, hkv, nq, ctx):
     assert worst <= 1e-3
 
 
+@pytest.mark.parametrize("bits,batch,hq,hkv,ctx", [(3, 4, 32, 8, 10000), (3, 4, 32, 8, 32768), (2, 3, 12, 3, 30001),
+                                                   (4, 4, 32, 8, 10000)])
+def test_logits_fused_rounds_match_split(B, bits, batch, hq, hkv, ctx, monkeypatch):
+    # grids of more than one block per compute unit at decode shapes: the fused
+    # kernel streams 2-4 rounds of 64-key groups per wave (double-buffered),
+    # 4-bit records take the split form; the two paths agree, and the oracle
+    # scores the last 130 keys of every head and 3000 random keys
+    say(f"fused rounds bits={bits} batch={batch} hq={hq} hkv={hkv} ctx={ctx}")
+    gc, oc = pair(B, 128, bits)
+    rng = np.random.default_rng(ctx + 3 * batch)
+    k = as_exact(rng.standard_normal((batch * hkv * ctx, 128), dtype=np.float32), "bf16")
+    q = as_exact(rng.standard_normal((batch, 1, hq, 128)), "bf16")
+    kp, _ = B.tq_encode_kv(gc, to_dev(k, "bf16"))
+    fused = B.tq_attn_logits(gc, to_dev(q, "bf16"), kp, ctx, hkv).cpu().numpy()
+    monkeypatch.setenv("TQ_LOGITS_FUSED", "0")
+    two = B.tq_attn_logits(gc, to_dev(q, "bf16"), kp, ctx, hkv).cpu().numpy()
+    monkeypatch.delenv("TQ_LOGITS_FUSED")
+    between = row_rel_err(fused.reshape(-1, ctx), two.reshape(-1, ctx).astype(np.float64)).max()
+    tail = (np.arange(batch * hkv)[:, None] * ctx + np.arange(ctx - 130, ctx)[None, :]).ravel()
+    rows = np.unique(np.concatenate([tail, rng.choice(batch * hkv * ctx, 3000, replace=False)]))
+    gk = {kk: x[rows] for kk, x in kp.numpy().items()}
+    rec = oracle_records_like(oc, k[rows].astype(np.float64), gk)
+    G = hq // hkv
+    worst = 0.0
+    for bk in np.unique(rows // ctx):
+        b, kh = bk // hkv, bk % hkv
+        sel = (rows // ctx) == bk
+        t = rows[sel] % ctx
+        qv = q[b, 0, kh * G:(kh + 1) * G]
+        ref = O.score(oc, qv.astype(np.float64), {kk: x[sel] for kk, x in rec.items()})
+        got = fused[b, kh * G:(kh + 1) * G, 0][:, t]
+        worst = max(worst, row_rel_err(got, ref).max())
+    say(f"  fused vs split {between:.2e}  max row err vs oracle {worst:.2e}")
+    assert between <= 1e-4 and worst <= 1e-3
+
+
 def test_logits_ctx_zero_is_noop(B):
     gc, _ = pair(B, 128, 3)
     kp = B.alloc_packed(gc, 1)
