@@ -169,6 +169,35 @@ __device__ __forceinline__ void fwht_lanes(float (&v)[E], int lane) {
   }
 }
 
+// The same transform with the partners fetched without LDS: lane distances
+// 1-8 through DPP within rows of 16, 16 and 32 through v_permlane16_swap /
+// v_permlane32_swap (with a = b = v the first result holds the other half of
+// the lane's pair for an upper lane, the second for a lower one).  The same
+// additions in the same order as fwht_lanes, so the results are identical.
+template <int E>
+__device__ __forceinline__ void fwht_lanes_dpp(float (&v)[E], int lane) {
+  auto stage = [&](auto fetch, bool upper) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o = fetch(v[e]);
+      v[e] = upper ? (o - v[e]) : (v[e] + o);
+    }
+  };
+  stage([](float x) { return __uint_as_float(lane_xor<0>(__float_as_uint(x))); }, lane & 1);
+  stage([](float x) { return __uint_as_float(lane_xor<1>(__float_as_uint(x))); }, (lane >> 1) & 1);
+  stage([](float x) { return __uint_as_float(lane_xor<2>(__float_as_uint(x))); }, (lane >> 2) & 1);
+  stage([](float x) { return __uint_as_float(lane_xor<3>(__float_as_uint(x))); }, (lane >> 3) & 1);
+  const bool up16 = (lane >> 4) & 1, up32 = (lane >> 5) & 1;
+  stage([up16](float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(up16 ? r[0] : r[1]);
+  }, up16);
+  stage([up32](float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(up32 ? r[0] : r[1]);
+  }, up32);
+}
+
 // Butterflies between registers (bits of e, i.e. bits 6.. of j) for a
 // power-of-two E: Sylvester H_E applied across the registers of each lane.
 template <int E>
@@ -188,7 +217,8 @@ __device__ __forceinline__ void fwht_regs(float (&v)[E]) {
 // y = H v for the wave layout.  E a power of two: Sylvester H_{64E}.  E = 24
 // (d = 1536): j = a*128 + i with a = e/2, i = (e%2)*64 + lane, H = H12 ⊗ H128;
 // `transpose` applies Hᵀ (H12 is not symmetric; Sylvester matrices are).
-template <int E, bool kTranspose = false>
+// kDpp: the lane stages through DPP and permlane swaps (fwht_lanes_dpp).
+template <int E, bool kTranspose = false, bool kDpp = false>
 __device__ __forceinline__ void hadamard_wave(float (&v)[E], int lane) {
   if constexpr (E == 24) {
     // H128 on i: register pairs (2a, 2a+1) then the lanes
@@ -198,7 +228,8 @@ __device__ __forceinline__ void hadamard_wave(float (&v)[E], int lane) {
       v[2 * a] = x + y;
       v[2 * a + 1] = x - y;
     }
-    fwht_lanes<24>(v, lane);
+    if constexpr (kDpp) fwht_lanes_dpp<24>(v, lane);
+    else fwht_lanes<24>(v, lane);
     // H12 on a, separately for each half of i
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
@@ -218,7 +249,8 @@ __device__ __forceinline__ void hadamard_wave(float (&v)[E], int lane) {
     }
   } else {
     fwht_regs<E>(v);
-    fwht_lanes<E>(v, lane);
+    if constexpr (kDpp) fwht_lanes_dpp<E>(v, lane);
+    else fwht_lanes<E>(v, lane);
   }
 }
 

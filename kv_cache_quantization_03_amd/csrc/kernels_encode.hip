@@ -10,6 +10,8 @@
 #include <cstdlib>
 #include <string>
 
+#include <utility>
+
 #include "kernels_common.h"
 
 namespace tq {
@@ -24,6 +26,13 @@ namespace tq {
 // (RM = kResF16; the same bytes).  An MSE-only codec (RM = kResNone) keeps
 // neither the residual nor γ: its record is the codes and ν.
 enum ResidualMode { kResF32, kResF16, kResNone };
+
+// f.template operator()<I>() for I = 0..N-1, I a constant expression in each call.
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f.template operator()<I>(), ...); }(
+      std::make_integer_sequence<int, N>{});
+}
 
 template <int E, typename T, int RM>
 __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x, int64_t n, DevParams P,
@@ -48,9 +57,19 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
   const float inv = nu > 0.f ? 1.0f / nu : 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] *= inv * Dsign[e * kWave + lane];
-  hadamard_wave<E>(v, lane);
+  hadamard_wave<E, false, true>(v, lane);
 
-  const int L = 1 << P.b;
+  // quantize (idx = #{k : t_k < y}, ties low).  The codebook is symmetric
+  // (c[L-1-k] = -c[k], middle boundary 0): with s = [y > 0] and m = #{positive
+  // boundaries below |y|} (at or below it when y <= 0, hence |y| one ulp up
+  // there), idx = s ? L/2 + m : L/2-1 - m and c[idx] = ±c[L/2 + m].  At most 3
+  // positive boundaries (L <= 8); the unused ones are +inf.
+  const int H = (1 << P.b) / 2;
+  float tb[3], tc[4];  // the positive boundaries and centroids (uniform; read once)
+#pragma unroll
+  for (int j = 0; j < 3; ++j) tb[j] = P.bound[H + j];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tc[j] = P.cent[min(H + j, 7)];
   int idx[E];
   float rs = 0.f;
   float* rr = rbuf + vec * d;
@@ -58,14 +77,19 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const float y = v[e] * P.inv_sqrt_d;
-    int c = 0;
-    float yh = P.cent[0];
-    for (int k = 0; k < L - 1; ++k) {
-      const bool gt = P.bound[k] < y;
-      c += gt;
-      yh = gt ? P.cent[k + 1] : yh;
+    const bool pos = y > 0.f;
+    const float a = __uint_as_float((__float_as_uint(y) & 0x7FFFFFFFu) + (pos ? 0u : 1u));
+    int mm = 0;
+    float mag = tc[0];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const bool gt = tb[j] < a;
+      mm += gt;
+      mag = gt ? tc[j + 1] : mag;
     }
-    idx[e] = c;
+    idx[e] = pos ? H + mm : H - 1 - mm;
+    asm volatile("" : "+v"(idx[e]));  // a vector register now, not lane masks kept for the packing
+    const float yh = pos ? mag : -mag;
     const float r = y - yh;
     if constexpr (RM == kResF16) {
       const float rsc = r * rscale;
@@ -79,23 +103,29 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
   }
   if constexpr (RM != kResNone) rs = wave_sum(rs);
 
-  // bit-plane packing: plane p, register e -> words p*(d/32) + 2e (+1)
+  // bit-plane packing: plane p, register e -> words p*(d/32) + 2e (+1), the
+  // ballot's two halves selected into lane (word % 64) of register word / 64
+  constexpr int WMAX = 3 * d / 32;                  // words of the widest record (b = 3)
+  constexpr int NW = (WMAX + kWave - 1) / kWave;    // registers of words per lane
   const int W = P.code_words;
   uint32_t* crow = codes + vec * W;
-  for (int base = 0; base < W; base += kWave) {
-    const int w = base + lane;
-    uint32_t word = 0;
-    for (int p = 0; p < P.b; ++p) {
+  uint32_t words[NW];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const uint64_t m = __ballot((idx[e] >> p) & 1);
-        const int w0 = p * (d / 32) + 2 * e;
-        word = (w == w0) ? static_cast<uint32_t>(m) : word;
-        word = (w == w0 + 1) ? static_cast<uint32_t>(m >> 32) : word;
-      }
-    }
-    if (w < W) crow[w] = word;
-  }
+  for (int r = 0; r < NW; ++r) words[r] = 0u;
+  static_for<3>([&]<int p>() {
+    if (p >= P.b) return;  // uniform
+    static_for<E>([&]<int e>() {
+      const uint64_t m = __ballot((idx[e] >> p) & 1);
+      constexpr int w0 = p * (d / 32) + 2 * e;  // even: both halves land in one register
+      uint32_t& wr = words[w0 / kWave];
+      wr = lane == w0 % kWave ? static_cast<uint32_t>(m) : wr;
+      wr = lane == w0 % kWave + 1 ? static_cast<uint32_t>(m >> 32) : wr;
+      __builtin_amdgcn_sched_barrier(0);  // each ballot's two scalar registers are used at once
+    });
+  });
+#pragma unroll
+  for (int r = 0; r < NW; ++r)
+    if (r * kWave + lane < W) crow[r * kWave + lane] = words[r];
   if (lane == 0) {
     norm[vec] = nu;
     if constexpr (RM != kResNone) rnorm[vec] = sqrtf(rs);
