@@ -174,28 +174,37 @@ __device__ __forceinline__ void fwht_lanes(float (&v)[E], int lane) {
 // v_permlane32_swap (with a = b = v the first result holds the other half of
 // the lane's pair for an upper lane, the second for a lower one).  The same
 // additions in the same order as fwht_lanes, so the results are identical.
+template <int K, int E>
+__device__ __forceinline__ void fwht_stage_dpp(float (&v)[E], int lane) {
+  const bool upper = (lane >> K) & 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float o = __uint_as_float(lane_xor<K>(__float_as_uint(v[e])));
+    v[e] = upper ? (o - v[e]) : (v[e] + o);
+  }
+}
 template <int E>
 __device__ __forceinline__ void fwht_lanes_dpp(float (&v)[E], int lane) {
-  auto stage = [&](auto fetch, bool upper) {
+  fwht_stage_dpp<0>(v, lane);
+  fwht_stage_dpp<1>(v, lane);
+  fwht_stage_dpp<2>(v, lane);
+  fwht_stage_dpp<3>(v, lane);
+  const bool up16 = (lane >> 4) & 1;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float o = fetch(v[e]);
-      v[e] = upper ? (o - v[e]) : (v[e] + o);
-    }
-  };
-  stage([](float x) { return __uint_as_float(lane_xor<0>(__float_as_uint(x))); }, lane & 1);
-  stage([](float x) { return __uint_as_float(lane_xor<1>(__float_as_uint(x))); }, (lane >> 1) & 1);
-  stage([](float x) { return __uint_as_float(lane_xor<2>(__float_as_uint(x))); }, (lane >> 2) & 1);
-  stage([](float x) { return __uint_as_float(lane_xor<3>(__float_as_uint(x))); }, (lane >> 3) & 1);
-  const bool up16 = (lane >> 4) & 1, up32 = (lane >> 5) & 1;
-  stage([up16](float x) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(up16 ? r[0] : r[1]);
-  }, up16);
-  stage([up32](float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(up32 ? r[0] : r[1]);
-  }, up32);
+  for (int e = 0; e < E; ++e) {
+    const uint32_t x = __float_as_uint(v[e]);
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const float o = __uint_as_float(up16 ? r[0] : r[1]);
+    v[e] = up16 ? (o - v[e]) : (v[e] + o);
+  }
+  const bool up32 = (lane >> 5) & 1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t x = __float_as_uint(v[e]);
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const float o = __uint_as_float(up32 ? r[0] : r[1]);
+    v[e] = up32 ? (o - v[e]) : (v[e] + o);
+  }
 }
 
 // Butterflies between registers (bits of e, i.e. bits 6.. of j) for a
