@@ -489,7 +489,11 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 namespace {
 constexpr int kPjB = 128;   // outputs and vectors per block
 constexpr int kPjK = 32;    // contraction step
-constexpr int kPjRow = 40;  // LDS row stride in halfs: 16-byte reads of 8 lanes hit distinct banks
+constexpr int kPjRow = 32;  // LDS row stride in halfs: no padding, so two blocks fit a CU's LDS
+// The 16-byte chunk c of LDS row r sits at chunk c ^ ((r >> 1) & 3): the eight
+// rows one ds_read_b128 phase touches (same c) then land in eight distinct
+// 4-bank groups, as the row stores do.
+__device__ __forceinline__ int pj_col(int row, int col) { return ((col >> 3) ^ ((row >> 1) & 3)) << 3; }
 
 __global__ __launch_bounds__(256) void sproj_mfma_kernel(const _Float16* __restrict__ r16, int64_t n, int d, int m,
                                                          const _Float16* __restrict__ S16,
@@ -498,16 +502,19 @@ __global__ __launch_bounds__(256) void sproj_mfma_kernel(const _Float16* __restr
   __shared__ __attribute__((aligned(16))) _Float16 sb[2][2][kPjB][kPjRow];  // [buffer][hi, lo][vector][k]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv & 1, wn = wv >> 1;  // the wave's 64 outputs and 64 vectors
-  // Blocks go to the 8 XCDs round-robin (block p to XCD p % 8).  All m/128 output
-  // tiles of one vector tile run on one XCD at about the same time, so that
-  // XCD's L2 serves the tile's r after the first read.
+  // Blocks go to the 8 XCDs round-robin (block p to XCD p % 8).  The XCDs split
+  // into go output groups x vparts vector parts: XCD x keeps the S rows of its
+  // tpg output tiles (tpg·128·d·4 bytes hi+lo: 2.4 MB at d = 1536) in its L2
+  // and streams every vparts-th vector tile, whose tpg output tiles run there
+  // back to back, so the L2 also serves the tile's r after the first read.
   const int nob = m / kPjB;
+  const int go = nob % 4 == 0 ? 4 : (nob % 2 == 0 ? 2 : 1), vparts = 8 / go, tpg = nob / go;
   const int64_t p = blockIdx.x, xcd = p % 8, kq = p / 8;
-  const int ot = static_cast<int>(kq % nob);
-  const int64_t vt = (kq / nob) * 8 + xcd;
+  const int ot = static_cast<int>((xcd % go) * tpg + kq % tpg);
+  const int64_t vt = (xcd / go) + vparts * (kq / tpg);
   const int o0 = ot * kPjB;
   const int64_t v0 = vt * kPjB;
-  if (v0 >= n) return;  // block-uniform: the padding of the last group of 8
+  if (v0 >= n) return;  // block-uniform: vector tiles past the end (the last round of each part)
   // staging: thread t moves row t/2, contraction elements 16(t%2)..+15 of both operands
   const int srow = tid >> 1, sk = 16 * (tid & 1);
   const _Float16* sp_hi = S16 + static_cast<int64_t>(o0 + srow) * d + sk;
@@ -529,8 +536,8 @@ __global__ __launch_bounds__(256) void sproj_mfma_kernel(const _Float16* __restr
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
-        *reinterpret_cast<h8*>(&sa[b][hl][srow][sk + 8 * i]) = ga[hl][i];
-        *reinterpret_cast<h8*>(&sb[b][hl][srow][sk + 8 * i]) = gb[hl][i];
+        *reinterpret_cast<h8*>(&sa[b][hl][srow][pj_col(srow, sk + 8 * i)]) = ga[hl][i];
+        *reinterpret_cast<h8*>(&sb[b][hl][srow][pj_col(srow, sk + 8 * i)]) = gb[hl][i];
       }
   };
   f4v acc[4][4];
@@ -548,12 +555,13 @@ __global__ __launch_bounds__(256) void sproj_mfma_kernel(const _Float16* __restr
     const int b = ks & 1;
     if (ks + 1 < nk) gload(kPjK * (ks + 1));
     h8 ah[4], al[4], bh[4], bl[4];
+    const int fc = pj_col(fr, fk);  // rows 16i + fr: (row >> 1) & 3 depends on fr only
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ah[i] = *reinterpret_cast<const h8*>(&sa[b][0][64 * wm + 16 * i + fr][fk]);
-      al[i] = *reinterpret_cast<const h8*>(&sa[b][1][64 * wm + 16 * i + fr][fk]);
-      bh[i] = *reinterpret_cast<const h8*>(&sb[b][0][64 * wn + 16 * i + fr][fk]);
-      bl[i] = *reinterpret_cast<const h8*>(&sb[b][1][64 * wn + 16 * i + fr][fk]);
+      ah[i] = *reinterpret_cast<const h8*>(&sa[b][0][64 * wm + 16 * i + fr][fc]);
+      al[i] = *reinterpret_cast<const h8*>(&sa[b][1][64 * wm + 16 * i + fr][fc]);
+      bh[i] = *reinterpret_cast<const h8*>(&sb[b][0][64 * wn + 16 * i + fr][fc]);
+      bl[i] = *reinterpret_cast<const h8*>(&sb[b][1][64 * wn + 16 * i + fr][fc]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -662,8 +670,10 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
     const int64_t per_launch = static_cast<int64_t>(1) << 24;  // vectors per launch (grid size well inside 2^32)
     for (int64_t v0 = 0; v0 < n; v0 += per_launch) {
       const int64_t nv = std::min(per_launch, n - v0);
-      // one-dimensional grid: every vector tile (rounded up to 8) times every output tile
-      const dim3 grid(static_cast<unsigned>(ceil_div(ceil_div(nv, kPjB), 8) * 8 * (P.m / kPjB)));
+      // one-dimensional grid: 8 XCDs x tpg output tiles x the vector tiles of each vector part
+      const int nob = P.m / kPjB;
+      const int go = nob % 4 == 0 ? 4 : (nob % 2 == 0 ? 2 : 1);
+      const dim3 grid(static_cast<unsigned>(8 * (nob / go) * ceil_div(ceil_div(nv, kPjB), 8 / go)));
       hipLaunchKernelGGL(sproj_mfma_kernel, grid, dim3(256), 0, s, r16 + v0 * 2 * P.d, nv, P.d, P.m, c->dS16,
                          out.signs + v0 * P.sign_words);
       const hipError_t e2 = hipGetLastError();
