@@ -187,9 +187,14 @@ def main():
         outd = torch.empty((1, 32, d), dtype=torch.bfloat16, device=dev)
         for _ in range(5):
             B.tq_decode_attn(cdc, cdc, qd, kpd, kpd, 131072, 8, 1 / math.sqrt(d), out=outd)
+        # and 5 with the same keys as a V cache in 32-row blocks
+        cvb = B.tq_codec_create_vblock(d, 3, False, I.CODEC_SEED)
+        vbd = B.tq_encode_kv(cvb, kd)[0]
+        for _ in range(5):
+            B.tq_decode_attn(cdc, cvb, qd, kpd, vbd, 131072, 8, 1 / math.sqrt(d), out=outd)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": True, "logits_launches": 20, "copy_bytes": 64 * 2 ** 20, "copies": 5,
-                          "decode_launches": 5, "encode_launches": 3}))
+                          "decode_launches": 10, "encode_launches": 4}))
         return
 
     # ---- the timed steps run as one HIP graph (no host launch cost per step)
