@@ -438,6 +438,8 @@ def _unpack_record(codec: Codec, packed: dict):
 def dequantize(codec: Codec, packed: dict) -> np.ndarray:
     """v̂ = ν Rᵀ (c[idx] + sqrt(pi/2)/m · γ · Sᵀ τ): the unbiased reconstruction
     (E_S[Sᵀ sign(S r)] = sqrt(2/pi) m r/||r||); ν Rᵀ c[idx] for an MSE-only codec."""
+    if isinstance(codec, PolarCodec):  # the recursive polar first stage (O8)
+        return polar_dequantize(codec, packed)
     idx, tau, nu, gamma = _unpack_record(codec, packed)
     chat = codec.c32.astype(np.float64)[idx]
     if not codec.qjl:
@@ -461,6 +463,8 @@ def prepare_query(codec: Codec, q: np.ndarray):
 
 def score(codec: Codec, q: np.ndarray, packed: dict) -> np.ndarray:
     """Logits of every query row against every packed key: (n_q, n_keys) fp64."""
+    if isinstance(codec, PolarCodec):  # the recursive polar first stage (O8)
+        return polar_score(codec, q, packed)
     if not codec.qjl:
         raise ValueError("an MSE-only codec has no unbiased score; keys take the two-stage codec")
     qr, p = prepare_query(codec, np.atleast_2d(q))
@@ -497,7 +501,10 @@ def attn_logits(codec: Codec, q: np.ndarray, packed: dict, batch: int,
 # O6. Fused decode attention: w = softmax(scale · ℓ) over the context,
 # o = Σ_i w_i v̂_i (V compressed like K: TurboQuant+ 深度解析 第五部分).
 # Two formulations that must agree: materialize every v̂_i, or accumulate
-# M = Σ w ν c[idx] and J = Σ w ν γ τ first and map back once.
+# M = Σ w ν c[idx] and J = Σ w ν γ τ first and map back once.  Either codec
+# may take the recursive polar first stage of O8 instead (深度拆解 第二部分
+# 第三步 compresses the whole KV cache that way): its score and v̂ keep the
+# same form with ŷ, rebuilt from the angle codes, in place of c[idx].
 # --------------------------------------------------------------------------
 def _softmax_weights(logits: np.ndarray, scale: float):
     s = scale * logits
@@ -534,8 +541,12 @@ def decode_attn_accumulated(codec_k: Codec, codec_v: Codec, q, k_packed, v_packe
         for kh in range(n_kv_heads):
             row0 = (bi * n_kv_heads + kh) * ctx_len
             keys = _slice_packed(k_packed, row0, row0 + ctx_len)
-            idx, tau, nu, gamma = _unpack_record(codec_v, _slice_packed(v_packed, row0, row0 + ctx_len))
-            chat = codec_v.c32.astype(np.float64)[idx]
+            vals = _slice_packed(v_packed, row0, row0 + ctx_len)
+            if isinstance(codec_v, PolarCodec):  # ŷ rebuilt from the angle codes (O8)
+                chat, tau, nu, gamma = _polar_unpack(codec_v, vals)
+            else:
+                idx, tau, nu, gamma = _unpack_record(codec_v, vals)
+                chat = codec_v.c32.astype(np.float64)[idx]
             hs = slice(kh * G, (kh + 1) * G)
             lg = score(codec_k, q[bi, hs], keys)
             e, l = _softmax_weights(lg, scale)
@@ -901,6 +912,10 @@ class PolarCodec:
     @property
     def b(self) -> int:
         return self.bits - 1
+
+    @property
+    def qjl(self) -> bool:  # the residual always takes the QJL stage
+        return True
 
     @property
     def levels(self) -> int:

@@ -794,6 +794,50 @@ def test_polar_score_unbiased_and_matches_dequantize():
     assert abs(vals.mean() - float((q @ x.T)[0, 0])) < 3.5 * vals.std() / math.sqrt(vals.size)
 
 
+def _dense_attention(qh, khat, vhat, scale):
+    """softmax(scale · q k̂ᵀ) v̂ for one KV group, in plain dense fp64 algebra."""
+    s = scale * (qh @ khat.T)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)) @ vhat
+
+
+@pytest.mark.parametrize("kpolar,vpolar", [(True, True), (False, True), (True, False)])
+def test_polar_decode_attention_is_dense_attention_over_reconstructions(kpolar, vpolar):
+    # Either codec with the recursive polar first stage: both formulations of
+    # decode attention (materialized v̂, and M/J accumulated in the rotated
+    # and QJL domains) equal dense attention over the dequantized keys and
+    # values, the logits taken as plain dot products q·k̂ (the score's
+    # unbiased form equals ⟨q, k̂⟩ exactly).
+    d, batch, hq, hkv, ctx = 32, 2, 4, 2, 9
+    ck = O.make_polar_codec(d, 3, seed=21) if kpolar else O.make_codec(d, 3, seed=21)
+    cv = O.make_polar_codec(d, 3, seed=22) if vpolar else O.make_codec(d, 3, seed=22)
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((batch * hkv * ctx, d)) * 1.5
+    v = rng.standard_normal((batch * hkv * ctx, d))
+    q = rng.standard_normal((batch, hq, d))
+    enc = lambda c, x: O.polar_encode(c, x) if isinstance(c, O.PolarCodec) else O.encode(c, x)
+    kr, vr = enc(ck, k), enc(cv, v)
+    khat, vhat = O.dequantize(ck, kr), O.dequantize(cv, vr)
+    scale = 0.4
+    a = O.decode_attn_materialized(ck, cv, q, kr, vr, batch, hq, hkv, ctx, scale)
+    b = O.decode_attn_accumulated(ck, cv, q, kr, vr, batch, hq, hkv, ctx, scale)
+    G = hq // hkv
+    for bi in range(batch):
+        for kh in range(hkv):
+            rows = slice((bi * hkv + kh) * ctx, (bi * hkv + kh + 1) * ctx)
+            hs = slice(kh * G, (kh + 1) * G)
+            ref = _dense_attention(q[bi, hs], khat[rows], vhat[rows], scale)
+            assert np.allclose(a[bi, hs], ref, rtol=1e-10, atol=1e-12)
+            assert np.allclose(b[bi, hs], ref, rtol=1e-10, atol=1e-12)
+    # one position: the output is that value's reconstruction, whatever the query
+    one = O.decode_attn_accumulated(ck, cv, q[:1, :2], {x: kr[x][:1] for x in ("codes", "signs", "norm", "rnorm")},
+                                    {x: vr[x][:1] for x in ("codes", "signs", "norm", "rnorm")}, 1, 2, 1, 1, scale)
+    assert np.allclose(one[0], np.repeat(vhat[:1], 2, axis=0), rtol=1e-12, atol=1e-12)
+    # the gated oracle at gate 0 is the plain one
+    g0, keep, _ = O.decode_attn_sparse_v(ck, cv, q, kr, vr, batch, hq, hkv, ctx, scale, 0.0, 4)
+    assert keep.all() and np.allclose(g0, b, rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------- bf16 rounding helper
 def _bf16_nearest(x32: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even to bfloat16 from its definition: of the two
