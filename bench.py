@@ -465,6 +465,38 @@ def mse_v_stage(B, codec3, dev, g, dsets, qd, out, ctx, d):
     return res
 
 
+def polar_decode_stage(B, I, codec3, dev, g, dsets, qd, out, ctx, d):
+    """Decode attention on the long-context shape with the recursive polar
+    first stage: polar K and V (3-bit, 56-byte records), and per-coordinate K
+    with polar V.  Three K/V sets."""
+    import torch
+    hkv, hq, scale = 8, 32, 1 / math.sqrt(d)
+    cp = B.tq_codec_create_polar(d, 3, 0, I.CODEC_SEED)
+    k = torch.randn((hkv * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((hkv * ctx, d), generator=g, device=dev).to(torch.bfloat16)
+    kp, vp = B.tq_encode_kv(cp, k, v)
+    del k, v
+    sets = [(kp, vp)] + [(B.Packed(kp.codes.clone(), kp.signs.clone(), kp.norm.clone(), kp.rnorm.clone()),
+                          B.Packed(vp.codes.clone(), vp.signs.clone(), vp.norm.clone(), vp.rnorm.clone()))
+                         for _ in range(len(dsets) - 1)]
+    res = {}
+    for name, ck, ksets in (("decode_attn_c4_polar_kv", cp, [s[0] for s in sets]),
+                            ("decode_attn_c4_polar_v", codec3, [s[0] for s in dsets])):
+        ws = torch.empty(B.tq_decode_attn_workspace(ck, cp, 1, hq, hkv, ctx), dtype=torch.uint8, device=dev)
+        it = iter(range(10 ** 9))
+
+        def step():
+            i = next(it) % len(sets)
+            B.tq_decode_attn(ck, cp, qd, ksets[i], sets[i][1], ctx, hkv, scale, out=out, ws=ws)
+        ms = _time(step, 30, graph=True)
+        res[name] = {"ms": ms, "buffer_sets": len(sets),
+                     **_hbm(ms, hkv * ctx * (ck.record_bytes + cp.record_bytes) + 2 * hq * d * 2)}
+        print(f"[bench] {name} {ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del ws
+    del sets, kp, vp, cp
+    return res
+
+
 def paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d):
     """Paged cache on the long-context decode shape.  (1) The same caches
     copied into 256-position pages in shuffled order, read through the page
@@ -729,6 +761,7 @@ def time_stages(B, I, codec3, dev, args):
         res.update(sparse_v_stage(B, codec3, dev, g, k_c4, vp, dsets, qd, out, ws, ctx, d, vblock=(cvb, vbsets)))
     res.update(paged_stage(B, codec3, dev, g, dsets, qd, out, ws, ctx, d))
     res.update(mse_v_stage(B, codec3, dev, g, dsets, qd, out, ctx, d))
+    res.update(polar_decode_stage(B, I, codec3, dev, g, dsets, qd, out, ctx, d))
     del kp, vp, dsets, ws, k_c4, vbp, vbsets
     if not args.no_stage_sparse_v:
         # Sparse V on the 32K decode shape: 12 K/V sets (about 2.6x the Infinity Cache)

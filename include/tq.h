@@ -166,8 +166,11 @@ tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uin
  * (fp32), and the residual y - ŷ takes the same QJL stage, so the record size
  * and the score ν(⟨q', ŷ⟩ + √(π/2)/m γ ⟨p, τ⟩) keep their form.
  * head_dim 128 only; bits 2, 3 or 4.  Such codecs are accepted by
- * tq_encode_kv, tq_attn_logits and its split form; the other calls return
- * TQ_ERROR_NOT_SUPPORTED for them. */
+ * tq_encode_kv, tq_attn_logits and its split form, and as either codec (ck,
+ * cv or both) of tq_decode_attn, tq_decode_attn_no_alloc and
+ * tq_decode_attn_sparse_v (深度拆解 第二部分 第三步: the whole KV cache in polar
+ * form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)); the paged calls and tq_search_topk
+ * return TQ_ERROR_NOT_SUPPORTED for them. */
 tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                   tq_codec_t* out);
 /* An MSE-only value codec: the same rotation and per-coordinate Lloyd-Max
@@ -281,7 +284,11 @@ tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, size_t prep_b
  *   ck, cv : codecs of K and V (they may be the same handle; their bits may
  *            differ; head_dim must match).  cv may be an MSE-only codec
  *            (tq_codec_create_mse): then v̂ = ν Rᵀ c[idx] and v.signs,
- *            v.rnorm are not read.
+ *            v.rnorm are not read.  Either may be a polar codec
+ *            (tq_codec_create_polar; then both have head_dim 128 and cv is
+ *            not a codec in 32-row blocks): the logits then come from the
+ *            key codec's scorer and are held in the workspace, and a polar
+ *            value's ŷ is rebuilt per position from its angle codes.
  *   q      : device [batch][n_q_heads][d], dtype q_dt.
  *   k, v   : packed rows [batch][n_kv_heads][ctx_len].
  *   out    : device [batch][n_q_heads][d], dtype out_dt (TQ_F32 or TQ_BF16,

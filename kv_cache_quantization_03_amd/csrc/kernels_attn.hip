@@ -412,6 +412,18 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   }
 }
 
+// The d = m = 128 combine over contiguous chunk partials (M only for an
+// MSE-only value codec).
+hipError_t launch_decode_combine128(const tq_codec_s* cv, const float* part, int batch, int n_q_heads,
+                                    int n_kv_heads, int n_chunks, int chunk, void* out, tq_dtype_t out_dt,
+                                    hipStream_t s) {
+  auto kern = cv->qjl ? decode_combine128_kernel<true> : decode_combine128_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part, n_q_heads, n_kv_heads,
+                     n_chunks, static_cast<const int32_t*>(nullptr), chunk, cv->dS, cv->dD, out,
+                     out_dt == TQ_BF16 ? 1 : 0);
+  return hipGetLastError();
+}
+
 bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why) {
   const int G = n_q_heads / n_kv_heads;
   if (G > 16) { *why = "at most 16 query heads per KV head"; return false; }
@@ -433,10 +445,18 @@ static size_t decode_prep_region(const tq_codec_s* ck, int batch, int n_q_heads,
   return (std::max(valu, mfma) + 255) / 256 * 256;
 }
 
+size_t decode_polar_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
+                             int64_t ctx, int CH);
+hipError_t launch_decode_polar(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
+                               int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx,
+                               float scale, bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws,
+                               int CH, hipStream_t s);
+
 size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                        int64_t ctx) {
   const int G = n_q_heads / n_kv_heads;
   const int CH = attn_chunk(G);
+  if (ck->polar || cv->polar) return decode_polar_ws_bytes(ck, cv, batch, n_q_heads, n_kv_heads, ctx, CH);
   const int64_t n_chunks = ceil_div(ctx, CH);
   const size_t part = static_cast<size_t>(batch) * n_kv_heads * n_chunks * G * (2 + cv->prm.d + cv->prm.m) * sizeof(float);
   return decode_prep_region(ck, batch, n_q_heads, n_kv_heads) + part;
@@ -464,6 +484,9 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
                          hipStream_t s) {
   const int G = n_q_heads / n_kv_heads;
   const int CH = attn_chunk(G);
+  if (ck->polar || cv->polar)  // logits by the key codec's scorer, then V from them (kernels_attn_polar.hip)
+    return launch_decode_polar(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, sparse_v, v_gate,
+                               out, out_dt, ws, CH, s);
   int n_chunks = static_cast<int>(ceil_div(ctx, CH));
   const int64_t nq = static_cast<int64_t>(batch) * n_q_heads;
   float* qrot = static_cast<float*>(ws);

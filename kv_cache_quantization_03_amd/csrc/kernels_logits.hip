@@ -6,6 +6,8 @@
 // This file holds the general VALU kernel (one thread per key, any head_dim,
 // any number of query vectors per KV head).  It is the reference kernel on the
 // GPU and covers shapes the MFMA kernel does not.
+#include <algorithm>
+
 #include "kernels_common.h"
 
 namespace tq {
@@ -102,6 +104,19 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // ----------------------------------------------------------------------------
 constexpr int kPolarKeys = 1024;
 
+// One key's record into registers (nothing past the context).
+template <int B>
+__device__ __forceinline__ void polar_fetch(const tq_packed_t& k, int64_t rowb, int64_t key, int64_t ctx, uint4 (&nc)[B],
+                                            uint4& ns, float& nn, float& ng) {
+  if (key < ctx) {
+#pragma unroll
+    for (int p = 0; p < B; ++p) nc[p] = reinterpret_cast<const uint4*>(k.codes + (rowb + key) * (4 * B))[p];
+    ns = reinterpret_cast<const uint4*>(k.signs)[rowb + key];
+    nn = k.norm[rowb + key];
+    ng = k.rnorm[rowb + key];
+  }
+}
+
 template <int B>
 __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
                                                            const float* __restrict__ proj, int Hq, int nq, int G,
@@ -176,17 +191,24 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     }
   }
   __syncthreads();
-  const int64_t key = static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid;
-  if (key >= ctx) return;
-  const int64_t row = static_cast<int64_t>(bk) * ctx + key;
+  // blocks stride over the context's 1024-key blocks; each thread's next
+  // record is loaded while the current one is scored
+  const int64_t nkb = (ctx + kPolarKeys - 1) / kPolarKeys;
+  const int64_t rowb = static_cast<int64_t>(bk) * ctx;
+  uint4 nc[B], ns = uint4{0u, 0u, 0u, 0u};
+  float nn = 0.f, ng = 0.f;
+  polar_fetch<B>(k, rowb, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, ctx, nc, ns, nn, ng);
+  for (int64_t kb = blockIdx.x; kb < nkb; kb += gridDim.x) {
+  const int64_t key = kb * kPolarKeys + tid;
   uint32_t w[B][4];
 #pragma unroll
   for (int p = 0; p < B; ++p) {
-    const uint4 u = reinterpret_cast<const uint4*>(k.codes + row * (4 * B))[p];
-    w[p][0] = u.x; w[p][1] = u.y; w[p][2] = u.z; w[p][3] = u.w;
+    w[p][0] = nc[p].x; w[p][1] = nc[p].y; w[p][2] = nc[p].z; w[p][3] = nc[p].w;
   }
-  const uint4 sg = reinterpret_cast<const uint4*>(k.signs)[row];
-  const uint32_t sw[4] = {sg.x, sg.y, sg.z, sg.w};
+  const uint32_t sw[4] = {ns.x, ns.y, ns.z, ns.w};
+  const float nu = nn, ga = ng;
+  polar_fetch<B>(k, rowb, key + static_cast<int64_t>(gridDim.x) * kPolarKeys, ctx, nc, ns, nn, ng);
+  if (key < ctx) {
   auto code = [&](int slot) {  // slot is a constant after unrolling
     int c = 0;
 #pragma unroll
@@ -249,10 +271,11 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     const float4 x = ptab[g][(sw[g >> 2] >> (8 * (g & 3))) & 255u];
     qj[0] += x.x; qj[1] += x.y; qj[2] += x.z; qj[3] += x.w;
   }
-  const float nu = k.norm[row], ga = k.rnorm[row];
 #pragma unroll
   for (int t = 0; t < 4; ++t)  // Σ p τ = 2 Σ_{τ=+1} p - Σ p
     if (orow[t] >= 0) logits[orow[t] + key] = nu * (mse[t] + P.qjl_kappa * ga * (2.f * qj[t] - psum[t]));
+  }
+  }
 }
 
 hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
@@ -261,8 +284,11 @@ hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, i
   const float* qrot = static_cast<const float*>(ws);
   const float* proj = qrot + nv * c->prm.d;
   const int G = n_q_heads / n_kv_heads;
-  const dim3 grid(static_cast<unsigned>(ceil_div(ctx, kPolarKeys)), batch * n_kv_heads,
-                  static_cast<unsigned>(ceil_div(static_cast<int64_t>(n_queries) * G, 4)));
+  // about one block per compute unit (a block's tables fill most of its LDS);
+  // each block then scores several 1024-key blocks with the tables it built
+  const int64_t nz = ceil_div(static_cast<int64_t>(n_queries) * G, 4), nkb = ceil_div(ctx, kPolarKeys);
+  const int64_t per = std::max<int64_t>(1, device_cu_count() / std::max<int64_t>(1, batch * n_kv_heads * nz));
+  const dim3 grid(static_cast<unsigned>(std::min(nkb, per)), batch * n_kv_heads, static_cast<unsigned>(nz));
   auto go = [&]<int B>() -> hipError_t {
     hipLaunchKernelGGL((logits_polar_kernel<B>), grid, dim3(kPolarKeys), 0, s, c->prm, c->pol, qrot, proj, n_q_heads,
                        n_queries, G, n_kv_heads, ctx, k, logits);

@@ -553,14 +553,6 @@ hipError_t launch_logits_mfma_prep(const tq_codec_s* c, const void* q, tq_dtype_
 
 constexpr int kFusedWaves = 16;  // 1024 keys per fused block
 
-static int device_cu_count() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
-  return n;
-}
-
 // Rounds of 64-key groups per wave of the fused kernel: enough that the grid
 // is about one block per compute unit (each block then rebuilds its operands
 // once and streams ngw rounds of records), never more rounds than the context

@@ -258,8 +258,11 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->polar || cv->polar) {
-    set_error("decode attention takes codecs with the per-coordinate first stage");
-    return TQ_ERROR_NOT_SUPPORTED;
+    if (pm) { set_error("paged decode takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
+    if (!tq::decode_polar_shape_ok(ck, cv)) {
+      set_error("decode attention with a polar codec needs head_dim 128 for K and V, qjl_dim 128 and V in row records");
+      return TQ_ERROR_NOT_SUPPORTED;
+    }
   }
   if (!ck->qjl) { set_error("the K codec must be a two-stage codec (an MSE-only codec is a value codec)"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!valid_dtype(q_dt) || (out_dt != TQ_F32 && out_dt != TQ_BF16)) { set_error("bad dtype"); return TQ_ERROR_INVALID_VALUE; }

@@ -164,6 +164,9 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
                          int64_t ctx, float scale, bool sparse_v, float v_gate, const PageMap* pm, void* out,
                          tq_dtype_t out_dt, void* ws, hipStream_t s);
 bool decode_paged_supported(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
+// Either codec polar (the logits by the key scorer, then V from them): d = m =
+// 128 and V in row records.
+bool decode_polar_shape_ok(const tq_codec_s* ck, const tq_codec_s* cv);
 
 size_t append_paged_ws_bytes(const tq_codec_s* c, int64_t n_rec);
 hipError_t launch_append_paged(const tq_codec_s* c, const void* x, tq_dtype_t dt, int batch, int n_kv_heads,

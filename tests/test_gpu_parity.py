@@ -991,7 +991,10 @@ def test_polar_encode_basis_vectors(B, bits):
 
 
 @pytest.mark.parametrize("bits,batch,hq,hkv,nq,ctx", [(3, 1, 8, 2, 1, 1000), (2, 2, 4, 4, 3, 333), (4, 1, 32, 8, 1, 257),
-                                                     (3, 1, 1, 1, 5, 1)])
+                                                     (3, 1, 1, 1, 5, 1),
+                                                     # 32 (sequence, KV head, 4-vector) groups: 8 blocks each
+                                                     # stride over 9 key blocks (the last ragged)
+                                                     (3, 2, 64, 8, 1, 9000)])
 def test_polar_logits_oracle_records(B, bits, batch, hq, hkv, nq, ctx):
     # the scorer alone: oracle-encoded records, fp32 queries, bar 1e-4
     say(f"polar logits bits={bits} batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx}")
@@ -1042,9 +1045,6 @@ def test_polar_codec_limits(B):
     with pytest.raises(B.TQError):
         B.tq_codec_create_polar(256, 3)
     kp = B.alloc_packed(gc, 64)
-    q = torch.zeros((1, 4, 128), device="cuda")
-    with pytest.raises(B.TQError):
-        B.tq_decode_attn(gc, gc, q, kp, kp, 64, 1, 0.1)
     with pytest.raises(B.TQError):
         B.tq_search_topk(gc, kp, torch.zeros((1, 128), device="cuda"), 5)
 

@@ -1,0 +1,204 @@
+"""GPU parity of decode attention when either codec takes the recursive polar
+first stage (「谷歌 TurboQuant 深度拆解」 第二部分 第三步: the whole KV cache in
+polar form), against the oracle's decode attention over the same records.
+Every call goes through the C ABI (ctypes binding over libtq.so)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.parity import assert_sparse_v_close, assert_sparse_v_within_plain_rule, polar_records_like, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from kv_cache_quantization_03_amd import binding
+    return binding
+
+
+_codecs = {}
+
+
+def codec(B, kind, bits, seed):
+    """(GPU codec, oracle codec): kind 'polar', 'scalar' (two-stage) or 'mse'."""
+    key = (kind, bits, seed)
+    if key not in _codecs:
+        if kind == "polar":
+            _codecs[key] = (B.tq_codec_create_polar(128, bits, 0, seed), O.make_polar_codec(128, bits, seed=seed))
+        elif kind == "mse":
+            _codecs[key] = (B.tq_codec_create_mse(128, bits, seed), O.make_mse_codec(128, bits, seed=seed))
+        else:
+            _codecs[key] = (B.tq_codec_create(128, bits, 0, seed), O.make_codec(128, bits, seed=seed))
+    return _codecs[key]
+
+
+def encode(oc, x):
+    r = O.polar_encode(oc, x) if isinstance(oc, O.PolarCodec) else O.encode(oc, x)
+    return {k: r[k] for k in ("codes", "signs", "norm", "rnorm")}
+
+
+def to_dev(x32, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).cuda()
+    return t.to(torch.bfloat16) if dtype == "bf16" else t
+
+
+def exact(x, dtype):
+    x = np.asarray(x, np.float32)
+    return O.bf16_round(x) if dtype == "bf16" else x
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("kk,kbits,vk,vbits,hq,hkv,ctx", [
+    ("polar", 3, "polar", 3, 8, 2, 3000),    # 1024-position chunks, ragged tail
+    ("scalar", 3, "polar", 3, 4, 1, 1025),   # per-coordinate K (fused scorer), polar V
+    ("polar", 3, "scalar", 3, 32, 8, 700),   # polar K, per-coordinate V
+    ("polar", 4, "polar", 2, 16, 1, 513),    # 16 query heads per KV head: 256-position chunks
+    ("polar", 2, "polar", 4, 2, 2, 1),       # one position
+    ("polar", 3, "mse", 3, 8, 2, 1500),      # polar K, MSE-only V (no J)
+    ("polar", 3, "polar", 3, 12, 2, 2049),   # 6 heads per KV head: 512-position chunks
+])
+def test_polar_decode_attn_parity(B, kk, kbits, vk, vbits, hq, hkv, ctx):
+    say(f"polar decode K {kk}{kbits} V {vk}{vbits} hq={hq} hkv={hkv} ctx={ctx}")
+    gk, ok = codec(B, kk, kbits, 1234)
+    gv, ov = codec(B, vk, vbits, 4321)
+    rng = np.random.default_rng(ctx + hq + kbits)
+    k = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    v = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    q = exact(rng.standard_normal((1, hq, 128)), "bf16")
+    kr, vr = encode(ok, k.astype(np.float64)), encode(ov, v.astype(np.float64))
+    scale = 1 / math.sqrt(128)
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale)
+    kp, vp = B.packed_from_numpy(kr), B.packed_from_numpy(vr)
+    out32 = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, scale, out_dtype=torch.float32)
+    out16 = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = out32.cpu().numpy()
+    err = row_rel_err(g32, ref)
+    say(f"  max row err {err.max():.3e}")
+    assert np.all(err <= 1e-4)
+    assert np.array_equal(out16.float().cpu().numpy(), O.bf16_round(g32))
+
+
+def test_polar_decode_end_to_end(B):
+    # GPU encode of K and V with polar codecs, then decode: against the oracle
+    # conditioned on the GPU's legitimate boundary choices
+    gk, ok = codec(B, "polar", 3, 1234)
+    gv, ov = codec(B, "polar", 3, 4321)
+    hq, hkv, ctx = 8, 2, 2500
+    rng = np.random.default_rng(91)
+    k = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    v = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
+    q = exact(rng.standard_normal((1, hq, 128)), "bf16")
+    kp = B.tq_encode_kv(gk, to_dev(k, "bf16"))[0]
+    vp = B.tq_encode_kv(gv, to_dev(v, "bf16"))[0]
+    out = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, 1 / math.sqrt(128), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kr = polar_records_like(ok, k.astype(np.float64), kp.numpy())
+    vr = polar_records_like(ov, v.astype(np.float64), vp.numpy())
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, 1 / math.sqrt(128))
+    err = row_rel_err(out.cpu().numpy(), ref).max()
+    say(f"polar decode end to end: max row err {err:.2e}")
+    assert err <= 1e-4
+
+
+def test_polar_decode_one_hot(B):
+    # one key takes all the weight: the output is that value's polar reconstruction
+    gk, ok = codec(B, "polar", 3, 1234)
+    gv, ov = codec(B, "polar", 3, 4321)
+    ctx = 900
+    rng = np.random.default_rng(6)
+    k = rng.standard_normal((ctx, 128))
+    v = rng.standard_normal((ctx, 128))
+    q = rng.standard_normal((1, 1, 128)).astype(np.float32)
+    kr, vr = encode(ok, k), encode(ov, v)
+    j = int(np.argmax(O.score(ok, q[0].astype(np.float64), kr)[0]))
+    kr["norm"] = kr["norm"].copy()
+    kr["norm"][j] *= 1e4
+    out = B.tq_decode_attn(gk, gv, to_dev(q, "f32"), B.packed_from_numpy(kr), B.packed_from_numpy(vr), ctx, 1, 1.0,
+                           out_dtype=torch.float32).cpu().numpy()
+    vhat = O.dequantize(ov, vr)[j]
+    assert np.max(np.abs(out[0, 0] - vhat)) <= 1e-4 * np.max(np.abs(vhat))
+
+
+@pytest.mark.parametrize("hq,hkv,ctx,gate,needles", [(8, 2, 3000, 1e-6, True), (16, 2, 1500, 1e-3, False)])
+def test_polar_decode_sparse_v(B, hq, hkv, ctx, gate, needles):
+    say(f"polar Sparse V hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles}")
+    gk, ok = codec(B, "polar", 3, 1234)
+    gv, ov = codec(B, "polar", 3, 4321)
+    rng = np.random.default_rng(ctx + hq)
+    G = hq // hkv
+    q = (1.0 if needles else 3.0) * rng.standard_normal((1, hq, 128))
+    k = rng.standard_normal((hkv * ctx, 128))
+    v = rng.standard_normal((hkv * ctx, 128))
+    if needles:  # one position per 1024 takes the weight of the group's queries
+        for kh in range(hkv):
+            u = q[0, kh * G:(kh + 1) * G].sum(axis=0)
+            u /= np.linalg.norm(u)
+            for t in range(200, ctx, 1024):
+                k[kh * ctx + t] += 60.0 * u
+    q, k, v = exact(q, "f32"), exact(k, "f32"), exact(v, "f32")
+    kr, vr = encode(ok, k.astype(np.float64)), encode(ov, v.astype(np.float64))
+    scale = 1 / math.sqrt(128)
+    chunk = B.tq_decode_attn_chunk(hq, hkv)
+    ref, keep, local = O.decode_attn_sparse_v(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale, gate,
+                                              chunk)
+    say(f"  dropped (head, key) {np.mean(~keep):.3f}")
+    assert np.mean(~keep) > 0.3
+    out = B.tq_decode_attn_sparse_v(gk, gv, to_dev(q, "f32"), B.packed_from_numpy(kr), B.packed_from_numpy(vr), ctx,
+                                    hkv, scale, gate, out_dtype=torch.float32).cpu().numpy()
+    vhat = O.dequantize(ov, vr)
+    assert_sparse_v_close(out, ref, local, gate, vhat, hkv, ctx, 1e-4)
+    plain, keep_p, w = O.decode_attn_sparse_v_plain(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale,
+                                                    gate)
+    assert np.all(keep | ~keep_p)
+    assert_sparse_v_within_plain_rule(out, plain, w, gate, vhat, hkv, ctx, 1e-4)
+
+
+def test_polar_decode_batch_and_workspace(B):
+    # batch 3: each sequence's heads read their own rows; the no-alloc entry
+    # point gives the same bits as the workspace one
+    gk, ok = codec(B, "polar", 3, 1234)
+    gv, ov = codec(B, "polar", 3, 4321)
+    batch, hq, hkv, ctx = 3, 4, 2, 777
+    rng = np.random.default_rng(12)
+    k = exact(rng.standard_normal((batch * hkv * ctx, 128)), "f32")
+    v = exact(rng.standard_normal((batch * hkv * ctx, 128)), "f32")
+    q = exact(rng.standard_normal((batch, hq, 128)), "f32")
+    kr, vr = encode(ok, k.astype(np.float64)), encode(ov, v.astype(np.float64))
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, batch, hq, hkv, ctx, 0.2)
+    kp, vp = B.packed_from_numpy(kr), B.packed_from_numpy(vr)
+    a = B.tq_decode_attn(gk, gv, to_dev(q, "f32"), kp, vp, ctx, hkv, 0.2, out_dtype=torch.float32)
+    b = B.tq_decode_attn_no_alloc(gk, gv, to_dev(q, "f32"), kp, vp, ctx, hkv, 0.2,
+                                  torch.empty((batch, hq, 128), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert np.array_equal(a, b)
+    assert row_rel_err(a, ref).max() <= 1e-4
+
+
+def test_polar_decode_refusals(B):
+    gk, _ = codec(B, "polar", 3, 1234)
+    gs, _ = codec(B, "scalar", 3, 1234)
+    q = torch.zeros((1, 4, 128), device="cuda")
+    kp = B.alloc_packed(gk, 256)
+    # paged caches take per-coordinate codecs only
+    cl = torch.tensor([100], dtype=torch.int32, device="cuda")
+    pt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn_paged(gk, gk, q, kp, kp, cl, pt, 256, 256, 1, 0.1)
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn_paged(gs, gk, q, B.alloc_packed(gs, 256), kp, cl, pt, 256, 256, 1, 0.1)
+    # a value cache in 32-row blocks is read by the matrix-core kernel only
+    gvb = B.tq_codec_create_vblock(128, 3, False, 1234)
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn(gk, gvb, q, kp, B.alloc_packed(gvb, 256), 256, 1, 0.1)
