@@ -381,9 +381,11 @@ tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dtype_t dt, i
  * [0, max_ctx]); an empty context gives a zero output.  max_ctx (host) bounds
  * every ctx_lens[b] and sizes the grid and the workspace:
  * tq_decode_attn_paged_workspace(..., max_ctx) bytes.  v_gate > 0 applies the
- * Sparse V gate of tq_decode_attn_sparse_v (0: plain attention).
- * Needs head_dim = qjl_dim = 128 for K and V and at most 4 query heads per KV
- * head (else TQ_ERROR_NOT_SUPPORTED), page_size a multiple of 128 and
+ * Sparse V gate of tq_decode_attn_sparse_v (0: plain attention).  Shapes as
+ * tq_decode_attn (head_dim = qjl_dim = 128 with at most 4 query heads per KV
+ * head runs on the matrix cores, other shapes on the general kernel; a V
+ * cache in 32-row blocks needs the former; polar codecs return
+ * TQ_ERROR_NOT_SUPPORTED), page_size a multiple of 128 and
  * 1 <= max_ctx <= max_pages * page_size (else TQ_ERROR_INVALID_VALUE).  Page
  * ids in the used part of the page table must be valid pages of the caches. */
 size_t tq_decode_attn_paged_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch, int32_t n_q_heads,

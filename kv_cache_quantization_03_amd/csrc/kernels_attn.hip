@@ -36,18 +36,30 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 }  // namespace
 
+// Row of position t of (sequence b, KV head kh): [batch][kv_head][ctx] rows
+// for a contiguous cache (pm.table null), else through the page table.
+__device__ __forceinline__ int64_t kv_row(const PageMap& pm, int bk, int nkv, int64_t ctx, int64_t t) {
+  if (!pm.table) return static_cast<int64_t>(bk) * ctx + t;
+  const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + t / pm.page_size];
+  return (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + t % pm.page_size;
+}
+
 // Partials per (bk, chunk, g): [mx, l, M[d], J[m]].  gate > 0 (Sparse V): the
 // value term of (head, key) is dropped when exp(s - mx) < gate · l, l keeps
-// every key, and a key dropped for every head is not read.
+// every key, and a key dropped for every head is not read.  A paged cache
+// (pm.table set): sequence b uses its first min(ctx_lens[b], ctx) positions; a
+// chunk past them writes mx = -inf, l = 0 and zero sums.
 __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
     DevParams PK, DevParams PV, const float* __restrict__ qrot, const float* __restrict__ proj, int Hq, int nkv,
-    int64_t ctx, int CH, tq_packed_t K, tq_packed_t V, float scale, float gate, float* __restrict__ part) {
+    int64_t ctx, int CH, tq_packed_t K, tq_packed_t V, float scale, float gate, PageMap pm,
+    float* __restrict__ part) {
   extern __shared__ float smem[];  // s[G][CH] then red[4]
   const int G = Hq / nkv;
   const int bk = blockIdx.y, chunk = blockIdx.x;
   const int b = bk / nkv, kh = bk % nkv;
   const int64_t t0 = static_cast<int64_t>(chunk) * CH;
-  const int n_in = static_cast<int>(min<int64_t>(CH, ctx - t0));
+  const int64_t ctx_b = pm.table ? max<int64_t>(0, min<int64_t>(pm.ctx_lens[b], ctx)) : ctx;
+  const int n_in = static_cast<int>(max<int64_t>(0, min<int64_t>(CH, ctx_b - t0)));
   float* s = smem;
   float* red = smem + G * CH;
   const int d = PK.d, m = PK.m, W = d / 32;
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
       for (int g = 0; g < G; ++g) s[g * CH + tl] = -INFINITY;
       continue;
     }
-    const int64_t row = static_cast<int64_t>(bk) * ctx + t0 + tl;
+    const int64_t row = kv_row(pm, bk, nkv, ctx, t0 + tl);
     const uint32_t* crow = K.codes + row * PK.code_words;
     const uint32_t* srow = K.signs + row * PK.sign_words;
     const float nu = K.norm[row], ga = K.rnorm[row];
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(kAttnThreads) void decode_split_kernel(
       for (int g = 0; g < G; ++g) any = any || s[g * CH + tl] > 0.f;
       if (!any) continue;
     }
-    const int64_t row = static_cast<int64_t>(bk) * ctx + t0 + tl;
+    const int64_t row = kv_row(pm, bk, nkv, ctx, t0 + tl);
     const float nu = V.norm[row];
     const float scl = is_m ? nu : (per > 0 ? nu * V.rnorm[row] : 0.f);  // an MSE-only V codec has no γ (mv = 0)
     for (int u = 0; u < per; ++u) {
@@ -196,7 +208,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
   // chunk weights and the total weight
   float lt = 0.f;
   for (int c = tid; c < n_chunks; c += kCombThreads) {
-    const float wc = __expf(base[c * cstride] - gm);
+    const float mc = base[c * cstride];
+    const float wc = mc != -INFINITY ? __expf(mc - gm) : 0.f;  // a chunk with no position weighs 0
     wsh[c] = wc;
     lt = fmaf(wc, base[c * cstride + 1], lt);
   }
@@ -236,8 +249,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
     }
   }
   __syncthreads();
-  // o' = (M + κ Sᵀ J)/l: coordinate j over four slices of i
-  const float inv_l = 1.0f / ltot;
+  // o' = (M + κ Sᵀ J)/l: coordinate j over four slices of i (an empty context gives 0)
+  const float inv_l = ltot > 0.f ? 1.0f / ltot : 0.f;
   if (d == 128) {
     const int j = tid & 127, part4 = tid >> 7;  // 8 slices of i
     const int i0 = part4 * (m / 8), i1 = i0 + m / 8;
@@ -494,7 +507,11 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                          decode_prep_region(ck, batch, n_q_heads, n_kv_heads));
   hipError_t e;
-  if (pm || cv->vblock || (decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH)) {
+  // paged caches take the matrix-core kernel where its shape fits (else the
+  // general kernel below, through the page table); a V cache in 32-row blocks
+  // always does (the caller checked its shape)
+  const bool mfma = decode_mfma_eligible(ck, cv, n_q_heads, n_kv_heads) && decode_mfma_chunk() == CH;
+  if (cv->vblock || (pm && decode_paged_supported(ck, cv, n_q_heads, n_kv_heads)) || mfma) {
     // matrix-core split kernel, same partial layout.  The query operands are
     // prepared once per KV head by their own launch (rebuilding them in every
     // block measured 58.7 against 55.5 us at 32 heads x 128K keys).
@@ -508,7 +525,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
     const size_t sh = (static_cast<size_t>(G) * CH + 8) * sizeof(float);
     hipLaunchKernelGGL(decode_split_kernel, dim3(n_chunks, batch * n_kv_heads), dim3(kAttnThreads), sh, s, ck->prm,
                        cv->prm, qrot, proj, n_q_heads, n_kv_heads, ctx, CH, k, v, scale, sparse_v ? v_gate : 0.f,
-                       part);
+                       pm ? *pm : PageMap{nullptr, nullptr, 0, 0}, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (cv->prm.d == 128 && (cv->prm.m == 128 || !cv->qjl)) {

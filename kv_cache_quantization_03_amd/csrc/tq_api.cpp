@@ -418,10 +418,6 @@ extern "C" tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const 
     set_error("need 1 <= max_ctx <= max_pages * page_size");
     return TQ_ERROR_INVALID_VALUE;
   }
-  if (n_kv_heads > 0 && n_q_heads % n_kv_heads == 0 && !tq::decode_paged_supported(ck, cv, n_q_heads, n_kv_heads)) {
-    set_error("paged decode needs head_dim = 128 for K and V, qjl_dim = 128 (or an MSE-only V codec) and at most 4 query heads per KV head");
-    return TQ_ERROR_NOT_SUPPORTED;
-  }
   if (batch > 0 && (!ctx_lens || !page_table)) { set_error("ctx_lens or page_table is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (batch > 0 && (!aligned(ctx_lens, 4) || !aligned(page_table, 4))) {
     set_error("ctx_lens or page_table misaligned");

@@ -619,29 +619,34 @@ def test_append_paged_matches_contiguous_encode(B, vmse):
     say(f"append paged: {written.sum()} rows written, {(~written).sum()} untouched")
 
 
-@pytest.mark.parametrize("kbits,vbits,gate,vmse", [(3, 3, 0.0, False), (4, 2, 0.0, False), (3, 3, 1e-3, False),
-                                                  (3, 3, 0.0, True), (4, 2, 1e-3, True)])
-def test_decode_paged_parity(B, kbits, vbits, gate, vmse):
+@pytest.mark.parametrize("kbits,vbits,gate,vmse,hq,d", [(3, 3, 0.0, False, 8, 128), (4, 2, 0.0, False, 8, 128),
+                                                       (3, 3, 1e-3, False, 8, 128), (3, 3, 0.0, True, 8, 128),
+                                                       (4, 2, 1e-3, True, 8, 128),
+                                                       # the general kernel through the page table: 8 and
+                                                       # 16 query heads per KV head, head_dim 256
+                                                       (3, 3, 0.0, False, 16, 128), (3, 2, 1e-3, True, 32, 128),
+                                                       (3, 3, 0.0, False, 4, 256), (4, 3, 1e-3, False, 8, 256)])
+def test_decode_paged_parity(B, kbits, vbits, gate, vmse, hq, d):
     # four sequences of different lengths (one empty, one of a single token,
     # one filling its page table) in shuffled pages with junk in the rest
-    say(f"paged decode K{kbits} V{vbits}{' mse' if vmse else ''} gate={gate}")
-    gk, ok = pair(B, 128, kbits)
-    gv, ov = vpair(B, 128, vbits, vmse)
-    hq, hkv, P, max_pages = 8, 2, 256, 8
+    say(f"paged decode K{kbits} V{vbits}{' mse' if vmse else ''} gate={gate} hq={hq} d={d}")
+    gk, ok = pair(B, d, kbits)
+    gv, ov = vpair(B, d, vbits, vmse)
+    hkv, P, max_pages = 2, 256, 8
     ctxs = [1500, 1, 0, max_pages * P]
     batch = len(ctxs)
     n_pages = batch * max_pages + 3
-    rng = np.random.default_rng(52 + kbits)
+    rng = np.random.default_rng(52 + kbits + hq + d)
     pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
-    q = as_exact((3.0 if gate else 1.0) * rng.standard_normal((batch, hq, 128)), "f32")
-    krec = [O.encode(ok, rng.standard_normal((hkv * n, 128))) if n else None for n in ctxs]
-    vrec = [O.encode(ov, rng.standard_normal((hkv * n, 128))) if n else None for n in ctxs]
-    junk_k = O.encode(ok, rng.standard_normal((50, 128)))
-    junk_v = O.encode(ov, rng.standard_normal((50, 128)))
+    q = as_exact((3.0 if gate else 1.0) * rng.standard_normal((batch, hq, d)), "f32")
+    krec = [O.encode(ok, rng.standard_normal((hkv * n, d))) if n else None for n in ctxs]
+    vrec = [O.encode(ov, rng.standard_normal((hkv * n, d))) if n else None for n in ctxs]
+    junk_k = O.encode(ok, rng.standard_normal((50, d)))
+    junk_v = O.encode(ov, rng.standard_normal((50, d)))
     empty = lambda R: {k: np.asarray(R[k])[:0] for k in R}
     kc = _fill_pages([r if r is not None else empty(junk_k) for r in krec], pt, hkv, P, n_pages, junk_k)
     vc = _fill_pages([r if r is not None else empty(junk_v) for r in vrec], pt, hkv, P, n_pages, junk_v)
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     out = B.tq_decode_attn_paged(gk, gv, to_dev(q, "f32"), B.packed_from_numpy(kc), B.packed_from_numpy(vc),
                                  torch.tensor(ctxs, dtype=torch.int32, device="cuda"), torch.from_numpy(pt).cuda(), P,
                                  max(ctxs), hkv, scale, gate, out_dtype=torch.float32).cpu().numpy()
@@ -940,8 +945,10 @@ def test_decode_paged_rejects_bad_arguments(B):
         B.tq_decode_attn_paged(gc, gc, q, kp, kp, ctx, pt, 100, 100, 1, 0.1)
     with pytest.raises(B.TQError):      # max_ctx beyond the page table
         B.tq_decode_attn_paged(gc, gc, q, kp, kp, ctx, pt, 128, 257, 1, 0.1)
-    with pytest.raises(B.TQError):      # more than 4 query heads per KV head
-        B.tq_decode_attn_paged(gc, gc, torch.zeros((1, 8, 128), device="cuda"), kp, kp, ctx, pt, 128, 128, 1, 0.1)
+    with pytest.raises(B.TQError):      # V in 32-row blocks with more than 4 query heads per KV head
+        gvb = B.tq_codec_create_vblock(128, 3, False, 1234)
+        B.tq_decode_attn_paged(gc, gvb, torch.zeros((1, 8, 128), device="cuda"), kp, B.alloc_packed(gvb, 1024), ctx,
+                               pt, 128, 128, 1, 0.1)
 
 
 # ---------------------------------------------------------------- PolarQuant first stage
