@@ -70,7 +70,41 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_mfma_kernel(
   // wave index through readfirstlane: every per-wave quantity is then known uniform (scalar registers)
   const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int g = lane >> 4, kl = lane & 15;
-  const int bk = blockIdx.y, chunk = blockIdx.x;
+  int bk = blockIdx.y, chunk = blockIdx.x;
+  if constexpr (PAGED) {
+    // Blocks take the (sequence, KV head, chunk) items that hold positions in
+    // order, so the grid's empty chunks (it is sized by the longest context)
+    // all come last and exit at once instead of sitting between the work.
+    // Every wave derives the same item from ctx_lens (no LDS, no barrier).
+    const int batch = gridDim.y / nkv;
+    const int64_t item = blockIdx.x + static_cast<int64_t>(blockIdx.y) * gridDim.x;
+    int64_t base = 0;
+    bool found = false;
+    for (int b0 = 0; b0 < batch && !found; b0 += 64) {
+      const int b = b0 + lane;
+      const int cb = b < batch ? (max(0, min(pm.ctx_lens[b], ctx_max)) + kDecChunk - 1) / kDecChunk : 0;
+      const int64_t items = static_cast<int64_t>(cb) * nkv;
+      int64_t incl = items;  // inclusive prefix over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      const int64_t total = __shfl(incl, 63, 64);
+      if (item < base + total) {
+        const unsigned long long hit = __ballot(base + incl > item);
+        const int bl = __builtin_ctzll(hit);  // the item's sequence, lane of this round
+        const int64_t excl = base + __shfl(incl - items, bl, 64);
+        const int cbl = __shfl(cb, bl, 64);
+        const int r = static_cast<int>(item - excl);
+        bk = __builtin_amdgcn_readfirstlane((b0 + bl) * nkv + r / cbl);
+        chunk = __builtin_amdgcn_readfirstlane(r % cbl);
+        found = true;
+      }
+      base += total;
+    }
+    if (!found) return;  // past every sequence's positions (block-uniform)
+  }
   const int G = Hq / nkv;
   const int kbase = chunk * kDecChunk + wv * kDecKeysPerWave;  // first key of the wave (within the head)
   const int64_t hrow = static_cast<int64_t>(bk) * ctx_max;     // first row of the head (contiguous cache)
