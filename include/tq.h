@@ -169,8 +169,9 @@ tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uin
  * tq_encode_kv, tq_attn_logits and its split form, and as either codec (ck,
  * cv or both) of tq_decode_attn, tq_decode_attn_no_alloc and
  * tq_decode_attn_sparse_v (深度拆解 第二部分 第三步: the whole KV cache in polar
- * form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)); the paged calls and tq_search_topk
- * return TQ_ERROR_NOT_SUPPORTED for them. */
+ * form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)), and by tq_search_topk (the polar
+ * score against every database record); the paged calls return
+ * TQ_ERROR_NOT_SUPPORTED for them. */
 tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                   tq_codec_t* out);
 /* An MSE-only value codec: the same rotation and per-coordinate Lloyd-Max

@@ -17,6 +17,12 @@ hipError_t launch_search_mfma_prep(const tq_codec_s* c, const float* qrot, const
                                    hipStream_t s);
 hipError_t launch_search_mfma_scores(const tq_codec_s* c, const void* prep, int nq, tq_packed_t db, int64_t n,
                                      float* scores, int64_t ld, hipStream_t s);
+hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+
+// A polar codec's scores come from the polar scorer (the queries as the query
+// heads of one KV head); the matrix-core search scorer reads per-coordinate codes.
+static bool search_use_mfma(const tq_codec_s* c) { return !c->polar && search_mfma_eligible(c); }
 
 namespace {
 constexpr int64_t kSearchChunk = 65536;
@@ -352,7 +358,7 @@ SearchLayout search_layout(const tq_codec_s* c, int64_t n_db, int nq, int topk) 
   L.qrot = 0;
   L.proj = align256(L.qrot + static_cast<size_t>(nq) * c->prm.d * sizeof(float));
   L.prep = align256(L.proj + static_cast<size_t>(nq) * c->prm.m * sizeof(float));
-  L.scores = L.prep + (search_mfma_eligible(c) ? search_mfma_prep_bytes(c, nq) : 0);
+  L.scores = L.prep + (search_use_mfma(c) ? search_mfma_prep_bytes(c, nq) : 0);
   L.cand_idx = align256(L.scores + static_cast<size_t>(nq) * chunk * sizeof(float));
   L.cand_score = align256(L.cand_idx + static_cast<size_t>(nq) * n_chunks * topk * sizeof(int64_t));
   L.total = align256(L.cand_score + static_cast<size_t>(nq) * n_chunks * topk * sizeof(float));
@@ -376,7 +382,7 @@ hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, cons
   float* scores = reinterpret_cast<float*>(w + SL.scores);
   int64_t* cand_idx = reinterpret_cast<int64_t*>(w + SL.cand_idx);
   float* cand_score = reinterpret_cast<float*>(w + SL.cand_score);
-  const bool mfma = search_mfma_eligible(c);
+  const bool mfma = search_use_mfma(c);
   hipError_t e = launch_qprep(c, queries, TQ_F32, nq, qrot, proj, s);
   if (e != hipSuccess) return e;
   if (mfma && (e = launch_search_mfma_prep(c, qrot, proj, nq, w + SL.prep, s)) != hipSuccess) return e;
@@ -384,8 +390,10 @@ hipError_t launch_search(const tq_codec_s* c, tq_packed_t db, int64_t n_db, cons
     const int64_t lo = ci * chunk;
     const int64_t len = std::min<int64_t>(chunk, n_db - lo);
     tq_packed_t sub{db.codes + lo * P.code_words, db.signs + lo * P.sign_words, db.norm + lo, db.rnorm + lo};
-    e = mfma ? launch_search_mfma_scores(c, w + SL.prep, nq, sub, len, scores, len, s)
-             : launch_scores(c, qrot, proj, nq, sub, len, scores, s);
+    // (qrot and proj are contiguous: nq·d floats is a multiple of 256 bytes)
+    e = c->polar ? launch_logits_polar(c, qrot, 1, nq, 1, 1, sub, len, scores, s)
+        : mfma   ? launch_search_mfma_scores(c, w + SL.prep, nq, sub, len, scores, len, s)
+                 : launch_scores(c, qrot, proj, nq, sub, len, scores, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_regs_kernel, dim3(nq), dim3(kTopThreads), 0, s, scores, len, lo, topk,
                        cand_score + ci * topk, cand_idx + ci * topk, static_cast<int64_t>(n_chunks * topk));

@@ -495,7 +495,6 @@ extern "C" tq_status_t tq_search_topk(tq_codec_t c, tq_packed_t db, int64_t n_db
   if (st != TQ_SUCCESS) return st;
   if (!vec_aligned(queries)) { set_error("queries must be 16-byte aligned"); return TQ_ERROR_MISALIGNED; }
   if (!c) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
-  if (c->polar) { set_error("search takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
   if (!c->qjl) return need_qjl(c, "tq_search_topk");
   if ((st = need_rows(c, "tq_search_topk")) != TQ_SUCCESS) return st;
   if (n_db < 1 || n_queries < 0) { set_error("need n_db >= 1 and n_queries >= 0"); return TQ_ERROR_INVALID_VALUE; }

@@ -1051,9 +1051,11 @@ def test_polar_codec_limits(B):
     gc, _ = polar_pair(B, 3)
     with pytest.raises(B.TQError):
         B.tq_codec_create_polar(256, 3)
-    kp = B.alloc_packed(gc, 64)
-    with pytest.raises(B.TQError):
-        B.tq_search_topk(gc, kp, torch.zeros((1, 128), device="cuda"), 5)
+    kp = B.alloc_packed(gc, 256)
+    with pytest.raises(B.TQError):  # paged logits read per-coordinate codes only
+        B.tq_attn_logits_paged(gc, torch.zeros((1, 1, 4, 128), device="cuda"), kp,
+                               torch.tensor([100], dtype=torch.int32, device="cuda"),
+                               torch.zeros((1, 2), dtype=torch.int32, device="cuda"), 128, 256, 1)
 
 
 # ---------------------------------------------------------------- search

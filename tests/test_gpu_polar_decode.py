@@ -1,6 +1,7 @@
 """GPU parity of decode attention when either codec takes the recursive polar
 first stage (「谷歌 TurboQuant 深度拆解」 第二部分 第三步: the whole KV cache in
-polar form), against the oracle's decode attention over the same records.
+polar form), against the oracle's decode attention over the same records, and
+of exhaustive search over a polar-compressed database.
 Every call goes through the C ABI (ctypes binding over libtq.so)."""
 import math
 import sys
@@ -202,3 +203,35 @@ def test_polar_decode_refusals(B):
     gvb = B.tq_codec_create_vblock(128, 3, False, 1234)
     with pytest.raises(B.TQError):
         B.tq_decode_attn(gk, gvb, q, kp, B.alloc_packed(gvb, 256), 256, 1, 0.1)
+
+
+@pytest.mark.parametrize("bits,n_db,nq,k", [(3, 70001, 9, 10), (4, 3000, 4, 100), (2, 1500, 1, 1)])
+def test_polar_search_parity(B, bits, n_db, nq, k):
+    # exhaustive search over a polar-compressed database (深度拆解 第三部分 向量搜索):
+    # the returned top-k against the oracle's polar scores of every record;
+    # duplicated records tie and go to the lower index
+    say(f"polar search bits={bits} n_db={n_db} nq={nq} k={k}")
+    gc, pc = codec(B, "polar", bits, 1234)
+    rng = np.random.default_rng(n_db + bits)
+    db = rng.standard_normal((n_db, 128))
+    db /= np.linalg.norm(db, axis=1, keepdims=True)
+    rec = encode(pc, db)
+    for key in ("codes", "signs", "norm", "rnorm"):
+        rec[key] = np.asarray(rec[key]).copy()
+        rec[key][10] = rec[key][4]
+        rec[key][n_db - 1] = rec[key][4]
+    qs = rng.standard_normal((nq, 128)).astype(np.float32)
+    qs[0] = (db[4] * 3).astype(np.float32)
+    idx, sc = B.tq_search_topk(gc, B.packed_from_numpy(rec), torch.from_numpy(qs).cuda(), k)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    ridx, rsc, full = O.search_topk(pc, rec, qs.astype(np.float64), k)
+    for qi in range(nq):
+        scale = np.max(np.abs(full[qi]))
+        assert len(set(idx[qi].tolist())) == k
+        assert np.all(full[qi, idx[qi]] >= rsc[qi, -1] - 1e-4 * scale)
+        assert np.allclose(sc[qi], full[qi, idx[qi]], rtol=0, atol=1e-4 * scale)
+        assert np.all(np.diff(sc[qi]) <= 0)
+    if k >= 3:
+        row = list(idx[0])
+        assert row.index(4) < row.index(10) < row.index(n_db - 1)
