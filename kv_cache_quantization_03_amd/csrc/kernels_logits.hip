@@ -219,25 +219,36 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
   float prod[9];  // prod[lv]: product of the factors of levels 7..lv along the current path
   prod[8] = 1.f;
   if constexpr (L2T) {
+    // Level-4 node m at a time (level-2 nodes 4m..4m+3): its factors of levels
+    // 7..3 (slots 126, 124 + m/4, 120 + m/2, 112 + m, 96 + 2m + s) and its four
+    // level-2 brackets are read together, one LDS round trip per group of
+    // four nodes; the products keep the top-down order.
+    const float2 f7 = tab[6][code(126)];
 #pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      // levels whose factor changes at level-2 node n: lv <= ctz(n) + 3 (all at n = 0)
-      const int hi = n == 0 ? 7 : (__builtin_ctz(n) + 3 < 7 ? __builtin_ctz(n) + 3 : 7);
+    for (int m = 0; m < 8; ++m) {
+      const float2 f6 = tab[5][code(124 + (m >> 2))];
+      const float2 f5 = tab[4][code(120 + (m >> 1))];
+      const float2 f4 = tab[3][code(112 + m)];
+      const float2 f3a = tab[2][code(96 + 2 * m)], f3b = tab[2][code(97 + 2 * m)];
+      float4 bq[4];
 #pragma unroll
-      for (int lv = 7; lv >= 3; --lv) {
-        if (lv > hi) continue;
-        const int node = n >> (lv - 2), side = (n >> (lv - 3)) & 1;
-        const float2 cs = tab[lv - 1][code(128 - (256 >> lv) + node)];
-        prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
+      for (int i = 0; i < 4; ++i) {
+        const int n = 4 * m + i;
+        int r = code(64 + n) << (2 * B);
+#pragma unroll
+        for (int p = 0; p < B; ++p) r |= static_cast<int>((w[p][n >> 4] >> (2 * (n & 15))) & 3u) << (2 * p);
+        bq[i] = q2tab[n][r];
       }
-      int r = code(64 + n) << (2 * B);
+      const float p5 = (((m >> 2) ? f7.y : f7.x) * (((m >> 1) & 1) ? f6.y : f6.x)) * ((m & 1) ? f5.y : f5.x);
+      const float p4a = p5 * f4.x, p4b = p5 * f4.y;
+      const float p3[4] = {p4a * f3a.x, p4a * f3a.y, p4b * f3b.x, p4b * f3b.y};
 #pragma unroll
-      for (int p = 0; p < B; ++p) r |= static_cast<int>((w[p][n >> 4] >> (2 * (n & 15))) & 3u) << (2 * p);
-      const float4 b = q2tab[n][r];
-      mse[0] = fmaf(prod[3], b.x, mse[0]);
-      mse[1] = fmaf(prod[3], b.y, mse[1]);
-      mse[2] = fmaf(prod[3], b.z, mse[2]);
-      mse[3] = fmaf(prod[3], b.w, mse[3]);
+      for (int i = 0; i < 4; ++i) {
+        mse[0] = fmaf(p3[i], bq[i].x, mse[0]);
+        mse[1] = fmaf(p3[i], bq[i].y, mse[1]);
+        mse[2] = fmaf(p3[i], bq[i].z, mse[2]);
+        mse[3] = fmaf(p3[i], bq[i].w, mse[3]);
+      }
 #pragma unroll
       for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(mse[t]));
       __builtin_amdgcn_sched_barrier(0);
