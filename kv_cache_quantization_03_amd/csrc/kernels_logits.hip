@@ -324,7 +324,7 @@ bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_
                            int64_t ctx);
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
-                               hipStream_t s);
+                               hipStream_t s, const PageMap* pm = nullptr);
 
 size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
   if (!c->polar && logits_mfma_eligible(c)) return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
@@ -390,6 +390,9 @@ size_t logits_paged_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int 
 hipError_t launch_logits_paged(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                int n_kv_heads, int n_queries, tq_packed_t k, int64_t max_ctx, const PageMap& pm,
                                float* logits, void* ws, hipStream_t s) {
+  // one launch where the fused kernel takes the shape (its records through the page table)
+  if (logits_fused_eligible(c, batch, n_q_heads, n_kv_heads, n_queries, max_ctx))
+    return launch_logits_fused(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, k, max_ctx, logits, s, &pm);
   hipError_t e = launch_logits_mfma_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
   if (e != hipSuccess) return e;
   return launch_logits_mfma(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, max_ctx, logits, s, &pm);

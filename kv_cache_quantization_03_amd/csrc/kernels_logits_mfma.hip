@@ -398,11 +398,16 @@ __global__ __launch_bounds__(WAVES * 64) void logits_mfma_kernel(const uint8_t* 
 // lines) instead of four 64-byte pieces.  vec_out = 0 (ctx not a multiple of
 // 4, or logits not 16-byte aligned) keeps the scalar stores.
 // ----------------------------------------------------------------------------
-template <int NP, int WAVES, typename T, bool LOOP>
+// PAGED: the records of sequence b's position t sit at row
+// (page_table[b][t / page_size] * nkv + kh) * page_size + t % page_size, and b
+// scores its first min(ctx_lens[b], ctx) positions (ctx = max_ctx, the logits
+// row length); page_size is a multiple of 128, so a 64-key group lies in one
+// page.  A block past its sequence's end exits before any barrier.
+template <int NP, int WAVES, typename T, bool LOOP, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
     const T* q, DevParams P, const float* Dsign, const float* Mt, int Hq, int nq, int G, int nkv, int ctx,
     const uint32_t* __restrict__ codes, const uint32_t* __restrict__ signs, const float* __restrict__ norm,
-    const float* __restrict__ rnorm, float* __restrict__ logits, int vec_out, int ngw) {
+    const float* __restrict__ rnorm, float* __restrict__ logits, int vec_out, int ngw, PageMap pm) {
   using L = RecLayout<NP, 1>;
   constexpr int NT = WAVES * 64, NKB = L::NKB;
   __shared__ uint32_t s_codes[WAVES][kKeysPerWave * L::CS];
@@ -414,9 +419,14 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   // The block's keys: ngw rounds of WAVES consecutive 64-key groups, wave wv
   // taking group wv of each round (every round reads one contiguous range).
   const int blk0 = blockIdx.x * ngw * (WAVES * kKeysPerWave);
+  int ctx_v = ctx;  // keys this row scores
+  if constexpr (PAGED) {
+    ctx_v = max(0, min(pm.ctx_lens[bk / nkv], ctx));
+    if (blk0 >= ctx_v) return;  // block-uniform, before any barrier
+  }
   auto group_key = [&](int i) { return blk0 + (i * WAVES + wv) * kKeysPerWave; };
   const int key0 = group_key(0);
-  const bool active = key0 < ctx;  // wave-uniform; idle waves still help with the operands
+  const bool active = key0 < ctx_v;  // wave-uniform; idle waves still help with the operands
 
   // The vector memory path returns data in request order, so an operand load
   // queued behind record loads (HBM misses) would wait for them: every wave's
@@ -431,10 +441,15 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   v4u cvA[L::CW / 4], svA[L::SW / 4], cvB[L::CW / 4], svB[L::SW / 4];
   float nuA, gaA, nuB, gaB;
   auto load = [&](int k0, v4u (&cv)[L::CW / 4], v4u (&sv)[L::SW / 4], float& nu, float& ga) {
-    const bool ok = k0 < ctx;
-    const int64_t row0 = static_cast<int64_t>(bk) * ctx + (ok ? k0 : ctx - 1);
+    const bool ok = k0 < ctx_v;
+    const int key = ok ? k0 : ctx_v - 1;  // ctx_v >= 1 here (the block holds a key)
+    int64_t row0 = static_cast<int64_t>(bk) * ctx + key;
+    if constexpr (PAGED) {
+      const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + key / pm.page_size];
+      row0 = (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + key % pm.page_size;
+    }
     load_wave_records<NP, 1>(cv, sv, nu, ga, codes + row0 * L::CW, signs + row0 * L::SW, norm + row0, rnorm + row0,
-                             ok ? min(kKeysPerWave, ctx - k0) : 1, lane);
+                             ok ? min(kKeysPerWave, ctx_v - k0) : 1, lane);
   };
   load(key0, cvA, svA, nuA, gaA);
   query_prep_build<NT, NP, NKB>(sh, pr, P, tile);
@@ -455,9 +470,9 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   auto step = [&](int i, v4u (&cv)[L::CW / 4], v4u (&sv)[L::SW / 4], float& nu, float& ga, v4u (&cvn)[L::CW / 4],
                   v4u (&svn)[L::SW / 4], float& nun, float& gan, bool prefetch) {
     const int k0 = group_key(i);
-    const bool more = i + 1 < ngw && group_key(i + 1) < ctx;
+    const bool more = i + 1 < ngw && group_key(i + 1) < ctx_v;
     if (prefetch && more) load(group_key(i + 1), cvn, svn, nun, gan);
-    const int nvalid = min(kKeysPerWave, ctx - k0);
+    const int nvalid = min(kKeysPerWave, ctx_v - k0);
     float val[kKeysPerWave / kKeysPerTile];
     score_wave_values<NP, 1>(cv, sv, nu, ga, s_codes[wv], s_signs[wv], a, cst, P.qjl_kappa, lane, val);
     if (!prefetch && more) load(group_key(i + 1), cvn, svn, nun, gan);
@@ -487,9 +502,9 @@ __global__ __launch_bounds__(WAVES * 64) void logits_fused_kernel(
   };
   if constexpr (LOOP) {
     for (int i = 0; i < ngw; i += 2) {
-      if (group_key(i) >= ctx) break;  // wave-uniform
+      if (group_key(i) >= ctx_v) break;  // wave-uniform
       step(i, cvA, svA, nuA, gaA, cvB, svB, nuB, gaB, true);
-      if (i + 1 >= ngw || group_key(i + 1) >= ctx) break;
+      if (i + 1 >= ngw || group_key(i + 1) >= ctx_v) break;
       step(i + 1, cvB, svB, nuB, gaB, cvA, svA, nuA, gaA, true);
     }
   } else {  // one round (ngw = 1)
@@ -632,7 +647,7 @@ bool logits_fused_eligible(const tq_codec_s* c, int batch, int n_q_heads, int n_
 
 hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits,
-                               hipStream_t s) {
+                               hipStream_t s, const PageMap* pm) {
   // 16 waves (1024 keys) per block: one block per CU at the decode shapes, so
   // the operand rebuild is paid once per CU rather than twice (measured 8.7 us
   // against 9.2 us for 8-wave blocks at 32 query heads x 32K keys).
@@ -645,12 +660,17 @@ hipError_t launch_logits_fused(const tq_codec_s* c, const void* q, tq_dtype_t dt
                     batch * n_kv_heads, 1);
     // several rounds: the double-buffered loop (not for 72-byte records: their
     // second buffer does not fit 128 registers, and the split form takes them)
-    auto kern = logits_fused_kernel<NP, WAVES, T, false>;
-    if constexpr (NP < 4) {
-      if (ngw > 1) kern = logits_fused_kernel<NP, WAVES, T, true>;
-    }
+    auto pick = [&]<bool PG>() {
+      auto kern = logits_fused_kernel<NP, WAVES, T, false, PG>;
+      if constexpr (NP < 4) {
+        if (ngw > 1) kern = logits_fused_kernel<NP, WAVES, T, true, PG>;
+      }
+      return kern;
+    };
+    auto kern = pm ? pick.template operator()<true>() : pick.template operator()<false>();
     hipLaunchKernelGGL(kern, grid, dim3(WAVES * 64), 0, s, qq, c->prm, c->dD, c->dMt, n_q_heads, n_queries, G,
-                       n_kv_heads, static_cast<int>(ctx), k.codes, k.signs, k.norm, k.rnorm, logits, vec_out, ngw);
+                       n_kv_heads, static_cast<int>(ctx), k.codes, k.signs, k.norm, k.rnorm, logits, vec_out, ngw,
+                       pm ? *pm : PageMap{nullptr, nullptr, 0, 0});
     return hipGetLastError();
   };
   auto by_np = [&]<typename T>(const T* qq) -> hipError_t {

@@ -839,13 +839,18 @@ def _gather_rows(B, pool, rows):
                     pool.norm.index_select(0, idx).contiguous(), pool.rnorm.index_select(0, idx).contiguous())
 
 
-def test_logits_paged_four_groups_per_wave(B):
-    # a grid of at least two blocks per compute unit takes the instance whose
-    # waves score four 64-key groups each (a page lookup per group, records of
-    # the next group prefetched across a page boundary at page_size 128); the
-    # contexts end inside a wave's 256-key span.  Logits equal the contiguous
-    # call's bit for bit on each sequence's positions and match the oracle on
-    # sampled heads; positions past a sequence's end stay untouched.
+@pytest.mark.parametrize("split", [False, True])
+def test_logits_paged_four_groups_per_wave(B, split, monkeypatch):
+    # a grid of at least two blocks per compute unit: the one-launch fused
+    # kernel streams four rounds of 64-key groups per wave, and the split form
+    # (TQ_LOGITS_FUSED=0) takes the instance whose waves score four groups
+    # each; both look up a page per group and prefetch the next group's
+    # records across a page boundary at page_size 128; the contexts end inside
+    # a wave's 256-key span.  Logits equal the contiguous call's (same form)
+    # bit for bit on each sequence's positions and match the oracle on sampled
+    # heads; positions past a sequence's end stay untouched.
+    if split:
+        monkeypatch.setenv("TQ_LOGITS_FUSED", "0")
     gc, oc = pair(B, 128, 3)
     batch, hq, hkv, P, max_pages = 4, 32, 8, 128, 256
     max_ctx = P * max_pages                                  # 32768
