@@ -8,7 +8,11 @@ benchmark times, on sampled outputs the oracle computes one by one.
   encode parity on sampled K and V rows, the 16 queries' logits on sampled keys.
 * long-context fused decode attention (128K tokens): two KV heads' outputs
   (eight query heads) against the oracle over all 131072 keys of those heads;
-  the same with the Sparse V gate on the needle variant of that workload.
+  the same with the Sparse V gate on the needle variant of that workload; with
+  V in 32-row blocks (bit-equal to the row layout); with polar K and V (two
+  KV heads against the oracle); the paged step of 8 sequences 1K..128K (each
+  bit-equal to the contiguous decode of its gathered records, two against the
+  oracle).
 * vector search (1e6 x 1536, 4-bit, top-10): sampled encode parity; for two
   queries, the returned top-10 against the oracle's scores of every database
   record (the GPU-encoded records, whose codes were checked on a sample).
@@ -22,7 +26,7 @@ import pytest
 import oracle as O
 from kv_cache_quantization_03_amd import inputs as I
 from tests.parity import (assert_sparse_v_close, assert_sparse_v_within_plain_rule, check_encode,
-                          oracle_records_like, row_rel_err)
+                          oracle_records_like, polar_records_like, row_rel_err)
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -203,6 +207,114 @@ def test_full_long_decode_sparse_v(B):
                                                          w["scale"], gate)
         assert np.all(keep | ~keep_p)
         assert_sparse_v_within_plain_rule(g32[:, hs], plain, wf, gate, vhat, 1, ctx, 1e-3)
+
+
+def test_full_long_decode_vblock(B):
+    # the long-context step with the value cache in 32-row blocks, as the
+    # benchmark times it: every output equals the row-record decode's bit for
+    # bit (the same records, another storage order)
+    w = I.long_decode()
+    say("decode attention, 128K context, V in 32-row blocks")
+    d, hq, hkv, ctx = 128, 32, 8, 131072
+    gc = B.tq_codec_create(d, 3, 0, I.CODEC_SEED)
+    gvb = B.tq_codec_create_vblock(d, 3, False, I.CODEC_SEED)
+    k = dev_tensor(w["keys"].rows(), "bf16")
+    v = dev_tensor(w["values"].rows(), "bf16")
+    kp, vp = B.tq_encode_kv(gc, k, v)
+    vb = B.tq_encode_kv(gvb, v)[0]
+    q = dev_tensor(w["queries"].rows().reshape(1, hq, d), "bf16")
+    a = B.tq_decode_attn(gc, gc, q, kp, vp, ctx, hkv, w["scale"], out_dtype=torch.float32)
+    b = B.tq_decode_attn(gc, gvb, q, kp, vb, ctx, hkv, w["scale"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    say(f"  bitwise equal to row V: {torch.equal(a, b)}")
+    assert torch.equal(a, b)
+
+
+def test_full_long_decode_polar(B):
+    # the long-context step with polar K and V (the benchmark's polar stage):
+    # two KV heads' outputs against the oracle over all 131072 positions, on
+    # records conditioned on the GPU's legitimate boundary choices
+    w = I.long_decode()
+    say("decode attention, 128K context, polar K and V 3-bit")
+    d, hq, hkv, ctx = 128, 32, 8, 131072
+    G = hq // hkv
+    gc = B.tq_codec_create_polar(d, 3, 0, I.CODEC_SEED)
+    pc = O.make_polar_codec(d, 3, seed=I.CODEC_SEED)
+    k = w["keys"].rows()
+    v = w["values"].rows()
+    kp, vp = B.tq_encode_kv(gc, dev_tensor(k, "bf16"), dev_tensor(v, "bf16"))
+    q = w["queries"].rows().reshape(1, hq, d)
+    out32 = B.tq_decode_attn(gc, gc, dev_tensor(q, "bf16"), kp, vp, ctx, hkv, w["scale"], out_dtype=torch.float32)
+    out16 = B.tq_decode_attn(gc, gc, dev_tensor(q, "bf16"), kp, vp, ctx, hkv, w["scale"], out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = out32.cpu().numpy()
+    assert np.array_equal(out16.float().cpu().numpy(), O.bf16_round(g32))
+    gk, gvv = kp.numpy(), vp.numpy()
+    for kh in (0, hkv - 1):
+        rows = slice(kh * ctx, (kh + 1) * ctx)
+        kr = polar_records_like(pc, k[rows].astype(np.float64), {kk: x[rows] for kk, x in gk.items()})
+        vr = polar_records_like(pc, v[rows].astype(np.float64), {kk: x[rows] for kk, x in gvv.items()})
+        hs = slice(kh * G, (kh + 1) * G)
+        ref = O.decode_attn_accumulated(pc, pc, q[:, hs].astype(np.float64), kr, vr, 1, G, 1, ctx, w["scale"])
+        err = row_rel_err(g32[:, hs], ref).max()
+        say(f"  kv head {kh}: max row err {err:.2e}")
+        assert err <= 1e-3
+
+
+def test_full_paged_eight_sequences(B):
+    # the benchmark's paged step: 8 sequences of 128K, 64K, ..., 1K positions in
+    # one pool of shuffled 256-position pages (random records), one grid sized
+    # by the longest; every sequence's output equals the contiguous decode of
+    # its gathered records bit for bit, and two sequences match the oracle on
+    # one KV head
+    d, hq, hkv, P, ctx = 128, 32, 8, 256, 131072
+    G = hq // hkv
+    lens = [ctx >> i for i in range(8)]
+    say(f"paged decode, 8 sequences {lens}")
+    gc = B.tq_codec_create(d, 3, 0, I.CODEC_SEED)
+    oc = O.make_codec(d, 3, seed=I.CODEC_SEED)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(81)
+    n_pages = sum(n // P for n in lens)
+    pools = []
+    for _ in range(2):
+        pool = B.alloc_packed(gc, n_pages * hkv * P)
+        for t in (pool.codes, pool.signs):
+            t.copy_(torch.randint(-2 ** 31, 2 ** 31 - 1, t.shape, generator=g, device="cuda", dtype=torch.int32))
+        pool.norm.copy_(torch.rand(pool.norm.shape, generator=g, device="cuda") + 0.5)
+        pool.rnorm.copy_(torch.rand(pool.rnorm.shape, generator=g, device="cuda") * 0.3)
+        pools.append(pool)
+    order = np.random.default_rng(82).permutation(n_pages).astype(np.int32)
+    pt = np.zeros((len(lens), ctx // P), dtype=np.int32)
+    o = 0
+    for b, n in enumerate(lens):
+        pt[b, :n // P] = order[o:o + n // P]
+        o += n // P
+    q = dev_tensor(np.random.default_rng(83).standard_normal((len(lens), hq, d)), "bf16")
+    scale = 1 / math.sqrt(d)
+    out = B.tq_decode_attn_paged(gc, gc, q, pools[0], pools[1], torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                 torch.from_numpy(pt).cuda(), P, ctx, hkv, scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        t = np.arange(n)
+        page = pt[b][t // P].astype(np.int64)
+        rows = torch.from_numpy(np.concatenate([(page * hkv + kh) * P + t % P for kh in range(hkv)])).cuda()
+        kv = [B.Packed(pl.codes.index_select(0, rows).contiguous(), pl.signs.index_select(0, rows).contiguous(),
+                       pl.norm.index_select(0, rows).contiguous(), pl.rnorm.index_select(0, rows).contiguous())
+              for pl in pools]
+        ref = B.tq_decode_attn(gc, gc, q[b:b + 1].contiguous(), kv[0], kv[1], n, hkv, scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(out[b:b + 1], ref), b
+        if b in (0, 7):  # the longest and the shortest against the oracle, KV head 3
+            kh = 3
+            hk = {k_: x[kh * n:(kh + 1) * n] for k_, x in kv[0].numpy().items()}
+            hv = {k_: x[kh * n:(kh + 1) * n] for k_, x in kv[1].numpy().items()}
+            hs = slice(kh * G, (kh + 1) * G)
+            oref = O.decode_attn_accumulated(oc, oc, q[b:b + 1, hs].float().cpu().numpy().astype(np.float64), hk, hv,
+                                             1, G, 1, n, scale)
+            err = row_rel_err(out[b:b + 1, hs].cpu().numpy(), oref).max()
+            say(f"  sequence {b} (ctx {n}) kv head {kh}: max row err {err:.2e}")
+            assert err <= 1e-3
 
 
 def test_full_vector_search(B):
