@@ -165,13 +165,13 @@ tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uin
  * unused (0); ŷ is rebuilt from radius 1 with cos and sin of the centroids
  * (fp32), and the residual y - ŷ takes the same QJL stage, so the record size
  * and the score ν(⟨q', ŷ⟩ + √(π/2)/m γ ⟨p, τ⟩) keep their form.
- * head_dim 128 only; bits 2, 3 or 4.  Such codecs are accepted by
- * tq_encode_kv, tq_attn_logits and its split form, and as either codec (ck,
- * cv or both) of tq_decode_attn, tq_decode_attn_no_alloc and
- * tq_decode_attn_sparse_v (深度拆解 第二部分 第三步: the whole KV cache in polar
- * form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)), and by tq_search_topk (the polar
- * score against every database record); the paged calls return
- * TQ_ERROR_NOT_SUPPORTED for them. */
+ * head_dim 64, 128 or 256 (log2 head_dim levels); bits 2, 3 or 4.  Such
+ * codecs are accepted by tq_encode_kv, tq_attn_logits and its split form, by
+ * tq_search_topk (the polar score against every database record), and, at
+ * head_dim 128 or 256, as either codec (ck, cv or both) of tq_decode_attn,
+ * tq_decode_attn_no_alloc and tq_decode_attn_sparse_v (深度拆解 第二部分 第三步:
+ * the whole KV cache in polar form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)); the
+ * paged calls return TQ_ERROR_NOT_SUPPORTED for them. */
 tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                   tq_codec_t* out);
 /* An MSE-only value codec: the same rotation and per-coordinate Lloyd-Max
@@ -212,10 +212,11 @@ tq_status_t tq_codec_create_mse(int32_t head_dim, int32_t bits, uint64_t seed, t
  * bits and seed (the codec tables are the same), bit for bit. */
 tq_status_t tq_codec_create_vblock(int32_t head_dim, int32_t bits, int32_t mse_only, uint64_t seed,
                                    tq_codec_t* out);
-/* Host only (no GPU needed): level l's (1..7) angle codebook of the polar
- * stage for head_dim 128 and the given bits: centroids[2^b] and
- * bounds[2^b - 1], fp64, ascending, and the Lloyd-Max iterations (0 for the
- * uniform level 1).  Any output pointer may be NULL. */
+/* Host only (no GPU needed): level l's (1..log2 head_dim) angle codebook of
+ * the polar stage for head_dim 64, 128 or 256 and the given bits:
+ * centroids[2^b] and bounds[2^b - 1], fp64, ascending, and the Lloyd-Max
+ * iterations (0 for the uniform level 1).  Level l's law depends on l only,
+ * not on head_dim.  Any output pointer may be NULL. */
 tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
                                double* bounds, int32_t* iterations);
 /* The caller guarantees that no work using c is still in flight. */
@@ -286,8 +287,8 @@ tq_status_t tq_attn_logits_prepped(tq_codec_t c, const void* prep, size_t prep_b
  *            differ; head_dim must match).  cv may be an MSE-only codec
  *            (tq_codec_create_mse): then v̂ = ν Rᵀ c[idx] and v.signs,
  *            v.rnorm are not read.  Either may be a polar codec
- *            (tq_codec_create_polar; then both have head_dim 128 and cv is
- *            not a codec in 32-row blocks): the logits then come from the
+ *            (tq_codec_create_polar; then both have head_dim 128 or 256 and
+ *            cv is not a codec in 32-row blocks): the logits then come from the
  *            key codec's scorer and are held in the workspace, and a polar
  *            value's ŷ is rebuilt per position from its angle codes.
  *   q      : device [batch][n_q_heads][d], dtype q_dt.

@@ -204,15 +204,15 @@ int polar_lloyd_max(int level, int b, std::vector<double>* cent, std::vector<dou
 }  // namespace
 
 tq_status_t build_polar_tables(int d, int bits, int m, uint64_t seed, HostTables* out) {
-  if (d != 128) {
-    set_error("the recursive polar stage is built for head_dim 128");
+  if (d != 64 && d != 128 && d != 256) {
+    set_error("the recursive polar stage is built for head_dim 64, 128 or 256");
     return TQ_ERROR_NOT_SUPPORTED;
   }
   tq_status_t st = build_host_tables(d, bits, m, seed, out);
   if (st != TQ_SUCCESS) return st;
   try {
     out->polar = true;
-    const int levels = 7;
+    const int levels = d == 64 ? 6 : d == 128 ? 7 : 8;  // log2 d
     out->pcent.resize(levels);
     out->pbound.resize(levels);
     out->piters.resize(levels);
@@ -533,12 +533,13 @@ extern "C" tq_status_t tq_codec_create_vblock(int32_t head_dim, int32_t bits, in
 extern "C" tq_status_t tq_polar_book_host(int32_t head_dim, int32_t bits, int32_t level, double* centroids,
                                           double* bounds, int32_t* iterations) {
   tq::clear_error();
-  if (head_dim != 128 || bits < 2 || bits > 4) {
-    set_error("the recursive polar stage is built for head_dim 128 and bits 2, 3 or 4");
+  if ((head_dim != 64 && head_dim != 128 && head_dim != 256) || bits < 2 || bits > 4) {
+    set_error("the recursive polar stage is built for head_dim 64, 128 or 256 and bits 2, 3 or 4");
     return TQ_ERROR_NOT_SUPPORTED;
   }
-  if (level < 1 || level > 7) {
-    set_error("level must be in 1..7 for head_dim 128");
+  const int levels = head_dim == 64 ? 6 : head_dim == 128 ? 7 : 8;
+  if (level < 1 || level > levels) {
+    set_error("level must be in 1..log2(head_dim)");
     return TQ_ERROR_INVALID_VALUE;
   }
   std::vector<double> c, t;

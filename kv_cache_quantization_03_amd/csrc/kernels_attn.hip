@@ -425,16 +425,24 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
   }
 }
 
-// The d = m = 128 combine over contiguous chunk partials (M only for an
-// MSE-only value codec).
-hipError_t launch_decode_combine128(const tq_codec_s* cv, const float* part, int batch, int n_q_heads,
-                                    int n_kv_heads, int n_chunks, int chunk, void* out, tq_dtype_t out_dt,
-                                    hipStream_t s) {
-  auto kern = cv->qjl ? decode_combine128_kernel<true> : decode_combine128_kernel<false>;
-  hipLaunchKernelGGL(kern, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part, n_q_heads, n_kv_heads,
-                     n_chunks, static_cast<const int32_t*>(nullptr), chunk, cv->dS, cv->dD, out,
-                     out_dt == TQ_BF16 ? 1 : 0);
-  return hipGetLastError();
+// The combine over contiguous chunk partials [mx, l, M[d], J[m]] (J absent
+// for an MSE-only value codec): the d = m = 128 kernel, else the general one.
+hipError_t launch_decode_combine_contig(const tq_codec_s* cv, const float* part, int batch, int n_q_heads,
+                                        int n_kv_heads, int n_chunks, int chunk, void* out, tq_dtype_t out_dt,
+                                        hipStream_t s) {
+  if (cv->prm.d == 128 && (cv->prm.m == 128 || !cv->qjl)) {
+    auto kern = cv->qjl ? decode_combine128_kernel<true> : decode_combine128_kernel<false>;
+    hipLaunchKernelGGL(kern, dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm, part, n_q_heads,
+                       n_kv_heads, n_chunks, static_cast<const int32_t*>(nullptr), chunk, cv->dS, cv->dD, out,
+                       out_dt == TQ_BF16 ? 1 : 0);
+    return hipGetLastError();
+  }
+  auto run = [&]<int E>() -> hipError_t {
+    hipLaunchKernelGGL((decode_combine_kernel<E>), dim3(batch * n_q_heads), dim3(kCombThreads), 0, s, cv->prm,
+                       part, n_q_heads, n_kv_heads, n_chunks, cv->dS, cv->dD, out, out_dt == TQ_BF16 ? 1 : 0);
+    return hipGetLastError();
+  };
+  return dispatch_E(cv->prm.d, run);
 }
 
 bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why) {

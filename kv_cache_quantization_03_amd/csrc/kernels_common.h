@@ -10,6 +10,8 @@
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include <algorithm>
 #include <cstdint>
 
@@ -284,6 +286,14 @@ __host__ inline hipError_t dispatch_E(int d, F&& f) {
     case 1536: return f.template operator()<24>();
     default: return hipErrorInvalidValue;
   }
+}
+
+// f.template operator()<I>() for I = 0..N-1, I a constant expression in each
+// call (an unrolling that does not depend on the optimizer's size limits).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f.template operator()<I>(), ...); }(
+      std::make_integer_sequence<int, N>{});
 }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

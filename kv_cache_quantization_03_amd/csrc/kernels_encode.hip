@@ -10,8 +10,6 @@
 #include <cstdlib>
 #include <string>
 
-#include <utility>
-
 #include "kernels_common.h"
 
 namespace tq {
@@ -27,11 +25,32 @@ namespace tq {
 // neither the residual nor γ: its record is the codes and ν.
 enum ResidualMode { kResF32, kResF16, kResNone };
 
-// f.template operator()<I>() for I = 0..N-1, I a constant expression in each call.
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  [&]<int... I>(std::integer_sequence<int, I...>) { (f.template operator()<I>(), ...); }(
-      std::make_integer_sequence<int, N>{});
+// Bit-plane packing of one vector's codes (code of coordinate e*64 + lane in
+// idx[e] of that lane): plane p, register e -> words p*(d/32) + 2e (+1), the
+// ballot's two halves selected into lane (word % 64) of register word / 64.
+template <int E>
+__device__ __forceinline__ void pack_code_planes(const int (&idx)[E], int lane, int nb, uint32_t* __restrict__ crow,
+                                                 int W) {
+  constexpr int d = E * kWave;
+  constexpr int WMAX = 3 * d / 32;                  // words of the widest record (b = 3)
+  constexpr int NW = (WMAX + kWave - 1) / kWave;    // registers of words per lane
+  uint32_t words[NW];
+#pragma unroll
+  for (int r = 0; r < NW; ++r) words[r] = 0u;
+  static_for<3>([&]<int p>() {
+    if (p >= nb) return;  // uniform
+    static_for<E>([&]<int e>() {
+      const uint64_t m = __ballot((idx[e] >> p) & 1);
+      constexpr int w0 = p * (d / 32) + 2 * e;  // even: both halves land in one register
+      uint32_t& wr = words[w0 / kWave];
+      wr = lane == w0 % kWave ? static_cast<uint32_t>(m) : wr;
+      wr = lane == w0 % kWave + 1 ? static_cast<uint32_t>(m >> 32) : wr;
+      __builtin_amdgcn_sched_barrier(0);  // each ballot's two scalar registers are used at once
+    });
+  });
+#pragma unroll
+  for (int r = 0; r < NW; ++r)
+    if (r * kWave + lane < W) crow[r * kWave + lane] = words[r];
 }
 
 template <int E, typename T, int RM>
@@ -103,29 +122,7 @@ __global__ __launch_bounds__(256) void encode_rq_kernel(const T* __restrict__ x,
   }
   if constexpr (RM != kResNone) rs = wave_sum(rs);
 
-  // bit-plane packing: plane p, register e -> words p*(d/32) + 2e (+1), the
-  // ballot's two halves selected into lane (word % 64) of register word / 64
-  constexpr int WMAX = 3 * d / 32;                  // words of the widest record (b = 3)
-  constexpr int NW = (WMAX + kWave - 1) / kWave;    // registers of words per lane
-  const int W = P.code_words;
-  uint32_t* crow = codes + vec * W;
-  uint32_t words[NW];
-#pragma unroll
-  for (int r = 0; r < NW; ++r) words[r] = 0u;
-  static_for<3>([&]<int p>() {
-    if (p >= P.b) return;  // uniform
-    static_for<E>([&]<int e>() {
-      const uint64_t m = __ballot((idx[e] >> p) & 1);
-      constexpr int w0 = p * (d / 32) + 2 * e;  // even: both halves land in one register
-      uint32_t& wr = words[w0 / kWave];
-      wr = lane == w0 % kWave ? static_cast<uint32_t>(m) : wr;
-      wr = lane == w0 % kWave + 1 ? static_cast<uint32_t>(m >> 32) : wr;
-      __builtin_amdgcn_sched_barrier(0);  // each ballot's two scalar registers are used at once
-    });
-  });
-#pragma unroll
-  for (int r = 0; r < NW; ++r)
-    if (r * kWave + lane < W) crow[r * kWave + lane] = words[r];
+  pack_code_planes<E>(idx, lane, P.b, codes + vec * P.code_words, P.code_words);
   if (lane == 0) {
     norm[vec] = nu;
     if constexpr (RM != kResNone) rnorm[vec] = sqrtf(rs);
@@ -475,6 +472,130 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
   }
 }
 
+// ----------------------------------------------------------------------------
+// Rotate + recursive polar quantize (「谷歌 TurboQuant 深度拆解」 第二部分
+// PolarQuant) for d = 64 and 256, the split encode's first step (d = 128 has
+// the fused kernel above): one wavefront per vector, lane holding coordinates
+// e*64 + lane.  Level l (1..log2 d) pairs the two children of each node, whose
+// coordinates differ in bit l-1: lanes lane ^ 2^(l-1) for l <= 6, registers
+// e ^ 2^(l-7) above; both members of a pair compute the same angle from the
+// same two values (level 1: atan2(y_2n+1, y_2n) taken into [0, 2π); above:
+// atan2 of the two child radii, in [0, π/2]; code = #{level boundaries below
+// the angle}).  ŷ_j is the fp32 product, top-down from radius 1, of cos or sin
+// (bit l-1 of j) of level l's centroid at node j >> l.  The codes reach their
+// slots (level l: d - 2d/2^l + node; slot d-1 holds 0) through LDS and are
+// packed as bit-planes like the per-coordinate codes; the residual y - ŷ, γ
+// and ν leave as in encode_rq_kernel.
+template <int E, typename T, int RM, int B>
+__global__ __launch_bounds__(256) void encode_polar_rq_kernel(const T* __restrict__ x, int64_t n, DevParams P,
+                                                              PolarParams PP, const float* __restrict__ Dsign,
+                                                              uint32_t* __restrict__ codes, float* __restrict__ norm,
+                                                              float* __restrict__ rnorm, float* __restrict__ rbuf,
+                                                              float rscale) {
+  static_assert(E == 1 || E == 2 || E == 4, "d = 64, 128 or 256");
+  constexpr int d = E * kWave, NL = 1 << B;
+  constexpr int LV = E == 1 ? 6 : (E == 2 ? 7 : 8);  // log2 d
+  __shared__ float2 tab[LV][NL];    // (cos, sin) of every level's centroids
+  __shared__ uint8_t pcode[4][d];   // each wave's codes by slot
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < LV * NL; e += blockDim.x)
+    tab[e / NL][e % NL] = float2{PP.cosc[e / NL][e % NL], PP.sinc[e / NL][e % NL]};
+  __syncthreads();
+  const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + wv;
+  if (vec >= n) return;  // wave-uniform
+  const T* xr = x + vec * d;
+  float v[E];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    v[e] = load_elem(xr, e * kWave + lane);
+    ss = fmaf(v[e], v[e], ss);
+  }
+  ss = wave_sum(ss);
+  const float nu = sqrtf(ss);
+  const float inv = nu > 0.f ? 1.0f / nu : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] *= inv * Dsign[e * kWave + lane];
+  hadamard_wave<E, false, true>(v, lane);
+  float y[E], rad[E];
+  int code[LV][E];  // level l's code at the node of coordinate e*64 + lane
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = v[e] * P.inv_sqrt_d;
+  static_for<6>([&]<int k>() {  // level k + 1: partner lane ^ 2^k
+    const bool hi = (lane >> k) & 1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float mine = k == 0 ? y[e] : rad[e];
+      const float o = __shfl_xor(mine, 1 << k, kWave);
+      const float a = hi ? o : mine, b = hi ? mine : o;
+      float th = atan2f(b, a);
+      if constexpr (k == 0) th = th < 0.f ? th + 6.28318530717958647f : th;
+      code[k][e] = polar_code<NL>(PP.bound[k], th);
+      rad[e] = sqrtf(a * a + b * b);
+    }
+  });
+  if constexpr (LV >= 7) {  // level 7: registers e, e + 1
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const float a = rad[e], b = rad[e + 1];
+      code[6][e] = code[6][e + 1] = polar_code<NL>(PP.bound[6], atan2f(b, a));
+      rad[e] = rad[e + 1] = sqrtf(a * a + b * b);
+    }
+  }
+  if constexpr (LV >= 8) {  // level 8: registers e, e + 2
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const int c = polar_code<NL>(PP.bound[7], atan2f(rad[e + 2], rad[e]));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) code[7][e + u] = c;
+    }
+  }
+  // each node's code from the member holding its first coordinate
+  static_for<LV>([&]<int k>() {
+    constexpr int l = k + 1, base = d - ((2 * d) >> l);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = e * kWave + lane;
+      if ((j & ((1 << l) - 1)) == 0) pcode[wv][base + (j >> l)] = static_cast<uint8_t>(code[k][e]);
+    }
+  });
+  if (lane == 0) pcode[wv][d - 1] = 0;
+  // ŷ top-down from radius 1, residual
+  float rs = 0.f;
+  float* rr = rbuf + vec * d;
+  _Float16* rh = reinterpret_cast<_Float16*>(rbuf) + vec * 2 * d;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = e * kWave + lane;
+    float R = 1.f;
+    static_for<LV>([&]<int k>() {
+      constexpr int l = LV - k;
+      const float2 f = tab[l - 1][code[l - 1][e]];
+      R *= ((j >> (l - 1)) & 1) ? f.y : f.x;
+    });
+    const float r = y[e] - R;
+    if constexpr (RM == kResF16) {
+      const float rsc = r * rscale;
+      const _Float16 hi = static_cast<_Float16>(rsc);
+      rh[e * kWave + lane] = hi;
+      rh[d + e * kWave + lane] = static_cast<_Float16>(rsc - static_cast<float>(hi));
+    } else if constexpr (RM == kResF32) {
+      rr[e * kWave + lane] = r;
+    }
+    rs = fmaf(r, r, rs);
+  }
+  if constexpr (RM != kResNone) rs = wave_sum(rs);
+  __builtin_amdgcn_wave_barrier();  // the wave's code writes land before its reads
+  int idx[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) idx[e] = pcode[wv][e * kWave + lane];
+  pack_code_planes<E>(idx, lane, B, codes + vec * P.code_words, P.code_words);
+  if (lane == 0) {
+    norm[vec] = nu;
+    if constexpr (RM != kResNone) rnorm[vec] = sqrtf(rs);
+  }
+}
+
 // The QJL projection z = S r with its sign bits on the fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16), for d = m a multiple of 128: the split encode's
 // second step.  S = S_hi + S_lo (fp16 pair, made at codec creation) and
@@ -607,7 +728,7 @@ bool sproj_mfma_eligible(const tq_codec_s* c) {
 }
 
 bool encode_fused_eligible(const tq_codec_s* c) {
-  if (c->polar) return true;  // the only polar encode (d = 128, made so at codec creation)
+  if (c->polar) return c->prm.d == 128;  // d = 64 and 256: the split path with the polar quantizer
   const char* v = std::getenv("TQ_ENCODE_KERNEL");
   if (v && std::string(v) == "split") return false;
   if (!c->qjl) return c->prm.d == 128;  // MSE-only: no projection
@@ -651,6 +772,28 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
   // 2^sc with sc = ceil(log2 sqrt(d)) + 4: r·2^sc is O(1) per coordinate and below 2^11
   const int sc = static_cast<int>(std::ceil(std::log2(std::sqrt(static_cast<double>(P.d))))) + 4;
   const dim3 grid_rq(static_cast<unsigned>(ceil_div(n, 4)));
+  if (c->polar) {  // d = 64 or 256 (d = m, the QJL stage always present)
+    auto prun = [&]<int E, int B>() -> hipError_t {
+      if (mfma)
+        hipLaunchKernelGGL((encode_polar_rq_kernel<E, T, kResF16, B>), grid_rq, dim3(256), 0, s, x, n, P, c->pol,
+                           c->dD, out.codes, out.norm, out.rnorm, ws_r, std::ldexp(1.0f, sc));
+      else
+        hipLaunchKernelGGL((encode_polar_rq_kernel<E, T, kResF32, B>), grid_rq, dim3(256), 0, s, x, n, P, c->pol,
+                           c->dD, out.codes, out.norm, out.rnorm, ws_r, 1.0f);
+      return hipGetLastError();
+    };
+    auto pb = [&]<int E>() -> hipError_t {
+      switch (P.b) {
+        case 1: return prun.template operator()<E, 1>();
+        case 2: return prun.template operator()<E, 2>();
+        case 3: return prun.template operator()<E, 3>();
+      }
+      return hipErrorInvalidValue;
+    };
+    hipError_t e = P.d == 64 ? pb.template operator()<1>() : P.d == 256 ? pb.template operator()<4>()
+                                                                       : hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+  }
   auto run = [&]<int E>() -> hipError_t {
     if (!c->qjl)
       hipLaunchKernelGGL((encode_rq_kernel<E, T, kResNone>), grid_rq, dim3(256), 0, s, x, n, P, c->dD, out.codes,
@@ -663,7 +806,7 @@ hipError_t encode_typed(const tq_codec_s* c, const T* x, int64_t n, tq_packed_t 
                          out.norm, out.rnorm, ws_r, 1.0f);
     return hipGetLastError();
   };
-  hipError_t e = dispatch_E(P.d, run);
+  hipError_t e = c->polar ? hipSuccess : dispatch_E(P.d, run);
   if (e != hipSuccess || !c->qjl) return e;
   if (mfma) {
     const _Float16* r16 = reinterpret_cast<const _Float16*>(ws_r);

@@ -83,54 +83,77 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 }
 
 // ----------------------------------------------------------------------------
-// Logits for a codec with the recursive polar first stage (d = 128): the MSE
-// term is ⟨q', ŷ⟩ with ŷ rebuilt from the angle codes, the QJL term is the
-// usual one.  One thread per key: it walks the 64 level-1 pairs in order,
-// keeping the products of the upper levels' factors along its path (the
-// factors of levels <= ctz(i) + 2 change at pair i, two per pair on average),
-// so ŷ costs about four multiplications per pair.  The query values are the
-// same for every thread of the block, so they are read as scalar operands;
-// the loops are unrolled, so every code's slot and bit are constants.  Up to
-// 4 query vectors per block (grid.z splits the rest).  The QJL sums
-// Σ_{τ_i = +1} p_i come from tables in LDS: for each byte g of the 128 sign
-// bits and each of its 256 values, the four vectors' sums of p over the set
-// bits (built once per block of 1024 keys), so a key takes 16 table reads
-// instead of 128 multiply-adds per vector.  Likewise the level-1 pair i with
-// code c contributes r_i (q'_2i cos θ_c + q'_2i+1 sin θ_c) to each vector's
-// MSE sum, r_i the product of the upper levels' factors: the bracket is read
-// from a table of the four vectors' values for every (pair, code); with at
-// most 4 codes per angle the same is done one level up, per (level-2 node,
-// its code, its two pairs' codes).
+// Logits for a codec with the recursive polar first stage (d = 2^LD, 64 to
+// 256): the MSE term is ⟨q', ŷ⟩ with ŷ rebuilt from the angle codes, the QJL
+// term is the usual one.  One thread per key: it walks the d/2 level-1 pairs
+// in order, keeping the products of the upper levels' factors along its path
+// (the factors of levels <= ctz(i) + 2 change at pair i, two per pair on
+// average), so ŷ costs about four multiplications per pair.  The query values
+// are the same for every thread of the block, so they are read as scalar
+// operands; the loops are unrolled, so every code's slot and bit are
+// constants.  Up to 4 query vectors per block (grid.z splits the rest).  The
+// QJL sums Σ_{τ_i = +1} p_i come from tables in LDS: for each byte g of the d
+// sign bits and each of its 256 values, the four vectors' sums of p over the
+// set bits (built once per block of 1024 keys), so a key takes d/8 table
+// reads instead of d multiply-adds per vector.  Likewise the level-1 pair i
+// with code c contributes r_i (q'_2i cos θ_c + q'_2i+1 sin θ_c) to each
+// vector's MSE sum, r_i the product of the upper levels' factors: the bracket
+// is read from a table of the four vectors' values for every (pair, code);
+// with at most 4 codes per angle and d <= 128 the same is done one level up,
+// per (level-2 node, its code, its two pairs' codes).  Level l's angles sit
+// in slots d - 2d/2^l + node.
 // ----------------------------------------------------------------------------
-constexpr int kPolarKeys = 1024;
+// Keys (and threads) per block: 1024, or 512 at d = 256, whose records and
+// path products need more than the 128 registers a 1024-thread block allows.
+template <int LD>
+constexpr int polar_keys() { return LD <= 7 ? 1024 : 512; }
+
+// NW consecutive 32-bit words (NW = 2: one 8-byte load; else 16-byte loads).
+template <int NW>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
+  if constexpr (NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x;
+    w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+  }
+}
 
 // One key's record into registers (nothing past the context).
-template <int B>
-__device__ __forceinline__ void polar_fetch(const tq_packed_t& k, int64_t rowb, int64_t key, int64_t ctx, uint4 (&nc)[B],
-                                            uint4& ns, float& nn, float& ng) {
+template <int B, int NW>
+__device__ __forceinline__ void polar_fetch(const tq_packed_t& k, int64_t rowb, int64_t key, int64_t ctx,
+                                            uint32_t (&nc)[B][NW], uint32_t (&ns)[NW], float& nn, float& ng) {
   if (key < ctx) {
 #pragma unroll
-    for (int p = 0; p < B; ++p) nc[p] = reinterpret_cast<const uint4*>(k.codes + (rowb + key) * (4 * B))[p];
-    ns = reinterpret_cast<const uint4*>(k.signs)[rowb + key];
+    for (int p = 0; p < B; ++p) load_words<NW>(k.codes + (rowb + key) * (NW * B) + NW * p, nc[p]);
+    load_words<NW>(k.signs + (rowb + key) * NW, ns);
     nn = k.norm[rowb + key];
     ng = k.rnorm[rowb + key];
   }
 }
 
-template <int B>
-__global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
+template <int B, int LD>
+__global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
                                                            const float* __restrict__ proj, int Hq, int nq, int G,
                                                            int nkv, int64_t ctx, tq_packed_t k,
                                                            float* __restrict__ logits) {
-  constexpr int d = 128, NL = 1 << B;
-  __shared__ float2 tab[7][NL];     // (cos, sin) of every level's centroids
-  __shared__ float psum[4];         // Σ_i p_i of each tile vector
-  __shared__ float4 pj[d];          // p_j of the four tile vectors
-  __shared__ float4 ptab[16][256];  // [byte g][value]: Σ over the set bits k of p_{8g+k}
-  __shared__ float4 qtab[64][NL];   // [pair i][code c]: q'_2i cos θ_c + q'_2i+1 sin θ_c
-  constexpr bool L2T = NL <= 4;     // level-2 table: 32 nodes x NL^3 entries
+  constexpr int d = 1 << LD, NL = 1 << B, NW = d / 32, kPolarKeys = polar_keys<LD>();
+  __shared__ float2 tab[LD][NL];      // (cos, sin) of every level's centroids
+  __shared__ float psum[4];           // Σ_i p_i of each tile vector
+  __shared__ float4 pj[d];            // p_j of the four tile vectors
+  __shared__ float4 ptab[d / 8][256]; // [byte g][value]: Σ over the set bits k of p_{8g+k}
+  __shared__ float4 qtab[d / 2][NL];  // [pair i][code c]: q'_2i cos θ_c + q'_2i+1 sin θ_c
+  constexpr bool L2T = NL <= 4 && d <= 128;  // level-2 table: d/4 nodes x NL^3 entries
   constexpr int N3 = L2T ? NL * NL * NL : 1;
-  __shared__ float4 q2tab[L2T ? 32 : 1][N3];
+  __shared__ float4 q2tab[L2T ? d / 4 : 1][N3];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
@@ -147,20 +170,23 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     pp[t] = proj + qr * d;
     orow[t] = ok ? ((static_cast<int64_t>(b) * Hq + h) * nq + qi) * ctx : -1;
   }
-  if (tid < 7 * NL) tab[tid / NL][tid % NL] = float2{PP.cosc[tid / NL][tid % NL], PP.sinc[tid / NL][tid % NL]};
+  if (tid < LD * NL) tab[tid / NL][tid % NL] = float2{PP.cosc[tid / NL][tid % NL], PP.sinc[tid / NL][tid % NL]};
   if (wv < 4) {
-    const float s = wave_sum(pp[wv][lane] + pp[wv][lane + 64]);  // wave w: tile vector w
+    float a = pp[wv][lane];
+#pragma unroll
+    for (int u = 1; u < d / 64; ++u) a += pp[wv][lane + 64 * u];
+    const float s = wave_sum(a);  // wave w: tile vector w
     if (lane == 0) psum[wv] = s;
   }
-  if (tid < d) pj[tid] = float4{pp[0][tid], pp[1][tid], pp[2][tid], pp[3][tid]};
-  if (tid < 64 * NL) {
-    const int i = tid / NL, c = tid % NL;
+  for (int e = tid; e < d; e += kPolarKeys) pj[e] = float4{pp[0][e], pp[1][e], pp[2][e], pp[3][e]};
+  for (int e = tid; e < (d / 2) * NL; e += kPolarKeys) {
+    const int i = e / NL, c = e % NL;
     const float cs = PP.cosc[0][c], sn = PP.sinc[0][c];
     qtab[i][c] = float4{fmaf(qp[0][2 * i + 1], sn, qp[0][2 * i] * cs), fmaf(qp[1][2 * i + 1], sn, qp[1][2 * i] * cs),
                         fmaf(qp[2][2 * i + 1], sn, qp[2][2 * i] * cs), fmaf(qp[3][2 * i + 1], sn, qp[3][2 * i] * cs)};
   }
   __syncthreads();
-  for (int e = tid; e < 16 * 256; e += kPolarKeys) {
+  for (int e = tid; e < (d / 8) * 256; e += kPolarKeys) {
     const int g = e >> 8, v = e & 255;
     float4 a = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -176,7 +202,7 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     // node n, codes (c2, ca, cb): cos θ2_c2 · qtab[2n][ca] + sin θ2_c2 · qtab[2n+1][cb].
     // Entry r = c2·4^B + Σ_p q_p·4^p with q_p the two bits of plane p at the
     // slots 2n, 2n+1 (bit 0: pair 2n), so a key forms r with one extract per plane.
-    for (int e = tid; e < 32 * N3; e += kPolarKeys) {
+    for (int e = tid; e < (d / 4) * N3; e += kPolarKeys) {
       const int n = e / N3, r = e % N3, c2 = r >> (2 * B);
       int ca = 0, cb = 0;
 #pragma unroll
@@ -195,19 +221,22 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
   // record is loaded while the current one is scored
   const int64_t nkb = (ctx + kPolarKeys - 1) / kPolarKeys;
   const int64_t rowb = static_cast<int64_t>(bk) * ctx;
-  uint4 nc[B], ns = uint4{0u, 0u, 0u, 0u};
+  uint32_t nc[B][NW], ns[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) ns[i] = 0u;
   float nn = 0.f, ng = 0.f;
-  polar_fetch<B>(k, rowb, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, ctx, nc, ns, nn, ng);
+  polar_fetch<B, NW>(k, rowb, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, ctx, nc, ns, nn, ng);
   for (int64_t kb = blockIdx.x; kb < nkb; kb += gridDim.x) {
   const int64_t key = kb * kPolarKeys + tid;
-  uint32_t w[B][4];
+  uint32_t w[B][NW], sw[NW];
 #pragma unroll
-  for (int p = 0; p < B; ++p) {
-    w[p][0] = nc[p].x; w[p][1] = nc[p].y; w[p][2] = nc[p].z; w[p][3] = nc[p].w;
+  for (int i = 0; i < NW; ++i) {
+#pragma unroll
+    for (int p = 0; p < B; ++p) w[p][i] = nc[p][i];
+    sw[i] = ns[i];
   }
-  const uint32_t sw[4] = {ns.x, ns.y, ns.z, ns.w};
   const float nu = nn, ga = ng;
-  polar_fetch<B>(k, rowb, key + static_cast<int64_t>(gridDim.x) * kPolarKeys, ctx, nc, ns, nn, ng);
+  polar_fetch<B, NW>(k, rowb, key + static_cast<int64_t>(gridDim.x) * kPolarKeys, ctx, nc, ns, nn, ng);
   if (key < ctx) {
   auto code = [&](int slot) {  // slot is a constant after unrolling
     int c = 0;
@@ -216,30 +245,32 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     return c;
   };
   float mse[4] = {0.f, 0.f, 0.f, 0.f}, qj[4] = {0.f, 0.f, 0.f, 0.f};
-  float prod[9];  // prod[lv]: product of the factors of levels 7..lv along the current path
-  prod[8] = 1.f;
+  float prod[LD + 2];  // prod[lv]: product of the factors of levels LD..lv along the current path
+  prod[LD + 1] = 1.f;
   if constexpr (L2T) {
     // Level-4 node m at a time (level-2 nodes 4m..4m+3): its factors of levels
-    // 7..3 (slots 126, 124 + m/4, 120 + m/2, 112 + m, 96 + 2m + s) and its four
-    // level-2 brackets are read together, one LDS round trip per group of
-    // four nodes; the products keep the top-down order.
-    const float2 f7 = tab[6][code(126)];
+    // LD..3 and its four level-2 brackets are read together, one LDS round
+    // trip per group of four nodes; the products keep the top-down order.
+    const float2 ftop = tab[LD - 1][code(d - 2)];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const float2 f6 = tab[5][code(124 + (m >> 2))];
-      const float2 f5 = tab[4][code(120 + (m >> 1))];
-      const float2 f4 = tab[3][code(112 + m)];
-      const float2 f3a = tab[2][code(96 + 2 * m)], f3b = tab[2][code(97 + 2 * m)];
+    for (int m = 0; m < d / 16; ++m) {
+      float2 fu[LD > 5 ? LD - 5 : 1];  // levels LD-1 .. 5
+#pragma unroll
+      for (int lv = LD - 1; lv >= 5; --lv) fu[LD - 1 - lv] = tab[lv - 1][code(d - ((2 * d) >> lv) + (m >> (lv - 4)))];
+      const float2 f4 = tab[3][code(d - d / 8 + m)];
+      const float2 f3a = tab[2][code(d - d / 4 + 2 * m)], f3b = tab[2][code(d - d / 4 + 1 + 2 * m)];
       float4 bq[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = 4 * m + i;
-        int r = code(64 + n) << (2 * B);
+        int r = code(d / 2 + n) << (2 * B);
 #pragma unroll
         for (int p = 0; p < B; ++p) r |= static_cast<int>((w[p][n >> 4] >> (2 * (n & 15))) & 3u) << (2 * p);
         bq[i] = q2tab[n][r];
       }
-      const float p5 = (((m >> 2) ? f7.y : f7.x) * (((m >> 1) & 1) ? f6.y : f6.x)) * ((m & 1) ? f5.y : f5.x);
+      float p5 = ((m >> (LD - 5)) & 1) ? ftop.y : ftop.x;
+#pragma unroll
+      for (int lv = LD - 1; lv >= 5; --lv) p5 = p5 * (((m >> (lv - 5)) & 1) ? fu[LD - 1 - lv].y : fu[LD - 1 - lv].x);
       const float p4a = p5 * f4.x, p4b = p5 * f4.y;
       const float p3[4] = {p4a * f3a.x, p4a * f3a.y, p4b * f3b.x, p4b * f3b.y};
 #pragma unroll
@@ -254,16 +285,14 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-#pragma unroll
-  for (int i = 0; i < (L2T ? 0 : 64); ++i) {
+  if constexpr (!L2T) static_for<d / 2>([&]<int i>() {
     // levels whose factor changes at pair i: lv <= ctz(i) + 2 (all at i = 0)
-    const int hi = i == 0 ? 7 : (__builtin_ctz(i) + 2 < 7 ? __builtin_ctz(i) + 2 : 7);
+    const int hi = i == 0 ? LD : (__builtin_ctz(i) + 2 < LD ? __builtin_ctz(i) + 2 : LD);
 #pragma unroll
-    for (int lv = 7; lv >= 2; --lv) {
+    for (int lv = LD; lv >= 2; --lv) {
       if (lv > hi) continue;
       const int node = i >> (lv - 1), side = (i >> (lv - 2)) & 1;
-      const int slot = 128 - (256 >> lv) + node;  // level lv's angles start at 128 - 2^(8-lv)
-      const float2 cs = tab[lv - 1][code(slot)];
+      const float2 cs = tab[lv - 1][code(d - ((2 * d) >> lv) + node)];
       prod[lv] = prod[lv + 1] * (side ? cs.y : cs.x);
     }
     const float4 b = qtab[i][code(i)];
@@ -272,13 +301,13 @@ __global__ __launch_bounds__(kPolarKeys) void logits_polar_kernel(DevParams P, P
     mse[2] = fmaf(prod[2], b.z, mse[2]);
     mse[3] = fmaf(prod[2], b.w, mse[3]);
     // one pair's work stays together: without these the compiler keeps all
-    // 128 ŷ values live and forms the dot products afterwards (256 registers)
+    // d ŷ values live and forms the dot products afterwards
 #pragma unroll
     for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(mse[t]));
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
 #pragma unroll
-  for (int g = 0; g < 16; ++g) {
+  for (int g = 0; g < d / 8; ++g) {
     const float4 x = ptab[g][(sw[g >> 2] >> (8 * (g & 3))) & 255u];
     qj[0] += x.x; qj[1] += x.y; qj[2] += x.z; qj[3] += x.w;
   }
@@ -296,19 +325,28 @@ hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, i
   const float* proj = qrot + nv * c->prm.d;
   const int G = n_q_heads / n_kv_heads;
   // about one block per compute unit (a block's tables fill most of its LDS);
-  // each block then scores several 1024-key blocks with the tables it built
-  const int64_t nz = ceil_div(static_cast<int64_t>(n_queries) * G, 4), nkb = ceil_div(ctx, kPolarKeys);
+  // each block then scores several key blocks with the tables it built
+  const int64_t nz = ceil_div(static_cast<int64_t>(n_queries) * G, 4);
   const int64_t per = std::max<int64_t>(1, device_cu_count() / std::max<int64_t>(1, batch * n_kv_heads * nz));
-  const dim3 grid(static_cast<unsigned>(std::min(nkb, per)), batch * n_kv_heads, static_cast<unsigned>(nz));
-  auto go = [&]<int B>() -> hipError_t {
-    hipLaunchKernelGGL((logits_polar_kernel<B>), grid, dim3(kPolarKeys), 0, s, c->prm, c->pol, qrot, proj, n_q_heads,
-                       n_queries, G, n_kv_heads, ctx, k, logits);
+  auto go = [&]<int B, int LD>() -> hipError_t {
+    const int64_t nkb = ceil_div(ctx, polar_keys<LD>());
+    const dim3 grid(static_cast<unsigned>(std::min(nkb, per)), batch * n_kv_heads, static_cast<unsigned>(nz));
+    hipLaunchKernelGGL((logits_polar_kernel<B, LD>), grid, dim3(polar_keys<LD>()), 0, s, c->prm, c->pol, qrot, proj,
+                       n_q_heads, n_queries, G, n_kv_heads, ctx, k, logits);
     return hipGetLastError();
   };
+  auto byd = [&]<int B>() -> hipError_t {
+    switch (c->prm.d) {
+      case 64: return go.template operator()<B, 6>();
+      case 128: return go.template operator()<B, 7>();
+      case 256: return go.template operator()<B, 8>();
+    }
+    return hipErrorInvalidValue;
+  };
   switch (c->prm.b) {
-    case 1: return go.template operator()<1>();
-    case 2: return go.template operator()<2>();
-    case 3: return go.template operator()<3>();
+    case 1: return byd.template operator()<1>();
+    case 2: return byd.template operator()<2>();
+    case 3: return byd.template operator()<3>();
   }
   return hipErrorInvalidValue;
 }
@@ -337,7 +375,7 @@ hipError_t launch_qprep128(const tq_codec_s* c, const void* q, tq_dtype_t dt, in
 
 hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                               int n_kv_heads, int n_queries, void* ws, hipStream_t s) {
-  if (c->polar) {  // fp32 q' and p for the polar scorer (d = 128)
+  if (c->polar && c->prm.d == 128) {  // fp32 q' and p for the polar scorer (other d: the general prep below)
     float* qrot = static_cast<float*>(ws);
     float* proj = qrot + static_cast<int64_t>(batch) * n_queries * n_q_heads * c->prm.d;
     return launch_qprep128(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, qrot, proj, s);

@@ -260,7 +260,8 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (ck->polar || cv->polar) {
     if (pm) { set_error("paged decode takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
     if (!tq::decode_polar_shape_ok(ck, cv)) {
-      set_error("decode attention with a polar codec needs head_dim 128 for K and V, qjl_dim 128 and V in row records");
+      set_error("decode attention with a polar codec needs head_dim 128 or 256 (the same for K and V), qjl_dim equal "
+                "to head_dim and V in row records");
       return TQ_ERROR_NOT_SUPPORTED;
     }
   }

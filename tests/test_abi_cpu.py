@@ -154,16 +154,22 @@ def test_codec_create_without_gpu_reports_hip_error(B):
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_host_polar_books_match_oracle(B, bits):
     # the C++ per-level angle codebooks (composite Gauss-Legendre first
-    # moments) against the oracle's (SciPy quadrature)
-    for level in range(1, 8):
-        c, t, it = B.tq_polar_book_host(128, bits, level)
+    # moments) against the oracle's (SciPy quadrature), levels 1..8 (head_dim
+    # 256); a level's law does not depend on head_dim
+    for level in range(1, 9):
+        c, t, it = B.tq_polar_book_host(256, bits, level)
         oc, ot, _ = O.polar_lloyd_max(level, bits - 1)
         assert np.allclose(c, oc, rtol=0, atol=1e-10) and np.allclose(t, ot, rtol=0, atol=1e-10), (bits, level)
         assert (it == 0) == (level == 1)
+        for d in (64, 128):
+            if level <= int(np.log2(d)):
+                c2, t2, _ = B.tq_polar_book_host(d, bits, level)
+                assert np.array_equal(c2, c) and np.array_equal(t2, t)
 
 
 def test_host_polar_books_reject(B):
+    for d, level in ((512, 1), (96, 1), (128, 8), (64, 7), (256, 9), (256, 0)):
+        with pytest.raises(B.TQError):
+            B.tq_polar_book_host(d, 3, level)
     with pytest.raises(B.TQError):
-        B.tq_polar_book_host(256, 3, 1)
-    with pytest.raises(B.TQError):
-        B.tq_polar_book_host(128, 3, 8)
+        B.tq_polar_book_host(128, 5, 1)

@@ -960,18 +960,21 @@ def test_decode_paged_rejects_bad_arguments(B):
 _polar = {}
 
 
-def polar_pair(B, bits, seed=1234):
-    if (bits, seed) not in _polar:
-        _polar[(bits, seed)] = (B.tq_codec_create_polar(128, bits, 0, seed), O.make_polar_codec(128, bits, seed=seed))
-    return _polar[(bits, seed)]
+def polar_pair(B, bits, seed=1234, d=128):
+    if (bits, seed, d) not in _polar:
+        _polar[(bits, seed, d)] = (B.tq_codec_create_polar(d, bits, 0, seed), O.make_polar_codec(d, bits, seed=seed))
+    return _polar[(bits, seed, d)]
 
 
-@pytest.mark.parametrize("bits,dtype", [(2, "f32"), (3, "bf16"), (3, "f32"), (4, "f16"), (4, "f32")])
-def test_polar_encode_parity(B, bits, dtype):
-    say(f"polar encode bits={bits} {dtype}")
-    gc, pc = polar_pair(B, bits)
+# head_dim 128: the fused encode; 64 and 256: rotate + polar quantize, then the projection
+@pytest.mark.parametrize("bits,dtype,d", [(2, "f32", 128), (3, "bf16", 128), (3, "f32", 128), (4, "f16", 128),
+                                          (4, "f32", 128), (2, "f32", 64), (3, "bf16", 64), (4, "f32", 64),
+                                          (2, "bf16", 256), (3, "f32", 256), (4, "bf16", 256)])
+def test_polar_encode_parity(B, bits, dtype, d):
+    say(f"polar encode bits={bits} {dtype} d={d}")
+    gc, pc = polar_pair(B, bits, d=d)
     assert gc.polar and gc.record_bytes == pc.record_bytes
-    x = rand_keys(1500, 128, seed=300 + bits, dtype=dtype)   # includes a zero vector and a near-basis one
+    x = rand_keys(1500, d, seed=300 + bits + d, dtype=dtype)   # includes a zero vector and a near-basis one
     kp, _ = B.tq_encode_kv(gc, to_dev(x, dtype))
     torch.cuda.synchronize()
     g = kp.numpy()
@@ -979,48 +982,52 @@ def test_polar_encode_parity(B, bits, dtype):
     gauss[[3, 5]] = False                                      # the zero and the basis-like rows
     st = check_polar_encode(pc, x[gauss].astype(np.float64), {k: v[gauss] for k, v in g.items()},
                             f"polar b{bits}", max_rate=1e-5)
-    say(f"  Gaussian rows: angle codes differing (in band): {st['code_mismatch']} of {gauss.sum() * 127}, "
+    say(f"  Gaussian rows: angle codes differing (in band): {st['code_mismatch']} of {gauss.sum() * (d - 1)}, "
         f"signs in band: {st['sign_mismatch']}")
     st = check_polar_encode(pc, x[~gauss].astype(np.float64), {k: v[~gauss] for k, v in g.items()},
                             f"polar b{bits} special rows")
     say(f"  zero and basis-like rows: angle codes differing (in band): {st['code_mismatch']}")
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
-def test_polar_encode_basis_vectors(B, bits):
+@pytest.mark.parametrize("bits,d", [(2, 128), (3, 128), (4, 128), (3, 64), (3, 256)])
+def test_polar_encode_basis_vectors(B, bits, d):
     # x = s·e_k: the rotated coordinates all have magnitude s/√d, so every
     # level-1 angle is an odd multiple of π/4 (a boundary of the uniform 2- and
     # 3-bit level-1 quantizers) and every higher-level angle is π/4; codes may
     # go either way there, each checked against its boundary, with no rate cap
-    gc, pc = polar_pair(B, bits)
-    x = np.zeros((128, 128))
-    x[np.arange(128), np.arange(128)] = np.linspace(0.5, 4.0, 128)
+    gc, pc = polar_pair(B, bits, d=d)
+    x = np.zeros((d, d))
+    x[np.arange(d), np.arange(d)] = np.linspace(0.5, 4.0, d)
     x = as_exact(x, "f32")
     kp, _ = B.tq_encode_kv(gc, to_dev(x, "f32"))
     torch.cuda.synchronize()
-    st = check_polar_encode(pc, x.astype(np.float64), kp.numpy(), f"polar basis b{bits}")
-    say(f"polar basis vectors b{bits}: angle codes differing (in band): {st['code_mismatch']} of {128 * 127}")
+    st = check_polar_encode(pc, x.astype(np.float64), kp.numpy(), f"polar basis b{bits} d{d}")
+    say(f"polar basis vectors b{bits} d={d}: angle codes differing (in band): {st['code_mismatch']} of {d * (d - 1)}")
 
 
-@pytest.mark.parametrize("bits,batch,hq,hkv,nq,ctx", [(3, 1, 8, 2, 1, 1000), (2, 2, 4, 4, 3, 333), (4, 1, 32, 8, 1, 257),
-                                                     (3, 1, 1, 1, 5, 1),
-                                                     # 32 (sequence, KV head, 4-vector) groups: 8 blocks each
-                                                     # stride over 9 key blocks (the last ragged)
-                                                     (3, 2, 64, 8, 1, 9000)])
-def test_polar_logits_oracle_records(B, bits, batch, hq, hkv, nq, ctx):
+@pytest.mark.parametrize("bits,batch,hq,hkv,nq,ctx,d", [
+    (3, 1, 8, 2, 1, 1000, 128), (2, 2, 4, 4, 3, 333, 128), (4, 1, 32, 8, 1, 257, 128), (3, 1, 1, 1, 5, 1, 128),
+    # 32 (sequence, KV head, 4-vector) groups: 8 blocks each stride over 9 key blocks (the last ragged)
+    (3, 2, 64, 8, 1, 9000, 128),
+    # head_dim 64 (level-2 table, 6 levels) and 256 (512-key blocks, 8 levels); the last ones stride over
+    # several key blocks per block, with a ragged tail
+    (2, 1, 8, 2, 1, 1000, 64), (3, 2, 4, 4, 3, 333, 64), (4, 1, 32, 8, 1, 2049, 64), (3, 2, 64, 8, 1, 9000, 64),
+    (2, 1, 8, 2, 1, 1000, 256), (3, 2, 4, 4, 3, 333, 256), (4, 1, 32, 8, 1, 700, 256), (3, 1, 1, 1, 5, 1, 256),
+    (3, 2, 64, 8, 1, 9000, 256)])
+def test_polar_logits_oracle_records(B, bits, batch, hq, hkv, nq, ctx, d):
     # the scorer alone: oracle-encoded records, fp32 queries, bar 1e-4
-    say(f"polar logits bits={bits} batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx}")
-    gc, pc = polar_pair(B, bits)
-    rng = np.random.default_rng(ctx + 17 * bits)
-    rec = O.polar_encode(pc, rng.standard_normal((batch * hkv * ctx, 128)) * rng.lognormal(0, 0.5, (batch * hkv * ctx, 1)))
-    q = as_exact(rng.standard_normal((batch, nq, hq, 128)), "f32")
+    say(f"polar logits bits={bits} batch={batch} hq={hq} hkv={hkv} nq={nq} ctx={ctx} d={d}")
+    gc, pc = polar_pair(B, bits, d=d)
+    rng = np.random.default_rng(ctx + 17 * bits + d)
+    rec = O.polar_encode(pc, rng.standard_normal((batch * hkv * ctx, d)) * rng.lognormal(0, 0.5, (batch * hkv * ctx, 1)))
+    q = as_exact(rng.standard_normal((batch, nq, hq, d)), "f32")
     lg = B.tq_attn_logits(gc, to_dev(q, "f32"), B.packed_from_numpy(rec), ctx, hkv).cpu().numpy()
     G = hq // hkv
     worst = 0.0
     for b in range(batch):
         for kh in range(hkv):
             rows = slice((b * hkv + kh) * ctx, (b * hkv + kh + 1) * ctx)
-            qv = q[b, :, kh * G:(kh + 1) * G].transpose(1, 0, 2).reshape(G * nq, 128)
+            qv = q[b, :, kh * G:(kh + 1) * G].transpose(1, 0, 2).reshape(G * nq, d)
             ref = O.polar_score(pc, qv.astype(np.float64), {k: rec[k][rows] for k in ("codes", "signs", "norm", "rnorm")})
             got = lg[b, kh * G:(kh + 1) * G].reshape(G * nq, ctx)
             worst = max(worst, row_rel_err(got, ref).max())
@@ -1028,12 +1035,13 @@ def test_polar_logits_oracle_records(B, bits, batch, hq, hkv, nq, ctx):
     assert worst <= 1e-4
 
 
-def test_polar_end_to_end_and_split_form(B):
-    gc, pc = polar_pair(B, 3)
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_polar_end_to_end_and_split_form(B, d):
+    gc, pc = polar_pair(B, 3, d=d)
     hq, hkv, ctx = 8, 2, 2000
-    rng = np.random.default_rng(71)
-    k = as_exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
-    q = as_exact(rng.standard_normal((1, 1, hq, 128)), "bf16")
+    rng = np.random.default_rng(71 + d)
+    k = as_exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    q = as_exact(rng.standard_normal((1, 1, hq, d)), "bf16")
     kp, _ = B.tq_encode_kv(gc, to_dev(k, "bf16"))
     lg = B.tq_attn_logits(gc, to_dev(q, "bf16"), kp, ctx, hkv)
     prep = B.tq_attn_query_prep(gc, to_dev(q, "bf16"), hkv)
@@ -1048,14 +1056,17 @@ def test_polar_end_to_end_and_split_form(B):
         ref = O.polar_score(pc, q[0, 0, kh * G:(kh + 1) * G].astype(np.float64),
                             {kk: x[rows] for kk, x in rec.items()})
         worst = max(worst, row_rel_err(lg[0, kh * G:(kh + 1) * G, 0].cpu().numpy(), ref).max())
-    say(f"polar end to end: max row err {worst:.2e}")
+    say(f"polar end to end d={d}: max row err {worst:.2e}")
     assert worst <= 1e-3
 
 
 def test_polar_codec_limits(B):
     gc, _ = polar_pair(B, 3)
+    for d in (512, 96, 32):
+        with pytest.raises(B.TQError):
+            B.tq_codec_create_polar(d, 3)
     with pytest.raises(B.TQError):
-        B.tq_codec_create_polar(256, 3)
+        B.tq_codec_create_polar(128, 3, 64)  # the QJL dimension is head_dim
     kp = B.alloc_packed(gc, 256)
     with pytest.raises(B.TQError):  # paged logits read per-coordinate codes only
         B.tq_attn_logits_paged(gc, torch.zeros((1, 1, 4, 128), device="cuda"), kp,

@@ -26,16 +26,16 @@ def B():
 _codecs = {}
 
 
-def codec(B, kind, bits, seed):
+def codec(B, kind, bits, seed, d=128):
     """(GPU codec, oracle codec): kind 'polar', 'scalar' (two-stage) or 'mse'."""
-    key = (kind, bits, seed)
+    key = (kind, bits, seed, d)
     if key not in _codecs:
         if kind == "polar":
-            _codecs[key] = (B.tq_codec_create_polar(128, bits, 0, seed), O.make_polar_codec(128, bits, seed=seed))
+            _codecs[key] = (B.tq_codec_create_polar(d, bits, 0, seed), O.make_polar_codec(d, bits, seed=seed))
         elif kind == "mse":
-            _codecs[key] = (B.tq_codec_create_mse(128, bits, seed), O.make_mse_codec(128, bits, seed=seed))
+            _codecs[key] = (B.tq_codec_create_mse(d, bits, seed), O.make_mse_codec(d, bits, seed=seed))
         else:
-            _codecs[key] = (B.tq_codec_create(128, bits, 0, seed), O.make_codec(128, bits, seed=seed))
+            _codecs[key] = (B.tq_codec_create(d, bits, 0, seed), O.make_codec(d, bits, seed=seed))
     return _codecs[key]
 
 
@@ -59,25 +59,32 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("kk,kbits,vk,vbits,hq,hkv,ctx", [
-    ("polar", 3, "polar", 3, 8, 2, 3000),    # 1024-position chunks, ragged tail
-    ("scalar", 3, "polar", 3, 4, 1, 1025),   # per-coordinate K (fused scorer), polar V
-    ("polar", 3, "scalar", 3, 32, 8, 700),   # polar K, per-coordinate V
-    ("polar", 4, "polar", 2, 16, 1, 513),    # 16 query heads per KV head: 256-position chunks
-    ("polar", 2, "polar", 4, 2, 2, 1),       # one position
-    ("polar", 3, "mse", 3, 8, 2, 1500),      # polar K, MSE-only V (no J)
-    ("polar", 3, "polar", 3, 12, 2, 2049),   # 6 heads per KV head: 512-position chunks
+@pytest.mark.parametrize("kk,kbits,vk,vbits,hq,hkv,ctx,d", [
+    ("polar", 3, "polar", 3, 8, 2, 3000, 128),    # 1024-position chunks, ragged tail
+    ("scalar", 3, "polar", 3, 4, 1, 1025, 128),   # per-coordinate K (fused scorer), polar V
+    ("polar", 3, "scalar", 3, 32, 8, 700, 128),   # polar K, per-coordinate V
+    ("polar", 4, "polar", 2, 16, 1, 513, 128),    # 16 query heads per KV head: 256-position chunks
+    ("polar", 2, "polar", 4, 2, 2, 1, 128),       # one position
+    ("polar", 3, "mse", 3, 8, 2, 1500, 128),      # polar K, MSE-only V (no J)
+    ("polar", 3, "polar", 3, 12, 2, 2049, 128),   # 6 heads per KV head: 512-position chunks
+    # head_dim 256: 16 threads per position in the value kernel, the general combine
+    ("polar", 3, "polar", 3, 8, 2, 2500, 256),
+    ("scalar", 3, "polar", 2, 4, 1, 1100, 256),   # per-coordinate K (matrix-core scorer), polar V
+    ("polar", 3, "scalar", 4, 16, 4, 700, 256),   # polar K, per-coordinate V
+    ("polar", 4, "mse", 3, 8, 8, 513, 256),       # polar K, MSE-only V
+    ("polar", 2, "polar", 4, 32, 8, 300, 256),
+    ("polar", 3, "polar", 3, 16, 1, 1, 256),      # one position, 256-position chunks
 ])
-def test_polar_decode_attn_parity(B, kk, kbits, vk, vbits, hq, hkv, ctx):
-    say(f"polar decode K {kk}{kbits} V {vk}{vbits} hq={hq} hkv={hkv} ctx={ctx}")
-    gk, ok = codec(B, kk, kbits, 1234)
-    gv, ov = codec(B, vk, vbits, 4321)
-    rng = np.random.default_rng(ctx + hq + kbits)
-    k = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
-    v = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
-    q = exact(rng.standard_normal((1, hq, 128)), "bf16")
+def test_polar_decode_attn_parity(B, kk, kbits, vk, vbits, hq, hkv, ctx, d):
+    say(f"polar decode K {kk}{kbits} V {vk}{vbits} hq={hq} hkv={hkv} ctx={ctx} d={d}")
+    gk, ok = codec(B, kk, kbits, 1234, d)
+    gv, ov = codec(B, vk, vbits, 4321, d)
+    rng = np.random.default_rng(ctx + hq + kbits + d)
+    k = exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    v = exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    q = exact(rng.standard_normal((1, hq, d)), "bf16")
     kr, vr = encode(ok, k.astype(np.float64)), encode(ov, v.astype(np.float64))
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale)
     kp, vp = B.packed_from_numpy(kr), B.packed_from_numpy(vr)
     out32 = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, scale, out_dtype=torch.float32)
@@ -90,25 +97,26 @@ def test_polar_decode_attn_parity(B, kk, kbits, vk, vbits, hq, hkv, ctx):
     assert np.array_equal(out16.float().cpu().numpy(), O.bf16_round(g32))
 
 
-def test_polar_decode_end_to_end(B):
+@pytest.mark.parametrize("d", [128, 256])
+def test_polar_decode_end_to_end(B, d):
     # GPU encode of K and V with polar codecs, then decode: against the oracle
     # conditioned on the GPU's legitimate boundary choices
-    gk, ok = codec(B, "polar", 3, 1234)
-    gv, ov = codec(B, "polar", 3, 4321)
+    gk, ok = codec(B, "polar", 3, 1234, d)
+    gv, ov = codec(B, "polar", 3, 4321, d)
     hq, hkv, ctx = 8, 2, 2500
-    rng = np.random.default_rng(91)
-    k = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
-    v = exact(rng.standard_normal((hkv * ctx, 128)), "bf16")
-    q = exact(rng.standard_normal((1, hq, 128)), "bf16")
+    rng = np.random.default_rng(91 + d)
+    k = exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    v = exact(rng.standard_normal((hkv * ctx, d)), "bf16")
+    q = exact(rng.standard_normal((1, hq, d)), "bf16")
     kp = B.tq_encode_kv(gk, to_dev(k, "bf16"))[0]
     vp = B.tq_encode_kv(gv, to_dev(v, "bf16"))[0]
-    out = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, 1 / math.sqrt(128), out_dtype=torch.float32)
+    out = B.tq_decode_attn(gk, gv, to_dev(q, "bf16"), kp, vp, ctx, hkv, 1 / math.sqrt(d), out_dtype=torch.float32)
     torch.cuda.synchronize()
     kr = polar_records_like(ok, k.astype(np.float64), kp.numpy())
     vr = polar_records_like(ov, v.astype(np.float64), vp.numpy())
-    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, 1 / math.sqrt(128))
+    ref = O.decode_attn_accumulated(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, 1 / math.sqrt(d))
     err = row_rel_err(out.cpu().numpy(), ref).max()
-    say(f"polar decode end to end: max row err {err:.2e}")
+    say(f"polar decode end to end d={d}: max row err {err:.2e}")
     assert err <= 1e-4
 
 
@@ -131,16 +139,17 @@ def test_polar_decode_one_hot(B):
     assert np.max(np.abs(out[0, 0] - vhat)) <= 1e-4 * np.max(np.abs(vhat))
 
 
-@pytest.mark.parametrize("hq,hkv,ctx,gate,needles", [(8, 2, 3000, 1e-6, True), (16, 2, 1500, 1e-3, False)])
-def test_polar_decode_sparse_v(B, hq, hkv, ctx, gate, needles):
-    say(f"polar Sparse V hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles}")
-    gk, ok = codec(B, "polar", 3, 1234)
-    gv, ov = codec(B, "polar", 3, 4321)
-    rng = np.random.default_rng(ctx + hq)
+@pytest.mark.parametrize("hq,hkv,ctx,gate,needles,d", [(8, 2, 3000, 1e-6, True, 128), (16, 2, 1500, 1e-3, False, 128),
+                                                       (8, 2, 3000, 1e-6, True, 256)])
+def test_polar_decode_sparse_v(B, hq, hkv, ctx, gate, needles, d):
+    say(f"polar Sparse V hq={hq} hkv={hkv} ctx={ctx} gate={gate} needles={needles} d={d}")
+    gk, ok = codec(B, "polar", 3, 1234, d)
+    gv, ov = codec(B, "polar", 3, 4321, d)
+    rng = np.random.default_rng(ctx + hq + d)
     G = hq // hkv
-    q = (1.0 if needles else 3.0) * rng.standard_normal((1, hq, 128))
-    k = rng.standard_normal((hkv * ctx, 128))
-    v = rng.standard_normal((hkv * ctx, 128))
+    q = (1.0 if needles else 3.0) * rng.standard_normal((1, hq, d)) * math.sqrt(d / 128)
+    k = rng.standard_normal((hkv * ctx, d))
+    v = rng.standard_normal((hkv * ctx, d))
     if needles:  # one position per 1024 takes the weight of the group's queries
         for kh in range(hkv):
             u = q[0, kh * G:(kh + 1) * G].sum(axis=0)
@@ -149,7 +158,7 @@ def test_polar_decode_sparse_v(B, hq, hkv, ctx, gate, needles):
                 k[kh * ctx + t] += 60.0 * u
     q, k, v = exact(q, "f32"), exact(k, "f32"), exact(v, "f32")
     kr, vr = encode(ok, k.astype(np.float64)), encode(ov, v.astype(np.float64))
-    scale = 1 / math.sqrt(128)
+    scale = 1 / math.sqrt(d)
     chunk = B.tq_decode_attn_chunk(hq, hkv)
     ref, keep, local = O.decode_attn_sparse_v(ok, ov, q.astype(np.float64), kr, vr, 1, hq, hkv, ctx, scale, gate,
                                               chunk)
@@ -203,24 +212,34 @@ def test_polar_decode_refusals(B):
     gvb = B.tq_codec_create_vblock(128, 3, False, 1234)
     with pytest.raises(B.TQError):
         B.tq_decode_attn(gk, gvb, q, kp, B.alloc_packed(gvb, 256), 256, 1, 0.1)
+    # head_dim 64: the polar codec encodes, scores and searches, decode attention takes head_dim >= 128
+    g64, _ = codec(B, "polar", 3, 1234, 64)
+    k64 = B.alloc_packed(g64, 256)
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn(g64, g64, torch.zeros((1, 4, 64), device="cuda"), k64, k64, 256, 1, 0.1)
+    # K and V codecs of different head_dim
+    g256, _ = codec(B, "polar", 3, 1234, 256)
+    with pytest.raises(B.TQError):
+        B.tq_decode_attn(gk, g256, q, kp, B.alloc_packed(g256, 256), 256, 1, 0.1)
 
 
-@pytest.mark.parametrize("bits,n_db,nq,k", [(3, 70001, 9, 10), (4, 3000, 4, 100), (2, 1500, 1, 1)])
-def test_polar_search_parity(B, bits, n_db, nq, k):
+@pytest.mark.parametrize("bits,n_db,nq,k,d", [(3, 70001, 9, 10, 128), (4, 3000, 4, 100, 128), (2, 1500, 1, 1, 128),
+                                              (3, 20001, 5, 10, 64), (4, 5000, 3, 10, 256), (2, 2000, 17, 7, 256)])
+def test_polar_search_parity(B, bits, n_db, nq, k, d):
     # exhaustive search over a polar-compressed database (深度拆解 第三部分 向量搜索):
     # the returned top-k against the oracle's polar scores of every record;
     # duplicated records tie and go to the lower index
-    say(f"polar search bits={bits} n_db={n_db} nq={nq} k={k}")
-    gc, pc = codec(B, "polar", bits, 1234)
-    rng = np.random.default_rng(n_db + bits)
-    db = rng.standard_normal((n_db, 128))
+    say(f"polar search bits={bits} n_db={n_db} nq={nq} k={k} d={d}")
+    gc, pc = codec(B, "polar", bits, 1234, d)
+    rng = np.random.default_rng(n_db + bits + d)
+    db = rng.standard_normal((n_db, d))
     db /= np.linalg.norm(db, axis=1, keepdims=True)
     rec = encode(pc, db)
     for key in ("codes", "signs", "norm", "rnorm"):
         rec[key] = np.asarray(rec[key]).copy()
         rec[key][10] = rec[key][4]
         rec[key][n_db - 1] = rec[key][4]
-    qs = rng.standard_normal((nq, 128)).astype(np.float32)
+    qs = rng.standard_normal((nq, d)).astype(np.float32)
     qs[0] = (db[4] * 3).astype(np.float32)
     idx, sc = B.tq_search_topk(gc, B.packed_from_numpy(rec), torch.from_numpy(qs).cuda(), k)
     torch.cuda.synchronize()

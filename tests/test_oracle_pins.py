@@ -764,17 +764,31 @@ def test_polar_reconstruction_closed_form_and_unit_norm():
     assert np.allclose(np.linalg.norm(O.polar_dequantize(pc, rec), axis=1), 1, atol=1e-6)
 
 
-def test_polar_encode_picks_nearest_angle():
-    pc = O.make_polar_codec(128, 4, seed=7)
-    e = O.polar_encode(pc, np.random.default_rng(63).standard_normal((200, 128)))
-    for lv, (lo, hi) in enumerate(O.polar_slots(128), start=1):
+def test_polar_slots_and_unit_norm_other_head_dims():
+    # level l's d/2^l angles sit in [d - d/2^(l-1), d - d/2^l); the last slot is unused
+    for d in (64, 256):
+        L = int(math.log2(d))
+        assert O.polar_slots(d) == [(d - (d >> (l - 1)), d - (d >> l)) for l in range(1, L + 1)]
+        pc = O.make_polar_codec(d, 3, seed=7)
+        assert pc.levels == L and pc.record_bytes == 4 * (2 * d // 32 + d // 32) + 8
+        rnd = np.random.default_rng(d).integers(0, 4, (40, d))
+        rec = {"codes": O.pack_planes(rnd, 2), "signs": np.zeros((40, d // 32), np.uint32),
+               "norm": np.ones(40, np.float32), "rnorm": np.zeros(40, np.float32)}
+        assert np.allclose(np.linalg.norm(O.polar_dequantize(pc, rec), axis=1), 1, atol=1e-6)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_polar_encode_picks_nearest_angle(d):
+    pc = O.make_polar_codec(d, 4, seed=7)
+    e = O.polar_encode(pc, np.random.default_rng(63).standard_normal((200, d)))
+    for lv, (lo, hi) in enumerate(O.polar_slots(d), start=1):
         th = e["angles"][lv - 1]
         c = pc.centroids[lv - 1]
         dist = np.abs(th[:, :, None] - c[None, None, :])
         if lv == 1:
             dist = np.minimum(dist, 2 * math.pi - dist)
         assert np.array_equal(e["idx"][:, lo:hi], np.argmin(dist, axis=2)), lv
-    assert np.all(e["idx"][:, 127] == 0)
+    assert np.all(e["idx"][:, d - 1] == 0)
 
 
 def test_polar_score_unbiased_and_matches_dequantize():
