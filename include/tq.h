@@ -166,12 +166,13 @@ tq_status_t tq_codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uin
  * (fp32), and the residual y - ŷ takes the same QJL stage, so the record size
  * and the score ν(⟨q', ŷ⟩ + √(π/2)/m γ ⟨p, τ⟩) keep their form.
  * head_dim 64, 128 or 256 (log2 head_dim levels); bits 2, 3 or 4.  Such
- * codecs are accepted by tq_encode_kv, tq_attn_logits and its split form, by
- * tq_search_topk (the polar score against every database record), and, at
- * head_dim 128 or 256, as either codec (ck, cv or both) of tq_decode_attn,
- * tq_decode_attn_no_alloc and tq_decode_attn_sparse_v (深度拆解 第二部分 第三步:
- * the whole KV cache in polar form; v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)); the
- * paged calls return TQ_ERROR_NOT_SUPPORTED for them. */
+ * codecs are accepted by tq_encode_kv, tq_encode_append_paged,
+ * tq_attn_logits, its split form and tq_attn_logits_paged, by tq_search_topk
+ * (the polar score against every database record), and, at head_dim 128 or
+ * 256, as either codec (ck, cv or both) of tq_decode_attn,
+ * tq_decode_attn_no_alloc, tq_decode_attn_sparse_v and tq_decode_attn_paged
+ * (深度拆解 第二部分 第三步: the whole KV cache in polar form;
+ * v̂ = ν Rᵀ (ŷ + √(π/2)/m γ Sᵀ τ)). */
 tq_status_t tq_codec_create_polar(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64_t seed,
                                   tq_codec_t* out);
 /* An MSE-only value codec: the same rotation and per-coordinate Lloyd-Max
@@ -386,8 +387,9 @@ tq_status_t tq_encode_append_paged(tq_codec_t c, const void* x, tq_dtype_t dt, i
  * Sparse V gate of tq_decode_attn_sparse_v (0: plain attention).  Shapes as
  * tq_decode_attn (head_dim = qjl_dim = 128 with at most 4 query heads per KV
  * head runs on the matrix cores, other shapes on the general kernel; a V
- * cache in 32-row blocks needs the former; polar codecs return
- * TQ_ERROR_NOT_SUPPORTED), page_size a multiple of 128 and
+ * cache in 32-row blocks needs the former; polar codecs as tq_decode_attn
+ * takes them: the key scorer's logits through the page table, then the
+ * value kernel reading its rows through it), page_size a multiple of 128 and
  * 1 <= max_ctx <= max_pages * page_size (else TQ_ERROR_INVALID_VALUE).  Page
  * ids in the used part of the page table must be valid pages of the caches. */
 size_t tq_decode_attn_paged_workspace(tq_codec_t ck, tq_codec_t cv, int32_t batch, int32_t n_q_heads,
@@ -405,8 +407,9 @@ tq_status_t tq_decode_attn_paged(tq_codec_t ck, tq_codec_t cv, const void* q, tq
  * of sequence b).  q and the logits as tq_attn_logits with max_ctx as the
  * context: logits [batch][n_q_heads][n_queries][max_ctx] fp32; sequence b
  * scores its first min(ctx_lens[b], max_ctx) positions, and the logits of the
- * positions past them are not written.  Needs a per-coordinate two-stage
- * codec with head_dim 128 or 256, page_size a positive multiple of 128 and
+ * positions past them are not written.  Needs a polar codec (any head_dim it
+ * takes) or a per-coordinate two-stage codec with head_dim 128 or 256,
+ * page_size a positive multiple of 128 and
  * 1 <= max_ctx <= max_pages * page_size (else an error, no launch).
  * ctx_lens [batch] and page_table [batch][max_pages] are device int32 arrays
  * that must hold valid page ids for every position below ctx_lens[b].

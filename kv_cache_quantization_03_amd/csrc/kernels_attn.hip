@@ -36,14 +36,6 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
 }
 }  // namespace
 
-// Row of position t of (sequence b, KV head kh): [batch][kv_head][ctx] rows
-// for a contiguous cache (pm.table null), else through the page table.
-__device__ __forceinline__ int64_t kv_row(const PageMap& pm, int bk, int nkv, int64_t ctx, int64_t t) {
-  if (!pm.table) return static_cast<int64_t>(bk) * ctx + t;
-  const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + t / pm.page_size];
-  return (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + t % pm.page_size;
-}
-
 // Partials per (bk, chunk, g): [mx, l, M[d], J[m]].  gate > 0 (Sparse V): the
 // value term of (head, key) is dropped when exp(s - mx) < gate · l, l keeps
 // every key, and a key dropped for every head is not read.  A paged cache
@@ -470,8 +462,8 @@ size_t decode_polar_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int bat
                              int64_t ctx, int CH);
 hipError_t launch_decode_polar(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
                                int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx,
-                               float scale, bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws,
-                               int CH, hipStream_t s);
+                               float scale, bool sparse_v, float v_gate, const PageMap* pm, void* out,
+                               tq_dtype_t out_dt, void* ws, int CH, hipStream_t s);
 
 size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                        int64_t ctx) {
@@ -507,7 +499,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
   const int CH = attn_chunk(G);
   if (ck->polar || cv->polar)  // logits by the key codec's scorer, then V from them (kernels_attn_polar.hip)
     return launch_decode_polar(ck, cv, q, q_dt, batch, n_q_heads, n_kv_heads, k, v, ctx, scale, sparse_v, v_gate,
-                               out, out_dt, ws, CH, s);
+                               pm, out, out_dt, ws, CH, s);
   int n_chunks = static_cast<int>(ceil_div(ctx, CH));
   const int64_t nq = static_cast<int64_t>(batch) * n_q_heads;
   float* qrot = static_cast<float*>(ws);

@@ -23,6 +23,8 @@
 // four query heads; the threads of a coordinate block are summed across lanes
 // and waves once, at the end.  Records are loaded one step ahead; the chunk's
 // logits, ν and γ at once, before any is used.
+#include <algorithm>
+
 #include "kernels_common.h"
 
 namespace tq {
@@ -117,9 +119,9 @@ __device__ __forceinline__ void polar_subtree16(const uint32_t (&w)[NB][D / 32],
 // unless it is past the chunk or the Sparse V gate dropped it for every head
 // of the block.
 template <int NB, bool VQ, int GT, int D>
-__device__ __forceinline__ bool fetch_record(const tq_packed_t& V, int64_t row0, int tl, int n_in, int CH,
-                                             const float* wm, float gate, int o, uint32_t (&cw)[NB][D / 32],
-                                             uint32_t& sw) {
+__device__ __forceinline__ bool fetch_record(const tq_packed_t& V, const PageMap& pm, int bk, int nkv, int64_t ctx,
+                                             int64_t t0, int tl, int n_in, int CH, const float* wm, float gate, int o,
+                                             uint32_t (&cw)[NB][D / 32], uint32_t& sw) {
   constexpr int NWD = D / 32;
   bool need = tl < n_in;
   if (need && gate > 0.f) {
@@ -129,7 +131,7 @@ __device__ __forceinline__ bool fetch_record(const tq_packed_t& V, int64_t row0,
     need = any;
   }
   if (need) {
-    const int64_t row = row0 + tl;
+    const int64_t row = kv_row(pm, bk, nkv, ctx, t0 + tl);
 #pragma unroll
     for (int p = 0; p < NB; ++p)
 #pragma unroll
@@ -151,11 +153,14 @@ __device__ __forceinline__ bool fetch_record(const tq_packed_t& V, int64_t row0,
 // (kq = tid/NO, o = tid%NO), NO = D/16, takes positions kq, kq + 256/NO, ...
 // of the chunk and coordinates [16o, 16o + 16).  Dynamic LDS (at most 52 KB):
 // wm[GT][CH] = w ν, gam[CH] = γ, then the cross-wave sums [4][GT][2D].  NB:
-// the value codec's code planes.
+// the value codec's code planes.  A paged cache (pm.table set): sequence b
+// uses its first min(ctx_lens[b], ctx) positions, rows through the page
+// table; a chunk past them writes mx = -inf, l = 0 and zero sums.  ctx is
+// the logits row stride either way.
 template <int NB, bool VP, bool VQ, int GT, int D>
 __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
     DevParams PV, PolarParams PP, const float* __restrict__ logits, int Hq, int nkv, int64_t ctx, int CH,
-    tq_packed_t V, float scale, float gate, float* __restrict__ part) {
+    tq_packed_t V, float scale, float gate, PageMap pm, float* __restrict__ part) {
   constexpr int NL = 1 << NB, NWD = D / 32, LD = D == 128 ? 7 : 8;
   constexpr int NO = D / 16, PS = kPvThreads / NO;  // threads per position, positions per step
   constexpr int NV = VQ ? 2 * D : D;  // values per partial record after (mx, l)
@@ -170,7 +175,8 @@ __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
   const int b = bk / nkv, kh = bk % nkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t t0 = static_cast<int64_t>(chunk) * CH;
-  const int n_in = static_cast<int>(min<int64_t>(CH, ctx - t0));
+  const int64_t ctx_v = pm.table ? max<int64_t>(0, min<int64_t>(pm.ctx_lens[b], ctx)) : ctx;
+  const int n_in = static_cast<int>(max<int64_t>(0, min<int64_t>(CH, ctx_v - t0)));
   float* wm = smem;
   float* gam = wm + GT * CH;
   float* wsum = gam + CH;  // [4 waves][GT][NV]
@@ -180,7 +186,6 @@ __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
     if (tid < 8) cent[tid] = PV.cent[tid];
   }
   // ---- scaled logits, chunk max and exp weights per query head
-  const int64_t row0 = static_cast<int64_t>(bk) * ctx + t0;
   const int lch = __builtin_ctz(CH);  // CH is a power of two
   float nv[4];
   {
@@ -195,8 +200,9 @@ __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tl = tid + kPvThreads * r;
-      nv[r] = tl < n_in ? V.norm[row0 + tl] : 0.f;
-      gv[r] = VQ && tl < n_in ? V.rnorm[row0 + tl] : 0.f;
+      const int64_t row = tl < n_in ? kv_row(pm, bk, nkv, ctx, t0 + tl) : 0;
+      nv[r] = tl < n_in ? V.norm[row] : 0.f;
+      gv[r] = VQ && tl < n_in ? V.rnorm[row] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
     for (int e = 0; e < 16; ++e) am[t][e] = aj[t][e] = 0.f;
   uint32_t cw[NB][NWD];
   uint32_t sw = 0u;
-  bool need = fetch_record<NB, VQ, GT, D>(V, row0, kq, n_in, CH, wm, gate, o, cw, sw);
+  bool need = fetch_record<NB, VQ, GT, D>(V, pm, bk, nkv, ctx, t0, kq, n_in, CH, wm, gate, o, cw, sw);
   for (int s0 = 0; s0 < n_in; s0 += PS) {
     const int tl = s0 + kq;
     uint32_t w[NB][NWD];
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(kPvThreads) void decode_from_logits_kernel(
       for (int i = 0; i < NWD; ++i) w[p][i] = cw[p][i];
     const bool have = need;
     const uint32_t sig = sw >> (16 * (o & 1));  // bit e: coordinate 16o + e
-    need = fetch_record<NB, VQ, GT, D>(V, row0, tl + PS, n_in, CH, wm, gate, o, cw, sw);
+    need = fetch_record<NB, VQ, GT, D>(V, pm, bk, nkv, ctx, t0, tl + PS, n_in, CH, wm, gate, o, cw, sw);
     if (have) {
       float y[16];
       if constexpr (VP) {
@@ -352,10 +358,6 @@ size_t align256p(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-size_t logits_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries);
-hipError_t launch_logits(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
-                         int n_kv_heads, int n_queries, tq_packed_t k, int64_t ctx, float* logits, void* ws,
-                         hipStream_t s);
 hipError_t launch_decode_combine_contig(const tq_codec_s* cv, const float* part, int batch, int n_q_heads,
                                         int n_kv_heads, int n_chunks, int chunk, void* out, tq_dtype_t out_dt,
                                         hipStream_t s);
@@ -372,27 +374,35 @@ static size_t polar_chunk_part_bytes(const tq_codec_s* cv, int batch, int n_q_he
   return static_cast<size_t>(batch) * n_q_heads * n_chunks * rec * sizeof(float);
 }
 
-// Workspace: the key scorer's own, the logits [batch][n_q_heads][ctx] fp32,
-// then the chunk partials.
+// Workspace: the key scorer's own (the larger of the contiguous and the paged
+// scorer's), the logits [batch][n_q_heads][ctx] fp32, then the chunk partials.
+static size_t scorer_ws_bytes(const tq_codec_s* ck, int batch, int n_q_heads, int n_kv_heads) {
+  size_t b = logits_ws_bytes(ck, batch, n_q_heads, n_kv_heads, 1);
+  if (logits_paged_supported(ck)) b = std::max(b, logits_paged_ws_bytes(ck, batch, n_q_heads, n_kv_heads, 1));
+  return align256p(b);
+}
+
 size_t decode_polar_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads, int n_kv_heads,
                              int64_t ctx, int CH) {
-  return align256p(logits_ws_bytes(ck, batch, n_q_heads, n_kv_heads, 1)) +
+  return scorer_ws_bytes(ck, batch, n_q_heads, n_kv_heads) +
          align256p(static_cast<size_t>(batch) * n_q_heads * ctx * sizeof(float)) +
          polar_chunk_part_bytes(cv, batch, n_q_heads, n_kv_heads, ctx, CH);
 }
 
 hipError_t launch_decode_polar(const tq_codec_s* ck, const tq_codec_s* cv, const void* q, tq_dtype_t q_dt,
                                int batch, int n_q_heads, int n_kv_heads, tq_packed_t k, tq_packed_t v, int64_t ctx,
-                               float scale, bool sparse_v, float v_gate, void* out, tq_dtype_t out_dt, void* ws,
-                               int CH, hipStream_t s) {
+                               float scale, bool sparse_v, float v_gate, const PageMap* pm, void* out,
+                               tq_dtype_t out_dt, void* ws, int CH, hipStream_t s) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   void* lws = p;
-  p += align256p(logits_ws_bytes(ck, batch, n_q_heads, n_kv_heads, 1));
+  p += scorer_ws_bytes(ck, batch, n_q_heads, n_kv_heads);
   float* logits = reinterpret_cast<float*>(p);
   p += align256p(static_cast<size_t>(batch) * n_q_heads * ctx * sizeof(float));
   float* part = reinterpret_cast<float*>(p);
-  hipError_t e = launch_logits(ck, q, q_dt, batch, n_q_heads, n_kv_heads, 1, k, ctx, logits, lws, s);
+  hipError_t e = pm ? launch_logits_paged(ck, q, q_dt, batch, n_q_heads, n_kv_heads, 1, k, ctx, *pm, logits, lws, s)
+                    : launch_logits(ck, q, q_dt, batch, n_q_heads, n_kv_heads, 1, k, ctx, logits, lws, s);
   if (e != hipSuccess) return e;
+  const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   const int G = n_q_heads / n_kv_heads;
   const int n_chunks = static_cast<int>(ceil_div(ctx, CH));
   const int GT = G == 1 ? 1 : G == 2 ? 2 : 4;  // query heads per block (grid z covers the rest)
@@ -405,10 +415,10 @@ hipError_t launch_decode_polar(const tq_codec_s* ck, const tq_codec_s* cv, const
     auto run = [&]<int H>() -> hipError_t {
       if (D == 128)
         hipLaunchKernelGGL((decode_from_logits_kernel<NB, VP, VQ, H, 128>), grid, dim3(kPvThreads), sh, s, cv->prm,
-                           cv->pol, logits, n_q_heads, n_kv_heads, ctx, CH, v, scale, gate, part);
+                           cv->pol, logits, n_q_heads, n_kv_heads, ctx, CH, v, scale, gate, pmv, part);
       else
         hipLaunchKernelGGL((decode_from_logits_kernel<NB, VP, VQ, H, 256>), grid, dim3(kPvThreads), sh, s, cv->prm,
-                           cv->pol, logits, n_q_heads, n_kv_heads, ctx, CH, v, scale, gate, part);
+                           cv->pol, logits, n_q_heads, n_kv_heads, ctx, CH, v, scale, gate, pmv, part);
       return hipGetLastError();
     };
     switch (GT) {

@@ -288,6 +288,15 @@ __host__ inline hipError_t dispatch_E(int d, F&& f) {
   }
 }
 
+// Row of position t of (sequence b, KV head kh), bk = b * nkv + kh:
+// [batch][kv_head][ctx] rows for a contiguous cache (pm.table null), else
+// through the page table.
+__device__ __forceinline__ int64_t kv_row(const PageMap& pm, int bk, int nkv, int64_t ctx, int64_t t) {
+  if (!pm.table) return static_cast<int64_t>(bk) * ctx + t;
+  const int page = pm.table[static_cast<int64_t>(bk / nkv) * pm.max_pages + t / pm.page_size];
+  return (static_cast<int64_t>(page) * nkv + bk % nkv) * pm.page_size + t % pm.page_size;
+}
+
 // f.template operator()<I>() for I = 0..N-1, I a constant expression in each
 // call (an unrolling that does not depend on the optimizer's size limits).
 template <int N, typename F>

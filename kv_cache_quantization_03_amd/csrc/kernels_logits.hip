@@ -127,24 +127,29 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW])
   }
 }
 
-// One key's record into registers (nothing past the context).
+// One key's record into registers (nothing past the sequence's context;
+// a paged cache looks the key's row up in the page table).
 template <int B, int NW>
-__device__ __forceinline__ void polar_fetch(const tq_packed_t& k, int64_t rowb, int64_t key, int64_t ctx,
-                                            uint32_t (&nc)[B][NW], uint32_t (&ns)[NW], float& nn, float& ng) {
-  if (key < ctx) {
+__device__ __forceinline__ void polar_fetch(const tq_packed_t& k, const PageMap& pm, int bk, int nkv, int64_t ctx,
+                                            int64_t ctx_v, int64_t key, uint32_t (&nc)[B][NW], uint32_t (&ns)[NW],
+                                            float& nn, float& ng) {
+  if (key < ctx_v) {
+    const int64_t row = kv_row(pm, bk, nkv, ctx, key);
 #pragma unroll
-    for (int p = 0; p < B; ++p) load_words<NW>(k.codes + (rowb + key) * (NW * B) + NW * p, nc[p]);
-    load_words<NW>(k.signs + (rowb + key) * NW, ns);
-    nn = k.norm[rowb + key];
-    ng = k.rnorm[rowb + key];
+    for (int p = 0; p < B; ++p) load_words<NW>(k.codes + row * (NW * B) + NW * p, nc[p]);
+    load_words<NW>(k.signs + row * NW, ns);
+    nn = k.norm[row];
+    ng = k.rnorm[row];
   }
 }
 
+// pm.table set (a paged cache): sequence b scores its first
+// min(ctx_lens[b], ctx) positions; ctx is the stride of the logits rows.
 template <int B, int LD>
 __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
                                                            const float* __restrict__ proj, int Hq, int nq, int G,
                                                            int nkv, int64_t ctx, tq_packed_t k,
-                                                           float* __restrict__ logits) {
+                                                           float* __restrict__ logits, PageMap pm) {
   constexpr int d = 1 << LD, NL = 1 << B, NW = d / 32, kPolarKeys = polar_keys<LD>();
   __shared__ float2 tab[LD][NL];      // (cos, sin) of every level's centroids
   __shared__ float psum[4];           // Σ_i p_i of each tile vector
@@ -156,6 +161,8 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
   __shared__ float4 q2tab[L2T ? d / 4 : 1][N3];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
+  const int64_t ctx_v = pm.table ? max<int64_t>(0, min<int64_t>(pm.ctx_lens[b], ctx)) : ctx;
+  if (static_cast<int64_t>(blockIdx.x) * kPolarKeys >= ctx_v) return;  // no key of this sequence for the block
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
   const float* qp[4];
   const float* pp[4];
@@ -219,13 +226,12 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
   __syncthreads();
   // blocks stride over the context's 1024-key blocks; each thread's next
   // record is loaded while the current one is scored
-  const int64_t nkb = (ctx + kPolarKeys - 1) / kPolarKeys;
-  const int64_t rowb = static_cast<int64_t>(bk) * ctx;
+  const int64_t nkb = (ctx_v + kPolarKeys - 1) / kPolarKeys;
   uint32_t nc[B][NW], ns[NW];
 #pragma unroll
   for (int i = 0; i < NW; ++i) ns[i] = 0u;
   float nn = 0.f, ng = 0.f;
-  polar_fetch<B, NW>(k, rowb, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, ctx, nc, ns, nn, ng);
+  polar_fetch<B, NW>(k, pm, bk, nkv, ctx, ctx_v, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, nc, ns, nn, ng);
   for (int64_t kb = blockIdx.x; kb < nkb; kb += gridDim.x) {
   const int64_t key = kb * kPolarKeys + tid;
   uint32_t w[B][NW], sw[NW];
@@ -236,8 +242,8 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
     sw[i] = ns[i];
   }
   const float nu = nn, ga = ng;
-  polar_fetch<B, NW>(k, rowb, key + static_cast<int64_t>(gridDim.x) * kPolarKeys, ctx, nc, ns, nn, ng);
-  if (key < ctx) {
+  polar_fetch<B, NW>(k, pm, bk, nkv, ctx, ctx_v, key + static_cast<int64_t>(gridDim.x) * kPolarKeys, nc, ns, nn, ng);
+  if (key < ctx_v) {
   auto code = [&](int slot) {  // slot is a constant after unrolling
     int c = 0;
 #pragma unroll
@@ -319,7 +325,9 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
 }
 
 hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
-                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s) {
+                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s,
+                               const PageMap* pm) {
+  const PageMap pmv = pm ? *pm : PageMap{nullptr, nullptr, 0, 0};
   const int64_t nv = static_cast<int64_t>(batch) * n_queries * n_q_heads;
   const float* qrot = static_cast<const float*>(ws);
   const float* proj = qrot + nv * c->prm.d;
@@ -332,7 +340,7 @@ hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, i
     const int64_t nkb = ceil_div(ctx, polar_keys<LD>());
     const dim3 grid(static_cast<unsigned>(std::min(nkb, per)), batch * n_kv_heads, static_cast<unsigned>(nz));
     hipLaunchKernelGGL((logits_polar_kernel<B, LD>), grid, dim3(polar_keys<LD>()), 0, s, c->prm, c->pol, qrot, proj,
-                       n_q_heads, n_queries, G, n_kv_heads, ctx, k, logits);
+                       n_q_heads, n_queries, G, n_kv_heads, ctx, k, logits, pmv);
     return hipGetLastError();
   };
   auto byd = [&]<int B>() -> hipError_t {
@@ -417,17 +425,26 @@ hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch,
 
 // Paged cache: the query operands, then the matrix-core scorer reading each
 // 64-key group from its page (per-sequence context lengths).
+// A polar codec (any head_dim it takes): its query prep, then the polar
+// scorer reading each key's row through the page table.
 bool logits_paged_supported(const tq_codec_s* c) {
-  return !c->polar && c->qjl && (c->prm.d == 128 || c->prm.d == 256) && c->prm.m == c->prm.d;
+  if (c->polar) return true;
+  return c->qjl && (c->prm.d == 128 || c->prm.d == 256) && c->prm.m == c->prm.d;
 }
 
 size_t logits_paged_ws_bytes(const tq_codec_s* c, int batch, int n_q_heads, int n_kv_heads, int n_queries) {
+  if (c->polar) return logits_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
   return logits_mfma_ws_bytes(c, batch, n_q_heads, n_kv_heads, n_queries);
 }
 
 hipError_t launch_logits_paged(const tq_codec_s* c, const void* q, tq_dtype_t dt, int batch, int n_q_heads,
                                int n_kv_heads, int n_queries, tq_packed_t k, int64_t max_ctx, const PageMap& pm,
                                float* logits, void* ws, hipStream_t s) {
+  if (c->polar) {
+    hipError_t e = launch_logits_prep(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_logits_polar(c, ws, batch, n_q_heads, n_kv_heads, n_queries, k, max_ctx, logits, s, &pm);
+  }
   // one launch where the fused kernel takes the shape (its records through the page table)
   if (logits_fused_eligible(c, batch, n_q_heads, n_kv_heads, n_queries, max_ctx))
     return launch_logits_fused(c, q, dt, batch, n_q_heads, n_kv_heads, n_queries, k, max_ctx, logits, s, &pm);

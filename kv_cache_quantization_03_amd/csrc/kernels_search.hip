@@ -17,8 +17,6 @@ hipError_t launch_search_mfma_prep(const tq_codec_s* c, const float* qrot, const
                                    hipStream_t s);
 hipError_t launch_search_mfma_scores(const tq_codec_s* c, const void* prep, int nq, tq_packed_t db, int64_t n,
                                      float* scores, int64_t ld, hipStream_t s);
-hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
-                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
 
 // A polar codec's scores come from the polar scorer (the queries as the query
 // heads of one KV head); the matrix-core search scorer reads per-coordinate codes.

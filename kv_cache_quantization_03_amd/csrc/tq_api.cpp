@@ -258,7 +258,6 @@ tq_status_t decode_common(tq_codec_t ck, tq_codec_t cv, const void* q, tq_dtype_
   if (!ck || !cv) { set_error("codec is NULL"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->prm.d != cv->prm.d) { set_error("K and V codecs must share head_dim"); return TQ_ERROR_INVALID_VALUE; }
   if (ck->polar || cv->polar) {
-    if (pm) { set_error("paged decode takes codecs with the per-coordinate first stage"); return TQ_ERROR_NOT_SUPPORTED; }
     if (!tq::decode_polar_shape_ok(ck, cv)) {
       set_error("decode attention with a polar codec needs head_dim 128 or 256 (the same for K and V), qjl_dim equal "
                 "to head_dim and V in row records");
@@ -449,7 +448,8 @@ extern "C" tq_status_t tq_attn_logits_paged(tq_codec_t c, const void* q, tq_dtyp
   if ((st = need_qjl(c, "tq_attn_logits_paged")) != TQ_SUCCESS) return st;
   if ((st = need_rows(c, "tq_attn_logits_paged")) != TQ_SUCCESS) return st;
   if (!tq::logits_paged_supported(c)) {
-    set_error("paged logits need a per-coordinate codec with head_dim 128 or 256 and qjl_dim = head_dim");
+    set_error("paged logits need a polar codec, or a per-coordinate codec with head_dim 128 or 256 and qjl_dim = "
+              "head_dim");
     return TQ_ERROR_NOT_SUPPORTED;
   }
   if ((st = check_heads(batch, n_q_heads, n_kv_heads)) != TQ_SUCCESS) return st;

@@ -152,6 +152,11 @@ hipError_t launch_logits_prep(const tq_codec_s* c, const void* q, tq_dtype_t dt,
                               int n_kv_heads, int n_queries, void* ws, hipStream_t s);
 hipError_t launch_logits_prepped(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
                                  int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s);
+// The polar scorer on prepped queries; pm set: a paged cache (ctx: the
+// largest context and the logits row stride).
+hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, int n_q_heads, int n_kv_heads,
+                               int n_queries, tq_packed_t k, int64_t ctx, float* logits, hipStream_t s,
+                               const PageMap* pm = nullptr);
 
 bool decode_supported(const tq_codec_s* cv, int n_q_heads, int n_kv_heads, int64_t ctx, const char** why);
 size_t decode_ws_bytes(const tq_codec_s* ck, const tq_codec_s* cv, int batch, int n_q_heads,
@@ -165,7 +170,7 @@ hipError_t launch_decode(const tq_codec_s* ck, const tq_codec_s* cv, const void*
                          tq_dtype_t out_dt, void* ws, hipStream_t s);
 bool decode_paged_supported(const tq_codec_s* ck, const tq_codec_s* cv, int n_q_heads, int n_kv_heads);
 // Either codec polar (the logits by the key scorer, then V from them): d = m =
-// 128 and V in row records.
+// 128 or 256, the same for K and V, and V in row records.
 bool decode_polar_shape_ok(const tq_codec_s* ck, const tq_codec_s* cv);
 
 size_t append_paged_ws_bytes(const tq_codec_s* c, int64_t n_rec);

@@ -198,3 +198,18 @@ def polar_records_like(pc: O.PolarCodec, x64: np.ndarray, gpu: dict) -> dict:
     nu = np.sqrt(np.sum(np.asarray(x64, np.float64) ** 2, axis=1)).astype(np.float32)
     return {"codes": np.asarray(gpu["codes"]).copy(), "signs": np.asarray(gpu["signs"]).copy(), "norm": nu,
             "rnorm": rd["rnorm"]}
+
+
+def fill_pages(rec_by_seq, page_table, hkv, P, n_pages, junk):
+    """A numpy cache with sequence b's records (rows [kv_head][position]) at
+    their page slots; every other row holds a junk record."""
+    cache = {k: np.asarray(junk[k])[np.arange(n_pages * hkv * P) % len(junk["norm"])].copy()
+             for k in ("codes", "signs", "norm", "rnorm")}
+    for b, rec in enumerate(rec_by_seq):
+        n = len(rec["norm"]) // hkv
+        for kh in range(hkv):
+            for t in range(n):
+                row = O.paged_row(page_table, b, kh, t, hkv, P)
+                for k in cache:
+                    cache[k][row] = np.asarray(rec[k])[kh * n + t]
+    return cache

@@ -13,6 +13,7 @@ import pytest
 import oracle as O
 from tests.parity import (assert_sparse_v_close, assert_sparse_v_within_plain_rule, check_encode, check_polar_encode, oracle_records_like,
                           polar_records_like, row_rel_err, tol_for)
+from tests.parity import fill_pages as _fill_pages
 
 pytestmark = pytest.mark.gpu
 
@@ -558,21 +559,6 @@ def test_decode_sparse_v_rejects_bad_gate(B):
 
 
 # ---------------------------------------------------------------- paged cache
-def _fill_pages(rec_by_seq, page_table, hkv, P, n_pages, junk):
-    """A numpy cache with sequence b's records (rows [kv_head][position]) at
-    their page slots; every other row holds a junk record."""
-    cache = {k: np.asarray(junk[k])[np.arange(n_pages * hkv * P) % len(junk["norm"])].copy()
-             for k in ("codes", "signs", "norm", "rnorm")}
-    for b, rec in enumerate(rec_by_seq):
-        n = len(rec["norm"]) // hkv
-        for kh in range(hkv):
-            for t in range(n):
-                row = O.paged_row(page_table, b, kh, t, hkv, P)
-                for k in cache:
-                    cache[k][row] = np.asarray(rec[k])[kh * n + t]
-    return cache
-
-
 @pytest.mark.parametrize("vmse", [False, True])
 def test_append_paged_matches_contiguous_encode(B, vmse):
     # tokens appended step by step (and one 70-token prefill) land at their page
@@ -801,16 +787,14 @@ def test_logits_paged_identity_equals_contiguous(B):
     pt = torch.arange(3, dtype=torch.int32, device="cuda").view(1, 3)
     b = B.tq_attn_logits_paged(gc, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
     assert torch.equal(a, b)
-    # refused: page sizes that are not multiples of 128, max_ctx past the table, polar and MSE-only codecs
+    # refused: page sizes that are not multiples of 128, max_ctx past the table, MSE-only codecs (polar codecs
+    # are accepted: tests/test_gpu_polar_decode.py)
     for bad in ((100, ctx), (P, 3 * P + 1)):
         with pytest.raises(B.TQError):
             B.tq_attn_logits_paged(gc, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, *bad, 1)
     gv, _ = mse_pair(B, 128, 3)
     with pytest.raises(B.TQError):
         B.tq_attn_logits_paged(gv, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
-    gp, _ = polar_pair(B, 3)
-    with pytest.raises(B.TQError):
-        B.tq_attn_logits_paged(gp, q, kp, torch.tensor([ctx], dtype=torch.int32, device="cuda"), pt, P, ctx, 1)
 
 
 def _paged_pool(B, gc, seed, batch, hkv, P, max_pages, spare=2):
@@ -1067,11 +1051,8 @@ def test_polar_codec_limits(B):
             B.tq_codec_create_polar(d, 3)
     with pytest.raises(B.TQError):
         B.tq_codec_create_polar(128, 3, 64)  # the QJL dimension is head_dim
-    kp = B.alloc_packed(gc, 256)
-    with pytest.raises(B.TQError):  # paged logits read per-coordinate codes only
-        B.tq_attn_logits_paged(gc, torch.zeros((1, 1, 4, 128), device="cuda"), kp,
-                               torch.tensor([100], dtype=torch.int32, device="cuda"),
-                               torch.zeros((1, 2), dtype=torch.int32, device="cuda"), 128, 256, 1)
+    with pytest.raises(B.TQError):
+        B.tq_codec_create_polar(128, 5)
 
 
 # ---------------------------------------------------------------- search

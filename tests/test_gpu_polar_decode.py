@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import oracle as O
-from tests.parity import assert_sparse_v_close, assert_sparse_v_within_plain_rule, polar_records_like, row_rel_err
+from tests.parity import (assert_sparse_v_close, assert_sparse_v_within_plain_rule, fill_pages, polar_records_like,
+                          row_rel_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,16 +199,15 @@ def test_polar_decode_batch_and_workspace(B):
 
 def test_polar_decode_refusals(B):
     gk, _ = codec(B, "polar", 3, 1234)
-    gs, _ = codec(B, "scalar", 3, 1234)
     q = torch.zeros((1, 4, 128), device="cuda")
     kp = B.alloc_packed(gk, 256)
-    # paged caches take per-coordinate codecs only
+    # paged calls: page_size a multiple of 128, as for the other codecs
     cl = torch.tensor([100], dtype=torch.int32, device="cuda")
-    pt = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
+    pt = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
     with pytest.raises(B.TQError):
-        B.tq_decode_attn_paged(gk, gk, q, kp, kp, cl, pt, 256, 256, 1, 0.1)
+        B.tq_decode_attn_paged(gk, gk, q, kp, kp, cl, pt, 64, 128, 1, 0.1)
     with pytest.raises(B.TQError):
-        B.tq_decode_attn_paged(gs, gk, q, B.alloc_packed(gs, 256), kp, cl, pt, 256, 256, 1, 0.1)
+        B.tq_attn_logits_paged(gk, torch.zeros((1, 1, 4, 128), device="cuda"), kp, cl, pt, 64, 128, 1)
     # a value cache in 32-row blocks is read by the matrix-core kernel only
     gvb = B.tq_codec_create_vblock(128, 3, False, 1234)
     with pytest.raises(B.TQError):
@@ -254,3 +254,124 @@ def test_polar_search_parity(B, bits, n_db, nq, k, d):
     if k >= 3:
         row = list(idx[0])
         assert row.index(4) < row.index(10) < row.index(n_db - 1)
+
+
+# ---------------------------------------------------------------- paged caches with polar codecs
+def _page_table(rng, batch, max_pages):
+    n_pages = batch * max_pages + 3
+    return rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32), n_pages
+
+
+def _pool(rng, oc, ctxs, hkv, P, pt, n_pages, d):
+    """Records of random rows for each sequence at their page slots, junk records elsewhere."""
+    recs = [encode(oc, rng.standard_normal((hkv * n, d))) if n else None for n in ctxs]
+    junk = encode(oc, rng.standard_normal((50, d)))
+    empty = {k: np.asarray(junk[k])[:0] for k in junk}
+    return fill_pages([r if r is not None else empty for r in recs], pt, hkv, P, n_pages, junk)
+
+
+@pytest.mark.parametrize("kk,kbits,vk,vbits,gate,hq,d", [
+    ("polar", 3, "polar", 3, 0.0, 8, 128),
+    ("scalar", 3, "polar", 3, 0.0, 8, 128),    # per-coordinate K through the paged matrix-core scorer
+    ("polar", 3, "mse", 3, 0.0, 8, 128),
+    ("polar", 4, "scalar", 3, 0.0, 16, 128),   # 8 query heads per KV head: 512-position chunks
+    ("polar", 3, "polar", 3, 1e-3, 8, 128),    # Sparse V
+    ("polar", 3, "polar", 2, 0.0, 4, 256),
+])
+def test_polar_decode_paged_parity(B, kk, kbits, vk, vbits, gate, hq, d):
+    # four sequences (a ragged one, one position, none, the whole page table)
+    # in shuffled pages with junk elsewhere; each against the oracle's decode
+    # over its own rows
+    say(f"paged polar decode K {kk}{kbits} V {vk}{vbits} gate={gate} hq={hq} d={d}")
+    gk, ok = codec(B, kk, kbits, 1234, d)
+    gv, ov = codec(B, vk, vbits, 4321, d)
+    hkv, P, max_pages = 2, 256, 8
+    ctxs = [1500, 1, 0, max_pages * P]
+    rng = np.random.default_rng(81 + kbits + hq + d)
+    pt, n_pages = _page_table(rng, len(ctxs), max_pages)
+    kc = _pool(rng, ok, ctxs, hkv, P, pt, n_pages, d)
+    vc = _pool(rng, ov, ctxs, hkv, P, pt, n_pages, d)
+    q = exact((3.0 if gate else 1.0) * rng.standard_normal((len(ctxs), hq, d)), "f32")
+    scale = 1 / math.sqrt(d)
+    out = B.tq_decode_attn_paged(gk, gv, to_dev(q, "f32"), B.packed_from_numpy(kc), B.packed_from_numpy(vc),
+                                 torch.tensor(ctxs, dtype=torch.int32, device="cuda"), torch.from_numpy(pt).cuda(), P,
+                                 max(ctxs), hkv, scale, gate, out_dtype=torch.float32).cpu().numpy()
+    assert np.all(out[2] == 0)  # the empty context
+    for b, n in enumerate(ctxs):
+        if n == 0:
+            continue
+        kr = O.gather_paged(kc, pt, b, hkv, n, P)
+        vr = O.gather_paged(vc, pt, b, hkv, n, P)
+        if gate == 0:
+            ref = O.decode_attn_accumulated(ok, ov, q[b:b + 1].astype(np.float64), kr, vr, 1, hq, hkv, n, scale)
+            err = row_rel_err(out[b:b + 1], ref).max()
+            say(f"  sequence {b} (ctx {n}): max row err {err:.2e}")
+            assert err <= 1e-4
+        else:
+            ref, keep, local = O.decode_attn_sparse_v(ok, ov, q[b:b + 1].astype(np.float64), kr, vr, 1, hq, hkv,
+                                                      n, scale, gate, B.tq_decode_attn_chunk(hq, hkv))
+            say(f"  sequence {b} (ctx {n}): dropped {np.mean(~keep):.3f}")
+            assert_sparse_v_close(out[b:b + 1], ref, local, gate, O.dequantize(ov, vr), hkv, n, 1e-4)
+
+
+@pytest.mark.parametrize("d,bits,hq,hkv,nq,P", [(128, 3, 8, 2, 1, 256), (64, 2, 4, 4, 3, 128), (256, 4, 8, 2, 2, 384)])
+def test_polar_logits_paged_parity(B, d, bits, hq, hkv, nq, P):
+    # a ragged sequence, one key, none and a full page table; logits past a
+    # sequence's length stay untouched
+    say(f"paged polar logits d={d} bits={bits} hq={hq} hkv={hkv} nq={nq} P={P}")
+    gc, pc = codec(B, "polar", bits, 1234, d)
+    max_pages = 4
+    max_ctx = max_pages * P
+    ctxs = [2 * max_ctx // 3 + 3, 1, 0, max_ctx]
+    rng = np.random.default_rng(83 + d + bits)
+    pt, n_pages = _page_table(rng, len(ctxs), max_pages)
+    kc = _pool(rng, pc, ctxs, hkv, P, pt, n_pages, d)
+    q = exact(rng.standard_normal((len(ctxs), nq, hq, d)), "f32")
+    out = torch.full((len(ctxs), hq, nq, max_ctx), 7.0, device="cuda")
+    B.tq_attn_logits_paged(gc, to_dev(q, "f32"), B.packed_from_numpy(kc),
+                           torch.tensor(ctxs, dtype=torch.int32, device="cuda"), torch.from_numpy(pt).cuda(), P,
+                           max_ctx, hkv, logits=out)
+    g = out.cpu().numpy()
+    G = hq // hkv
+    for b, n in enumerate(ctxs):
+        assert np.all(g[b, :, :, n:] == 7.0)
+        if n == 0:
+            continue
+        kr = O.gather_paged(kc, pt, b, hkv, n, P)
+        worst = 0.0
+        for kh in range(hkv):
+            rows = slice(kh * n, (kh + 1) * n)
+            qv = q[b, :, kh * G:(kh + 1) * G].transpose(1, 0, 2).reshape(G * nq, d)
+            ref = O.polar_score(pc, qv.astype(np.float64), {k: kr[k][rows] for k in kr})
+            worst = max(worst, row_rel_err(g[b, kh * G:(kh + 1) * G, :, :n].reshape(G * nq, n), ref).max())
+        say(f"  sequence {b} (ctx {n}): max row err {worst:.2e}")
+        assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_polar_append_paged_matches_contiguous_encode(B, d):
+    # polar records appended into pages (one token, then a 70-token block) are
+    # exactly those of a contiguous encode of the same rows
+    gc, _ = codec(B, "polar", 3, 1234, d)
+    batch, hkv, P, max_pages, n_pages = 2, 2, 128, 3, 8
+    rng = np.random.default_rng(84 + d)
+    pt = rng.permutation(n_pages)[:batch * max_pages].reshape(batch, max_pages).astype(np.int32)
+    ctx0 = np.array([3, 200], dtype=np.int32)
+    xs = [exact(rng.standard_normal((batch, hkv, n, d)), "bf16") for n in (1, 70)]
+    cache = B.alloc_packed(gc, n_pages * hkv * P)
+    ctx = torch.from_numpy(ctx0.copy()).cuda()
+    ptd = torch.from_numpy(pt).cuda()
+    for x in xs:
+        B.tq_encode_append_paged(gc, to_dev(x, "bf16"), ctx, ptd, P, n_pages, cache)
+        ctx += x.shape[2]
+    torch.cuda.synchronize()
+    got = cache.numpy()
+    allx = np.concatenate(xs, axis=2)
+    ref = B.tq_encode_kv(gc, to_dev(allx.reshape(-1, d), "bf16"))[0].numpy()
+    for b in range(batch):
+        for kh in range(hkv):
+            for t in range(allx.shape[2]):
+                row = O.paged_row(pt, b, kh, int(ctx0[b]) + t, hkv, P)
+                i = (b * hkv + kh) * allx.shape[2] + t
+                for k in got:
+                    assert np.array_equal(got[k][row], ref[k][i]), (b, kh, t, k)
