@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(const T* __restrict__ x, in
   float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) v[e] = load_elem(x + vec * d, e * kWave + lane) * Dsign[e * kWave + lane];
-  hadamard_wave<E>(v, lane);
+  hadamard_wave<E, false, true>(v, lane);
 #pragma unroll
   for (int e = 0; e < E; ++e) out[vec * d + e * kWave + lane] = v[e] * inv_sqrt_d;
 }

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void attn_prep_mfma_kernel(const T* __restrict
       qr[wv][e * kWave + lane] = v[e];
       v[e] *= Dsign[e * kWave + lane];
     }
-    hadamard_wave<E>(v, lane);
+    hadamard_wave<E, false, true>(v, lane);
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {

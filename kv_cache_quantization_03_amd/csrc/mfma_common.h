@@ -419,7 +419,7 @@ __device__ __forceinline__ void query_prep_build(QueryPrepShared<NT, NKB>& sh, c
     float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) v[e] = sh.qs[wv][e * kWave + lane];
-    hadamard_wave<2>(v, lane);
+    hadamard_wave<2, false, true>(v, lane);
 #pragma unroll
     for (int e = 0; e < 2; ++e) sh.qs[wv][e * kWave + lane] = v[e] * P.inv_sqrt_d;
   }
