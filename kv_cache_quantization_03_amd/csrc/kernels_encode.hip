@@ -475,17 +475,20 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 // ----------------------------------------------------------------------------
 // Rotate + recursive polar quantize (「谷歌 TurboQuant 深度拆解」 第二部分
 // PolarQuant) for d = 64 and 256, the split encode's first step (d = 128 has
-// the fused kernel above): one wavefront per vector, lane holding coordinates
-// e*64 + lane.  Level l (1..log2 d) pairs the two children of each node, whose
-// coordinates differ in bit l-1: lanes lane ^ 2^(l-1) for l <= 6, registers
-// e ^ 2^(l-7) above; both members of a pair compute the same angle from the
-// same two values (level 1: atan2(y_2n+1, y_2n) taken into [0, 2π); above:
+// the fused kernel above): one wavefront per vector, lane holding the E
+// consecutive coordinates E*lane .. E*lane + E-1.  Level l (1..log2 d) pairs
+// the two children of each node, whose coordinates differ in bit l-1: the
+// lane's registers for l <= log2 E (each angle once), lanes lane ^
+// 2^(l-1-log2 E) above (both lanes of a pair compute the same angle from the
+// same two radii).  Level 1: atan2(y_2n+1, y_2n) taken into [0, 2π); above:
 // atan2 of the two child radii, in [0, π/2]; code = #{level boundaries below
-// the angle}).  ŷ_j is the fp32 product, top-down from radius 1, of cos or sin
-// (bit l-1 of j) of level l's centroid at node j >> l.  The codes reach their
-// slots (level l: d - 2d/2^l + node; slot d-1 holds 0) through LDS and are
-// packed as bit-planes like the per-coordinate codes; the residual y - ŷ, γ
-// and ν leave as in encode_rq_kernel.
+// the angle}.  The rotation's butterflies run over the register bits, then the
+// lane bits (the Sylvester matrix is a product over coordinate bits, so the
+// order is free).  ŷ_j is the fp32 product, top-down from radius 1, of cos or
+// sin (bit l-1 of j) of level l's centroid at node j >> l.  The codes reach
+// their slots (level l: d - 2d/2^l + node; slot d-1 holds 0) through LDS and
+// are packed as bit-planes like the per-coordinate codes; the residual y - ŷ,
+// γ and ν leave as in encode_rq_kernel.
 template <int E, typename T, int RM, int B>
 __global__ __launch_bounds__(256) void encode_polar_rq_kernel(const T* __restrict__ x, int64_t n, DevParams P,
                                                               PolarParams PP, const float* __restrict__ Dsign,
@@ -494,7 +497,8 @@ __global__ __launch_bounds__(256) void encode_polar_rq_kernel(const T* __restric
                                                               float rscale) {
   static_assert(E == 1 || E == 2 || E == 4, "d = 64, 128 or 256");
   constexpr int d = E * kWave, NL = 1 << B;
-  constexpr int LV = E == 1 ? 6 : (E == 2 ? 7 : 8);  // log2 d
+  constexpr int RL = E == 1 ? 0 : (E == 2 ? 1 : 2);  // levels inside a lane's registers
+  constexpr int LV = 6 + RL;                          // log2 d
   __shared__ float2 tab[LV][NL];    // (cos, sin) of every level's centroids
   __shared__ uint8_t pcode[4][d];   // each wave's codes by slot
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x >> 6;
@@ -503,84 +507,92 @@ __global__ __launch_bounds__(256) void encode_polar_rq_kernel(const T* __restric
   __syncthreads();
   const int64_t vec = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   if (vec >= n) return;  // wave-uniform
-  const T* xr = x + vec * d;
+  const T* xr = x + vec * d + E * lane;
   float v[E];
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    v[e] = load_elem(xr, e * kWave + lane);
+    v[e] = load_elem(xr, e);
     ss = fmaf(v[e], v[e], ss);
   }
   ss = wave_sum(ss);
   const float nu = sqrtf(ss);
   const float inv = nu > 0.f ? 1.0f / nu : 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) v[e] *= inv * Dsign[e * kWave + lane];
-  hadamard_wave<E, false, true>(v, lane);
-  float y[E], rad[E];
-  int code[LV][E];  // level l's code at the node of coordinate e*64 + lane
+  for (int e = 0; e < E; ++e) v[e] *= inv * Dsign[E * lane + e];
+  fwht_regs<E>(v);
+  fwht_lanes_dpp<E>(v, lane);
+  float y[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) y[e] = v[e] * P.inv_sqrt_d;
-  static_for<6>([&]<int k>() {  // level k + 1: partner lane ^ 2^k
-    const bool hi = (lane >> k) & 1;
+  // register levels: node u of level l holds registers [u 2^l, (u+1) 2^l)
+  int creg[RL > 0 ? RL : 1][E > 1 ? E / 2 : 1];
+  float rad[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float mine = k == 0 ? y[e] : rad[e];
-      const float o = __shfl_xor(mine, 1 << k, kWave);
-      const float a = hi ? o : mine, b = hi ? mine : o;
+  for (int e = 0; e < E; ++e) rad[e] = y[e];
+  static_for<RL>([&]<int k>() {  // level k + 1
+    constexpr int W = 1 << k;     // child spacing in registers
+#pragma unroll
+    for (int u = 0; u < E / (2 * W); ++u) {
+      const float a = rad[2 * W * u], b = rad[2 * W * u + W];
       float th = atan2f(b, a);
       if constexpr (k == 0) th = th < 0.f ? th + 6.28318530717958647f : th;
-      code[k][e] = polar_code<NL>(PP.bound[k], th);
-      rad[e] = sqrtf(a * a + b * b);
+      creg[k][u] = polar_code<NL>(PP.bound[k], th);
+      rad[2 * W * u] = sqrtf(a * a + b * b);
     }
   });
-  if constexpr (LV >= 7) {  // level 7: registers e, e + 1
-#pragma unroll
-    for (int e = 0; e < E; e += 2) {
-      const float a = rad[e], b = rad[e + 1];
-      code[6][e] = code[6][e + 1] = polar_code<NL>(PP.bound[6], atan2f(b, a));
-      rad[e] = rad[e + 1] = sqrtf(a * a + b * b);
-    }
-  }
-  if constexpr (LV >= 8) {  // level 8: registers e, e + 2
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const int c = polar_code<NL>(PP.bound[7], atan2f(rad[e + 2], rad[e]));
-#pragma unroll
-      for (int u = 0; u < 4; ++u) code[7][e + u] = c;
-    }
+  // lane levels: the lane's node radius in rad[0]
+  int clane[6];
+  {
+    float r = rad[0];
+    static_for<6>([&]<int k>() {  // level RL + k + 1: partner lane ^ 2^k
+      const bool hi = (lane >> k) & 1;
+      const float o = __shfl_xor(r, 1 << k, kWave);
+      const float a = hi ? o : r, b = hi ? r : o;
+      float th = atan2f(b, a);
+      if constexpr (RL + k == 0) th = th < 0.f ? th + 6.28318530717958647f : th;
+      clane[k] = polar_code<NL>(PP.bound[RL + k], th);
+      r = sqrtf(a * a + b * b);
+    });
   }
   // each node's code from the member holding its first coordinate
-  static_for<LV>([&]<int k>() {
+  static_for<RL>([&]<int k>() {
     constexpr int l = k + 1, base = d - ((2 * d) >> l);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = e * kWave + lane;
-      if ((j & ((1 << l) - 1)) == 0) pcode[wv][base + (j >> l)] = static_cast<uint8_t>(code[k][e]);
-    }
+    for (int u = 0; u < E / (2 << k); ++u)
+      pcode[wv][base + ((E * lane + (2 << k) * u) >> l)] = static_cast<uint8_t>(creg[k][u]);
+  });
+  static_for<6>([&]<int k>() {
+    constexpr int l = RL + k + 1, base = d - ((2 * d) >> l);
+    if (((E * lane) & ((1 << l) - 1)) == 0) pcode[wv][base + ((E * lane) >> l)] = static_cast<uint8_t>(clane[k]);
   });
   if (lane == 0) pcode[wv][d - 1] = 0;
-  // ŷ top-down from radius 1, residual
+  // ŷ top-down from radius 1: the lane levels, then the register levels
+  float R = 1.f;
+  static_for<6>([&]<int k>() {
+    constexpr int kk = 5 - k, l = RL + kk + 1;  // level l = LV down to RL + 1
+    const float2 f = tab[l - 1][clane[kk]];
+    R *= (((E * lane) >> (l - 1)) & 1) ? f.y : f.x;
+  });
   float rs = 0.f;
   float* rr = rbuf + vec * d;
   _Float16* rh = reinterpret_cast<_Float16*>(rbuf) + vec * 2 * d;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = e * kWave + lane;
-    float R = 1.f;
-    static_for<LV>([&]<int k>() {
-      constexpr int l = LV - k;
-      const float2 f = tab[l - 1][code[l - 1][e]];
-      R *= ((j >> (l - 1)) & 1) ? f.y : f.x;
+    float Re = R;
+    static_for<RL>([&]<int k>() {
+      constexpr int kk = RL - 1 - k, l = kk + 1;  // level l = RL down to 1
+      const float2 f = tab[l - 1][creg[kk][e >> l]];
+      Re *= ((e >> (l - 1)) & 1) ? f.y : f.x;
     });
-    const float r = y[e] - R;
+    const float r = y[e] - Re;
     if constexpr (RM == kResF16) {
       const float rsc = r * rscale;
       const _Float16 hi = static_cast<_Float16>(rsc);
-      rh[e * kWave + lane] = hi;
-      rh[d + e * kWave + lane] = static_cast<_Float16>(rsc - static_cast<float>(hi));
+      rh[E * lane + e] = hi;
+      rh[d + E * lane + e] = static_cast<_Float16>(rsc - static_cast<float>(hi));
     } else if constexpr (RM == kResF32) {
-      rr[e * kWave + lane] = r;
+      rr[E * lane + e] = r;
     }
     rs = fmaf(r, r, rs);
   }
