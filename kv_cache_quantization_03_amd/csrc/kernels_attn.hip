@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DevParams 
     float v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = osh[e * kWave + lane];
-    hadamard_wave<E, true, true>(v, lane);
+    hadamard_wave<E, true>(v, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int j = e * kWave + lane;
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine128_kernel(DevPara
       }
       v[e] = (osh[jo] + PV.qjl_kappa * t) * inv_l;
     }
-    hadamard_wave<2, true, true>(v, tid);
+    hadamard_wave<2, true>(v, tid);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int jo = e * kWave + tid;
