@@ -192,9 +192,15 @@ def main():
         vbd = B.tq_encode_kv(cvb, kd)[0]
         for _ in range(5):
             B.tq_decode_attn(cdc, cvb, qd, kpd, vbd, 131072, 8, 1 / math.sqrt(d), out=outd)
+        del vbd
+        # and 5 with PolarQuant K and V records of the same keys (the polar scorer, then the value kernel)
+        cpo = B.tq_codec_create_polar(d, 3, 0, I.CODEC_SEED)
+        kpo = B.tq_encode_kv(cpo, kd)[0]
+        for _ in range(5):
+            B.tq_decode_attn(cpo, cpo, qd, kpo, kpo, 131072, 8, 1 / math.sqrt(d), out=outd)
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": True, "logits_launches": 20, "copy_bytes": 64 * 2 ** 20, "copies": 5,
-                          "decode_launches": 10, "encode_launches": 4}))
+                          "decode_launches": 15, "encode_launches": 5}))
         return
 
     # ---- the timed steps run as one HIP graph (no host launch cost per step)
