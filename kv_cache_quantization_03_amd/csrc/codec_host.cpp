@@ -415,6 +415,10 @@ tq_status_t codec_create(int32_t head_dim, int32_t bits, int32_t qjl_dim, uint64
         pp.cosc[l][k] = in ? static_cast<float>(std::cos(c->host.pcent[l][k])) : 0.f;
         pp.sinc[l][k] = in ? static_cast<float>(std::sin(c->host.pcent[l][k])) : 0.f;
         pp.bound[l][k] = in && k + 1 < pp.nl ? static_cast<float>(c->host.pbound[l][k]) : INFINITY;
+        const double bt = in && k + 1 < pp.nl ? c->host.pbound[l][k] : 0.0;
+        const double cb = std::cos(bt), sb = std::sin(bt);
+        pp.bcs[l][k] = l == 0 ? float2{static_cast<float>(cb), static_cast<float>(sb)}
+                              : float2{static_cast<float>(cb * cb), static_cast<float>(sb * sb)};
       }
   }
   const auto& h = c->host;

@@ -237,12 +237,30 @@ __global__ __launch_bounds__(256) void sproj_kernel(const float* __restrict__ A,
 typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int kEncPasses = 8;
 
-// Code of an angle: #{boundaries of its level below th} (ties low).
+// Angle codes, #{boundaries β of the level below θ} (ties low), decided
+// without forming θ.
+// Level 1, θ = atan2(b, a) taken into [0, 2π) for the pair (a, b): sin(θ - β)
+// has the sign of b cos β - a sin β, and θ > β holds iff θ lies in the later
+// half-turn (θ >= π > β) or in β's half-turn with sin(θ - β) > 0.
 template <int NL>
-__device__ __forceinline__ int polar_code(const float (&bound)[16], float th) {
+__device__ __forceinline__ int polar_code_l1(const PolarParams& PP, float a, float b) {
+  const bool up = b < 0.f || (b == 0.f && a < 0.f);  // θ in [π, 2π)
   int c = 0;
 #pragma unroll
-  for (int k = 0; k + 1 < NL; ++k) c += bound[k] < th;
+  for (int k = 0; k + 1 < NL; ++k) {
+    const float2 t = PP.bcs[0][k];
+    const bool pos = fmaf(b, t.x, -(a * t.y)) > 0.f;
+    c += PP.bound[0][k] < 3.14159265358979324f ? (up || pos) : (up && pos);
+  }
+  return c;
+}
+// Upper levels, θ = atan2(√rb2, √ra2) in [0, π/2] from the children's squared
+// radii; the boundaries lie inside (0, π/2), where θ > β iff rb2 cos²β > ra2 sin²β.
+template <int NL>
+__device__ __forceinline__ int polar_code_up(const float2 (&t)[16], float ra2, float rb2) {
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k + 1 < NL; ++k) c += fmaf(rb2, t[k].x, -(ra2 * t[k].y)) > 0.f;
   return c;
 }
 
@@ -338,29 +356,27 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = v[e] * kscale;
       int c1[4], c2[2];
-      float r1[4], r2[2];
+      float r1[4], r2[2];  // squared radii
 #pragma unroll
       for (int i = 0; i < 4; ++i) {  // level 1: angles in [0, 2π)
-        float th = atan2f(y[2 * i + 1], y[2 * i]);
-        th = th < 0.f ? th + 6.28318530717958647f : th;
-        c1[i] = polar_code<NL>(PP.bound[0], th);
-        r1[i] = sqrtf(y[2 * i] * y[2 * i] + y[2 * i + 1] * y[2 * i + 1]);
+        c1[i] = polar_code_l1<NL>(PP, y[2 * i], y[2 * i + 1]);
+        r1[i] = fmaf(y[2 * i], y[2 * i], y[2 * i + 1] * y[2 * i + 1]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        c2[i] = polar_code<NL>(PP.bound[1], atan2f(r1[2 * i + 1], r1[2 * i]));
-        r2[i] = sqrtf(r1[2 * i] * r1[2 * i] + r1[2 * i + 1] * r1[2 * i + 1]);
+        c2[i] = polar_code_up<NL>(PP.bcs[1], r1[2 * i], r1[2 * i + 1]);
+        r2[i] = r1[2 * i] + r1[2 * i + 1];
       }
-      const int c3 = polar_code<NL>(PP.bound[2], atan2f(r2[1], r2[0]));
-      float rad = sqrtf(r2[0] * r2[0] + r2[1] * r2[1]);
-      int ck[4];  // levels 4..7: lanes l and l ^ 2^k
+      const int c3 = polar_code_up<NL>(PP.bcs[2], r2[0], r2[1]);
+      float rad = r2[0] + r2[1];
+      int ck[4];  // levels 4..7: lanes l and l ^ 2^k (the same sum on both)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float o = lane_xor_f(rad, k);
         const bool hi = (l >> k) & 1;
         const float a = hi ? o : rad, b = hi ? rad : o;
-        ck[k] = polar_code<NL>(PP.bound[3 + k], atan2f(b, a));
-        rad = sqrtf(a * a + b * b);
+        ck[k] = polar_code_up<NL>(PP.bcs[3 + k], a, b);
+        rad = a + b;
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) pcode[vrow][4 * l + i] = static_cast<uint8_t>(c1[i]);
@@ -479,10 +495,10 @@ __global__ __launch_bounds__(256) void encode_fused_kernel(const T* __restrict__
 // consecutive coordinates E*lane .. E*lane + E-1.  Level l (1..log2 d) pairs
 // the two children of each node, whose coordinates differ in bit l-1: the
 // lane's registers for l <= log2 E (each angle once), lanes lane ^
-// 2^(l-1-log2 E) above (both lanes of a pair compute the same angle from the
-// same two radii).  Level 1: atan2(y_2n+1, y_2n) taken into [0, 2π); above:
-// atan2 of the two child radii, in [0, π/2]; code = #{level boundaries below
-// the angle}.  The rotation's butterflies run over the register bits, then the
+// 2^(l-1-log2 E) above (both lanes of a pair compute the same code from the
+// same two radii).  Level 1: the angle of (y_2n, y_2n+1) in [0, 2π); above:
+// that of the two child radii, in [0, π/2]; code = #{level boundaries below
+// the angle}, found by sign tests (polar_code_l1, polar_code_up).  The rotation's butterflies run over the register bits, then the
 // lane bits (the Sylvester matrix is a product over coordinate bits, so the
 // order is free).  ŷ_j is the fp32 product, top-down from radius 1, of cos or
 // sin (bit l-1 of j) of level l's centroid at node j >> l.  The codes reach
@@ -530,29 +546,36 @@ __global__ __launch_bounds__(256) void encode_polar_rq_kernel(const T* __restric
   float rad[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) rad[e] = y[e];
+  // (rad: the coordinates, then from level 1 on the squared radii)
   static_for<RL>([&]<int k>() {  // level k + 1
     constexpr int W = 1 << k;     // child spacing in registers
 #pragma unroll
     for (int u = 0; u < E / (2 * W); ++u) {
       const float a = rad[2 * W * u], b = rad[2 * W * u + W];
-      float th = atan2f(b, a);
-      if constexpr (k == 0) th = th < 0.f ? th + 6.28318530717958647f : th;
-      creg[k][u] = polar_code<NL>(PP.bound[k], th);
-      rad[2 * W * u] = sqrtf(a * a + b * b);
+      if constexpr (k == 0) {
+        creg[k][u] = polar_code_l1<NL>(PP, a, b);
+        rad[2 * W * u] = fmaf(a, a, b * b);
+      } else {
+        creg[k][u] = polar_code_up<NL>(PP.bcs[k], a, b);
+        rad[2 * W * u] = a + b;
+      }
     }
   });
-  // lane levels: the lane's node radius in rad[0]
+  // lane levels: the lane's node (squared) radius in rad[0]
   int clane[6];
   {
     float r = rad[0];
     static_for<6>([&]<int k>() {  // level RL + k + 1: partner lane ^ 2^k
       const bool hi = (lane >> k) & 1;
       const float o = __shfl_xor(r, 1 << k, kWave);
-      const float a = hi ? o : r, b = hi ? r : o;
-      float th = atan2f(b, a);
-      if constexpr (RL + k == 0) th = th < 0.f ? th + 6.28318530717958647f : th;
-      clane[k] = polar_code<NL>(PP.bound[RL + k], th);
-      r = sqrtf(a * a + b * b);
+      const float a = hi ? o : r, b = hi ? r : o;  // the same on both lanes of the pair
+      if constexpr (RL + k == 0) {
+        clane[k] = polar_code_l1<NL>(PP, a, b);
+        r = fmaf(a, a, b * b);
+      } else {
+        clane[k] = polar_code_up<NL>(PP.bcs[RL + k], a, b);
+        r = a + b;
+      }
     });
   }
   // each node's code from the member holding its first coordinate

@@ -55,12 +55,15 @@ struct DevParams {
 };
 
 // Tables of the recursive polar stage for the kernels: per level l (index
-// l-1), cos and sin of every centroid (fp32) and the boundaries (unused +inf).
+// l-1), cos and sin of every centroid (fp32) and the boundaries (unused +inf);
+// bcs: the boundary tests of the encode, (cos β, sin β) at level 1 and
+// (cos² β, sin² β) above (from the fp64 boundaries).
 constexpr int kPolarMaxLevels = 8;
 struct PolarParams {
   float cosc[kPolarMaxLevels][16];
   float sinc[kPolarMaxLevels][16];
   float bound[kPolarMaxLevels][16];
+  float2 bcs[kPolarMaxLevels][16];
   int levels, nl;  // log2 d, 2^b
 };
 
