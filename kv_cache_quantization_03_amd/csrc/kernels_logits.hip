@@ -163,6 +163,11 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
   const int bk = blockIdx.y, b = bk / nkv, kh = bk % nkv;
   const int64_t ctx_v = pm.table ? max<int64_t>(0, min<int64_t>(pm.ctx_lens[b], ctx)) : ctx;
   if (static_cast<int64_t>(blockIdx.x) * kPolarKeys >= ctx_v) return;  // no key of this sequence for the block
+  uint32_t nc[B][NW], ns[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) ns[i] = 0u;
+  float nn = 0.f, ng = 0.f;
+  polar_fetch<B, NW>(k, pm, bk, nkv, ctx, ctx_v, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, nc, ns, nn, ng);
   const int nqv = nq * G, qv0 = blockIdx.z * 4;
   const float* qp[4];
   const float* pp[4];
@@ -225,13 +230,9 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
   }
   __syncthreads();
   // blocks stride over the context's 1024-key blocks; each thread's next
-  // record is loaded while the current one is scored
+  // record is loaded while the current one is scored (the first one while
+  // the tables are built)
   const int64_t nkb = (ctx_v + kPolarKeys - 1) / kPolarKeys;
-  uint32_t nc[B][NW], ns[NW];
-#pragma unroll
-  for (int i = 0; i < NW; ++i) ns[i] = 0u;
-  float nn = 0.f, ng = 0.f;
-  polar_fetch<B, NW>(k, pm, bk, nkv, ctx, ctx_v, static_cast<int64_t>(blockIdx.x) * kPolarKeys + tid, nc, ns, nn, ng);
   for (int64_t kb = blockIdx.x; kb < nkb; kb += gridDim.x) {
   const int64_t key = kb * kPolarKeys + tid;
   uint32_t w[B][NW], sw[NW];
