@@ -92,10 +92,12 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // are the same for every thread of the block, so they are read as scalar
 // operands; the loops are unrolled, so every code's slot and bit are
 // constants.  Up to 4 query vectors per block (grid.z splits the rest).  The
-// QJL sums Σ_{τ_i = +1} p_i come from tables in LDS: for each byte g of the d
-// sign bits and each of its 256 values, the four vectors' sums of p over the
-// set bits (built once per block of 1024 keys), so a key takes d/8 table
-// reads instead of d multiply-adds per vector.  Likewise the level-1 pair i
+// QJL sums Σ_{τ_i = +1} p_i come from tables in LDS: for each 4-bit group h of
+// the d sign bits and each of its 16 values, the four vectors' sums of p over
+// the set bits (built once per block), so a key takes d/4 table reads instead
+// of d multiply-adds per vector; a group's 16 entries (256 bytes) sit in
+// distinct LDS banks, so lanes that read different entries do not collide
+// (8-bit groups at d = 256: d/8 reads).  Likewise the level-1 pair i
 // with code c contributes r_i (q'_2i cos θ_c + q'_2i+1 sin θ_c) to each
 // vector's MSE sum, r_i the product of the upper levels' factors: the bracket
 // is read from a table of the four vectors' values for every (pair, code);
@@ -103,10 +105,19 @@ __global__ __launch_bounds__(256) void logits_valu_kernel(DevParams P, const flo
 // per (level-2 node, its code, its two pairs' codes).  Level l's angles sit
 // in slots d - 2d/2^l + node.
 // ----------------------------------------------------------------------------
-// Keys (and threads) per block: 1024, or 512 at d = 256, whose records and
-// path products need more than the 128 registers a 1024-thread block allows.
+// Keys (and threads) per block: 512.  Up to d = 128 two blocks share a
+// compute unit (tables of at most 46 KB, at most 128 registers), so one
+// block's table reads run under the other's VALU work; at d = 256 the records
+// and path products take up to 254 registers and a block has the unit alone.
 template <int LD>
-constexpr int polar_keys() { return LD <= 7 ? 1024 : 512; }
+constexpr int polar_keys() { return 512; }
+template <int LD>
+constexpr int polar_blocks_per_cu() { return LD <= 7 ? 2 : 1; }
+// Sign bits per QJL table index: 4 (16-entry tables) up to d = 128; 8 at
+// d = 256, whose registers cannot take twice the table reads (the block has
+// the unit's LDS to itself there).
+template <int LD>
+constexpr int polar_tab_bits() { return LD <= 7 ? 4 : 8; }
 
 // NW consecutive 32-bit words (NW = 2: one 8-byte load; else 16-byte loads).
 template <int NW>
@@ -146,7 +157,8 @@ __device__ __forceinline__ void polar_fetch(const tq_packed_t& k, const PageMap&
 // pm.table set (a paged cache): sequence b scores its first
 // min(ctx_lens[b], ctx) positions; ctx is the stride of the logits rows.
 template <int B, int LD>
-__global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
+__global__ __launch_bounds__(polar_keys<LD>())
+__attribute__((amdgpu_waves_per_eu(polar_blocks_per_cu<LD>() * polar_keys<LD>() / 256))) void logits_polar_kernel(DevParams P, PolarParams PP, const float* __restrict__ qrot,
                                                            const float* __restrict__ proj, int Hq, int nq, int G,
                                                            int nkv, int64_t ctx, tq_packed_t k,
                                                            float* __restrict__ logits, PageMap pm) {
@@ -154,7 +166,8 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
   __shared__ float2 tab[LD][NL];      // (cos, sin) of every level's centroids
   __shared__ float psum[4];           // Σ_i p_i of each tile vector
   __shared__ float4 pj[d];            // p_j of the four tile vectors
-  __shared__ float4 ptab[d / 8][256]; // [byte g][value]: Σ over the set bits k of p_{8g+k}
+  constexpr int PB = polar_tab_bits<LD>(), PV = 1 << PB, PG = 32 / PB;  // PG: groups per sign word
+  __shared__ float4 ptab[d / PB][PV];  // [group h][value]: Σ over the set bits k of p_{PB h + k}
   __shared__ float4 qtab[d / 2][NL];  // [pair i][code c]: q'_2i cos θ_c + q'_2i+1 sin θ_c
   constexpr bool L2T = NL <= 4 && d <= 128;  // level-2 table: d/4 nodes x NL^3 entries
   constexpr int N3 = L2T ? NL * NL * NL : 1;
@@ -198,17 +211,17 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
                         fmaf(qp[2][2 * i + 1], sn, qp[2][2 * i] * cs), fmaf(qp[3][2 * i + 1], sn, qp[3][2 * i] * cs)};
   }
   __syncthreads();
-  for (int e = tid; e < (d / 8) * 256; e += kPolarKeys) {
-    const int g = e >> 8, v = e & 255;
+  for (int e = tid; e < (d / PB) * PV; e += kPolarKeys) {
+    const int h = e >> PB, v = e & (PV - 1);
     float4 a = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
+    for (int kb = 0; kb < PB; ++kb) {
       if ((v >> kb) & 1) {
-        const float4 x = pj[8 * g + kb];
+        const float4 x = pj[PB * h + kb];
         a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
       }
     }
-    ptab[g][v] = a;
+    ptab[h][v] = a;
   }
   if constexpr (L2T) {
     // node n, codes (c2, ca, cb): cos θ2_c2 · qtab[2n][ca] + sin θ2_c2 · qtab[2n+1][cb].
@@ -229,7 +242,7 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
     }
   }
   __syncthreads();
-  // blocks stride over the context's 1024-key blocks; each thread's next
+  // blocks stride over the context's 512-key blocks; each thread's next
   // record is loaded while the current one is scored (the first one while
   // the tables are built)
   const int64_t nkb = (ctx_v + kPolarKeys - 1) / kPolarKeys;
@@ -314,9 +327,14 @@ __global__ __launch_bounds__(polar_keys<LD>()) void logits_polar_kernel(DevParam
     __builtin_amdgcn_sched_barrier(0);
   });
 #pragma unroll
-  for (int g = 0; g < d / 8; ++g) {
-    const float4 x = ptab[g][(sw[g >> 2] >> (8 * (g & 3))) & 255u];
+  for (int h = 0; h < d / PB; ++h) {
+    const float4 x = ptab[h][(sw[h / PG] >> (PB * (h % PG))) & (PV - 1u)];
     qj[0] += x.x; qj[1] += x.y; qj[2] += x.z; qj[3] += x.w;
+    if (h % 8 == 7) {  // eight reads in flight at a time: all of them at once would spill
+#pragma unroll
+      for (int t = 0; t < 4; ++t) asm volatile("" : "+v"(qj[t]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t)  // Σ p τ = 2 Σ_{τ=+1} p - Σ p
@@ -333,11 +351,12 @@ hipError_t launch_logits_polar(const tq_codec_s* c, const void* ws, int batch, i
   const float* qrot = static_cast<const float*>(ws);
   const float* proj = qrot + nv * c->prm.d;
   const int G = n_q_heads / n_kv_heads;
-  // about one block per compute unit (a block's tables fill most of its LDS);
-  // each block then scores several key blocks with the tables it built
+  // polar_blocks_per_cu blocks per compute unit in all; each block then
+  // scores several key blocks with the tables it built
   const int64_t nz = ceil_div(static_cast<int64_t>(n_queries) * G, 4);
-  const int64_t per = std::max<int64_t>(1, device_cu_count() / std::max<int64_t>(1, batch * n_kv_heads * nz));
   auto go = [&]<int B, int LD>() -> hipError_t {
+    const int64_t per = std::max<int64_t>(
+        1, polar_blocks_per_cu<LD>() * device_cu_count() / std::max<int64_t>(1, batch * n_kv_heads * nz));
     const int64_t nkb = ceil_div(ctx, polar_keys<LD>());
     const dim3 grid(static_cast<unsigned>(std::min(nkb, per)), batch * n_kv_heads, static_cast<unsigned>(nz));
     hipLaunchKernelGGL((logits_polar_kernel<B, LD>), grid, dim3(polar_keys<LD>()), 0, s, c->prm, c->pol, qrot, proj,
